@@ -1,0 +1,431 @@
+#!/usr/bin/env python
+"""Benchmark of one Qwen Sparse Attention layer on one MI355X.
+
+Prints ONE JSON line.  `value` is prefill throughput (new tokens/s) of the
+1M-context chunked prefill (104858 new tokens after a 943718-token cached
+prefix, the pages' 90% prefix-cache-hit setting), one step = every step of the
+layer (rotary of the new Q/K rows, compression of the blocks they complete,
+index scores, block selection and sparse attention for all 8192-query chunks).
+The same line carries the 1M-context decode step (B=4, one new token each)
+under "decode".  Inputs are seeded synthetic tensors already resident in HBM.
+
+Timing: W untimed warm-up steps, then K steps between two device
+synchronisations; per-kernel durations come from HIP events recorded on the
+launch stream around every launch inside the timed steps.  Decode steps are
+timed one by one with a 1 GiB cache flush between them (outside the events),
+so the k-bar scan reads HBM rather than the 256 MB last-level cache.
+
+Rooflines (MI355X published peaks): HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s.
+`roofline` is the dominant prefill kernel (the sparse-attention gather);
+`decode.roofline` the dominant decode kernel (the block-key scan).  Achieved
+figures are algorithmic bytes (or flops) per launch over the measured average
+launch time.  `cpu_baseline` is the CPU oracle timed on a sample of rows.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QSA prefill tokens/s + decode step µs at 1M ctx; % of MFMA / HBM roofline"
+HBM_PEAK = 8.0e12
+BF16_PEAK = 2.5e15
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="prefill_prefix943718_chunk104858")
+    ap.add_argument("--decode-workload", default="decode_B4_ctx1M")
+    ap.add_argument("--decode-steps", type=int, default=30)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="oracle rows timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ workload geometry
+
+def attended_tokens(pos: int, budget: int) -> int:
+    o = pos // 4
+    return 4 * min(budget - 1, o) + (pos % 4) + 1
+
+
+def prefill_geometry(wl, c0: int, c1: int):
+    """Algorithmic bytes / flops of query rows [c0, c1) of a prefill chunk."""
+    n_tok = 0
+    cand = 0
+    for i in range(c0, c1):
+        p = wl.ctx + i
+        n_tok += attended_tokens(p, wl.budget)
+        cand += p // 4
+    rows = (c1 - c0) * wl.batch
+    n_tok *= wl.batch
+    cand *= wl.batch
+    return dict(
+        rows=rows,
+        gathered_tokens=n_tok,
+        # K and V rows of both KV heads (2 x 2 x 256 bf16 = 2 KiB per token), Q read, O written
+        attn_bytes=n_tok * 2 * 2 * 256 * 2 + rows * 24 * 256 * 2 * 2,
+        attn_flops=n_tok * 24 * 256 * 2 * 2,
+        candidates=cand,
+        # folded minimum: 2 * 128 flop per (query, candidate); kbar read once, scores written
+        index_flops=cand * 2 * 128,
+        index_bytes_min=cand * 4,
+    )
+
+
+# ------------------------------------------------------------------ device set-up
+
+class Prefill:
+    def __init__(self, wl, x, torch, qsa):
+        B, L, ctx, T = wl.batch, wl.length, wl.ctx, wl.tq
+        dev = "cuda"
+        self.wl, self.qsa, self.torch = wl, qsa, torch
+        self.q_raw = x.q.to(dev)
+        self.k_new = x.k[:, ctx:].contiguous().to(dev)
+        self.q_idx = x.q_idx.to(dev)
+        self.k_idx = x.k_idx.to(dev)
+        self.v_cache = x.v.to(dev)
+        self.k_cache = x.k.to(dev)
+        if ctx > 0:
+            qsa.rope_apply(self.k_cache[:, :ctx], [0] * B)
+        self.kbar = torch.zeros((B, max(1, L // 4), 128), dtype=torch.bfloat16, device=dev)
+        if ctx // 4 > 0:
+            qsa.compress_block_keys(self.k_idx, 0, ctx // 4, self.kbar)
+        self.bufs = qsa.PrefillBuffers(B, T, ctx, wl.budget, wl.chunk)
+        self.out = torch.empty((B, T, 24, 256), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, T, 24), dtype=torch.float32, device=dev)
+        self.q_rot = torch.empty_like(self.q_raw)
+        torch.cuda.synchronize()
+
+    def step(self, timer=None):
+        """One layer step; `timer(name)` returns a context that brackets launches with events."""
+        wl, q = self.wl, self.qsa
+        B, T, ctx = wl.batch, wl.tq, wl.ctx
+        pos = [ctx] * B
+        with timer("rope"):
+            q.rope_apply(self.q_raw, pos, out=self.q_rot)
+            q.rope_apply(self.k_new, pos, out=self.k_cache[:, ctx:ctx + T])
+        with timer("compress"):
+            q.compress_block_keys(self.k_idx, ctx // 4, (ctx + T) // 4, self.kbar)
+        ch = self.bufs.chunk
+        for c0 in range(0, T, ch):
+            c1 = min(T, c0 + ch)
+            cpos = [ctx + c0] * B
+            with timer("index_scores"):
+                q.index_scores(self.q_idx[:, c0:c1], self.kbar, cpos, self.bufs.scores)
+            with timer("select_topk"):
+                q.select_topk(self.bufs.scores, cpos, wl.budget, self.bufs.sel[:, c0:c1])
+            with timer("sparse_attn_prefill"):
+                q.sparse_attn_prefill(self.q_rot[:, c0:c1], self.k_cache, self.v_cache, self.bufs.sel[:, c0:c1],
+                                      cpos, self.out[:, c0:c1], self.lse[:, c0:c1])
+
+
+class Decode:
+    def __init__(self, wl, x, torch, qsa):
+        B, ctx = wl.batch, wl.ctx
+        dev = "cuda"
+        self.wl, self.qsa, self.torch = wl, qsa, torch
+        self.pos = ctx
+        self.k_cache = x.k.to(dev)
+        qsa.rope_apply(self.k_cache[:, :ctx], [0] * B)
+        self.v_cache = x.v.to(dev)
+        self.k_idx = x.k_idx.to(dev)
+        self.kbar = torch.zeros((B, max(1, (ctx + 1) // 4), 128), dtype=torch.bfloat16, device=dev)
+        qsa.compress_block_keys(self.k_idx, 0, ctx // 4, self.kbar)
+        self.q_raw = x.q.to(dev)
+        self.k_new = x.k[:, ctx:ctx + 1].contiguous().to(dev)
+        self.q_idx = x.q_idx.to(dev)
+        ld = max(4, (ctx // 4 + 3) // 4 * 4)
+        self.scores = torch.empty((B, 1, ld), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((B, 1, wl.budget), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, 24, 256), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, 24), dtype=torch.float32, device=dev)
+        self.ws = qsa.decode_workspace(B, wl.budget)
+        self.q_rot = torch.empty_like(self.q_raw)
+        torch.cuda.synchronize()
+
+    def step(self, timer):
+        wl, q = self.wl, self.qsa
+        B, pos = wl.batch, self.pos
+        p = [pos] * B
+        with timer("rope"):
+            q.rope_apply(self.q_raw, p, out=self.q_rot)
+            q.rope_apply(self.k_new, p, out=self.k_cache[:, pos:pos + 1])
+        if (pos + 1) % 4 == 0:
+            with timer("compress"):
+                q.compress_block_keys(self.k_idx, pos // 4, pos // 4 + 1, self.kbar)
+        with timer("index_scores"):
+            q.index_scores(self.q_idx, self.kbar, p, self.scores)
+        with timer("select_topk"):
+            q.select_topk(self.scores, p, wl.budget, self.sel)
+        with timer("sparse_attn_decode"):
+            q.sparse_attn_decode(self.q_rot[:, 0], self.k_cache, self.v_cache, self.sel[:, 0], p, self.out,
+                                 self.lse, self.ws)
+
+
+class EventTimer:
+    """Records a start/end HIP event pair on the current stream around each
+    bracketed group of launches; durations are read after synchronising."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []          # (name, start, end)
+
+    def __call__(self, name):
+        timer = self
+
+        class _Ctx:
+            def __enter__(self_inner):
+                self_inner.s = timer.torch.cuda.Event(enable_timing=True)
+                self_inner.s.record()
+
+            def __exit__(self_inner, *exc):
+                e = timer.torch.cuda.Event(enable_timing=True)
+                e.record()
+                timer.pairs.append((name, self_inner.s, e))
+                return False
+
+        return _Ctx()
+
+    def totals(self):
+        out = {}
+        for name, s, e in self.pairs:
+            ms = s.elapsed_time(e)
+            tot, n = out.get(name, (0.0, 0))
+            out[name] = (tot + ms, n + 1)
+        return out
+
+
+class NullTimer:
+    def __call__(self, name):
+        class _Ctx:
+            def __enter__(self):
+                return None
+
+            def __exit__(self, *exc):
+                return False
+        return _Ctx()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_sparse_long_12_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, src: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash(src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(wl, x, n_rows: int, args):
+    from threadpoolctl import threadpool_limits
+
+    from block_sparse_long_12_amd import inputs as I
+    from oracle import qsa_oracle as O
+    rows = I.sample_rows(wl, n_rows)
+    B = O.bits
+    with threadpool_limits(limits=1):
+        layer = O.OracleLayer(B(x.q), B(x.q_idx), B(x.k), B(x.v), B(x.k_idx), x.q_pos0, wl.budget)
+        t0 = time.perf_counter()
+        for b in sorted({r[0] for r in rows}):
+            layer.kbar_bits(b)
+        t_setup = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        layer.rows(rows)
+        t_rows = time.perf_counter() - t0
+    per_row = t_rows / len(rows)
+    total_rows = wl.batch * wl.tq
+    full = t_setup + per_row * total_rows
+    log(args, f"cpu oracle: {len(rows)} rows in {t_rows:.2f}s (+{t_setup:.2f}s block keys)")
+    return {
+        "value": total_rows / full if wl.kind == "prefill" else full * 1e6,
+        "unit": "tokens/s" if wl.kind == "prefill" else "us/step",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(rows)} seeded query rows of {wl.name} (block keys of the whole context compressed "
+                  f"once, {t_setup:.2f}s); per-row time {per_row * 1e3:.1f} ms extrapolated to "
+                  f"{total_rows} rows; numpy float64, 1 BLAS thread",
+    }
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus N with N > 1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    from block_sparse_long_12_amd import inputs as I
+    from block_sparse_long_12_amd import qsa
+    if not os.path.exists(qsa.LIB_PATH):
+        from block_sparse_long_12_amd import build as _b
+        _b.build()
+    qsa.lib()
+    assert torch.cuda.is_available(), "bench needs a GPU"
+
+    wl = I.WORKLOADS[args.workload]
+    t0 = time.time()
+    x = I.make_inputs(wl)
+    log(args, f"inputs {wl.name}: {time.time() - t0:.1f}s")
+    pf = Prefill(wl, x, torch, qsa)
+    for _ in range(args.warmup):
+        pf.step(NullTimer())
+    torch.cuda.synchronize()
+    timer = EventTimer(torch)
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        pf.step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    kern = timer.totals()
+    ms_per_step = wall * 1e3 / args.steps
+    step_gpu_ms = sum(t for t, _ in kern.values()) / args.steps
+    tokens = wl.batch * wl.tq
+    value = tokens / (ms_per_step / 1e3)
+
+    geo = prefill_geometry(wl, 0, wl.tq)
+    n_chunks = math.ceil(wl.tq / (wl.chunk or wl.tq))
+    attn_ms, attn_n = kern["sparse_attn_prefill"]
+    attn_avg_s = attn_ms / attn_n / 1e3
+    attn_bytes_per_launch = geo["attn_bytes"] / n_chunks
+    idx_ms, idx_n = kern["index_scores"]
+    sel_ms, sel_n = kern["select_topk"]
+    roofline = {
+        "bound": "hbm",
+        "kernel": "sparse_attn_prefill",
+        "achieved": attn_bytes_per_launch / attn_avg_s / 1e9,
+        "peak": HBM_PEAK / 1e9,
+        "unit": "GB/s",
+        "frac": attn_bytes_per_launch / attn_avg_s / HBM_PEAK,
+        "traffic": measured_traffic("sparse_attn_prefill", "attention.hip"),
+    }
+    mfma = {
+        "index_scores_frac": (geo["index_flops"] / n_chunks) / (idx_ms / idx_n / 1e3) / BF16_PEAK,
+        "layer_frac": (geo["index_flops"] + geo["attn_flops"]) / (ms_per_step / 1e3) / BF16_PEAK,
+        "note": "folded indexer minimum (2*128 flop per query-candidate pair) plus attention flops",
+    }
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "new_tokens": wl.tq, "cached_tokens": wl.ctx,
+                   "context": wl.length, "budget_blocks": wl.budget, "block_tokens": 4,
+                   "query_chunk": wl.chunk, "heads": "24q/2kv x 256, indexer 4q/1k x 128"},
+        "roofline": roofline,
+        "mfma": mfma,
+        "kernels_ms_per_step": {k: t / args.steps for k, (t, n) in kern.items()},
+        "launches_per_step": {k: n // args.steps for k, (t, n) in kern.items()},
+        "gpu_ms_per_step": step_gpu_ms,
+        "gather_bytes_per_step": geo["gathered_tokens"] * 2 * 2 * 256 * 2,
+    }
+    log(args, f"prefill: {ms_per_step:.1f} ms/step, {value:.0f} tok/s; kernels {rec['kernels_ms_per_step']}")
+    del pf
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        dwl = I.WORKLOADS[args.decode_workload]
+        t0 = time.time()
+        dx = I.make_inputs(dwl)
+        log(args, f"inputs {dwl.name}: {time.time() - t0:.1f}s")
+        dd = Decode(dwl, dx, torch, qsa)
+        del dx
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            dd.step(NullTimer())
+        torch.cuda.synchronize()
+        steps_ms = []
+        dtimer = EventTimer(torch)
+        for _ in range(args.decode_steps):
+            flush.zero_()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            dd.step(dtimer)
+            e.record()
+            torch.cuda.synchronize()
+            steps_ms.append(s.elapsed_time(e))
+        dk = dtimer.totals()
+        steps_ms.sort()
+        med = steps_ms[len(steps_ms) // 2]
+        o = dwl.ctx // 4
+        scan_bytes = dwl.batch * (o * 128 * 2 + o * 4 + 4 * 128 * 2)
+        gather = dwl.batch * attended_tokens(dwl.ctx, dwl.budget) * 2 * 2 * 256 * 2
+        step_bytes = scan_bytes + gather + dwl.batch * (24 * 256 * 2 * 2 + dwl.budget * 4 * 2)
+        i_ms, i_n = dk["index_scores"]
+        i_avg = i_ms / i_n / 1e3
+        rec["decode"] = {
+            "workload": dwl.name,
+            "batch": dwl.batch,
+            "context": dwl.ctx,
+            "budget_blocks": dwl.budget,
+            "step_us_median": med * 1e3,
+            "step_us_min": steps_ms[0] * 1e3,
+            "steps": args.decode_steps,
+            "cache_flushed": True,
+            "hbm_frac_step": step_bytes / (med / 1e3) / HBM_PEAK,
+            "algorithmic_bytes_per_step": step_bytes,
+            "kernels_us_per_step": {k: t * 1e3 / args.decode_steps for k, (t, n) in dk.items()},
+            "roofline": {
+                "bound": "hbm",
+                "kernel": "index_scores",
+                "achieved": scan_bytes / i_avg / 1e9,
+                "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s",
+                "frac": scan_bytes / i_avg / HBM_PEAK,
+                "traffic": measured_traffic("index_scores", "index_scores.hip"),
+            },
+        }
+        log(args, f"decode: median {med * 1e3:.1f} us/step; kernels {rec['decode']['kernels_us_per_step']}")
+        del dd, flush
+        torch.cuda.empty_cache()
+
+    if args.cpu_rows > 0:
+        rec["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_rows, args)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

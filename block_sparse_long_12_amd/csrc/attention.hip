@@ -1,0 +1,307 @@
+// Step 4: grouped-query attention over the selected micro-blocks
+// (Qwen3.8-Flash-Next model card, "Model Overview": 24 query heads, 2 KV
+// heads, head dim 256; blog "Attention: GDN + QSA": attention runs over the
+// selected regions; "QSA's Attention Kernel" covers prefill and decode).
+//
+// For query position p, KV head g and each of its 12 query heads h:
+//   out[h] = sum_n softmax_n(scale * q[h] . k[n][g]) v[n][g]
+// over the tokens n = 4j + e of the selected blocks j, with n <= p.
+//
+// One wave per (query, KV head).  The wave walks the selected blocks 4 at a
+// time (16 tokens):
+//   - each lane gathers one token row of K and of V (lane & 15 = token slot,
+//     lane >> 4 = which 16-byte slice), 8 KiB + 8 KiB per step per wave, as
+//     whole 512-byte rows of the token-major cache;
+//   - S^T (16 tokens x 16 head slots, 12 real) = K Q^T on
+//     v_mfma_f32_16x16x32_bf16 with Q^T held in registers;
+//   - online softmax in float32 (exp2 with the scale folded into log2 e);
+//     each lane owns one head for all its accumulators, so rescaling is a
+//     per-lane multiply;
+//   - O^T (256 dims x 16 heads) += V^T P^T on v_mfma_f32_16x16x16bf16_1k.
+//     The S^T accumulator layout (lane: tokens 4*(l/16)+r of head l%16) is
+//     exactly the B-operand layout the PV product needs, so P never moves
+//     between lanes; V is transposed through a wave-private LDS tile.
+// The gather is the bound (12 flop per gathered byte), not the matrix cores.
+#include <math.h>
+
+#include "qsa_internal.h"
+
+namespace qsa {
+
+constexpr int kVtStride = 20;                 // bf16 per dim row of the V^T tile (16 tokens + pad)
+constexpr int kVtElems = kD * kVtStride;      // one wave's tile
+
+struct WaveState {
+    float m;            // running max of raw logits q.k for this lane's head
+    float l;            // running softmax denominator
+    f32x4_t acc[16];    // O^T rows 16*nt + 4*(lane/16) + r, head lane%16
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Attend over sel[blk_begin .. blk_end) for the query at position p.
+// kg / vg point at KV head g of the sequence (token stride 2 * 256).
+__device__ __forceinline__ void attend_blocks(const uint16_t* __restrict__ kg,
+                                              const uint16_t* __restrict__ vg,
+                                              const int32_t* __restrict__ selrow, int blk_begin,
+                                              int blk_end, int p, const bf16x8_t (&qf)[8],
+                                              float c, WaveState& st, uint16_t* vt) {
+    const int lane = threadIdx.x & 63;
+    const int c16 = lane & 15;
+    const int G = lane >> 4;
+    const int o = p / kBlock;
+    for (int cb = blk_begin; cb < blk_end; cb += 4) {
+        const int slot_blk = cb + (c16 >> 2);
+        const int j = (slot_blk < blk_end) ? selrow[slot_blk] : -1;
+        const int n = kBlock * j + (c16 & 3);
+        const bool valid = (j >= 0) && (j <= o) && (n <= p);
+        const uint16_t* kr = kg + static_cast<int64_t>(n) * (kHkv * kD);
+        const uint16_t* vr = vg + static_cast<int64_t>(n) * (kHkv * kD);
+        bf16x8_t ka[8], vv[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (valid) {
+                ka[s] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * s + 8 * G);
+                vv[s] = *reinterpret_cast<const bf16x8_t*>(vr + 8 * (4 * s + G));
+            } else {
+                ka[s] = bf16x8_t{};
+                vv[s] = bf16x8_t{};
+            }
+        }
+        const uint64_t vmask = __ballot(valid);
+        if (vmask == 0) continue;                              // wave-uniform
+
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qf[ks], s, 0, 0, 0);
+
+        float sv[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool ok = (vmask >> (4 * G + r)) & 1ull;
+            sv[r] = ok ? s[r] : -INFINITY;
+            mx = fmaxf(mx, sv[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(st.m, mx);
+        const float alpha = exp2f((st.m - m_new) * c);        // 0 when st.m = -inf
+        s16x4_t pb;
+        float ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pr = (sv[r] == -INFINITY) ? 0.f : exp2f((sv[r] - m_new) * c);
+            const uint16_t pbits = f32_to_bf16(pr);
+            pb[r] = static_cast<short>(pbits);
+            ps += bf16_to_f32(pbits);          // the denominator uses the weights the product sees
+        }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        st.l = st.l * alpha + ps;
+        st.m = m_new;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) st.acc[t] *= alpha;
+
+        // V^T tile: vt[dim * kVtStride + token slot]
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+            const uint16_t* e = reinterpret_cast<const uint16_t*>(&vv[s2]);
+            const int d0 = 8 * (4 * s2 + G);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) vt[(d0 + q) * kVtStride + c16] = e[q];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int nt = 0; nt < 16; ++nt) {
+            const s16x4_t va = *reinterpret_cast<const s16x4_t*>(vt + (16 * nt + c16) * kVtStride + 4 * G);
+            st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, st.acc[nt], 0, 0, 0);
+        }
+        wave_lds_sync();
+    }
+}
+
+__device__ __forceinline__ void load_q_frags(const uint16_t* qh, bool ok, bf16x8_t (&qf)[8]) {
+    const int G = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+        qf[ks] = ok ? *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * G) : bf16x8_t{};
+}
+
+__device__ __forceinline__ void init_state(WaveState& st) {
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// ---------------------------------------------------------------- prefill
+
+__global__ __launch_bounds__(128) void attn_prefill_kernel(
+    const uint16_t* __restrict__ q, int64_t qs, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t kvs, const int32_t* __restrict__ sel, int64_t sels,
+    Positions pos0, int tq, int budget, float scale, float c, uint16_t* __restrict__ out,
+    int64_t os, float* __restrict__ lse, int64_t lss) {
+    __shared__ uint16_t vt_all[2 * kVtElems];
+    const int g = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int c16 = lane & 15;
+    const int G = lane >> 4;
+    const int b = blockIdx.x / tq;
+    const int i = blockIdx.x % tq;
+    const int p = pos0.p[b] + i;
+    const int head = g * kGroup + c16;
+    const bool head_ok = c16 < kGroup;
+
+    bf16x8_t qf[8];
+    const uint16_t* qrow = q + b * qs + static_cast<int64_t>(i) * (kHq * kD);
+    load_q_frags(qrow + (head_ok ? head : 0) * kD, head_ok, qf);
+    WaveState st;
+    init_state(st);
+    attend_blocks(k + b * kvs + g * kD, v + b * kvs + g * kD, sel + b * sels + static_cast<int64_t>(i) * budget,
+                  0, budget, p, qf, c, st, vt_all + g * kVtElems);
+
+    if (head_ok) {
+        const float inv_l = 1.f / st.l;
+        uint16_t* orow = out + b * os + static_cast<int64_t>(i) * (kHq * kD) + head * kD + 4 * G;
+#pragma unroll
+        for (int nt = 0; nt < 16; ++nt) {
+            uint2 w;
+            w.x = f32_to_bf16(st.acc[nt][0] * inv_l) | (static_cast<uint32_t>(f32_to_bf16(st.acc[nt][1] * inv_l)) << 16);
+            w.y = f32_to_bf16(st.acc[nt][2] * inv_l) | (static_cast<uint32_t>(f32_to_bf16(st.acc[nt][3] * inv_l)) << 16);
+            *reinterpret_cast<uint2*>(orow + 16 * nt) = w;
+        }
+        if (lse != nullptr && G == 0)
+            lse[b * lss + static_cast<int64_t>(i) * kHq + head] = st.m * scale + logf(st.l);
+    }
+}
+
+hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
+                               const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
+                               const Positions& pos0, int batch, int tq, int budget, float scale,
+                               uint16_t* out, int64_t os, float* lse, int64_t lss,
+                               hipStream_t stream) {
+    const int64_t rows = static_cast<int64_t>(batch) * tq;
+    if (rows == 0) return hipSuccess;
+    const float c = scale * 1.4426950408889634f;
+    hipLaunchKernelGGL(attn_prefill_kernel, dim3(static_cast<unsigned>(rows)), dim3(128), 0, stream,
+                       q, qs, k, v, kvs, sel, sels, pos0, tq, budget, scale, c, out, os, lse, lss);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- decode
+
+// Split the budget over n_split workgroups per sequence; each writes the
+// partial (max, sum, unnormalised O) of its blocks for the 24 heads.
+static void decode_split(int batch, int budget, int* n_split, int* bps) {
+    int s = 128 / (batch > 0 ? batch : 1);
+    if (s < 1) s = 1;
+    const int max_s = (budget + 3) / 4;
+    if (s > max_s) s = max_s;
+    int per = (budget + s - 1) / s;
+    per = (per + 3) & ~3;
+    *bps = per;
+    *n_split = (budget + per - 1) / per;
+}
+
+size_t decode_workspace_bytes(int batch, int budget) {
+    int s, per;
+    decode_split(batch, budget, &s, &per);
+    return static_cast<size_t>(batch) * s * kHq * (2 + kD) * sizeof(float);
+}
+
+__global__ __launch_bounds__(128) void attn_decode_split_kernel(
+    const uint16_t* __restrict__ q, int64_t qs, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t kvs, const int32_t* __restrict__ sel, int64_t sels,
+    Positions pos, int budget, int n_split, int bps, float c, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc) {
+    __shared__ uint16_t vt_all[2 * kVtElems];
+    const int g = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int c16 = lane & 15;
+    const int G = lane >> 4;
+    const int b = blockIdx.x / n_split;
+    const int s = blockIdx.x % n_split;
+    const int p = pos.p[b];
+    const int head = g * kGroup + c16;
+    const bool head_ok = c16 < kGroup;
+
+    bf16x8_t qf[8];
+    load_q_frags(q + b * qs + (head_ok ? head : 0) * kD, head_ok, qf);
+    WaveState st;
+    init_state(st);
+    const int blk_begin = s * bps;
+    const int blk_end = min(budget, blk_begin + bps);
+    attend_blocks(k + b * kvs + g * kD, v + b * kvs + g * kD, sel + b * sels, blk_begin, blk_end, p,
+                  qf, c, st, vt_all + g * kVtElems);
+    if (head_ok) {
+        const int64_t idx = (static_cast<int64_t>(b) * n_split + s) * kHq + head;
+        if (G == 0) {
+            ws_ml[2 * idx] = st.m;
+            ws_ml[2 * idx + 1] = st.l;
+        }
+        float* a = ws_acc + idx * kD + 4 * G;
+#pragma unroll
+        for (int nt = 0; nt < 16; ++nt)
+            *reinterpret_cast<float4*>(a + 16 * nt) = make_float4(st.acc[nt][0], st.acc[nt][1], st.acc[nt][2], st.acc[nt][3]);
+    }
+}
+
+// One wave per (sequence, head): merge the n_split partial states.
+__global__ __launch_bounds__(64) void attn_decode_combine_kernel(
+    const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, int n_split, float scale,
+    float c, uint16_t* __restrict__ out, int64_t os, float* __restrict__ lse) {
+    const int lane = threadIdx.x;
+    const int b = blockIdx.x / kHq;
+    const int h = blockIdx.x % kHq;
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s)
+        M = fmaxf(M, ws_ml[2 * ((static_cast<int64_t>(b) * n_split + s) * kHq + h)]);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < n_split; ++s) {
+        const int64_t idx = (static_cast<int64_t>(b) * n_split + s) * kHq + h;
+        const float m = ws_ml[2 * idx];
+        if (m == -INFINITY) continue;
+        const float w = exp2f((m - M) * c);
+        L += w * ws_ml[2 * idx + 1];
+        const float4 a = *reinterpret_cast<const float4*>(ws_acc + idx * kD + 4 * lane);
+        acc.x += w * a.x;
+        acc.y += w * a.y;
+        acc.z += w * a.z;
+        acc.w += w * a.w;
+    }
+    const float inv = 1.f / L;
+    uint2 o;
+    o.x = f32_to_bf16(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
+    o.y = f32_to_bf16(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(out + b * os + h * kD + 4 * lane) = o;
+    if (lse != nullptr && lane == 0) lse[static_cast<int64_t>(b) * kHq + h] = M * scale + logf(L);
+}
+
+hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
+                              const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
+                              const Positions& pos, int batch, int budget, float scale,
+                              uint16_t* out, int64_t os, float* lse, void* ws,
+                              hipStream_t stream) {
+    if (batch == 0) return hipSuccess;
+    int n_split, bps;
+    decode_split(batch, budget, &n_split, &bps);
+    float* ws_ml = static_cast<float*>(ws);
+    float* ws_acc = ws_ml + static_cast<size_t>(batch) * n_split * kHq * 2;
+    const float c = scale * 1.4426950408889634f;
+    hipLaunchKernelGGL(attn_decode_split_kernel, dim3(static_cast<unsigned>(batch * n_split)),
+                       dim3(128), 0, stream, q, qs, k, v, kvs, sel, sels, pos, budget, n_split, bps,
+                       c, ws_ml, ws_acc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(static_cast<unsigned>(batch * kHq)), dim3(64),
+                       0, stream, ws_ml, ws_acc, n_split, scale, c, out, os, lse);
+    return hipGetLastError();
+}
+
+}  // namespace qsa

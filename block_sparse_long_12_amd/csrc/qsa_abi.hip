@@ -1,0 +1,282 @@
+// C ABI of libqsa: argument validation, then one launch sequence per call on
+// the caller's stream.  Validation touches no device memory and makes no HIP
+// call, so every rejected call returns before anything is launched.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "qsa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qsa_status_t fail(qsa_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+qsa_status_t ok() {
+    g_err[0] = '\0';
+    return QSA_OK;
+}
+
+qsa_status_t hip_result(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(QSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool stride_ok(int64_t s) { return s > 0 && (s % 8) == 0; }
+
+#define CHECK(cond, ...)                                            \
+    do {                                                            \
+        if (!(cond)) return fail(QSA_ERR_INVALID_ARGUMENT, __VA_ARGS__); \
+    } while (0)
+
+// Copies host positions into the by-value kernel argument; every position
+// plus `span` must stay representable and non-negative.
+qsa_status_t take_positions(const int32_t* pos, int32_t batch, int32_t span, const char* name,
+                            qsa::Positions& out) {
+    CHECK(pos != nullptr, "%s is NULL", name);
+    for (int b = 0; b < batch; ++b) {
+        CHECK(pos[b] >= 0, "%s[%d] = %d is negative", name, b, pos[b]);
+        CHECK(static_cast<int64_t>(pos[b]) + span < (int64_t{1} << 30), "%s[%d] = %d too large", name,
+              b, pos[b]);
+        out.p[b] = pos[b];
+    }
+    for (int b = batch; b < QSA_MAX_BATCH; ++b) out.p[b] = 0;
+    return QSA_OK;
+}
+
+qsa_status_t check_batch(int32_t batch) {
+    CHECK(batch >= 1 && batch <= QSA_MAX_BATCH, "batch = %d outside [1, %d]", batch, QSA_MAX_BATCH);
+    return QSA_OK;
+}
+
+#define TRY(expr)                          \
+    do {                                   \
+        qsa_status_t _s = (expr);          \
+        if (_s != QSA_OK) return _s;       \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+qsa_status_t qsa_get_dims(qsa_dims_t* out) {
+    CHECK(out != nullptr, "out is NULL");
+    *out = qsa_dims_t{qsa::kBlock, qsa::kHq, qsa::kHkv, qsa::kD, qsa::kRot, qsa::kHi, qsa::kDi};
+    return ok();
+}
+
+const char* qsa_status_string(qsa_status_t s) {
+    switch (s) {
+        case QSA_OK: return "ok";
+        case QSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case QSA_ERR_UNSUPPORTED: return "unsupported";
+        case QSA_ERR_WORKSPACE: return "workspace too small";
+        case QSA_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* qsa_last_error(void) { return g_err; }
+
+qsa_status_t qsa_rope_apply(const uint16_t* x, int64_t x_seq_stride, int64_t x_tok_stride,
+                            uint16_t* y, int64_t y_seq_stride, int64_t y_tok_stride,
+                            int32_t batch, int32_t n_tokens, int32_t n_heads,
+                            const int32_t* pos0, double rope_theta, hipStream_t stream) {
+    TRY(check_batch(batch));
+    CHECK(x != nullptr && y != nullptr, "x or y is NULL");
+    CHECK(aligned16(x) && aligned16(y), "x and y must be 16-byte aligned");
+    CHECK(n_tokens >= 0, "n_tokens = %d is negative", n_tokens);
+    CHECK(n_heads >= 1 && n_heads <= 64, "n_heads = %d outside [1, 64]", n_heads);
+    CHECK(stride_ok(x_tok_stride) && stride_ok(y_tok_stride), "token strides must be positive multiples of 8");
+    CHECK(x_tok_stride >= int64_t{n_heads} * qsa::kD && y_tok_stride >= int64_t{n_heads} * qsa::kD,
+          "token stride smaller than n_heads * 256");
+    CHECK(batch == 1 || (stride_ok(x_seq_stride) && stride_ok(y_seq_stride)),
+          "sequence strides must be positive multiples of 8");
+    CHECK(isfinite(rope_theta) && rope_theta > 1.0, "rope_theta must be finite and > 1");
+    qsa::Positions p;
+    TRY(take_positions(pos0, batch, n_tokens, "pos0", p));
+    const bool in_place = (x == y);
+    CHECK(!in_place || (x_seq_stride == y_seq_stride && x_tok_stride == y_tok_stride),
+          "in-place rotation needs identical strides");
+    if (n_tokens == 0) return ok();
+    return hip_result(qsa::launch_rope(x, x_seq_stride, x_tok_stride, y, y_seq_stride, y_tok_stride,
+                                       batch, n_tokens, n_heads, p, rope_theta, in_place, stream),
+                      "rope_apply launch");
+}
+
+qsa_status_t qsa_compress_block_keys(const uint16_t* k_idx, int64_t k_idx_seq_stride,
+                                     int32_t batch, int32_t block_begin, int32_t block_end,
+                                     uint16_t* kbar, int64_t kbar_seq_stride, hipStream_t stream) {
+    TRY(check_batch(batch));
+    CHECK(k_idx != nullptr && kbar != nullptr, "k_idx or kbar is NULL");
+    CHECK(aligned16(k_idx) && aligned16(kbar), "k_idx and kbar must be 16-byte aligned");
+    CHECK(block_begin >= 0 && block_end >= block_begin, "bad block range [%d, %d)", block_begin, block_end);
+    CHECK(block_end < (1 << 28), "block_end = %d too large", block_end);
+    CHECK(batch == 1 || (stride_ok(k_idx_seq_stride) && stride_ok(kbar_seq_stride)),
+          "sequence strides must be positive multiples of 8");
+    CHECK(batch == 1 || k_idx_seq_stride >= int64_t{block_end} * qsa::kBlock * qsa::kDi,
+          "k_idx_seq_stride too small for block_end");
+    CHECK(batch == 1 || kbar_seq_stride >= int64_t{block_end} * qsa::kDi, "kbar_seq_stride too small for block_end");
+    if (block_end == block_begin) return ok();
+    return hip_result(qsa::launch_compress(k_idx, k_idx_seq_stride, batch, block_begin, block_end,
+                                           kbar, kbar_seq_stride, stream),
+                      "compress_block_keys launch");
+}
+
+static qsa_status_t check_scores_layout(const void* scores, int64_t ld, int64_t ss, int32_t batch,
+                                        int32_t tq, const qsa::Positions& p) {
+    CHECK(scores != nullptr, "scores is NULL");
+    CHECK(aligned16(scores), "scores must be 16-byte aligned");
+    CHECK(ld > 0 && ld % 4 == 0, "scores_ld = %lld must be a positive multiple of 4", (long long)ld);
+    int64_t need = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t o_last = (static_cast<int64_t>(p.p[b]) + tq - 1) / qsa::kBlock;
+        if (o_last > need) need = o_last;
+    }
+    CHECK(ld >= need, "scores_ld = %lld < %lld blocks seen by the last row", (long long)ld, (long long)need);
+    CHECK(batch == 1 || (ss % 4 == 0 && ss >= ld * tq), "scores_seq_stride must be a multiple of 4 and >= tq * ld");
+    return QSA_OK;
+}
+
+qsa_status_t qsa_index_scores(const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                              const uint16_t* kbar, int64_t kbar_seq_stride,
+                              const int32_t* q_pos0, int32_t batch, int32_t tq,
+                              float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                              hipStream_t stream) {
+    TRY(check_batch(batch));
+    CHECK(q_idx != nullptr && kbar != nullptr, "q_idx or kbar is NULL");
+    CHECK(aligned16(q_idx) && aligned16(kbar), "q_idx and kbar must be 16-byte aligned");
+    CHECK(tq >= 0, "tq = %d is negative", tq);
+    qsa::Positions p;
+    TRY(take_positions(q_pos0, batch, tq, "q_pos0", p));
+    if (tq == 0) return ok();
+    CHECK(batch == 1 || (stride_ok(q_idx_seq_stride) && q_idx_seq_stride >= int64_t{tq} * qsa::kHi * qsa::kDi),
+          "q_idx_seq_stride must be a multiple of 8 and >= tq * 4 * 128");
+    CHECK(batch == 1 || stride_ok(kbar_seq_stride), "kbar_seq_stride must be a positive multiple of 8");
+    TRY(check_scores_layout(scores, scores_ld, scores_seq_stride, batch, tq, p));
+    return hip_result(qsa::launch_index_scores(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch,
+                                               tq, scores, scores_ld, scores_seq_stride, stream),
+                      "index_scores launch");
+}
+
+size_t qsa_select_workspace_bytes(int32_t batch, int32_t tq, int32_t budget) {
+    (void)batch;
+    (void)tq;
+    (void)budget;
+    return 0;
+}
+
+qsa_status_t qsa_select_topk(const float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                             const int32_t* q_pos0, int32_t batch, int32_t tq, int32_t budget,
+                             int32_t* sel, int64_t sel_seq_stride,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    TRY(check_batch(batch));
+    CHECK(tq >= 0, "tq = %d is negative", tq);
+    CHECK(budget >= 1 && budget <= QSA_MAX_BUDGET, "budget = %d outside [1, %d]", budget, QSA_MAX_BUDGET);
+    CHECK(sel != nullptr, "sel is NULL");
+    CHECK((reinterpret_cast<uintptr_t>(sel) & 3u) == 0, "sel must be 4-byte aligned");
+    qsa::Positions p;
+    TRY(take_positions(q_pos0, batch, tq, "q_pos0", p));
+    if (tq == 0) return ok();
+    TRY(check_scores_layout(scores, scores_ld, scores_seq_stride, batch, tq, p));
+    CHECK(batch == 1 || sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
+    return hip_result(qsa::launch_select(scores, scores_ld, scores_seq_stride, p, batch, tq, budget, sel,
+                                         sel_seq_stride, stream),
+                      "select_topk launch");
+}
+
+static qsa_status_t check_attn_common(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                      const int32_t* sel, const uint16_t* out, int32_t budget,
+                                      float scale) {
+    CHECK(q != nullptr && k != nullptr && v != nullptr && sel != nullptr && out != nullptr,
+          "q, k_cache, v_cache, sel and out must be non-NULL");
+    CHECK(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out),
+          "q, k_cache, v_cache and out must be 16-byte aligned");
+    CHECK((reinterpret_cast<uintptr_t>(sel) & 3u) == 0, "sel must be 4-byte aligned");
+    CHECK(budget >= 1 && budget <= QSA_MAX_BUDGET, "budget = %d outside [1, %d]", budget, QSA_MAX_BUDGET);
+    CHECK(isfinite(scale) && scale > 0.f, "softmax_scale must be finite and > 0");
+    return QSA_OK;
+}
+
+qsa_status_t qsa_sparse_attn_prefill(const uint16_t* q, int64_t q_seq_stride,
+                                     const uint16_t* k_cache, const uint16_t* v_cache,
+                                     int64_t kv_seq_stride,
+                                     const int32_t* sel, int64_t sel_seq_stride,
+                                     const int32_t* q_pos0, int32_t batch, int32_t tq,
+                                     int32_t budget, float softmax_scale,
+                                     uint16_t* out, int64_t out_seq_stride, float* lse,
+                                     int64_t lse_seq_stride, hipStream_t stream) {
+    TRY(check_batch(batch));
+    TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
+    CHECK(tq >= 0, "tq = %d is negative", tq);
+    CHECK(lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) == 0, "lse must be 4-byte aligned");
+    qsa::Positions p;
+    TRY(take_positions(q_pos0, batch, tq, "q_pos0", p));
+    if (tq == 0) return ok();
+    if (batch > 1) {
+        int64_t max_len = 0;
+        for (int b = 0; b < batch; ++b) max_len = p.p[b] + tq > max_len ? p.p[b] + tq : max_len;
+        CHECK(stride_ok(q_seq_stride) && q_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD, "q_seq_stride too small");
+        CHECK(stride_ok(out_seq_stride) && out_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD, "out_seq_stride too small");
+        CHECK(stride_ok(kv_seq_stride) && kv_seq_stride >= max_len * qsa::kHkv * qsa::kD,
+              "kv_seq_stride smaller than the rows the queries reach");
+        CHECK(sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
+        CHECK(lse == nullptr || lse_seq_stride >= int64_t{tq} * qsa::kHq, "lse_seq_stride < tq * 24");
+    }
+    return hip_result(qsa::launch_attn_prefill(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
+                                               sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
+                                               out_seq_stride, lse, lse_seq_stride, stream),
+                      "sparse_attn_prefill launch");
+}
+
+size_t qsa_decode_workspace_bytes(int32_t batch, int32_t budget) {
+    if (batch < 1 || batch > QSA_MAX_BATCH || budget < 1 || budget > QSA_MAX_BUDGET) return 0;
+    return qsa::decode_workspace_bytes(batch, budget);
+}
+
+qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
+                                    const uint16_t* k_cache, const uint16_t* v_cache,
+                                    int64_t kv_seq_stride,
+                                    const int32_t* sel, int64_t sel_seq_stride,
+                                    const int32_t* q_pos, int32_t batch, int32_t budget,
+                                    float softmax_scale, uint16_t* out, int64_t out_seq_stride,
+                                    float* lse, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    TRY(check_batch(batch));
+    TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
+    CHECK(lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) == 0, "lse must be 4-byte aligned");
+    qsa::Positions p;
+    TRY(take_positions(q_pos, batch, 1, "q_pos", p));
+    if (batch > 1) {
+        int64_t max_len = 0;
+        for (int b = 0; b < batch; ++b) max_len = p.p[b] + 1 > max_len ? p.p[b] + 1 : max_len;
+        CHECK(stride_ok(q_seq_stride) && q_seq_stride >= qsa::kHq * qsa::kD, "q_seq_stride too small");
+        CHECK(stride_ok(out_seq_stride) && out_seq_stride >= qsa::kHq * qsa::kD, "out_seq_stride too small");
+        CHECK(stride_ok(kv_seq_stride) && kv_seq_stride >= max_len * qsa::kHkv * qsa::kD,
+              "kv_seq_stride smaller than the rows the queries reach");
+        CHECK(sel_seq_stride >= budget, "sel_seq_stride < budget");
+    }
+    const size_t need = qsa::decode_workspace_bytes(batch, budget);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(QSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
+                    workspace == nullptr ? size_t{0} : workspace_bytes);
+    CHECK(aligned16(workspace), "workspace must be 16-byte aligned");
+    return hip_result(qsa::launch_attn_decode(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
+                                              sel_seq_stride, p, batch, budget, softmax_scale, out,
+                                              out_seq_stride, lse, workspace, stream),
+                      "sparse_attn_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Internal declarations shared by the libqsa kernels and the C-ABI shim.
+// gfx950 (CDNA4) only: 64-lane wavefronts, bf16 matrix-core (MFMA) tiles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+namespace qsa {
+
+constexpr int kBlock = 4;     // tokens per micro-block
+constexpr int kHq = 24;       // attention query heads
+constexpr int kHkv = 2;       // attention KV heads
+constexpr int kGroup = kHq / kHkv;
+constexpr int kD = 256;       // attention head dim
+constexpr int kRot = 64;      // rotary slice
+constexpr int kHi = 4;        // indexer query heads
+constexpr int kDi = 128;      // indexer head dim
+
+// host positions travel by value inside the kernel arguments
+struct Positions {
+    int32_t p[QSA_MAX_BATCH];
+};
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bf16, round to nearest, ties to even (NaN -> quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// float64 -> bf16 in ONE rounding step (nearest, ties to even): round the
+// 52-bit mantissa to 7 bits on the integer pattern (add half of the 45
+// dropped bits' range minus one, plus the kept lsb, then truncate), so the
+// result is an exact float32 whose upper half is the bf16 pattern.  Finite
+// inputs in bf16's normal range (or zero) are assumed.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+    uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    u += 0x0fffffffffffull + ((u >> 45) & 1ull);
+    u &= ~0x1fffffffffffull;
+    float f = static_cast<float>(__longlong_as_double(static_cast<long long>(u)));
+    return static_cast<uint16_t>(__float_as_uint(f) >> 16);
+}
+
+// Monotone map of float32 onto uint32 for selection: larger score -> larger
+// key; -0.0 and +0.0 share a key; every NaN maps to 0, below all numbers.
+__device__ __forceinline__ uint32_t score_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if ((u & 0x7fffffffu) == 0) return 0x80000000u;
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace qsa
+
+// ---- launchers (one per kernel file); arguments are already validated ----
+namespace qsa {
+
+hipError_t launch_rope(const uint16_t* x, int64_t xs, int64_t xt, uint16_t* y, int64_t ys,
+                       int64_t yt, int batch, int n_tokens, int n_heads, const Positions& pos0,
+                       double theta, bool in_place, hipStream_t stream);
+
+hipError_t launch_compress(const uint16_t* k_idx, int64_t ks, int batch, int block_begin,
+                           int block_end, uint16_t* kbar, int64_t kbs, hipStream_t stream);
+
+hipError_t launch_index_scores(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
+                               int64_t kbs, const Positions& pos0, int batch, int tq,
+                               float* scores, int64_t ld, int64_t ss, hipStream_t stream);
+
+hipError_t launch_select(const float* scores, int64_t ld, int64_t ss, const Positions& pos0,
+                         int batch, int tq, int budget, int32_t* sel, int64_t sels,
+                         hipStream_t stream);
+
+hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
+                               const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
+                               const Positions& pos0, int batch, int tq, int budget, float scale,
+                               uint16_t* out, int64_t os, float* lse, int64_t lss,
+                               hipStream_t stream);
+
+size_t decode_workspace_bytes(int batch, int budget);
+hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
+                              const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
+                              const Positions& pos, int batch, int budget, float scale,
+                              uint16_t* out, int64_t os, float* lse, void* ws,
+                              hipStream_t stream);
+
+}  // namespace qsa

@@ -1,0 +1,312 @@
+"""Python binding of libqsa (one QSA layer on gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in include/qsa.h.  Tensors are torch CUDA (HIP) tensors used for
+device memory; the stream is torch's current stream unless one is passed.
+There is no fallback: if the library is not built, or a call is rejected,
+a QSAError is raised.
+
+Function names follow the C ABI: rope_apply, compress_block_keys,
+index_scores, select_topk, sparse_attn_prefill, sparse_attn_decode.  Two
+helpers chain them for a whole prefill chunk or decode step.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqsa.so")
+
+BLOCK, HQ, HKV, D, ROT, HI, DI = 4, 24, 2, 256, 64, 4, 128
+ROPE_THETA = 1.0e7
+MAX_BATCH = 256
+MAX_BUDGET = 2048
+
+_c_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "qsa_abi_version": (_i32, []),
+    "qsa_get_dims": (_i32, [_c_p]),
+    "qsa_status_string": (ctypes.c_char_p, [_i32]),
+    "qsa_last_error": (ctypes.c_char_p, []),
+    "qsa_rope_apply": (_i32, [_c_p, _i64, _i64, _c_p, _i64, _i64, _i32, _i32, _i32, _c_p,
+                              ctypes.c_double, _c_p]),
+    "qsa_compress_block_keys": (_i32, [_c_p, _i64, _i32, _i32, _i32, _c_p, _i64, _c_p]),
+    "qsa_index_scores": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _c_p, _i64, _i64, _c_p]),
+    "qsa_select_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "qsa_select_topk": (_i32, [_c_p, _i64, _i64, _c_p, _i32, _i32, _i32, _c_p, _i64, _c_p, _sz, _c_p]),
+    "qsa_sparse_attn_prefill": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32,
+                                       _i32, ctypes.c_float, _c_p, _i64, _c_p, _i64, _c_p]),
+    "qsa_decode_workspace_bytes": (_sz, [_i32, _i32]),
+    "qsa_sparse_attn_decode": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32,
+                                      ctypes.c_float, _c_p, _i64, _c_p, _c_p, _sz, _c_p]),
+}
+
+EXPORTED = tuple(_SIGNATURES)
+
+
+class QSAError(RuntimeError):
+    pass
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [(n, _i32) for n in ("block", "hq", "hkv", "d", "rot_dim", "hi", "di")]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqsa.so (built in-tree by block_sparse_long_12_amd.build)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise QSAError(f"{LIB_PATH} is not built: run `python -m block_sparse_long_12_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        if L.qsa_abi_version() != 1:
+            raise QSAError("libqsa ABI version mismatch")
+        _LIB = L
+    return _LIB
+
+
+def dims() -> dict:
+    d = _Dims()
+    _check(lib().qsa_get_dims(ctypes.byref(d)), "qsa_get_dims")
+    return {n: getattr(d, n) for n, _ in _Dims._fields_}
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        L = lib()
+        raise QSAError(f"{what}: {L.qsa_status_string(status).decode()} "
+                       f"({L.qsa_last_error().decode()})")
+
+
+def _stream(stream) -> _c_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _c_p(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> _c_p:
+    return _c_p(0 if t is None else t.data_ptr())
+
+
+def _positions(pos, batch: int):
+    vals = [int(x) for x in (pos.tolist() if hasattr(pos, "tolist") else pos)]
+    if len(vals) != batch:
+        raise QSAError(f"expected {batch} positions, got {len(vals)}")
+    return (ctypes.c_int32 * batch)(*vals)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, inner: tuple[int, ...]) -> None:
+    """t must be a device tensor of `dtype` whose dims after the first are
+    packed: shape[1:] contiguous (the C ABI takes one stride per sequence)."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise QSAError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise QSAError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape[-len(inner):]) != inner and inner:
+        raise QSAError(f"{name} trailing shape {tuple(t.shape)} does not end with {inner}")
+    expect = 1
+    for size, stride in zip(reversed(t.shape[1:]), reversed(t.stride()[1:])):
+        if size != 1 and stride != expect:
+            raise QSAError(f"{name} must be packed after its first dimension")
+        expect *= size
+
+
+# ------------------------------------------------------------------ steps
+
+def rope_apply(x: torch.Tensor, pos0, out: torch.Tensor | None = None,
+               theta: float = ROPE_THETA, stream=None) -> torch.Tensor:
+    """Rotate dims 0..63 of x [B, T, H, 256] (bf16) at positions pos0[b] + t.
+    out=None rotates in place; otherwise out [B, T, H, 256] receives the result."""
+    _need(x, "x", torch.bfloat16, (D,))
+    B, T, H = x.shape[0], x.shape[1], x.shape[2]
+    y = x if out is None else out
+    if out is not None:
+        _need(out, "out", torch.bfloat16, (D,))
+        if tuple(out.shape) != tuple(x.shape):
+            raise QSAError("out must have the shape of x")
+    _check(lib().qsa_rope_apply(_ptr(x), x.stride(0), x.stride(1), _ptr(y), y.stride(0), y.stride(1),
+                                B, T, H, _positions(pos0, B), float(theta), _stream(stream)),
+           "qsa_rope_apply")
+    return y
+
+
+def compress_block_keys(k_idx: torch.Tensor, block_begin: int, block_end: int,
+                        kbar: torch.Tensor, stream=None) -> torch.Tensor:
+    """kbar[b, j] = bf16 mean of k_idx[b, 4j .. 4j+3] for j in [block_begin, block_end)."""
+    _need(k_idx, "k_idx", torch.bfloat16, (DI,))
+    _need(kbar, "kbar", torch.bfloat16, (DI,))
+    B = k_idx.shape[0]
+    if kbar.shape[0] != B or k_idx.shape[1] < BLOCK * block_end or kbar.shape[1] < block_end:
+        raise QSAError("k_idx / kbar too short for block_end")
+    _check(lib().qsa_compress_block_keys(_ptr(k_idx), k_idx.stride(0), B, block_begin, block_end,
+                                         _ptr(kbar), kbar.stride(0), _stream(stream)),
+           "qsa_compress_block_keys")
+    return kbar
+
+
+def index_scores(q_idx: torch.Tensor, kbar: torch.Tensor, q_pos0, scores: torch.Tensor,
+                 stream=None) -> torch.Tensor:
+    """scores[b, t, j] = sum_h q_idx[b, t, h] . kbar[b, j] for j < (q_pos0[b] + t) // 4."""
+    _need(q_idx, "q_idx", torch.bfloat16, (HI, DI))
+    _need(kbar, "kbar", torch.bfloat16, (DI,))
+    _need(scores, "scores", torch.float32, ())
+    B, T = q_idx.shape[0], q_idx.shape[1]
+    pos = _positions(q_pos0, B)
+    need = max((int(pos[b]) + T - 1) // BLOCK for b in range(B)) if T else 0
+    if scores.shape[0] != B or scores.shape[1] < T or kbar.shape[0] != B or kbar.shape[1] < need:
+        raise QSAError("scores / kbar shapes do not cover the queries")
+    _check(lib().qsa_index_scores(_ptr(q_idx), q_idx.stride(0), _ptr(kbar), kbar.stride(0), pos, B, T,
+                                  _ptr(scores), scores.stride(1), scores.stride(0), _stream(stream)),
+           "qsa_index_scores")
+    return scores
+
+
+def select_topk(scores: torch.Tensor, q_pos0, budget: int, sel: torch.Tensor,
+                stream=None) -> torch.Tensor:
+    """sel[b, t] = ascending top-(budget-1) blocks by score plus the own block, -1 padded."""
+    _need(scores, "scores", torch.float32, ())
+    _need(sel, "sel", torch.int32, (budget,))
+    B, T = sel.shape[0], sel.shape[1]
+    if scores.shape[0] != B or scores.shape[1] < T:
+        raise QSAError("scores does not cover sel's rows")
+    L = lib()
+    ws_bytes = L.qsa_select_workspace_bytes(B, T, budget)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=sel.device) if ws_bytes else None
+    _check(L.qsa_select_topk(_ptr(scores), scores.stride(1), scores.stride(0), _positions(q_pos0, B), B, T,
+                             budget, _ptr(sel), sel.stride(0), _ptr(ws), ws_bytes, _stream(stream)),
+           "qsa_select_topk")
+    return sel
+
+
+def sparse_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        sel: torch.Tensor, q_pos0, out: torch.Tensor, lse: torch.Tensor | None = None,
+                        scale: float = 1.0 / math.sqrt(D), stream=None) -> torch.Tensor:
+    """out[b, t] = attention of q[b, t] (24 heads) over the tokens of sel[b, t]."""
+    _need(q, "q", torch.bfloat16, (HQ, D))
+    _need(k_cache, "k_cache", torch.bfloat16, (HKV, D))
+    _need(v_cache, "v_cache", torch.bfloat16, (HKV, D))
+    _need(out, "out", torch.bfloat16, (HQ, D))
+    B, T = q.shape[0], q.shape[1]
+    budget = sel.shape[-1]
+    _need(sel, "sel", torch.int32, (budget,))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (HQ,))
+        if tuple(lse.shape) != (B, T, HQ):
+            raise QSAError("lse must be [B, T, 24]")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise QSAError("k_cache and v_cache must share shape and strides")
+    pos = _positions(q_pos0, B)
+    if any(int(pos[b]) + T > k_cache.shape[1] for b in range(B)):
+        raise QSAError("KV caches shorter than the query positions")
+    _check(lib().qsa_sparse_attn_prefill(_ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0),
+                                         _ptr(sel), sel.stride(0), pos, B, T, budget, float(scale),
+                                         _ptr(out), out.stride(0), _ptr(lse),
+                                         0 if lse is None else lse.stride(0), _stream(stream)),
+           "qsa_sparse_attn_prefill")
+    return out
+
+
+def decode_workspace(batch: int, budget: int, device="cuda") -> torch.Tensor:
+    n = lib().qsa_decode_workspace_bytes(batch, budget)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       sel: torch.Tensor, q_pos, out: torch.Tensor, lse: torch.Tensor | None,
+                       workspace: torch.Tensor, scale: float = 1.0 / math.sqrt(D),
+                       stream=None) -> torch.Tensor:
+    """Decode form: q [B, 24, 256] at positions q_pos[b], sel [B, budget]."""
+    _need(q, "q", torch.bfloat16, (HQ, D))
+    _need(out, "out", torch.bfloat16, (HQ, D))
+    _need(k_cache, "k_cache", torch.bfloat16, (HKV, D))
+    _need(v_cache, "v_cache", torch.bfloat16, (HKV, D))
+    B, budget = sel.shape
+    _need(sel, "sel", torch.int32, (budget,))
+    if lse is not None and (not lse.is_contiguous() or tuple(lse.shape) != (B, HQ)):
+        raise QSAError("lse must be contiguous [B, 24]")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise QSAError("k_cache and v_cache must share shape and strides")
+    pos = _positions(q_pos, B)
+    if any(int(pos[b]) + 1 > k_cache.shape[1] for b in range(B)):
+        raise QSAError("KV caches shorter than the query positions")
+    _check(lib().qsa_sparse_attn_decode(_ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0),
+                                        _ptr(sel), sel.stride(0), pos, B, budget, float(scale), _ptr(out),
+                                        out.stride(0), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                        _stream(stream)),
+           "qsa_sparse_attn_decode")
+    return out
+
+
+# ------------------------------------------------------------------ chained steps
+
+class PrefillBuffers:
+    """Device buffers for one prefill layer call: scores for one query chunk
+    and the per-token selection."""
+
+    def __init__(self, batch: int, tq: int, ctx: int, budget: int, chunk: int | None, device="cuda"):
+        self.chunk = min(tq, chunk or tq)
+        ld = max(4, ((ctx + tq - 1) // BLOCK + 3) // 4 * 4)
+        self.scores = torch.empty((batch, self.chunk, ld), dtype=torch.float32, device=device)
+        self.sel = torch.empty((batch, tq, budget), dtype=torch.int32, device=device)
+
+
+def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0: int, budget: int,
+                  out, lse, bufs: PrefillBuffers, q_rot, stream=None):
+    """One QSA layer over tq new tokens of every sequence, all at q_pos0.
+
+    q_raw [B, tq, 24, 256] and k_new_raw [B, tq, 2, 256] are unrotated; the
+    rotated K rows are written into k_cache[:, q_pos0 : q_pos0 + tq] (V rows
+    are expected in v_cache already, k_idx rows in k_idx).  Steps: rotary
+    (Q -> q_rot, K -> cache), compress the blocks the chunk completes, then per
+    query chunk index scores -> selection, then attention.
+    """
+    B, tq = q_raw.shape[0], q_raw.shape[1]
+    pos = [q_pos0] * B
+    rope_apply(q_raw, pos, out=q_rot, stream=stream)
+    rope_apply(k_new_raw, pos, out=k_cache[:, q_pos0:q_pos0 + tq], stream=stream)
+    b0, b1 = q_pos0 // BLOCK, (q_pos0 + tq) // BLOCK
+    compress_block_keys(k_idx, b0, b1, kbar, stream=stream)
+    for c0 in range(0, tq, bufs.chunk):
+        c1 = min(tq, c0 + bufs.chunk)
+        cpos = [q_pos0 + c0] * B
+        index_scores(q_idx[:, c0:c1], kbar, cpos, bufs.scores, stream=stream)
+        select_topk(bufs.scores, cpos, budget, bufs.sel[:, c0:c1], stream=stream)
+        sparse_attn_prefill(q_rot[:, c0:c1], k_cache, v_cache, bufs.sel[:, c0:c1], cpos, out[:, c0:c1],
+                            None if lse is None else lse[:, c0:c1], stream=stream)
+    return out
+
+
+def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos: int, budget: int,
+                out, lse, scores, sel, workspace, q_rot, stream=None):
+    """One decode step for B sequences, each with one new token at position pos.
+
+    q_raw [B, 1, 24, 256] and k_new_raw [B, 1, 2, 256] are unrotated; the
+    rotated K row goes to k_cache[:, pos] (the V and k_idx rows are expected
+    in place); kbar must hold blocks 0 .. pos // 4 - 1.  When the new token
+    completes its block, that block's key is compressed too.
+    """
+    B = q_raw.shape[0]
+    p = [pos] * B
+    rope_apply(q_raw, p, out=q_rot, stream=stream)
+    rope_apply(k_new_raw, p, out=k_cache[:, pos:pos + 1], stream=stream)
+    if (pos + 1) % BLOCK == 0:
+        compress_block_keys(k_idx, pos // BLOCK, pos // BLOCK + 1, kbar, stream=stream)
+    index_scores(q_idx, kbar, p, scores, stream=stream)
+    select_topk(scores, p, budget, sel, stream=stream)
+    sparse_attn_decode(q_rot[:, 0], k_cache, v_cache, sel[:, 0], p, out, lse, workspace, stream=stream)
+    return out

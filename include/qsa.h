@@ -1,0 +1,175 @@
+/*
+ * qsa.h -- C ABI of libqsa: one layer of Qwen Sparse Attention (QSA) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages state it (Qwen3.8-Flash-Next blog, section
+ * "Attention: GDN + QSA"): a lightweight indexer aggregates the sequence into
+ * micro-blocks, estimates importance per block, selects the most relevant
+ * blocks, and attention runs over the selected regions only.  Shapes (model
+ * card, "Model Overview" -> "Qwen Sparse Attention"): 24 query heads, 2 KV
+ * heads, head dim 256, rotary dim 64, indexer = MQA with 4 query heads and 1
+ * shared key head of dim 128, budget 512 blocks or 2048 tokens, hence 4 tokens
+ * per micro-block.  The calls below are those steps, in that order:
+ *
+ *   qsa_rope_apply           rotary embedding of Q / K rows     (step 0)
+ *   qsa_compress_block_keys  indexer keys -> block keys          (step 1)
+ *   qsa_index_scores         block scores of the MQA indexer     (step 2)
+ *   qsa_select_topk          per-token top-(budget-1) + own block (step 3)
+ *   qsa_sparse_attn_prefill  attention over the selected tokens  (step 4)
+ *   qsa_sparse_attn_decode   the same for one new token per sequence
+ *
+ * Conventions shared by every call
+ *   - bf16 tensors are passed as uint16_t bit patterns; every tensor pointer
+ *     is caller-owned DEVICE memory, 16-byte aligned; strides are in
+ *     elements and must be multiples of 8 (16 bytes).
+ *   - Layouts are token-major with the last dimension contiguous:
+ *       Q       [B][T][24][256]      K, V caches [B][L][2][256]
+ *       q_idx   [B][T][4][128]       k_idx       [B][L][128]
+ *       kbar    [B][L/4][128]        scores      [B][T][ld] float
+ *       sel     [B][T][budget] int32
+ *     "seq_stride" is the distance between sequences b and b+1.
+ *   - Positions are HOST int32 arrays of length `batch` (at most
+ *     QSA_MAX_BATCH), so validation and grid sizing never wait on the GPU.
+ *     Query row i of sequence b sits at absolute position q_pos0[b] + i; its
+ *     own block is o = position / 4.
+ *   - Every call is asynchronous on `stream`, never synchronises, never
+ *     allocates, and launches nothing when validation fails.  Errors come
+ *     back as a status; qsa_last_error() gives the message (thread-local).
+ *   - Calls on one stream run in order; calls on different streams that
+ *     share output buffers race.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+#define QSA_MAX_BATCH 256
+#define QSA_MAX_BUDGET 2048
+
+typedef enum {
+    QSA_OK = 0,
+    QSA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or stride */
+    QSA_ERR_UNSUPPORTED = 2,      /* legal but outside what this build handles  */
+    QSA_ERR_WORKSPACE = 3,        /* workspace missing or too small             */
+    QSA_ERR_HIP = 4               /* a HIP runtime call or launch failed        */
+} qsa_status_t;
+
+/* Fixed head geometry (model card "Model Overview"): block 4 tokens, 24 Q
+ * heads, 2 KV heads, head dim 256, rotary dim 64, 4 indexer heads of dim 128. */
+typedef struct {
+    int32_t block, hq, hkv, d, rot_dim, hi, di;
+} qsa_dims_t;
+
+int32_t      qsa_abi_version(void);
+qsa_status_t qsa_get_dims(qsa_dims_t* out);
+const char*  qsa_status_string(qsa_status_t s);
+const char*  qsa_last_error(void);
+
+/*
+ * Step 0 -- rotary embedding (model card, "Processing Ultra-Long Texts",
+ * rope_parameters: rope_theta 1e7, partial_rotary_factor 0.25, i.e. the first
+ * 64 of 256 dims; mRoPE sections [11, 11, 10] reduce to 1-D rotary for text).
+ * For every row (b, i) and head h of x [B][n_tokens][n_heads][256]:
+ * pair (d, d + 32), d < 32, is turned by angle p * theta^(-d/32) with
+ * p = pos0[b] + i:  (a, c) -> (a cos - c sin, c cos + a sin).  Angles, sines
+ * and the rotation are evaluated in float64, the result rounded once to bf16;
+ * dims 64..255 are copied unchanged.  y may equal x (same strides) for an
+ * in-place update; otherwise x and y must not overlap.
+ */
+qsa_status_t qsa_rope_apply(const uint16_t* x, int64_t x_seq_stride, int64_t x_tok_stride,
+                            uint16_t* y, int64_t y_seq_stride, int64_t y_tok_stride,
+                            int32_t batch, int32_t n_tokens, int32_t n_heads,
+                            const int32_t* pos0, double rope_theta, hipStream_t stream);
+
+/*
+ * Step 1 -- block keys (blog, "Attention: GDN + QSA": aggregate into
+ * micro-blocks).  For blocks j in [block_begin, block_end) of every sequence:
+ *   kbar[b][j][d] = bf16( ((k[4j][d] + k[4j+1][d]) + k[4j+2][d]) + k[4j+3][d]) * 0.25 )
+ * with the additions in float32 in token order and round-to-nearest-even.
+ * k_idx [B][>= 4*block_end][128], kbar [B][>= block_end][128].
+ */
+qsa_status_t qsa_compress_block_keys(const uint16_t* k_idx, int64_t k_idx_seq_stride,
+                                     int32_t batch, int32_t block_begin, int32_t block_end,
+                                     uint16_t* kbar, int64_t kbar_seq_stride, hipStream_t stream);
+
+/*
+ * Step 2 -- block scores of the MQA indexer (model card: 4 query heads share
+ * 1 key head of dim 128).  For query row i of sequence b at position
+ * p = q_pos0[b] + i and every complete block j < p / 4:
+ *   scores[b][i][j] = sum_h sum_d q_idx[b][i][h][d] * kbar[b][j][d]
+ * with exact bf16 products accumulated in float32 (matrix-core tiles).
+ * Entries j >= p / 4 of a row are left unspecified (not written, or written
+ * with values the selection never reads).  Needs scores_ld >= (q_pos0[b] +
+ * tq - 1) / 4 for all b, scores_ld % 4 == 0, and kbar holding those blocks.
+ */
+qsa_status_t qsa_index_scores(const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                              const uint16_t* kbar, int64_t kbar_seq_stride,
+                              const int32_t* q_pos0, int32_t batch, int32_t tq,
+                              float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                              hipStream_t stream);
+
+/*
+ * Step 3 -- block selection (blog: select the most relevant regions; model
+ * card: budget 512 blocks).  For query row i at position p, own block
+ * o = p / 4: keep min(budget - 1, o) of the candidates j < o ordered by
+ * (score descending, j ascending), with -0.0 equal to +0.0 and NaN below
+ * every number, add o, and write the set ascending into sel[b][i][0..budget),
+ * padded with -1.  The selection is exact: it depends only on the float32
+ * score bits.  workspace may be NULL when qsa_select_workspace_bytes() is 0.
+ */
+size_t       qsa_select_workspace_bytes(int32_t batch, int32_t tq, int32_t budget);
+qsa_status_t qsa_select_topk(const float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                             const int32_t* q_pos0, int32_t batch, int32_t tq, int32_t budget,
+                             int32_t* sel, int64_t sel_seq_stride,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Step 4 -- sparse grouped-query attention (model card: 24 Q heads, 2 KV
+ * heads, dim 256).  For query row i at position p and head h, with KV head
+ * g = h / 12: softmax over the tokens n of the selected blocks (4 per block,
+ * n <= p) of scale * q[h] . k[n][g], times v[n][g]; float32 accumulation,
+ * online softmax.  out [B][tq][24][256] bf16; lse [B][tq][24] float (natural
+ * log of the softmax denominator, including the scale; sequence stride
+ * lse_seq_stride elements), may be NULL.
+ * k_cache / v_cache rows must hold positions 0 .. q_pos0[b] + tq - 1; q and K
+ * are expected already rotated.  sel entries outside [0, p/4] are skipped.
+ */
+qsa_status_t qsa_sparse_attn_prefill(const uint16_t* q, int64_t q_seq_stride,
+                                     const uint16_t* k_cache, const uint16_t* v_cache,
+                                     int64_t kv_seq_stride,
+                                     const int32_t* sel, int64_t sel_seq_stride,
+                                     const int32_t* q_pos0, int32_t batch, int32_t tq,
+                                     int32_t budget, float softmax_scale,
+                                     uint16_t* out, int64_t out_seq_stride, float* lse,
+                                     int64_t lse_seq_stride, hipStream_t stream);
+
+/*
+ * Step 4, decode form: one query token per sequence at position q_pos[b]
+ * (q [B][24][256], sel [B][budget], out [B][24][256], lse [B][24]).  The
+ * selected blocks are split over many workgroups whose partial softmax
+ * states (max, sum, weighted V) go to `workspace` and are merged by a final
+ * reduction.  workspace must hold qsa_decode_workspace_bytes(batch, budget).
+ */
+size_t       qsa_decode_workspace_bytes(int32_t batch, int32_t budget);
+qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
+                                    const uint16_t* k_cache, const uint16_t* v_cache,
+                                    int64_t kv_seq_stride,
+                                    const int32_t* sel, int64_t sel_seq_stride,
+                                    const int32_t* q_pos, int32_t batch, int32_t budget,
+                                    float softmax_scale, uint16_t* out, int64_t out_seq_stride,
+                                    float* lse, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,172 @@
+"""Shared helpers of the GPU parity tests: device set-up of a workload through
+the HIP path, and the comparisons against the CPU oracle."""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+from block_sparse_long_12_amd import inputs as I
+from block_sparse_long_12_amd import qsa
+from oracle import qsa_oracle as O
+
+# tolerances of the attention output (bf16 in, float32 accumulate)
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+LSE_ABS = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return O.bits(t.detach().cpu())
+
+
+def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """|a - b| in bf16 units in the last place (sign-magnitude patterns)."""
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def score_bound(q_idx_bits: np.ndarray, kbar_bits: np.ndarray) -> np.ndarray:
+    """Worst-case float32 accumulation error of sum_{h,d} q[h,d] k[j,d] for
+    512 exact products: 2^-15 * sum |q k| (n * 2^-24 with n = 512)."""
+    q = np.abs(O.bf16_to_f64(q_idx_bits))           # [Hi, Di]
+    k = np.abs(O.bf16_to_f64(kbar_bits))            # [n, Di]
+    return (k @ q.sum(axis=0)) * 2.0 ** -15 + 1e-30
+
+
+class DevicePrefill:
+    """A prefill workload on the device, run through the HIP path."""
+
+    def __init__(self, x: I.Inputs):
+        wl = x.workload
+        self.x, self.wl = x, wl
+        B, L, ctx, T = wl.batch, wl.length, wl.ctx, wl.tq
+        dev = "cuda"
+        self.q_raw = x.q.to(dev)
+        self.k_new = x.k[:, ctx:].contiguous().to(dev)
+        self.q_idx = x.q_idx.to(dev)
+        self.k_idx = x.k_idx.to(dev)
+        self.v_cache = x.v.to(dev)
+        self.k_cache = x.k.to(dev)
+        if ctx > 0:     # the cached prefix is stored rotated
+            qsa.rope_apply(self.k_cache[:, :ctx], [0] * B)
+        self.kbar = torch.zeros((B, max(1, L // 4), 128), dtype=torch.bfloat16, device=dev)
+        if ctx // 4 > 0:
+            qsa.compress_block_keys(self.k_idx, 0, ctx // 4, self.kbar)
+        self.bufs = qsa.PrefillBuffers(B, T, ctx, wl.budget, wl.chunk)
+        self.out = torch.empty((B, T, 24, 256), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, T, 24), dtype=torch.float32, device=dev)
+        self.q_rot = torch.empty_like(self.q_raw)
+
+    def run(self):
+        qsa.prefill_layer(self.q_raw, self.k_new, self.q_idx, self.k_idx, self.k_cache, self.v_cache,
+                          self.kbar, self.wl.ctx, self.wl.budget, self.out, self.lse, self.bufs, self.q_rot)
+        torch.cuda.synchronize()
+
+
+class DeviceDecode:
+    """A decode workload on the device: caches prefilled, one new token."""
+
+    def __init__(self, x: I.Inputs):
+        wl = x.workload
+        self.x, self.wl = x, wl
+        B, ctx = wl.batch, wl.ctx
+        dev = "cuda"
+        self.pos = ctx
+        self.k_cache = x.k.to(dev)
+        qsa.rope_apply(self.k_cache[:, :ctx], [0] * B)
+        self.v_cache = x.v.to(dev)
+        self.k_idx = x.k_idx.to(dev)
+        self.kbar = torch.zeros((B, max(1, (ctx + 1) // 4), 128), dtype=torch.bfloat16, device=dev)
+        if ctx // 4 > 0:
+            qsa.compress_block_keys(self.k_idx, 0, ctx // 4, self.kbar)
+        self.q_raw = x.q.to(dev)                     # [B, 1, 24, 256]
+        self.k_new = x.k[:, ctx:ctx + 1].contiguous().to(dev)
+        self.q_idx = x.q_idx.to(dev)                 # [B, 1, 4, 128]
+        ld = max(4, (ctx // 4 + 3) // 4 * 4)
+        self.scores = torch.empty((B, 1, ld), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((B, 1, wl.budget), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, 24, 256), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, 24), dtype=torch.float32, device=dev)
+        self.ws = qsa.decode_workspace(B, wl.budget)
+        self.q_rot = torch.empty_like(self.q_raw)
+
+    def run(self):
+        qsa.decode_step(self.q_raw, self.k_new, self.q_idx, self.k_idx, self.k_cache, self.v_cache, self.kbar,
+                        self.pos, self.wl.budget, self.out, self.lse, self.scores, self.sel, self.ws, self.q_rot)
+        torch.cuda.synchronize()
+
+
+def oracle_layer(x: I.Inputs) -> O.OracleLayer:
+    B = O.bits
+    return O.OracleLayer(B(x.q), B(x.q_idx), B(x.k), B(x.v), B(x.k_idx), x.q_pos0, x.workload.budget)
+
+
+def compare_rows(layer: O.OracleLayer, x: I.Inputs, rows, gpu_scores, gpu_sel, gpu_out, gpu_lse):
+    """The end-to-end protocol on query rows [(b, t)]:
+      (i)   GPU scores within the float32 accumulation bound of the oracle's;
+      (ii)  where the selected sets differ, every swapped pair is a near tie
+            (oracle scores within the two bounds);
+      (iii) the GPU output equals the oracle's attention recomputed with the
+            GPU's own selection (max-abs / mean-abs tolerances);
+      (iv)  every planted needle of the row is selected.
+    gpu_scores(b, t) -> float32 [o], gpu_sel(b, t) -> int32 [budget],
+    gpu_out(b, t) -> float [24, 256], gpu_lse(b, t) -> float [24]."""
+    ref = layer.rows(rows)
+    needles = {}
+    for b, t, j in x.needles:
+        needles.setdefault((int(b), int(t)), []).append(int(j))
+    swaps = 0
+    override = {}
+    worst_score = 0.0
+    for (b, t), r in zip(rows, ref):
+        o = t // 4
+        sg = gpu_scores(b, t) if gpu_scores is not None else None
+        kb = layer.kbar_bits(b)[:o]
+        qb = layer.q_idx[b, t - layer.q_pos0[b]]
+        bound = score_bound(qb, kb) if o > 0 else np.zeros(0)
+        if sg is not None and o > 0:
+            err = np.abs(sg.astype(np.float64) - r.scores.astype(np.float64))
+            assert np.all(err <= bound), (b, t, float(err.max()), float(bound[np.argmax(err - bound)]))
+            worst_score = max(worst_score, float((err / bound).max()))
+        sgpu = gpu_sel(b, t)
+        A = set(int(v) for v in sgpu if v >= 0)
+        Bs = set(int(v) for v in r.sel if v >= 0)
+        assert len(A) == len(Bs) and o in A, (b, t)
+        assert sorted(A) == [int(v) for v in sgpu[:len(A)]] and np.all(sgpu[len(A):] == -1), (b, t)
+        if A != Bs:
+            swaps += 1
+            for a in A - Bs:
+                for c in Bs - A:
+                    gap = abs(float(r.scores[a]) - float(r.scores[c]))
+                    assert gap <= bound[a] + bound[c], (b, t, a, c, gap)
+        for j in needles.get((b, t), []):
+            assert j in A, (b, t, j)
+        override[(b, t)] = sgpu
+    again = layer.rows(rows, sel_override=override)
+    max_abs = 0.0
+    sum_abs = 0.0
+    n = 0
+    lse_abs = 0.0
+    for (b, t), r in zip(rows, again):
+        go = gpu_out(b, t).astype(np.float64)
+        d = np.abs(go - r.out)
+        max_abs = max(max_abs, float(d.max()))
+        sum_abs += float(d.sum())
+        n += d.size
+        lse_abs = max(lse_abs, float(np.abs(gpu_lse(b, t).astype(np.float64) - r.lse).max()))
+    mean_abs = sum_abs / max(1, n)
+    say(f"  rows={len(rows)} near-tie rows={swaps} worst score err/bound={worst_score:.3g} "
+        f"max_abs={max_abs:.3g} mean_abs={mean_abs:.3g} lse_abs={lse_abs:.3g}")
+    assert max_abs <= MAX_ABS and mean_abs <= MEAN_ABS and lse_abs <= LSE_ABS
+    return swaps

@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments before any launch (validation makes no HIP call,
+so fake device addresses are never touched)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_long_12_amd import qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+FAKE = 0x10000          # aligned fake device address: validation must fail before any use
+NULL = 0
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qsa.LIB_PATH):
+        from block_sparse_long_12_amd import build
+        build.build()
+    return qsa.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_steps():
+    names = _declared()
+    for n in ("qsa_rope_apply", "qsa_compress_block_keys", "qsa_index_scores", "qsa_select_topk",
+              "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", qsa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (qsa_[a-z0-9_]+)$", out, flags=re.M))
+    for name in _declared():
+        assert name in exported, name
+        assert name in qsa.EXPORTED, name
+        assert hasattr(L, name)
+
+
+def test_dims_and_strings(L):
+    assert qsa.dims() == dict(block=4, hq=24, hkv=2, d=256, rot_dim=64, hi=4, di=128)
+    assert L.qsa_abi_version() == 1
+    for s in range(5):
+        assert L.qsa_status_string(s)
+
+
+def _pos(*v):
+    return (ctypes.c_int32 * len(v))(*v)
+
+
+def _err(L):
+    return L.qsa_last_error().decode()
+
+
+def test_rope_validation(L):
+    p = _pos(0)
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 0, 1, 1, p, 1e7, None) == INVALID
+    assert "batch" in _err(L)
+    assert L.qsa_rope_apply(NULL, 0, 256, FAKE, 0, 256, 1, 1, 1, p, 1e7, None) == INVALID
+    assert L.qsa_rope_apply(FAKE + 2, 0, 256, FAKE, 0, 256, 1, 1, 1, p, 1e7, None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 255, FAKE, 0, 256, 1, 1, 1, p, 1e7, None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 2, p, 1e7, None) == INVALID   # stride < heads*256
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 1, p, 0.5, None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 1, _pos(-3), 1e7, None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 1, None, 1e7, None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 512, 1, 1, 1, p, 1e7, None) == INVALID   # in place, strides differ
+
+
+def test_compress_validation(L):
+    assert L.qsa_compress_block_keys(FAKE, 0, 1, 5, 4, FAKE, 0, None) == INVALID
+    assert L.qsa_compress_block_keys(FAKE, 0, 1, -1, 4, FAKE, 0, None) == INVALID
+    assert L.qsa_compress_block_keys(NULL, 0, 1, 0, 4, FAKE, 0, None) == INVALID
+    assert L.qsa_compress_block_keys(FAKE, 8, 2, 0, 4, FAKE, 512, None) == INVALID   # k stride < 4*4*128
+    assert L.qsa_compress_block_keys(FAKE, 0, 1, 3, 3, FAKE, 0, None) == OK          # empty range: no launch
+
+
+def test_index_scores_validation(L):
+    p = _pos(100)
+    # ld smaller than the blocks the last row sees ((100 + 10 - 1) // 4 = 27)
+    assert L.qsa_index_scores(FAKE, 0, FAKE, 0, p, 1, 10, FAKE, 24, 0, None) == INVALID
+    assert "scores_ld" in _err(L)
+    assert L.qsa_index_scores(FAKE, 0, FAKE, 0, p, 1, 10, FAKE, 30, 0, None) == INVALID    # ld % 4
+    assert L.qsa_index_scores(FAKE, 0, FAKE, 0, p, 1, 10, FAKE + 4, 28, 0, None) == INVALID
+    assert L.qsa_index_scores(FAKE, 0, FAKE, 0, p, 1, -1, FAKE, 28, 0, None) == INVALID
+    assert L.qsa_index_scores(FAKE, 0, FAKE, 0, p, 1, 0, FAKE, 28, 0, None) == OK          # nothing to do
+
+
+def test_select_validation(L):
+    p = _pos(100)
+    assert L.qsa_select_topk(FAKE, 28, 0, p, 1, 10, 0, FAKE, 0, None, 0, None) == INVALID
+    assert "budget" in _err(L)
+    assert L.qsa_select_topk(FAKE, 28, 0, p, 1, 10, 4096, FAKE, 0, None, 0, None) == INVALID
+    assert L.qsa_select_topk(FAKE, 28, 0, p, 1, 10, 8, NULL, 0, None, 0, None) == INVALID
+    assert L.qsa_select_topk(FAKE, 24, 0, p, 1, 10, 8, FAKE, 0, None, 0, None) == INVALID
+    assert L.qsa_select_topk(FAKE, 28, 0, _pos(100, 100), 2, 10, 8, FAKE, 80, None, 0, None) == INVALID  # seq stride 0
+    assert L.qsa_select_workspace_bytes(1, 8192, 512) == 0
+
+
+def test_attention_validation(L):
+    p = _pos(40)
+    # only invalid combinations are exercised: a valid one would launch
+    assert L.qsa_sparse_attn_prefill(FAKE, 0, FAKE, FAKE, 0, FAKE, 0, p, 1, 4, 0, 0.0625, FAKE, 0, None, 0, None) == INVALID
+    assert L.qsa_sparse_attn_prefill(FAKE, 0, FAKE, FAKE, 0, FAKE, 0, p, 1, 4, 16, 0.0, FAKE, 0, None, 0, None) == INVALID
+    assert L.qsa_sparse_attn_prefill(FAKE, 0, NULL, FAKE, 0, FAKE, 0, p, 1, 4, 16, 0.0625, FAKE, 0, None, 0, None) == INVALID
+    assert L.qsa_sparse_attn_prefill(FAKE, 0, FAKE, FAKE, 0, FAKE + 2, 0, p, 1, 4, 16, 0.0625, FAKE, 0, None, 0, None) == INVALID
+
+
+def test_decode_workspace(L):
+    need = L.qsa_decode_workspace_bytes(4, 512)
+    assert need > 0
+    assert L.qsa_decode_workspace_bytes(0, 512) == 0
+    p = _pos(1048576, 1048576, 1048576, 1048576)
+    st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048577 * 512, FAKE, 512, p, 4, 512, 0.0625, FAKE,
+                                  6144, FAKE, FAKE, need - 16, None)
+    assert st == WORKSPACE, _err(L)
+    st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048577 * 512, FAKE, 512, p, 4, 512, 0.0625, FAKE,
+                                  6144, FAKE, NULL, need, None)
+    assert st == WORKSPACE
+    # KV sequence stride too small for position 1048576
+    st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048576 * 512, FAKE, 512, p, 4, 512, 0.0625, FAKE,
+                                  6144, FAKE, FAKE, need, None)
+    assert st == INVALID
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros((1, 4, 2, 256), dtype=torch.bfloat16)
+    with pytest.raises(qsa.QSAError):
+        qsa.rope_apply(x, [0])

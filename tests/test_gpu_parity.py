@@ -1,0 +1,309 @@
+"""HIP path against the CPU oracle, step by step and end to end.
+
+Per-step tests feed both sides identical inputs (oracle-made where a step
+consumes an earlier step's result); end-to-end tests run every step on the
+GPU from the raw seeded inputs and compare with the near-tie protocol of
+tests/gpu_common.compare_rows.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_12_amd import inputs as I
+from block_sparse_long_12_amd import qsa
+from oracle import qsa_oracle as O
+from tests.gpu_common import (MAX_ABS, MEAN_ABS, LSE_ABS, DeviceDecode, DevicePrefill, bf16_ulp_diff,
+                              bits, compare_rows, oracle_layer, say, score_bound)
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_bf16(shape, seed, sigma=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * sigma).to(torch.bfloat16)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    qsa.lib()
+
+
+# ------------------------------------------------------------------ step 0
+
+@pytest.mark.parametrize("heads", [24, 2])
+def test_rope_matches_oracle(heads):
+    say(f"rope heads={heads}")
+    x = _rand_bf16((2, 37, heads, 256), 1 + heads)
+    pos0 = [0, 1048000]
+    xd = x.cuda()
+    yd = torch.empty_like(xd)
+    qsa.rope_apply(xd, pos0, out=yd)
+    got = bits(yd)
+    ref = np.stack([O.rope_rotate(bits(x[b]), np.arange(37) + pos0[b]) for b in range(2)])
+    assert np.array_equal(got[..., 64:], bits(x)[..., 64:])
+    ulp = bf16_ulp_diff(got, ref)
+    assert ulp.max() <= 1 and np.mean(ulp == 0) >= 0.9999, (ulp.max(), np.mean(ulp == 0))
+    # in place equals out of place
+    qsa.rope_apply(xd, pos0)
+    assert np.array_equal(bits(xd), got)
+
+
+# ------------------------------------------------------------------ step 1
+
+def test_compress_is_bit_exact():
+    say("compress")
+    k = _rand_bf16((3, 4 * 701 + 2, 128), 11, sigma=1 / math.sqrt(128))
+    # the hand-derived cases in the first blocks of sequence 0
+    import json, os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "compress_cases.json")))["cases"]
+    for ci, c in enumerate(cases):
+        for r, h in enumerate(c["keys"]):
+            k[0, 4 * ci + r, :] = float.fromhex(h)
+    kd = k.cuda()
+    kbar = torch.zeros((3, 701, 128), dtype=torch.bfloat16, device="cuda")
+    qsa.compress_block_keys(kd, 0, 701, kbar)
+    got = bits(kbar)
+    for b in range(3):
+        assert np.array_equal(got[b], O.compress_block_keys(bits(k[b]), 0, 701))
+    for ci, c in enumerate(cases):
+        assert np.all(got[0, ci] == int(c["bits"], 16)), c
+    part = torch.zeros_like(kbar)
+    qsa.compress_block_keys(kd, 100, 333, part)
+    pg = bits(part)
+    assert np.array_equal(pg[:, 100:333], got[:, 100:333]) and not pg[:, :100].any() and not pg[:, 333:].any()
+
+
+# ------------------------------------------------------------------ step 2
+
+INDEX_CASES = [
+    ("prefill ragged", 1, [0], 77),
+    ("prefill batched offsets", 2, [1003, 50], 70),
+    ("decode long", 3, [70001, 4096, 9999], 1),
+    ("prefill one tile", 1, [4 * 64 + 1], 16),
+]
+
+
+def _index_case(B, pos0, tq, seed):
+    q = _rand_bf16((B, tq, 4, 128), seed, sigma=1 / math.sqrt(128))
+    nblk = max((p + tq - 1) // 4 for p in pos0)
+    kbar = _rand_bf16((B, max(1, nblk), 128), seed + 1, sigma=1 / math.sqrt(512))
+    ld = max(4, (nblk + 3) // 4 * 4)
+    scores = torch.full((B, tq, ld), float("nan"), dtype=torch.float32, device="cuda")
+    qsa.index_scores(q.cuda(), kbar.cuda(), pos0, scores)
+    return q, kbar, scores.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,B,pos0,tq", INDEX_CASES, ids=[c[0] for c in INDEX_CASES])
+def test_index_scores_within_float32_bound(name, B, pos0, tq):
+    say(f"index_scores {name}")
+    q, kbar, got = _index_case(B, pos0, tq, 21 + tq)
+    exact = 0
+    total = 0
+    for b in range(B):
+        kb = bits(kbar[b])
+        ref = O.index_scores(bits(q[b]), O.bf16_to_f64(kb))
+        for i in range(tq):
+            o = (pos0[b] + i) // 4
+            if o == 0:
+                continue
+            bound = score_bound(bits(q[b, i]), kb[:o])
+            err = np.abs(got[b, i, :o].astype(np.float64) - ref[i, :o].astype(np.float64))
+            assert np.all(err <= bound), (b, i, err.max())
+            exact += int(np.sum(got[b, i, :o] == ref[i, :o]))
+            total += o
+    say(f"  exactly rounded: {exact}/{total}")
+
+
+def test_index_scores_do_not_depend_on_launch_shape():
+    say("index_scores launch-shape independence")
+    B, pos0, tq = 1, [2000], 64
+    q, kbar, full = _index_case(B, pos0, tq, 5)
+    sub = torch.full((1, 20, full.shape[2]), float("nan"), dtype=torch.float32, device="cuda")
+    qsa.index_scores(q[:, 10:30].contiguous().cuda(), kbar.cuda(), [pos0[0] + 10], sub)
+    sub = sub.cpu().numpy()
+    for i in range(20):
+        o = (pos0[0] + 10 + i) // 4
+        assert np.array_equal(sub[0, i, :o], full[0, 10 + i, :o])
+
+
+# ------------------------------------------------------------------ step 3
+
+def _select_gpu(scores_rows: np.ndarray, p0: int, budget: int) -> np.ndarray:
+    """scores_rows [T, ld] float32 for rows at positions p0 .. p0+T-1."""
+    T, ld = scores_rows.shape
+    s = torch.from_numpy(np.ascontiguousarray(scores_rows)).reshape(1, T, ld).cuda()
+    sel = torch.empty((1, T, budget), dtype=torch.int32, device="cuda")
+    qsa.select_topk(s, [p0], budget, sel)
+    return sel.cpu().numpy()[0]
+
+
+def _rows(kind, n_cand, T, rng):
+    if kind == "normal":
+        return rng.standard_normal((T, n_cand)).astype(np.float32) * np.float32(0.088)
+    if kind == "equal":
+        return np.full((T, n_cand), 0.25, np.float32)
+    if kind == "coarse":
+        return (rng.integers(-4, 5, (T, n_cand)) * 0.5).astype(np.float32)
+    if kind == "signed_zero":
+        v = rng.choice(np.array([-0.0, 0.0, 1.0, -1.0], np.float32), (T, n_cand))
+        return v.astype(np.float32)
+    if kind == "specials":
+        v = rng.standard_normal((T, n_cand)).astype(np.float32)
+        m = rng.random((T, n_cand))
+        v[m < 0.05] = np.nan
+        v[(m >= 0.05) & (m < 0.08)] = np.inf
+        v[(m >= 0.08) & (m < 0.11)] = -np.inf
+        return v
+    if kind == "clustered":    # every key shares its top bits: several radix digits
+        return (np.float32(1.0) + rng.integers(0, 6000, (T, n_cand)).astype(np.float32) * np.float32(2.0 ** -23)).astype(np.float32)
+    if kind == "tie_flood":    # a few winners, then thousands of exact ties at the threshold
+        v = np.full((T, n_cand), 0.5, np.float32)
+        v[:, rng.choice(n_cand, 300, replace=False)] = 2.0
+        v[:, rng.choice(n_cand, 200, replace=False)] = -1.0
+        return v
+    raise ValueError(kind)
+
+
+SELECT_CASES = [
+    ("normal", 70000, 512), ("normal", 2047, 512), ("normal", 5000, 64), ("normal", 600, 2048),
+    ("normal", 9000, 1), ("normal", 9000, 2), ("normal", 3000, 17),
+    ("equal", 10000, 512), ("coarse", 8000, 512), ("signed_zero", 6000, 300),
+    ("specials", 7000, 512), ("clustered", 20000, 512), ("tie_flood", 12000, 512),
+    ("tie_flood", 12000, 2048),
+]
+
+
+@pytest.mark.parametrize("kind,n_cand,budget", SELECT_CASES,
+                         ids=[f"{k}-{n}-{b}" for k, n, b in SELECT_CASES])
+def test_select_is_bit_exact_on_identical_scores(kind, n_cand, budget):
+    say(f"select {kind} n={n_cand} budget={budget}")
+    rng = np.random.default_rng(n_cand + budget)
+    T = 6
+    p0 = 4 * n_cand - 2                         # rows see n_cand - 1 .. n_cand + 1 candidates
+    o_max = (p0 + T - 1) // 4
+    ld = (o_max + 3) // 4 * 4
+    rows = np.full((T, ld), np.float32(7.0))    # poison past each row's candidates
+    rows[:, :o_max] = _rows(kind, o_max, T, rng)
+    got = _select_gpu(rows, p0, budget)
+    for i in range(T):
+        ref = O.select_blocks(rows[i], p0 + i, budget)
+        assert np.array_equal(got[i], ref), (i, got[i][:8], ref[:8])
+
+
+def test_select_small_rows_and_early_tokens():
+    say("select early tokens")
+    rng = np.random.default_rng(3)
+    T = 300
+    rows = rng.standard_normal((T, 76)).astype(np.float32)
+    got = _select_gpu(rows, 0, 8)
+    for i in range(T):
+        assert np.array_equal(got[i], O.select_blocks(rows[i], i, 8)), i
+
+
+# ------------------------------------------------------------------ step 4
+
+def _oracle_inputs_for_attention(x: I.Inputs):
+    """Oracle-rotated Q and K (the attention step's inputs) as device tensors."""
+    wl = x.workload
+    qr = np.stack([O.rope_rotate(bits(x.q[b]), wl.ctx + np.arange(wl.tq)) for b in range(wl.batch)])
+    kr = np.stack([O.rope_rotate(bits(x.k[b]), np.arange(wl.length)) for b in range(wl.batch)])
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return to_dev(qr), to_dev(kr)
+
+
+def _check_attention(got_out, got_lse, ref_rows):
+    d = np.abs(got_out.astype(np.float64) - np.stack([r.out for r in ref_rows]))
+    dl = np.abs(got_lse.astype(np.float64) - np.stack([r.lse for r in ref_rows]))
+    say(f"  max_abs={d.max():.3g} mean_abs={d.mean():.3g} lse_abs={dl.max():.3g}")
+    assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS and dl.max() <= LSE_ABS
+
+
+@pytest.mark.parametrize("ctx,tq,budget", [(300, 90, 32), (0, 70, 8), (5000, 33, 512)])
+def test_attention_prefill_with_oracle_selection(ctx, tq, budget):
+    say(f"attention prefill ctx={ctx} tq={tq} budget={budget}")
+    wl = I.custom_workload("prefill", batch=2, ctx=ctx, tq=tq, budget=budget, seed=ctx + tq)
+    x = I.make_inputs(wl)
+    layer = oracle_layer(x)
+    rows = [(b, ctx + i) for b in range(2) for i in range(tq)]
+    ref = layer.rows(rows)
+    qd, kd = _oracle_inputs_for_attention(x)
+    sel = torch.from_numpy(np.stack([r.sel for r in ref]).reshape(2, tq, budget)).cuda()
+    out = torch.empty((2, tq, 24, 256), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((2, tq, 24), dtype=torch.float32, device="cuda")
+    qsa.sparse_attn_prefill(qd, kd, x.v.cuda(), sel, [ctx, ctx], out, lse)
+    _check_attention(out.float().cpu().numpy().reshape(-1, 24, 256), lse.cpu().numpy().reshape(-1, 24), ref)
+
+
+@pytest.mark.parametrize("ctx,budget", [(8000, 512), (8000, 64), (100, 512), (1, 4)])
+def test_attention_decode_with_oracle_selection(ctx, budget):
+    say(f"attention decode ctx={ctx} budget={budget}")
+    B = 3
+    wl = I.custom_workload("decode", batch=B, ctx=ctx, tq=1, budget=budget, seed=ctx + budget)
+    x = I.make_inputs(wl)
+    layer = oracle_layer(x)
+    rows = [(b, ctx) for b in range(B)]
+    ref = layer.rows(rows)
+    qd, kd = _oracle_inputs_for_attention(x)
+    sel = torch.from_numpy(np.stack([r.sel for r in ref])).cuda()
+    out = torch.empty((B, 24, 256), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 24), dtype=torch.float32, device="cuda")
+    ws = qsa.decode_workspace(B, budget)
+    qsa.sparse_attn_decode(qd[:, 0], kd, x.v.cuda(), sel, [ctx] * B, out, lse, ws)
+    _check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ end to end
+
+def test_end_to_end_prefill_T2048_budget64_every_row():
+    wl = I.WORKLOADS["prefill_T2048_budget64"]
+    say(f"end-to-end {wl.name}")
+    x = I.make_inputs(wl)
+    dp = DevicePrefill(x)
+    dp.run()
+    scores = dp.bufs.scores.cpu().numpy()
+    sel = dp.bufs.sel.cpu().numpy()
+    out = dp.out.float().cpu().numpy()
+    lse = dp.lse.cpu().numpy()
+    layer = oracle_layer(x)
+    rows = [(0, t) for t in range(wl.tq)]
+    compare_rows(layer, x, rows,
+                 lambda b, t: scores[b, t, :t // 4], lambda b, t: sel[b, t],
+                 lambda b, t: out[b, t], lambda b, t: lse[b, t])
+
+
+def test_end_to_end_prefill_with_prefix_and_chunks():
+    wl = I.custom_workload("prefill", batch=2, ctx=6001, tq=700, budget=64, n_needles=6, seed=77, chunk=256)
+    say(f"end-to-end {wl.name}")
+    x = I.make_inputs(wl)
+    dp = DevicePrefill(x)
+    dp.run()
+    sel = dp.bufs.sel.cpu().numpy()
+    out = dp.out.float().cpu().numpy()
+    lse = dp.lse.cpu().numpy()
+    layer = oracle_layer(x)
+    rows = [(b, wl.ctx + i) for b in range(2) for i in range(0, wl.tq, 7)] + \
+           [(int(b), int(t)) for b, t, _ in x.needles]
+    rows = sorted(set(rows))
+    compare_rows(layer, x, rows, None, lambda b, t: sel[b, t - wl.ctx],
+                 lambda b, t: out[b, t - wl.ctx], lambda b, t: lse[b, t - wl.ctx])
+
+
+def test_end_to_end_decode_B32_ctx32K():
+    wl = I.WORKLOADS["decode_B32_ctx32K"]
+    say(f"end-to-end {wl.name}")
+    x = I.make_inputs(wl)
+    dd = DeviceDecode(x)
+    dd.run()
+    scores = dd.scores.cpu().numpy()
+    sel = dd.sel.cpu().numpy()
+    out = dd.out.float().cpu().numpy()
+    lse = dd.lse.cpu().numpy()
+    layer = oracle_layer(x)
+    rows = [(b, wl.ctx) for b in range(wl.batch)]
+    o = wl.ctx // 4
+    compare_rows(layer, x, rows, lambda b, t: scores[b, 0, :o], lambda b, t: sel[b, 0],
+                 lambda b, t: out[b], lambda b, t: lse[b])
