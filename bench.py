@@ -158,27 +158,17 @@ class Decode:
         self.sel = torch.empty((B, 1, wl.budget), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, 24, 256), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, 24), dtype=torch.float32, device=dev)
-        self.ws = qsa.decode_workspace(B, wl.budget)
-        self.q_rot = torch.empty_like(self.q_raw)
+        self.ws = qsa.decode_step_workspace(B, wl.budget)
         torch.cuda.synchronize()
 
     def step(self, timer):
+        """One decode step through the single qsa_decode_step call (rotary of the
+        new q/k rows, block scores, selection, attention); a block completed by
+        the new token would be compressed after it."""
         wl, q = self.wl, self.qsa
-        B, pos = wl.batch, self.pos
-        p = [pos] * B
-        with timer("rope"):
-            q.rope_apply(self.q_raw, p, out=self.q_rot)
-            q.rope_apply(self.k_new, p, out=self.k_cache[:, pos:pos + 1])
-        if (pos + 1) % 4 == 0:
-            with timer("compress"):
-                q.compress_block_keys(self.k_idx, pos // 4, pos // 4 + 1, self.kbar)
-        with timer("index_scores"):
-            q.index_scores(self.q_idx, self.kbar, p, self.scores)
-        with timer("select_topk"):
-            q.select_topk(self.scores, p, wl.budget, self.sel)
-        with timer("sparse_attn_decode"):
-            q.sparse_attn_decode(self.q_rot[:, 0], self.k_cache, self.v_cache, self.sel[:, 0], p, self.out,
-                                 self.lse, self.ws)
+        with timer("decode_step"):
+            q.decode_step(self.q_raw, self.k_new, self.q_idx, self.k_idx, self.k_cache, self.v_cache, self.kbar,
+                          self.pos, wl.budget, self.out, self.lse, self.scores, self.sel, self.ws)
 
 
 class EventTimer:
@@ -377,7 +367,7 @@ def main():
             dd.step(NullTimer())
         torch.cuda.synchronize()
         steps_ms = []
-        dtimer = EventTimer(torch)
+        dtimer = NullTimer()
         for _ in range(args.decode_steps):
             flush.zero_()
             s = torch.cuda.Event(enable_timing=True)
@@ -387,15 +377,26 @@ def main():
             e.record()
             torch.cuda.synchronize()
             steps_ms.append(s.elapsed_time(e))
-        dk = dtimer.totals()
         steps_ms.sort()
         med = steps_ms[len(steps_ms) // 2]
+        # the dominant kernels alone: the fused index-select (block-key scan +
+        # threshold filter), same launch configuration as inside the step
+        sel_ws = qsa.index_select_workspace(dwl.batch)
+        idx_ms = []
+        for _ in range(args.decode_steps):
+            flush.zero_()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            qsa.index_select_decode(dd.q_idx, dd.kbar, [dd.pos] * dwl.batch, dwl.budget, dd.scores, dd.sel, sel_ws)
+            e.record()
+            torch.cuda.synchronize()
+            idx_ms.append(s.elapsed_time(e))
+        idx_avg = sum(idx_ms) / len(idx_ms) / 1e3
         o = dwl.ctx // 4
-        scan_bytes = dwl.batch * (o * 128 * 2 + o * 4 + 4 * 128 * 2)
+        kbar_bytes = dwl.batch * (o * 128 * 2 + 4 * 128 * 2)
         gather = dwl.batch * attended_tokens(dwl.ctx, dwl.budget) * 2 * 2 * 256 * 2
-        step_bytes = scan_bytes + gather + dwl.batch * (24 * 256 * 2 * 2 + dwl.budget * 4 * 2)
-        i_ms, i_n = dk["index_scores"]
-        i_avg = i_ms / i_n / 1e3
+        step_bytes = kbar_bytes + gather + dwl.batch * (24 * 256 * 2 * 2 + dwl.budget * 4)
         rec["decode"] = {
             "workload": dwl.name,
             "batch": dwl.batch,
@@ -407,18 +408,18 @@ def main():
             "cache_flushed": True,
             "hbm_frac_step": step_bytes / (med / 1e3) / HBM_PEAK,
             "algorithmic_bytes_per_step": step_bytes,
-            "kernels_us_per_step": {k: t * 1e3 / args.decode_steps for k, (t, n) in dk.items()},
             "roofline": {
                 "bound": "hbm",
-                "kernel": "index_scores",
-                "achieved": scan_bytes / i_avg / 1e9,
+                "kernel": "decode_scan_kernel + decode_filter_kernel (qsa_index_select_decode)",
+                "achieved": kbar_bytes / idx_avg / 1e9,
                 "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s",
-                "frac": scan_bytes / i_avg / HBM_PEAK,
-                "traffic": measured_traffic("index_scores", "index_scores.hip"),
+                "frac": kbar_bytes / idx_avg / HBM_PEAK,
+                "launch_us": idx_avg * 1e6,
+                "traffic": measured_traffic("decode_index_select", "decode.hip"),
             },
         }
-        log(args, f"decode: median {med * 1e3:.1f} us/step; kernels {rec['decode']['kernels_us_per_step']}")
+        log(args, f"decode: median {med * 1e3:.1f} us/step; index-select {idx_avg * 1e6:.1f} us")
         del dd, flush
         torch.cuda.empty_cache()
 

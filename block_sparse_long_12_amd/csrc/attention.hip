@@ -11,12 +11,18 @@
 // time (16 tokens):
 //   - each lane gathers one token row of K and of V (lane & 15 = token slot,
 //     lane >> 4 = which 16-byte slice), 8 KiB + 8 KiB per step per wave, as
-//     whole 512-byte rows of the token-major cache;
+//     whole 512-byte rows of the token-major cache; the next step's rows are
+//     requested before the current step is computed.  Slots that hold no
+//     token (padding, or past the query in its own block) read the query's
+//     own row instead and are masked out of the softmax, so no load is ever
+//     predicated or zero-filled;
 //   - S^T (16 tokens x 16 head slots, 12 real) = K Q^T on
 //     v_mfma_f32_16x16x32_bf16 with Q^T held in registers;
-//   - online softmax in float32 (exp2 with the scale folded into log2 e);
-//     each lane owns one head for all its accumulators, so rescaling is a
-//     per-lane multiply;
+//   - online softmax in float32 (exp2, scale folded into log2 e).  Each lane
+//     owns one head for all its accumulators.  The reference maximum of a head
+//     is only raised when a logit exceeds it by more than 8 in exp2 units, so
+//     the accumulators are rescaled once or twice per query instead of every
+//     step; the weights stay below 2^8 and the result is the same softmax;
 //   - O^T (256 dims x 16 heads) += V^T P^T on v_mfma_f32_16x16x16bf16_1k.
 //     The S^T accumulator layout (lane: tokens 4*(l/16)+r of head l%16) is
 //     exactly the B-operand layout the PV product needs, so P never moves
@@ -24,23 +30,111 @@
 // The gather is the bound (12 flop per gathered byte), not the matrix cores.
 #include <math.h>
 
-#include "qsa_internal.h"
+#include "rope_common.h"
 
 namespace qsa {
 
 constexpr int kVtStride = 20;                 // bf16 per dim row of the V^T tile (16 tokens + pad)
 constexpr int kVtElems = kD * kVtStride;      // one wave's tile
+constexpr float kRescaleSlack = 8.0f;         // exp2 units a logit may exceed the reference max
 
 struct WaveState {
-    float m;            // running max of raw logits q.k for this lane's head
-    float l;            // running softmax denominator
+    float m;            // reference max of raw logits q.k for this lane's head
+    float l;            // softmax denominator relative to m
     f32x4_t acc[16];    // O^T rows 16*nt + 4*(lane/16) + r, head lane%16
+};
+
+struct Chunk {
+    bf16x8_t ka[8];
+    bf16x8_t vv[8];
+    uint64_t vmask;     // token slots holding a real token
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+                                           const int32_t* __restrict__ selrow, int cb, int blk_end, int p,
+                                           Chunk& ch) {
+    const int lane = threadIdx.x & 63;
+    const int c16 = lane & 15;
+    const int G = lane >> 4;
+    const int slot_blk = cb + (c16 >> 2);
+    const int j = (slot_blk < blk_end) ? selrow[slot_blk] : -1;
+    const int n = kBlock * j + (c16 & 3);
+    const bool valid = (j >= 0) && (j <= p / kBlock) && (n <= p);
+    const int64_t row = valid ? n : p;
+    const uint16_t* kr = kg + row * (kHkv * kD);
+    const uint16_t* vr = vg + row * (kHkv * kD);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        ch.ka[s] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * s + 8 * G);
+        ch.vv[s] = *reinterpret_cast<const bf16x8_t*>(vr + 8 * (4 * s + G));
+    }
+    ch.vmask = __ballot(valid);
+}
+
+__device__ __forceinline__ void attend_chunk(const Chunk& ch, const bf16x8_t (&qf)[8], float c,
+                                             WaveState& st, uint16_t* vt) {
+    const int lane = threadIdx.x & 63;
+    const int c16 = lane & 15;
+    const int G = lane >> 4;
+
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.ka[ks], qf[ks], s, 0, 0, 0);
+
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool ok = (ch.vmask >> (4 * G + r)) & 1ull;
+        sv[r] = ok ? s[r] : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // raise the reference max only when the new logits would exceed it by the slack
+    const bool raise = (mx - st.m) * c > kRescaleSlack;     // always true while st.m = -inf
+    if (__ballot(raise) != 0ull) {                          // wave-uniform
+        const float m_new = raise ? mx : st.m;
+        const float alpha = exp2f((st.m - m_new) * c);      // 1 for heads not raised, 0 from -inf
+        st.l *= alpha;
+        st.m = m_new;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) st.acc[t] *= alpha;
+    }
+    s16x4_t pb;
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float pr = exp2f((sv[r] - st.m) * c);         // 0 for masked slots
+        const uint16_t pbits = f32_to_bf16(pr);
+        pb[r] = static_cast<short>(pbits);
+        ps += bf16_to_f32(pbits);          // the denominator uses the weights the product sees
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    st.l += ps;
+
+    // V^T tile: vt[dim * kVtStride + token slot]
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(&ch.vv[s2]);
+        const int d0 = 8 * (4 * s2 + G);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) vt[(d0 + q) * kVtStride + c16] = e[q];
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt) {
+        const s16x4_t va = *reinterpret_cast<const s16x4_t*>(vt + (16 * nt + c16) * kVtStride + 4 * G);
+        st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, st.acc[nt], 0, 0, 0);
+    }
+    wave_lds_sync();
 }
 
 // Attend over sel[blk_begin .. blk_end) for the query at position p.
@@ -50,86 +144,41 @@ __device__ __forceinline__ void attend_blocks(const uint16_t* __restrict__ kg,
                                               const int32_t* __restrict__ selrow, int blk_begin,
                                               int blk_end, int p, const bf16x8_t (&qf)[8],
                                               float c, WaveState& st, uint16_t* vt) {
-    const int lane = threadIdx.x & 63;
-    const int c16 = lane & 15;
-    const int G = lane >> 4;
-    const int o = p / kBlock;
+    if (blk_begin >= blk_end) return;
+    Chunk cur;
+    load_chunk(kg, vg, selrow, blk_begin, blk_end, p, cur);
     for (int cb = blk_begin; cb < blk_end; cb += 4) {
-        const int slot_blk = cb + (c16 >> 2);
-        const int j = (slot_blk < blk_end) ? selrow[slot_blk] : -1;
-        const int n = kBlock * j + (c16 & 3);
-        const bool valid = (j >= 0) && (j <= o) && (n <= p);
-        const uint16_t* kr = kg + static_cast<int64_t>(n) * (kHkv * kD);
-        const uint16_t* vr = vg + static_cast<int64_t>(n) * (kHkv * kD);
-        bf16x8_t ka[8], vv[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            if (valid) {
-                ka[s] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * s + 8 * G);
-                vv[s] = *reinterpret_cast<const bf16x8_t*>(vr + 8 * (4 * s + G));
-            } else {
-                ka[s] = bf16x8_t{};
-                vv[s] = bf16x8_t{};
-            }
-        }
-        const uint64_t vmask = __ballot(valid);
-        if (vmask == 0) continue;                              // wave-uniform
-
-        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qf[ks], s, 0, 0, 0);
-
-        float sv[4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const bool ok = (vmask >> (4 * G + r)) & 1ull;
-            sv[r] = ok ? s[r] : -INFINITY;
-            mx = fmaxf(mx, sv[r]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(st.m, mx);
-        const float alpha = exp2f((st.m - m_new) * c);        // 0 when st.m = -inf
-        s16x4_t pb;
-        float ps = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float pr = (sv[r] == -INFINITY) ? 0.f : exp2f((sv[r] - m_new) * c);
-            const uint16_t pbits = f32_to_bf16(pr);
-            pb[r] = static_cast<short>(pbits);
-            ps += bf16_to_f32(pbits);          // the denominator uses the weights the product sees
-        }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        st.l = st.l * alpha + ps;
-        st.m = m_new;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) st.acc[t] *= alpha;
-
-        // V^T tile: vt[dim * kVtStride + token slot]
-#pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) {
-            const uint16_t* e = reinterpret_cast<const uint16_t*>(&vv[s2]);
-            const int d0 = 8 * (4 * s2 + G);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) vt[(d0 + q) * kVtStride + c16] = e[q];
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int nt = 0; nt < 16; ++nt) {
-            const s16x4_t va = *reinterpret_cast<const s16x4_t*>(vt + (16 * nt + c16) * kVtStride + 4 * G);
-            st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, st.acc[nt], 0, 0, 0);
-        }
-        wave_lds_sync();
+        Chunk nxt;
+        const bool more = cb + 4 < blk_end;
+        if (more) load_chunk(kg, vg, selrow, cb + 4, blk_end, p, nxt);
+        if (cur.vmask != 0ull) attend_chunk(cur, qf, c, st, vt);
+        if (more) cur = nxt;
     }
 }
 
-__device__ __forceinline__ void load_q_frags(const uint16_t* qh, bool ok, bf16x8_t (&qf)[8]) {
+// Q^T fragments of this lane's head (lane & 15 < 12), k slices 32*ks + 8*(lane/16).
+// With `rope`, the rotary pairs (d, d + 32), d = 8*(lane/16) + e, sit in
+// fragments 0 and 1 of the same lane and are rotated here exactly as the
+// rotary kernel does, so an unrotated q gives the same bits as a pre-rotated one.
+__device__ __forceinline__ void load_q_frags(const uint16_t* qh, bool ok, int p, const InvFreq* rope,
+                                             bf16x8_t (&qf)[8]) {
     const int G = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
         qf[ks] = ok ? *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * G) : bf16x8_t{};
+    if (rope != nullptr) {
+        uint16_t* lo = reinterpret_cast<uint16_t*>(&qf[0]);
+        uint16_t* hi = reinterpret_cast<uint16_t*>(&qf[1]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            double sn, cs;
+            sincos(static_cast<double>(p) * rope->f[8 * G + e], &sn, &cs);
+            const double a = bf16_to_f32(lo[e]);
+            const double b = bf16_to_f32(hi[e]);
+            lo[e] = rotate_half_elem(a, b, cs, sn, true);
+            hi[e] = rotate_half_elem(b, a, cs, sn, false);
+        }
+    }
 }
 
 __device__ __forceinline__ void init_state(WaveState& st) {
@@ -145,7 +194,7 @@ __global__ __launch_bounds__(128) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int64_t qs, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs, const int32_t* __restrict__ sel, int64_t sels,
     Positions pos0, int tq, int budget, float scale, float c, uint16_t* __restrict__ out,
-    int64_t os, float* __restrict__ lse, int64_t lss) {
+    int64_t os, float* __restrict__ lse, int64_t lss, InvFreq inv, int rope_q) {
     __shared__ uint16_t vt_all[2 * kVtElems];
     const int g = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -159,7 +208,7 @@ __global__ __launch_bounds__(128) void attn_prefill_kernel(
 
     bf16x8_t qf[8];
     const uint16_t* qrow = q + b * qs + static_cast<int64_t>(i) * (kHq * kD);
-    load_q_frags(qrow + (head_ok ? head : 0) * kD, head_ok, qf);
+    load_q_frags(qrow + (head_ok ? head : 0) * kD, head_ok, p, rope_q ? &inv : nullptr, qf);
     WaveState st;
     init_state(st);
     attend_blocks(k + b * kvs + g * kD, v + b * kvs + g * kD, sel + b * sels + static_cast<int64_t>(i) * budget,
@@ -188,18 +237,20 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
     const int64_t rows = static_cast<int64_t>(batch) * tq;
     if (rows == 0) return hipSuccess;
     const float c = scale * 1.4426950408889634f;
+    const InvFreq inv = make_inv_freq(1.0e7);
     hipLaunchKernelGGL(attn_prefill_kernel, dim3(static_cast<unsigned>(rows)), dim3(128), 0, stream,
-                       q, qs, k, v, kvs, sel, sels, pos0, tq, budget, scale, c, out, os, lse, lss);
+                       q, qs, k, v, kvs, sel, sels, pos0, tq, budget, scale, c, out, os, lse, lss, inv, 0);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- decode
 
 // Split the budget over n_split workgroups per sequence; each writes the
-// partial (max, sum, unnormalised O) of its blocks for the 24 heads.
+// partial (reference max, sum, unnormalised O) of its blocks for the 24 heads.
 static void decode_split(int batch, int budget, int* n_split, int* bps) {
     int s = 128 / (batch > 0 ? batch : 1);
     if (s < 1) s = 1;
+    if (s > 64) s = 64;
     const int max_s = (budget + 3) / 4;
     if (s > max_s) s = max_s;
     int per = (budget + s - 1) / s;
@@ -218,7 +269,7 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     const uint16_t* __restrict__ q, int64_t qs, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs, const int32_t* __restrict__ sel, int64_t sels,
     Positions pos, int budget, int n_split, int bps, float c, float* __restrict__ ws_ml,
-    float* __restrict__ ws_acc) {
+    float* __restrict__ ws_acc, InvFreq inv, int rope_q) {
     __shared__ uint16_t vt_all[2 * kVtElems];
     const int g = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -231,7 +282,7 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     const bool head_ok = c16 < kGroup;
 
     bf16x8_t qf[8];
-    load_q_frags(q + b * qs + (head_ok ? head : 0) * kD, head_ok, qf);
+    load_q_frags(q + b * qs + (head_ok ? head : 0) * kD, head_ok, p, rope_q ? &inv : nullptr, qf);
     WaveState st;
     init_state(st);
     const int blk_begin = s * bps;
@@ -251,29 +302,35 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     }
 }
 
-// One wave per (sequence, head): merge the n_split partial states.
+// One wave per (sequence, head): lane s reads split s's (max, sum), the wave
+// forms the merge weights, then every lane merges 4 dims over the splits.
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, int n_split, float scale,
     float c, uint16_t* __restrict__ out, int64_t os, float* __restrict__ lse) {
     const int lane = threadIdx.x;
     const int b = blockIdx.x / kHq;
     const int h = blockIdx.x % kHq;
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s)
-        M = fmaxf(M, ws_ml[2 * ((static_cast<int64_t>(b) * n_split + s) * kHq + h)]);
-    float L = 0.f;
+    const int64_t base = static_cast<int64_t>(b) * n_split * kHq + h;    // split s at base + s * kHq
+    float m = -INFINITY, l = 0.f;
+    if (lane < n_split) {
+        m = ws_ml[2 * (base + static_cast<int64_t>(lane) * kHq)];
+        l = ws_ml[2 * (base + static_cast<int64_t>(lane) * kHq) + 1];
+    }
+    float M = m;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = (m == -INFINITY) ? 0.f : exp2f((m - M) * c);
+    float L = w * l;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < n_split; ++s) {
-        const int64_t idx = (static_cast<int64_t>(b) * n_split + s) * kHq + h;
-        const float m = ws_ml[2 * idx];
-        if (m == -INFINITY) continue;
-        const float w = exp2f((m - M) * c);
-        L += w * ws_ml[2 * idx + 1];
-        const float4 a = *reinterpret_cast<const float4*>(ws_acc + idx * kD + 4 * lane);
-        acc.x += w * a.x;
-        acc.y += w * a.y;
-        acc.z += w * a.z;
-        acc.w += w * a.w;
+        const float ws = __shfl(w, s);
+        const float4 a = *reinterpret_cast<const float4*>(ws_acc + (base + static_cast<int64_t>(s) * kHq) * kD + 4 * lane);
+        acc.x += ws * a.x;
+        acc.y += ws * a.y;
+        acc.z += ws * a.z;
+        acc.w += ws * a.w;
     }
     const float inv = 1.f / L;
     uint2 o;
@@ -283,25 +340,35 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     if (lse != nullptr && lane == 0) lse[static_cast<int64_t>(b) * kHq + h] = M * scale + logf(L);
 }
 
-hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
-                              const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
-                              const Positions& pos, int batch, int budget, float scale,
-                              uint16_t* out, int64_t os, float* lse, void* ws,
-                              hipStream_t stream) {
+hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* k,
+                                 const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
+                                 const Positions& pos, int batch, int budget, float scale,
+                                 uint16_t* out, int64_t os, float* lse, void* ws, double rope_theta,
+                                 hipStream_t stream) {
     if (batch == 0) return hipSuccess;
     int n_split, bps;
     decode_split(batch, budget, &n_split, &bps);
     float* ws_ml = static_cast<float*>(ws);
     float* ws_acc = ws_ml + static_cast<size_t>(batch) * n_split * kHq * 2;
     const float c = scale * 1.4426950408889634f;
+    const InvFreq inv = make_inv_freq(rope_theta > 0.0 ? rope_theta : 1.0e7);
     hipLaunchKernelGGL(attn_decode_split_kernel, dim3(static_cast<unsigned>(batch * n_split)),
                        dim3(128), 0, stream, q, qs, k, v, kvs, sel, sels, pos, budget, n_split, bps,
-                       c, ws_ml, ws_acc);
+                       c, ws_ml, ws_acc, inv, rope_theta > 0.0 ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(static_cast<unsigned>(batch * kHq)), dim3(64),
                        0, stream, ws_ml, ws_acc, n_split, scale, c, out, os, lse);
     return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
+                              const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
+                              const Positions& pos, int batch, int budget, float scale,
+                              uint16_t* out, int64_t os, float* lse, void* ws,
+                              hipStream_t stream) {
+    return launch_attn_decode_ex(q, qs, k, v, kvs, sel, sels, pos, batch, budget, scale, out, os, lse,
+                                 ws, 0.0, stream);
 }
 
 }  // namespace qsa

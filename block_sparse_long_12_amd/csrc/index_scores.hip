@@ -19,7 +19,7 @@
 // of block columns, streaming 64 blocks (16 KiB of kbar) per step; each lane
 // stores one float4 per row tile, and 16 lanes cover 256 contiguous bytes of
 // a score row.  Causality: a wave stops at the last block its last row sees.
-#include "qsa_internal.h"
+#include "index_common.h"
 
 namespace qsa {
 
@@ -49,48 +49,26 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
     const int G = lane >> 4;
     const int m_tiles = (n_tok + 3) / 4;
 
-    // A operand: row tile m, lane row c16 -> token t0 + 4m + c16/4, head c16 % 4
     bf16x8_t a[4][4];
     const uint16_t* qb = q_idx + b * qs;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int tok = t0 + 4 * m + (c16 >> 2);
-        const uint16_t* qr = qb + (static_cast<int64_t>(tok) * kHi + (c16 & 3)) * kDi + 8 * G;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (tok < tq) a[m][ks] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * ks);
-            else a[m][ks] = bf16x8_t{};
-        }
-    }
+    for (int m = 0; m < 4; ++m) load_index_a(qb, t0 + 4 * m, tq, a[m]);
 
     const uint16_t* kb = kbar + b * kbs;
     float* sb = scores + b * ss;
     for (int j0 = j_begin; j0 < j_end; j0 += kColStep) {
         bf16x8_t bf[4][4];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int j = j0 + 4 * c16 + n;
-            const uint16_t* kr = kb + static_cast<int64_t>(j) * kDi + 8 * G;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (j < j_end) bf[n][ks] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * ks);
-                else bf[n][ks] = bf16x8_t{};
-            }
-        }
+        for (int n = 0; n < 4; ++n) load_index_b(kb, j0, n, j_end, bf[n]);
         const int jj = j0 + 4 * c16;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             if (m < m_tiles) {                               // wave-uniform
                 float4 out;
-                float* o = &out.x;
-#pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][ks], bf[n][ks], acc, 0, 0, 0);
-                    o[n] = ((acc[0] + acc[1]) + acc[2]) + acc[3];
-                }
+                out.x = block_score(a[m], bf[0]);
+                out.y = block_score(a[m], bf[1]);
+                out.z = block_score(a[m], bf[2]);
+                out.w = block_score(a[m], bf[3]);
                 const int tok = t0 + 4 * m + G;
                 if (tok < tq && jj < j_end)
                     *reinterpret_cast<float4*>(sb + static_cast<int64_t>(tok) * ld + jj) = out;

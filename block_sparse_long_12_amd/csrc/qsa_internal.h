@@ -88,6 +88,21 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
                                hipStream_t stream);
 
 size_t decode_workspace_bytes(int batch, int budget);
+// decode attention with optional rotation of q on load (rope_theta > 0)
+hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* k,
+                                 const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
+                                 const Positions& pos, int batch, int budget, float scale,
+                                 uint16_t* out, int64_t os, float* lse, void* ws, double rope_theta,
+                                 hipStream_t stream);
+
+// fused decode index-select (scores + selection of one query row per sequence);
+// the workspace must be zero before its first use and is left zero by each call
+size_t decode_select_ws_bytes(int batch);
+hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
+                                      int64_t kbs, const Positions& pos, int batch, int budget,
+                                      float* scores, int64_t ss, int32_t* sel, int64_t sels, void* ws,
+                                      const uint16_t* k_new, int64_t kns, uint16_t* k_cache,
+                                      int64_t kcs, double rope_theta, hipStream_t stream);
 hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
                               const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                               const Positions& pos, int batch, int budget, float scale,

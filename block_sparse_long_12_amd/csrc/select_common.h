@@ -1,0 +1,240 @@
+// Exact per-row block selection, shared by the selection kernel and the
+// fallback of the fused decode index-select.
+//
+// Row semantics (Qwen3.8-Flash-Next blog, "Attention: GDN + QSA": the most
+// relevant blocks are selected; model card: budget 512 blocks): for the query
+// with own block o, keep the top `keep` = min(budget - 1, o) candidates j < o
+// by (score desc, j asc), add o, write ascending into out[0 .. budget),
+// padded with -1.
+//
+// Exact radix select on ordered uint32 keys (score_key: monotone in the
+// float, -0.0 == +0.0, NaN lowest), one workgroup per row:
+//   1. histogram passes over the row (LDS atomics) on key digits of 11, 11
+//      and 10 bits, each restricted to the current prefix, until the bin that
+//      holds the threshold has at most kSelectCap members;
+//   2. a collect pass: keys above the threshold bin are taken outright, bin
+//      members go to LDS as (key << 32 | ~j) and are bitonic-sorted, the first
+//      `remaining` are taken;
+//   3. if all 32 bits are resolved and the tied keys still exceed kSelectCap,
+//      the ties are taken in index order with a workgroup prefix count;
+//   4. the chosen indices plus o are bitonic-sorted ascending and written.
+// The result depends only on the score bits, never on thread timing.
+#pragma once
+
+#include "qsa_internal.h"
+
+namespace qsa {
+
+constexpr int kSelectCap = 2048;     // threshold-bin members held in LDS
+
+struct SelectSmem {
+    uint32_t hist[2048];
+    uint64_t cand[kSelectCap];
+    int32_t chosen[QSA_MAX_BUDGET];
+    int wave_tot[16];
+    int n_chosen, n_cand, sh_above;
+    uint32_t sh_bin;
+};
+
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const int t = wave_tot[w];
+        before += (w < wave) ? t : 0;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + x - v;
+}
+
+template <int NT, typename T, bool kDescending>
+__device__ void bitonic_sort(T* a, int n) {
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n; i += NT) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const T x = a[i];
+                    const T y = a[ixj];
+                    const bool first_half_up = ((i & k) == 0) != kDescending;
+                    if (first_half_up ? (x > y) : (x < y)) {
+                        a[i] = y;
+                        a[ixj] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+__device__ __forceinline__ int next_pow2(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+// Threshold bin of a histogram walked from the top: the bin where the
+// running count (from the highest bin down) first reaches `remaining`.
+// Sets *sh_bin and *sh_above (count strictly above that bin).  Every thread
+// of the workgroup must call it; nb must be a multiple of NT.
+template <int NT>
+__device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, int nb, int remaining,
+                                                   int* wave_tot, uint32_t* sh_bin, int* sh_above) {
+    const int tid = threadIdx.x;
+    const int bpt = nb / NT;
+    const int hi = nb - 1 - tid * bpt;
+    int local = 0;
+    for (int q = 0; q < bpt; ++q) local += static_cast<int>(hist[hi - q]);
+    int total;
+    const int above = block_exclusive_scan<NT>(local, wave_tot, &total);
+    if (above < remaining && above + local >= remaining) {
+        int run = above;
+        for (int q = 0; q < bpt; ++q) {
+            const int h = static_cast<int>(hist[hi - q]);
+            if (run + h >= remaining) {
+                *sh_bin = static_cast<uint32_t>(hi - q);
+                *sh_above = run;
+                break;
+            }
+            run += h;
+        }
+    }
+    __syncthreads();
+}
+
+// Writes the final ascending selection: sm.chosen[0 .. keep) plus o.
+template <int NT>
+__device__ __forceinline__ void write_selection(SelectSmem& sm, int keep, int o, int budget,
+                                                int32_t* out) {
+    const int tid = threadIdx.x;
+    const int nsel = keep + 1;
+    const int np2 = next_pow2(nsel);
+    if (tid == 0) sm.chosen[keep] = o;
+    for (int k = nsel + tid; k < np2; k += NT) sm.chosen[k] = 0x7fffffff;
+    __syncthreads();
+    bitonic_sort<NT, int32_t, false>(sm.chosen, np2);
+    for (int k = tid; k < budget; k += NT) out[k] = (k < nsel) ? sm.chosen[k] : -1;
+}
+
+// Trivial rows: every candidate fits the budget, or the budget is the own block alone.
+__device__ __forceinline__ bool trivial_selection(int keep, int o, int budget, int32_t* out, int nt) {
+    if (keep != o && keep != 0) return false;
+    for (int k = threadIdx.x; k < budget; k += nt)
+        out[k] = (keep == o) ? (k <= o ? k : -1) : (k == 0 ? o : -1);
+    return true;
+}
+
+// Full selection of one row held in global memory (16-byte aligned).
+template <int NT>
+__device__ void select_row(const float* __restrict__ row, int o, int keep, int budget,
+                           int32_t* __restrict__ out, SelectSmem& sm) {
+    const int tid = threadIdx.x;
+    if (trivial_selection(keep, o, budget, out, NT)) return;
+    const int n4 = o >> 2;
+    const float4* row4 = reinterpret_cast<const float4*>(row);
+
+    uint32_t prefix = 0, pmask = 0;
+    int remaining = keep;                    // still to take among keys matching the prefix
+    int bin_count = o;
+    int shift = 32;
+    for (int d = 0; d < 3 && bin_count > kSelectCap; ++d) {
+        const int bits = (d < 2) ? 11 : 10;
+        shift -= bits;
+        const int nb = 1 << bits;
+        const uint32_t dmask = static_cast<uint32_t>(nb - 1);
+        for (int k = tid; k < nb; k += NT) sm.hist[k] = 0;
+        __syncthreads();
+        for (int k = tid; k < n4; k += NT) {
+            const float4 v = row4[k];
+            const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t key = score_key(f[e]);
+                if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & dmask], 1u);
+            }
+        }
+        for (int j = 4 * n4 + tid; j < o; j += NT) {
+            const uint32_t key = score_key(row[j]);
+            if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        find_threshold_bin<NT>(sm.hist, nb, remaining, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
+        const uint32_t tb = sm.sh_bin;
+        remaining -= sm.sh_above;
+        prefix |= tb << shift;
+        pmask |= dmask << shift;
+        bin_count = static_cast<int>(sm.hist[tb]);
+        __syncthreads();
+    }
+
+    if (tid == 0) {
+        sm.n_chosen = 0;
+        sm.n_cand = 0;
+    }
+    __syncthreads();
+
+    if (bin_count <= kSelectCap) {
+        for (int k = tid; k < n4; k += NT) {
+            const float4 v = row4[k];
+            const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t key = score_key(f[e]);
+                const uint32_t mk = key & pmask;
+                const int j = 4 * k + e;
+                if (mk > prefix) sm.chosen[atomicAdd(&sm.n_chosen, 1)] = j;
+                else if (mk == prefix)
+                    sm.cand[atomicAdd(&sm.n_cand, 1)] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~j);
+            }
+        }
+        for (int j = 4 * n4 + tid; j < o; j += NT) {
+            const uint32_t key = score_key(row[j]);
+            const uint32_t mk = key & pmask;
+            if (mk > prefix) sm.chosen[atomicAdd(&sm.n_chosen, 1)] = j;
+            else if (mk == prefix)
+                sm.cand[atomicAdd(&sm.n_cand, 1)] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~j);
+        }
+        __syncthreads();
+        const int nc = sm.n_cand;
+        const int base = sm.n_chosen;        // == keep - remaining
+        const int np2 = next_pow2(nc);
+        for (int k = nc + tid; k < np2; k += NT) sm.cand[k] = 0;   // below every real entry
+        __syncthreads();
+        bitonic_sort<NT, uint64_t, true>(sm.cand, np2);
+        for (int k = tid; k < remaining; k += NT)
+            sm.chosen[base + k] = static_cast<int32_t>(~static_cast<uint32_t>(sm.cand[k]));
+        __syncthreads();
+    } else {
+        // all 32 key bits fixed: key == prefix are ties, taken by ascending index
+        int tie_base = 0;
+        for (int base = 0; base < o; base += NT) {
+            const int j = base + tid;
+            const uint32_t key = (j < o) ? score_key(row[j]) : 0u;
+            const bool gt = (j < o) && key > prefix;
+            const bool eq = (j < o) && key == prefix;
+            if (gt) sm.chosen[atomicAdd(&sm.n_chosen, 1)] = j;
+            int total;
+            const int rank = block_exclusive_scan<NT>(eq ? 1 : 0, sm.wave_tot, &total);
+            if (eq && tie_base + rank < remaining) sm.chosen[atomicAdd(&sm.n_chosen, 1)] = j;
+            tie_base += total;
+        }
+        __syncthreads();
+    }
+    write_selection<NT>(sm, keep, o, budget, out);
+}
+
+}  // namespace qsa

@@ -48,6 +48,13 @@ _SIGNATURES = {
     "qsa_decode_workspace_bytes": (_sz, [_i32, _i32]),
     "qsa_sparse_attn_decode": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32,
                                       ctypes.c_float, _c_p, _i64, _c_p, _c_p, _sz, _c_p]),
+    "qsa_index_select_decode_workspace_bytes": (_sz, [_i32]),
+    "qsa_index_select_decode": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _c_p, _i64, _c_p, _i64,
+                                       _c_p, _sz, _c_p]),
+    "qsa_decode_step_workspace_bytes": (_sz, [_i32, _i32]),
+    "qsa_decode_step": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32,
+                               _i32, ctypes.c_float, ctypes.c_double, _c_p, _i64, _c_p, _i64, _c_p, _i64,
+                               _c_p, _c_p, _sz, _c_p]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -291,22 +298,88 @@ def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0
     return out
 
 
+def index_select_workspace(batch: int, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace of the fused decode index-select (reusable across calls)."""
+    n = lib().qsa_index_select_decode_workspace_bytes(batch)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def index_select_decode(q_idx: torch.Tensor, kbar: torch.Tensor, q_pos, budget: int, scores: torch.Tensor,
+                        sel: torch.Tensor, workspace: torch.Tensor, stream=None):
+    """Fused steps 2 + 3 for decode rows: q_idx [B, 4, 128] (or [B, 1, 4, 128]),
+    scores [B, ld] or [B, 1, ld], sel [B, budget] or [B, 1, budget]."""
+    _need(q_idx, "q_idx", torch.bfloat16, (HI, DI))
+    _need(kbar, "kbar", torch.bfloat16, (DI,))
+    _need(scores, "scores", torch.float32, ())
+    _need(sel, "sel", torch.int32, (budget,))
+    B = q_idx.shape[0]
+    pos = _positions(q_pos, B)
+    need = max(int(pos[b]) // BLOCK for b in range(B))
+    if scores.shape[-1] < need or kbar.shape[1] < need or scores.shape[-1] % 4:
+        raise QSAError("scores / kbar do not cover the candidate blocks")
+    _check(lib().qsa_index_select_decode(_ptr(q_idx), q_idx.stride(0), _ptr(kbar), kbar.stride(0), pos, B,
+                                         budget, _ptr(scores), scores.stride(0), _ptr(sel), sel.stride(0),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+           "qsa_index_select_decode")
+    return sel
+
+
+def decode_step_workspace(batch: int, budget: int, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace of qsa_decode_step (reusable across calls)."""
+    n = lib().qsa_decode_step_workspace_bytes(batch, budget)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
 def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos: int, budget: int,
-                out, lse, scores, sel, workspace, q_rot, stream=None):
-    """One decode step for B sequences, each with one new token at position pos.
+                out, lse, scores, sel, workspace, stream=None, scale: float = 1.0 / math.sqrt(D)):
+    """One decode step for B sequences, each with one new token at position pos,
+    through the single qsa_decode_step call.
 
     q_raw [B, 1, 24, 256] and k_new_raw [B, 1, 2, 256] are unrotated; the
     rotated K row goes to k_cache[:, pos] (the V and k_idx rows are expected
-    in place); kbar must hold blocks 0 .. pos // 4 - 1.  When the new token
-    completes its block, that block's key is compressed too.
+    in place); kbar must hold blocks 0 .. pos // 4 - 1; workspace comes from
+    decode_step_workspace.  When the new token completes its block, that
+    block's key is compressed afterwards for the next steps.
     """
+    B = q_raw.shape[0]
+    _need(q_raw, "q", torch.bfloat16, (HQ, D))
+    _need(k_new_raw, "k_new", torch.bfloat16, (HKV, D))
+    _need(q_idx, "q_idx", torch.bfloat16, (HI, DI))
+    _need(k_cache, "k_cache", torch.bfloat16, (HKV, D))
+    _need(v_cache, "v_cache", torch.bfloat16, (HKV, D))
+    _need(kbar, "kbar", torch.bfloat16, (DI,))
+    _need(out, "out", torch.bfloat16, (HQ, D))
+    _need(scores, "scores", torch.float32, ())
+    _need(sel, "sel", torch.int32, (budget,))
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape or k_cache.shape[1] <= pos:
+        raise QSAError("k_cache / v_cache must share shape and strides and hold position pos")
+    if lse is not None and (not lse.is_contiguous() or tuple(lse.shape) != (B, HQ)):
+        raise QSAError("lse must be contiguous [B, 24]")
+    if scores.shape[-1] < pos // BLOCK or scores.shape[-1] % 4 or kbar.shape[1] < pos // BLOCK:
+        raise QSAError("scores / kbar do not cover the candidate blocks")
+    p = _positions([pos] * B, B)
+    _check(lib().qsa_decode_step(_ptr(q_raw), q_raw.stride(0), _ptr(k_new_raw), k_new_raw.stride(0), _ptr(q_idx),
+                                 q_idx.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0), _ptr(kbar),
+                                 kbar.stride(0), p, B, budget, float(scale), ROPE_THETA, _ptr(scores),
+                                 scores.stride(0), _ptr(sel), sel.stride(0), _ptr(out), out.stride(0), _ptr(lse),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)),
+           "qsa_decode_step")
+    if (pos + 1) % BLOCK == 0:
+        compress_block_keys(k_idx, pos // BLOCK, pos // BLOCK + 1, kbar, stream=stream)
+    return out
+
+
+def decode_step_primitives(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos: int, budget: int,
+                           out, lse, scores, sel, workspace, q_rot, stream=None):
+    """The same decode step as a chain of the primitive calls (rope, scores,
+    selection, attention); workspace from decode_workspace."""
     B = q_raw.shape[0]
     p = [pos] * B
     rope_apply(q_raw, p, out=q_rot, stream=stream)
     rope_apply(k_new_raw, p, out=k_cache[:, pos:pos + 1], stream=stream)
-    if (pos + 1) % BLOCK == 0:
-        compress_block_keys(k_idx, pos // BLOCK, pos // BLOCK + 1, kbar, stream=stream)
     index_scores(q_idx, kbar, p, scores, stream=stream)
     select_topk(scores, p, budget, sel, stream=stream)
     sparse_attn_decode(q_rot[:, 0], k_cache, v_cache, sel[:, 0], p, out, lse, workspace, stream=stream)
+    if (pos + 1) % BLOCK == 0:
+        compress_block_keys(k_idx, pos // BLOCK, pos // BLOCK + 1, kbar, stream=stream)
     return out

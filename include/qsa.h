@@ -168,6 +168,52 @@ qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
                                     float* lse, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/*
+ * Steps 2 + 3 fused for decode rows (one query token per sequence at
+ * position q_pos[b]): writes the same scores as qsa_index_scores (tq = 1)
+ * and the same selection as qsa_select_topk, bit for bit, in two launches
+ * that spread each row over many workgroups (a scan that also histograms the
+ * score keys, then a threshold filter whose last workgroup finishes the
+ * exact selection).  scores [B][>= q_pos/4] (seq stride, 16-byte aligned,
+ * multiple of 4), sel [B][budget].  The workspace
+ * (qsa_index_select_decode_workspace_bytes) must be zero-filled before its
+ * first use; every call leaves it zeroed again.  Calls that share a
+ * workspace must not overlap.
+ */
+size_t       qsa_index_select_decode_workspace_bytes(int32_t batch);
+qsa_status_t qsa_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                     const uint16_t* kbar, int64_t kbar_seq_stride,
+                                     const int32_t* q_pos, int32_t batch, int32_t budget,
+                                     float* scores, int64_t scores_seq_stride,
+                                     int32_t* sel, int64_t sel_seq_stride,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One whole decode step of the layer for B sequences, each with one new token
+ * at position q_pos[b] (steps 0, 2, 3 and 4): the unrotated new key row
+ * k_new [B][2][256] is rotated into k_cache[b][q_pos[b]] (the new V row must
+ * already be in v_cache), the block scores and the selection are computed as
+ * by qsa_index_select_decode, and attention runs with q [B][24][256]
+ * (unrotated; rotated on load exactly as qsa_rope_apply would).  kbar must
+ * hold blocks 0 .. q_pos[b]/4 - 1; compressing the block a new token
+ * completes is left to qsa_compress_block_keys (the step never scores it).
+ * Equals rope_apply + index_scores + select_topk + sparse_attn_decode bit
+ * for bit.  The workspace (qsa_decode_step_workspace_bytes) must be
+ * zero-filled before its first use.
+ */
+size_t       qsa_decode_step_workspace_bytes(int32_t batch, int32_t budget);
+qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
+                             const uint16_t* k_new, int64_t k_new_seq_stride,
+                             const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                             uint16_t* k_cache, const uint16_t* v_cache, int64_t kv_seq_stride,
+                             const uint16_t* kbar, int64_t kbar_seq_stride,
+                             const int32_t* q_pos, int32_t batch, int32_t budget,
+                             float softmax_scale, double rope_theta,
+                             float* scores, int64_t scores_seq_stride,
+                             int32_t* sel, int64_t sel_seq_stride,
+                             uint16_t* out, int64_t out_seq_stride, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

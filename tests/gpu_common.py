@@ -98,12 +98,11 @@ class DeviceDecode:
         self.sel = torch.empty((B, 1, wl.budget), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, 24, 256), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, 24), dtype=torch.float32, device=dev)
-        self.ws = qsa.decode_workspace(B, wl.budget)
-        self.q_rot = torch.empty_like(self.q_raw)
+        self.ws = qsa.decode_step_workspace(B, wl.budget)
 
     def run(self):
         qsa.decode_step(self.q_raw, self.k_new, self.q_idx, self.k_idx, self.k_cache, self.v_cache, self.kbar,
-                        self.pos, self.wl.budget, self.out, self.lse, self.scores, self.sel, self.ws, self.q_rot)
+                        self.pos, self.wl.budget, self.out, self.lse, self.scores, self.sel, self.ws)
         torch.cuda.synchronize()
 
 

@@ -1,0 +1,108 @@
+"""Fused fast paths against the primitive chain, bit for bit.
+
+The fused decode index-select and the one-call decode step must produce the
+same scores, selection, output and LSE bits as rope_apply + index_scores +
+select_topk + sparse_attn_decode on the same inputs, including score patterns
+that overflow the fused path's candidate capacity (exact fallback), and must
+leave their workspace zeroed for the next call.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_12_amd import inputs as I
+from block_sparse_long_12_amd import qsa
+from tests.gpu_common import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(shape, seed, sigma):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * sigma).to(torch.bfloat16)
+
+
+def _kbar(kind, B, nblk, seed):
+    if kind == "normal":
+        return _rand((B, nblk, 128), seed, 1 / math.sqrt(512))
+    if kind == "equal":          # every block scores the same: exact ties everywhere
+        row = _rand((1, 1, 128), seed, 1 / math.sqrt(512))
+        return row.expand(B, nblk, 128).contiguous()
+    if kind == "few_values":     # 5 distinct keys: huge tie groups at the threshold
+        rows = _rand((5, 128), seed, 1 / math.sqrt(512))
+        idx = torch.from_numpy(np.random.default_rng(seed).integers(0, 5, (B, nblk)))
+        return rows[idx]
+    raise ValueError(kind)
+
+
+CASES = [("normal", [1048576 // 16, 70001, 4096 + 3], 512), ("normal", [9000, 9001, 9002], 64),
+         ("equal", [40000, 40000, 40000], 512), ("few_values", [50000, 12345, 8000], 512),
+         ("normal", [100, 2047, 2048], 512), ("normal", [3, 50000, 7], 1), ("normal", [20000, 1, 20001], 2)]
+
+
+@pytest.mark.parametrize("kind,pos,budget", CASES, ids=[f"{k}-{p[0]}-{b}" for k, p, b in CASES])
+def test_index_select_decode_matches_primitives(kind, pos, budget):
+    say(f"index_select_decode {kind} pos={pos} budget={budget}")
+    B = len(pos)
+    nblk = max(1, max(pos) // 4)
+    q = _rand((B, 1, 4, 128), sum(pos), 1 / math.sqrt(128)).cuda()
+    kbar = _kbar(kind, B, nblk, budget).cuda()
+    ld = (nblk + 3) // 4 * 4
+    s_ref = torch.full((B, 1, ld), float("nan"), device="cuda")
+    sel_ref = torch.empty((B, 1, budget), dtype=torch.int32, device="cuda")
+    qsa.index_scores(q, kbar, pos, s_ref)
+    qsa.select_topk(s_ref, pos, budget, sel_ref)
+    ws = qsa.index_select_workspace(B)
+    for rep in range(2):                     # the second call reuses the workspace
+        s_f = torch.full((B, 1, ld), float("nan"), device="cuda")
+        sel_f = torch.empty((B, 1, budget), dtype=torch.int32, device="cuda")
+        qsa.index_select_decode(q, kbar, pos, budget, s_f, sel_f, ws)
+        torch.cuda.synchronize()
+        for b in range(B):
+            o = pos[b] // 4
+            assert torch.equal(s_f[b, 0, :o].view(torch.int32), s_ref[b, 0, :o].view(torch.int32)), (rep, b)
+        assert torch.equal(sel_f, sel_ref), rep
+        assert int(ws.count_nonzero()) == 0, "workspace not left zeroed"
+
+
+@pytest.mark.parametrize("ctx,budget,B", [(32768, 512, 8), (5001, 64, 3), (99, 512, 2)])
+def test_decode_step_matches_primitives(ctx, budget, B):
+    say(f"decode_step ctx={ctx} budget={budget} B={B}")
+    wl = I.custom_workload("decode", batch=B, ctx=ctx, tq=1, budget=budget, n_needles=2, seed=ctx)
+    x = I.make_inputs(wl)
+    dev = "cuda"
+
+    def caches():
+        kc = x.k.to(dev)
+        qsa.rope_apply(kc[:, :ctx], [0] * B)
+        ki = x.k_idx.to(dev)
+        kb = torch.zeros((B, max(1, (ctx + 1) // 4), 128), dtype=torch.bfloat16, device=dev)
+        if ctx // 4:
+            qsa.compress_block_keys(ki, 0, ctx // 4, kb)
+        return kc, ki, kb
+
+    ld = max(4, (ctx // 4 + 3) // 4 * 4)
+    outs = []
+    for fused in (False, True):
+        kc, ki, kb = caches()
+        v = x.v.to(dev)
+        scores = torch.full((B, 1, ld), float("nan"), device=dev)
+        sel = torch.empty((B, 1, budget), dtype=torch.int32, device=dev)
+        out = torch.empty((B, 24, 256), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, 24), dtype=torch.float32, device=dev)
+        q_raw, k_new, q_idx = x.q.to(dev), x.k[:, ctx:ctx + 1].contiguous().to(dev), x.q_idx.to(dev)
+        if fused:
+            ws = qsa.decode_step_workspace(B, budget)
+            for _ in range(2):
+                qsa.decode_step(q_raw, k_new, q_idx, ki, kc, v, kb, ctx, budget, out, lse, scores, sel, ws)
+        else:
+            ws = qsa.decode_workspace(B, budget)
+            qsa.decode_step_primitives(q_raw, k_new, q_idx, ki, kc, v, kb, ctx, budget, out, lse, scores, sel, ws,
+                                       torch.empty_like(q_raw))
+        torch.cuda.synchronize()
+        outs.append((kc[:, ctx].clone(), scores[:, 0, :ctx // 4].clone(), sel.clone(), out.clone(), lse.clone()))
+    for name, a, b in zip(("k row", "scores", "sel", "out", "lse"), outs[0], outs[1]):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
