@@ -12,8 +12,9 @@ under "decode".  Inputs are seeded synthetic tensors already resident in HBM.
 Timing: W untimed warm-up steps, then K steps between two device
 synchronisations; per-kernel durations come from HIP events recorded on the
 launch stream around every launch inside the timed steps.  Decode steps are
-timed one by one with a 1 GiB cache flush between them (outside the events),
-so the k-bar scan reads HBM rather than the 256 MB last-level cache.
+timed one by one after reading a 1 GiB buffer (outside the events), which
+leaves the 256 MB last-level cache full of clean, unrelated lines, so the
+k-bar scan reads HBM and pays no write-back of dirty lines.
 
 Rooflines (MI355X published peaks): HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s.
 `roofline` is the dominant prefill kernel (the sparse-attention gather);
@@ -362,14 +363,15 @@ def main():
         log(args, f"inputs {dwl.name}: {time.time() - t0:.1f}s")
         dd = Decode(dwl, dx, torch, qsa)
         del dx
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+
         for _ in range(3):
             dd.step(NullTimer())
         torch.cuda.synchronize()
         steps_ms = []
         dtimer = NullTimer()
         for _ in range(args.decode_steps):
-            flush.zero_()
+            flush.sum()
             s = torch.cuda.Event(enable_timing=True)
             e = torch.cuda.Event(enable_timing=True)
             s.record()
@@ -384,7 +386,7 @@ def main():
         sel_ws = qsa.index_select_workspace(dwl.batch)
         idx_ms = []
         for _ in range(args.decode_steps):
-            flush.zero_()
+            flush.sum()
             s = torch.cuda.Event(enable_timing=True)
             e = torch.cuda.Event(enable_timing=True)
             s.record()

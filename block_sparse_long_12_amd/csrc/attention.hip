@@ -62,8 +62,18 @@ __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ kg, cons
     const int lane = threadIdx.x & 63;
     const int c16 = lane & 15;
     const int G = lane >> 4;
-    const int slot_blk = cb + (c16 >> 2);
-    const int j = (slot_blk < blk_end) ? selrow[slot_blk] : -1;
+    // the chunk's 4 selection entries through wave-uniform (scalar) loads, so
+    // waiting for them never waits on the K/V gathers still in flight
+    const int cbu = __builtin_amdgcn_readfirstlane(cb);
+    const int endu = __builtin_amdgcn_readfirstlane(blk_end);
+    const int s0 = selrow[min(cbu + 0, endu - 1)];
+    const int s1 = selrow[min(cbu + 1, endu - 1)];
+    const int s2 = selrow[min(cbu + 2, endu - 1)];
+    const int s3 = selrow[min(cbu + 3, endu - 1)];
+    const int q4 = c16 >> 2;
+    const int slot_blk = cb + q4;
+    const int jl = (q4 == 0) ? s0 : (q4 == 1) ? s1 : (q4 == 2) ? s2 : s3;
+    const int j = (slot_blk < blk_end) ? jl : -1;
     const int n = kBlock * j + (c16 & 3);
     const bool valid = (j >= 0) && (j <= p / kBlock) && (n <= p);
     const int64_t row = valid ? n : p;
@@ -139,20 +149,32 @@ __device__ __forceinline__ void attend_chunk(const Chunk& ch, const bf16x8_t (&q
 
 // Attend over sel[blk_begin .. blk_end) for the query at position p.
 // kg / vg point at KV head g of the sequence (token stride 2 * 256).
+// `cur` must hold the loads of the first chunk (issued by the caller, so they
+// can overlap the query set-up).  Chunks are processed in statically unrolled
+// groups of kUnroll with two named buffers: inside a group the code is
+// straight-line, so each wait covers only the chunk about to be used and the
+// next chunk's rows stay in flight (a loop-carried pipeline makes the
+// compiler drain all loads at every loop head).  Steps past the end re-read
+// the last chunk's rows (cache hits) and are skipped.
+template <int kUnroll>
 __device__ __forceinline__ void attend_blocks(const uint16_t* __restrict__ kg,
                                               const uint16_t* __restrict__ vg,
                                               const int32_t* __restrict__ selrow, int blk_begin,
                                               int blk_end, int p, const bf16x8_t (&qf)[8],
-                                              float c, WaveState& st, uint16_t* vt) {
-    if (blk_begin >= blk_end) return;
-    Chunk cur;
-    load_chunk(kg, vg, selrow, blk_begin, blk_end, p, cur);
-    for (int cb = blk_begin; cb < blk_end; cb += 4) {
-        Chunk nxt;
-        const bool more = cb + 4 < blk_end;
-        if (more) load_chunk(kg, vg, selrow, cb + 4, blk_end, p, nxt);
-        if (cur.vmask != 0ull) attend_chunk(cur, qf, c, st, vt);
-        if (more) cur = nxt;
+                                              float c, WaveState& st, uint16_t* vt, Chunk& cur) {
+    const int last = blk_begin + (blk_end - 1 - blk_begin) / 4 * 4;      // first block of the last chunk
+    Chunk other;
+    for (int cb = blk_begin; cb < blk_end; cb += 4 * kUnroll) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; u += 2) {
+            const int c0 = cb + 4 * u;
+            const int c1 = c0 + 4;
+            const int c2 = c1 + 4;
+            load_chunk(kg, vg, selrow, min(c1, last), blk_end, p, other);
+            if (c0 < blk_end && cur.vmask != 0ull) attend_chunk(cur, qf, c, st, vt);
+            load_chunk(kg, vg, selrow, min(c2, last), blk_end, p, cur);
+            if (c1 < blk_end && other.vmask != 0ull) attend_chunk(other, qf, c, st, vt);
+        }
     }
 }
 
@@ -206,13 +228,17 @@ __global__ __launch_bounds__(128) void attn_prefill_kernel(
     const int head = g * kGroup + c16;
     const bool head_ok = c16 < kGroup;
 
+    const uint16_t* kg = k + b * kvs + g * kD;
+    const uint16_t* vg = v + b * kvs + g * kD;
+    const int32_t* selrow = sel + b * sels + static_cast<int64_t>(i) * budget;
+    Chunk first;
+    load_chunk(kg, vg, selrow, 0, budget, p, first);
     bf16x8_t qf[8];
     const uint16_t* qrow = q + b * qs + static_cast<int64_t>(i) * (kHq * kD);
     load_q_frags(qrow + (head_ok ? head : 0) * kD, head_ok, p, rope_q ? &inv : nullptr, qf);
     WaveState st;
     init_state(st);
-    attend_blocks(k + b * kvs + g * kD, v + b * kvs + g * kD, sel + b * sels + static_cast<int64_t>(i) * budget,
-                  0, budget, p, qf, c, st, vt_all + g * kVtElems);
+    attend_blocks<8>(kg, vg, selrow, 0, budget, p, qf, c, st, vt_all + g * kVtElems, first);
 
     if (head_ok) {
         const float inv_l = 1.f / st.l;
@@ -248,7 +274,7 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
 // Split the budget over n_split workgroups per sequence; each writes the
 // partial (reference max, sum, unnormalised O) of its blocks for the 24 heads.
 static void decode_split(int batch, int budget, int* n_split, int* bps) {
-    int s = 128 / (batch > 0 ? batch : 1);
+    int s = 256 / (batch > 0 ? batch : 1);
     if (s < 1) s = 1;
     if (s > 64) s = 64;
     const int max_s = (budget + 3) / 4;
@@ -281,14 +307,17 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     const int head = g * kGroup + c16;
     const bool head_ok = c16 < kGroup;
 
+    const int blk_begin = s * bps;
+    const int blk_end = min(budget, blk_begin + bps);
+    const uint16_t* kg = k + b * kvs + g * kD;
+    const uint16_t* vg = v + b * kvs + g * kD;
+    Chunk first;
+    load_chunk(kg, vg, sel + b * sels, blk_begin, blk_end, p, first);
     bf16x8_t qf[8];
     load_q_frags(q + b * qs + (head_ok ? head : 0) * kD, head_ok, p, rope_q ? &inv : nullptr, qf);
     WaveState st;
     init_state(st);
-    const int blk_begin = s * bps;
-    const int blk_end = min(budget, blk_begin + bps);
-    attend_blocks(k + b * kvs + g * kD, v + b * kvs + g * kD, sel + b * sels, blk_begin, blk_end, p,
-                  qf, c, st, vt_all + g * kVtElems);
+    attend_blocks<2>(kg, vg, sel + b * sels, blk_begin, blk_end, p, qf, c, st, vt_all + g * kVtElems, first);
     if (head_ok) {
         const int64_t idx = (static_cast<int64_t>(b) * n_split + s) * kHq + head;
         if (G == 0) {
@@ -302,42 +331,75 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     }
 }
 
-// One wave per (sequence, head): lane s reads split s's (max, sum), the wave
-// forms the merge weights, then every lane merges 4 dims over the splits.
-__global__ __launch_bounds__(64) void attn_decode_combine_kernel(
+// One workgroup of 256 threads per (sequence, head): thread t merges dims
+// 4*(t%64) .. +3 over the splits s = t/64 + 4k, with all its loads issued
+// before any is used; the 4 partial sums meet in LDS.
+__global__ __launch_bounds__(256) void attn_decode_combine_kernel(
     const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, int n_split, float scale,
     float c, uint16_t* __restrict__ out, int64_t os, float* __restrict__ lse) {
-    const int lane = threadIdx.x;
+    __shared__ float w_s[64];
+    __shared__ float4 part[3][64];
+    __shared__ float sh_M, sh_L;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int quarter = tid >> 6;
     const int b = blockIdx.x / kHq;
     const int h = blockIdx.x % kHq;
     const int64_t base = static_cast<int64_t>(b) * n_split * kHq + h;    // split s at base + s * kHq
-    float m = -INFINITY, l = 0.f;
-    if (lane < n_split) {
-        m = ws_ml[2 * (base + static_cast<int64_t>(lane) * kHq)];
-        l = ws_ml[2 * (base + static_cast<int64_t>(lane) * kHq) + 1];
+    if (quarter == 0) {
+        float m = -INFINITY, l = 0.f;
+        if (lane < n_split) {
+            m = ws_ml[2 * (base + static_cast<int64_t>(lane) * kHq)];
+            l = ws_ml[2 * (base + static_cast<int64_t>(lane) * kHq) + 1];
+        }
+        float M = m;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        const float w = (m == -INFINITY) ? 0.f : exp2f((m - M) * c);
+        float L = w * l;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+        w_s[lane] = w;
+        if (lane == 0) {
+            sh_M = M;
+            sh_L = L;
+        }
     }
-    float M = m;
+    float4 a[16];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float w = (m == -INFINITY) ? 0.f : exp2f((m - M) * c);
-    float L = w * l;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    for (int k = 0; k < 16; ++k) {
+        const int s = quarter + 4 * k;
+        a[k] = (s < n_split) ? *reinterpret_cast<const float4*>(ws_acc + (base + static_cast<int64_t>(s) * kHq) * kD + 4 * lane)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < n_split; ++s) {
-        const float ws = __shfl(w, s);
-        const float4 a = *reinterpret_cast<const float4*>(ws_acc + (base + static_cast<int64_t>(s) * kHq) * kD + 4 * lane);
-        acc.x += ws * a.x;
-        acc.y += ws * a.y;
-        acc.z += ws * a.z;
-        acc.w += ws * a.w;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int s = quarter + 4 * k;
+        const float ws = (s < n_split) ? w_s[s] : 0.f;
+        acc.x += ws * a[k].x;
+        acc.y += ws * a[k].y;
+        acc.z += ws * a[k].z;
+        acc.w += ws * a[k].w;
     }
-    const float inv = 1.f / L;
-    uint2 o;
-    o.x = f32_to_bf16(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
-    o.y = f32_to_bf16(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
-    *reinterpret_cast<uint2*>(out + b * os + h * kD + 4 * lane) = o;
-    if (lse != nullptr && lane == 0) lse[static_cast<int64_t>(b) * kHq + h] = M * scale + logf(L);
+    if (quarter > 0) part[quarter - 1][lane] = acc;
+    __syncthreads();
+    if (quarter == 0) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            acc.x += part[q][lane].x;
+            acc.y += part[q][lane].y;
+            acc.z += part[q][lane].z;
+            acc.w += part[q][lane].w;
+        }
+        const float inv = 1.f / sh_L;
+        uint2 o;
+        o.x = f32_to_bf16(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
+        o.y = f32_to_bf16(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
+        *reinterpret_cast<uint2*>(out + b * os + h * kD + 4 * lane) = o;
+        if (lse != nullptr && lane == 0) lse[static_cast<int64_t>(b) * kHq + h] = sh_M * scale + logf(sh_L);
+    }
 }
 
 hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* k,
@@ -357,7 +419,7 @@ hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* 
                        c, ws_ml, ws_acc, inv, rope_theta > 0.0 ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(static_cast<unsigned>(batch * kHq)), dim3(64),
+    hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(static_cast<unsigned>(batch * kHq)), dim3(256),
                        0, stream, ws_ml, ws_acc, n_split, scale, c, out, os, lse);
     return hipGetLastError();
 }

@@ -1,29 +1,29 @@
 // Fused index-select for decode rows (one query token per sequence, up to
 // 262144 candidate blocks): the same scores and the same selection as
-// index_scores_kernel followed by select_kernel, in two launches that spread
-// each row over hundreds of workgroups.
+// index_scores_kernel followed by select_kernel, spread over hundreds of
+// workgroups per row.  Three launches; every hand-off between workgroups
+// goes through a kernel boundary or a device-scope atomic, never through an
+// in-kernel fence (an agent-scope fence writes back and invalidates the L2 of
+// the XCD, which costs microseconds per workgroup on this part):
 //
-//  decode_scan_kernel     B x G workgroups.  Scores every candidate block with
-//                         the shared MFMA block_score (bit-identical to the
-//                         index_scores path), stores them, and counts the top
-//                         12 bits of each ordered key in an LDS histogram that
-//                         is added to a per-sequence global histogram.  The
-//                         last workgroup of a sequence to finish (ticket
-//                         counter) finds the bin holding the threshold and
-//                         clears the global histogram.  Optionally it also
-//                         rotates the new K row into the cache (step 0).
-//  decode_filter_kernel   B x F workgroups over the stored scores: keys above
-//                         the threshold bin are appended to a list of winners,
-//                         keys in the bin to a candidate list (wave-aggregated
-//                         atomics).  The last workgroup of a sequence sorts the
-//                         candidates in LDS, takes the ones still needed,
-//                         merges, sorts ascending and writes sel; if the bin
-//                         overflows LDS it runs the full radix select on the
-//                         stored row instead.  It leaves the control words
-//                         zeroed for the next call.
-// Cross-workgroup hand-off uses the release/acquire pattern: results, then
-// __threadfence(), then the ticket atomic; the last workgroup fences again
-// before reading.  No workgroup ever waits on another, so nothing can hang.
+//  decode_scan_kernel      B x G workgroups, long-lived waves that stream
+//                          64-block groups with the next group's loads in
+//                          flight.  Scores every candidate with the shared MFMA
+//                          block_score (bit-identical to index_scores_kernel),
+//                          stores the scores, counts the top 12 bits of each
+//                          ordered key in an LDS histogram and adds it to a
+//                          per-sequence global histogram.  Optionally rotates
+//                          the new K row into the cache (step 0).
+//  decode_filter_kernel    B x F workgroups: each finds the threshold bin from
+//                          the global histogram, then collects its slice's keys
+//                          above the bin (winners) and in the bin (candidates)
+//                          in LDS and appends them to per-sequence lists with
+//                          one atomic reservation per list.
+//  decode_finalize_kernel  B workgroups: sorts the candidates, takes the ones
+//                          still needed, merges, sorts ascending and writes sel;
+//                          if the bin overflowed the list it runs the full radix
+//                          select on the stored row.  Leaves the histogram and
+//                          counters zeroed for the next call.
 #include "index_common.h"
 #include "rope_common.h"
 #include "select_common.h"
@@ -63,18 +63,16 @@ static DecodeWs carve(void* ws, int batch) {
     return w;
 }
 
+template <int STEPS>
 __global__ __launch_bounds__(256) void decode_scan_kernel(
     const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
-    Positions pos, int budget, int wg_per_seq, int blocks_per_wg, float* __restrict__ scores,
+    Positions pos, int budget, int wg_per_seq, float* __restrict__ scores,
     int64_t ss, DecodeWs ws, const uint16_t* __restrict__ k_new, int64_t kns,
     uint16_t* __restrict__ k_cache, int64_t kcs, InvFreq inv, int rope_k) {
     __shared__ uint32_t hist[kDecHistBins];
-    __shared__ int wave_tot[4];
-    __shared__ uint32_t sh_bin;
-    __shared__ int sh_above, sh_last;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // scalar: loop control stays uniform
     const int b = blockIdx.x / wg_per_seq;
     const int g = blockIdx.x % wg_per_seq;
     const int p = pos.p[b];
@@ -95,12 +93,12 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     load_index_a(q_idx + b * qs, 0, 1, a);
     const uint16_t* kb = kbar + b * kbs;
     float* sb = scores + b * ss;
-    const int j_lo = g * blocks_per_wg;
-    const int j_hi = min(o, j_lo + blocks_per_wg);
-    for (int j0 = j_lo + wave * 64; j0 < j_hi; j0 += 256) {
-        bf16x8_t bf[4][4];
-#pragma unroll
-        for (int n = 0; n < 4; ++n) load_index_b(kb, j0, n, j_hi, bf[n]);
+    const int j_lo = g * (256 * STEPS);
+    const int j_hi = min(o, j_lo + 256 * STEPS);
+    // two named buffers, loop unrolled by two: one group computes while the
+    // next is in flight (the next-group address is clamped, never skipped)
+    auto step_of = [&](int j) { return (j < j_hi) ? j : (j_hi - 1) / 64 * 64; };
+    auto score_group = [&](const bf16x8_t (&bf)[4][4], int j0) {
         float s[4];
 #pragma unroll
         for (int n = 0; n < 4; ++n) s[n] = block_score(a, bf[n]);
@@ -113,55 +111,46 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
                     if (jj + n < j_hi) atomicAdd(&hist[score_key(s[n]) >> kDecShift], 1u);
             }
         }
-    }
-    __syncthreads();
-    if (need_hist) {
-        for (int k = tid; k < kDecHistBins; k += 256) {
-            const uint32_t v = hist[k];
-            if (v) atomicAdd(&ws.hist[static_cast<int64_t>(b) * kDecHistBins + k], v);
+    };
+    // STEPS groups of 64 blocks per wave (stride 256 over the workgroup's
+    // range), fully unrolled: straight-line code lets every wait count only
+    // the loads it needs, so the next group is always in flight
+    const int j0 = j_lo + wave * 64;
+    if (j0 < j_hi) {
+        bf16x8_t buf[2][4][4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) load_index_b(kb, j0, n, j_hi, buf[0][n]);
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            if (st + 1 < STEPS) {
+#pragma unroll
+                for (int n = 0; n < 4; ++n) load_index_b(kb, step_of(j0 + 256 * (st + 1)), n, j_hi, buf[(st + 1) & 1][n]);
+            }
+            if (j0 + 256 * st < j_hi) score_group(buf[st & 1], j0 + 256 * st);
         }
     }
-    __threadfence();
+    if (!need_hist) return;
     __syncthreads();
-    uint32_t* ctrl = ws.ctrl + b * kCtrl;
-    if (tid == 0) sh_last = atomicAdd(&ctrl[kDoneScan], 1u) == static_cast<uint32_t>(wg_per_seq - 1);
-    __syncthreads();
-    if (!sh_last) return;
-    __threadfence();
-    if (need_hist) {
-        for (int k = tid; k < kDecHistBins; k += 256)
-            hist[k] = atomicExch(&ws.hist[static_cast<int64_t>(b) * kDecHistBins + k], 0u);
-        __syncthreads();
-        find_threshold_bin<256>(hist, kDecHistBins, keep, wave_tot, &sh_bin, &sh_above);
-        if (tid == 0) {
-            ctrl[kBin] = sh_bin;
-            ctrl[kAbove] = static_cast<uint32_t>(sh_above);
-            ctrl[kInBin] = hist[sh_bin];
-        }
+    for (int k = tid; k < kDecHistBins; k += 256) {
+        const uint32_t v = hist[k];
+        if (v) atomicAdd(&ws.hist[static_cast<int64_t>(b) * kDecHistBins + k], v);
     }
-    if (tid == 0) ctrl[kDoneScan] = 0;
-}
-
-__device__ __forceinline__ void wave_append(uint32_t* counter, bool pred, uint32_t* off_out) {
-    const uint64_t m = __ballot(pred);
-    const int lane = threadIdx.x & 63;
-    uint32_t base = 0;
-    if (m != 0) {
-        if (lane == 0) base = atomicAdd(counter, static_cast<uint32_t>(__popcll(m)));
-        base = __shfl(base, 0);
-    }
-    *off_out = base + static_cast<uint32_t>(__popcll(m & ((1ull << lane) - 1ull)));
 }
 
 struct FilterSmem {
-    SelectSmem s;
+    uint32_t hist[kDecHistBins];
+    int32_t def[QSA_MAX_BUDGET];
     uint64_t cand[kDecCap];
-    int sh_last;
+    int wave_tot[4];
+    uint32_t sh_bin;
+    int sh_above, n_def, n_cand, base_def, base_cand;
 };
+
+constexpr int kFiltPer = 4096;      // scores per filter workgroup: 4 float4 per thread
 
 __global__ __launch_bounds__(256) void decode_filter_kernel(
     const float* __restrict__ scores, int64_t ss, Positions pos, int budget, int wg_per_seq,
-    int per_wg, DecodeWs ws, int32_t* __restrict__ sel, int64_t sels) {
+    DecodeWs ws) {
     __shared__ FilterSmem sm;
     const int tid = threadIdx.x;
     const int b = blockIdx.x / wg_per_seq;
@@ -169,75 +158,200 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(
     const int p = pos.p[b];
     const int o = p / kBlock;
     const int keep = min(budget - 1, o);
-    const bool nontrivial = keep > 0 && keep < o;
+    if (!(keep > 0 && keep < o)) return;                 // trivial rows need no filter
     uint32_t* ctrl = ws.ctrl + b * kCtrl;
-    const float* row = scores + b * ss;
-    int32_t* out = sel + b * sels;
 
-    if (nontrivial) {
-        const uint32_t tbin = ctrl[kBin];
-        int32_t* defl = ws.defl + static_cast<int64_t>(b) * QSA_MAX_BUDGET;
-        uint64_t* cand = ws.cand + static_cast<int64_t>(b) * kDecCap;
-        const int j_lo = g * per_wg;
-        const int j_hi = min(o, j_lo + per_wg);
-        for (int base = j_lo; base < j_hi; base += 4 * 256) {      // uniform trip count
-            const int j4 = base + 4 * tid;
-            const bool in = j4 < j_hi;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (in) v = *reinterpret_cast<const float4*>(row + j4);
-            const float f[4] = {v.x, v.y, v.z, v.w};
+    // this workgroup's scores first (independent of the threshold), 4 float4 per thread
+    const float* row = scores + b * ss;
+    const int j_lo = g * kFiltPer;
+    const int j_hi = min(o, j_lo + kFiltPer);
+    float4 v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = j4 + e;
-                const bool valid = in && j < j_hi;
-                const uint32_t key = score_key(f[e]);
-                const uint32_t bin = key >> kDecShift;
-                const bool is_def = valid && bin > tbin;
-                const bool is_cand = valid && bin == tbin;
-                uint32_t off;
-                wave_append(&ctrl[kNDef], is_def, &off);
-                if (is_def && off < static_cast<uint32_t>(QSA_MAX_BUDGET)) defl[off] = j;
-                wave_append(&ctrl[kNCand], is_cand, &off);
-                if (is_cand && off < static_cast<uint32_t>(kDecCap))
-                    cand[off] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~j);
+    for (int it = 0; it < 4; ++it) {
+        const int j4 = min(j_lo + 4 * tid + 1024 * it, (o - 1) & ~3);   // clamped: always a legal load
+        v[it] = *reinterpret_cast<const float4*>(row + j4);
+    }
+
+    // the threshold bin, from the global histogram the scan completed
+    const uint32_t* gh = ws.hist + static_cast<int64_t>(b) * kDecHistBins;
+    for (int k = tid; k < kDecHistBins; k += 256) sm.hist[k] = gh[k];
+    if (tid == 0) {
+        sm.n_def = 0;
+        sm.n_cand = 0;
+    }
+    __syncthreads();
+    find_threshold_bin<256>(sm.hist, kDecHistBins, keep, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
+    const uint32_t tbin = sm.sh_bin;
+    if (g == 0 && tid == 0) {
+        ctrl[kBin] = tbin;
+        ctrl[kAbove] = static_cast<uint32_t>(sm.sh_above);
+        ctrl[kInBin] = sm.hist[tbin];
+    }
+
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int j4 = j_lo + 4 * tid + 1024 * it;
+        const float f[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = j4 + e;
+            if (j >= j_hi) continue;
+            const uint32_t key = score_key(f[e]);
+            const uint32_t bin = key >> kDecShift;
+            if (bin > tbin) {
+                const int k = atomicAdd(&sm.n_def, 1);
+                if (k < QSA_MAX_BUDGET) sm.def[k] = j;
+            } else if (bin == tbin) {
+                const int k = atomicAdd(&sm.n_cand, 1);
+                if (k < kDecCap) sm.cand[k] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~j);
             }
         }
     }
-    __threadfence();
     __syncthreads();
-    if (tid == 0) sm.sh_last = atomicAdd(&ctrl[kDoneFilter], 1u) == static_cast<uint32_t>(wg_per_seq - 1);
-    __syncthreads();
-    if (!sm.sh_last) return;
-    __threadfence();
-
-    if (!nontrivial) {
-        trivial_selection(keep, o, budget, out, 256);
-    } else {
-        const int above = static_cast<int>(ctrl[kAbove]);
-        const int inbin = static_cast<int>(ctrl[kInBin]);
-        const int remaining = keep - above;
-        if (inbin <= kDecCap) {
-            const int32_t* defl = ws.defl + static_cast<int64_t>(b) * QSA_MAX_BUDGET;
-            const uint64_t* cand = ws.cand + static_cast<int64_t>(b) * kDecCap;
-            for (int k = tid; k < above; k += 256) sm.s.chosen[k] = defl[k];
-            const int np2 = next_pow2(inbin);
-            for (int k = tid; k < np2; k += 256) sm.cand[k] = (k < inbin) ? cand[k] : 0ull;
-            __syncthreads();
-            bitonic_sort<256, uint64_t, true>(sm.cand, np2);
-            for (int k = tid; k < remaining; k += 256)
-                sm.s.chosen[above + k] = static_cast<int32_t>(~static_cast<uint32_t>(sm.cand[k]));
-            __syncthreads();
-            write_selection<256>(sm.s, keep, o, budget, out);
-        } else {
-            select_row<256>(row, o, keep, budget, out, sm.s);
-        }
-    }
-    __syncthreads();
+    const int nd = min(sm.n_def, QSA_MAX_BUDGET);
+    const int nc = sm.n_cand;
     if (tid == 0) {
-        ctrl[kNDef] = 0;
-        ctrl[kNCand] = 0;
-        ctrl[kDoneFilter] = 0;
+        sm.base_def = nd ? static_cast<int>(atomicAdd(&ctrl[kNDef], static_cast<uint32_t>(nd))) : 0;
+        sm.base_cand = nc ? static_cast<int>(atomicAdd(&ctrl[kNCand], static_cast<uint32_t>(nc))) : 0;
     }
+    __syncthreads();
+    int32_t* defl = ws.defl + static_cast<int64_t>(b) * QSA_MAX_BUDGET;
+    uint64_t* cand = ws.cand + static_cast<int64_t>(b) * kDecCap;
+    for (int k = tid; k < nd; k += 256)
+        if (sm.base_def + k < QSA_MAX_BUDGET) defl[sm.base_def + k] = sm.def[k];
+    for (int k = tid; k < min(nc, kDecCap); k += 256)
+        if (sm.base_cand + k < kDecCap) cand[sm.base_cand + k] = sm.cand[k];
+}
+
+constexpr int kFinNT = 1024;                 // finalize threads
+constexpr int kBitmapWords = 8192;           // ascending order by bitmap for blocks < 262144
+
+struct FinalizeSmem {
+    union {
+        SelectSmem s;                                        // overflow: full radix select
+        struct {
+            uint32_t bm[kBitmapWords];                       // one bit per candidate block
+            alignas(16) int32_t chosen[QSA_MAX_BUDGET];      // selection, any order
+            alignas(16) uint64_t cand[kDecCap];              // threshold-bin candidates
+            uint32_t h2[kDecHistBins];                       // second radix level over them
+            alignas(16) uint64_t sub[kDecCap];               // members of the cut sub-bin
+            int wave_tot[16];
+            uint32_t sh_bin;
+            int sh_above, n_taken, n_sub;
+        } m;
+    } u;
+};
+
+__global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __restrict__ scores, int64_t ss,
+                                                                 Positions pos, int budget, DecodeWs ws,
+                                                                 int32_t* __restrict__ sel, int64_t sels) {
+    __shared__ FinalizeSmem sm;
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    const int p = pos.p[b];
+    const int o = p / kBlock;
+    const int keep = min(budget - 1, o);
+    int32_t* out = sel + b * sels;
+    uint32_t* ctrl = ws.ctrl + b * kCtrl;
+    if (trivial_selection(keep, o, budget, out, kFinNT)) return;   // nothing was accumulated
+
+    const int above = static_cast<int>(ctrl[kAbove]);
+    const int inbin = static_cast<int>(ctrl[kInBin]);
+    const int remaining = keep - above;
+    if (inbin > kDecCap) {
+        select_row<kFinNT>(scores + b * ss, o, keep, budget, out, sm.u.s);
+    } else {
+        const int32_t* __restrict__ defl = ws.defl + static_cast<int64_t>(b) * QSA_MAX_BUDGET;
+        const uint64_t* __restrict__ cg = ws.cand + static_cast<int64_t>(b) * kDecCap;
+        int32_t* chosen = sm.u.m.chosen;
+        const bool bitmap = o <= 32 * kBitmapWords;
+        if (bitmap)
+            for (int k = tid; k < kBitmapWords; k += kFinNT) sm.u.m.bm[k] = 0u;
+        for (int k = tid; k < above; k += kFinNT) chosen[k] = defl[k];
+        if (tid == 0) chosen[keep] = o;
+        // candidates of the threshold bin share the top 12 key bits: a second
+        // radix level on the next 12 bits (LDS histogram) splits them into
+        // those surely taken, the few in the sub-bin holding the cut, and the rest
+        uint64_t* lc = sm.u.m.cand;
+        uint32_t* h2 = sm.u.m.h2;
+        for (int k = tid; k < kDecHistBins; k += kFinNT) h2[k] = 0u;
+        for (int k = tid; k < inbin; k += kFinNT) lc[k] = cg[k];
+        if (tid == 0) sm.u.m.n_taken = 0;
+        __syncthreads();
+        for (int k = tid; k < inbin; k += kFinNT)
+            atomicAdd(&h2[static_cast<uint32_t>(lc[k] >> 40) & (kDecHistBins - 1)], 1u);
+        __syncthreads();
+        find_threshold_bin<kFinNT>(h2, kDecHistBins, remaining, sm.u.m.wave_tot, &sm.u.m.sh_bin, &sm.u.m.sh_above);
+        const uint32_t t2 = sm.u.m.sh_bin;
+        const int above2 = sm.u.m.sh_above;                   // taken outright
+        const int need2 = remaining - above2;                 // still to take from sub-bin t2
+        // members of the cut sub-bin go to a short list; the rest are decided here
+        uint64_t* sub = sm.u.m.sub;
+        if (tid == 0) sm.u.m.n_sub = 0;
+        __syncthreads();
+        for (int i = tid; i < inbin; i += kFinNT) {
+            const uint64_t x = lc[i];
+            const uint32_t d2 = static_cast<uint32_t>(x >> 40) & (kDecHistBins - 1);
+            if (d2 > t2)
+                chosen[above + atomicAdd(&sm.u.m.n_taken, 1)] = static_cast<int32_t>(~static_cast<uint32_t>(x));
+            else if (d2 == t2)
+                sub[atomicAdd(&sm.u.m.n_sub, 1)] = x;
+        }
+        __syncthreads();
+        const int n_sub = sm.u.m.n_sub;
+        int32_t* dst = chosen + above + above2;
+        if (n_sub <= 256) {
+            // rank among the few members of the sub-bin: full key, then index
+            for (int i = tid; i < n_sub; i += kFinNT) {
+                const uint64_t x = sub[i];
+                int r = 0;
+#pragma unroll 8
+                for (int k = 0; k < n_sub; ++k) r += sub[k] > x ? 1 : 0;
+                if (r < need2) dst[r] = static_cast<int32_t>(~static_cast<uint32_t>(x));
+            }
+        } else {
+            const int np2 = next_pow2(n_sub);
+            for (int k = n_sub + tid; k < np2; k += kFinNT) sub[k] = 0ull;
+            __syncthreads();
+            bitonic_sort<kFinNT, uint64_t, true>(sub, np2);
+            for (int k = tid; k < need2; k += kFinNT) dst[k] = static_cast<int32_t>(~static_cast<uint32_t>(sub[k]));
+        }
+        __syncthreads();
+        if (bitmap) {
+            for (int k = tid; k <= keep; k += kFinNT) {
+                const int v = chosen[k];
+                atomicOr(&sm.u.m.bm[v >> 5], 1u << (v & 31));
+            }
+            __syncthreads();
+            // thread t owns words 8t .. 8t+7: prefix count of set bits, then emit in order
+            constexpr int kWpt = kBitmapWords / kFinNT;
+            uint32_t w[kWpt];
+            int cnt = 0;
+#pragma unroll
+            for (int q = 0; q < kWpt; ++q) {
+                w[q] = sm.u.m.bm[kWpt * tid + q];
+                cnt += __popc(w[q]);
+            }
+            int total;
+            int base = block_exclusive_scan<kFinNT>(cnt, sm.u.m.wave_tot, &total);
+#pragma unroll
+            for (int q = 0; q < kWpt; ++q) {
+                uint32_t bits = w[q];
+                while (bits) {
+                    const int bit = __ffs(bits) - 1;
+                    out[base++] = 32 * (kWpt * tid + q) + bit;
+                    bits &= bits - 1;
+                }
+            }
+        } else {
+            rank_write_ascending<kFinNT>(chosen, keep + 1, out);
+        }
+        for (int k = keep + 1 + tid; k < budget; k += kFinNT) out[k] = -1;
+    }
+    __syncthreads();
+    uint32_t* gh = ws.hist + static_cast<int64_t>(b) * kDecHistBins;
+    for (int k = tid; k < kDecHistBins; k += kFinNT) gh[k] = 0u;
+    if (tid < kCtrl) ctrl[tid] = 0u;
 }
 
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
@@ -247,26 +361,44 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
                                       int64_t kcs, double rope_theta, hipStream_t stream) {
     int o_max = 0;
     for (int b = 0; b < batch; ++b) o_max = max(o_max, pos.p[b] / kBlock);
-    // scan: ~1024 workgroups in total, ranges in whole 256-block steps
-    int wg_scan = max(1, min((o_max + 255) / 256, (1024 + batch - 1) / batch));
-    int per_scan = ((o_max + wg_scan - 1) / wg_scan + 255) / 256 * 256;
-    if (per_scan == 0) per_scan = 256;
-    wg_scan = max(1, (o_max + per_scan - 1) / per_scan);
-    // filter: up to 64 workgroups per sequence, ranges in whole 1024-score steps
-    int wg_filt = max(1, min((o_max + 4095) / 4096, 64));
-    int per_filt = ((o_max + wg_filt - 1) / wg_filt + 1023) / 1024 * 1024;
-    if (per_filt == 0) per_filt = 1024;
-    wg_filt = max(1, (o_max + per_filt - 1) / per_filt);
+    // scan: 256 * STEPS blocks per workgroup; STEPS is the largest of 8, 4, 2, 1
+    // that still gives about 2 workgroups per CU
+    const int64_t groups = static_cast<int64_t>(batch) * ((o_max + 255) / 256);
+    const int steps = groups >= 8 * 512 ? 8 : groups >= 4 * 512 ? 4 : groups >= 2 * 512 ? 2 : 1;
+    const int wg_scan = max(1, (o_max + 256 * steps - 1) / (256 * steps));
+    // filter: kFiltPer scores per workgroup
+    const int wg_filt = max(1, (o_max + kFiltPer - 1) / kFiltPer);
 
     const DecodeWs w = carve(ws, batch);
     const InvFreq inv = make_inv_freq(rope_theta > 0.0 ? rope_theta : 1.0e7);
-    hipLaunchKernelGGL(decode_scan_kernel, dim3(static_cast<unsigned>(batch * wg_scan)), dim3(256), 0, stream,
-                       q_idx, qs, kbar, kbs, pos, budget, wg_scan, per_scan, scores, ss, w, k_new, kns,
-                       k_cache, kcs, inv, (rope_theta > 0.0 && k_new != nullptr) ? 1 : 0);
+    const int rope_k = (rope_theta > 0.0 && k_new != nullptr) ? 1 : 0;
+    const dim3 grid(static_cast<unsigned>(batch * wg_scan));
+    switch (steps) {
+        case 8:
+            hipLaunchKernelGGL(decode_scan_kernel<8>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
+                               wg_scan, scores, ss, w, k_new, kns, k_cache, kcs, inv, rope_k);
+            break;
+        case 4:
+            hipLaunchKernelGGL(decode_scan_kernel<4>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
+                               wg_scan, scores, ss, w, k_new, kns, k_cache, kcs, inv, rope_k);
+            break;
+        case 2:
+            hipLaunchKernelGGL(decode_scan_kernel<2>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
+                               wg_scan, scores, ss, w, k_new, kns, k_cache, kcs, inv, rope_k);
+            break;
+        default:
+            hipLaunchKernelGGL(decode_scan_kernel<1>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
+                               wg_scan, scores, ss, w, k_new, kns, k_cache, kcs, inv, rope_k);
+            break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_filter_kernel, dim3(static_cast<unsigned>(batch * wg_filt)), dim3(256), 0,
-                       stream, scores, ss, pos, budget, wg_filt, per_filt, w, sel, sels);
+                       stream, scores, ss, pos, budget, wg_filt, w);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_finalize_kernel, dim3(static_cast<unsigned>(batch)), dim3(kFinNT), 0, stream,
+                       scores, ss, pos, budget, w, sel, sels);
     return hipGetLastError();
 }
 

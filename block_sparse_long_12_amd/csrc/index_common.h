@@ -35,18 +35,18 @@ __device__ __forceinline__ void load_index_a(const uint16_t* qb, int tok0, int n
 }
 
 // B operand of column tile n for the 64 blocks starting at j0: lane column
-// c16 is block j0 + 4 * c16 + n; blocks at or past j_end read as zero.
+// c16 is block j0 + 4 * c16 + n.  Columns at or past j_end (>= 1) read block
+// j_end - 1 instead, so every load is issued unconditionally (the loop stays
+// branch-free and the next step's loads can stay in flight); their scores
+// land only where the result is unspecified and are never used.
 __device__ __forceinline__ void load_index_b(const uint16_t* kb, int j0, int n, int j_end, bf16x8_t (&b)[4]) {
     const int lane = threadIdx.x & 63;
     const int c16 = lane & 15;
     const int G = lane >> 4;
-    const int j = j0 + 4 * c16 + n;
+    const int j = min(j0 + 4 * c16 + n, j_end - 1);
     const uint16_t* kr = kb + static_cast<int64_t>(j) * kDi + 8 * G;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        if (j < j_end) b[ks] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * ks);
-        else b[ks] = bf16x8_t{};
-    }
+    for (int ks = 0; ks < 4; ++ks) b[ks] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * ks);
 }
 
 }  // namespace qsa

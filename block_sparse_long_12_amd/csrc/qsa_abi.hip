@@ -299,7 +299,8 @@ static qsa_status_t check_index_select_decode(const uint16_t* q_idx, int64_t q_i
         for (int b = 0; b < batch; ++b) o_max = p.p[b] / qsa::kBlock > o_max ? p.p[b] / qsa::kBlock : o_max;
         CHECK(stride_ok(q_idx_seq_stride) && q_idx_seq_stride >= qsa::kHi * qsa::kDi, "q_idx_seq_stride too small");
         CHECK(stride_ok(kbar_seq_stride) && kbar_seq_stride >= o_max * qsa::kDi, "kbar_seq_stride too small");
-        CHECK(scores_seq_stride % 4 == 0 && scores_seq_stride >= o_max, "scores_seq_stride must be a multiple of 4 and >= q_pos / 4");
+        CHECK(scores_seq_stride % 4 == 0 && scores_seq_stride >= (o_max + 3) / 4 * 4,
+              "scores_seq_stride must be a multiple of 4 and >= q_pos / 4 rounded up to 4");
         CHECK(sel_seq_stride >= budget, "sel_seq_stride < budget");
     }
     return QSA_OK;

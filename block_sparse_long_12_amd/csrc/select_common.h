@@ -29,8 +29,8 @@ constexpr int kSelectCap = 2048;     // threshold-bin members held in LDS
 
 struct SelectSmem {
     uint32_t hist[2048];
-    uint64_t cand[kSelectCap];
-    int32_t chosen[QSA_MAX_BUDGET];
+    alignas(16) uint64_t cand[kSelectCap];
+    alignas(16) int32_t chosen[QSA_MAX_BUDGET];
     int wave_tot[16];
     int n_chosen, n_cand, sh_above;
     uint32_t sh_bin;
@@ -128,6 +128,51 @@ __device__ __forceinline__ void write_selection(SelectSmem& sm, int keep, int o,
     __syncthreads();
     bitonic_sort<NT, int32_t, false>(sm.chosen, np2);
     for (int k = tid; k < budget; k += NT) out[k] = (k < nsel) ? sm.chosen[k] : -1;
+}
+
+// The `take` largest of cand[0 .. n) (distinct keys) by counting: entry i
+// goes to dst[rank_i] (as the block index ~key) when rank_i < take, so dst
+// ends in descending key order.  cand must be 16-byte aligned with room for
+// an even count; the odd tail is padded with 0 (below every real key).
+// Every lane reads the same 16 bytes at a time (LDS broadcast), 8 reads in
+// flight.  O(n^2 / NT) work per thread: for lists of a few hundred.
+template <int NT>
+__device__ __forceinline__ void rank_take_desc(uint64_t* cand, int n, int take, int32_t* dst) {
+    if (threadIdx.x == 0 && (n & 1)) cand[n] = 0ull;
+    __syncthreads();
+    const int n2 = (n + 1) >> 1;
+    const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
+    for (int i = threadIdx.x; i < n; i += NT) {
+        const uint64_t x = cand[i];
+        int r = 0;
+#pragma unroll 8
+        for (int k = 0; k < n2; ++k) {
+            const ulonglong2 v = c2[k];
+            r += (v.x > x ? 1 : 0) + (v.y > x ? 1 : 0);
+        }
+        if (r < take) dst[r] = static_cast<int32_t>(~static_cast<uint32_t>(x));
+    }
+}
+
+// vals[0 .. n) (distinct, below INT32_MAX) written ascending into out[0 .. n)
+// by counting; vals must be 16-byte aligned with room for n rounded up to 4
+// (the tail is padded with INT32_MAX).
+template <int NT>
+__device__ __forceinline__ void rank_write_ascending(int32_t* vals, int n, int32_t* out) {
+    const int n4 = (n + 3) >> 2;
+    for (int k = n + threadIdx.x; k < 4 * n4; k += NT) vals[k] = 0x7fffffff;
+    __syncthreads();
+    const int4* v4 = reinterpret_cast<const int4*>(vals);
+    for (int i = threadIdx.x; i < n; i += NT) {
+        const int32_t x = vals[i];
+        int r = 0;
+#pragma unroll 8
+        for (int k = 0; k < n4; ++k) {
+            const int4 v = v4[k];
+            r += (v.x < x ? 1 : 0) + (v.y < x ? 1 : 0) + (v.z < x ? 1 : 0) + (v.w < x ? 1 : 0);
+        }
+        out[r] = x;
+    }
 }
 
 // Trivial rows: every candidate fits the budget, or the budget is the own block alone.

@@ -174,8 +174,9 @@ qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
  * and the same selection as qsa_select_topk, bit for bit, in two launches
  * that spread each row over many workgroups (a scan that also histograms the
  * score keys, then a threshold filter whose last workgroup finishes the
- * exact selection).  scores [B][>= q_pos/4] (seq stride, 16-byte aligned,
- * multiple of 4), sel [B][budget].  The workspace
+ * exact selection).  scores [B][ld] float with ld >= q_pos/4 rounded up to a
+ * multiple of 4 (the tail past q_pos/4 is scratch), 16-byte aligned;
+ * sel [B][budget].  The workspace
  * (qsa_index_select_decode_workspace_bytes) must be zero-filled before its
  * first use; every call leaves it zeroed again.  Calls that share a
  * workspace must not overlap.

@@ -65,7 +65,10 @@ def test_index_select_decode_matches_primitives(kind, pos, budget):
             o = pos[b] // 4
             assert torch.equal(s_f[b, 0, :o].view(torch.int32), s_ref[b, 0, :o].view(torch.int32)), (rep, b)
         assert torch.equal(sel_f, sel_ref), rep
-        assert int(ws.count_nonzero()) == 0, "workspace not left zeroed"
+        # histogram and control words (the head of the workspace) are left zeroed;
+        # the candidate lists after them are scratch
+        head = B * (4096 + 16) * 4
+        assert int(ws[:head].count_nonzero()) == 0, "histogram / control words not left zeroed"
 
 
 @pytest.mark.parametrize("ctx,budget,B", [(32768, 512, 8), (5001, 64, 3), (99, 512, 2)])
