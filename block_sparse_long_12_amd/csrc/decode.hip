@@ -9,7 +9,7 @@
 //  decode_scan_kernel      B x G workgroups, long-lived waves that stream
 //                          64-block groups with the next group's loads in
 //                          flight.  Scores every candidate with the shared MFMA
-//                          block_score (bit-identical to index_scores_kernel),
+//                          block_scores (bit-identical to index_scores_kernel),
 //                          stores the scores, counts the top 12 bits of each
 //                          ordered key in an LDS histogram and adds it to a
 //                          per-sequence global histogram.  Optionally rotates
@@ -89,8 +89,8 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
 
     const int c16 = lane & 15;
     const int G = lane >> 4;
-    bf16x8_t a[4];
-    load_index_a(q_idx + b * qs, 0, 1, a);
+    bf16x8_t qf[16];
+    load_index_q(q_idx + b * qs, 0, 1, qf);             // token 0 in column 0, zero columns elsewhere
     const uint16_t* kb = kbar + b * kbs;
     float* sb = scores + b * ss;
     const int j_lo = g * (256 * STEPS);
@@ -98,17 +98,20 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     // two named buffers, loop unrolled by two: one group computes while the
     // next is in flight (the next-group address is clamped, never skipped)
     auto step_of = [&](int j) { return (j < j_hi) ? j : (j_hi - 1) / 64 * 64; };
-    auto score_group = [&](const bf16x8_t (&bf)[4][4], int j0) {
-        float s[4];
+    // 4 tiles of 16 blocks; the lanes of column 0 hold the scores, 4
+    // consecutive blocks each
+    auto score_group = [&](const bf16x8_t (&kf)[4][4], int j0) {
 #pragma unroll
-        for (int n = 0; n < 4; ++n) s[n] = block_score(a, bf[n]);
-        const int jj = j0 + 4 * c16;
-        if (G == 0 && jj < j_hi) {
-            *reinterpret_cast<float4*>(sb + jj) = make_float4(s[0], s[1], s[2], s[3]);
-            if (need_hist) {
+        for (int nt = 0; nt < 4; ++nt) {
+            const f32x4_t s = block_scores(kf[nt], qf);
+            const int jj = j0 + 16 * nt + 4 * G;
+            if (c16 == 0 && jj < j_hi) {
+                *reinterpret_cast<float4*>(sb + jj) = make_float4(s[0], s[1], s[2], s[3]);
+                if (need_hist) {
 #pragma unroll
-                for (int n = 0; n < 4; ++n)
-                    if (jj + n < j_hi) atomicAdd(&hist[score_key(s[n]) >> kDecShift], 1u);
+                    for (int n = 0; n < 4; ++n)
+                        if (jj + n < j_hi) atomicAdd(&hist[score_key(s[n]) >> kDecShift], 1u);
+                }
             }
         }
     };
@@ -119,12 +122,13 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     if (j0 < j_hi) {
         bf16x8_t buf[2][4][4];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) load_index_b(kb, j0, n, j_hi, buf[0][n]);
+        for (int nt = 0; nt < 4; ++nt) load_index_k(kb, j0 + 16 * nt, j_hi, buf[0][nt]);
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             if (st + 1 < STEPS) {
 #pragma unroll
-                for (int n = 0; n < 4; ++n) load_index_b(kb, step_of(j0 + 256 * (st + 1)), n, j_hi, buf[(st + 1) & 1][n]);
+                for (int nt = 0; nt < 4; ++nt)
+                    load_index_k(kb, step_of(j0 + 256 * (st + 1)) + 16 * nt, j_hi, buf[(st + 1) & 1][nt]);
             }
             if (j0 + 256 * st < j_hi) score_group(buf[st & 1], j0 + 256 * st);
         }

@@ -18,12 +18,227 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ sc
                    sel + b * sels + static_cast<int64_t>(i) * budget, sm);
 }
 
+// ---------------------------------------------------------------------------
+// Single-read selection (budgets up to 1024).  The multi-pass radix select
+// above reads a long row two to four times; this one reads it once in the
+// common case and falls back to it otherwise, so results are identical:
+//   1. a sample of 8192 scores (32 evenly spread runs of 256) gives, by a two
+//      level radix select in LDS, a key threshold tau whose expected count in
+//      the whole row is sqrt(keep * kSpCap) -- far from both keep and the LDS
+//      capacity;
+//   2. one pass over the row appends every candidate with key >= tau to its
+//      wave's LDS segment (ballot + mbcnt, no atomics), as (key << 32 | ~j);
+//   3. if the segments did not overflow and hold at least `keep` entries, the
+//      exact top `keep` of the whole row lies among them: a radix select over
+//      the 64-bit entries (descending key, then ascending j) finds it;
+//      otherwise the row is redone by select_row.
+// Rows with at most kSpCap candidates skip the threshold and take them all.
+constexpr int kSpNT = 512;
+constexpr int kSpWaves = kSpNT / 64;
+constexpr int kSpCap = 4096;                  // candidates held in LDS
+constexpr int kSpSeg = kSpCap / kSpWaves;     // per-wave segment
+constexpr int kSpShort = 256;                 // threshold-bin list resolved by ranking
+constexpr int kSpRuns = 32;                   // sample runs of 64 float4
+constexpr int kSpSample = kSpRuns * 64 * 4;
+constexpr int kSpMaxBudget = 1024;
+
+struct SampledSmem {
+    alignas(16) uint64_t cand[kSpCap];
+    alignas(16) uint64_t shortl[kSpShort + 2];
+    alignas(16) int32_t chosen[kSpMaxBudget];
+    uint32_t hist[2048];
+    int wave_tot[16];
+    int seg_cnt[kSpWaves];
+    int n_chosen, n_short, sh_above;
+    uint32_t sh_bin;
+};
+
+union SelectAllSmem {
+    SampledSmem s;
+    SelectSmem f;
+};
+
+// float whose score_key is `key` (key must not be a NaN pattern's image)
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Appends (key(s) << 32 | ~j) for the lanes with q to the wave's segment.
+// cnt is wave-uniform; entries past the segment are counted, not written.
+__device__ __forceinline__ void wave_append(bool q, float s, int j, uint64_t* seg, int& cnt) {
+    const uint64_t m = __ballot(q);
+    if (m != 0ull) {
+        if (q) {
+            const int pos = cnt + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                      static_cast<uint32_t>(m >> 32),
+                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+            if (pos < kSpSeg)
+                seg[pos] = (static_cast<uint64_t>(score_key(s)) << 32) | static_cast<uint32_t>(~j);
+        }
+        cnt += __popcll(m);
+    }
+}
+
+__global__ __launch_bounds__(kSpNT) void select_sampled_kernel(const float* __restrict__ scores, int64_t ld,
+                                                               int64_t ss, Positions pos0, int tq, int budget,
+                                                               int32_t* __restrict__ sel, int64_t sels) {
+    __shared__ SelectAllSmem smu;
+    SampledSmem& sm = smu.s;
+    const int b = blockIdx.x / tq;
+    const int i = blockIdx.x % tq;
+    const int o = (pos0.p[b] + i) / kBlock;
+    const int keep = min(budget - 1, o);
+    const float* row = scores + b * ss + static_cast<int64_t>(i) * ld;
+    int32_t* out = sel + b * sels + static_cast<int64_t>(i) * budget;
+    if (trivial_selection(keep, o, budget, out, kSpNT)) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int o4 = o >> 2;
+    const float4* row4 = reinterpret_cast<const float4*>(row);
+    const bool take_all = o <= kSpCap;
+
+    // ---- 1. threshold from the sample ----
+    float tf = 0.0f;
+    bool fallback = false;
+    if (!take_all) {
+        uint32_t sk[16];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int f = tid + kSpNT * it;
+            const int run = f >> 6;
+            const int start4 = static_cast<int>(static_cast<int64_t>(run) * (o4 - 64) / (kSpRuns - 1));
+            const float4 v = row4[start4 + (f & 63)];
+            sk[4 * it + 0] = score_key(v.x);
+            sk[4 * it + 1] = score_key(v.y);
+            sk[4 * it + 2] = score_key(v.z);
+            sk[4 * it + 3] = score_key(v.w);
+        }
+        const int target = static_cast<int>(sqrtf(static_cast<float>(keep) * kSpCap));
+        const int r = static_cast<int>((static_cast<int64_t>(target) * kSpSample + o - 1) / o);
+        for (int k = tid; k < 2048; k += kSpNT) sm.hist[k] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 16; ++e) atomicAdd(&sm.hist[sk[e] >> 21], 1u);
+        __syncthreads();
+        find_threshold_bin<kSpNT>(sm.hist, 2048, r, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
+        const uint32_t b1 = sm.sh_bin;
+        const int r2 = r - sm.sh_above;
+        __syncthreads();
+        for (int k = tid; k < 2048; k += kSpNT) sm.hist[k] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if ((sk[e] >> 21) == b1) atomicAdd(&sm.hist[(sk[e] >> 10) & 2047u], 1u);
+        __syncthreads();
+        find_threshold_bin<kSpNT>(sm.hist, 2048, r2, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
+        const uint32_t tkey = (b1 << 21) | (sm.sh_bin << 10);
+        // at or below the key of -inf the float threshold would be a NaN
+        fallback = tkey <= 0x007fffffu;
+        tf = key_to_float(tkey);
+    }
+
+    // ---- 2. one pass: candidates into per-wave segments ----
+    if (!fallback) {
+        uint64_t* seg = sm.cand + wave * kSpSeg;
+        int cnt = 0;
+        for (int k0 = 0; k0 < o4; k0 += 4 * kSpNT) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = row4[min(k0 + u * kSpNT + tid, o4 - 1)];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k = k0 + u * kSpNT + tid;
+                const bool valid = k < o4;
+                wave_append(valid && (take_all || v[u].x >= tf), v[u].x, 4 * k + 0, seg, cnt);
+                wave_append(valid && (take_all || v[u].y >= tf), v[u].y, 4 * k + 1, seg, cnt);
+                wave_append(valid && (take_all || v[u].z >= tf), v[u].z, 4 * k + 2, seg, cnt);
+                wave_append(valid && (take_all || v[u].w >= tf), v[u].w, 4 * k + 3, seg, cnt);
+            }
+        }
+        if (wave == kSpWaves - 1) {          // the o % 4 trailing scores
+            const int j = 4 * o4 + lane;
+            const bool valid = lane < (o & 3);
+            const float s = valid ? row[j] : 0.0f;
+            wave_append(valid && (take_all || s >= tf), s, j, seg, cnt);
+        }
+        if (lane == 0) sm.seg_cnt[wave] = cnt;
+    }
+    __syncthreads();
+    int total = 0;
+    if (!fallback) {
+#pragma unroll
+        for (int w = 0; w < kSpWaves; ++w) {
+            const int c = sm.seg_cnt[w];
+            fallback |= c > kSpSeg;
+            total += c;
+        }
+        fallback |= total < keep;
+    }
+    if (fallback) {                           // uniform: every thread read the same counts
+        __syncthreads();
+        select_row<kSpNT>(row, o, keep, budget, out, smu.f);
+        return;
+    }
+
+    // ---- 3. exact top `keep` among the candidates ----
+    uint64_t c[kSpWaves];
+    bool cv[kSpWaves];
+#pragma unroll
+    for (int w = 0; w < kSpWaves; ++w) {
+        cv[w] = tid < sm.seg_cnt[w];
+        c[w] = cv[w] ? sm.cand[w * kSpSeg + tid] : 0ull;
+    }
+    uint64_t prefix = 0ull, pmask = 0ull;
+    int rem = keep;
+    int bin_count = total;
+    for (int sh = 53; bin_count > kSpShort; sh = max(sh - 11, 0)) {
+        for (int k = tid; k < 2048; k += kSpNT) sm.hist[k] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kSpWaves; ++w)
+            if (cv[w] && (c[w] & pmask) == prefix)
+                atomicAdd(&sm.hist[static_cast<uint32_t>(c[w] >> sh) & 2047u], 1u);
+        __syncthreads();
+        find_threshold_bin<kSpNT>(sm.hist, 2048, rem, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
+        const uint32_t tb = sm.sh_bin;
+        rem -= sm.sh_above;
+        prefix |= static_cast<uint64_t>(tb) << sh;
+        pmask |= 2047ull << sh;
+        bin_count = static_cast<int>(sm.hist[tb]);
+        __syncthreads();
+        if (sh == 0) break;
+    }
+    if (tid == 0) {
+        sm.n_chosen = 0;
+        sm.n_short = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kSpWaves; ++w) {
+        if (cv[w]) {
+            const uint64_t mk = c[w] & pmask;
+            if (mk > prefix) sm.chosen[atomicAdd(&sm.n_chosen, 1)] = static_cast<int32_t>(~static_cast<uint32_t>(c[w]));
+            else if (mk == prefix) sm.shortl[atomicAdd(&sm.n_short, 1)] = c[w];
+        }
+    }
+    __syncthreads();
+    rank_take_desc<kSpNT>(sm.shortl, sm.n_short, rem, sm.chosen + (keep - rem));
+    if (tid == 0) sm.chosen[keep] = o;
+    rank_write_ascending<kSpNT>(sm.chosen, keep + 1, out);
+    for (int k = keep + 1 + tid; k < budget; k += kSpNT) out[k] = -1;
+}
+
 hipError_t launch_select(const float* scores, int64_t ld, int64_t ss, const Positions& pos0,
                          int batch, int tq, int budget, int32_t* sel, int64_t sels,
                          hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(batch) * tq;
     if (rows == 0) return hipSuccess;
-    if (rows < 1024) {
+    if (budget <= kSpMaxBudget) {
+        hipLaunchKernelGGL(select_sampled_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSpNT), 0, stream,
+                           scores, ld, ss, pos0, tq, budget, sel, sels);
+    } else if (rows < 1024) {
         hipLaunchKernelGGL(select_kernel<1024>, dim3(static_cast<unsigned>(rows)), dim3(1024), 0,
                            stream, scores, ld, ss, pos0, tq, budget, sel, sels);
     } else {

@@ -160,6 +160,10 @@ def _rows(kind, n_cand, T, rng):
         return v
     if kind == "clustered":    # every key shares its top bits: several radix digits
         return (np.float32(1.0) + rng.integers(0, 6000, (T, n_cand)).astype(np.float32) * np.float32(2.0 ** -23)).astype(np.float32)
+    if kind == "front_loaded":   # the row's head outranks the rest: a sample there overestimates the tail
+        v = rng.standard_normal((T, n_cand)).astype(np.float32)
+        v[:, :256] += np.float32(10.0)
+        return v
     if kind == "tie_flood":    # a few winners, then thousands of exact ties at the threshold
         v = np.full((T, n_cand), 0.5, np.float32)
         v[:, rng.choice(n_cand, 300, replace=False)] = 2.0
@@ -173,7 +177,8 @@ SELECT_CASES = [
     ("normal", 9000, 1), ("normal", 9000, 2), ("normal", 3000, 17),
     ("equal", 10000, 512), ("coarse", 8000, 512), ("signed_zero", 6000, 300),
     ("specials", 7000, 512), ("clustered", 20000, 512), ("tie_flood", 12000, 512),
-    ("tie_flood", 12000, 2048),
+    ("tie_flood", 12000, 2048), ("front_loaded", 70000, 512), ("normal", 262144, 512),
+    ("normal", 262144, 1024), ("normal", 4096, 1024), ("specials", 70000, 64),
 ]
 
 
