@@ -130,10 +130,9 @@ class Prefill:
         for c0 in range(0, T, ch):
             c1 = min(T, c0 + ch)
             cpos = [ctx + c0] * B
-            with timer("index_scores"):
-                q.index_scores(self.q_idx[:, c0:c1], self.kbar, cpos, self.bufs.scores)
-            with timer("select_topk"):
-                q.select_topk(self.bufs.scores, cpos, wl.budget, self.bufs.sel[:, c0:c1])
+            with timer("index_select"):
+                q.index_select_prefill(self.q_idx[:, c0:c1], self.kbar, cpos, wl.budget, self.bufs.scores,
+                                       self.bufs.sel[:, c0:c1], self.bufs.workspace)
             with timer("sparse_attn_prefill"):
                 q.sparse_attn_prefill(self.q_rot[:, c0:c1], self.k_cache, self.v_cache, self.bufs.sel[:, c0:c1],
                                       cpos, self.out[:, c0:c1], self.lse[:, c0:c1])
@@ -313,8 +312,7 @@ def main():
     attn_ms, attn_n = kern["sparse_attn_prefill"]
     attn_avg_s = attn_ms / attn_n / 1e3
     attn_bytes_per_launch = geo["attn_bytes"] / n_chunks
-    idx_ms, idx_n = kern["index_scores"]
-    sel_ms, sel_n = kern["select_topk"]
+    idx_ms, idx_n = kern["index_select"]
     roofline = {
         "bound": "hbm",
         "kernel": "sparse_attn_prefill",
@@ -325,7 +323,7 @@ def main():
         "traffic": measured_traffic("sparse_attn_prefill", "attention.hip"),
     }
     mfma = {
-        "index_scores_frac": (geo["index_flops"] / n_chunks) / (idx_ms / idx_n / 1e3) / BF16_PEAK,
+        "index_select_frac": (geo["index_flops"] / n_chunks) / (idx_ms / idx_n / 1e3) / BF16_PEAK,
         "layer_frac": (geo["index_flops"] + geo["attn_flops"]) / (ms_per_step / 1e3) / BF16_PEAK,
         "note": "folded indexer minimum (2*128 flop per query-candidate pair) plus attention flops",
     }

@@ -7,23 +7,33 @@
 // A dense bf16 contraction on the matrix cores with the head sum folded into
 // K (index_common.h): per 16 blocks x 16 tokens, one chain of 16
 // v_mfma_f32_16x16x32_bf16 gives finished scores, 4 consecutive blocks of one
-// token per lane.  Every launch shape computes a given score with the same
-// instruction sequence, so scores do not depend on tiling.
+// token per lane.  Every launch shape and mode computes a given score with
+// the same instruction sequence, so scores do not depend on tiling.
 //
 // A workgroup of 4 waves owns 64 query rows (16 per wave, whose B operands
 // stay in registers) and a chunk of block columns.  Each step the workgroup
-// stages 64 blocks (16 KiB) of kbar in LDS -- LDS-direct loads issued two
-// steps ahead into three buffers -- and every wave reads its A operands from
-// there, so each kbar byte crosses the vector memory path once per 64 rows.
-// A wave stores 4 float4 per lane per step (16 rows x 256 bytes).
-// Causality: the workgroup stops at the last block its last row sees.
+// stages 64 blocks (16 KiB) of kbar in LDS with LDS-direct loads and every
+// wave reads its A operands from there, so each kbar byte crosses the vector
+// memory path once per 64 rows.  Three modes share the machinery:
+//   scores  -- store every score (4 float4 per lane per step), three LDS
+//              buffers so loads run two steps ahead of the stores;
+//   sample  -- the same over a fixed sample of blocks (32 evenly spread runs
+//              of 256), stored compactly; feeds the per-row thresholds;
+//   collect -- no score matrix: scores at or above the row's threshold are
+//              appended to an LDS list and, at the end, to the row's global
+//              candidate list (one atomic per row and workgroup).
+// Causality: a workgroup stops at the last block its last row sees; collect
+// also drops each row's blocks at or past its own block.
 #include "index_common.h"
+#include "select_common.h"
 
 namespace qsa {
 
 constexpr int kTokTile = 16;    // query rows per wave
 constexpr int kWgTok = 64;      // query rows per workgroup
 constexpr int kColStep = 64;    // blocks per step
+
+enum { kModeScores = 0, kModeSample = 1, kModeCollect = 2 };
 
 // One step of kbar in LDS: block jb of the step is row jb (256 bytes); the
 // 16-byte chunk c of row r is stored at position c ^ (r % 16), so the 16
@@ -33,13 +43,29 @@ struct KTile {
     uint4 chunk[kColStep][16];
 };
 
-// The three step buffers are separate LDS objects.
+// The step buffers are separate LDS objects; collect uses two of them plus
+// the candidate list.
 __shared__ KTile tA, tB, tC;
+__shared__ uint64_t lcand[kCollectCap];
+__shared__ int lrow[kWgTok];
+__shared__ int lrow_base[kWgTok];
+__shared__ int lcount;
+
+// Block of column jv: itself, or in sample mode run jv / 256 of 32 runs of
+// 256 blocks spread evenly over [0, omin).
+template <int kMode>
+__device__ __forceinline__ int column_block(int jv, int omin) {
+    if (kMode == kModeSample) {
+        const int run = jv >> 8;
+        return static_cast<int>(static_cast<int64_t>(run) * (omin - 256) / (kSampleRuns - 1)) + (jv & 255);
+    }
+    return jv;
+}
 
 // Stages one step of kbar into t with LDS-direct loads (no registers): wave
 // w fills rows 16w .. 16w + 15 with 4 loads of 1 KiB; lane L of load i
-// writes row 16w + 4i + L / 16 at position L % 16.  Blocks at or past j_end
-// read block j_end - 1 (never stored as a score).
+// writes row 16w + 4i + L / 16 at position L % 16.  Columns at or past j_end
+// read column j_end - 1 (never stored or collected).
 //
 // The load is issued from inline assembly: with the compiler's LDS-DMA
 // intrinsic, its wait-count pass assumes every LDS read may depend on every
@@ -47,15 +73,16 @@ __shared__ KTile tA, tB, tC;
 // before each step, which serialises the score stores with the next step.
 // The instruction has no register results (it writes LDS only, and its
 // address registers are read at issue); completion is tracked explicitly by
-// step_sync's vmcnt waits.
-__device__ __forceinline__ void stage_dma(const uint16_t* kb, int j0, int j_end, KTile& t) {
+// the vmcnt waits of the step loop.
+template <int kMode>
+__device__ __forceinline__ void stage_dma(const uint16_t* kb, int j0, int j_end, int omin, KTile& t) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 16 * wave + 4 * i + (lane >> 4);
         const int c = (lane & 15) ^ (r & 15);
-        const int j = min(j0 + r, j_end - 1);
+        const int j = column_block<kMode>(min(j0 + r, j_end - 1), omin);
         const uint16_t* src = kb + static_cast<int64_t>(j) * kDi + 8 * c;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(
             static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&t.chunk[16 * wave + 4 * i][0])));
@@ -66,28 +93,35 @@ __device__ __forceinline__ void stage_dma(const uint16_t* kb, int j0, int j_end,
     }
 }
 
-// Wait until this wave's loads of step s have landed, then meet the other
-// waves.  Vector memory ops complete in issue order; after the 4 loads of
-// step s a wave with rows issues 4 score stores per scored step and the 4
-// loads of step s + 1, so at most that many may stay in flight.  A wave
-// without rows (at most three per launch, in the last row tile) waits for all.
-__device__ __forceinline__ void step_sync(int s, bool has_rows) {
-    if (!has_rows) __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0)
-    else if (s == 0) __builtin_amdgcn_s_waitcnt(0x0f74);   // vmcnt(4)
-    else if (s == 1) __builtin_amdgcn_s_waitcnt(0x0f78);   // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0f7c);               // vmcnt(12)
+// Waits for this wave's vector memory ops until at most N are in flight,
+// then meets the other waves.
+template <int N>
+__device__ __forceinline__ void wait_and_meet() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
 
-// Scores of one staged step (4 tiles of 16 blocks) for the wave's 16 rows.
-__device__ __forceinline__ void score_step(const KTile& t, const bf16x8_t (&qf)[16], int j0, int j_end,
-                                           int t0, int tq, float* sb, int64_t ld) {
+// scores / sample: wait until this wave's loads of step s have landed.
+// Vector memory ops complete in issue order; after the 4 loads of step s a
+// wave with rows issues 4 score stores per scored step and the 4 loads of
+// step s + 1, so at most that many may stay in flight.  A wave without rows
+// (only in the last row tile) waits for all.
+__device__ __forceinline__ void step_sync(int s, bool has_rows) {
+    if (!has_rows) wait_and_meet<0>();
+    else if (s == 0) wait_and_meet<4>();
+    else if (s == 1) wait_and_meet<8>();
+    else wait_and_meet<12>();
+}
+
+// Scores of one staged step (4 tiles of 16 blocks) for the wave's 16 rows:
+// lane l ends with blocks j0 + 16 nt + 4 (l / 16) .. + 3 of token l % 16.
+__device__ __forceinline__ void step_scores(const KTile& t, const bf16x8_t (&qf)[16], f32x4_t (&acc)[4]) {
     const int lane = threadIdx.x & 63;
     const int c16 = lane & 15;
     const int G = lane >> 4;
-    f32x4_t acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
         bf16x8_t kf[4];
@@ -98,19 +132,58 @@ __device__ __forceinline__ void score_step(const KTile& t, const bf16x8_t (&qf)[
         }
         acc[nt] = block_scores(kf, qf);
     }
-    const int tok = t0 + c16;
+}
+
+__device__ __forceinline__ void store_step(const KTile& t, const bf16x8_t (&qf)[16], int j0, int j_end, int t0,
+                                           int tq, float* sb, int64_t ld) {
+    f32x4_t acc[4];
+    step_scores(t, qf, acc);
+    const int lane = threadIdx.x & 63;
+    const int tok = t0 + (lane & 15);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-        const int jj = j0 + 16 * nt + 4 * G;
+        const int jj = j0 + 16 * nt + 4 * (lane >> 4);
         if (tok < tq && jj < j_end)        // streaming store: the scores are read back once, much later
             __builtin_nontemporal_store(acc[nt], reinterpret_cast<f32x4_t*>(sb + static_cast<int64_t>(tok) * ld + jj));
     }
 }
 
-__global__ __launch_bounds__(256) void index_scores_kernel(
+// collect: append (key << 32 | row_local << 16 | (j - j_begin)) for every
+// score of the lane's row at or above its threshold tau, for blocks below
+// lim (the row's own block and the chunk end).  For a number tau whose key
+// has zero low bits, score >= tau (IEEE) holds exactly when score_key(score)
+// >= score_key(tau); a NaN tau passes nothing.
+__device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf)[16], int j0, int lim,
+                                             float tau, int row_local, int j_begin) {
+    f32x4_t acc[4];
+    step_scores(t, qf, acc);
+    const int lane = threadIdx.x & 63;
+    const int jl = j0 + 4 * (lane >> 4);
+    uint32_t qmask = 0;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            if (jl + 16 * nt + n < lim && acc[nt][n] >= tau) qmask |= 1u << (4 * nt + n);
+    if (qmask != 0u) {
+        int k = atomicAdd(&lcount, __popc(qmask));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if (qmask & (1u << e)) {
+                if (k < kCollectCap)
+                    lcand[k] = (static_cast<uint64_t>(score_key(acc[e >> 2][e & 3])) << 32) |
+                               static_cast<uint32_t>((row_local << 16) | (jl + 16 * (e >> 2) + (e & 3) - j_begin));
+                ++k;
+            }
+        }
+    }
+}
+
+template <int kMode>
+__global__ __launch_bounds__(256) void index_kernel(
     const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
     Positions pos0, int tq, int n_wt, int n_cc, int cols_per_chunk, int64_t n_wg,
-    float* __restrict__ scores, int64_t ld, int64_t ss) {
+    float* __restrict__ scores, int64_t ld, int64_t ss, const int* __restrict__ flags, IndexCollect col) {
     // workgroups are dealt to the 8 XCDs round-robin; renumber them so each
     // XCD works through one contiguous range, and the row tiles that share a
     // column chunk of kbar share that XCD's L2
@@ -124,67 +197,162 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
 
     const int t_wg = wt * kWgTok;
     const int n_tok_wg = min(kWgTok, tq - t_wg);
-    const int jmax = (pos0.p[b] + t_wg + n_tok_wg - 1) / kBlock;   // blocks the last row sees
+    if (kMode == kModeScores && flags != nullptr) {       // only the row tiles holding a flagged row
+        if (col.n_flagged != nullptr && *col.n_flagged == 0) return;
+        const int tid = threadIdx.x;
+        const bool mine = tid < n_tok_wg && flags[static_cast<int64_t>(b) * tq + t_wg + tid] != 0;
+        if (!__syncthreads_or(mine)) return;
+    }
+    const int omin = pos0.p[b] / kBlock;
+    const int jmax = (kMode == kModeSample) ? kSampleCols : (pos0.p[b] + t_wg + n_tok_wg - 1) / kBlock;
     const int j_begin = cc * cols_per_chunk;
     const int j_end = min(j_begin + cols_per_chunk, jmax);
     if (j_begin >= j_end) return;                         // whole workgroup
 
+    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t0 = t_wg + kTokTile * wave;
     const bool has_rows = t0 < tq;
 
     bf16x8_t qf[16];
     load_index_q(q_idx + b * qs, t0, tq, qf);
-    __builtin_amdgcn_s_waitcnt(0x0f70);                   // B in registers before the load pipeline starts
 
     const uint16_t* kb = kbar + b * kbs;
-    float* sb = scores + b * ss;
     const int n_steps = (j_end - j_begin + kColStep - 1) / kColStep;
-    // three LDS buffers: step s is scored while steps s + 1 and s + 2 load
-    stage_dma(kb, j_begin, j_end, tA);
-    stage_dma(kb, j_begin + kColStep, j_end, tB);
-    for (int s = 0; s < n_steps; s += 3) {
-        step_sync(s, has_rows);
-        stage_dma(kb, j_begin + kColStep * (s + 2), j_end, tC);
-        if (has_rows) score_step(tA, qf, j_begin + kColStep * s, j_end, t0, tq, sb, ld);
-        if (s + 1 >= n_steps) break;
-        step_sync(s + 1, has_rows);
-        stage_dma(kb, j_begin + kColStep * (s + 3), j_end, tA);
-        if (has_rows) score_step(tB, qf, j_begin + kColStep * (s + 1), j_end, t0, tq, sb, ld);
-        if (s + 2 >= n_steps) break;
-        step_sync(s + 2, has_rows);
-        stage_dma(kb, j_begin + kColStep * (s + 4), j_end, tB);
-        if (has_rows) score_step(tC, qf, j_begin + kColStep * (s + 2), j_end, t0, tq, sb, ld);
+
+    if constexpr (kMode == kModeCollect) {
+        const int tok = t0 + (lane & 15);
+        const int64_t row = static_cast<int64_t>(b) * tq + tok;
+        const float tau = tok < tq ? col.tau[row] : __uint_as_float(0x7fc00000u);
+        const int lim = min((pos0.p[b] + tok) / kBlock, j_end);
+        if (threadIdx.x < kWgTok) lrow[threadIdx.x] = 0;
+        if (threadIdx.x == 0) lcount = 0;
+        __builtin_amdgcn_s_waitcnt(0x0f70);               // q and tau in registers before the pipeline starts
+        __syncthreads();
+        // two LDS buffers: step s + 1 loads while step s is scored; the loop
+        // issues no other vector memory op, so "all landed" is vmcnt(0)
+        stage_dma<kMode>(kb, j_begin, j_end, omin, tA);
+        for (int s = 0; s < n_steps; s += 2) {
+            wait_and_meet<0>();
+            stage_dma<kMode>(kb, j_begin + kColStep * (s + 1), j_end, omin, tB);
+            if (has_rows) collect_step(tA, qf, j_begin + kColStep * s, lim, tau, tok - t_wg, j_begin);
+            if (s + 1 >= n_steps) break;
+            wait_and_meet<0>();
+            stage_dma<kMode>(kb, j_begin + kColStep * (s + 2), j_end, omin, tA);
+            if (has_rows) collect_step(tB, qf, j_begin + kColStep * (s + 1), lim, tau, tok - t_wg, j_begin);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);               // no load into LDS outlives the workgroup
+        __syncthreads();
+        // hand the list to the rows: count per row, one global reservation per row
+        const int n = lcount;
+        if (n > kCollectCap) {                            // list overflow: every row of the tile falls back
+            if (threadIdx.x < n_tok_wg) atomicAdd(&col.row_cnt[static_cast<int64_t>(b) * tq + t_wg + threadIdx.x], kRowCap + 1);
+            return;
+        }
+        int slot[kCollectCap / 256];
+#pragma unroll
+        for (int k = 0; k < kCollectCap / 256; ++k) {
+            const int i = threadIdx.x + 256 * k;
+            slot[k] = (i < n) ? atomicAdd(&lrow[(lcand[i] >> 16) & 63], 1) : 0;
+        }
+        __syncthreads();
+        if (threadIdx.x < n_tok_wg && lrow[threadIdx.x] > 0)
+            lrow_base[threadIdx.x] = atomicAdd(&col.row_cnt[static_cast<int64_t>(b) * tq + t_wg + threadIdx.x], lrow[threadIdx.x]);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kCollectCap / 256; ++k) {
+            const int i = threadIdx.x + 256 * k;
+            if (i < n) {
+                const uint64_t e = lcand[i];
+                const int rl = static_cast<int>((e >> 16) & 63);
+                const int pos = lrow_base[rl] + slot[k];
+                if (pos < kRowCap) {
+                    const int j = j_begin + static_cast<int>(e & 0xffffu);
+                    col.list[(static_cast<int64_t>(b) * tq + t_wg + rl) * kRowCap + pos] =
+                        (e & 0xffffffff00000000ull) | static_cast<uint32_t>(~j);
+                }
+            }
+        }
+    } else {
+        __builtin_amdgcn_s_waitcnt(0x0f70);               // B in registers before the load pipeline starts
+        float* sb = scores + b * ss;
+        // three LDS buffers: step s is scored while steps s + 1 and s + 2 load
+        stage_dma<kMode>(kb, j_begin, j_end, omin, tA);
+        stage_dma<kMode>(kb, j_begin + kColStep, j_end, omin, tB);
+        for (int s = 0; s < n_steps; s += 3) {
+            step_sync(s, has_rows);
+            stage_dma<kMode>(kb, j_begin + kColStep * (s + 2), j_end, omin, tC);
+            if (has_rows) store_step(tA, qf, j_begin + kColStep * s, j_end, t0, tq, sb, ld);
+            if (s + 1 >= n_steps) break;
+            step_sync(s + 1, has_rows);
+            stage_dma<kMode>(kb, j_begin + kColStep * (s + 3), j_end, omin, tA);
+            if (has_rows) store_step(tB, qf, j_begin + kColStep * (s + 1), j_end, t0, tq, sb, ld);
+            if (s + 2 >= n_steps) break;
+            step_sync(s + 2, has_rows);
+            stage_dma<kMode>(kb, j_begin + kColStep * (s + 4), j_end, omin, tB);
+            if (has_rows) store_step(tC, qf, j_begin + kColStep * (s + 2), j_end, t0, tq, sb, ld);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);               // no load into LDS outlives the workgroup
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);                   // no load into LDS outlives the workgroup
 }
 
-static void index_grid(const Positions& pos0, int batch, int tq, int* n_wt, int* n_cc, int* cols_per_chunk,
+// Grid: batch x column chunks x 64-row tiles, the chunk width a multiple of
+// 64 blocks (at most max_cols) so that a few thousand workgroups fill the chip.
+static void index_grid(int jmax, int batch, int tq, int max_cols, int* n_wt, int* n_cc, int* cols_per_chunk,
                        int64_t* n_wg) {
-    int jmax = 0;
-    for (int b = 0; b < batch; ++b) jmax = max(jmax, (pos0.p[b] + tq - 1) / kBlock);
     *n_wt = (tq + kWgTok - 1) / kWgTok;
     const int64_t steps = (jmax + kColStep - 1) / kColStep;
-    // enough workgroups to fill 256 CUs several times over, at most 64 steps each
     const int64_t target_wgs = 4096;
     int64_t per = (static_cast<int64_t>(batch) * *n_wt * steps) / target_wgs;
-    per = per < 1 ? 1 : (per > 64 ? 64 : per);
+    per = per < 1 ? 1 : (per > max_cols / kColStep ? max_cols / kColStep : per);
     *cols_per_chunk = static_cast<int>(per * kColStep);
     *n_cc = max(1, static_cast<int>((jmax + *cols_per_chunk - 1) / *cols_per_chunk));
     *n_wg = static_cast<int64_t>(batch) * *n_cc * *n_wt;
 }
 
-hipError_t launch_index_scores(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
-                               int64_t kbs, const Positions& pos0, int batch, int tq,
-                               float* scores, int64_t ld, int64_t ss, hipStream_t stream) {
-    if (tq <= 0) return hipSuccess;
+template <int kMode>
+static hipError_t launch_mode(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
+                              const Positions& pos0, int batch, int tq, int jmax, int max_cols, float* scores,
+                              int64_t ld, int64_t ss, const int* flags, const IndexCollect& col,
+                              hipStream_t stream) {
+    if (tq <= 0 || jmax <= 0) return hipSuccess;
     int n_wt, n_cc, cpc;
     int64_t n_wg;
-    index_grid(pos0, batch, tq, &n_wt, &n_cc, &cpc, &n_wg);
+    index_grid(jmax, batch, tq, max_cols, &n_wt, &n_cc, &cpc, &n_wg);
     const unsigned grid = static_cast<unsigned>((n_wg + 7) / 8 * 8);
-    hipLaunchKernelGGL(index_scores_kernel, dim3(grid), dim3(256), 0, stream, q_idx, qs, kbar, kbs,
-                       pos0, tq, n_wt, n_cc, cpc, n_wg, scores, ld, ss);
+    hipLaunchKernelGGL(index_kernel<kMode>, dim3(grid), dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos0, tq,
+                       n_wt, n_cc, cpc, n_wg, scores, ld, ss, flags, col);
     return hipGetLastError();
+}
+
+static int max_visible_block(const Positions& pos0, int batch, int tq) {
+    int jmax = 0;
+    for (int b = 0; b < batch; ++b) jmax = max(jmax, (pos0.p[b] + tq - 1) / kBlock);
+    return jmax;
+}
+
+hipError_t launch_index_scores(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
+                               int64_t kbs, const Positions& pos0, int batch, int tq,
+                               float* scores, int64_t ld, int64_t ss, const int* row_flags,
+                               const int* n_flagged, hipStream_t stream) {
+    IndexCollect col{};
+    col.n_flagged = n_flagged;
+    return launch_mode<kModeScores>(q_idx, qs, kbar, kbs, pos0, batch, tq, max_visible_block(pos0, batch, tq),
+                                    4096, scores, ld, ss, row_flags, col, stream);
+}
+
+hipError_t launch_index_sample(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
+                               const Positions& pos0, int batch, int tq, float* sample, hipStream_t stream) {
+    return launch_mode<kModeSample>(q_idx, qs, kbar, kbs, pos0, batch, tq, kSampleCols, 4096, sample,
+                                    kSampleCols, static_cast<int64_t>(tq) * kSampleCols, nullptr, IndexCollect{},
+                                    stream);
+}
+
+hipError_t launch_index_collect(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
+                                const Positions& pos0, int batch, int tq, int max_cols, const IndexCollect& col,
+                                hipStream_t stream) {
+    return launch_mode<kModeCollect>(q_idx, qs, kbar, kbs, pos0, batch, tq, max_visible_block(pos0, batch, tq),
+                                     max_cols, nullptr, 0, 0, nullptr, col, stream);
 }
 
 }  // namespace qsa

@@ -165,7 +165,7 @@ qsa_status_t qsa_index_scores(const uint16_t* q_idx, int64_t q_idx_seq_stride,
     CHECK(batch == 1 || stride_ok(kbar_seq_stride), "kbar_seq_stride must be a positive multiple of 8");
     TRY(check_scores_layout(scores, scores_ld, scores_seq_stride, batch, tq, p));
     return hip_result(qsa::launch_index_scores(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch,
-                                               tq, scores, scores_ld, scores_seq_stride, stream),
+                                               tq, scores, scores_ld, scores_seq_stride, nullptr, nullptr, stream),
                       "index_scores launch");
 }
 
@@ -193,8 +193,45 @@ qsa_status_t qsa_select_topk(const float* scores, int64_t scores_ld, int64_t sco
     TRY(check_scores_layout(scores, scores_ld, scores_seq_stride, batch, tq, p));
     CHECK(batch == 1 || sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
     return hip_result(qsa::launch_select(scores, scores_ld, scores_seq_stride, p, batch, tq, budget, sel,
-                                         sel_seq_stride, stream),
+                                         sel_seq_stride, nullptr, stream),
                       "select_topk launch");
+}
+
+size_t qsa_index_select_prefill_workspace_bytes(int32_t batch, int32_t tq) {
+    if (batch < 1 || batch > QSA_MAX_BATCH || tq < 0) return 0;
+    return qsa::prefill_select_ws_bytes(batch, tq);
+}
+
+qsa_status_t qsa_index_select_prefill(const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                      const uint16_t* kbar, int64_t kbar_seq_stride,
+                                      const int32_t* q_pos0, int32_t batch, int32_t tq, int32_t budget,
+                                      float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                      int32_t* sel, int64_t sel_seq_stride,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    TRY(check_batch(batch));
+    CHECK(q_idx != nullptr && kbar != nullptr, "q_idx or kbar is NULL");
+    CHECK(aligned16(q_idx) && aligned16(kbar), "q_idx and kbar must be 16-byte aligned");
+    CHECK(tq >= 0, "tq = %d is negative", tq);
+    CHECK(budget >= 1 && budget <= QSA_MAX_BUDGET, "budget = %d outside [1, %d]", budget, QSA_MAX_BUDGET);
+    CHECK(sel != nullptr, "sel is NULL");
+    CHECK((reinterpret_cast<uintptr_t>(sel) & 3u) == 0, "sel must be 4-byte aligned");
+    qsa::Positions p;
+    TRY(take_positions(q_pos0, batch, tq, "q_pos0", p));
+    if (tq == 0) return ok();
+    CHECK(batch == 1 || (stride_ok(q_idx_seq_stride) && q_idx_seq_stride >= int64_t{tq} * qsa::kHi * qsa::kDi),
+          "q_idx_seq_stride must be a multiple of 8 and >= tq * 4 * 128");
+    CHECK(batch == 1 || stride_ok(kbar_seq_stride), "kbar_seq_stride must be a positive multiple of 8");
+    TRY(check_scores_layout(scores, scores_ld, scores_seq_stride, batch, tq, p));
+    CHECK(batch == 1 || sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
+    const size_t need = qsa::prefill_select_ws_bytes(batch, tq);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(QSA_ERR_WORKSPACE, "index-select workspace needs %zu bytes, got %zu", need,
+                    workspace == nullptr ? size_t{0} : workspace_bytes);
+    CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, "workspace must be 256-byte aligned");
+    return hip_result(qsa::launch_prefill_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq,
+                                                       budget, scores, scores_ld, scores_seq_stride, sel,
+                                                       sel_seq_stride, workspace, stream),
+                      "index_select_prefill launch");
 }
 
 static qsa_status_t check_attn_common(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -73,13 +73,44 @@ hipError_t launch_rope(const uint16_t* x, int64_t xs, int64_t xt, uint16_t* y, i
 hipError_t launch_compress(const uint16_t* k_idx, int64_t ks, int batch, int block_begin,
                            int block_end, uint16_t* kbar, int64_t kbs, hipStream_t stream);
 
+// row_flags (may be null): only the 64-row tiles holding a row with a nonzero flag are
+// scored, and nothing while *n_flagged (if given) is zero
 hipError_t launch_index_scores(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
                                int64_t kbs, const Positions& pos0, int batch, int tq,
-                               float* scores, int64_t ld, int64_t ss, hipStream_t stream);
+                               float* scores, int64_t ld, int64_t ss, const int* row_flags,
+                               const int* n_flagged, hipStream_t stream);
 
+// row_flags (may be null): only rows with a nonzero flag are selected; their flags are cleared
 hipError_t launch_select(const float* scores, int64_t ld, int64_t ss, const Positions& pos0,
-                         int batch, int tq, int budget, int32_t* sel, int64_t sels,
+                         int batch, int tq, int budget, int32_t* sel, int64_t sels, int* row_flags,
                          hipStream_t stream);
+
+// ---- fused prefill index-select (threshold from a sample, candidate lists) ----
+constexpr int kSampleRuns = 32;                   // sample runs of 256 blocks per sequence
+constexpr int kSampleCols = kSampleRuns * 256;    // sampled scores per row
+constexpr int kCollectCap = 2048;                 // candidates listed in LDS per workgroup
+constexpr int kRowCap = 4096;                     // candidates kept per row
+
+struct IndexCollect {
+    const float* tau;           // [rows] threshold per row
+    int* row_cnt;               // [rows] candidates appended (zero before the launch)
+    uint64_t* list;             // [rows][kRowCap] key << 32 | ~j
+    const int* n_flagged;       // scores mode with row flags: nothing to do while *n_flagged == 0
+};
+
+hipError_t launch_index_sample(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
+                               const Positions& pos0, int batch, int tq, float* sample, hipStream_t stream);
+hipError_t launch_index_collect(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
+                                const Positions& pos0, int batch, int tq, int max_cols, const IndexCollect& col,
+                                hipStream_t stream);
+
+size_t prefill_select_ws_bytes(int batch, int tq);
+// whole index-select of a prefill chunk; scores [B][tq][ld] is used only by rows
+// that need the exact fallback (or by every row when the fused path does not apply)
+hipError_t launch_prefill_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
+                                       const Positions& pos0, int batch, int tq, int budget, float* scores,
+                                       int64_t ld, int64_t ss, int32_t* sel, int64_t sels, void* ws,
+                                       hipStream_t stream);
 
 hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
                                const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,

@@ -4,13 +4,26 @@
 
 namespace qsa {
 
+// Rows with a zero flag are skipped when flags is given; a processed row's
+// flag is cleared (every thread has read it first).
+__device__ __forceinline__ bool take_flagged_row(int* flags, int64_t row, int* sh) {
+    if (flags == nullptr) return true;
+    if (threadIdx.x == 0) *sh = flags[row];
+    __syncthreads();
+    const int f = *sh;
+    if (f != 0 && threadIdx.x == 0) flags[row] = 0;
+    return f != 0;
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ scores, int64_t ld,
                                                     int64_t ss, Positions pos0, int tq, int budget,
-                                                    int32_t* __restrict__ sel, int64_t sels) {
+                                                    int32_t* __restrict__ sel, int64_t sels, int* flags) {
     __shared__ SelectSmem sm;
+    __shared__ int sh_flag;
     const int b = blockIdx.x / tq;
     const int i = blockIdx.x % tq;
+    if (!take_flagged_row(flags, blockIdx.x, &sh_flag)) return;
     const int p = pos0.p[b] + i;
     const int o = p / kBlock;
     const int keep = min(budget - 1, o);
@@ -37,31 +50,19 @@ constexpr int kSpNT = 512;
 constexpr int kSpWaves = kSpNT / 64;
 constexpr int kSpCap = 4096;                  // candidates held in LDS
 constexpr int kSpSeg = kSpCap / kSpWaves;     // per-wave segment
-constexpr int kSpShort = 256;                 // threshold-bin list resolved by ranking
 constexpr int kSpRuns = 32;                   // sample runs of 64 float4
 constexpr int kSpSample = kSpRuns * 64 * 4;
-constexpr int kSpMaxBudget = 1024;
 
 struct SampledSmem {
     alignas(16) uint64_t cand[kSpCap];
-    alignas(16) uint64_t shortl[kSpShort + 2];
-    alignas(16) int32_t chosen[kSpMaxBudget];
-    uint32_t hist[2048];
-    int wave_tot[16];
+    ResolveSmem res;
     int seg_cnt[kSpWaves];
-    int n_chosen, n_short, sh_above;
-    uint32_t sh_bin;
 };
 
 union SelectAllSmem {
     SampledSmem s;
     SelectSmem f;
 };
-
-// float whose score_key is `key` (key must not be a NaN pattern's image)
-__device__ __forceinline__ float key_to_float(uint32_t key) {
-    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
 
 // Appends (key(s) << 32 | ~j) for the lanes with q to the wave's segment.
 // cnt is wave-uniform; entries past the segment are counted, not written.
@@ -81,11 +82,13 @@ __device__ __forceinline__ void wave_append(bool q, float s, int j, uint64_t* se
 
 __global__ __launch_bounds__(kSpNT) void select_sampled_kernel(const float* __restrict__ scores, int64_t ld,
                                                                int64_t ss, Positions pos0, int tq, int budget,
-                                                               int32_t* __restrict__ sel, int64_t sels) {
+                                                               int32_t* __restrict__ sel, int64_t sels, int* flags) {
     __shared__ SelectAllSmem smu;
+    __shared__ int sh_flag;
     SampledSmem& sm = smu.s;
     const int b = blockIdx.x / tq;
     const int i = blockIdx.x % tq;
+    if (!take_flagged_row(flags, blockIdx.x, &sh_flag)) return;
     const int o = (pos0.p[b] + i) / kBlock;
     const int keep = min(budget - 1, o);
     const float* row = scores + b * ss + static_cast<int64_t>(i) * ld;
@@ -101,7 +104,6 @@ __global__ __launch_bounds__(kSpNT) void select_sampled_kernel(const float* __re
 
     // ---- 1. threshold from the sample ----
     float tf = 0.0f;
-    bool fallback = false;
     if (!take_all) {
         uint32_t sk[16];
 #pragma unroll
@@ -115,32 +117,16 @@ __global__ __launch_bounds__(kSpNT) void select_sampled_kernel(const float* __re
             sk[4 * it + 2] = score_key(v.z);
             sk[4 * it + 3] = score_key(v.w);
         }
-        const int target = static_cast<int>(sqrtf(static_cast<float>(keep) * kSpCap));
-        const int r = static_cast<int>((static_cast<int64_t>(target) * kSpSample + o - 1) / o);
-        for (int k = tid; k < 2048; k += kSpNT) sm.hist[k] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 16; ++e) atomicAdd(&sm.hist[sk[e] >> 21], 1u);
-        __syncthreads();
-        find_threshold_bin<kSpNT>(sm.hist, 2048, r, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
-        const uint32_t b1 = sm.sh_bin;
-        const int r2 = r - sm.sh_above;
-        __syncthreads();
-        for (int k = tid; k < 2048; k += kSpNT) sm.hist[k] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            if ((sk[e] >> 21) == b1) atomicAdd(&sm.hist[(sk[e] >> 10) & 2047u], 1u);
-        __syncthreads();
-        find_threshold_bin<kSpNT>(sm.hist, 2048, r2, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
-        const uint32_t tkey = (b1 << 21) | (sm.sh_bin << 10);
-        // at or below the key of -inf the float threshold would be a NaN
-        fallback = tkey <= 0x007fffffu;
-        tf = key_to_float(tkey);
+        const int64_t target = threshold_target(keep);
+        const int r = static_cast<int>(min<int64_t>((target * kSpSample + o - 1) / o, kSpSample));
+        tf = sample_threshold<kSpNT, 16>(sk, r, sm.res);
     }
 
-    // ---- 2. one pass: candidates into per-wave segments ----
-    if (!fallback) {
+    // ---- 2. one pass: candidates (score >= tf) into per-wave segments ----
+    // For a number tf whose key has zero low bits, score >= tf (IEEE) holds
+    // exactly when score_key(score) >= score_key(tf): -0.0 passes with +0.0
+    // and NaN never passes; a NaN tf passes nothing.
+    {
         uint64_t* seg = sm.cand + wave * kSpSeg;
         int cnt = 0;
         for (int k0 = 0; k0 < o4; k0 += 4 * kSpNT) {
@@ -166,16 +152,15 @@ __global__ __launch_bounds__(kSpNT) void select_sampled_kernel(const float* __re
         if (lane == 0) sm.seg_cnt[wave] = cnt;
     }
     __syncthreads();
+    bool fallback = false;
     int total = 0;
-    if (!fallback) {
 #pragma unroll
-        for (int w = 0; w < kSpWaves; ++w) {
-            const int c = sm.seg_cnt[w];
-            fallback |= c > kSpSeg;
-            total += c;
-        }
-        fallback |= total < keep;
+    for (int w = 0; w < kSpWaves; ++w) {
+        const int c = sm.seg_cnt[w];
+        fallback |= c > kSpSeg;
+        total += c;
     }
+    fallback |= total < keep;
     if (fallback) {                           // uniform: every thread read the same counts
         __syncthreads();
         select_row<kSpNT>(row, o, keep, budget, out, smu.f);
@@ -190,60 +175,23 @@ __global__ __launch_bounds__(kSpNT) void select_sampled_kernel(const float* __re
         cv[w] = tid < sm.seg_cnt[w];
         c[w] = cv[w] ? sm.cand[w * kSpSeg + tid] : 0ull;
     }
-    uint64_t prefix = 0ull, pmask = 0ull;
-    int rem = keep;
-    int bin_count = total;
-    for (int sh = 53; bin_count > kSpShort; sh = max(sh - 11, 0)) {
-        for (int k = tid; k < 2048; k += kSpNT) sm.hist[k] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int w = 0; w < kSpWaves; ++w)
-            if (cv[w] && (c[w] & pmask) == prefix)
-                atomicAdd(&sm.hist[static_cast<uint32_t>(c[w] >> sh) & 2047u], 1u);
-        __syncthreads();
-        find_threshold_bin<kSpNT>(sm.hist, 2048, rem, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
-        const uint32_t tb = sm.sh_bin;
-        rem -= sm.sh_above;
-        prefix |= static_cast<uint64_t>(tb) << sh;
-        pmask |= 2047ull << sh;
-        bin_count = static_cast<int>(sm.hist[tb]);
-        __syncthreads();
-        if (sh == 0) break;
-    }
-    if (tid == 0) {
-        sm.n_chosen = 0;
-        sm.n_short = 0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kSpWaves; ++w) {
-        if (cv[w]) {
-            const uint64_t mk = c[w] & pmask;
-            if (mk > prefix) sm.chosen[atomicAdd(&sm.n_chosen, 1)] = static_cast<int32_t>(~static_cast<uint32_t>(c[w]));
-            else if (mk == prefix) sm.shortl[atomicAdd(&sm.n_short, 1)] = c[w];
-        }
-    }
-    __syncthreads();
-    rank_take_desc<kSpNT>(sm.shortl, sm.n_short, rem, sm.chosen + (keep - rem));
-    if (tid == 0) sm.chosen[keep] = o;
-    rank_write_ascending<kSpNT>(sm.chosen, keep + 1, out);
-    for (int k = keep + 1 + tid; k < budget; k += kSpNT) out[k] = -1;
+    finish_from_candidates<kSpNT, kSpWaves>(c, cv, total, keep, o, budget, out, sm.res);
 }
 
 hipError_t launch_select(const float* scores, int64_t ld, int64_t ss, const Positions& pos0,
-                         int batch, int tq, int budget, int32_t* sel, int64_t sels,
+                         int batch, int tq, int budget, int32_t* sel, int64_t sels, int* flags,
                          hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(batch) * tq;
     if (rows == 0) return hipSuccess;
-    if (budget <= kSpMaxBudget) {
+    if (budget <= kResMaxBudget) {
         hipLaunchKernelGGL(select_sampled_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSpNT), 0, stream,
-                           scores, ld, ss, pos0, tq, budget, sel, sels);
+                           scores, ld, ss, pos0, tq, budget, sel, sels, flags);
     } else if (rows < 1024) {
         hipLaunchKernelGGL(select_kernel<1024>, dim3(static_cast<unsigned>(rows)), dim3(1024), 0,
-                           stream, scores, ld, ss, pos0, tq, budget, sel, sels);
+                           stream, scores, ld, ss, pos0, tq, budget, sel, sels, flags);
     } else {
         hipLaunchKernelGGL(select_kernel<256>, dim3(static_cast<unsigned>(rows)), dim3(256), 0,
-                           stream, scores, ld, ss, pos0, tq, budget, sel, sels);
+                           stream, scores, ld, ss, pos0, tq, budget, sel, sels, flags);
     }
     return hipGetLastError();
 }

@@ -282,4 +282,109 @@ __device__ void select_row(const float* __restrict__ row, int o, int keep, int b
     write_selection<NT>(sm, keep, o, budget, out);
 }
 
+// ---------------------------------------------------------------------------
+// Pieces of the threshold-based selections (the single-read select and the
+// fused prefill index-select): a key threshold estimated from a sample, and
+// the exact finish among the candidates at or above it.
+
+constexpr int kResShort = 256;        // threshold-bin members resolved by ranking
+constexpr int kResMaxBudget = 1024;   // budgets the threshold paths serve
+
+struct ResolveSmem {
+    alignas(16) uint64_t shortl[kResShort + 2];
+    alignas(16) int32_t chosen[kResMaxBudget];
+    uint32_t hist[2048];
+    int wave_tot[16];
+    int n_chosen, n_short, sh_above;
+    uint32_t sh_bin;
+};
+
+// float whose score_key is `key` (key must not be the image of a NaN pattern)
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Expected number of candidates the threshold aims at for a row keeping
+// `keep`: far above keep (a short count forces the exact fallback) and far
+// below the capacities of the candidate buffers.
+__device__ __forceinline__ int threshold_target(int keep) { return 2 * keep + 512; }
+
+// Key threshold from sample keys held PER per thread: the lower edge of the
+// 22-bit key prefix holding the r-th largest sample key (two 11-bit radix
+// levels in LDS).  Returned as the float to compare scores against; a quiet
+// NaN (no score passes) when the threshold would sit at or below -inf.
+template <int NT, int PER>
+__device__ float sample_threshold(const uint32_t (&sk)[PER], int r, ResolveSmem& sm) {
+    const int tid = threadIdx.x;
+    for (int k = tid; k < 2048; k += NT) sm.hist[k] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) atomicAdd(&sm.hist[sk[e] >> 21], 1u);
+    __syncthreads();
+    find_threshold_bin<NT>(sm.hist, 2048, r, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
+    const uint32_t b1 = sm.sh_bin;
+    const int r2 = r - sm.sh_above;
+    __syncthreads();
+    for (int k = tid; k < 2048; k += NT) sm.hist[k] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+        if ((sk[e] >> 21) == b1) atomicAdd(&sm.hist[(sk[e] >> 10) & 2047u], 1u);
+    __syncthreads();
+    find_threshold_bin<NT>(sm.hist, 2048, r2, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
+    const uint32_t tkey = (b1 << 21) | (sm.sh_bin << 10);
+    __syncthreads();
+    return tkey <= 0x007fffffu ? __uint_as_float(0x7fc00000u) : key_to_float(tkey);
+}
+
+// Exact top `keep` (descending key, then ascending j) among `total` distinct
+// candidates (key << 32 | ~j), K per thread in registers (valid where cv),
+// that contain the row's true top `keep`; writes them and the own block o
+// ascending into out[0 .. budget), padded with -1.  Radix passes over the
+// 64-bit entries until the threshold bin holds at most kResShort, which are
+// ranked.  keep < kResMaxBudget.
+template <int NT, int K>
+__device__ void finish_from_candidates(const uint64_t (&c)[K], const bool (&cv)[K], int total, int keep, int o,
+                                       int budget, int32_t* out, ResolveSmem& sm) {
+    const int tid = threadIdx.x;
+    uint64_t prefix = 0ull, pmask = 0ull;
+    int rem = keep;
+    int bin_count = total;
+    for (int sh = 53; bin_count > kResShort; sh = max(sh - 11, 0)) {
+        for (int k = tid; k < 2048; k += NT) sm.hist[k] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < K; ++w)
+            if (cv[w] && (c[w] & pmask) == prefix)
+                atomicAdd(&sm.hist[static_cast<uint32_t>(c[w] >> sh) & 2047u], 1u);
+        __syncthreads();
+        find_threshold_bin<NT>(sm.hist, 2048, rem, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
+        const uint32_t tb = sm.sh_bin;
+        rem -= sm.sh_above;
+        prefix |= static_cast<uint64_t>(tb) << sh;
+        pmask |= 2047ull << sh;
+        bin_count = static_cast<int>(sm.hist[tb]);
+        __syncthreads();
+        if (sh == 0) break;
+    }
+    if (tid == 0) {
+        sm.n_chosen = 0;
+        sm.n_short = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < K; ++w) {
+        if (cv[w]) {
+            const uint64_t mk = c[w] & pmask;
+            if (mk > prefix) sm.chosen[atomicAdd(&sm.n_chosen, 1)] = static_cast<int32_t>(~static_cast<uint32_t>(c[w]));
+            else if (mk == prefix) sm.shortl[atomicAdd(&sm.n_short, 1)] = c[w];
+        }
+    }
+    __syncthreads();
+    rank_take_desc<NT>(sm.shortl, sm.n_short, rem, sm.chosen + (keep - rem));
+    if (tid == 0) sm.chosen[keep] = o;
+    rank_write_ascending<NT>(sm.chosen, keep + 1, out);
+    for (int k = keep + 1 + tid; k < budget; k += NT) out[k] = -1;
+}
+
 }  // namespace qsa

@@ -43,6 +43,9 @@ _SIGNATURES = {
     "qsa_index_scores": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _c_p, _i64, _i64, _c_p]),
     "qsa_select_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "qsa_select_topk": (_i32, [_c_p, _i64, _i64, _c_p, _i32, _i32, _i32, _c_p, _i64, _c_p, _sz, _c_p]),
+    "qsa_index_select_prefill_workspace_bytes": (_sz, [_i32, _i32]),
+    "qsa_index_select_prefill": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, _c_p, _i64, _i64,
+                                        _c_p, _i64, _c_p, _sz, _c_p]),
     "qsa_sparse_attn_prefill": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32,
                                        _i32, ctypes.c_float, _c_p, _i64, _c_p, _i64, _c_p]),
     "qsa_decode_workspace_bytes": (_sz, [_i32, _i32]),
@@ -261,15 +264,44 @@ def sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
 
 # ------------------------------------------------------------------ chained steps
 
+def index_select_prefill_workspace(batch: int, tq: int, device="cuda") -> torch.Tensor:
+    """Workspace of the fused prefill index-select (any contents; reusable across calls)."""
+    n = lib().qsa_index_select_prefill_workspace_bytes(batch, tq)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def index_select_prefill(q_idx: torch.Tensor, kbar: torch.Tensor, q_pos0, budget: int, scores: torch.Tensor,
+                         sel: torch.Tensor, workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """Steps 2 + 3 for a prefill chunk (same result as index_scores + select_topk):
+    q_idx [B, T, 4, 128], scores [B, >= T, ld] scratch, sel [B, T, budget]."""
+    _need(q_idx, "q_idx", torch.bfloat16, (HI, DI))
+    _need(kbar, "kbar", torch.bfloat16, (DI,))
+    _need(scores, "scores", torch.float32, ())
+    _need(sel, "sel", torch.int32, (budget,))
+    B, T = q_idx.shape[0], q_idx.shape[1]
+    pos = _positions(q_pos0, B)
+    need = max((int(pos[b]) + T - 1) // BLOCK for b in range(B)) if T else 0
+    if scores.shape[0] != B or scores.shape[1] < T or kbar.shape[0] != B or kbar.shape[1] < need:
+        raise QSAError("scores / kbar shapes do not cover the queries")
+    if sel.shape[0] != B or sel.shape[1] != T:
+        raise QSAError("sel must be [B, T, budget]")
+    _check(lib().qsa_index_select_prefill(_ptr(q_idx), q_idx.stride(0), _ptr(kbar), kbar.stride(0), pos, B, T,
+                                          budget, _ptr(scores), scores.stride(1), scores.stride(0), _ptr(sel),
+                                          sel.stride(0), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "qsa_index_select_prefill")
+    return sel
+
+
 class PrefillBuffers:
-    """Device buffers for one prefill layer call: scores for one query chunk
-    and the per-token selection."""
+    """Device buffers for one prefill layer call: scratch scores for one query
+    chunk, the fused index-select workspace and the per-token selection."""
 
     def __init__(self, batch: int, tq: int, ctx: int, budget: int, chunk: int | None, device="cuda"):
         self.chunk = min(tq, chunk or tq)
         ld = max(4, ((ctx + tq - 1) // BLOCK + 3) // 4 * 4)
         self.scores = torch.empty((batch, self.chunk, ld), dtype=torch.float32, device=device)
         self.sel = torch.empty((batch, tq, budget), dtype=torch.int32, device=device)
+        self.workspace = index_select_prefill_workspace(batch, self.chunk, device=device)
 
 
 def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0: int, budget: int,
@@ -280,7 +312,7 @@ def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0
     rotated K rows are written into k_cache[:, q_pos0 : q_pos0 + tq] (V rows
     are expected in v_cache already, k_idx rows in k_idx).  Steps: rotary
     (Q -> q_rot, K -> cache), compress the blocks the chunk completes, then per
-    query chunk index scores -> selection, then attention.
+    query chunk the fused index-select, then attention.
     """
     B, tq = q_raw.shape[0], q_raw.shape[1]
     pos = [q_pos0] * B
@@ -291,8 +323,8 @@ def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0
     for c0 in range(0, tq, bufs.chunk):
         c1 = min(tq, c0 + bufs.chunk)
         cpos = [q_pos0 + c0] * B
-        index_scores(q_idx[:, c0:c1], kbar, cpos, bufs.scores, stream=stream)
-        select_topk(bufs.scores, cpos, budget, bufs.sel[:, c0:c1], stream=stream)
+        index_select_prefill(q_idx[:, c0:c1], kbar, cpos, budget, bufs.scores, bufs.sel[:, c0:c1],
+                             bufs.workspace, stream=stream)
         sparse_attn_prefill(q_rot[:, c0:c1], k_cache, v_cache, bufs.sel[:, c0:c1], cpos, out[:, c0:c1],
                             None if lse is None else lse[:, c0:c1], stream=stream)
     return out

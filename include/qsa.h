@@ -15,6 +15,7 @@
  *   qsa_compress_block_keys  indexer keys -> block keys          (step 1)
  *   qsa_index_scores         block scores of the MQA indexer     (step 2)
  *   qsa_select_topk          per-token top-(budget-1) + own block (step 3)
+ *   qsa_index_select_prefill steps 2 + 3 for a prefill chunk, no score matrix
  *   qsa_sparse_attn_prefill  attention over the selected tokens  (step 4)
  *   qsa_sparse_attn_decode   the same for one new token per sequence
  *
@@ -130,6 +131,32 @@ qsa_status_t qsa_select_topk(const float* scores, int64_t scores_ld, int64_t sco
                              const int32_t* q_pos0, int32_t batch, int32_t tq, int32_t budget,
                              int32_t* sel, int64_t sel_seq_stride,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Steps 2 + 3 fused for a prefill chunk (blog "Attention: GDN + QSA": blocks
+ * are scored and the most relevant kept): the same selection as
+ * qsa_index_scores followed by qsa_select_topk, bit for bit, without
+ * materialising the score matrix when the chunk is long.  The indexer first
+ * scores a fixed sample of 8192 blocks per row to set a per-row threshold,
+ * then scores every block keeping only those at or above it, and an exact
+ * radix select finishes each row from that list.  Rows whose list is short
+ * or overflows are redone exactly from full scores, so the result never
+ * depends on the threshold.  The fused path is taken when budget <= 1024 and
+ * every sequence's first row sees at least 16384 blocks; otherwise the call
+ * runs qsa_index_scores + qsa_select_topk.
+ * scores [B][tq][ld] float, laid out as for qsa_index_scores, is scratch for
+ * those exact paths (its contents are unspecified afterwards); sel
+ * [B][tq][budget].  The workspace (qsa_index_select_prefill_workspace_bytes,
+ * about 64 KiB per query row, 256-byte aligned) needs no initialisation;
+ * calls that share a workspace must not overlap.
+ */
+size_t       qsa_index_select_prefill_workspace_bytes(int32_t batch, int32_t tq);
+qsa_status_t qsa_index_select_prefill(const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                      const uint16_t* kbar, int64_t kbar_seq_stride,
+                                      const int32_t* q_pos0, int32_t batch, int32_t tq, int32_t budget,
+                                      float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                      int32_t* sel, int64_t sel_seq_stride,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Step 4 -- sparse grouped-query attention (model card: 24 Q heads, 2 KV

@@ -108,6 +108,29 @@ def test_select_validation(L):
     assert L.qsa_select_workspace_bytes(1, 8192, 512) == 0
 
 
+def test_index_select_prefill_validation(L):
+    p = _pos(70000)
+    need = L.qsa_index_select_prefill_workspace_bytes(1, 10)
+    assert need >= 10 * (4096 * 8 + 8192 * 4)
+    assert L.qsa_index_select_prefill_workspace_bytes(0, 10) == 0
+    ld = (70000 + 9) // 4 // 4 * 4 + 4
+    # every call below is invalid somewhere, so nothing is launched
+    assert L.qsa_index_select_prefill(FAKE, 0, FAKE, 0, p, 1, 10, 0, FAKE, ld, 0, FAKE, 0, FAKE, need, None) == INVALID
+    assert "budget" in _err(L)
+    assert L.qsa_index_select_prefill(FAKE, 0, FAKE, 0, p, 1, 10, 512, FAKE, ld - 8, 0, FAKE, 0, FAKE, need,
+                                      None) == INVALID
+    assert L.qsa_index_select_prefill(FAKE, 0, FAKE, 0, p, 1, 10, 512, FAKE, ld, 0, NULL, 0, FAKE, need,
+                                      None) == INVALID
+    assert L.qsa_index_select_prefill(FAKE, 0, FAKE, 0, p, 1, 10, 512, FAKE, ld, 0, FAKE, 0, FAKE, need - 1,
+                                      None) == WORKSPACE
+    assert L.qsa_index_select_prefill(FAKE, 0, FAKE, 0, p, 1, 10, 512, FAKE, ld, 0, FAKE, 0, NULL, need,
+                                      None) == WORKSPACE
+    assert L.qsa_index_select_prefill(FAKE, 0, FAKE, 0, p, 1, 10, 512, FAKE, ld, 0, FAKE, 0, FAKE + 16, need,
+                                      None) == INVALID       # workspace alignment
+    assert L.qsa_index_select_prefill(FAKE, 0, FAKE, 0, p, 1, 0, 512, FAKE, ld, 0, FAKE, 0, NULL, 0,
+                                      None) == OK            # nothing to do
+
+
 def test_attention_validation(L):
     p = _pos(40)
     # only invalid combinations are exercised: a valid one would launch

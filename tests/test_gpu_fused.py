@@ -4,7 +4,10 @@ The fused decode index-select and the one-call decode step must produce the
 same scores, selection, output and LSE bits as rope_apply + index_scores +
 select_topk + sparse_attn_decode on the same inputs, including score patterns
 that overflow the fused path's candidate capacity (exact fallback), and must
-leave their workspace zeroed for the next call.
+leave their workspace zeroed for the next call.  The fused prefill
+index-select must give the selection of index_scores + select_topk on its
+fast path, on every fallback trigger (tie floods, a sample that overstates
+the tail) and on the shapes that bypass it, with a reused workspace.
 """
 
 import math
@@ -109,3 +112,86 @@ def test_decode_step_matches_primitives(ctx, budget, B):
         outs.append((kc[:, ctx].clone(), scores[:, 0, :ctx // 4].clone(), sel.clone(), out.clone(), lse.clone()))
     for name, a, b in zip(("k row", "scores", "sel", "out", "lse"), outs[0], outs[1]):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+
+
+# ---------------------------------------------------------------- prefill index-select
+
+def _run_starts(omin):
+    """First block of each of the 32 sampled runs of 256 blocks (spread over [0, omin))."""
+    return [r * (omin - 256) // 31 for r in range(32)]
+
+
+def _prefill_kbar(kind, B, nblk, seed, pos0):
+    if kind in ("normal", "equal", "few_values"):
+        return _kbar(kind, B, nblk, seed)
+    if kind == "sample_high":    # the sampled runs outrank the rest: the sample overstates the tail
+        kb = _rand((B, nblk, 128), seed, 1 / math.sqrt(512)) * 0.01
+        for b in range(B):
+            for s in _run_starts(pos0[b] // 4):
+                kb[b, s:s + 256] = kb[b, s:s + 256] * 100 + 0.05
+        return kb.to(torch.bfloat16)
+    raise ValueError(kind)
+
+
+PREFILL_CASES = [
+    ("normal", [70000, 70000], 700, 512, "fused"),
+    ("normal", [70000, 91003], 333, 64, "fused"),
+    ("normal", [80000], 1000, 1024, "fused"),
+    ("normal", [80000], 200, 1025, "unfused"),
+    ("normal", [30000], 300, 512, "unfused"),
+    ("equal", [70000, 70000], 300, 512, "fallback"),
+    ("few_values", [66000], 500, 512, "either"),
+    ("sample_high", [160000], 256, 512, "fallback"),
+]
+
+
+@pytest.mark.parametrize("kind,pos0,tq,budget,path", PREFILL_CASES,
+                         ids=[f"{c[0]}-{c[1][0]}-{c[2]}-{c[3]}" for c in PREFILL_CASES])
+def test_index_select_prefill_matches_primitives(kind, pos0, tq, budget, path):
+    say(f"index_select_prefill {kind} pos0={pos0} tq={tq} budget={budget} ({path})")
+    B = len(pos0)
+    nblk = max((p + tq - 1) // 4 for p in pos0) + 1
+    q = _rand((B, tq, 4, 128), tq + budget, 1 / math.sqrt(128)).cuda()
+    if kind == "sample_high":    # every query row leans the same way so the high blocks rank first
+        q = (q.float() * 0.1 + 0.05).to(torch.bfloat16)
+    kbar = _prefill_kbar(kind, B, nblk, budget, pos0).cuda()
+    ld = (nblk + 3) // 4 * 4
+    s_ref = torch.empty((B, tq, ld), device="cuda")
+    sel_ref = torch.empty((B, tq, budget), dtype=torch.int32, device="cuda")
+    qsa.index_scores(q, kbar, pos0, s_ref)
+    qsa.select_topk(s_ref, pos0, budget, sel_ref)
+    ws = qsa.index_select_prefill_workspace(B, tq)
+    ws.fill_(0xA5)                                    # no initialisation is required
+    for rep in range(2):                              # the second call reuses the workspace
+        scratch = torch.empty((B, tq, ld), device="cuda")
+        sel = torch.full((B, tq, budget), -7, dtype=torch.int32, device="cuda")
+        qsa.index_select_prefill(q, kbar, pos0, budget, scratch, sel, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, sel_ref), (rep, int((sel != sel_ref).any(dim=-1).sum()))
+        if path != "unfused":
+            n_flagged = int(ws[:4].view(torch.int32)[0])
+            say(f"  rows taking the exact fallback: {n_flagged} of {B * tq}")
+            if path == "fused":
+                assert n_flagged == 0
+            elif path == "fallback":
+                assert n_flagged > 0
+
+
+def test_index_select_prefill_workspace_reuse_across_shapes():
+    say("index_select_prefill: one workspace, shapes that change between calls")
+    ws = qsa.index_select_prefill_workspace(2, 600)
+    for (kind, pos0, tq, budget) in [("equal", [70000, 70000], 600, 512), ("normal", [72000], 250, 512),
+                                     ("normal", [70000, 75000], 600, 300)]:
+        B = len(pos0)
+        nblk = max((p + tq - 1) // 4 for p in pos0) + 1
+        q = _rand((B, tq, 4, 128), tq, 1 / math.sqrt(128)).cuda()
+        kbar = _prefill_kbar(kind, B, nblk, 3, pos0).cuda()
+        ld = (nblk + 3) // 4 * 4
+        s_ref = torch.empty((B, tq, ld), device="cuda")
+        sel_ref = torch.empty((B, tq, budget), dtype=torch.int32, device="cuda")
+        qsa.index_scores(q, kbar, pos0, s_ref)
+        qsa.select_topk(s_ref, pos0, budget, sel_ref)
+        sel = torch.empty_like(sel_ref)
+        qsa.index_select_prefill(q, kbar, pos0, budget, torch.empty_like(s_ref), sel, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, sel_ref), (kind, pos0, tq)

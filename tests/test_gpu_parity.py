@@ -297,6 +297,26 @@ def test_end_to_end_prefill_with_prefix_and_chunks():
                  lambda b, t: out[b, t - wl.ctx], lambda b, t: lse[b, t - wl.ctx])
 
 
+def test_end_to_end_prefill_long_context_fused_select():
+    """A chunk long enough for the fused index-select (its rows see > 16384
+    blocks), sampled rows and every needle against the oracle."""
+    wl = I.custom_workload("prefill", batch=1, ctx=70001, tq=1024, budget=512, n_needles=8, seed=5, chunk=512)
+    say(f"end-to-end {wl.name}")
+    x = I.make_inputs(wl)
+    dp = DevicePrefill(x)
+    dp.run()
+    sel = dp.bufs.sel.cpu().numpy()
+    out = dp.out.float().cpu().numpy()
+    lse = dp.lse.cpu().numpy()
+    n_flagged = int(dp.bufs.workspace[:4].view(torch.int32)[0].item())
+    say(f"  rows that took the exact fallback in the last chunk: {n_flagged}")
+    layer = oracle_layer(x)
+    rows = [(0, wl.ctx + i) for i in range(0, wl.tq, 16)] + [(int(b), int(t)) for b, t, _ in x.needles]
+    rows = sorted(set(rows))
+    compare_rows(layer, x, rows, None, lambda b, t: sel[b, t - wl.ctx],
+                 lambda b, t: out[b, t - wl.ctx], lambda b, t: lse[b, t - wl.ctx])
+
+
 def test_end_to_end_decode_B32_ctx32K():
     wl = I.WORKLOADS["decode_B32_ctx32K"]
     say(f"end-to-end {wl.name}")
