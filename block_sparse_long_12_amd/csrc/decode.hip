@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(
 }
 
 constexpr int kFinNT = 1024;                 // finalize threads
-constexpr int kBitmapWords = 8192;           // ascending order by bitmap for blocks < 262144
+constexpr int kBitmapWords = 8192;           // ascending order by bitmap for candidates j < 262144
 
 struct FinalizeSmem {
     union {
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         const int32_t* __restrict__ defl = ws.defl + static_cast<int64_t>(b) * QSA_MAX_BUDGET;
         const uint64_t* __restrict__ cg = ws.cand + static_cast<int64_t>(b) * kDecCap;
         int32_t* chosen = sm.u.m.chosen;
-        const bool bitmap = o <= 32 * kBitmapWords;
+        const bool bitmap = o <= 32 * kBitmapWords;             // every chosen j < o has a bit; o goes last
         if (bitmap)
             for (int k = tid; k < kBitmapWords; k += kFinNT) sm.u.m.bm[k] = 0u;
         for (int k = tid; k < above; k += kFinNT) chosen[k] = defl[k];
@@ -322,10 +322,11 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         }
         __syncthreads();
         if (bitmap) {
-            for (int k = tid; k <= keep; k += kFinNT) {
+            for (int k = tid; k < keep; k += kFinNT) {
                 const int v = chosen[k];
                 atomicOr(&sm.u.m.bm[v >> 5], 1u << (v & 31));
             }
+            if (tid == 0) out[keep] = o;                     // above every candidate
             __syncthreads();
             // thread t owns words 8t .. 8t+7: prefix count of set bits, then emit in order
             constexpr int kWpt = kBitmapWords / kFinNT;

@@ -42,6 +42,7 @@ def _kbar(kind, B, nblk, seed):
 
 
 CASES = [("normal", [1048576 // 16, 70001, 4096 + 3], 512), ("normal", [9000, 9001, 9002], 64),
+         ("normal", [1048576, 1048575, 1048579], 512),      # own block 262144 / 262143: bitmap edge
          ("equal", [40000, 40000, 40000], 512), ("few_values", [50000, 12345, 8000], 512),
          ("normal", [100, 2047, 2048], 512), ("normal", [3, 50000, 7], 1), ("normal", [20000, 1, 20001], 2)]
 
