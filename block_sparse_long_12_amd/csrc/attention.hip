@@ -189,12 +189,17 @@ __device__ __forceinline__ void load_q_frags(const uint16_t* qh, bool ok, int p,
     for (int ks = 0; ks < 8; ++ks)
         qf[ks] = ok ? *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * G) : bf16x8_t{};
     if (rope != nullptr) {
+        // each lane evaluates one of the 32 angles (the same call as
+        // rope_row_wave), then takes the 8 its k slice needs from its peers
+        const int lane = threadIdx.x & 63;
+        double sn_l, cs_l;
+        sincos(static_cast<double>(p) * rope->f[lane & 31], &sn_l, &cs_l);
         uint16_t* lo = reinterpret_cast<uint16_t*>(&qf[0]);
         uint16_t* hi = reinterpret_cast<uint16_t*>(&qf[1]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            double sn, cs;
-            sincos(static_cast<double>(p) * rope->f[8 * G + e], &sn, &cs);
+            const double cs = __shfl(cs_l, 8 * G + e);
+            const double sn = __shfl(sn_l, 8 * G + e);
             const double a = bf16_to_f32(lo[e]);
             const double b = bf16_to_f32(hi[e]);
             lo[e] = rotate_half_elem(a, b, cs, sn, true);
