@@ -20,8 +20,8 @@
 //   sample  -- the same over a fixed sample of blocks (32 evenly spread runs
 //              of 256), stored compactly; feeds the per-row thresholds;
 //   collect -- no score matrix: scores at or above the row's threshold are
-//              appended to an LDS list and, at the end, to the row's global
-//              candidate list (one atomic per row and workgroup).
+//              appended to per-wave LDS lists and, at the end, to the row's
+//              global candidate list (one atomic per row and workgroup).
 // Causality: a workgroup stops at the last block its last row sees; collect
 // also drops each row's blocks at or past its own block.
 #include "index_common.h"
@@ -49,7 +49,7 @@ __shared__ KTile tA, tB, tC;
 __shared__ uint64_t lcand[kCollectCap];
 __shared__ int lrow[kWgTok];
 __shared__ int lrow_base[kWgTok];
-__shared__ int lcount;
+__shared__ int lwcnt[4];
 
 // Block of column jv: itself, or in sample mode run jv / 256 of 32 runs of
 // 256 blocks spread evenly over [0, omin).
@@ -150,31 +150,31 @@ __device__ __forceinline__ void store_step(const KTile& t, const bf16x8_t (&qf)[
 
 // collect: append (key << 32 | row_local << 16 | (j - j_begin)) for every
 // score of the lane's row at or above its threshold tau, for blocks below
-// lim (the row's own block and the chunk end).  For a number tau whose key
-// has zero low bits, score >= tau (IEEE) holds exactly when score_key(score)
-// >= score_key(tau); a NaN tau passes nothing.
+// lim (the row's own block and the chunk end), to the wave's own LDS list:
+// one ballot per score slot, positions by mbcnt, the count kept wave-uniform
+// (no atomics).  For a number tau whose key has zero low bits, score >= tau
+// (IEEE) holds exactly when score_key(score) >= score_key(tau); a NaN tau
+// passes nothing.
 __device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf)[16], int j0, int lim,
-                                             float tau, int row_local, int j_begin) {
+                                             float tau, int row_local, int j_begin, uint64_t* seg, int& cnt) {
     f32x4_t acc[4];
     step_scores(t, qf, acc);
     const int lane = threadIdx.x & 63;
     const int jl = j0 + 4 * (lane >> 4);
-    uint32_t qmask = 0;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-            if (jl + 16 * nt + n < lim && acc[nt][n] >= tau) qmask |= 1u << (4 * nt + n);
-    if (qmask != 0u) {
-        int k = atomicAdd(&lcount, __popc(qmask));
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            if (qmask & (1u << e)) {
-                if (k < kCollectCap)
-                    lcand[k] = (static_cast<uint64_t>(score_key(acc[e >> 2][e & 3])) << 32) |
+    for (int e = 0; e < 16; ++e) {
+        const bool q = jl + 16 * (e >> 2) + (e & 3) < lim && acc[e >> 2][e & 3] >= tau;
+        const uint64_t m = __ballot(q);
+        if (m != 0ull) {                                  // wave-uniform
+            if (q) {
+                const int pos = cnt + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                          static_cast<uint32_t>(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+                if (pos < kCollectCap / 4)
+                    seg[pos] = (static_cast<uint64_t>(score_key(acc[e >> 2][e & 3])) << 32) |
                                static_cast<uint32_t>((row_local << 16) | (jl + 16 * (e >> 2) + (e & 3) - j_begin));
-                ++k;
             }
+            cnt += __popcll(m);
         }
     }
 }
@@ -226,7 +226,8 @@ __global__ __launch_bounds__(256) void index_kernel(
         const float tau = tok < tq ? col.tau[row] : __uint_as_float(0x7fc00000u);
         const int lim = min((pos0.p[b] + tok) / kBlock, j_end);
         if (threadIdx.x < kWgTok) lrow[threadIdx.x] = 0;
-        if (threadIdx.x == 0) lcount = 0;
+        uint64_t* seg = lcand + wave * (kCollectCap / 4);    // this wave's list
+        int cnt = 0;
         __builtin_amdgcn_s_waitcnt(0x0f70);               // q and tau in registers before the pipeline starts
         __syncthreads();
         // two LDS buffers: step s + 1 loads while step s is scored; the loop
@@ -235,17 +236,21 @@ __global__ __launch_bounds__(256) void index_kernel(
         for (int s = 0; s < n_steps; s += 2) {
             wait_and_meet<0>();
             stage_dma<kMode>(kb, j_begin + kColStep * (s + 1), j_end, omin, tB);
-            if (has_rows) collect_step(tA, qf, j_begin + kColStep * s, lim, tau, tok - t_wg, j_begin);
+            if (has_rows) collect_step(tA, qf, j_begin + kColStep * s, lim, tau, tok - t_wg, j_begin, seg, cnt);
             if (s + 1 >= n_steps) break;
             wait_and_meet<0>();
             stage_dma<kMode>(kb, j_begin + kColStep * (s + 2), j_end, omin, tA);
-            if (has_rows) collect_step(tB, qf, j_begin + kColStep * (s + 1), lim, tau, tok - t_wg, j_begin);
+            if (has_rows) collect_step(tB, qf, j_begin + kColStep * (s + 1), lim, tau, tok - t_wg, j_begin, seg, cnt);
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);               // no load into LDS outlives the workgroup
         __syncthreads();
-        // hand the list to the rows: count per row, one global reservation per row
-        const int n = lcount;
-        if (n > kCollectCap) {                            // list overflow: every row of the tile falls back
+        // hand the lists to the rows: count per row, one global reservation per row
+        if (lane == 0) lwcnt[wave] = cnt;
+        __syncthreads();
+        bool overflow = false;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) overflow |= lwcnt[w] > kCollectCap / 4;
+        if (overflow) {                                   // a list overflowed: every row of the tile falls back
             if (threadIdx.x < n_tok_wg) atomicAdd(&col.row_cnt[static_cast<int64_t>(b) * tq + t_wg + threadIdx.x], kRowCap + 1);
             return;
         }
@@ -253,7 +258,8 @@ __global__ __launch_bounds__(256) void index_kernel(
 #pragma unroll
         for (int k = 0; k < kCollectCap / 256; ++k) {
             const int i = threadIdx.x + 256 * k;
-            slot[k] = (i < n) ? atomicAdd(&lrow[(lcand[i] >> 16) & 63], 1) : 0;
+            const bool v = (i % (kCollectCap / 4)) < lwcnt[i / (kCollectCap / 4)];
+            slot[k] = v ? atomicAdd(&lrow[(lcand[i] >> 16) & 63], 1) : -1;
         }
         __syncthreads();
         if (threadIdx.x < n_tok_wg && lrow[threadIdx.x] > 0)
@@ -262,7 +268,7 @@ __global__ __launch_bounds__(256) void index_kernel(
 #pragma unroll
         for (int k = 0; k < kCollectCap / 256; ++k) {
             const int i = threadIdx.x + 256 * k;
-            if (i < n) {
+            if (slot[k] >= 0) {
                 const uint64_t e = lcand[i];
                 const int rl = static_cast<int>((e >> 16) & 63);
                 const int pos = lrow_base[rl] + slot[k];
