@@ -100,6 +100,7 @@ __global__ __launch_bounds__(kThrNT) void threshold_kernel(const float* __restri
 __global__ __launch_bounds__(kFinNT) void prefill_finalize_kernel(Positions pos0, int tq, int budget, PrefillWs ws,
                                                                   int32_t* __restrict__ sel, int64_t sels) {
     __shared__ ResolveSmem sm;
+    __shared__ uint32_t bitmap[kResBitmapWords];
     __shared__ int sh_n;
     const int64_t row = blockIdx.x;
     const int b = static_cast<int>(row / tq);
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(kFinNT) void prefill_finalize_kernel(Positions pos0
         cv[k] = idx < n;
         c[k] = cv[k] ? lst[idx] : 0ull;
     }
-    finish_from_candidates<kFinNT, K>(c, cv, n, keep, o, budget, out, sm);
+    finish_from_candidates<kFinNT, K>(c, cv, n, keep, o, budget, out, sm, bitmap);
 }
 
 hipError_t launch_prefill_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,

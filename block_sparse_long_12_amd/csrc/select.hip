@@ -175,7 +175,9 @@ __global__ __launch_bounds__(kSpNT) void select_sampled_kernel(const float* __re
         cv[w] = tid < sm.seg_cnt[w];
         c[w] = cv[w] ? sm.cand[w * kSpSeg + tid] : 0ull;
     }
-    finish_from_candidates<kSpNT, kSpWaves>(c, cv, total, keep, o, budget, out, sm.res);
+    __syncthreads();                                      // every thread holds its candidates: the list is free
+    finish_from_candidates<kSpNT, kSpWaves>(c, cv, total, keep, o, budget, out, sm.res,
+                                            reinterpret_cast<uint32_t*>(sm.cand));
 }
 
 hipError_t launch_select(const float* scores, int64_t ld, int64_t ss, const Positions& pos0,

@@ -290,10 +290,13 @@ __device__ void select_row(const float* __restrict__ row, int o, int keep, int b
 constexpr int kResShort = 256;        // threshold-bin members resolved by ranking
 constexpr int kResMaxBudget = 1024;   // budgets the threshold paths serve
 
+constexpr int kResBitmapWords = 8192;  // ascending output by bitmap for o <= 262144
+
 struct ResolveSmem {
     alignas(16) uint64_t shortl[kResShort + 2];
     alignas(16) int32_t chosen[kResMaxBudget];
     uint32_t hist[2048];
+    uint64_t wave_hi[16], wave_lo[16];
     int wave_tot[16];
     int n_chosen, n_short, sh_above;
     uint32_t sh_bin;
@@ -341,16 +344,51 @@ __device__ float sample_threshold(const uint32_t (&sk)[PER], int r, ResolveSmem&
 // candidates (key << 32 | ~j), K per thread in registers (valid where cv),
 // that contain the row's true top `keep`; writes them and the own block o
 // ascending into out[0 .. budget), padded with -1.  Radix passes over the
-// 64-bit entries until the threshold bin holds at most kResShort, which are
-// ranked.  keep < kResMaxBudget.
+// 64-bit entries, the first digit placed just below the bits every candidate
+// shares (from the largest and smallest entry), until the threshold bin holds
+// at most kResShort, which are ranked.  The ascending output goes through a
+// bitmap of the blocks when `bitmap` (kResBitmapWords words of free LDS) is
+// given and o fits it, else by counting.  keep < kResMaxBudget.
 template <int NT, int K>
 __device__ void finish_from_candidates(const uint64_t (&c)[K], const bool (&cv)[K], int total, int keep, int o,
-                                       int budget, int32_t* out, ResolveSmem& sm) {
+                                       int budget, int32_t* out, ResolveSmem& sm, uint32_t* bitmap) {
     const int tid = threadIdx.x;
-    uint64_t prefix = 0ull, pmask = 0ull;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    // the bits all candidates share
+    uint64_t hi = 0ull, lo = ~0ull;
+#pragma unroll
+    for (int w = 0; w < K; ++w) {
+        if (cv[w]) {
+            hi = c[w] > hi ? c[w] : hi;
+            lo = c[w] < lo ? c[w] : lo;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t h2 = __shfl_xor(hi, off);
+        const uint64_t l2 = __shfl_xor(lo, off);
+        hi = h2 > hi ? h2 : hi;
+        lo = l2 < lo ? l2 : lo;
+    }
+    if (lane == 0) {
+        sm.wave_hi[wave] = hi;
+        sm.wave_lo[wave] = lo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        hi = sm.wave_hi[w] > hi ? sm.wave_hi[w] : hi;
+        lo = sm.wave_lo[w] < lo ? sm.wave_lo[w] : lo;
+    }
+    const uint64_t diff = hi ^ lo;
+    const int top = diff ? 63 - __clzll(diff) : 0;       // highest bit where candidates differ
+    int sh = top > 10 ? top - 10 : 0;
+    uint64_t pmask = (sh + 11 >= 64) ? 0ull : ~((1ull << (sh + 11)) - 1ull);
+    uint64_t prefix = hi & pmask;
     int rem = keep;
     int bin_count = total;
-    for (int sh = 53; bin_count > kResShort; sh = max(sh - 11, 0)) {
+    while (bin_count > kResShort) {
         for (int k = tid; k < 2048; k += NT) sm.hist[k] = 0u;
         __syncthreads();
 #pragma unroll
@@ -366,6 +404,7 @@ __device__ void finish_from_candidates(const uint64_t (&c)[K], const bool (&cv)[
         bin_count = static_cast<int>(sm.hist[tb]);
         __syncthreads();
         if (sh == 0) break;
+        sh = sh > 11 ? sh - 11 : 0;
     }
     if (tid == 0) {
         sm.n_chosen = 0;
@@ -382,8 +421,38 @@ __device__ void finish_from_candidates(const uint64_t (&c)[K], const bool (&cv)[
     }
     __syncthreads();
     rank_take_desc<NT>(sm.shortl, sm.n_short, rem, sm.chosen + (keep - rem));
-    if (tid == 0) sm.chosen[keep] = o;
-    rank_write_ascending<NT>(sm.chosen, keep + 1, out);
+    if (bitmap != nullptr && o <= 32 * kResBitmapWords) {
+        constexpr int kWpt = kResBitmapWords / NT;
+        for (int k = tid; k < kResBitmapWords; k += NT) bitmap[k] = 0u;
+        __syncthreads();                                  // chosen complete, bitmap clear
+        for (int k = tid; k < keep; k += NT) {
+            const int v = sm.chosen[k];
+            atomicOr(&bitmap[v >> 5], 1u << (v & 31));
+        }
+        if (tid == 0) out[keep] = o;                      // above every candidate
+        __syncthreads();
+        uint32_t wv[kWpt];
+        int cnt = 0;
+#pragma unroll
+        for (int q = 0; q < kWpt; ++q) {
+            wv[q] = bitmap[kWpt * tid + q];
+            cnt += __popc(wv[q]);
+        }
+        int all;
+        int base = block_exclusive_scan<NT>(cnt, sm.wave_tot, &all);
+#pragma unroll
+        for (int q = 0; q < kWpt; ++q) {
+            uint32_t bits = wv[q];
+            while (bits) {
+                const int bit = __ffs(bits) - 1;
+                out[base++] = 32 * (kWpt * tid + q) + bit;
+                bits &= bits - 1;
+            }
+        }
+    } else {
+        if (tid == 0) sm.chosen[keep] = o;
+        rank_write_ascending<NT>(sm.chosen, keep + 1, out);
+    }
     for (int k = keep + 1 + tid; k < budget; k += NT) out[k] = -1;
 }
 
