@@ -17,7 +17,7 @@
 // memory path once per 64 rows.  Three modes share the machinery:
 //   scores  -- store every score (4 float4 per lane per step), three LDS
 //              buffers so loads run two steps ahead of the stores;
-//   sample  -- the same over a fixed sample of blocks (32 evenly spread runs
+//   sample  -- the same over a fixed sample of blocks (16 evenly spread runs
 //              of 256), stored compactly; feeds the per-row thresholds;
 //   collect -- no score matrix: scores at or above the row's threshold are
 //              appended to per-wave LDS lists and, at the end, to the row's
@@ -51,8 +51,8 @@ __shared__ int lrow[kWgTok];
 __shared__ int lrow_base[kWgTok];
 __shared__ int lwcnt[4];
 
-// Block of column jv: itself, or in sample mode run jv / 256 of 32 runs of
-// 256 blocks spread evenly over [0, omin).
+// Block of column jv: itself, or in sample mode run jv / 256 of kSampleRuns
+// runs of 256 blocks spread evenly over [0, omin).
 template <int kMode>
 __device__ __forceinline__ int column_block(int jv, int omin) {
     if (kMode == kModeSample) {

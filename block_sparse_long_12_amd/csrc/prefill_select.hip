@@ -3,7 +3,7 @@
 // GDN + QSA": blocks are scored and the most relevant ones kept; model card:
 // budget 512 blocks), without writing and re-reading the score matrix.
 //
-//  1. sample      the indexer scores a fixed sample of 8192 blocks per row (32
+//  1. sample      the indexer scores a fixed sample of 4096 blocks per row (16
 //                 runs of 256 spread over the blocks every row of the chunk
 //                 sees);
 //  2. threshold   per row, a key threshold from the sample whose expected
@@ -62,7 +62,7 @@ static PrefillWs carve(void* ws, int batch, int tq) {
     return w;
 }
 
-// One workgroup per row: the threshold from the row's 8192 sampled scores.
+// One workgroup per row: the threshold from the row's 4096 sampled scores.
 __global__ __launch_bounds__(kThrNT) void threshold_kernel(const float* __restrict__ sample, Positions pos0, int tq,
                                                            int budget, PrefillWs ws) {
     __shared__ ResolveSmem sm;

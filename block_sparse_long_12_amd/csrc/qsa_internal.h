@@ -86,7 +86,7 @@ hipError_t launch_select(const float* scores, int64_t ld, int64_t ss, const Posi
                          hipStream_t stream);
 
 // ---- fused prefill index-select (threshold from a sample, candidate lists) ----
-constexpr int kSampleRuns = 32;                   // sample runs of 256 blocks per sequence
+constexpr int kSampleRuns = 16;                   // sample runs of 256 blocks per sequence
 constexpr int kSampleCols = kSampleRuns * 256;    // sampled scores per row
 constexpr int kCollectCap = 2048;                 // candidates listed in LDS per workgroup
 constexpr int kRowCap = 4096;                     // candidates kept per row

@@ -137,7 +137,7 @@ qsa_status_t qsa_select_topk(const float* scores, int64_t scores_ld, int64_t sco
  * are scored and the most relevant kept): the same selection as
  * qsa_index_scores followed by qsa_select_topk, bit for bit, without
  * materialising the score matrix when the chunk is long.  The indexer first
- * scores a fixed sample of 8192 blocks per row to set a per-row threshold,
+ * scores a fixed sample of 4096 blocks per row to set a per-row threshold,
  * then scores every block keeping only those at or above it, and an exact
  * radix select finishes each row from that list.  Rows whose list is short
  * or overflows are redone exactly from full scores, so the result never

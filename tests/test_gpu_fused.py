@@ -117,9 +117,12 @@ def test_decode_step_matches_primitives(ctx, budget, B):
 
 # ---------------------------------------------------------------- prefill index-select
 
+SAMPLE_RUNS = 16     # the fused prefill index-select samples this many runs of 256 blocks per row
+
+
 def _run_starts(omin):
-    """First block of each of the 32 sampled runs of 256 blocks (spread over [0, omin))."""
-    return [r * (omin - 256) // 31 for r in range(32)]
+    """First block of each sampled run of 256 blocks (spread evenly over [0, omin))."""
+    return [r * (omin - 256) // (SAMPLE_RUNS - 1) for r in range(SAMPLE_RUNS)]
 
 
 def _prefill_kbar(kind, B, nblk, seed, pos0):
