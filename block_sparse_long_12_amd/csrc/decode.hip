@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
 
     const int c16 = lane & 15;
     const int G = lane >> 4;
-    bf16x8_t qf[16];
+    bf16x8_t qf[kIdxSlices];
     load_index_q(q_idx + b * qs, 0, 1, qf);             // token 0 in column 0, zero columns elsewhere
     const uint16_t* kb = kbar + b * kbs;
     float* sb = scores + b * ss;

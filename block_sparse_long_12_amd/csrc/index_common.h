@@ -1,13 +1,16 @@
 // Block scores of the MQA indexer on the matrix cores, shared by every kernel
 // that scores blocks so that all of them produce the same bits.
 //
-// The head sum is folded into the contraction: with K = 4 heads x 128 dims,
-//   s[t][j] = sum_{k<512} q_idx[t][k] * kbar'[j][k],  kbar'[j][h*128 + d] = kbar[j][d],
-// so one chain of 16 v_mfma_f32_16x16x32_bf16 (k-slices of 32 in increasing k,
-// i.e. head-major) yields finished scores: 512 exact bf16 products summed in
-// float32, no per-head partial sums.
-//   A (16 x 32): rows are 16 consecutive blocks; the k-slice of head h and
-//                dims 32q .. 32q + 31 is the same kbar slice q for every h;
+// The head sum is taken on the query side: for each dim d the 4 heads'
+// values are added in float32, ((q0 + q1) + q2) + q3 (exact unless their
+// exponents are very far apart), and the sum is split exactly into three
+// bf16 terms hi + mid + lo.  The score is then
+//   s[t][j] = sum over 3 terms x 128 dims of term[t][d] * kbar[j][d],
+// 384 exact bf16 products accumulated in float32 by one chain of 12
+// v_mfma_f32_16x16x32_bf16 (k-slices of 32 dims, term-major), with no
+// per-head partial sums.
+//   A (16 x 32): rows are 16 consecutive blocks; k-slice ks uses kbar dims
+//                32 (ks % 4) ..  + 31 (the same slice for every term);
 //   B (32 x 16): columns are 16 query tokens;
 //   D (16 x 16): lane l holds blocks 4*(l/16) .. 4*(l/16) + 3 for token l%16,
 //                i.e. 4 consecutive scores of one row (a float4 store).
@@ -17,27 +20,51 @@
 
 namespace qsa {
 
+constexpr int kIdxSlices = 12;   // k-slices: 3 terms x 4 groups of 32 dims
+
 // kf[q]: this lane's 8 dims of kbar slice q (dims 32q + 8*(lane/16) ..) of its
-// block row; qf[ks]: its token's 8 dims of k-slice ks (head ks/4, dims
+// block row; qf[ks]: its token's 8 dims of k-slice ks (term ks/4, dims
 // 32*(ks%4) + 8*(lane/16) ..).
-__device__ __forceinline__ f32x4_t block_scores(const bf16x8_t (&kf)[4], const bf16x8_t (&qf)[16]) {
+__device__ __forceinline__ f32x4_t block_scores(const bf16x8_t (&kf)[4], const bf16x8_t (&qf)[kIdxSlices]) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks & 3], qf[ks], acc, 0, 0, 0);
+    for (int ks = 0; ks < kIdxSlices; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks & 3], qf[ks], acc, 0, 0, 0);
     return acc;
 }
 
 // B operand for the 16 tokens t0 .. t0 + 15 of one sequence's q_idx
 // [T][4][128] (512 contiguous values per token): lane column l%16 is token
-// t0 + l%16; tokens at or past n_tok are zero columns.
-__device__ __forceinline__ void load_index_q(const uint16_t* qb, int t0, int n_tok, bf16x8_t (&qf)[16]) {
+// t0 + l%16, whose 4 heads are summed and split into the three terms;
+// tokens at or past n_tok are zero columns.
+__device__ __forceinline__ void load_index_q(const uint16_t* qb, int t0, int n_tok, bf16x8_t (&qf)[kIdxSlices]) {
     const int lane = threadIdx.x & 63;
     const int tok = t0 + (lane & 15);
     const uint16_t* qr = qb + static_cast<int64_t>(tok) * (kHi * kDi) + 8 * (lane >> 4);
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-        if (tok < n_tok) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * ks);
-        else qf[ks] = bf16x8_t{};
+    for (int dq = 0; dq < 4; ++dq) {
+        if (tok < n_tok) {
+            uint16_t h[kHi][8];
+#pragma unroll
+            for (int hh = 0; hh < kHi; ++hh)
+                *reinterpret_cast<uint4*>(h[hh]) = *reinterpret_cast<const uint4*>(qr + hh * kDi + 32 * dq);
+            uint16_t t_hi[8], t_mid[8], t_lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+#pragma clang fp contract(off)
+                const float s = ((bf16_to_f32(h[0][e]) + bf16_to_f32(h[1][e])) + bf16_to_f32(h[2][e])) + bf16_to_f32(h[3][e]);
+                t_hi[e] = f32_to_bf16(s);
+                const float r1 = s - bf16_to_f32(t_hi[e]);
+                t_mid[e] = f32_to_bf16(r1);
+                t_lo[e] = f32_to_bf16(r1 - bf16_to_f32(t_mid[e]));
+            }
+            qf[dq] = *reinterpret_cast<const bf16x8_t*>(t_hi);
+            qf[4 + dq] = *reinterpret_cast<const bf16x8_t*>(t_mid);
+            qf[8 + dq] = *reinterpret_cast<const bf16x8_t*>(t_lo);
+        } else {
+            qf[dq] = bf16x8_t{};
+            qf[4 + dq] = bf16x8_t{};
+            qf[8 + dq] = bf16x8_t{};
+        }
     }
 }
 

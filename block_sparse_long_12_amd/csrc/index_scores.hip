@@ -4,10 +4,10 @@
 //
 //   s[t][j] = sum_{h<4} sum_{d<128} q_idx[t][h][d] * kbar[j][d],   j < (q_pos0 + t) / 4
 //
-// A dense bf16 contraction on the matrix cores with the head sum folded into
-// K (index_common.h): per 16 blocks x 16 tokens, one chain of 16
-// v_mfma_f32_16x16x32_bf16 gives finished scores, 4 consecutive blocks of one
-// token per lane.  Every launch shape and mode computes a given score with
+// A dense bf16 contraction on the matrix cores with the head sum taken on
+// the query side and split into three exact bf16 terms (index_common.h): per
+// 16 blocks x 16 tokens, one chain of 12 v_mfma_f32_16x16x32_bf16 gives
+// finished scores, 4 consecutive blocks of one token per lane.  Every launch shape and mode computes a given score with
 // the same instruction sequence, so scores do not depend on tiling.
 //
 // A workgroup of 4 waves owns 64 query rows (16 per wave, whose B operands
@@ -118,7 +118,7 @@ __device__ __forceinline__ void step_sync(int s, bool has_rows) {
 
 // Scores of one staged step (4 tiles of 16 blocks) for the wave's 16 rows:
 // lane l ends with blocks j0 + 16 nt + 4 (l / 16) .. + 3 of token l % 16.
-__device__ __forceinline__ void step_scores(const KTile& t, const bf16x8_t (&qf)[16], f32x4_t (&acc)[4]) {
+__device__ __forceinline__ void step_scores(const KTile& t, const bf16x8_t (&qf)[kIdxSlices], f32x4_t (&acc)[4]) {
     const int lane = threadIdx.x & 63;
     const int c16 = lane & 15;
     const int G = lane >> 4;
@@ -134,7 +134,7 @@ __device__ __forceinline__ void step_scores(const KTile& t, const bf16x8_t (&qf)
     }
 }
 
-__device__ __forceinline__ void store_step(const KTile& t, const bf16x8_t (&qf)[16], int j0, int j_end, int t0,
+__device__ __forceinline__ void store_step(const KTile& t, const bf16x8_t (&qf)[kIdxSlices], int j0, int j_end, int t0,
                                            int tq, float* sb, int64_t ld) {
     f32x4_t acc[4];
     step_scores(t, qf, acc);
@@ -155,7 +155,7 @@ __device__ __forceinline__ void store_step(const KTile& t, const bf16x8_t (&qf)[
 // (no atomics).  For a number tau whose key has zero low bits, score >= tau
 // (IEEE) holds exactly when score_key(score) >= score_key(tau); a NaN tau
 // passes nothing.
-__device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf)[16], int j0, int lim,
+__device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf)[kIdxSlices], int j0, int lim,
                                              float tau, int row_local, int j_begin, uint64_t* seg, int& cnt) {
     f32x4_t acc[4];
     step_scores(t, qf, acc);
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void index_kernel(
     const int t0 = t_wg + kTokTile * wave;
     const bool has_rows = t0 < tq;
 
-    bf16x8_t qf[16];
+    bf16x8_t qf[kIdxSlices];
     load_index_q(q_idx + b * qs, t0, tq, qf);
 
     const uint16_t* kb = kbar + b * kbs;

@@ -106,7 +106,10 @@ qsa_status_t qsa_compress_block_keys(const uint16_t* k_idx, int64_t k_idx_seq_st
  * 1 key head of dim 128).  For query row i of sequence b at position
  * p = q_pos0[b] + i and every complete block j < p / 4:
  *   scores[b][i][j] = sum_h sum_d q_idx[b][i][h][d] * kbar[b][j][d]
- * with exact bf16 products accumulated in float32 (matrix-core tiles).
+ * computed as sum_d (sum_h q_idx[b][i][h][d]) * kbar[b][j][d]: the head sum
+ * in float32, split exactly into three bf16 terms, whose 384 exact products
+ * with kbar accumulate in float32 (matrix-core tiles); every entry point that
+ * scores blocks produces the same bits.
  * Entries j >= p / 4 of a row are left unspecified (not written, or written
  * with values the selection never reads).  Needs scores_ld >= (q_pos0[b] +
  * tq - 1) / 4 for all b, scores_ld % 4 == 0, and kbar holding those blocks.
