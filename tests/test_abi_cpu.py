@@ -111,7 +111,7 @@ def test_select_validation(L):
 def test_index_select_prefill_validation(L):
     p = _pos(70000)
     need = L.qsa_index_select_prefill_workspace_bytes(1, 10)
-    assert need >= 10 * (4096 * 8 + 8192 * 4)
+    assert need >= 10 * (4096 * 8 + 4096 * 4)      # per row: candidate list + 4096 sampled scores
     assert L.qsa_index_select_prefill_workspace_bytes(0, 10) == 0
     ld = (70000 + 9) // 4 // 4 * 4 + 4
     # every call below is invalid somewhere, so nothing is launched
