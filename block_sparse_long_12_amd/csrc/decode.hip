@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
 }
 
 struct FilterSmem {
-    uint32_t hist[kDecHistBins];
+    alignas(16) uint32_t hist[kDecHistBins];
     int32_t def[QSA_MAX_BUDGET];
     uint64_t cand[kDecCap];
     int wave_tot[4];
@@ -176,9 +176,14 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(
         v[it] = *reinterpret_cast<const float4*>(row + j4);
     }
 
-    // the threshold bin, from the global histogram the scan completed
-    const uint32_t* gh = ws.hist + static_cast<int64_t>(b) * kDecHistBins;
-    for (int k = tid; k < kDecHistBins; k += 256) sm.hist[k] = gh[k];
+    // the threshold bin, from the global histogram the scan completed (all
+    // 16 words of a thread in flight at once, then stored to LDS)
+    const uint4* gh = reinterpret_cast<const uint4*>(ws.hist + static_cast<int64_t>(b) * kDecHistBins);
+    uint4 hv[kDecHistBins / 1024];
+#pragma unroll
+    for (int it = 0; it < kDecHistBins / 1024; ++it) hv[it] = gh[tid + 256 * it];
+#pragma unroll
+    for (int it = 0; it < kDecHistBins / 1024; ++it) reinterpret_cast<uint4*>(sm.hist)[tid + 256 * it] = hv[it];
     if (tid == 0) {
         sm.n_def = 0;
         sm.n_cand = 0;
@@ -259,19 +264,29 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
     uint32_t* ctrl = ws.ctrl + b * kCtrl;
     if (trivial_selection(keep, o, budget, out, kFinNT)) return;   // nothing was accumulated
 
+    // every load of both lists in flight at once, with the control words (the
+    // lists have fixed capacities: unused tails are read and dropped)
+    const int32_t* __restrict__ defl = ws.defl + static_cast<int64_t>(b) * QSA_MAX_BUDGET;
+    const uint64_t* __restrict__ cg = ws.cand + static_cast<int64_t>(b) * kDecCap;
+    int32_t dv[QSA_MAX_BUDGET / kFinNT];
+    uint64_t cv[kDecCap / kFinNT];
+#pragma unroll
+    for (int it = 0; it < QSA_MAX_BUDGET / kFinNT; ++it) dv[it] = defl[tid + kFinNT * it];
+#pragma unroll
+    for (int it = 0; it < kDecCap / kFinNT; ++it) cv[it] = cg[tid + kFinNT * it];
     const int above = static_cast<int>(ctrl[kAbove]);
     const int inbin = static_cast<int>(ctrl[kInBin]);
     const int remaining = keep - above;
     if (inbin > kDecCap) {
         select_row<kFinNT>(scores + b * ss, o, keep, budget, out, sm.u.s);
     } else {
-        const int32_t* __restrict__ defl = ws.defl + static_cast<int64_t>(b) * QSA_MAX_BUDGET;
-        const uint64_t* __restrict__ cg = ws.cand + static_cast<int64_t>(b) * kDecCap;
         int32_t* chosen = sm.u.m.chosen;
         const bool bitmap = o <= 32 * kBitmapWords;             // every chosen j < o has a bit; o goes last
         if (bitmap)
             for (int k = tid; k < kBitmapWords; k += kFinNT) sm.u.m.bm[k] = 0u;
-        for (int k = tid; k < above; k += kFinNT) chosen[k] = defl[k];
+#pragma unroll
+        for (int it = 0; it < QSA_MAX_BUDGET / kFinNT; ++it)
+            if (tid + kFinNT * it < above) chosen[tid + kFinNT * it] = dv[it];
         if (tid == 0) chosen[keep] = o;
         // candidates of the threshold bin share the top 12 key bits: a second
         // radix level on the next 12 bits (LDS histogram) splits them into
@@ -279,7 +294,9 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         uint64_t* lc = sm.u.m.cand;
         uint32_t* h2 = sm.u.m.h2;
         for (int k = tid; k < kDecHistBins; k += kFinNT) h2[k] = 0u;
-        for (int k = tid; k < inbin; k += kFinNT) lc[k] = cg[k];
+#pragma unroll
+        for (int it = 0; it < kDecCap / kFinNT; ++it)
+            if (tid + kFinNT * it < inbin) lc[tid + kFinNT * it] = cv[it];
         if (tid == 0) sm.u.m.n_taken = 0;
         __syncthreads();
         for (int k = tid; k < inbin; k += kFinNT)

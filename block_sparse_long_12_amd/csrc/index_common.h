@@ -35,48 +35,55 @@ __device__ __forceinline__ f32x4_t block_scores(const bf16x8_t (&kf)[4], const b
 // B operand for the 16 tokens t0 .. t0 + 15 of one sequence's q_idx
 // [T][4][128] (512 contiguous values per token): lane column l%16 is token
 // t0 + l%16, whose 4 heads are summed and split into the three terms;
-// tokens at or past n_tok are zero columns.
+// tokens at or past n_tok (>= 1) are zero columns.  All 16 loads of a lane
+// are issued before any is used (columns past n_tok read row n_tok - 1 and
+// are zeroed afterwards), so the set-up costs one memory round trip.
 __device__ __forceinline__ void load_index_q(const uint16_t* qb, int t0, int n_tok, bf16x8_t (&qf)[kIdxSlices]) {
     const int lane = threadIdx.x & 63;
     const int tok = t0 + (lane & 15);
-    const uint16_t* qr = qb + static_cast<int64_t>(tok) * (kHi * kDi) + 8 * (lane >> 4);
+    const bool ok = tok < n_tok;
+    const uint16_t* qr = qb + static_cast<int64_t>(min(tok, n_tok - 1)) * (kHi * kDi) + 8 * (lane >> 4);
+    uint4 raw[4][kHi];
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+        for (int hh = 0; hh < kHi; ++hh) raw[dq][hh] = *reinterpret_cast<const uint4*>(qr + hh * kDi + 32 * dq);
 #pragma unroll
     for (int dq = 0; dq < 4; ++dq) {
-        if (tok < n_tok) {
-            uint16_t h[kHi][8];
+        uint16_t h[kHi][8];
 #pragma unroll
-            for (int hh = 0; hh < kHi; ++hh)
-                *reinterpret_cast<uint4*>(h[hh]) = *reinterpret_cast<const uint4*>(qr + hh * kDi + 32 * dq);
-            uint16_t t_hi[8], t_mid[8], t_lo[8];
+        for (int hh = 0; hh < kHi; ++hh)
+            *reinterpret_cast<uint4*>(h[hh]) = ok ? raw[dq][hh] : make_uint4(0u, 0u, 0u, 0u);
+        uint16_t t_hi[8], t_mid[8], t_lo[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 8; ++e) {
 #pragma clang fp contract(off)
-                const float s = ((bf16_to_f32(h[0][e]) + bf16_to_f32(h[1][e])) + bf16_to_f32(h[2][e])) + bf16_to_f32(h[3][e]);
-                t_hi[e] = f32_to_bf16(s);
-                const float r1 = s - bf16_to_f32(t_hi[e]);
-                t_mid[e] = f32_to_bf16(r1);
-                t_lo[e] = f32_to_bf16(r1 - bf16_to_f32(t_mid[e]));
-            }
-            qf[dq] = *reinterpret_cast<const bf16x8_t*>(t_hi);
-            qf[4 + dq] = *reinterpret_cast<const bf16x8_t*>(t_mid);
-            qf[8 + dq] = *reinterpret_cast<const bf16x8_t*>(t_lo);
-        } else {
-            qf[dq] = bf16x8_t{};
-            qf[4 + dq] = bf16x8_t{};
-            qf[8 + dq] = bf16x8_t{};
+            const float s = ((bf16_to_f32(h[0][e]) + bf16_to_f32(h[1][e])) + bf16_to_f32(h[2][e])) + bf16_to_f32(h[3][e]);
+            t_hi[e] = f32_to_bf16(s);
+            const float r1 = s - bf16_to_f32(t_hi[e]);
+            t_mid[e] = f32_to_bf16(r1);
+            t_lo[e] = f32_to_bf16(r1 - bf16_to_f32(t_mid[e]));
         }
+        qf[dq] = *reinterpret_cast<const bf16x8_t*>(t_hi);
+        qf[4 + dq] = *reinterpret_cast<const bf16x8_t*>(t_mid);
+        qf[8 + dq] = *reinterpret_cast<const bf16x8_t*>(t_lo);
     }
+}
+
+// This lane's part of an A operand row from global memory: its 8 dims of each
+// slice of block j.
+__device__ __forceinline__ void load_index_k_row(const uint16_t* kb, int j, bf16x8_t (&kf)[4]) {
+    const int lane = threadIdx.x & 63;
+    const uint16_t* kr = kb + static_cast<int64_t>(j) * kDi + 8 * (lane >> 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kf[q] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * q);
 }
 
 // A operand from global memory: lane row l%16 is block j0 + l%16; blocks at
 // or past j_end (>= 1) read block j_end - 1 instead, so every load is issued
 // unconditionally; their scores land only where the result is unspecified.
 __device__ __forceinline__ void load_index_k(const uint16_t* kb, int j0, int j_end, bf16x8_t (&kf)[4]) {
-    const int lane = threadIdx.x & 63;
-    const int j = min(j0 + (lane & 15), j_end - 1);
-    const uint16_t* kr = kb + static_cast<int64_t>(j) * kDi + 8 * (lane >> 4);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) kf[q] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * q);
+    load_index_k_row(kb, min(j0 + static_cast<int>(threadIdx.x & 15), j_end - 1), kf);
 }
 
 }  // namespace qsa

@@ -312,12 +312,11 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
 // below the capacities of the candidate buffers.
 __device__ __forceinline__ int threshold_target(int keep) { return 2 * keep + 512; }
 
-// Key threshold from sample keys held PER per thread: the lower edge of the
-// 22-bit key prefix holding the r-th largest sample key (two 11-bit radix
-// levels in LDS).  Returned as the float to compare scores against; a quiet
-// NaN (no score passes) when the threshold would sit at or below -inf.
+// Key threshold from sample keys held PER per thread (1 <= r <= NT * PER):
+// the lower edge of the 22-bit key prefix holding the r-th largest sample key
+// (two 11-bit radix levels in LDS).
 template <int NT, int PER>
-__device__ float sample_threshold(const uint32_t (&sk)[PER], int r, ResolveSmem& sm) {
+__device__ uint32_t sample_threshold_key(const uint32_t (&sk)[PER], int r, ResolveSmem& sm) {
     const int tid = threadIdx.x;
     for (int k = tid; k < 2048; k += NT) sm.hist[k] = 0u;
     __syncthreads();
@@ -337,6 +336,14 @@ __device__ float sample_threshold(const uint32_t (&sk)[PER], int r, ResolveSmem&
     find_threshold_bin<NT>(sm.hist, 2048, r2, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
     const uint32_t tkey = (b1 << 21) | (sm.sh_bin << 10);
     __syncthreads();
+    return tkey;
+}
+
+// The same threshold as the float to compare scores against; a quiet NaN (no
+// score passes) when it would sit at or below -inf.
+template <int NT, int PER>
+__device__ float sample_threshold(const uint32_t (&sk)[PER], int r, ResolveSmem& sm) {
+    const uint32_t tkey = sample_threshold_key<NT, PER>(sk, r, sm);
     return tkey <= 0x007fffffu ? __uint_as_float(0x7fc00000u) : key_to_float(tkey);
 }
 

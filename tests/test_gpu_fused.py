@@ -44,7 +44,12 @@ def _kbar(kind, B, nblk, seed):
 CASES = [("normal", [1048576 // 16, 70001, 4096 + 3], 512), ("normal", [9000, 9001, 9002], 64),
          ("normal", [1048576, 1048575, 1048579], 512),      # own block 262144 / 262143: bitmap edge
          ("equal", [40000, 40000, 40000], 512), ("few_values", [50000, 12345, 8000], 512),
-         ("normal", [100, 2047, 2048], 512), ("normal", [3, 50000, 7], 1), ("normal", [20000, 1, 20001], 2)]
+         ("normal", [100, 2047, 2048], 512), ("normal", [3, 50000, 7], 1), ("normal", [20000, 1, 20001], 2),
+         ("normal", [200000, 262144, 300001], 512),       # long rows of different lengths
+         ("normal", [1048576, 1048576, 1048576, 1048576], 1024),
+         ("normal", [65536, 65537, 65540, 65543], 64),
+         ("equal", [70000, 70000, 70000], 512),               # every key equal: the threshold bin overflows
+         ("few_values", [80000, 66000], 512)]                 # tie groups of thousands at the threshold
 
 
 @pytest.mark.parametrize("kind,pos,budget", CASES, ids=[f"{k}-{p[0]}-{b}" for k, p, b in CASES])
@@ -75,7 +80,7 @@ def test_index_select_decode_matches_primitives(kind, pos, budget):
         assert int(ws[:head].count_nonzero()) == 0, "histogram / control words not left zeroed"
 
 
-@pytest.mark.parametrize("ctx,budget,B", [(32768, 512, 8), (5001, 64, 3), (99, 512, 2)])
+@pytest.mark.parametrize("ctx,budget,B", [(32768, 512, 8), (5001, 64, 3), (99, 512, 2), (131072, 512, 2)])
 def test_decode_step_matches_primitives(ctx, budget, B):
     say(f"decode_step ctx={ctx} budget={budget} B={B}")
     wl = I.custom_workload("decode", batch=B, ctx=ctx, tq=1, budget=budget, n_needles=2, seed=ctx)
