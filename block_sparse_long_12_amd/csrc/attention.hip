@@ -179,33 +179,49 @@ __device__ __forceinline__ void attend_blocks(const uint16_t* __restrict__ kg,
 }
 
 // Q^T fragments of this lane's head (lane & 15 < 12), k slices 32*ks + 8*(lane/16).
-// With `rope`, the rotary pairs (d, d + 32), d = 8*(lane/16) + e, sit in
-// fragments 0 and 1 of the same lane and are rotated here exactly as the
-// rotary kernel does, so an unrotated q gives the same bits as a pre-rotated one.
-__device__ __forceinline__ void load_q_frags(const uint16_t* qh, bool ok, int p, const InvFreq* rope,
-                                             bf16x8_t (&qf)[8]) {
+__device__ __forceinline__ void issue_q_frags(const uint16_t* qh, bool ok, bf16x8_t (&qf)[8]) {
     const int G = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
         qf[ks] = ok ? *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * G) : bf16x8_t{};
-    if (rope != nullptr) {
-        // each lane evaluates one of the 32 angles (the same call as
-        // rope_row_wave), then takes the 8 its k slice needs from its peers
-        const int lane = threadIdx.x & 63;
-        double sn_l, cs_l;
-        sincos(static_cast<double>(p) * rope->f[lane & 31], &sn_l, &cs_l);
-        uint16_t* lo = reinterpret_cast<uint16_t*>(&qf[0]);
-        uint16_t* hi = reinterpret_cast<uint16_t*>(&qf[1]);
+}
+
+// Rotary angles of position p: each lane evaluates one of the 32 angles (the
+// same call as rope_row_wave); needs no loaded data, so it can run while loads
+// are in flight.
+struct RopeAngle {
+    double sn, cs;
+};
+__device__ __forceinline__ RopeAngle rope_angle(int p, const InvFreq& inv) {
+    RopeAngle a;
+    sincos(static_cast<double>(p) * inv.f[threadIdx.x & 31], &a.sn, &a.cs);
+    return a;
+}
+
+// Rotates the loaded fragments: the rotary pairs (d, d + 32), d = 8*(lane/16)
+// + e, sit in fragments 0 and 1 of the same lane; each takes the 8 angles its
+// k slice needs from its peers, exactly as the rotary kernel rotates, so an
+// unrotated q gives the same bits as a pre-rotated one.
+__device__ __forceinline__ void rotate_q_frags(const RopeAngle& a, bf16x8_t (&qf)[8]) {
+    const int G = (threadIdx.x & 63) >> 4;
+    uint16_t* lo = reinterpret_cast<uint16_t*>(&qf[0]);
+    uint16_t* hi = reinterpret_cast<uint16_t*>(&qf[1]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const double cs = __shfl(cs_l, 8 * G + e);
-            const double sn = __shfl(sn_l, 8 * G + e);
-            const double a = bf16_to_f32(lo[e]);
-            const double b = bf16_to_f32(hi[e]);
-            lo[e] = rotate_half_elem(a, b, cs, sn, true);
-            hi[e] = rotate_half_elem(b, a, cs, sn, false);
-        }
+    for (int e = 0; e < 8; ++e) {
+        const double cs = __shfl(a.cs, 8 * G + e);
+        const double sn = __shfl(a.sn, 8 * G + e);
+        const double x = bf16_to_f32(lo[e]);
+        const double y = bf16_to_f32(hi[e]);
+        lo[e] = rotate_half_elem(x, y, cs, sn, true);
+        hi[e] = rotate_half_elem(y, x, cs, sn, false);
     }
+}
+
+// Loads (and, with `rope`, rotates) the query fragments.
+__device__ __forceinline__ void load_q_frags(const uint16_t* qh, bool ok, int p, const InvFreq* rope,
+                                             bf16x8_t (&qf)[8]) {
+    issue_q_frags(qh, ok, qf);
+    if (rope != nullptr) rotate_q_frags(rope_angle(p, *rope), qf);
 }
 
 __device__ __forceinline__ void init_state(WaveState& st) {
@@ -316,10 +332,13 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     const int blk_end = min(budget, blk_begin + bps);
     const uint16_t* kg = k + b * kvs + g * kD;
     const uint16_t* vg = v + b * kvs + g * kD;
+    // query loads first, then the selection and the first chunk; the rotary
+    // angles are computed while those are in flight
+    bf16x8_t qf[8];
+    issue_q_frags(q + b * qs + (head_ok ? head : 0) * kD, head_ok, qf);
     Chunk first;
     load_chunk(kg, vg, sel + b * sels, blk_begin, blk_end, p, first);
-    bf16x8_t qf[8];
-    load_q_frags(q + b * qs + (head_ok ? head : 0) * kD, head_ok, p, rope_q ? &inv : nullptr, qf);
+    if (rope_q) rotate_q_frags(rope_angle(p, inv), qf);
     WaveState st;
     init_state(st);
     attend_blocks<2>(kg, vg, sel + b * sels, blk_begin, blk_end, p, qf, c, st, vt_all + g * kVtElems, first);
