@@ -3,15 +3,12 @@
 //
 // The head sum is taken on the query side: for each dim d the 4 heads'
 // values are added in float32, ((q0 + q1) + q2) + q3 (exact unless their
-// exponents are very far apart), and the sum is written as two bf16 terms
-// hi + mid (hi = bf16(sum), mid = bf16(sum - hi): 16 significant bits, so
-// |sum - hi - mid| <= 2^-18 |sum|).  The score is then
-//   s[t][j] = sum over 2 terms x 128 dims of term[t][d] * kbar[j][d],
-// 256 exact bf16 products accumulated in float32 by one chain of 8
+// exponents are very far apart), and the sum is split exactly into three
+// bf16 terms hi + mid + lo.  The score is then
+//   s[t][j] = sum over 3 terms x 128 dims of term[t][d] * kbar[j][d],
+// 384 exact bf16 products accumulated in float32 by one chain of 12
 // v_mfma_f32_16x16x32_bf16 (k-slices of 32 dims, term-major), with no
-// per-head partial sums.  The dropped remainder adds at most 2^-18 of
-// sum |q k| to the error, which stays inside the float32 accumulation bound
-// of the per-head form (512 products: 2^-15 of sum over heads of |q k|).
+// per-head partial sums.
 //   A (16 x 32): rows are 16 consecutive blocks; k-slice ks uses kbar dims
 //                32 (ks % 4) ..  + 31 (the same slice for every term);
 //   B (32 x 16): columns are 16 query tokens;
@@ -23,7 +20,7 @@
 
 namespace qsa {
 
-constexpr int kIdxSlices = 8;    // k-slices: 2 terms x 4 groups of 32 dims
+constexpr int kIdxSlices = 12;   // k-slices: 3 terms x 4 groups of 32 dims
 
 // kf[q]: this lane's 8 dims of kbar slice q (dims 32q + 8*(lane/16) ..) of its
 // block row; qf[ks]: its token's 8 dims of k-slice ks (term ks/4, dims
@@ -37,7 +34,7 @@ __device__ __forceinline__ f32x4_t block_scores(const bf16x8_t (&kf)[4], const b
 
 // B operand for the 16 tokens t0 .. t0 + 15 of one sequence's q_idx
 // [T][4][128] (512 contiguous values per token): lane column l%16 is token
-// t0 + l%16, whose 4 heads are summed and written as the two terms;
+// t0 + l%16, whose 4 heads are summed and split into the three terms;
 // tokens at or past n_tok (>= 1) are zero columns.  All 16 loads of a lane
 // are issued before any is used (columns past n_tok read row n_tok - 1 and
 // are zeroed afterwards), so the set-up costs one memory round trip.
@@ -57,16 +54,19 @@ __device__ __forceinline__ void load_index_q(const uint16_t* qb, int t0, int n_t
 #pragma unroll
         for (int hh = 0; hh < kHi; ++hh)
             *reinterpret_cast<uint4*>(h[hh]) = ok ? raw[dq][hh] : make_uint4(0u, 0u, 0u, 0u);
-        uint16_t t_hi[8], t_mid[8];
+        uint16_t t_hi[8], t_mid[8], t_lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
 #pragma clang fp contract(off)
             const float s = ((bf16_to_f32(h[0][e]) + bf16_to_f32(h[1][e])) + bf16_to_f32(h[2][e])) + bf16_to_f32(h[3][e]);
             t_hi[e] = f32_to_bf16(s);
-            t_mid[e] = f32_to_bf16(s - bf16_to_f32(t_hi[e]));
+            const float r1 = s - bf16_to_f32(t_hi[e]);
+            t_mid[e] = f32_to_bf16(r1);
+            t_lo[e] = f32_to_bf16(r1 - bf16_to_f32(t_mid[e]));
         }
         qf[dq] = *reinterpret_cast<const bf16x8_t*>(t_hi);
         qf[4 + dq] = *reinterpret_cast<const bf16x8_t*>(t_mid);
+        qf[8 + dq] = *reinterpret_cast<const bf16x8_t*>(t_lo);
     }
 }
 

@@ -107,11 +107,9 @@ qsa_status_t qsa_compress_block_keys(const uint16_t* k_idx, int64_t k_idx_seq_st
  * p = q_pos0[b] + i and every complete block j < p / 4:
  *   scores[b][i][j] = sum_h sum_d q_idx[b][i][h][d] * kbar[b][j][d]
  * computed as sum_d (sum_h q_idx[b][i][h][d]) * kbar[b][j][d]: the head sum
- * in float32, written as two bf16 terms (16 significant bits; the remainder,
- * at most 2^-18 of the sum, is dropped), whose 256 exact products with kbar
- * accumulate in float32 (matrix-core tiles).  The result lies within the
- * float32 accumulation bound of the per-head form, 2^-15 * sum |q k|; every
- * entry point that scores blocks produces the same bits.
+ * in float32, split exactly into three bf16 terms, whose 384 exact products
+ * with kbar accumulate in float32 (matrix-core tiles); every entry point that
+ * scores blocks produces the same bits.
  * Entries j >= p / 4 of a row are left unspecified (not written, or written
  * with values the selection never reads).  Needs scores_ld >= (q_pos0[b] +
  * tq - 1) / 4 for all b, scores_ld % 4 == 0, and kbar holding those blocks.
