@@ -152,6 +152,8 @@ class Decode:
         qsa.compress_block_keys(self.k_idx, 0, ctx // 4, self.kbar)
         self.q_raw = x.q.to(dev)
         self.k_new = x.k[:, ctx:ctx + 1].contiguous().to(dev)
+        self.v_new = x.v[:, ctx:ctx + 1].contiguous().to(dev)
+        self.k_idx_new = x.k_idx[:, ctx:ctx + 1].contiguous().to(dev)
         self.q_idx = x.q_idx.to(dev)
         ld = max(4, (ctx // 4 + 3) // 4 * 4)
         self.scores = torch.empty((B, 1, ld), dtype=torch.float32, device=dev)
@@ -162,13 +164,15 @@ class Decode:
         torch.cuda.synchronize()
 
     def step(self, timer):
-        """One decode step through the single qsa_decode_step call (rotary of the
-        new q/k rows, block scores, selection, attention); a block completed by
-        the new token would be compressed after it."""
+        """One serving decode step through the single qsa_decode_step call: the
+        new token's K (rotated), V and indexer-key rows appended to the caches,
+        block scores, selection, attention with q rotated on load (a block
+        completed by the new token would be compressed in the same call)."""
         wl, q = self.wl, self.qsa
         with timer("decode_step"):
             q.decode_step(self.q_raw, self.k_new, self.q_idx, self.k_idx, self.k_cache, self.v_cache, self.kbar,
-                          self.pos, wl.budget, self.out, self.lse, self.scores, self.sel, self.ws)
+                          self.pos, wl.budget, self.out, self.lse, self.scores, self.sel, self.ws,
+                          v_new=self.v_new, k_idx_new=self.k_idx_new)
 
 
 class EventTimer:

@@ -12,8 +12,8 @@
 //                          block_scores (bit-identical to index_scores_kernel),
 //                          stores the scores, counts the top 12 bits of each
 //                          ordered key in an LDS histogram and adds it to a
-//                          per-sequence global histogram.  Optionally rotates
-//                          the new K row into the cache (step 0).
+//                          per-sequence global histogram.  In a decode step it
+//                          also appends the new rows (append_rows).
 //  decode_filter_kernel    B x F workgroups: each finds the threshold bin from
 //                          the global histogram, then collects its slice's keys
 //                          above the bin (winners) and in the bin (candidates)
@@ -24,6 +24,7 @@
 //                          if the bin overflowed the list it runs the full radix
 //                          select on the stored row.  Leaves the histogram and
 //                          counters zeroed for the next call.
+#include "compress_common.h"
 #include "index_common.h"
 #include "rope_common.h"
 #include "select_common.h"
@@ -63,12 +64,65 @@ static DecodeWs carve(void* ws, int batch) {
     return w;
 }
 
+// Device copy of DecodeAppend, with the rotary table.
+struct AppendArgs {
+    const uint16_t* k_new;
+    int64_t kns;
+    uint16_t* k_cache;
+    const uint16_t* v_new;
+    int64_t vns;
+    uint16_t* v_cache;
+    int64_t kvs;
+    const uint16_t* k_idx_new;
+    int64_t kins;
+    uint16_t* k_idx;
+    int64_t kis;
+    uint16_t* kbar;
+    int64_t kbs;
+    InvFreq inv;
+};
+
+// The rows of one sequence's new position p, by the first workgroup of the
+// sequence: wave 0 rotates the K row into the cache (step 0), wave 1 copies
+// the V row, wave 2 copies the indexer key row and, when p completes its
+// block, compresses the block (step 1) for the next positions.  Nothing else
+// in the step reads these rows (the scan reads blocks j < p / 4 only; the
+// attention runs in a later launch).
+__device__ __forceinline__ void append_rows(const AppendArgs& ap, int b, int p, int wave) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(p) * (kHkv * kD);
+    if (wave == 0 && ap.k_new != nullptr)
+        rope_row_wave(ap.k_new + b * ap.kns, ap.k_cache + b * ap.kvs + row, kHkv, static_cast<double>(p), ap.inv,
+                      false);
+    if (wave == 1 && ap.v_new != nullptr)        // 2 x 256 values: 16 B per lane
+        *reinterpret_cast<uint4*>(ap.v_cache + b * ap.kvs + row + 8 * lane) =
+            *reinterpret_cast<const uint4*>(ap.v_new + b * ap.vns + 8 * lane);
+    if (wave == 2 && ap.k_idx != nullptr && lane < kDi / 8) {
+        uint16_t* kr = ap.k_idx + b * ap.kis + 8 * lane;
+        uint4 cur;
+        if (ap.k_idx_new != nullptr) {
+            cur = *reinterpret_cast<const uint4*>(ap.k_idx_new + b * ap.kins + 8 * lane);
+            *reinterpret_cast<uint4*>(kr + static_cast<int64_t>(p) * kDi) = cur;
+        } else {
+            cur = *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(p) * kDi);
+        }
+        if (p % kBlock == kBlock - 1) {
+            uint4 r[kBlock];
+#pragma unroll
+            for (int t = 0; t < kBlock - 1; ++t)
+                r[t] = *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(p - (kBlock - 1) + t) * kDi);
+            r[kBlock - 1] = cur;
+            *reinterpret_cast<uint4*>(ap.kbar + b * ap.kbs + static_cast<int64_t>(p / kBlock) * kDi + 8 * lane) =
+                compress_rows(r);
+        }
+    }
+}
+
 template <int STEPS>
 __global__ __launch_bounds__(256) void decode_scan_kernel(
     const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
     Positions pos, int budget, int wg_per_seq, float* __restrict__ scores,
-    int64_t ss, DecodeWs ws, const uint16_t* __restrict__ k_new, int64_t kns,
-    uint16_t* __restrict__ k_cache, int64_t kcs, InvFreq inv, int rope_k) {
+    int64_t ss, DecodeWs ws, AppendArgs ap, int append) {
     __shared__ uint32_t hist[kDecHistBins];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -80,9 +134,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     const int keep = min(budget - 1, o);
     const bool need_hist = keep > 0 && keep < o;
 
-    if (rope_k && g == 0 && wave == 0)
-        rope_row_wave(k_new + b * kns, k_cache + b * kcs + static_cast<int64_t>(p) * (kHkv * kD), kHkv,
-                      static_cast<double>(p), inv, false);
+    if (append && g == 0) append_rows(ap, b, p, wave);
 
     for (int k = tid; k < kDecHistBins; k += 256) hist[k] = 0;
     __syncthreads();
@@ -379,8 +431,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
                                       int64_t kbs, const Positions& pos, int batch, int budget,
                                       float* scores, int64_t ss, int32_t* sel, int64_t sels, void* ws,
-                                      const uint16_t* k_new, int64_t kns, uint16_t* k_cache,
-                                      int64_t kcs, double rope_theta, hipStream_t stream) {
+                                      const DecodeAppend* append, hipStream_t stream) {
     int o_max = 0;
     for (int b = 0; b < batch; ++b) o_max = max(o_max, pos.p[b] / kBlock);
     // scan: 256 * STEPS blocks per workgroup; STEPS is the largest of 8, 4, 2, 1
@@ -392,25 +443,41 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
     const int wg_filt = max(1, (o_max + kFiltPer - 1) / kFiltPer);
 
     const DecodeWs w = carve(ws, batch);
-    const InvFreq inv = make_inv_freq(rope_theta > 0.0 ? rope_theta : 1.0e7);
-    const int rope_k = (rope_theta > 0.0 && k_new != nullptr) ? 1 : 0;
+    AppendArgs ap{};
+    if (append != nullptr) {
+        ap.k_new = append->k_new;
+        ap.kns = append->kns;
+        ap.k_cache = append->k_cache;
+        ap.v_new = append->v_new;
+        ap.vns = append->vns;
+        ap.v_cache = append->v_cache;
+        ap.kvs = append->kvs;
+        ap.k_idx_new = append->k_idx_new;
+        ap.kins = append->kins;
+        ap.k_idx = append->k_idx;
+        ap.kis = append->kis;
+        ap.kbar = append->kbar;
+        ap.kbs = append->kbs;
+        ap.inv = make_inv_freq(append->rope_theta > 0.0 ? append->rope_theta : 1.0e7);
+    }
+    const int do_append = append != nullptr ? 1 : 0;
     const dim3 grid(static_cast<unsigned>(batch * wg_scan));
     switch (steps) {
         case 8:
             hipLaunchKernelGGL(decode_scan_kernel<8>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               wg_scan, scores, ss, w, k_new, kns, k_cache, kcs, inv, rope_k);
+                               wg_scan, scores, ss, w, ap, do_append);
             break;
         case 4:
             hipLaunchKernelGGL(decode_scan_kernel<4>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               wg_scan, scores, ss, w, k_new, kns, k_cache, kcs, inv, rope_k);
+                               wg_scan, scores, ss, w, ap, do_append);
             break;
         case 2:
             hipLaunchKernelGGL(decode_scan_kernel<2>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               wg_scan, scores, ss, w, k_new, kns, k_cache, kcs, inv, rope_k);
+                               wg_scan, scores, ss, w, ap, do_append);
             break;
         default:
             hipLaunchKernelGGL(decode_scan_kernel<1>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               wg_scan, scores, ss, w, k_new, kns, k_cache, kcs, inv, rope_k);
+                               wg_scan, scores, ss, w, ap, do_append);
             break;
     }
     hipError_t e = hipGetLastError();

@@ -361,7 +361,7 @@ qsa_status_t qsa_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_st
     CHECK(aligned16(workspace), "workspace must be 16-byte aligned");
     return hip_result(qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch,
                                                       budget, scores, scores_seq_stride, sel, sel_seq_stride,
-                                                      workspace, nullptr, 0, nullptr, 0, 0.0, stream),
+                                                      workspace, nullptr, stream),
                       "index_select_decode launch");
 }
 
@@ -373,10 +373,12 @@ size_t qsa_decode_step_workspace_bytes(int32_t batch, int32_t budget) {
 }
 
 qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
-                             const uint16_t* k_new, int64_t k_new_seq_stride,
+                             const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
                              const uint16_t* q_idx, int64_t q_idx_seq_stride,
-                             uint16_t* k_cache, const uint16_t* v_cache, int64_t kv_seq_stride,
-                             const uint16_t* kbar, int64_t kbar_seq_stride,
+                             const uint16_t* k_idx_new,
+                             uint16_t* k_cache, uint16_t* v_cache, int64_t kv_seq_stride,
+                             uint16_t* k_idx, int64_t k_idx_seq_stride,
+                             uint16_t* kbar, int64_t kbar_seq_stride,
                              const int32_t* q_pos, int32_t batch, int32_t budget,
                              float softmax_scale, double rope_theta,
                              float* scores, int64_t scores_seq_stride,
@@ -390,16 +392,25 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
                                   scores_seq_stride, sel, sel_seq_stride));
     TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
     CHECK(k_new != nullptr && aligned16(k_new), "k_new must be non-NULL and 16-byte aligned");
+    CHECK(v_new == nullptr || aligned16(v_new), "v_new must be 16-byte aligned");
+    CHECK(k_idx_new == nullptr || k_idx != nullptr, "k_idx_new needs the k_idx cache");
+    CHECK(k_idx_new == nullptr || aligned16(k_idx_new), "k_idx_new must be 16-byte aligned");
+    CHECK(k_idx == nullptr || aligned16(k_idx), "k_idx must be 16-byte aligned");
     CHECK(isfinite(rope_theta) && rope_theta > 1.0, "rope_theta must be finite and > 1");
     CHECK(lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) == 0, "lse must be 4-byte aligned");
     if (batch > 1) {
         int64_t max_len = 0;
         for (int b = 0; b < batch; ++b) max_len = p.p[b] + 1 > max_len ? p.p[b] + 1 : max_len;
         CHECK(stride_ok(q_seq_stride) && q_seq_stride >= qsa::kHq * qsa::kD, "q_seq_stride too small");
-        CHECK(stride_ok(k_new_seq_stride) && k_new_seq_stride >= qsa::kHkv * qsa::kD, "k_new_seq_stride too small");
+        CHECK(stride_ok(kv_new_seq_stride) && kv_new_seq_stride >= qsa::kHkv * qsa::kD,
+              "kv_new_seq_stride too small");
         CHECK(stride_ok(out_seq_stride) && out_seq_stride >= qsa::kHq * qsa::kD, "out_seq_stride too small");
         CHECK(stride_ok(kv_seq_stride) && kv_seq_stride >= max_len * qsa::kHkv * qsa::kD,
               "kv_seq_stride smaller than the rows the queries reach");
+        CHECK(k_idx == nullptr || (stride_ok(k_idx_seq_stride) && k_idx_seq_stride >= max_len * qsa::kDi),
+              "k_idx_seq_stride smaller than the rows the new tokens reach");
+        CHECK(k_idx == nullptr || kbar_seq_stride >= (max_len / qsa::kBlock) * qsa::kDi,
+              "kbar_seq_stride smaller than the blocks the new tokens complete");
     }
     const size_t sel_ws = align256(qsa::decode_select_ws_bytes(batch));
     const size_t need = sel_ws + qsa::decode_workspace_bytes(batch, budget);
@@ -407,10 +418,24 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
         return fail(QSA_ERR_WORKSPACE, "decode step workspace needs %zu bytes, got %zu", need,
                     workspace == nullptr ? size_t{0} : workspace_bytes);
     CHECK(aligned16(workspace), "workspace must be 16-byte aligned");
+    qsa::DecodeAppend ap{};
+    ap.k_new = k_new;
+    ap.kns = kv_new_seq_stride;
+    ap.k_cache = k_cache;
+    ap.v_new = v_new;
+    ap.vns = kv_new_seq_stride;
+    ap.v_cache = v_cache;
+    ap.kvs = kv_seq_stride;
+    ap.k_idx_new = k_idx_new;
+    ap.kins = qsa::kDi;
+    ap.k_idx = k_idx;
+    ap.kis = k_idx_seq_stride;
+    ap.kbar = kbar;
+    ap.kbs = kbar_seq_stride;
+    ap.rope_theta = rope_theta;
     hipError_t e = qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch,
                                                    budget, scores, scores_seq_stride, sel, sel_seq_stride,
-                                                   workspace, k_new, k_new_seq_stride, k_cache, kv_seq_stride,
-                                                   rope_theta, stream);
+                                                   workspace, &ap, stream);
     if (e != hipSuccess) return hip_result(e, "decode_step index-select launch");
     return hip_result(qsa::launch_attn_decode_ex(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
                                                  sel_seq_stride, p, batch, budget, softmax_scale, out,

@@ -129,11 +129,29 @@ hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* 
 // fused decode index-select (scores + selection of one query row per sequence);
 // the workspace must be zero before its first use and is left zero by each call
 size_t decode_select_ws_bytes(int batch);
+// Rows a decode step appends at each sequence's new position p before it
+// scores (every pointer may be null: then that part is not done).
+struct DecodeAppend {
+    const uint16_t* k_new;       // [B][2][256] unrotated: rotated into k_cache[b][p]
+    int64_t kns;
+    uint16_t* k_cache;
+    const uint16_t* v_new;       // [B][2][256]: copied into v_cache[b][p]
+    int64_t vns;
+    uint16_t* v_cache;
+    int64_t kvs;                 // sequence stride of both KV caches
+    const uint16_t* k_idx_new;   // [B][128]: copied into k_idx[b][p]
+    int64_t kins;
+    uint16_t* k_idx;             // indexer key cache; with it, a block that p completes
+    int64_t kis;                 // (p % 4 == 3) is compressed into kbar[b][p / 4]
+    uint16_t* kbar;
+    int64_t kbs;
+    double rope_theta;
+};
+
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
                                       int64_t kbs, const Positions& pos, int batch, int budget,
                                       float* scores, int64_t ss, int32_t* sel, int64_t sels, void* ws,
-                                      const uint16_t* k_new, int64_t kns, uint16_t* k_cache,
-                                      int64_t kcs, double rope_theta, hipStream_t stream);
+                                      const DecodeAppend* append, hipStream_t stream);
 hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
                               const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                               const Positions& pos, int batch, int budget, float scale,

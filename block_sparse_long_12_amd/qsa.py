@@ -55,9 +55,9 @@ _SIGNATURES = {
     "qsa_index_select_decode": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _c_p, _i64, _c_p, _i64,
                                        _c_p, _sz, _c_p]),
     "qsa_decode_step_workspace_bytes": (_sz, [_i32, _i32]),
-    "qsa_decode_step": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32,
-                               _i32, ctypes.c_float, ctypes.c_double, _c_p, _i64, _c_p, _i64, _c_p, _i64,
-                               _c_p, _c_p, _sz, _c_p]),
+    "qsa_decode_step": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _i64, _c_p, _i64,
+                               _c_p, _i64, _c_p, _i32, _i32, ctypes.c_float, ctypes.c_double, _c_p, _i64, _c_p,
+                               _i64, _c_p, _i64, _c_p, _c_p, _sz, _c_p]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -362,18 +362,26 @@ def decode_step_workspace(batch: int, budget: int, device="cuda") -> torch.Tenso
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos: int, budget: int,
-                out, lse, scores, sel, workspace, stream=None, scale: float = 1.0 / math.sqrt(D)):
-    """One decode step for B sequences, each with one new token at position pos,
-    through the single qsa_decode_step call.
+def _decode_positions(pos, B: int) -> list[int]:
+    return [int(pos)] * B if isinstance(pos, int) else [int(x) for x in pos]
+
+
+def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,
+                out, lse, scores, sel, workspace, stream=None, scale: float = 1.0 / math.sqrt(D),
+                v_new=None, k_idx_new=None):
+    """One decode step for B sequences, each with one new token at position
+    pos[b] (an int: the same for all), through the single qsa_decode_step call.
 
     q_raw [B, 1, 24, 256] and k_new_raw [B, 1, 2, 256] are unrotated; the
-    rotated K row goes to k_cache[:, pos] (the V and k_idx rows are expected
-    in place); kbar must hold blocks 0 .. pos // 4 - 1; workspace comes from
-    decode_step_workspace.  When the new token completes its block, that
-    block's key is compressed afterwards for the next steps.
+    rotated K row goes to k_cache[b, pos[b]]. v_new [B, 1, 2, 256] and
+    k_idx_new [B, 1, 128] (optional) are appended to v_cache / k_idx at
+    pos[b]; without them those rows are expected in place. kbar must hold
+    blocks 0 .. pos[b] // 4 - 1; when the new token completes its block the
+    step writes that block's key (from k_idx) for the next steps. workspace
+    comes from decode_step_workspace.
     """
     B = q_raw.shape[0]
+    p_list = _decode_positions(pos, B)
     _need(q_raw, "q", torch.bfloat16, (HQ, D))
     _need(k_new_raw, "k_new", torch.bfloat16, (HKV, D))
     _need(q_idx, "q_idx", torch.bfloat16, (HI, DI))
@@ -383,35 +391,60 @@ def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos: int
     _need(out, "out", torch.bfloat16, (HQ, D))
     _need(scores, "scores", torch.float32, ())
     _need(sel, "sel", torch.int32, (budget,))
-    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape or k_cache.shape[1] <= pos:
-        raise QSAError("k_cache / v_cache must share shape and strides and hold position pos")
+    if k_idx is not None:
+        _need(k_idx, "k_idx", torch.bfloat16, (DI,))
+    if v_new is not None:
+        _need(v_new, "v_new", torch.bfloat16, (HKV, D))
+        if v_new.stride(0) != k_new_raw.stride(0):
+            raise QSAError("v_new and k_new must share their sequence stride")
+    if k_idx_new is not None:
+        if k_idx is None:
+            raise QSAError("k_idx_new needs the k_idx cache")
+        if (not isinstance(k_idx_new, torch.Tensor) or k_idx_new.device.type != "cuda"
+                or k_idx_new.dtype != torch.bfloat16 or not k_idx_new.is_contiguous()
+                or k_idx_new.numel() != B * DI):
+            raise QSAError("k_idx_new must be a contiguous bf16 device tensor [B, 1, 128]")
+    top = max(p_list)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape or k_cache.shape[1] <= top:
+        raise QSAError("k_cache / v_cache must share shape and strides and hold every new position")
+    if k_idx is not None and k_idx.shape[1] <= top:
+        raise QSAError("k_idx must hold every new position")
     if lse is not None and (not lse.is_contiguous() or tuple(lse.shape) != (B, HQ)):
         raise QSAError("lse must be contiguous [B, 24]")
-    if scores.shape[-1] < pos // BLOCK or scores.shape[-1] % 4 or kbar.shape[1] < pos // BLOCK:
-        raise QSAError("scores / kbar do not cover the candidate blocks")
-    p = _positions([pos] * B, B)
-    _check(lib().qsa_decode_step(_ptr(q_raw), q_raw.stride(0), _ptr(k_new_raw), k_new_raw.stride(0), _ptr(q_idx),
-                                 q_idx.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0), _ptr(kbar),
-                                 kbar.stride(0), p, B, budget, float(scale), ROPE_THETA, _ptr(scores),
+    if scores.shape[-1] < top // BLOCK or scores.shape[-1] % 4:
+        raise QSAError("scores do not cover the candidate blocks")
+    if kbar.shape[1] < max((x + 1) // BLOCK if k_idx is not None else x // BLOCK for x in p_list):
+        raise QSAError("kbar does not cover the candidate (and completed) blocks")
+    p = _positions(p_list, B)
+    _check(lib().qsa_decode_step(_ptr(q_raw), q_raw.stride(0), _ptr(k_new_raw), _ptr(v_new), k_new_raw.stride(0),
+                                 _ptr(q_idx), q_idx.stride(0), _ptr(k_idx_new), _ptr(k_cache), _ptr(v_cache),
+                                 k_cache.stride(0), _ptr(k_idx), 0 if k_idx is None else k_idx.stride(0),
+                                 _ptr(kbar), kbar.stride(0), p, B, budget, float(scale), ROPE_THETA, _ptr(scores),
                                  scores.stride(0), _ptr(sel), sel.stride(0), _ptr(out), out.stride(0), _ptr(lse),
                                  _ptr(workspace), workspace.numel(), _stream(stream)),
            "qsa_decode_step")
-    if (pos + 1) % BLOCK == 0:
-        compress_block_keys(k_idx, pos // BLOCK, pos // BLOCK + 1, kbar, stream=stream)
     return out
 
 
-def decode_step_primitives(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos: int, budget: int,
-                           out, lse, scores, sel, workspace, q_rot, stream=None):
-    """The same decode step as a chain of the primitive calls (rope, scores,
-    selection, attention); workspace from decode_workspace."""
+def decode_step_primitives(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,
+                           out, lse, scores, sel, workspace, q_rot, stream=None, v_new=None, k_idx_new=None):
+    """The same decode step as a chain of the primitive calls (rotary, row
+    copies, scores, selection, attention, block compression); workspace from
+    decode_workspace."""
     B = q_raw.shape[0]
-    p = [pos] * B
+    p = _decode_positions(pos, B)
     rope_apply(q_raw, p, out=q_rot, stream=stream)
-    rope_apply(k_new_raw, p, out=k_cache[:, pos:pos + 1], stream=stream)
+    for b in range(B):
+        rope_apply(k_new_raw[b:b + 1], [p[b]], out=k_cache[b:b + 1, p[b]:p[b] + 1], stream=stream)
+        if v_new is not None:
+            v_cache[b, p[b]].copy_(v_new[b, 0])
+        if k_idx_new is not None:
+            k_idx[b, p[b]].copy_(k_idx_new.reshape(B, DI)[b])
     index_scores(q_idx, kbar, p, scores, stream=stream)
     select_topk(scores, p, budget, sel, stream=stream)
     sparse_attn_decode(q_rot[:, 0], k_cache, v_cache, sel[:, 0], p, out, lse, workspace, stream=stream)
-    if (pos + 1) % BLOCK == 0:
-        compress_block_keys(k_idx, pos // BLOCK, pos // BLOCK + 1, kbar, stream=stream)
+    if k_idx is not None:
+        for b in range(B):
+            if (p[b] + 1) % BLOCK == 0:
+                compress_block_keys(k_idx[b:b + 1], p[b] // BLOCK, p[b] // BLOCK + 1, kbar[b:b + 1], stream=stream)
     return out

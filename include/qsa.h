@@ -221,23 +221,36 @@ qsa_status_t qsa_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_st
 
 /*
  * One whole decode step of the layer for B sequences, each with one new token
- * at position q_pos[b] (steps 0, 2, 3 and 4): the unrotated new key row
- * k_new [B][2][256] is rotated into k_cache[b][q_pos[b]] (the new V row must
- * already be in v_cache), the block scores and the selection are computed as
- * by qsa_index_select_decode, and attention runs with q [B][24][256]
- * (unrotated; rotated on load exactly as qsa_rope_apply would).  kbar must
- * hold blocks 0 .. q_pos[b]/4 - 1; compressing the block a new token
- * completes is left to qsa_compress_block_keys (the step never scores it).
- * Equals rope_apply + index_scores + select_topk + sparse_attn_decode bit
- * for bit.  The workspace (qsa_decode_step_workspace_bytes) must be
- * zero-filled before its first use.
+ * at its own position q_pos[b] (steps 0 to 4; positions may differ per
+ * sequence).  In order, as one asynchronous call:
+ *  - appends the new token's rows: the unrotated key row k_new [B][2][256]
+ *    is rotated into k_cache[b][q_pos[b]]; v_new [B][2][256] (NULL: the row
+ *    is already in v_cache) is copied to v_cache[b][q_pos[b]]; k_idx_new
+ *    [B][128] contiguous (NULL: the row is already in k_idx) is copied to
+ *    k_idx[b][q_pos[b]];
+ *  - scores blocks 0 .. q_pos[b]/4 - 1 of kbar and selects as
+ *    qsa_index_select_decode does;
+ *  - attends with q [B][24][256] (unrotated; rotated on load exactly as
+ *    qsa_rope_apply would) over the selection and the own block;
+ *  - when the new token completes its block (q_pos[b] % 4 == 3) and k_idx is
+ *    given, writes that block's key kbar[b][q_pos[b]/4] exactly as
+ *    qsa_compress_block_keys would, for the next steps (this step never
+ *    scores it).  k_idx NULL: no indexer-key append and no compression.
+ * k_new / v_new share kv_new_seq_stride; k_cache and v_cache share
+ * kv_seq_stride; k_idx is [B][L][128] with k_idx_seq_stride.  Equals the
+ * chain rope_apply + row copies + index_scores + select_topk +
+ * sparse_attn_decode + compress_block_keys bit for bit.  The workspace
+ * (qsa_decode_step_workspace_bytes) must be zero-filled before its first use;
+ * every call leaves it zeroed again.
  */
 size_t       qsa_decode_step_workspace_bytes(int32_t batch, int32_t budget);
 qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
-                             const uint16_t* k_new, int64_t k_new_seq_stride,
+                             const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
                              const uint16_t* q_idx, int64_t q_idx_seq_stride,
-                             uint16_t* k_cache, const uint16_t* v_cache, int64_t kv_seq_stride,
-                             const uint16_t* kbar, int64_t kbar_seq_stride,
+                             const uint16_t* k_idx_new,
+                             uint16_t* k_cache, uint16_t* v_cache, int64_t kv_seq_stride,
+                             uint16_t* k_idx, int64_t k_idx_seq_stride,
+                             uint16_t* kbar, int64_t kbar_seq_stride,
                              const int32_t* q_pos, int32_t batch, int32_t budget,
                              float softmax_scale, double rope_theta,
                              float* scores, int64_t scores_seq_stride,

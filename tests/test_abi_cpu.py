@@ -162,3 +162,28 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros((1, 4, 2, 256), dtype=torch.bfloat16)
     with pytest.raises(qsa.QSAError):
         qsa.rope_apply(x, [0])
+
+
+def test_decode_step_validation(L):
+    """qsa_decode_step rejects, before any launch: an indexer-key row without
+    the indexer-key cache, misaligned new rows, a k_idx stride that does not
+    reach the new positions, and a short workspace."""
+    B, budget = 2, 512
+    p = _pos(4099, 9000)
+    ld = 9000 // 4 // 4 * 4 + 4
+    ws_need = L.qsa_decode_step_workspace_bytes(B, budget)
+    assert ws_need > 0 and L.qsa_decode_step_workspace_bytes(0, budget) == 0
+
+    def call(v_new=FAKE, k_idx_new=FAKE, k_idx=FAKE, k_idx_stride=9001 * 128, ws=ws_need):
+        return L.qsa_decode_step(FAKE, 24 * 256, FAKE, v_new, 2 * 256, FAKE, 4 * 128, k_idx_new,
+                                 FAKE, FAKE, 9001 * 512, k_idx, k_idx_stride, FAKE, 2251 * 128,
+                                 p, B, budget, 0.0625, 1.0e7, FAKE, ld, FAKE, budget, FAKE, 24 * 256,
+                                 NULL, FAKE, ws, None)
+
+    assert call(k_idx=NULL) == INVALID
+    assert "k_idx" in L.qsa_last_error().decode()
+    assert call(v_new=FAKE + 8) == INVALID
+    assert call(k_idx_new=FAKE + 8) == INVALID
+    assert call(k_idx_stride=9000 * 128) == INVALID              # row 9000 out of reach
+    assert "k_idx_seq_stride" in L.qsa_last_error().decode()
+    assert call(ws=ws_need - 1) == WORKSPACE

@@ -204,3 +204,62 @@ def test_index_select_prefill_workspace_reuse_across_shapes():
         qsa.index_select_prefill(q, kbar, pos0, budget, torch.empty_like(s_ref), sel, ws)
         torch.cuda.synchronize()
         assert torch.equal(sel, sel_ref), (kind, pos0, tq)
+
+
+# ---------------------------------------------------------------- serving decode step
+
+@pytest.mark.parametrize("pos,budget", [([4099, 9000, 4103], 512), ([20003, 7, 65539], 64), ([3, 1, 2], 8)])
+def test_decode_step_appends_rows_and_compresses(pos, budget):
+    """The one-call step with the new V and indexer-key rows and per-sequence
+    positions equals the primitive chain bit for bit, including the rows it
+    appends and the block key it writes when a new token completes a block."""
+    say(f"decode_step serving pos={pos} budget={budget}")
+    B = len(pos)
+    L = max(pos) + 1
+    wl = I.custom_workload("decode", batch=B, ctx=L - 1, tq=1, budget=budget, n_needles=0, seed=sum(pos))
+    x = I.make_inputs(wl)
+    dev = "cuda"
+    g = torch.Generator().manual_seed(5)
+    v_new = (torch.randn((B, 1, 2, 256), generator=g)).to(torch.bfloat16).to(dev)
+    k_idx_new = (torch.randn((B, 1, 128), generator=g) / math.sqrt(128)).to(torch.bfloat16).to(dev)
+    k_new = (torch.randn((B, 1, 2, 256), generator=g)).to(torch.bfloat16).to(dev)
+    ld = max(4, (L // 4 + 3) // 4 * 4)
+    outs = []
+    for fused in (False, True):
+        kc = x.k.to(dev)
+        qsa.rope_apply(kc, [0] * B)
+        v = x.v.to(dev)
+        ki = x.k_idx.to(dev)
+        for b in range(B):                            # the rows the step must write hold garbage
+            kc[b, pos[b]] = 7.0
+            v[b, pos[b]] = -3.0
+            ki[b, pos[b]] = 5.0
+        kb = torch.full((B, L // 4 + 1, 128), 9.0, dtype=torch.bfloat16, device=dev)
+        for b in range(B):
+            if pos[b] // 4:
+                qsa.compress_block_keys(ki[b:b + 1], 0, pos[b] // 4, kb[b:b + 1])
+        scores = torch.full((B, 1, ld), float("nan"), device=dev)
+        sel = torch.empty((B, 1, budget), dtype=torch.int32, device=dev)
+        out = torch.empty((B, 24, 256), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, 24), dtype=torch.float32, device=dev)
+        q_raw, q_idx = x.q.to(dev), x.q_idx.to(dev)
+        if fused:
+            qsa.decode_step(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel,
+                            qsa.decode_step_workspace(B, budget), v_new=v_new, k_idx_new=k_idx_new)
+        else:
+            qsa.decode_step_primitives(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel,
+                                       qsa.decode_workspace(B, budget), torch.empty_like(q_raw), v_new=v_new,
+                                       k_idx_new=k_idx_new)
+        torch.cuda.synchronize()
+        rows = [(kc[b, pos[b]].clone(), v[b, pos[b]].clone(), ki[b, pos[b]].clone(), kb[b].clone(),
+                 scores[b, 0, :pos[b] // 4].clone(), sel[b].clone()) for b in range(B)]
+        outs.append((rows, out.clone(), lse.clone()))
+    (ra, oa, la), (rb, ob, lb) = outs
+    for b in range(B):
+        for name, a, c in zip(("k row", "v row", "k_idx row", "kbar", "scores", "sel"), ra[b], rb[b]):
+            assert torch.equal(a.view(torch.uint8), c.view(torch.uint8)), (b, name)
+        assert torch.equal(rb[b][1], v_new[b, 0]) and torch.equal(rb[b][2], k_idx_new[b, 0]), b
+        if (pos[b] + 1) % 4 == 0:                     # the completed block was written, the next one not
+            assert not torch.equal(rb[b][3][pos[b] // 4], torch.full_like(rb[b][3][0], 9.0)), b
+    assert torch.equal(oa.view(torch.uint8), ob.view(torch.uint8))
+    assert torch.equal(la.view(torch.uint8), lb.view(torch.uint8))

@@ -332,3 +332,44 @@ def test_end_to_end_decode_B32_ctx32K():
     o = wl.ctx // 4
     compare_rows(layer, x, rows, lambda b, t: scores[b, 0, :o], lambda b, t: sel[b, 0],
                  lambda b, t: out[b], lambda b, t: lse[b])
+
+
+def test_consecutive_decode_steps_match_the_oracle_rows():
+    """Serving decode steps one token at a time (each appends its K, V and
+    indexer-key rows and compresses the block it completes) give, row by
+    row, the oracle's causal QSA output for those tokens."""
+    B, ctx, S, budget = 2, 20001, 6, 512
+    wl = I.custom_workload("prefill", batch=B, ctx=ctx, tq=S, budget=budget, n_needles=4, seed=31)
+    say(f"consecutive decode steps {wl.name}")
+    x = I.make_inputs(wl)
+    dev = "cuda"
+    L = ctx + S
+    kc = torch.zeros((B, L, 2, 256), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(kc)
+    ki = torch.zeros((B, L, 128), dtype=torch.bfloat16, device=dev)
+    kc[:, :ctx] = x.k[:, :ctx].to(dev)
+    qsa.rope_apply(kc[:, :ctx], [0] * B)
+    v[:, :ctx] = x.v[:, :ctx].to(dev)
+    ki[:, :ctx] = x.k_idx[:, :ctx].to(dev)
+    kb = torch.zeros((B, L // 4 + 1, 128), dtype=torch.bfloat16, device=dev)
+    qsa.compress_block_keys(ki, 0, ctx // 4, kb)
+    ld = (L // 4 + 3) // 4 * 4
+    ws = qsa.decode_step_workspace(B, budget)
+    res = {}
+    for s in range(S):
+        t = ctx + s
+        scores = torch.empty((B, 1, ld), dtype=torch.float32, device=dev)
+        sel = torch.empty((B, 1, budget), dtype=torch.int32, device=dev)
+        out = torch.empty((B, 24, 256), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, 24), dtype=torch.float32, device=dev)
+        qsa.decode_step(x.q[:, s:s + 1].contiguous().to(dev), x.k[:, t:t + 1].contiguous().to(dev),
+                        x.q_idx[:, s:s + 1].contiguous().to(dev), ki, kc, v, kb, t, budget, out, lse, scores, sel,
+                        ws, v_new=x.v[:, t:t + 1].contiguous().to(dev),
+                        k_idx_new=x.k_idx[:, t:t + 1].contiguous().to(dev))
+        torch.cuda.synchronize()
+        for b in range(B):
+            res[(b, t)] = (scores[b, 0, :t // 4].cpu().numpy(), sel[b, 0].cpu().numpy(),
+                           out[b].float().cpu().numpy(), lse[b].cpu().numpy())
+    rows = sorted(res)
+    compare_rows(oracle_layer(x), x, rows, lambda b, t: res[(b, t)][0], lambda b, t: res[(b, t)][1],
+                 lambda b, t: res[(b, t)][2], lambda b, t: res[(b, t)][3])
