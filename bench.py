@@ -6,8 +6,12 @@ Prints ONE JSON line.  `value` is prefill throughput (new tokens/s) of the
 prefix, the pages' 90% prefix-cache-hit setting), one step = every step of the
 layer (rotary of the new Q/K rows, compression of the blocks they complete,
 index scores, block selection and sparse attention for all 8192-query chunks).
-The same line carries the 1M-context decode step (B=4, one new token each)
-under "decode".  Inputs are seeded synthetic tensors already resident in HBM.
+The same line carries the 1M-context serving decode step (B=4, one new token
+each: its K/V/indexer-key rows appended, scores, selection, attention) under
+"decode", and the same step with 4 new tokens per sequence (the shape of
+multi-token prediction or speculative verification) under
+"decode_multi_token".  Inputs are seeded synthetic tensors already resident
+in HBM.
 
 Timing: W untimed warm-up steps, then K steps between two device
 synchronisations; per-kernel durations come from HIP events recorded on the
@@ -51,6 +55,8 @@ def parse():
     ap.add_argument("--decode-workload", default="decode_B4_ctx1M")
     ap.add_argument("--decode-steps", type=int, default=30)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-tq", type=int, default=4,
+                    help="also time a decode step of this many new tokens per sequence (1 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=48, help="oracle rows timed for cpu_baseline (0 = skip)")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -144,11 +150,16 @@ class Decode:
         dev = "cuda"
         self.wl, self.qsa, self.torch = wl, qsa, torch
         self.pos = ctx
-        self.k_cache = x.k.to(dev)
+        # caches with room for up to 4 new tokens (the multi-token step)
+        L = ctx + 4
+        self.k_cache = torch.zeros((B, L, 2, 256), dtype=torch.bfloat16, device=dev)
+        self.k_cache[:, :ctx + 1].copy_(x.k)
         qsa.rope_apply(self.k_cache[:, :ctx], [0] * B)
-        self.v_cache = x.v.to(dev)
-        self.k_idx = x.k_idx.to(dev)
-        self.kbar = torch.zeros((B, max(1, (ctx + 1) // 4), 128), dtype=torch.bfloat16, device=dev)
+        self.v_cache = torch.zeros_like(self.k_cache)
+        self.v_cache[:, :ctx + 1].copy_(x.v)
+        self.k_idx = torch.zeros((B, L, 128), dtype=torch.bfloat16, device=dev)
+        self.k_idx[:, :ctx + 1].copy_(x.k_idx)
+        self.kbar = torch.zeros((B, L // 4 + 1, 128), dtype=torch.bfloat16, device=dev)
         qsa.compress_block_keys(self.k_idx, 0, ctx // 4, self.kbar)
         self.q_raw = x.q.to(dev)
         self.k_new = x.k[:, ctx:ctx + 1].contiguous().to(dev)
@@ -162,6 +173,31 @@ class Decode:
         self.lse = torch.empty((B, 24), dtype=torch.float32, device=dev)
         self.ws = qsa.decode_step_workspace(B, wl.budget)
         torch.cuda.synchronize()
+
+    def multi_setup(self, tq: int, seed: int = 77):
+        """Synthetic rows of tq new tokens per sequence (same distributions as
+        the workload's): the shape of a multi-token prediction or speculative
+        verification step."""
+        torch, qsa = self.torch, self.qsa
+        B, dev, bf = self.wl.batch, "cuda", torch.bfloat16
+        g = torch.Generator().manual_seed(seed)
+        self.m_tq = tq
+        self.m_q = torch.randn((B, tq, 24, 256), generator=g).to(bf).to(dev)
+        self.m_q_idx = (torch.randn((B, tq, 4, 128), generator=g) / 128 ** 0.5).to(bf).to(dev)
+        self.m_k = torch.randn((B, tq, 2, 256), generator=g).to(bf).to(dev)
+        self.m_v = torch.randn((B, tq, 2, 256), generator=g).to(bf).to(dev)
+        self.m_k_idx = (torch.randn((B, tq, 128), generator=g) / 128 ** 0.5).to(bf).to(dev)
+        ld = self.scores.shape[-1] + 4
+        self.m_scores = torch.empty((B, tq, ld), dtype=torch.float32, device=dev)
+        self.m_sel = torch.empty((B, tq, self.wl.budget), dtype=torch.int32, device=dev)
+        self.m_out = torch.empty((B, tq, 24, 256), dtype=bf, device=dev)
+        self.m_lse = torch.empty((B, tq, 24), dtype=torch.float32, device=dev)
+        self.m_ws = qsa.decode_step_workspace(B, self.wl.budget, tq=tq)
+
+    def multi_step(self):
+        self.qsa.decode_step(self.m_q, self.m_k, self.m_q_idx, self.k_idx, self.k_cache, self.v_cache, self.kbar,
+                             self.pos, self.wl.budget, self.m_out, self.m_lse, self.m_scores, self.m_sel, self.m_ws,
+                             v_new=self.m_v, k_idx_new=self.m_k_idx)
 
     def step(self, timer):
         """One serving decode step through the single qsa_decode_step call: the
@@ -424,6 +460,41 @@ def main():
             },
         }
         log(args, f"decode: median {med * 1e3:.1f} us/step; index-select {idx_avg * 1e6:.1f} us")
+        if args.decode_tq > 1:
+            # tq new tokens per sequence in one step: one pass over the block
+            # keys scores all of them; each row has its own selection and attention
+            mt = args.decode_tq
+            dd.multi_setup(mt)
+            for _ in range(3):
+                dd.multi_step()
+            torch.cuda.synchronize()
+            m_ms = []
+            for _ in range(args.decode_steps):
+                flush.sum()
+                s = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                s.record()
+                dd.multi_step()
+                e.record()
+                torch.cuda.synchronize()
+                m_ms.append(s.elapsed_time(e))
+            m_ms.sort()
+            m_med = m_ms[len(m_ms) // 2]
+            m_gather = dwl.batch * sum(attended_tokens(dwl.ctx + t, dwl.budget) for t in range(mt)) * 2 * 2 * 256 * 2
+            m_bytes = kbar_bytes + m_gather + dwl.batch * mt * (24 * 256 * 2 * 2 + dwl.budget * 4)
+            rec["decode_multi_token"] = {
+                "tokens_per_sequence": mt,
+                "batch": dwl.batch,
+                "context": dwl.ctx,
+                "step_us_median": m_med * 1e3,
+                "step_us_min": m_ms[0] * 1e3,
+                "us_per_token": m_med * 1e3 / (dwl.batch * mt),
+                "single_token_us_per_token": med * 1e3 / dwl.batch,
+                "hbm_frac_step": m_bytes / (m_med / 1e3) / HBM_PEAK,
+                "algorithmic_bytes_per_step": m_bytes,
+                "data": "synthetic new-token rows of the workload's distributions",
+            }
+            log(args, f"decode, {mt} tokens per sequence: median {m_med * 1e3:.1f} us/step")
         del dd, flush
         torch.cuda.empty_cache()
 

@@ -292,10 +292,12 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
 
 // ---------------------------------------------------------------- decode
 
-// Split the budget over n_split workgroups per sequence; each writes the
-// partial (reference max, sum, unnormalised O) of its blocks for the 24 heads.
-static void decode_split(int batch, int budget, int* n_split, int* bps) {
-    int s = 256 / (batch > 0 ? batch : 1);
+// Decode rows: token t of sequence b (row r = b * tq + t) sits at position
+// pos[b] + t; per sequence q and out are [tq][24][256] and sel [tq][budget].
+// Split each row's budget over n_split workgroups; each writes the partial
+// (reference max, sum, unnormalised O) of its blocks for the 24 heads.
+static void decode_split(int rows, int budget, int* n_split, int* bps) {
+    int s = 256 / (rows > 0 ? rows : 1);
     if (s < 1) s = 1;
     if (s > 64) s = 64;
     const int max_s = (budget + 3) / 4;
@@ -306,25 +308,29 @@ static void decode_split(int batch, int budget, int* n_split, int* bps) {
     *n_split = (budget + per - 1) / per;
 }
 
-size_t decode_workspace_bytes(int batch, int budget) {
+size_t decode_workspace_bytes(int rows, int budget) {
     int s, per;
-    decode_split(batch, budget, &s, &per);
-    return static_cast<size_t>(batch) * s * kHq * (2 + kD) * sizeof(float);
+    decode_split(rows, budget, &s, &per);
+    return static_cast<size_t>(rows) * s * kHq * (2 + kD) * sizeof(float);
 }
 
 __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     const uint16_t* __restrict__ q, int64_t qs, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs, const int32_t* __restrict__ sel, int64_t sels,
-    Positions pos, int budget, int n_split, int bps, float c, float* __restrict__ ws_ml,
+    Positions pos, int budget, int tq, int n_split, int bps, float c, float* __restrict__ ws_ml,
     float* __restrict__ ws_acc, InvFreq inv, int rope_q) {
     __shared__ uint16_t vt_all[2 * kVtElems];
     const int g = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int c16 = lane & 15;
     const int G = lane >> 4;
-    const int b = blockIdx.x / n_split;
+    const int r = blockIdx.x / n_split;
     const int s = blockIdx.x % n_split;
-    const int p = pos.p[b];
+    const int b = r / tq;
+    const int t = r % tq;
+    const int p = pos.p[b] + t;
+    const int32_t* selrow = sel + b * sels + t * budget;
+    const uint16_t* qrow = q + b * qs + t * (kHq * kD);
     const int head = g * kGroup + c16;
     const bool head_ok = c16 < kGroup;
 
@@ -335,15 +341,15 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     // query loads first, then the selection and the first chunk; the rotary
     // angles are computed while those are in flight
     bf16x8_t qf[8];
-    issue_q_frags(q + b * qs + (head_ok ? head : 0) * kD, head_ok, qf);
+    issue_q_frags(qrow + (head_ok ? head : 0) * kD, head_ok, qf);
     Chunk first;
-    load_chunk(kg, vg, sel + b * sels, blk_begin, blk_end, p, first);
+    load_chunk(kg, vg, selrow, blk_begin, blk_end, p, first);
     if (rope_q) rotate_q_frags(rope_angle(p, inv), qf);
     WaveState st;
     init_state(st);
-    attend_blocks<2>(kg, vg, sel + b * sels, blk_begin, blk_end, p, qf, c, st, vt_all + g * kVtElems, first);
+    attend_blocks<2>(kg, vg, selrow, blk_begin, blk_end, p, qf, c, st, vt_all + g * kVtElems, first);
     if (head_ok) {
-        const int64_t idx = (static_cast<int64_t>(b) * n_split + s) * kHq + head;
+        const int64_t idx = (static_cast<int64_t>(r) * n_split + s) * kHq + head;
         if (G == 0) {
             ws_ml[2 * idx] = st.m;
             ws_ml[2 * idx + 1] = st.l;
@@ -355,11 +361,11 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     }
 }
 
-// One workgroup of 256 threads per (sequence, head): thread t merges dims
+// One workgroup of 256 threads per (row, head): thread t merges dims
 // 4*(t%64) .. +3 over the splits s = t/64 + 4k, with all its loads issued
 // before any is used; the 4 partial sums meet in LDS.
 __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
-    const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, int n_split, float scale,
+    const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, int tq, int n_split, float scale,
     float c, uint16_t* __restrict__ out, int64_t os, float* __restrict__ lse) {
     __shared__ float w_s[64];
     __shared__ float4 part[3][64];
@@ -367,9 +373,11 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int quarter = tid >> 6;
-    const int b = blockIdx.x / kHq;
+    const int r = blockIdx.x / kHq;                       // row = token t of sequence b
     const int h = blockIdx.x % kHq;
-    const int64_t base = static_cast<int64_t>(b) * n_split * kHq + h;    // split s at base + s * kHq
+    const int b = r / tq;
+    const int t = r % tq;
+    const int64_t base = static_cast<int64_t>(r) * n_split * kHq + h;    // split s at base + s * kHq
     if (quarter == 0) {
         float m = -INFINITY, l = 0.f;
         if (lane < n_split) {
@@ -421,39 +429,40 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
         uint2 o;
         o.x = f32_to_bf16(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
         o.y = f32_to_bf16(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
-        *reinterpret_cast<uint2*>(out + b * os + h * kD + 4 * lane) = o;
-        if (lse != nullptr && lane == 0) lse[static_cast<int64_t>(b) * kHq + h] = sh_M * scale + logf(sh_L);
+        *reinterpret_cast<uint2*>(out + b * os + (t * kHq + h) * kD + 4 * lane) = o;
+        if (lse != nullptr && lane == 0) lse[static_cast<int64_t>(r) * kHq + h] = sh_M * scale + logf(sh_L);
     }
 }
 
 hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* k,
                                  const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
-                                 const Positions& pos, int batch, int budget, float scale,
+                                 const Positions& pos, int batch, int tq, int budget, float scale,
                                  uint16_t* out, int64_t os, float* lse, void* ws, double rope_theta,
                                  hipStream_t stream) {
-    if (batch == 0) return hipSuccess;
+    const int rows = batch * tq;
+    if (rows == 0) return hipSuccess;
     int n_split, bps;
-    decode_split(batch, budget, &n_split, &bps);
+    decode_split(rows, budget, &n_split, &bps);
     float* ws_ml = static_cast<float*>(ws);
-    float* ws_acc = ws_ml + static_cast<size_t>(batch) * n_split * kHq * 2;
+    float* ws_acc = ws_ml + static_cast<size_t>(rows) * n_split * kHq * 2;
     const float c = scale * 1.4426950408889634f;
     const InvFreq inv = make_inv_freq(rope_theta > 0.0 ? rope_theta : 1.0e7);
-    hipLaunchKernelGGL(attn_decode_split_kernel, dim3(static_cast<unsigned>(batch * n_split)),
-                       dim3(128), 0, stream, q, qs, k, v, kvs, sel, sels, pos, budget, n_split, bps,
+    hipLaunchKernelGGL(attn_decode_split_kernel, dim3(static_cast<unsigned>(rows * n_split)),
+                       dim3(128), 0, stream, q, qs, k, v, kvs, sel, sels, pos, budget, tq, n_split, bps,
                        c, ws_ml, ws_acc, inv, rope_theta > 0.0 ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(static_cast<unsigned>(batch * kHq)), dim3(256),
-                       0, stream, ws_ml, ws_acc, n_split, scale, c, out, os, lse);
+    hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(static_cast<unsigned>(rows * kHq)), dim3(256),
+                       0, stream, ws_ml, ws_acc, tq, n_split, scale, c, out, os, lse);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
                               const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
-                              const Positions& pos, int batch, int budget, float scale,
+                              const Positions& pos, int batch, int tq, int budget, float scale,
                               uint16_t* out, int64_t os, float* lse, void* ws,
                               hipStream_t stream) {
-    return launch_attn_decode_ex(q, qs, k, v, kvs, sel, sels, pos, batch, budget, scale, out, os, lse,
+    return launch_attn_decode_ex(q, qs, k, v, kvs, sel, sels, pos, batch, tq, budget, scale, out, os, lse,
                                  ws, 0.0, stream);
 }
 

@@ -1,7 +1,9 @@
-// Fused index-select for decode rows (one query token per sequence, up to
-// 262144 candidate blocks): the same scores and the same selection as
-// index_scores_kernel followed by select_kernel, spread over hundreds of
-// workgroups per row.  Three launches; every hand-off between workgroups
+// Fused index-select for decode rows (1 to 4 consecutive query tokens per
+// sequence, up to 262144 candidate blocks each; a row is one token of one
+// sequence): the same scores and the same selection as index_scores_kernel
+// followed by select_kernel, spread over hundreds of workgroups per row.  The
+// tokens of a sequence share one pass over its block keys (they are columns
+// of the same matrix-core tiles).  Three launches; every hand-off between workgroups
 // goes through a kernel boundary or a device-scope atomic, never through an
 // in-kernel fence (an agent-scope fence writes back and invalidates the L2 of
 // the XCD, which costs microseconds per workgroup on this part):
@@ -11,15 +13,15 @@
 //                          flight.  Scores every candidate with the shared MFMA
 //                          block_scores (bit-identical to index_scores_kernel),
 //                          stores the scores, counts the top 12 bits of each
-//                          ordered key in an LDS histogram and adds it to a
-//                          per-sequence global histogram.  In a decode step it
-//                          also appends the new rows (append_rows).
-//  decode_filter_kernel    B x F workgroups: each finds the threshold bin from
+//                          ordered key in an LDS histogram per token and adds
+//                          them to per-row global histograms.  In a decode step
+//                          it also appends the new rows (append_rows).
+//  decode_filter_kernel    rows x F workgroups: each finds the threshold bin from
 //                          the global histogram, then collects its slice's keys
 //                          above the bin (winners) and in the bin (candidates)
-//                          in LDS and appends them to per-sequence lists with
+//                          in LDS and appends them to per-row lists with
 //                          one atomic reservation per list.
-//  decode_finalize_kernel  B workgroups: sorts the candidates, takes the ones
+//  decode_finalize_kernel  one workgroup per row: sorts the candidates, takes the ones
 //                          still needed, merges, sorts ascending and writes sel;
 //                          if the bin overflowed the list it runs the full radix
 //                          select on the stored row.  Leaves the histogram and
@@ -35,31 +37,32 @@ constexpr int kDecHistBits = 12;
 constexpr int kDecHistBins = 1 << kDecHistBits;
 constexpr int kDecShift = 32 - kDecHistBits;
 constexpr int kDecCap = 4096;        // threshold-bin candidates sorted in LDS by the last workgroup
-constexpr int kCtrl = 16;            // control words per sequence
+constexpr int kCtrl = 16;            // control words per row
 
 enum { kDoneScan = 0, kDoneFilter, kNDef, kNCand, kBin, kAbove, kInBin };
 
+// per row r = b * tq + t (token t of sequence b, at position q_pos[b] + t)
 struct DecodeWs {
-    uint32_t* hist;     // [B][4096]
-    uint32_t* ctrl;     // [B][16]
-    int32_t* defl;      // [B][QSA_MAX_BUDGET]  keys above the threshold bin
-    uint64_t* cand;     // [B][kDecCap]         keys in the threshold bin: key << 32 | ~j
+    uint32_t* hist;     // [rows][4096]
+    uint32_t* ctrl;     // [rows][16]
+    int32_t* defl;      // [rows][QSA_MAX_BUDGET]  keys above the threshold bin
+    uint64_t* cand;     // [rows][kDecCap]         keys in the threshold bin: key << 32 | ~j
 };
 
-size_t decode_select_ws_bytes(int batch) {
-    return static_cast<size_t>(batch) *
+size_t decode_select_ws_bytes(int rows) {
+    return static_cast<size_t>(rows) *
            (kDecHistBins * 4 + kCtrl * 4 + QSA_MAX_BUDGET * 4 + kDecCap * 8);
 }
 
-static DecodeWs carve(void* ws, int batch) {
+static DecodeWs carve(void* ws, int rows) {
     char* p = static_cast<char*>(ws);
     DecodeWs w;
     w.hist = reinterpret_cast<uint32_t*>(p);
-    p += static_cast<size_t>(batch) * kDecHistBins * 4;
+    p += static_cast<size_t>(rows) * kDecHistBins * 4;
     w.ctrl = reinterpret_cast<uint32_t*>(p);
-    p += static_cast<size_t>(batch) * kCtrl * 4;
+    p += static_cast<size_t>(rows) * kCtrl * 4;
     w.defl = reinterpret_cast<int32_t*>(p);
-    p += static_cast<size_t>(batch) * QSA_MAX_BUDGET * 4;
+    p += static_cast<size_t>(rows) * QSA_MAX_BUDGET * 4;
     w.cand = reinterpret_cast<uint64_t*>(p);
     return w;
 }
@@ -82,87 +85,104 @@ struct AppendArgs {
     InvFreq inv;
 };
 
-// The rows of one sequence's new position p, by the first workgroup of the
-// sequence: wave 0 rotates the K row into the cache (step 0), wave 1 copies
-// the V row, wave 2 copies the indexer key row and, when p completes its
-// block, compresses the block (step 1) for the next positions.  Nothing else
-// in the step reads these rows (the scan reads blocks j < p / 4 only; the
-// attention runs in a later launch).
-__device__ __forceinline__ void append_rows(const AppendArgs& ap, int b, int p, int wave) {
+// The rows of one sequence's new tokens p0 .. p0 + tq - 1: wave 0 rotates the
+// K rows into the cache (step 0), wave 1 copies the V rows, wave 2 copies the
+// indexer key rows and, for each new token that completes its block,
+// compresses the block (step 1), taking the block's new rows from the inputs
+// (not back through memory).  With one token per sequence this runs in the
+// first scan workgroup of the sequence: the scan reads blocks j < p0 / 4 only
+// and attention runs in a later launch.  With several, a block an earlier new
+// token completes is a candidate of the later ones, so it runs in its own
+// launch (decode_append_kernel) before the scan.
+__device__ __forceinline__ void append_rows(const AppendArgs& ap, int b, int p0, int tq, int wave) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = static_cast<int64_t>(p) * (kHkv * kD);
     if (wave == 0 && ap.k_new != nullptr)
-        rope_row_wave(ap.k_new + b * ap.kns, ap.k_cache + b * ap.kvs + row, kHkv, static_cast<double>(p), ap.inv,
-                      false);
-    if (wave == 1 && ap.v_new != nullptr)        // 2 x 256 values: 16 B per lane
-        *reinterpret_cast<uint4*>(ap.v_cache + b * ap.kvs + row + 8 * lane) =
-            *reinterpret_cast<const uint4*>(ap.v_new + b * ap.vns + 8 * lane);
+        for (int t = 0; t < tq; ++t)
+            rope_row_wave(ap.k_new + b * ap.kns + t * (kHkv * kD),
+                          ap.k_cache + b * ap.kvs + static_cast<int64_t>(p0 + t) * (kHkv * kD), kHkv,
+                          static_cast<double>(p0 + t), ap.inv, false);
+    if (wave == 1 && ap.v_new != nullptr)        // 2 x 256 values per row: 16 B per lane
+        for (int t = 0; t < tq; ++t)
+            *reinterpret_cast<uint4*>(ap.v_cache + b * ap.kvs + static_cast<int64_t>(p0 + t) * (kHkv * kD) + 8 * lane) =
+                *reinterpret_cast<const uint4*>(ap.v_new + b * ap.vns + t * (kHkv * kD) + 8 * lane);
     if (wave == 2 && ap.k_idx != nullptr && lane < kDi / 8) {
         uint16_t* kr = ap.k_idx + b * ap.kis + 8 * lane;
-        uint4 cur;
-        if (ap.k_idx_new != nullptr) {
-            cur = *reinterpret_cast<const uint4*>(ap.k_idx_new + b * ap.kins + 8 * lane);
-            *reinterpret_cast<uint4*>(kr + static_cast<int64_t>(p) * kDi) = cur;
-        } else {
-            cur = *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(p) * kDi);
-        }
-        if (p % kBlock == kBlock - 1) {
+        const uint16_t* kn = ap.k_idx_new != nullptr ? ap.k_idx_new + b * ap.kins + 8 * lane : nullptr;
+        auto row = [&](int x) -> uint4 {           // indexer key row x of this sequence, this lane's 8 dims
+            return (kn != nullptr && x >= p0) ? *reinterpret_cast<const uint4*>(kn + (x - p0) * kDi)
+                                              : *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(x) * kDi);
+        };
+        if (kn != nullptr)
+            for (int t = 0; t < tq; ++t)
+                *reinterpret_cast<uint4*>(kr + static_cast<int64_t>(p0 + t) * kDi) =
+                    *reinterpret_cast<const uint4*>(kn + t * kDi);
+        for (int t = 0; t < tq; ++t) {
+            const int x = p0 + t;
+            if (x % kBlock != kBlock - 1) continue;
             uint4 r[kBlock];
 #pragma unroll
-            for (int t = 0; t < kBlock - 1; ++t)
-                r[t] = *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(p - (kBlock - 1) + t) * kDi);
-            r[kBlock - 1] = cur;
-            *reinterpret_cast<uint4*>(ap.kbar + b * ap.kbs + static_cast<int64_t>(p / kBlock) * kDi + 8 * lane) =
+            for (int i = 0; i < kBlock; ++i) r[i] = row(x - (kBlock - 1) + i);
+            *reinterpret_cast<uint4*>(ap.kbar + b * ap.kbs + static_cast<int64_t>(x / kBlock) * kDi + 8 * lane) =
                 compress_rows(r);
         }
     }
 }
 
+__global__ __launch_bounds__(192) void decode_append_kernel(Positions pos, int tq, AppendArgs ap) {
+    append_rows(ap, blockIdx.x, pos.p[blockIdx.x], tq, threadIdx.x >> 6);
+}
+
+// hist: tq x 4096 words of dynamic LDS (one histogram per token)
 template <int STEPS>
 __global__ __launch_bounds__(256) void decode_scan_kernel(
     const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
-    Positions pos, int budget, int wg_per_seq, float* __restrict__ scores,
-    int64_t ss, DecodeWs ws, AppendArgs ap, int append) {
-    __shared__ uint32_t hist[kDecHistBins];
+    Positions pos, int budget, int tq, int wg_per_seq, float* __restrict__ scores,
+    int64_t ss, int64_t sld, DecodeWs ws, AppendArgs ap, int append) {
+    extern __shared__ uint32_t hist[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // scalar: loop control stays uniform
     const int b = blockIdx.x / wg_per_seq;
     const int g = blockIdx.x % wg_per_seq;
-    const int p = pos.p[b];
-    const int o = p / kBlock;
-    const int keep = min(budget - 1, o);
-    const bool need_hist = keep > 0 && keep < o;
+    const int p0 = pos.p[b];
+    const int o_last = (p0 + tq - 1) / kBlock;           // blocks below the last token's own block
 
-    if (append && g == 0) append_rows(ap, b, p, wave);
+    if (append && g == 0) append_rows(ap, b, p0, tq, wave);
 
-    for (int k = tid; k < kDecHistBins; k += 256) hist[k] = 0;
+    for (int k = tid; k < tq * kDecHistBins; k += 256) hist[k] = 0;
     __syncthreads();
 
     const int c16 = lane & 15;
     const int G = lane >> 4;
+    // column c16 < tq: token c16, its candidates j < o_c; histogram only when
+    // its selection is not trivial
+    const int o_c = (p0 + c16) / kBlock;
+    const int keep_c = min(budget - 1, o_c);
+    const bool col_hist = c16 < tq && keep_c > 0 && keep_c < o_c;
+    uint32_t* hist_c = hist + (c16 < tq ? c16 : 0) * kDecHistBins;
     bf16x8_t qf[kIdxSlices];
-    load_index_q(q_idx + b * qs, 0, 1, qf);             // token 0 in column 0, zero columns elsewhere
+    load_index_q(q_idx + b * qs, 0, tq, qf);            // tokens 0 .. tq-1 in columns 0 .. tq-1, zero elsewhere
     const uint16_t* kb = kbar + b * kbs;
-    float* sb = scores + b * ss;
+    float* sb = scores + b * ss + (c16 < tq ? c16 : 0) * sld;
     const int j_lo = g * (256 * STEPS);
-    const int j_hi = min(o, j_lo + 256 * STEPS);
+    const int j_hi = min(o_last, j_lo + 256 * STEPS);
     // two named buffers, loop unrolled by two: one group computes while the
     // next is in flight (the next-group address is clamped, never skipped)
     auto step_of = [&](int j) { return (j < j_hi) ? j : (j_hi - 1) / 64 * 64; };
-    // 4 tiles of 16 blocks; the lanes of column 0 hold the scores, 4
-    // consecutive blocks each
+    // 4 tiles of 16 blocks; the lanes of column c < tq hold token c's scores,
+    // 4 consecutive blocks each
+    const int lim_c = min(j_hi, o_c);
     auto score_group = [&](const bf16x8_t (&kf)[4][4], int j0) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const f32x4_t s = block_scores(kf[nt], qf);
             const int jj = j0 + 16 * nt + 4 * G;
-            if (c16 == 0 && jj < j_hi) {
+            if (c16 < tq && jj < j_hi) {
                 *reinterpret_cast<float4*>(sb + jj) = make_float4(s[0], s[1], s[2], s[3]);
-                if (need_hist) {
+                if (col_hist) {
 #pragma unroll
                     for (int n = 0; n < 4; ++n)
-                        if (jj + n < j_hi) atomicAdd(&hist[score_key(s[n]) >> kDecShift], 1u);
+                        if (jj + n < lim_c) atomicAdd(&hist_c[score_key(s[n]) >> kDecShift], 1u);
                 }
             }
         }
@@ -185,11 +205,16 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
             if (j0 + 256 * st < j_hi) score_group(buf[st & 1], j0 + 256 * st);
         }
     }
-    if (!need_hist) return;
     __syncthreads();
-    for (int k = tid; k < kDecHistBins; k += 256) {
-        const uint32_t v = hist[k];
-        if (v) atomicAdd(&ws.hist[static_cast<int64_t>(b) * kDecHistBins + k], v);
+    for (int t = 0; t < tq; ++t) {
+        const int o_t = (p0 + t) / kBlock;
+        const int keep_t = min(budget - 1, o_t);
+        if (!(keep_t > 0 && keep_t < o_t)) continue;     // uniform
+        uint32_t* gh = ws.hist + static_cast<int64_t>(b * tq + t) * kDecHistBins;
+        for (int k = tid; k < kDecHistBins; k += 256) {
+            const uint32_t v = hist[t * kDecHistBins + k];
+            if (v) atomicAdd(&gh[k], v);
+        }
     }
 }
 
@@ -205,20 +230,22 @@ struct FilterSmem {
 constexpr int kFiltPer = 4096;      // scores per filter workgroup: 4 float4 per thread
 
 __global__ __launch_bounds__(256) void decode_filter_kernel(
-    const float* __restrict__ scores, int64_t ss, Positions pos, int budget, int wg_per_seq,
+    const float* __restrict__ scores, int64_t ss, int64_t sld, Positions pos, int budget, int tq, int wg_per_row,
     DecodeWs ws) {
     __shared__ FilterSmem sm;
     const int tid = threadIdx.x;
-    const int b = blockIdx.x / wg_per_seq;
-    const int g = blockIdx.x % wg_per_seq;
-    const int p = pos.p[b];
+    const int r = blockIdx.x / wg_per_row;                 // row = token t of sequence b
+    const int g = blockIdx.x % wg_per_row;
+    const int b = r / tq;
+    const int t = r % tq;
+    const int p = pos.p[b] + t;
     const int o = p / kBlock;
     const int keep = min(budget - 1, o);
     if (!(keep > 0 && keep < o)) return;                 // trivial rows need no filter
-    uint32_t* ctrl = ws.ctrl + b * kCtrl;
+    uint32_t* ctrl = ws.ctrl + r * kCtrl;
 
     // this workgroup's scores first (independent of the threshold), 4 float4 per thread
-    const float* row = scores + b * ss;
+    const float* row = scores + b * ss + t * sld;
     const int j_lo = g * kFiltPer;
     const int j_hi = min(o, j_lo + kFiltPer);
     float4 v[4];
@@ -230,7 +257,7 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(
 
     // the threshold bin, from the global histogram the scan completed (all
     // 16 words of a thread in flight at once, then stored to LDS)
-    const uint4* gh = reinterpret_cast<const uint4*>(ws.hist + static_cast<int64_t>(b) * kDecHistBins);
+    const uint4* gh = reinterpret_cast<const uint4*>(ws.hist + static_cast<int64_t>(r) * kDecHistBins);
     uint4 hv[kDecHistBins / 1024];
 #pragma unroll
     for (int it = 0; it < kDecHistBins / 1024; ++it) hv[it] = gh[tid + 256 * it];
@@ -276,8 +303,8 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(
         sm.base_cand = nc ? static_cast<int>(atomicAdd(&ctrl[kNCand], static_cast<uint32_t>(nc))) : 0;
     }
     __syncthreads();
-    int32_t* defl = ws.defl + static_cast<int64_t>(b) * QSA_MAX_BUDGET;
-    uint64_t* cand = ws.cand + static_cast<int64_t>(b) * kDecCap;
+    int32_t* defl = ws.defl + static_cast<int64_t>(r) * QSA_MAX_BUDGET;
+    uint64_t* cand = ws.cand + static_cast<int64_t>(r) * kDecCap;
     for (int k = tid; k < nd; k += 256)
         if (sm.base_def + k < QSA_MAX_BUDGET) defl[sm.base_def + k] = sm.def[k];
     for (int k = tid; k < min(nc, kDecCap); k += 256)
@@ -304,22 +331,25 @@ struct FinalizeSmem {
 };
 
 __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __restrict__ scores, int64_t ss,
-                                                                 Positions pos, int budget, DecodeWs ws,
-                                                                 int32_t* __restrict__ sel, int64_t sels) {
+                                                                 int64_t sld, Positions pos, int budget, int tq,
+                                                                 DecodeWs ws, int32_t* __restrict__ sel,
+                                                                 int64_t sels) {
     __shared__ FinalizeSmem sm;
     const int tid = threadIdx.x;
-    const int b = blockIdx.x;
-    const int p = pos.p[b];
+    const int r = blockIdx.x;                             // row = token t of sequence b
+    const int b = r / tq;
+    const int t = r % tq;
+    const int p = pos.p[b] + t;
     const int o = p / kBlock;
     const int keep = min(budget - 1, o);
-    int32_t* out = sel + b * sels;
-    uint32_t* ctrl = ws.ctrl + b * kCtrl;
+    int32_t* out = sel + b * sels + t * budget;
+    uint32_t* ctrl = ws.ctrl + r * kCtrl;
     if (trivial_selection(keep, o, budget, out, kFinNT)) return;   // nothing was accumulated
 
     // every load of both lists in flight at once, with the control words (the
     // lists have fixed capacities: unused tails are read and dropped)
-    const int32_t* __restrict__ defl = ws.defl + static_cast<int64_t>(b) * QSA_MAX_BUDGET;
-    const uint64_t* __restrict__ cg = ws.cand + static_cast<int64_t>(b) * kDecCap;
+    const int32_t* __restrict__ defl = ws.defl + static_cast<int64_t>(r) * QSA_MAX_BUDGET;
+    const uint64_t* __restrict__ cg = ws.cand + static_cast<int64_t>(r) * kDecCap;
     int32_t dv[QSA_MAX_BUDGET / kFinNT];
     uint64_t cv[kDecCap / kFinNT];
 #pragma unroll
@@ -330,7 +360,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
     const int inbin = static_cast<int>(ctrl[kInBin]);
     const int remaining = keep - above;
     if (inbin > kDecCap) {
-        select_row<kFinNT>(scores + b * ss, o, keep, budget, out, sm.u.s);
+        select_row<kFinNT>(scores + b * ss + t * sld, o, keep, budget, out, sm.u.s);
     } else {
         int32_t* chosen = sm.u.m.chosen;
         const bool bitmap = o <= 32 * kBitmapWords;             // every chosen j < o has a bit; o goes last
@@ -423,17 +453,18 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         for (int k = keep + 1 + tid; k < budget; k += kFinNT) out[k] = -1;
     }
     __syncthreads();
-    uint32_t* gh = ws.hist + static_cast<int64_t>(b) * kDecHistBins;
+    uint32_t* gh = ws.hist + static_cast<int64_t>(r) * kDecHistBins;
     for (int k = tid; k < kDecHistBins; k += kFinNT) gh[k] = 0u;
     if (tid < kCtrl) ctrl[tid] = 0u;
 }
 
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
-                                      int64_t kbs, const Positions& pos, int batch, int budget,
-                                      float* scores, int64_t ss, int32_t* sel, int64_t sels, void* ws,
-                                      const DecodeAppend* append, hipStream_t stream) {
+                                      int64_t kbs, const Positions& pos, int batch, int tq, int budget,
+                                      float* scores, int64_t ss, int64_t sld, int32_t* sel, int64_t sels,
+                                      void* ws, const DecodeAppend* append, hipStream_t stream) {
+    const int rows = batch * tq;
     int o_max = 0;
-    for (int b = 0; b < batch; ++b) o_max = max(o_max, pos.p[b] / kBlock);
+    for (int b = 0; b < batch; ++b) o_max = max(o_max, (pos.p[b] + tq - 1) / kBlock);
     // scan: 256 * STEPS blocks per workgroup; STEPS is the largest of 8, 4, 2, 1
     // that still gives about 2 workgroups per CU
     const int64_t groups = static_cast<int64_t>(batch) * ((o_max + 255) / 256);
@@ -442,7 +473,7 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
     // filter: kFiltPer scores per workgroup
     const int wg_filt = max(1, (o_max + kFiltPer - 1) / kFiltPer);
 
-    const DecodeWs w = carve(ws, batch);
+    const DecodeWs w = carve(ws, rows);
     AppendArgs ap{};
     if (append != nullptr) {
         ap.k_new = append->k_new;
@@ -460,34 +491,42 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
         ap.kbs = append->kbs;
         ap.inv = make_inv_freq(append->rope_theta > 0.0 ? append->rope_theta : 1.0e7);
     }
-    const int do_append = append != nullptr ? 1 : 0;
+    hipError_t e;
+    // one token per sequence: the rows are appended by the scan; several: first,
+    // because a block an earlier new token completes is scored for the later ones
+    int scan_appends = append != nullptr ? 1 : 0;
+    if (append != nullptr && tq > 1) {
+        hipLaunchKernelGGL(decode_append_kernel, dim3(static_cast<unsigned>(batch)), dim3(192), 0, stream, pos, tq,
+                           ap);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        scan_appends = 0;
+    }
     const dim3 grid(static_cast<unsigned>(batch * wg_scan));
+    const size_t lds = static_cast<size_t>(tq) * kDecHistBins * 4;
     switch (steps) {
         case 8:
-            hipLaunchKernelGGL(decode_scan_kernel<8>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               wg_scan, scores, ss, w, ap, do_append);
+            hipLaunchKernelGGL(decode_scan_kernel<8>, grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, budget,
+                               tq, wg_scan, scores, ss, sld, w, ap, scan_appends);
             break;
         case 4:
-            hipLaunchKernelGGL(decode_scan_kernel<4>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               wg_scan, scores, ss, w, ap, do_append);
+            hipLaunchKernelGGL(decode_scan_kernel<4>, grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, budget,
+                               tq, wg_scan, scores, ss, sld, w, ap, scan_appends);
             break;
         case 2:
-            hipLaunchKernelGGL(decode_scan_kernel<2>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               wg_scan, scores, ss, w, ap, do_append);
+            hipLaunchKernelGGL(decode_scan_kernel<2>, grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, budget,
+                               tq, wg_scan, scores, ss, sld, w, ap, scan_appends);
             break;
         default:
-            hipLaunchKernelGGL(decode_scan_kernel<1>, grid, dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               wg_scan, scores, ss, w, ap, do_append);
+            hipLaunchKernelGGL(decode_scan_kernel<1>, grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, budget,
+                               tq, wg_scan, scores, ss, sld, w, ap, scan_appends);
             break;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_filter_kernel, dim3(static_cast<unsigned>(batch * wg_filt)), dim3(256), 0,
-                       stream, scores, ss, pos, budget, wg_filt, w);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_finalize_kernel, dim3(static_cast<unsigned>(batch)), dim3(kFinNT), 0, stream,
-                       scores, ss, pos, budget, w, sel, sels);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_filter_kernel, dim3(static_cast<unsigned>(rows * wg_filt)), dim3(256), 0,
+                       stream, scores, ss, sld, pos, budget, tq, wg_filt, w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_finalize_kernel, dim3(static_cast<unsigned>(rows)), dim3(kFinNT), 0, stream,
+                       scores, ss, sld, pos, budget, tq, w, sel, sels);
     return hipGetLastError();
 }
 

@@ -278,98 +278,117 @@ qsa_status_t qsa_sparse_attn_prefill(const uint16_t* q, int64_t q_seq_stride,
                       "sparse_attn_prefill launch");
 }
 
-size_t qsa_decode_workspace_bytes(int32_t batch, int32_t budget) {
-    if (batch < 1 || batch > QSA_MAX_BATCH || budget < 1 || budget > QSA_MAX_BUDGET) return 0;
-    return qsa::decode_workspace_bytes(batch, budget);
+static bool tq_ok(int32_t tq) { return tq >= 1 && tq <= qsa::kMaxDecodeTq; }
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t qsa_decode_workspace_bytes(int32_t batch, int32_t tq, int32_t budget) {
+    if (batch < 1 || batch > QSA_MAX_BATCH || !tq_ok(tq) || budget < 1 || budget > QSA_MAX_BUDGET) return 0;
+    return qsa::decode_workspace_bytes(batch * tq, budget);
+}
+
+// decode rows: per sequence q / out [tq][24][256], sel [tq][budget], lse [B*tq][24]
+static qsa_status_t check_decode_attn(const qsa::Positions& p, int32_t batch, int32_t tq, int32_t budget,
+                                      int64_t q_seq_stride, int64_t kv_seq_stride, int64_t sel_seq_stride,
+                                      int64_t out_seq_stride, const float* lse) {
+    CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
+    CHECK(lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) == 0, "lse must be 4-byte aligned");
+    if (batch > 1) {
+        int64_t max_len = 0;
+        for (int b = 0; b < batch; ++b) max_len = p.p[b] + tq > max_len ? p.p[b] + tq : max_len;
+        CHECK(stride_ok(q_seq_stride) && q_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD, "q_seq_stride too small");
+        CHECK(stride_ok(out_seq_stride) && out_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD,
+              "out_seq_stride too small");
+        CHECK(stride_ok(kv_seq_stride) && kv_seq_stride >= max_len * qsa::kHkv * qsa::kD,
+              "kv_seq_stride smaller than the rows the queries reach");
+        CHECK(sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
+    }
+    return QSA_OK;
 }
 
 qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
                                     const uint16_t* k_cache, const uint16_t* v_cache,
                                     int64_t kv_seq_stride,
                                     const int32_t* sel, int64_t sel_seq_stride,
-                                    const int32_t* q_pos, int32_t batch, int32_t budget,
+                                    const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
                                     float softmax_scale, uint16_t* out, int64_t out_seq_stride,
                                     float* lse, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream) {
     TRY(check_batch(batch));
     TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
-    CHECK(lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) == 0, "lse must be 4-byte aligned");
+    CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
     qsa::Positions p;
-    TRY(take_positions(q_pos, batch, 1, "q_pos", p));
-    if (batch > 1) {
-        int64_t max_len = 0;
-        for (int b = 0; b < batch; ++b) max_len = p.p[b] + 1 > max_len ? p.p[b] + 1 : max_len;
-        CHECK(stride_ok(q_seq_stride) && q_seq_stride >= qsa::kHq * qsa::kD, "q_seq_stride too small");
-        CHECK(stride_ok(out_seq_stride) && out_seq_stride >= qsa::kHq * qsa::kD, "out_seq_stride too small");
-        CHECK(stride_ok(kv_seq_stride) && kv_seq_stride >= max_len * qsa::kHkv * qsa::kD,
-              "kv_seq_stride smaller than the rows the queries reach");
-        CHECK(sel_seq_stride >= budget, "sel_seq_stride < budget");
-    }
-    const size_t need = qsa::decode_workspace_bytes(batch, budget);
+    TRY(take_positions(q_pos, batch, tq, "q_pos", p));
+    TRY(check_decode_attn(p, batch, tq, budget, q_seq_stride, kv_seq_stride, sel_seq_stride, out_seq_stride, lse));
+    const size_t need = qsa::decode_workspace_bytes(batch * tq, budget);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(QSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
                     workspace == nullptr ? size_t{0} : workspace_bytes);
     CHECK(aligned16(workspace), "workspace must be 16-byte aligned");
     return hip_result(qsa::launch_attn_decode(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
-                                              sel_seq_stride, p, batch, budget, softmax_scale, out,
+                                              sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
                                               out_seq_stride, lse, workspace, stream),
                       "sparse_attn_decode launch");
 }
 
-size_t qsa_index_select_decode_workspace_bytes(int32_t batch) {
-    if (batch < 1 || batch > QSA_MAX_BATCH) return 0;
-    return qsa::decode_select_ws_bytes(batch);
+size_t qsa_index_select_decode_workspace_bytes(int32_t batch, int32_t tq) {
+    if (batch < 1 || batch > QSA_MAX_BATCH || !tq_ok(tq)) return 0;
+    return qsa::decode_select_ws_bytes(batch * tq);
 }
 
+// per sequence q_idx [tq][4][128], scores [tq][scores_ld], sel [tq][budget]
 static qsa_status_t check_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_stride,
                                               const uint16_t* kbar, int64_t kbar_seq_stride,
-                                              const qsa::Positions& p, int32_t batch, int32_t budget,
-                                              const float* scores, int64_t scores_seq_stride,
+                                              const qsa::Positions& p, int32_t batch, int32_t tq, int32_t budget,
+                                              const float* scores, int64_t scores_ld, int64_t scores_seq_stride,
                                               const int32_t* sel, int64_t sel_seq_stride) {
+    CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
     CHECK(q_idx != nullptr && kbar != nullptr && scores != nullptr && sel != nullptr,
           "q_idx, kbar, scores and sel must be non-NULL");
     CHECK(aligned16(q_idx) && aligned16(kbar) && aligned16(scores), "q_idx, kbar and scores must be 16-byte aligned");
     CHECK((reinterpret_cast<uintptr_t>(sel) & 3u) == 0, "sel must be 4-byte aligned");
     CHECK(budget >= 1 && budget <= QSA_MAX_BUDGET, "budget = %d outside [1, %d]", budget, QSA_MAX_BUDGET);
+    int64_t o_max = 0;
+    for (int b = 0; b < batch; ++b)
+        o_max = (p.p[b] + tq - 1) / qsa::kBlock > o_max ? (p.p[b] + tq - 1) / qsa::kBlock : o_max;
+    CHECK(scores_ld % 4 == 0 && scores_ld >= (o_max + 3) / 4 * 4,
+          "scores_ld must be a multiple of 4 and >= (q_pos + tq - 1) / 4 rounded up to 4");
     if (batch > 1) {
-        int64_t o_max = 0;
-        for (int b = 0; b < batch; ++b) o_max = p.p[b] / qsa::kBlock > o_max ? p.p[b] / qsa::kBlock : o_max;
-        CHECK(stride_ok(q_idx_seq_stride) && q_idx_seq_stride >= qsa::kHi * qsa::kDi, "q_idx_seq_stride too small");
+        CHECK(stride_ok(q_idx_seq_stride) && q_idx_seq_stride >= int64_t{tq} * qsa::kHi * qsa::kDi,
+              "q_idx_seq_stride too small");
         CHECK(stride_ok(kbar_seq_stride) && kbar_seq_stride >= o_max * qsa::kDi, "kbar_seq_stride too small");
-        CHECK(scores_seq_stride % 4 == 0 && scores_seq_stride >= (o_max + 3) / 4 * 4,
-              "scores_seq_stride must be a multiple of 4 and >= q_pos / 4 rounded up to 4");
-        CHECK(sel_seq_stride >= budget, "sel_seq_stride < budget");
+        CHECK(scores_seq_stride % 4 == 0 && scores_seq_stride >= int64_t{tq} * scores_ld,
+              "scores_seq_stride must be a multiple of 4 and >= tq * scores_ld");
+        CHECK(sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
     }
     return QSA_OK;
 }
 
 qsa_status_t qsa_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_stride,
                                      const uint16_t* kbar, int64_t kbar_seq_stride,
-                                     const int32_t* q_pos, int32_t batch, int32_t budget,
-                                     float* scores, int64_t scores_seq_stride,
+                                     const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
+                                     float* scores, int64_t scores_ld, int64_t scores_seq_stride,
                                      int32_t* sel, int64_t sel_seq_stride,
                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
     TRY(check_batch(batch));
+    CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
     qsa::Positions p;
-    TRY(take_positions(q_pos, batch, 1, "q_pos", p));
-    TRY(check_index_select_decode(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, budget, scores,
-                                  scores_seq_stride, sel, sel_seq_stride));
-    const size_t need = qsa::decode_select_ws_bytes(batch);
+    TRY(take_positions(q_pos, batch, tq, "q_pos", p));
+    TRY(check_index_select_decode(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq, budget, scores,
+                                  scores_ld, scores_seq_stride, sel, sel_seq_stride));
+    const size_t need = qsa::decode_select_ws_bytes(batch * tq);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(QSA_ERR_WORKSPACE, "index-select workspace needs %zu bytes, got %zu", need,
                     workspace == nullptr ? size_t{0} : workspace_bytes);
     CHECK(aligned16(workspace), "workspace must be 16-byte aligned");
-    return hip_result(qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch,
-                                                      budget, scores, scores_seq_stride, sel, sel_seq_stride,
-                                                      workspace, nullptr, stream),
+    return hip_result(qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq,
+                                                      budget, scores, scores_seq_stride, scores_ld, sel,
+                                                      sel_seq_stride, workspace, nullptr, stream),
                       "index_select_decode launch");
 }
 
-static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-size_t qsa_decode_step_workspace_bytes(int32_t batch, int32_t budget) {
-    if (batch < 1 || batch > QSA_MAX_BATCH || budget < 1 || budget > QSA_MAX_BUDGET) return 0;
-    return align256(qsa::decode_select_ws_bytes(batch)) + qsa::decode_workspace_bytes(batch, budget);
+size_t qsa_decode_step_workspace_bytes(int32_t batch, int32_t tq, int32_t budget) {
+    if (batch < 1 || batch > QSA_MAX_BATCH || !tq_ok(tq) || budget < 1 || budget > QSA_MAX_BUDGET) return 0;
+    return align256(qsa::decode_select_ws_bytes(batch * tq)) + qsa::decode_workspace_bytes(batch * tq, budget);
 }
 
 qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
@@ -379,41 +398,38 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
                              uint16_t* k_cache, uint16_t* v_cache, int64_t kv_seq_stride,
                              uint16_t* k_idx, int64_t k_idx_seq_stride,
                              uint16_t* kbar, int64_t kbar_seq_stride,
-                             const int32_t* q_pos, int32_t batch, int32_t budget,
+                             const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
                              float softmax_scale, double rope_theta,
-                             float* scores, int64_t scores_seq_stride,
+                             float* scores, int64_t scores_ld, int64_t scores_seq_stride,
                              int32_t* sel, int64_t sel_seq_stride,
                              uint16_t* out, int64_t out_seq_stride, float* lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
     TRY(check_batch(batch));
+    CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
     qsa::Positions p;
-    TRY(take_positions(q_pos, batch, 1, "q_pos", p));
-    TRY(check_index_select_decode(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, budget, scores,
-                                  scores_seq_stride, sel, sel_seq_stride));
+    TRY(take_positions(q_pos, batch, tq, "q_pos", p));
+    TRY(check_index_select_decode(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq, budget, scores,
+                                  scores_ld, scores_seq_stride, sel, sel_seq_stride));
     TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
+    TRY(check_decode_attn(p, batch, tq, budget, q_seq_stride, kv_seq_stride, sel_seq_stride, out_seq_stride, lse));
     CHECK(k_new != nullptr && aligned16(k_new), "k_new must be non-NULL and 16-byte aligned");
     CHECK(v_new == nullptr || aligned16(v_new), "v_new must be 16-byte aligned");
     CHECK(k_idx_new == nullptr || k_idx != nullptr, "k_idx_new needs the k_idx cache");
     CHECK(k_idx_new == nullptr || aligned16(k_idx_new), "k_idx_new must be 16-byte aligned");
     CHECK(k_idx == nullptr || aligned16(k_idx), "k_idx must be 16-byte aligned");
     CHECK(isfinite(rope_theta) && rope_theta > 1.0, "rope_theta must be finite and > 1");
-    CHECK(lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) == 0, "lse must be 4-byte aligned");
     if (batch > 1) {
         int64_t max_len = 0;
-        for (int b = 0; b < batch; ++b) max_len = p.p[b] + 1 > max_len ? p.p[b] + 1 : max_len;
-        CHECK(stride_ok(q_seq_stride) && q_seq_stride >= qsa::kHq * qsa::kD, "q_seq_stride too small");
-        CHECK(stride_ok(kv_new_seq_stride) && kv_new_seq_stride >= qsa::kHkv * qsa::kD,
+        for (int b = 0; b < batch; ++b) max_len = p.p[b] + tq > max_len ? p.p[b] + tq : max_len;
+        CHECK(stride_ok(kv_new_seq_stride) && kv_new_seq_stride >= int64_t{tq} * qsa::kHkv * qsa::kD,
               "kv_new_seq_stride too small");
-        CHECK(stride_ok(out_seq_stride) && out_seq_stride >= qsa::kHq * qsa::kD, "out_seq_stride too small");
-        CHECK(stride_ok(kv_seq_stride) && kv_seq_stride >= max_len * qsa::kHkv * qsa::kD,
-              "kv_seq_stride smaller than the rows the queries reach");
         CHECK(k_idx == nullptr || (stride_ok(k_idx_seq_stride) && k_idx_seq_stride >= max_len * qsa::kDi),
               "k_idx_seq_stride smaller than the rows the new tokens reach");
         CHECK(k_idx == nullptr || kbar_seq_stride >= (max_len / qsa::kBlock) * qsa::kDi,
               "kbar_seq_stride smaller than the blocks the new tokens complete");
     }
-    const size_t sel_ws = align256(qsa::decode_select_ws_bytes(batch));
-    const size_t need = sel_ws + qsa::decode_workspace_bytes(batch, budget);
+    const size_t sel_ws = align256(qsa::decode_select_ws_bytes(batch * tq));
+    const size_t need = sel_ws + qsa::decode_workspace_bytes(batch * tq, budget);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(QSA_ERR_WORKSPACE, "decode step workspace needs %zu bytes, got %zu", need,
                     workspace == nullptr ? size_t{0} : workspace_bytes);
@@ -427,18 +443,18 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
     ap.v_cache = v_cache;
     ap.kvs = kv_seq_stride;
     ap.k_idx_new = k_idx_new;
-    ap.kins = qsa::kDi;
+    ap.kins = int64_t{tq} * qsa::kDi;
     ap.k_idx = k_idx;
     ap.kis = k_idx_seq_stride;
     ap.kbar = kbar;
     ap.kbs = kbar_seq_stride;
     ap.rope_theta = rope_theta;
-    hipError_t e = qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch,
-                                                   budget, scores, scores_seq_stride, sel, sel_seq_stride,
+    hipError_t e = qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq,
+                                                   budget, scores, scores_seq_stride, scores_ld, sel, sel_seq_stride,
                                                    workspace, &ap, stream);
     if (e != hipSuccess) return hip_result(e, "decode_step index-select launch");
     return hip_result(qsa::launch_attn_decode_ex(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
-                                                 sel_seq_stride, p, batch, budget, softmax_scale, out,
+                                                 sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
                                                  out_seq_stride, lse, static_cast<char*>(workspace) + sel_ws,
                                                  rope_theta, stream),
                       "decode_step attention launch");

@@ -118,43 +118,49 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
                                uint16_t* out, int64_t os, float* lse, int64_t lss,
                                hipStream_t stream);
 
-size_t decode_workspace_bytes(int batch, int budget);
+// Decode rows: tq (1 .. kMaxDecodeTq) consecutive query tokens per sequence,
+// token t of sequence b at position pos[b] + t; row r = b * tq + t.  Per
+// sequence, q / out are [tq][24][256], q_idx [tq][4][128], sel [tq][budget],
+// scores [tq][sld]; lse is [B * tq][24].
+constexpr int kMaxDecodeTq = QSA_MAX_DECODE_TQ;
+
+size_t decode_workspace_bytes(int rows, int budget);
 // decode attention with optional rotation of q on load (rope_theta > 0)
 hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* k,
                                  const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
-                                 const Positions& pos, int batch, int budget, float scale,
+                                 const Positions& pos, int batch, int tq, int budget, float scale,
                                  uint16_t* out, int64_t os, float* lse, void* ws, double rope_theta,
                                  hipStream_t stream);
 
-// fused decode index-select (scores + selection of one query row per sequence);
-// the workspace must be zero before its first use and is left zero by each call
-size_t decode_select_ws_bytes(int batch);
-// Rows a decode step appends at each sequence's new position p before it
-// scores (every pointer may be null: then that part is not done).
+// fused decode index-select (scores + selection of the decode rows); the
+// workspace must be zero before its first use and is left zero by each call
+size_t decode_select_ws_bytes(int rows);
+// Rows a decode step appends at each sequence's new positions p0 .. p0+tq-1
+// before it scores (every pointer may be null: then that part is not done).
 struct DecodeAppend {
-    const uint16_t* k_new;       // [B][2][256] unrotated: rotated into k_cache[b][p]
+    const uint16_t* k_new;       // [B][tq][2][256] unrotated: rotated into k_cache[b][p0 + t]
     int64_t kns;
     uint16_t* k_cache;
-    const uint16_t* v_new;       // [B][2][256]: copied into v_cache[b][p]
+    const uint16_t* v_new;       // [B][tq][2][256]: copied into v_cache[b][p0 + t]
     int64_t vns;
     uint16_t* v_cache;
     int64_t kvs;                 // sequence stride of both KV caches
-    const uint16_t* k_idx_new;   // [B][128]: copied into k_idx[b][p]
+    const uint16_t* k_idx_new;   // [B][tq][128]: copied into k_idx[b][p0 + t]
     int64_t kins;
-    uint16_t* k_idx;             // indexer key cache; with it, a block that p completes
-    int64_t kis;                 // (p % 4 == 3) is compressed into kbar[b][p / 4]
+    uint16_t* k_idx;             // indexer key cache; with it, a block that a new token
+    int64_t kis;                 // completes (p % 4 == 3) is compressed into kbar[b][p / 4]
     uint16_t* kbar;
     int64_t kbs;
     double rope_theta;
 };
 
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
-                                      int64_t kbs, const Positions& pos, int batch, int budget,
-                                      float* scores, int64_t ss, int32_t* sel, int64_t sels, void* ws,
-                                      const DecodeAppend* append, hipStream_t stream);
+                                      int64_t kbs, const Positions& pos, int batch, int tq, int budget,
+                                      float* scores, int64_t ss, int64_t sld, int32_t* sel, int64_t sels,
+                                      void* ws, const DecodeAppend* append, hipStream_t stream);
 hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
                               const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
-                              const Positions& pos, int batch, int budget, float scale,
+                              const Positions& pos, int batch, int tq, int budget, float scale,
                               uint16_t* out, int64_t os, float* lse, void* ws,
                               hipStream_t stream);
 

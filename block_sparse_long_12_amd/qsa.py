@@ -48,16 +48,16 @@ _SIGNATURES = {
                                         _c_p, _i64, _c_p, _sz, _c_p]),
     "qsa_sparse_attn_prefill": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32,
                                        _i32, ctypes.c_float, _c_p, _i64, _c_p, _i64, _c_p]),
-    "qsa_decode_workspace_bytes": (_sz, [_i32, _i32]),
-    "qsa_sparse_attn_decode": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32,
+    "qsa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "qsa_sparse_attn_decode": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _i32,
                                       ctypes.c_float, _c_p, _i64, _c_p, _c_p, _sz, _c_p]),
-    "qsa_index_select_decode_workspace_bytes": (_sz, [_i32]),
-    "qsa_index_select_decode": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _c_p, _i64, _c_p, _i64,
-                                       _c_p, _sz, _c_p]),
-    "qsa_decode_step_workspace_bytes": (_sz, [_i32, _i32]),
+    "qsa_index_select_decode_workspace_bytes": (_sz, [_i32, _i32]),
+    "qsa_index_select_decode": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, _c_p, _i64, _i64, _c_p,
+                                       _i64, _c_p, _sz, _c_p]),
+    "qsa_decode_step_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "qsa_decode_step": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _i64, _c_p, _i64,
-                               _c_p, _i64, _c_p, _i32, _i32, ctypes.c_float, ctypes.c_double, _c_p, _i64, _c_p,
-                               _i64, _c_p, _i64, _c_p, _c_p, _sz, _c_p]),
+                               _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, ctypes.c_double, _c_p, _i64,
+                               _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _sz, _c_p]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -231,31 +231,41 @@ def sparse_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
     return out
 
 
-def decode_workspace(batch: int, budget: int, device="cuda") -> torch.Tensor:
-    n = lib().qsa_decode_workspace_bytes(batch, budget)
+def decode_workspace(batch: int, budget: int, device="cuda", tq: int = 1) -> torch.Tensor:
+    """Workspace of sparse_attn_decode for batch sequences of tq decode tokens."""
+    n = lib().qsa_decode_workspace_bytes(batch, tq, budget)
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _decode_rows(q: torch.Tensor, inner: int) -> int:
+    """tq of a decode tensor: [B, <inner dims>] is one token, [B, tq, <inner>] tq."""
+    return 1 if q.dim() == 1 + inner else q.shape[1]
 
 
 def sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                        sel: torch.Tensor, q_pos, out: torch.Tensor, lse: torch.Tensor | None,
                        workspace: torch.Tensor, scale: float = 1.0 / math.sqrt(D),
                        stream=None) -> torch.Tensor:
-    """Decode form: q [B, 24, 256] at positions q_pos[b], sel [B, budget]."""
+    """Decode form: q [B, 24, 256] (or [B, tq, 24, 256]: tq consecutive tokens
+    per sequence, token t at q_pos[b] + t), sel [B, budget] (or [B, tq, budget]),
+    out like q, lse [B, 24] (or [B, tq, 24])."""
     _need(q, "q", torch.bfloat16, (HQ, D))
     _need(out, "out", torch.bfloat16, (HQ, D))
     _need(k_cache, "k_cache", torch.bfloat16, (HKV, D))
     _need(v_cache, "v_cache", torch.bfloat16, (HKV, D))
-    B, budget = sel.shape
+    B, tq, budget = q.shape[0], _decode_rows(q, 2), sel.shape[-1]
     _need(sel, "sel", torch.int32, (budget,))
-    if lse is not None and (not lse.is_contiguous() or tuple(lse.shape) != (B, HQ)):
-        raise QSAError("lse must be contiguous [B, 24]")
+    if tuple(out.shape) != tuple(q.shape) or sel.shape[0] != B or sel.numel() != B * tq * budget:
+        raise QSAError("out must have the shape of q and sel hold [B, tq, budget]")
+    if lse is not None and (not lse.is_contiguous() or lse.numel() != B * tq * HQ):
+        raise QSAError("lse must be contiguous [B, tq, 24]")
     if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
         raise QSAError("k_cache and v_cache must share shape and strides")
     pos = _positions(q_pos, B)
-    if any(int(pos[b]) + 1 > k_cache.shape[1] for b in range(B)):
+    if any(int(pos[b]) + tq > k_cache.shape[1] for b in range(B)):
         raise QSAError("KV caches shorter than the query positions")
     _check(lib().qsa_sparse_attn_decode(_ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0),
-                                        _ptr(sel), sel.stride(0), pos, B, budget, float(scale), _ptr(out),
+                                        _ptr(sel), sel.stride(0), pos, B, tq, budget, float(scale), _ptr(out),
                                         out.stride(0), _ptr(lse), _ptr(workspace), workspace.numel(),
                                         _stream(stream)),
            "qsa_sparse_attn_decode")
@@ -330,35 +340,38 @@ def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0
     return out
 
 
-def index_select_workspace(batch: int, device="cuda") -> torch.Tensor:
+def index_select_workspace(batch: int, device="cuda", tq: int = 1) -> torch.Tensor:
     """Zero-filled workspace of the fused decode index-select (reusable across calls)."""
-    n = lib().qsa_index_select_decode_workspace_bytes(batch)
+    n = lib().qsa_index_select_decode_workspace_bytes(batch, tq)
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def index_select_decode(q_idx: torch.Tensor, kbar: torch.Tensor, q_pos, budget: int, scores: torch.Tensor,
                         sel: torch.Tensor, workspace: torch.Tensor, stream=None):
-    """Fused steps 2 + 3 for decode rows: q_idx [B, 4, 128] (or [B, 1, 4, 128]),
-    scores [B, ld] or [B, 1, ld], sel [B, budget] or [B, 1, budget]."""
+    """Fused steps 2 + 3 for decode rows: q_idx [B, 4, 128] or [B, tq, 4, 128]
+    (token t at q_pos[b] + t), scores [B, ld] or [B, tq, ld], sel [B, budget] or
+    [B, tq, budget]."""
     _need(q_idx, "q_idx", torch.bfloat16, (HI, DI))
     _need(kbar, "kbar", torch.bfloat16, (DI,))
     _need(scores, "scores", torch.float32, ())
     _need(sel, "sel", torch.int32, (budget,))
-    B = q_idx.shape[0]
+    B, tq = q_idx.shape[0], _decode_rows(q_idx, 2)
     pos = _positions(q_pos, B)
-    need = max(int(pos[b]) // BLOCK for b in range(B))
+    need = max((int(pos[b]) + tq - 1) // BLOCK for b in range(B))
     if scores.shape[-1] < need or kbar.shape[1] < need or scores.shape[-1] % 4:
         raise QSAError("scores / kbar do not cover the candidate blocks")
-    _check(lib().qsa_index_select_decode(_ptr(q_idx), q_idx.stride(0), _ptr(kbar), kbar.stride(0), pos, B,
-                                         budget, _ptr(scores), scores.stride(0), _ptr(sel), sel.stride(0),
-                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+    if scores.numel() < B * tq * scores.shape[-1] or sel.numel() != B * tq * budget:
+        raise QSAError("scores / sel must hold [B, tq, ...]")
+    _check(lib().qsa_index_select_decode(_ptr(q_idx), q_idx.stride(0), _ptr(kbar), kbar.stride(0), pos, B, tq,
+                                         budget, _ptr(scores), scores.shape[-1], scores.stride(0), _ptr(sel),
+                                         sel.stride(0), _ptr(workspace), workspace.numel(), _stream(stream)),
            "qsa_index_select_decode")
     return sel
 
 
-def decode_step_workspace(batch: int, budget: int, device="cuda") -> torch.Tensor:
+def decode_step_workspace(batch: int, budget: int, device="cuda", tq: int = 1) -> torch.Tensor:
     """Zero-filled workspace of qsa_decode_step (reusable across calls)."""
-    n = lib().qsa_decode_step_workspace_bytes(batch, budget)
+    n = lib().qsa_decode_step_workspace_bytes(batch, tq, budget)
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
@@ -369,18 +382,20 @@ def _decode_positions(pos, B: int) -> list[int]:
 def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,
                 out, lse, scores, sel, workspace, stream=None, scale: float = 1.0 / math.sqrt(D),
                 v_new=None, k_idx_new=None):
-    """One decode step for B sequences, each with one new token at position
-    pos[b] (an int: the same for all), through the single qsa_decode_step call.
+    """One decode step through the single qsa_decode_step call, for tq new
+    tokens per sequence (tq = q_raw.shape[1], 1 .. 4): token t of sequence b
+    at position pos[b] + t (pos an int: the same for all sequences).
 
-    q_raw [B, 1, 24, 256] and k_new_raw [B, 1, 2, 256] are unrotated; the
-    rotated K row goes to k_cache[b, pos[b]]. v_new [B, 1, 2, 256] and
-    k_idx_new [B, 1, 128] (optional) are appended to v_cache / k_idx at
-    pos[b]; without them those rows are expected in place. kbar must hold
-    blocks 0 .. pos[b] // 4 - 1; when the new token completes its block the
-    step writes that block's key (from k_idx) for the next steps. workspace
-    comes from decode_step_workspace.
+    q_raw [B, tq, 24, 256] and k_new_raw [B, tq, 2, 256] are unrotated; the
+    rotated K rows go to k_cache[b, pos[b] + t]. v_new [B, tq, 2, 256] and
+    k_idx_new [B, tq, 128] (optional) are appended to v_cache / k_idx; without
+    them those rows are expected in place. kbar must hold the blocks before
+    pos[b] // 4; the step writes the key of every block a new token completes
+    (from k_idx). scores [B, tq, ld], sel [B, tq, budget], out [B, 24, 256]
+    (tq = 1) or [B, tq, 24, 256], lse [B, 24] or [B, tq, 24]. workspace comes
+    from decode_step_workspace(B, budget, tq=tq).
     """
-    B = q_raw.shape[0]
+    B, tq = q_raw.shape[0], q_raw.shape[1]
     p_list = _decode_positions(pos, B)
     _need(q_raw, "q", torch.bfloat16, (HQ, D))
     _need(k_new_raw, "k_new", torch.bfloat16, (HKV, D))
@@ -391,37 +406,42 @@ def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, bud
     _need(out, "out", torch.bfloat16, (HQ, D))
     _need(scores, "scores", torch.float32, ())
     _need(sel, "sel", torch.int32, (budget,))
+    if k_new_raw.shape[1] != tq or q_idx.numel() != B * tq * HI * DI or out.numel() != B * tq * HQ * D:
+        raise QSAError("k_new, q_idx and out must hold tq rows per sequence")
+    if sel.numel() != B * tq * budget or scores.numel() < B * tq * scores.shape[-1]:
+        raise QSAError("sel / scores must hold [B, tq, ...]")
     if k_idx is not None:
         _need(k_idx, "k_idx", torch.bfloat16, (DI,))
     if v_new is not None:
         _need(v_new, "v_new", torch.bfloat16, (HKV, D))
-        if v_new.stride(0) != k_new_raw.stride(0):
-            raise QSAError("v_new and k_new must share their sequence stride")
+        if v_new.stride(0) != k_new_raw.stride(0) or v_new.shape[1] != tq:
+            raise QSAError("v_new must match k_new in shape and sequence stride")
     if k_idx_new is not None:
         if k_idx is None:
             raise QSAError("k_idx_new needs the k_idx cache")
         if (not isinstance(k_idx_new, torch.Tensor) or k_idx_new.device.type != "cuda"
                 or k_idx_new.dtype != torch.bfloat16 or not k_idx_new.is_contiguous()
-                or k_idx_new.numel() != B * DI):
-            raise QSAError("k_idx_new must be a contiguous bf16 device tensor [B, 1, 128]")
-    top = max(p_list)
+                or k_idx_new.numel() != B * tq * DI):
+            raise QSAError("k_idx_new must be a contiguous bf16 device tensor [B, tq, 128]")
+    top = max(p_list) + tq - 1
     if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape or k_cache.shape[1] <= top:
         raise QSAError("k_cache / v_cache must share shape and strides and hold every new position")
     if k_idx is not None and k_idx.shape[1] <= top:
         raise QSAError("k_idx must hold every new position")
-    if lse is not None and (not lse.is_contiguous() or tuple(lse.shape) != (B, HQ)):
-        raise QSAError("lse must be contiguous [B, 24]")
+    if lse is not None and (not lse.is_contiguous() or lse.numel() != B * tq * HQ):
+        raise QSAError("lse must be contiguous [B, tq, 24]")
     if scores.shape[-1] < top // BLOCK or scores.shape[-1] % 4:
         raise QSAError("scores do not cover the candidate blocks")
-    if kbar.shape[1] < max((x + 1) // BLOCK if k_idx is not None else x // BLOCK for x in p_list):
+    if kbar.shape[1] < max((x + tq) // BLOCK if k_idx is not None else (x + tq - 1) // BLOCK for x in p_list):
         raise QSAError("kbar does not cover the candidate (and completed) blocks")
     p = _positions(p_list, B)
     _check(lib().qsa_decode_step(_ptr(q_raw), q_raw.stride(0), _ptr(k_new_raw), _ptr(v_new), k_new_raw.stride(0),
                                  _ptr(q_idx), q_idx.stride(0), _ptr(k_idx_new), _ptr(k_cache), _ptr(v_cache),
                                  k_cache.stride(0), _ptr(k_idx), 0 if k_idx is None else k_idx.stride(0),
-                                 _ptr(kbar), kbar.stride(0), p, B, budget, float(scale), ROPE_THETA, _ptr(scores),
-                                 scores.stride(0), _ptr(sel), sel.stride(0), _ptr(out), out.stride(0), _ptr(lse),
-                                 _ptr(workspace), workspace.numel(), _stream(stream)),
+                                 _ptr(kbar), kbar.stride(0), p, B, tq, budget, float(scale), ROPE_THETA,
+                                 _ptr(scores), scores.shape[-1], scores.stride(0), _ptr(sel), sel.stride(0),
+                                 _ptr(out), out.stride(0), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)),
            "qsa_decode_step")
     return out
 
@@ -429,22 +449,25 @@ def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, bud
 def decode_step_primitives(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,
                            out, lse, scores, sel, workspace, q_rot, stream=None, v_new=None, k_idx_new=None):
     """The same decode step as a chain of the primitive calls (rotary, row
-    copies, scores, selection, attention, block compression); workspace from
-    decode_workspace."""
-    B = q_raw.shape[0]
+    copies, block compression, scores, selection, attention); workspace from
+    decode_workspace(B, budget, tq=tq)."""
+    B, tq = q_raw.shape[0], q_raw.shape[1]
     p = _decode_positions(pos, B)
     rope_apply(q_raw, p, out=q_rot, stream=stream)
     for b in range(B):
-        rope_apply(k_new_raw[b:b + 1], [p[b]], out=k_cache[b:b + 1, p[b]:p[b] + 1], stream=stream)
+        rope_apply(k_new_raw[b:b + 1], [p[b]], out=k_cache[b:b + 1, p[b]:p[b] + tq], stream=stream)
         if v_new is not None:
-            v_cache[b, p[b]].copy_(v_new[b, 0])
+            v_cache[b, p[b]:p[b] + tq].copy_(v_new[b])
         if k_idx_new is not None:
-            k_idx[b, p[b]].copy_(k_idx_new.reshape(B, DI)[b])
-    index_scores(q_idx, kbar, p, scores, stream=stream)
-    select_topk(scores, p, budget, sel, stream=stream)
-    sparse_attn_decode(q_rot[:, 0], k_cache, v_cache, sel[:, 0], p, out, lse, workspace, stream=stream)
+            k_idx[b, p[b]:p[b] + tq].copy_(k_idx_new.reshape(B, tq, DI)[b])
     if k_idx is not None:
         for b in range(B):
-            if (p[b] + 1) % BLOCK == 0:
-                compress_block_keys(k_idx[b:b + 1], p[b] // BLOCK, p[b] // BLOCK + 1, kbar[b:b + 1], stream=stream)
+            j0, j1 = p[b] // BLOCK, (p[b] + tq) // BLOCK            # blocks j with 4j + 3 in [p, p + tq)
+            if j1 > j0:
+                compress_block_keys(k_idx[b:b + 1], j0, j1, kbar[b:b + 1], stream=stream)
+    index_scores(q_idx, kbar, p, scores, stream=stream)
+    select_topk(scores, p, budget, sel, stream=stream)
+    q_att = q_rot if tq > 1 else q_rot[:, 0]
+    sel_att = sel if tq > 1 else sel[:, 0]
+    sparse_attn_decode(q_att, k_cache, v_cache, sel_att, p, out, lse, workspace, stream=stream)
     return out

@@ -182,68 +182,80 @@ qsa_status_t qsa_sparse_attn_prefill(const uint16_t* q, int64_t q_seq_stride,
                                      int64_t lse_seq_stride, hipStream_t stream);
 
 /*
- * Step 4, decode form: one query token per sequence at position q_pos[b]
- * (q [B][24][256], sel [B][budget], out [B][24][256], lse [B][24]).  The
- * selected blocks are split over many workgroups whose partial softmax
- * states (max, sum, weighted V) go to `workspace` and are merged by a final
- * reduction.  workspace must hold qsa_decode_workspace_bytes(batch, budget).
+ * Decode rows.  The decode entries below take tq = 1 .. QSA_MAX_DECODE_TQ
+ * consecutive query tokens per sequence (one for plain decoding, several for
+ * multi-token prediction or speculative verification): token t of sequence b
+ * sits at position q_pos[b] + t and attends causally, so it sees the earlier
+ * new tokens.  Each (sequence, token) is a row with its own selection.  Per
+ * sequence: q and out [tq][24][256], q_idx [tq][4][128], sel [tq][budget],
+ * scores [tq][scores_ld]; lse is [batch * tq][24].  The tokens of a sequence
+ * share one pass over its block keys (they are columns of the same
+ * matrix-core tiles).
  */
-size_t       qsa_decode_workspace_bytes(int32_t batch, int32_t budget);
+#define QSA_MAX_DECODE_TQ 4
+
+/*
+ * Step 4, decode form, for decode rows.  The selected blocks of every row are
+ * split over many workgroups whose partial softmax states (max, sum, weighted
+ * V) go to `workspace` and are merged by a final reduction.  workspace must
+ * hold qsa_decode_workspace_bytes(batch, tq, budget).
+ */
+size_t       qsa_decode_workspace_bytes(int32_t batch, int32_t tq, int32_t budget);
 qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
                                     const uint16_t* k_cache, const uint16_t* v_cache,
                                     int64_t kv_seq_stride,
                                     const int32_t* sel, int64_t sel_seq_stride,
-                                    const int32_t* q_pos, int32_t batch, int32_t budget,
+                                    const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
                                     float softmax_scale, uint16_t* out, int64_t out_seq_stride,
                                     float* lse, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
 /*
- * Steps 2 + 3 fused for decode rows (one query token per sequence at
- * position q_pos[b]): writes the same scores as qsa_index_scores (tq = 1)
- * and the same selection as qsa_select_topk, bit for bit, in two launches
- * that spread each row over many workgroups (a scan that also histograms the
- * score keys, then a threshold filter whose last workgroup finishes the
- * exact selection).  scores [B][ld] float with ld >= q_pos/4 rounded up to a
- * multiple of 4 (the tail past q_pos/4 is scratch), 16-byte aligned;
- * sel [B][budget].  The workspace
+ * Steps 2 + 3 fused for decode rows: writes the same scores as
+ * qsa_index_scores (q_pos0 = q_pos, the same tq) and the same selection as
+ * qsa_select_topk, bit for bit, in three launches that spread each row over
+ * many workgroups (a scan that also histograms the score keys, a threshold
+ * filter, a per-row exact finish).  scores [B][tq][scores_ld] float with
+ * scores_ld >= (q_pos + tq - 1)/4 rounded up to a multiple of 4 (entries past
+ * a row's own block are scratch), 16-byte aligned.  The workspace
  * (qsa_index_select_decode_workspace_bytes) must be zero-filled before its
  * first use; every call leaves it zeroed again.  Calls that share a
  * workspace must not overlap.
  */
-size_t       qsa_index_select_decode_workspace_bytes(int32_t batch);
+size_t       qsa_index_select_decode_workspace_bytes(int32_t batch, int32_t tq);
 qsa_status_t qsa_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_stride,
                                      const uint16_t* kbar, int64_t kbar_seq_stride,
-                                     const int32_t* q_pos, int32_t batch, int32_t budget,
-                                     float* scores, int64_t scores_seq_stride,
+                                     const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
+                                     float* scores, int64_t scores_ld, int64_t scores_seq_stride,
                                      int32_t* sel, int64_t sel_seq_stride,
                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * One whole decode step of the layer for B sequences, each with one new token
- * at its own position q_pos[b] (steps 0 to 4; positions may differ per
- * sequence).  In order, as one asynchronous call:
- *  - appends the new token's rows: the unrotated key row k_new [B][2][256]
- *    is rotated into k_cache[b][q_pos[b]]; v_new [B][2][256] (NULL: the row
- *    is already in v_cache) is copied to v_cache[b][q_pos[b]]; k_idx_new
- *    [B][128] contiguous (NULL: the row is already in k_idx) is copied to
- *    k_idx[b][q_pos[b]];
- *  - scores blocks 0 .. q_pos[b]/4 - 1 of kbar and selects as
+ * One whole decode step of the layer for decode rows: tq new tokens per
+ * sequence at positions q_pos[b] .. q_pos[b] + tq - 1 (steps 0 to 4;
+ * positions may differ per sequence).  In order, as one asynchronous call:
+ *  - appends the new tokens' rows: the unrotated key rows k_new
+ *    [B][tq][2][256] are rotated into k_cache[b][q_pos[b] + t]; v_new
+ *    [B][tq][2][256] (NULL: the rows are already in v_cache) is copied to
+ *    v_cache; k_idx_new [B][tq][128] contiguous (NULL: the rows are already in
+ *    k_idx) is copied to k_idx;
+ *  - when a new token completes its block (position % 4 == 3) and k_idx is
+ *    given, writes that block's key into kbar exactly as
+ *    qsa_compress_block_keys would (the later new tokens of the step score it;
+ *    a block the last token completes serves the next steps);
+ *  - scores the candidate blocks of each row and selects as
  *    qsa_index_select_decode does;
- *  - attends with q [B][24][256] (unrotated; rotated on load exactly as
- *    qsa_rope_apply would) over the selection and the own block;
- *  - when the new token completes its block (q_pos[b] % 4 == 3) and k_idx is
- *    given, writes that block's key kbar[b][q_pos[b]/4] exactly as
- *    qsa_compress_block_keys would, for the next steps (this step never
- *    scores it).  k_idx NULL: no indexer-key append and no compression.
- * k_new / v_new share kv_new_seq_stride; k_cache and v_cache share
- * kv_seq_stride; k_idx is [B][L][128] with k_idx_seq_stride.  Equals the
- * chain rope_apply + row copies + index_scores + select_topk +
- * sparse_attn_decode + compress_block_keys bit for bit.  The workspace
+ *  - attends with q (unrotated; rotated on load exactly as qsa_rope_apply
+ *    would) over each row's selection and own block.
+ * k_idx NULL: no indexer-key append and no compression.  k_new / v_new share
+ * kv_new_seq_stride; k_cache and v_cache share kv_seq_stride; k_idx is
+ * [B][L][128] with k_idx_seq_stride.  Equals the chain rope_apply + row
+ * copies + compress_block_keys + index_scores + select_topk +
+ * sparse_attn_decode bit for bit.  The workspace
  * (qsa_decode_step_workspace_bytes) must be zero-filled before its first use;
  * every call leaves it zeroed again.
  */
-size_t       qsa_decode_step_workspace_bytes(int32_t batch, int32_t budget);
+size_t       qsa_decode_step_workspace_bytes(int32_t batch, int32_t tq, int32_t budget);
 qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
                              const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
                              const uint16_t* q_idx, int64_t q_idx_seq_stride,
@@ -251,9 +263,9 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
                              uint16_t* k_cache, uint16_t* v_cache, int64_t kv_seq_stride,
                              uint16_t* k_idx, int64_t k_idx_seq_stride,
                              uint16_t* kbar, int64_t kbar_seq_stride,
-                             const int32_t* q_pos, int32_t batch, int32_t budget,
+                             const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
                              float softmax_scale, double rope_theta,
-                             float* scores, int64_t scores_seq_stride,
+                             float* scores, int64_t scores_ld, int64_t scores_seq_stride,
                              int32_t* sel, int64_t sel_seq_stride,
                              uint16_t* out, int64_t out_seq_stride, float* lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -141,20 +141,27 @@ def test_attention_validation(L):
 
 
 def test_decode_workspace(L):
-    need = L.qsa_decode_workspace_bytes(4, 512)
+    need = L.qsa_decode_workspace_bytes(4, 1, 512)
     assert need > 0
-    assert L.qsa_decode_workspace_bytes(0, 512) == 0
+    assert L.qsa_decode_workspace_bytes(0, 1, 512) == 0
+    assert L.qsa_decode_workspace_bytes(4, 5, 512) == 0          # at most 4 decode tokens per sequence
+    assert L.qsa_decode_workspace_bytes(4, 4, 512) > 0            # 16 rows share the ~256 split workgroups
     p = _pos(1048576, 1048576, 1048576, 1048576)
-    st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048577 * 512, FAKE, 512, p, 4, 512, 0.0625, FAKE,
+    st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048577 * 512, FAKE, 512, p, 4, 1, 512, 0.0625, FAKE,
                                   6144, FAKE, FAKE, need - 16, None)
     assert st == WORKSPACE, _err(L)
-    st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048577 * 512, FAKE, 512, p, 4, 512, 0.0625, FAKE,
+    st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048577 * 512, FAKE, 512, p, 4, 1, 512, 0.0625, FAKE,
                                   6144, FAKE, NULL, need, None)
     assert st == WORKSPACE
     # KV sequence stride too small for position 1048576
-    st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048576 * 512, FAKE, 512, p, 4, 512, 0.0625, FAKE,
+    st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048576 * 512, FAKE, 512, p, 4, 1, 512, 0.0625, FAKE,
                                   6144, FAKE, FAKE, need, None)
     assert st == INVALID
+    # two tokens per sequence: sel rows must hold tq * budget per sequence
+    need2 = L.qsa_decode_workspace_bytes(4, 2, 512)
+    st = L.qsa_sparse_attn_decode(FAKE, 2 * 6144, FAKE, FAKE, 1048578 * 512, FAKE, 512, p, 4, 2, 512, 0.0625,
+                                  FAKE, 2 * 6144, FAKE, FAKE, need2, None)
+    assert st == INVALID and "sel_seq_stride" in _err(L)
 
 
 def test_binding_refuses_host_tensors():
@@ -171,14 +178,14 @@ def test_decode_step_validation(L):
     B, budget = 2, 512
     p = _pos(4099, 9000)
     ld = 9000 // 4 // 4 * 4 + 4
-    ws_need = L.qsa_decode_step_workspace_bytes(B, budget)
-    assert ws_need > 0 and L.qsa_decode_step_workspace_bytes(0, budget) == 0
+    ws_need = L.qsa_decode_step_workspace_bytes(B, 1, budget)
+    assert ws_need > 0 and L.qsa_decode_step_workspace_bytes(0, 1, budget) == 0
 
-    def call(v_new=FAKE, k_idx_new=FAKE, k_idx=FAKE, k_idx_stride=9001 * 128, ws=ws_need):
-        return L.qsa_decode_step(FAKE, 24 * 256, FAKE, v_new, 2 * 256, FAKE, 4 * 128, k_idx_new,
-                                 FAKE, FAKE, 9001 * 512, k_idx, k_idx_stride, FAKE, 2251 * 128,
-                                 p, B, budget, 0.0625, 1.0e7, FAKE, ld, FAKE, budget, FAKE, 24 * 256,
-                                 NULL, FAKE, ws, None)
+    def call(v_new=FAKE, k_idx_new=FAKE, k_idx=FAKE, k_idx_stride=9001 * 128, ws=ws_need, tq=1):
+        return L.qsa_decode_step(FAKE, tq * 24 * 256, FAKE, v_new, tq * 2 * 256, FAKE, tq * 4 * 128, k_idx_new,
+                                 FAKE, FAKE, 9004 * 512, k_idx, k_idx_stride, FAKE, 2252 * 128,
+                                 p, B, tq, budget, 0.0625, 1.0e7, FAKE, ld, tq * ld, FAKE, tq * budget, FAKE,
+                                 tq * 24 * 256, NULL, FAKE, ws, None)
 
     assert call(k_idx=NULL) == INVALID
     assert "k_idx" in L.qsa_last_error().decode()
@@ -187,3 +194,5 @@ def test_decode_step_validation(L):
     assert call(k_idx_stride=9000 * 128) == INVALID              # row 9000 out of reach
     assert "k_idx_seq_stride" in L.qsa_last_error().decode()
     assert call(ws=ws_need - 1) == WORKSPACE
+    assert call(tq=5) == INVALID and "tq" in L.qsa_last_error().decode()
+    assert call(tq=4, k_idx_stride=9001 * 128) == INVALID          # rows 9001 .. 9003 out of reach

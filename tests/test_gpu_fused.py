@@ -263,3 +263,94 @@ def test_decode_step_appends_rows_and_compresses(pos, budget):
             assert not torch.equal(rb[b][3][pos[b] // 4], torch.full_like(rb[b][3][0], 9.0)), b
     assert torch.equal(oa.view(torch.uint8), ob.view(torch.uint8))
     assert torch.equal(la.view(torch.uint8), lb.view(torch.uint8))
+
+
+# ---------------------------------------------------------------- several decode tokens per sequence
+
+@pytest.mark.parametrize("pos,tq,budget", [([4097, 9000, 70001], 4, 512), ([4099, 8191], 2, 512),
+                                           ([131069, 131072], 3, 512), ([1, 6], 4, 8)])
+def test_multi_token_decode_step_matches_primitives(pos, tq, budget):
+    """tq new tokens per sequence in one step (one pass over the block keys
+    scores every token) equal the primitive chain bit for bit: the appended
+    rows, the key of every block a new token completes (a later token of the
+    same step scores it), scores, selections, outputs and LSEs."""
+    say(f"multi-token decode_step pos={pos} tq={tq} budget={budget}")
+    B = len(pos)
+    L = max(pos) + tq
+    dev = "cuda"
+    g = torch.Generator().manual_seed(11 + tq)
+    bf = torch.bfloat16
+    k_cpu = torch.randn((B, L, 2, 256), generator=g).to(bf)
+    v_cpu = torch.randn((B, L, 2, 256), generator=g).to(bf)
+    ki_cpu = (torch.randn((B, L, 128), generator=g) / math.sqrt(128)).to(bf)
+    q_raw = torch.randn((B, tq, 24, 256), generator=g).to(bf).to(dev)
+    q_idx = (torch.randn((B, tq, 4, 128), generator=g) / math.sqrt(128)).to(bf).to(dev)
+    k_new = torch.randn((B, tq, 2, 256), generator=g).to(bf).to(dev)
+    v_new = torch.randn((B, tq, 2, 256), generator=g).to(bf).to(dev)
+    k_idx_new = (torch.randn((B, tq, 128), generator=g) / math.sqrt(128)).to(bf).to(dev)
+    ld = max(4, ((L - 1) // 4 + 3) // 4 * 4)
+    outs = []
+    for fused in (False, True):
+        kc, v, ki = k_cpu.to(dev), v_cpu.to(dev), ki_cpu.to(dev)
+        qsa.rope_apply(kc, [0] * B)
+        kb = torch.full((B, L // 4 + 1, 128), 9.0, dtype=bf, device=dev)
+        for b in range(B):
+            if pos[b] // 4:
+                qsa.compress_block_keys(ki[b:b + 1], 0, pos[b] // 4, kb[b:b + 1])
+        scores = torch.full((B, tq, ld), float("nan"), device=dev)
+        sel = torch.empty((B, tq, budget), dtype=torch.int32, device=dev)
+        out = torch.empty((B, tq, 24, 256), dtype=bf, device=dev)
+        lse = torch.empty((B, tq, 24), dtype=torch.float32, device=dev)
+        if fused:
+            ws = qsa.decode_step_workspace(B, budget, tq=tq)
+            for _ in range(2):                        # the second call reuses the workspace
+                qsa.decode_step(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel, ws,
+                                v_new=v_new, k_idx_new=k_idx_new)
+            assert int(ws[:B * tq * (4096 + 16) * 4].count_nonzero()) == 0
+        else:
+            qsa.decode_step_primitives(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel,
+                                       qsa.decode_workspace(B, budget, tq=tq), torch.empty_like(q_raw),
+                                       v_new=v_new, k_idx_new=k_idx_new)
+        torch.cuda.synchronize()
+        per = []
+        for b in range(B):
+            rows = slice(pos[b], pos[b] + tq)
+            per.append((kc[b, rows].clone(), v[b, rows].clone(), ki[b, rows].clone(), kb[b].clone(),
+                        [scores[b, t, :(pos[b] + t) // 4].clone() for t in range(tq)], sel[b].clone()))
+        outs.append((per, out.clone(), lse.clone()))
+    (pa, oa, la), (pb, ob, lb) = outs
+    for b in range(B):
+        for name, a, c in zip(("k rows", "v rows", "k_idx rows", "kbar", "", "sel"), pa[b], pb[b]):
+            if name:
+                assert torch.equal(a.view(torch.uint8), c.view(torch.uint8)), (b, name)
+        for t in range(tq):
+            assert torch.equal(pa[b][4][t].view(torch.int32), pb[b][4][t].view(torch.int32)), (b, t, "scores")
+        for x in range(pos[b], pos[b] + tq):          # every completed block was written
+            if x % 4 == 3:
+                assert not torch.equal(pb[b][3][x // 4], torch.full_like(pb[b][3][0], 9.0)), (b, x)
+    assert torch.equal(oa.view(torch.uint8), ob.view(torch.uint8))
+    assert torch.equal(la.view(torch.uint8), lb.view(torch.uint8))
+
+
+@pytest.mark.parametrize("pos,tq,budget", [([70001, 262141], 4, 512), ([5000, 5001, 5002], 3, 64)])
+def test_multi_token_index_select_decode_matches_primitives(pos, tq, budget):
+    say(f"multi-token index_select_decode pos={pos} tq={tq}")
+    B = len(pos)
+    nblk = (max(pos) + tq - 1) // 4
+    q = _rand((B, tq, 4, 128), sum(pos) + tq, 1 / math.sqrt(128)).cuda()
+    kbar = _kbar("normal", B, max(1, nblk), budget).cuda()
+    ld = (nblk + 3) // 4 * 4
+    s_ref = torch.full((B, tq, ld), float("nan"), device="cuda")
+    sel_ref = torch.empty((B, tq, budget), dtype=torch.int32, device="cuda")
+    qsa.index_scores(q, kbar, pos, s_ref)
+    qsa.select_topk(s_ref, pos, budget, sel_ref)
+    ws = qsa.index_select_workspace(B, tq=tq)
+    s_f = torch.full((B, tq, ld), float("nan"), device="cuda")
+    sel_f = torch.empty((B, tq, budget), dtype=torch.int32, device="cuda")
+    qsa.index_select_decode(q, kbar, pos, budget, s_f, sel_f, ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for t in range(tq):
+            o = (pos[b] + t) // 4
+            assert torch.equal(s_f[b, t, :o].view(torch.int32), s_ref[b, t, :o].view(torch.int32)), (b, t)
+    assert torch.equal(sel_f, sel_ref)

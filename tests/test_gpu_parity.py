@@ -373,3 +373,49 @@ def test_consecutive_decode_steps_match_the_oracle_rows():
     rows = sorted(res)
     compare_rows(oracle_layer(x), x, rows, lambda b, t: res[(b, t)][0], lambda b, t: res[(b, t)][1],
                  lambda b, t: res[(b, t)][2], lambda b, t: res[(b, t)][3])
+
+
+def test_multi_token_decode_steps_match_the_oracle_rows():
+    """Decode steps of 3 new tokens each (the shape of speculative
+    verification), run back to back, give the oracle's causal QSA rows for
+    every token; blocks completed inside a step are scored by its later
+    tokens."""
+    B, ctx, tq, n_steps, budget = 2, 30001, 3, 3, 512
+    S = tq * n_steps
+    wl = I.custom_workload("prefill", batch=B, ctx=ctx, tq=S, budget=budget, n_needles=4, seed=47)
+    say(f"multi-token decode steps {wl.name}")
+    x = I.make_inputs(wl)
+    dev = "cuda"
+    L = ctx + S
+    kc = torch.zeros((B, L, 2, 256), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(kc)
+    ki = torch.zeros((B, L, 128), dtype=torch.bfloat16, device=dev)
+    kc[:, :ctx] = x.k[:, :ctx].to(dev)
+    qsa.rope_apply(kc[:, :ctx], [0] * B)
+    v[:, :ctx] = x.v[:, :ctx].to(dev)
+    ki[:, :ctx] = x.k_idx[:, :ctx].to(dev)
+    kb = torch.zeros((B, L // 4 + 1, 128), dtype=torch.bfloat16, device=dev)
+    qsa.compress_block_keys(ki, 0, ctx // 4, kb)
+    ld = (L // 4 + 3) // 4 * 4
+    ws = qsa.decode_step_workspace(B, budget, tq=tq)
+    res = {}
+    for st in range(n_steps):
+        s0, t0 = tq * st, ctx + tq * st
+        scores = torch.empty((B, tq, ld), dtype=torch.float32, device=dev)
+        sel = torch.empty((B, tq, budget), dtype=torch.int32, device=dev)
+        out = torch.empty((B, tq, 24, 256), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, tq, 24), dtype=torch.float32, device=dev)
+        sl = slice(s0, s0 + tq)
+        qsa.decode_step(x.q[:, sl].contiguous().to(dev), x.k[:, t0:t0 + tq].contiguous().to(dev),
+                        x.q_idx[:, sl].contiguous().to(dev), ki, kc, v, kb, t0, budget, out, lse, scores, sel, ws,
+                        v_new=x.v[:, t0:t0 + tq].contiguous().to(dev),
+                        k_idx_new=x.k_idx[:, t0:t0 + tq].contiguous().to(dev))
+        torch.cuda.synchronize()
+        for b in range(B):
+            for t in range(tq):
+                p = t0 + t
+                res[(b, p)] = (scores[b, t, :p // 4].cpu().numpy(), sel[b, t].cpu().numpy(),
+                               out[b, t].float().cpu().numpy(), lse[b, t].cpu().numpy())
+    rows = sorted(res)
+    compare_rows(oracle_layer(x), x, rows, lambda b, t: res[(b, t)][0], lambda b, t: res[(b, t)][1],
+                 lambda b, t: res[(b, t)][2], lambda b, t: res[(b, t)][3])
