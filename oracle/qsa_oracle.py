@@ -35,7 +35,11 @@ Readings taken where the pages are silent (each restated at its function):
                 head floor(h / 12); softmax scale 1/sqrt(256); tokens of the
                 own block are attended only up to the query itself;
   rotary      = rotate-half pairing (i, i + 32) inside the first 64 dims,
-                angle = position * theta**(-i / 32), applied to Q and K only.
+                angle = position * theta**(-i / 32), applied to Q and K only;
+  output gate = (optional) out * sigmoid(g) per head dim, g an input of the
+                output's shape (blog, "Training stability": the attention
+                output gating mechanism is retained; its definition is not
+                given).
 
 Arithmetic is float64 except where a stored precision is part of the
 definition (bf16 block keys, float32 scores).  Functions take generic head
@@ -227,6 +231,21 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
 
 
 # --------------------------------------------------------------------------
+# optional epilogue of step 4: the attention output gate
+# --------------------------------------------------------------------------
+
+def output_gate(out: np.ndarray, gate_bits: np.ndarray) -> np.ndarray:
+    """Gated attention output (blog, "Training stability": the attention
+    output gating mechanism is retained; the pages do not define it).
+    Reading: every head's output is scaled elementwise by the logistic
+    function of a gate logit, out * 1 / (1 + exp(-g)), with the logits g
+    (bf16, the output's shape) an input of the layer like Q, K and V.
+    float64; the log-sum-exp of the softmax is not gated."""
+    g = bf16_to_f64(gate_bits)
+    return out / (1.0 + np.exp(-g))
+
+
+# --------------------------------------------------------------------------
 # the layer, row by row
 # --------------------------------------------------------------------------
 
@@ -246,12 +265,14 @@ class OracleLayer:
     q_pos0[b] is the position of the first query row of sequence b.  Q and K
     are rotated here (K rows stand in the cache rotated), block keys are
     compressed here from k_idx, then every row is scored, selected and
-    attended independently.
+    attended independently.  gate (optional, bf16 bits [B, tq, Hq, D]) gates
+    the outputs (output_gate).
     """
 
     def __init__(self, q, q_idx, k, v, k_idx, q_pos0, budget: int,
-                 rot_dim: int = 64, theta: float = ROPE_THETA, scale: float | None = None):
+                 rot_dim: int = 64, theta: float = ROPE_THETA, scale: float | None = None, gate=None):
         self.q, self.q_idx, self.k, self.v, self.k_idx = q, q_idx, k, v, k_idx
+        self.gate = gate
         self.q_pos0 = np.asarray(q_pos0, np.int64)
         self.budget = budget
         self.rot_dim, self.theta = rot_dim, theta
@@ -291,6 +312,8 @@ class OracleLayer:
                 kr = rope_rotate(self.k[b, tok], tok, self.rot_dim, self.theta)
                 out, lse = attend(bf16_to_f64(qr), bf16_to_f64(kr), bf16_to_f64(self.v[b, tok]),
                                   self.scale)
+                if self.gate is not None:
+                    out = output_gate(out, self.gate[b, r_idx[i]])
                 cache[(b, t)] = RowResult(scores, sel, out, lse)
         for b, t in rows:
             results.append(cache[(b, t)])

@@ -122,6 +122,15 @@ MUTANTS = [
      [P.test_layer_equals_dense_causal_attention_when_budget_covers_everything]),
     ("attention: own block not cut at the query", "expand_tokens", _expand_no_causal_cut,
      [P.test_layer_equals_dense_causal_attention_when_budget_covers_everything]),
+    ("gate: sigmoid of the wrong sign", "output_gate",
+     lambda out, g: out / (1.0 + np.exp(O.bf16_to_f64(g))),
+     [P.test_output_gate_special_values, P.test_output_gate_is_the_logistic_function]),
+    ("gate: tanh instead of the logistic function", "output_gate",
+     lambda out, g: out * np.tanh(O.bf16_to_f64(g)),
+     [P.test_output_gate_special_values, P.test_output_gate_is_the_logistic_function]),
+    ("gate: multiplies by the logit", "output_gate",
+     lambda out, g: out * O.bf16_to_f64(g),
+     [P.test_output_gate_special_values, P.test_output_gate_is_the_logistic_function]),
 ]
 
 

@@ -319,3 +319,48 @@ def test_generator_is_deterministic_and_thread_independent():
     assert np.array_equal(a.needles, b.needles)
     assert float(a.q.float().std()) == pytest.approx(1.0, rel=0.05)
     assert float(a.q_idx.float().std()) == pytest.approx(1 / math.sqrt(128), rel=0.05)
+
+
+# ---------------------------------------------------------------- output gate
+
+def _gate_bits(values):
+    return O.f64_to_bf16(np.asarray(values, np.float64))
+
+
+def test_output_gate_special_values():
+    """sigmoid(0) = 1/2 halves the output exactly; large logits pass it
+    (sigmoid(30) = 1 - 9.4e-14) or block it (sigmoid(-30) = 9.4e-14)."""
+    out = np.array([[1.5, -2.25, 3.0e-3, 7.0]])
+    assert np.array_equal(O.output_gate(out, _gate_bits(np.zeros((1, 4)))), out / 2)
+    up = O.output_gate(out, _gate_bits(np.full((1, 4), 30.0)))
+    down = O.output_gate(out, _gate_bits(np.full((1, 4), -30.0)))
+    assert np.allclose(up, out, rtol=1e-12, atol=0) and np.all(np.abs(down) <= 1e-12 * np.abs(out))
+
+
+def test_output_gate_is_the_logistic_function():
+    """Against scipy's logistic function on random logits, and the symmetry
+    sigmoid(g) + sigmoid(-g) = 1: gating with g and with -g sums to the
+    ungated output."""
+    from scipy.special import expit
+    rng = np.random.default_rng(3)
+    out = rng.standard_normal((24, 256))
+    g_bits = _gate_bits(rng.standard_normal((24, 256)) * 4)
+    g = O.bf16_to_f64(g_bits)
+    assert np.allclose(O.output_gate(out, g_bits), out * expit(g), rtol=1e-14, atol=1e-300)
+    both = O.output_gate(out, g_bits) + O.output_gate(out, O.f64_to_bf16(-g))
+    assert np.allclose(both, out, rtol=1e-13, atol=1e-15)
+
+
+def test_layer_gate_scales_outputs_and_leaves_lse():
+    wl = I.custom_workload("prefill", batch=1, ctx=40, tq=6, budget=8, seed=5)
+    x = I.make_inputs(wl)
+    B = O.bits
+    g = np.random.default_rng(4).standard_normal((1, 6, 24, 256))
+    g_bits = _gate_bits(g)
+    plain = O.OracleLayer(B(x.q), B(x.q_idx), B(x.k), B(x.v), B(x.k_idx), x.q_pos0, wl.budget)
+    gated = O.OracleLayer(B(x.q), B(x.q_idx), B(x.k), B(x.v), B(x.k_idx), x.q_pos0, wl.budget, gate=g_bits)
+    rows = [(0, 40 + i) for i in range(6)]
+    for i, (a, c) in enumerate(zip(plain.rows(rows), gated.rows(rows))):
+        s = 1.0 / (1.0 + np.exp(-O.bf16_to_f64(g_bits[0, i])))
+        assert np.allclose(c.out, a.out * s, rtol=1e-14, atol=1e-300)
+        assert np.array_equal(c.lse, a.lse) and np.array_equal(c.sel, a.sel)
