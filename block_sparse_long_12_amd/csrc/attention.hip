@@ -224,6 +224,24 @@ __device__ __forceinline__ void load_q_frags(const uint16_t* qh, bool ok, int p,
     if (rope != nullptr) rotate_q_frags(rope_angle(p, *rope), qf);
 }
 
+// Output gate (blog, "Training stability": the attention output gating
+// mechanism is retained): the factor 1 / (1 + exp(-g)) of a bf16 gate logit.
+__device__ __forceinline__ float gate_factor(uint16_t g) { return 1.f / (1.f + expf(-bf16_to_f32(g))); }
+
+// The 4 gated output values of one lane (4 consecutive dims), packed as bf16.
+__device__ __forceinline__ uint2 pack_out4(float o0, float o1, float o2, float o3, const uint2* g) {
+    if (g != nullptr) {
+        o0 *= gate_factor(static_cast<uint16_t>(g->x));
+        o1 *= gate_factor(static_cast<uint16_t>(g->x >> 16));
+        o2 *= gate_factor(static_cast<uint16_t>(g->y));
+        o3 *= gate_factor(static_cast<uint16_t>(g->y >> 16));
+    }
+    uint2 w;
+    w.x = f32_to_bf16(o0) | (static_cast<uint32_t>(f32_to_bf16(o1)) << 16);
+    w.y = f32_to_bf16(o2) | (static_cast<uint32_t>(f32_to_bf16(o3)) << 16);
+    return w;
+}
+
 __device__ __forceinline__ void init_state(WaveState& st) {
     st.m = -INFINITY;
     st.l = 0.f;
@@ -237,7 +255,8 @@ __global__ __launch_bounds__(128) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int64_t qs, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs, const int32_t* __restrict__ sel, int64_t sels,
     Positions pos0, int tq, int budget, float scale, float c, uint16_t* __restrict__ out,
-    int64_t os, float* __restrict__ lse, int64_t lss, InvFreq inv, int rope_q) {
+    int64_t os, float* __restrict__ lse, int64_t lss, const uint16_t* __restrict__ gate, int64_t gs,
+    InvFreq inv, int rope_q) {
     __shared__ uint16_t vt_all[2 * kVtElems];
     const int g = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -263,14 +282,18 @@ __global__ __launch_bounds__(128) void attn_prefill_kernel(
 
     if (head_ok) {
         const float inv_l = 1.f / st.l;
-        uint16_t* orow = out + b * os + static_cast<int64_t>(i) * (kHq * kD) + head * kD + 4 * G;
+        const int64_t off = static_cast<int64_t>(i) * (kHq * kD) + head * kD + 4 * G;
+        uint16_t* orow = out + b * os + off;
+        uint2 gv[16];
+        if (gate != nullptr) {
 #pragma unroll
-        for (int nt = 0; nt < 16; ++nt) {
-            uint2 w;
-            w.x = f32_to_bf16(st.acc[nt][0] * inv_l) | (static_cast<uint32_t>(f32_to_bf16(st.acc[nt][1] * inv_l)) << 16);
-            w.y = f32_to_bf16(st.acc[nt][2] * inv_l) | (static_cast<uint32_t>(f32_to_bf16(st.acc[nt][3] * inv_l)) << 16);
-            *reinterpret_cast<uint2*>(orow + 16 * nt) = w;
+            for (int nt = 0; nt < 16; ++nt) gv[nt] = *reinterpret_cast<const uint2*>(gate + b * gs + off + 16 * nt);
         }
+#pragma unroll
+        for (int nt = 0; nt < 16; ++nt)
+            *reinterpret_cast<uint2*>(orow + 16 * nt) =
+                pack_out4(st.acc[nt][0] * inv_l, st.acc[nt][1] * inv_l, st.acc[nt][2] * inv_l,
+                          st.acc[nt][3] * inv_l, gate != nullptr ? &gv[nt] : nullptr);
         if (lse != nullptr && G == 0)
             lse[b * lss + static_cast<int64_t>(i) * kHq + head] = st.m * scale + logf(st.l);
     }
@@ -279,14 +302,15 @@ __global__ __launch_bounds__(128) void attn_prefill_kernel(
 hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
                                const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                                const Positions& pos0, int batch, int tq, int budget, float scale,
-                               uint16_t* out, int64_t os, float* lse, int64_t lss,
-                               hipStream_t stream) {
+                               uint16_t* out, int64_t os, float* lse, int64_t lss, const uint16_t* gate,
+                               int64_t gs, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(batch) * tq;
     if (rows == 0) return hipSuccess;
     const float c = scale * 1.4426950408889634f;
     const InvFreq inv = make_inv_freq(1.0e7);
     hipLaunchKernelGGL(attn_prefill_kernel, dim3(static_cast<unsigned>(rows)), dim3(128), 0, stream,
-                       q, qs, k, v, kvs, sel, sels, pos0, tq, budget, scale, c, out, os, lse, lss, inv, 0);
+                       q, qs, k, v, kvs, sel, sels, pos0, tq, budget, scale, c, out, os, lse, lss, gate, gs, inv,
+                       0);
     return hipGetLastError();
 }
 
@@ -366,7 +390,8 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
 // before any is used; the 4 partial sums meet in LDS.
 __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
     const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, int tq, int n_split, float scale,
-    float c, uint16_t* __restrict__ out, int64_t os, float* __restrict__ lse) {
+    float c, uint16_t* __restrict__ out, int64_t os, float* __restrict__ lse, const uint16_t* __restrict__ gate,
+    int64_t gs) {
     __shared__ float w_s[64];
     __shared__ float4 part[3][64];
     __shared__ float sh_M, sh_L;
@@ -426,10 +451,11 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
             acc.w += part[q][lane].w;
         }
         const float inv = 1.f / sh_L;
-        uint2 o;
-        o.x = f32_to_bf16(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
-        o.y = f32_to_bf16(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
-        *reinterpret_cast<uint2*>(out + b * os + (t * kHq + h) * kD + 4 * lane) = o;
+        const int64_t off = static_cast<int64_t>(t * kHq + h) * kD + 4 * lane;
+        uint2 gv;
+        if (gate != nullptr) gv = *reinterpret_cast<const uint2*>(gate + b * gs + off);
+        *reinterpret_cast<uint2*>(out + b * os + off) =
+            pack_out4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv, gate != nullptr ? &gv : nullptr);
         if (lse != nullptr && lane == 0) lse[static_cast<int64_t>(r) * kHq + h] = sh_M * scale + logf(sh_L);
     }
 }
@@ -437,8 +463,8 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
 hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* k,
                                  const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                                  const Positions& pos, int batch, int tq, int budget, float scale,
-                                 uint16_t* out, int64_t os, float* lse, void* ws, double rope_theta,
-                                 hipStream_t stream) {
+                                 uint16_t* out, int64_t os, float* lse, const uint16_t* gate, int64_t gs,
+                                 void* ws, double rope_theta, hipStream_t stream) {
     const int rows = batch * tq;
     if (rows == 0) return hipSuccess;
     int n_split, bps;
@@ -453,17 +479,17 @@ hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(static_cast<unsigned>(rows * kHq)), dim3(256),
-                       0, stream, ws_ml, ws_acc, tq, n_split, scale, c, out, os, lse);
+                       0, stream, ws_ml, ws_acc, tq, n_split, scale, c, out, os, lse, gate, gs);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
                               const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                               const Positions& pos, int batch, int tq, int budget, float scale,
-                              uint16_t* out, int64_t os, float* lse, void* ws,
-                              hipStream_t stream) {
+                              uint16_t* out, int64_t os, float* lse, const uint16_t* gate, int64_t gs,
+                              void* ws, hipStream_t stream) {
     return launch_attn_decode_ex(q, qs, k, v, kvs, sel, sels, pos, batch, tq, budget, scale, out, os, lse,
-                                 ws, 0.0, stream);
+                                 gate, gs, ws, 0.0, stream);
 }
 
 }  // namespace qsa

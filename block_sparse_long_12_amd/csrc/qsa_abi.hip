@@ -254,11 +254,13 @@ qsa_status_t qsa_sparse_attn_prefill(const uint16_t* q, int64_t q_seq_stride,
                                      const int32_t* q_pos0, int32_t batch, int32_t tq,
                                      int32_t budget, float softmax_scale,
                                      uint16_t* out, int64_t out_seq_stride, float* lse,
-                                     int64_t lse_seq_stride, hipStream_t stream) {
+                                     int64_t lse_seq_stride, const uint16_t* gate, int64_t gate_seq_stride,
+                                     hipStream_t stream) {
     TRY(check_batch(batch));
     TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
     CHECK(tq >= 0, "tq = %d is negative", tq);
     CHECK(lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) == 0, "lse must be 4-byte aligned");
+    CHECK(gate == nullptr || aligned16(gate), "gate must be 16-byte aligned");
     qsa::Positions p;
     TRY(take_positions(q_pos0, batch, tq, "q_pos0", p));
     if (tq == 0) return ok();
@@ -271,10 +273,12 @@ qsa_status_t qsa_sparse_attn_prefill(const uint16_t* q, int64_t q_seq_stride,
               "kv_seq_stride smaller than the rows the queries reach");
         CHECK(sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
         CHECK(lse == nullptr || lse_seq_stride >= int64_t{tq} * qsa::kHq, "lse_seq_stride < tq * 24");
+        CHECK(gate == nullptr || (stride_ok(gate_seq_stride) && gate_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD),
+              "gate_seq_stride too small");
     }
     return hip_result(qsa::launch_attn_prefill(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
                                                sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
-                                               out_seq_stride, lse, lse_seq_stride, stream),
+                                               out_seq_stride, lse, lse_seq_stride, gate, gate_seq_stride, stream),
                       "sparse_attn_prefill launch");
 }
 
@@ -289,8 +293,13 @@ size_t qsa_decode_workspace_bytes(int32_t batch, int32_t tq, int32_t budget) {
 // decode rows: per sequence q / out [tq][24][256], sel [tq][budget], lse [B*tq][24]
 static qsa_status_t check_decode_attn(const qsa::Positions& p, int32_t batch, int32_t tq, int32_t budget,
                                       int64_t q_seq_stride, int64_t kv_seq_stride, int64_t sel_seq_stride,
-                                      int64_t out_seq_stride, const float* lse) {
+                                      int64_t out_seq_stride, const float* lse, const uint16_t* gate,
+                                      int64_t gate_seq_stride) {
     CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
+    CHECK(gate == nullptr || aligned16(gate), "gate must be 16-byte aligned");
+    CHECK(gate == nullptr || batch == 1 ||
+              (stride_ok(gate_seq_stride) && gate_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD),
+          "gate_seq_stride too small");
     CHECK(lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) == 0, "lse must be 4-byte aligned");
     if (batch > 1) {
         int64_t max_len = 0;
@@ -311,14 +320,15 @@ qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
                                     const int32_t* sel, int64_t sel_seq_stride,
                                     const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
                                     float softmax_scale, uint16_t* out, int64_t out_seq_stride,
-                                    float* lse, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
+                                    float* lse, const uint16_t* gate, int64_t gate_seq_stride,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
     TRY(check_batch(batch));
     TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
     CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
     qsa::Positions p;
     TRY(take_positions(q_pos, batch, tq, "q_pos", p));
-    TRY(check_decode_attn(p, batch, tq, budget, q_seq_stride, kv_seq_stride, sel_seq_stride, out_seq_stride, lse));
+    TRY(check_decode_attn(p, batch, tq, budget, q_seq_stride, kv_seq_stride, sel_seq_stride, out_seq_stride, lse,
+                          gate, gate_seq_stride));
     const size_t need = qsa::decode_workspace_bytes(batch * tq, budget);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(QSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
@@ -326,7 +336,7 @@ qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
     CHECK(aligned16(workspace), "workspace must be 16-byte aligned");
     return hip_result(qsa::launch_attn_decode(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
                                               sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
-                                              out_seq_stride, lse, workspace, stream),
+                                              out_seq_stride, lse, gate, gate_seq_stride, workspace, stream),
                       "sparse_attn_decode launch");
 }
 
@@ -403,6 +413,7 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
                              float* scores, int64_t scores_ld, int64_t scores_seq_stride,
                              int32_t* sel, int64_t sel_seq_stride,
                              uint16_t* out, int64_t out_seq_stride, float* lse,
+                             const uint16_t* gate, int64_t gate_seq_stride,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
     TRY(check_batch(batch));
     CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
@@ -411,7 +422,8 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
     TRY(check_index_select_decode(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq, budget, scores,
                                   scores_ld, scores_seq_stride, sel, sel_seq_stride));
     TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
-    TRY(check_decode_attn(p, batch, tq, budget, q_seq_stride, kv_seq_stride, sel_seq_stride, out_seq_stride, lse));
+    TRY(check_decode_attn(p, batch, tq, budget, q_seq_stride, kv_seq_stride, sel_seq_stride, out_seq_stride, lse,
+                          gate, gate_seq_stride));
     CHECK(k_new != nullptr && aligned16(k_new), "k_new must be non-NULL and 16-byte aligned");
     CHECK(v_new == nullptr || aligned16(v_new), "v_new must be 16-byte aligned");
     CHECK(k_idx_new == nullptr || k_idx != nullptr, "k_idx_new needs the k_idx cache");
@@ -455,8 +467,8 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
     if (e != hipSuccess) return hip_result(e, "decode_step index-select launch");
     return hip_result(qsa::launch_attn_decode_ex(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
                                                  sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
-                                                 out_seq_stride, lse, static_cast<char*>(workspace) + sel_ws,
-                                                 rope_theta, stream),
+                                                 out_seq_stride, lse, gate, gate_seq_stride,
+                                                 static_cast<char*>(workspace) + sel_ws, rope_theta, stream),
                       "decode_step attention launch");
 }
 

@@ -115,8 +115,8 @@ hipError_t launch_prefill_index_select(const uint16_t* q_idx, int64_t qs, const 
 hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
                                const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                                const Positions& pos0, int batch, int tq, int budget, float scale,
-                               uint16_t* out, int64_t os, float* lse, int64_t lss,
-                               hipStream_t stream);
+                               uint16_t* out, int64_t os, float* lse, int64_t lss, const uint16_t* gate,
+                               int64_t gs, hipStream_t stream);
 
 // Decode rows: tq (1 .. kMaxDecodeTq) consecutive query tokens per sequence,
 // token t of sequence b at position pos[b] + t; row r = b * tq + t.  Per
@@ -125,12 +125,13 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
 constexpr int kMaxDecodeTq = QSA_MAX_DECODE_TQ;
 
 size_t decode_workspace_bytes(int rows, int budget);
-// decode attention with optional rotation of q on load (rope_theta > 0)
+// decode attention with optional rotation of q on load (rope_theta > 0);
+// gate (nullable, laid out as out with sequence stride gs): the output gate
 hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* k,
                                  const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                                  const Positions& pos, int batch, int tq, int budget, float scale,
-                                 uint16_t* out, int64_t os, float* lse, void* ws, double rope_theta,
-                                 hipStream_t stream);
+                                 uint16_t* out, int64_t os, float* lse, const uint16_t* gate, int64_t gs,
+                                 void* ws, double rope_theta, hipStream_t stream);
 
 // fused decode index-select (scores + selection of the decode rows); the
 // workspace must be zero before its first use and is left zero by each call
@@ -161,7 +162,7 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
 hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
                               const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                               const Positions& pos, int batch, int tq, int budget, float scale,
-                              uint16_t* out, int64_t os, float* lse, void* ws,
-                              hipStream_t stream);
+                              uint16_t* out, int64_t os, float* lse, const uint16_t* gate, int64_t gs,
+                              void* ws, hipStream_t stream);
 
 }  // namespace qsa

@@ -47,17 +47,17 @@ _SIGNATURES = {
     "qsa_index_select_prefill": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, _c_p, _i64, _i64,
                                         _c_p, _i64, _c_p, _sz, _c_p]),
     "qsa_sparse_attn_prefill": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32,
-                                       _i32, ctypes.c_float, _c_p, _i64, _c_p, _i64, _c_p]),
+                                       _i32, ctypes.c_float, _c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p]),
     "qsa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "qsa_sparse_attn_decode": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _i32,
-                                      ctypes.c_float, _c_p, _i64, _c_p, _c_p, _sz, _c_p]),
+                                      ctypes.c_float, _c_p, _i64, _c_p, _c_p, _i64, _c_p, _sz, _c_p]),
     "qsa_index_select_decode_workspace_bytes": (_sz, [_i32, _i32]),
     "qsa_index_select_decode": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, _c_p, _i64, _i64, _c_p,
                                        _i64, _c_p, _sz, _c_p]),
     "qsa_decode_step_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "qsa_decode_step": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _i64, _c_p, _i64,
                                _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, ctypes.c_double, _c_p, _i64,
-                               _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _sz, _c_p]),
+                               _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p, _sz, _c_p]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -118,6 +118,16 @@ def _positions(pos, batch: int):
     if len(vals) != batch:
         raise QSAError(f"expected {batch} positions, got {len(vals)}")
     return (ctypes.c_int32 * batch)(*vals)
+
+
+def _gate_args(gate, out: torch.Tensor):
+    """(pointer, sequence stride) of an optional output gate laid out as out."""
+    if gate is None:
+        return _c_p(0), 0
+    _need(gate, "gate", torch.bfloat16, (HQ, D))
+    if tuple(gate.shape) != tuple(out.shape):
+        raise QSAError("gate must have the shape of out")
+    return _ptr(gate), gate.stride(0)
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, inner: tuple[int, ...]) -> None:
@@ -205,8 +215,9 @@ def select_topk(scores: torch.Tensor, q_pos0, budget: int, sel: torch.Tensor,
 
 def sparse_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                         sel: torch.Tensor, q_pos0, out: torch.Tensor, lse: torch.Tensor | None = None,
-                        scale: float = 1.0 / math.sqrt(D), stream=None) -> torch.Tensor:
-    """out[b, t] = attention of q[b, t] (24 heads) over the tokens of sel[b, t]."""
+                        scale: float = 1.0 / math.sqrt(D), stream=None, gate=None) -> torch.Tensor:
+    """out[b, t] = attention of q[b, t] (24 heads) over the tokens of sel[b, t];
+    with gate (bf16, out's shape) each value is scaled by sigmoid(gate)."""
     _need(q, "q", torch.bfloat16, (HQ, D))
     _need(k_cache, "k_cache", torch.bfloat16, (HKV, D))
     _need(v_cache, "v_cache", torch.bfloat16, (HKV, D))
@@ -223,10 +234,11 @@ def sparse_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
     pos = _positions(q_pos0, B)
     if any(int(pos[b]) + T > k_cache.shape[1] for b in range(B)):
         raise QSAError("KV caches shorter than the query positions")
+    g_ptr, g_stride = _gate_args(gate, out)
     _check(lib().qsa_sparse_attn_prefill(_ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0),
                                          _ptr(sel), sel.stride(0), pos, B, T, budget, float(scale),
                                          _ptr(out), out.stride(0), _ptr(lse),
-                                         0 if lse is None else lse.stride(0), _stream(stream)),
+                                         0 if lse is None else lse.stride(0), g_ptr, g_stride, _stream(stream)),
            "qsa_sparse_attn_prefill")
     return out
 
@@ -245,10 +257,10 @@ def _decode_rows(q: torch.Tensor, inner: int) -> int:
 def sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                        sel: torch.Tensor, q_pos, out: torch.Tensor, lse: torch.Tensor | None,
                        workspace: torch.Tensor, scale: float = 1.0 / math.sqrt(D),
-                       stream=None) -> torch.Tensor:
+                       stream=None, gate=None) -> torch.Tensor:
     """Decode form: q [B, 24, 256] (or [B, tq, 24, 256]: tq consecutive tokens
     per sequence, token t at q_pos[b] + t), sel [B, budget] (or [B, tq, budget]),
-    out like q, lse [B, 24] (or [B, tq, 24])."""
+    out like q, lse [B, 24] (or [B, tq, 24]), optional output gate like out."""
     _need(q, "q", torch.bfloat16, (HQ, D))
     _need(out, "out", torch.bfloat16, (HQ, D))
     _need(k_cache, "k_cache", torch.bfloat16, (HKV, D))
@@ -264,10 +276,11 @@ def sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     pos = _positions(q_pos, B)
     if any(int(pos[b]) + tq > k_cache.shape[1] for b in range(B)):
         raise QSAError("KV caches shorter than the query positions")
+    g_ptr, g_stride = _gate_args(gate, out)
     _check(lib().qsa_sparse_attn_decode(_ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0),
                                         _ptr(sel), sel.stride(0), pos, B, tq, budget, float(scale), _ptr(out),
-                                        out.stride(0), _ptr(lse), _ptr(workspace), workspace.numel(),
-                                        _stream(stream)),
+                                        out.stride(0), _ptr(lse), g_ptr, g_stride, _ptr(workspace),
+                                        workspace.numel(), _stream(stream)),
            "qsa_sparse_attn_decode")
     return out
 
@@ -315,14 +328,15 @@ class PrefillBuffers:
 
 
 def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0: int, budget: int,
-                  out, lse, bufs: PrefillBuffers, q_rot, stream=None):
+                  out, lse, bufs: PrefillBuffers, q_rot, stream=None, gate=None):
     """One QSA layer over tq new tokens of every sequence, all at q_pos0.
 
     q_raw [B, tq, 24, 256] and k_new_raw [B, tq, 2, 256] are unrotated; the
     rotated K rows are written into k_cache[:, q_pos0 : q_pos0 + tq] (V rows
     are expected in v_cache already, k_idx rows in k_idx).  Steps: rotary
     (Q -> q_rot, K -> cache), compress the blocks the chunk completes, then per
-    query chunk the fused index-select, then attention.
+    query chunk the fused index-select, then attention (with the optional
+    output gate [B, tq, 24, 256]).
     """
     B, tq = q_raw.shape[0], q_raw.shape[1]
     pos = [q_pos0] * B
@@ -336,7 +350,8 @@ def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0
         index_select_prefill(q_idx[:, c0:c1], kbar, cpos, budget, bufs.scores, bufs.sel[:, c0:c1],
                              bufs.workspace, stream=stream)
         sparse_attn_prefill(q_rot[:, c0:c1], k_cache, v_cache, bufs.sel[:, c0:c1], cpos, out[:, c0:c1],
-                            None if lse is None else lse[:, c0:c1], stream=stream)
+                            None if lse is None else lse[:, c0:c1], stream=stream,
+                            gate=None if gate is None else gate[:, c0:c1])
     return out
 
 
@@ -381,7 +396,7 @@ def _decode_positions(pos, B: int) -> list[int]:
 
 def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,
                 out, lse, scores, sel, workspace, stream=None, scale: float = 1.0 / math.sqrt(D),
-                v_new=None, k_idx_new=None):
+                v_new=None, k_idx_new=None, gate=None):
     """One decode step through the single qsa_decode_step call, for tq new
     tokens per sequence (tq = q_raw.shape[1], 1 .. 4): token t of sequence b
     at position pos[b] + t (pos an int: the same for all sequences).
@@ -392,8 +407,9 @@ def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, bud
     them those rows are expected in place. kbar must hold the blocks before
     pos[b] // 4; the step writes the key of every block a new token completes
     (from k_idx). scores [B, tq, ld], sel [B, tq, budget], out [B, 24, 256]
-    (tq = 1) or [B, tq, 24, 256], lse [B, 24] or [B, tq, 24]. workspace comes
-    from decode_step_workspace(B, budget, tq=tq).
+    (tq = 1) or [B, tq, 24, 256], lse [B, 24] or [B, tq, 24], gate (optional
+    output gate) like out. workspace comes from decode_step_workspace(B,
+    budget, tq=tq).
     """
     B, tq = q_raw.shape[0], q_raw.shape[1]
     p_list = _decode_positions(pos, B)
@@ -435,19 +451,21 @@ def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, bud
     if kbar.shape[1] < max((x + tq) // BLOCK if k_idx is not None else (x + tq - 1) // BLOCK for x in p_list):
         raise QSAError("kbar does not cover the candidate (and completed) blocks")
     p = _positions(p_list, B)
+    g_ptr, g_stride = _gate_args(gate, out)
     _check(lib().qsa_decode_step(_ptr(q_raw), q_raw.stride(0), _ptr(k_new_raw), _ptr(v_new), k_new_raw.stride(0),
                                  _ptr(q_idx), q_idx.stride(0), _ptr(k_idx_new), _ptr(k_cache), _ptr(v_cache),
                                  k_cache.stride(0), _ptr(k_idx), 0 if k_idx is None else k_idx.stride(0),
                                  _ptr(kbar), kbar.stride(0), p, B, tq, budget, float(scale), ROPE_THETA,
                                  _ptr(scores), scores.shape[-1], scores.stride(0), _ptr(sel), sel.stride(0),
-                                 _ptr(out), out.stride(0), _ptr(lse), _ptr(workspace), workspace.numel(),
-                                 _stream(stream)),
+                                 _ptr(out), out.stride(0), _ptr(lse), g_ptr, g_stride, _ptr(workspace),
+                                 workspace.numel(), _stream(stream)),
            "qsa_decode_step")
     return out
 
 
 def decode_step_primitives(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,
-                           out, lse, scores, sel, workspace, q_rot, stream=None, v_new=None, k_idx_new=None):
+                           out, lse, scores, sel, workspace, q_rot, stream=None, v_new=None, k_idx_new=None,
+                           gate=None):
     """The same decode step as a chain of the primitive calls (rotary, row
     copies, block compression, scores, selection, attention); workspace from
     decode_workspace(B, budget, tq=tq)."""
@@ -469,5 +487,5 @@ def decode_step_primitives(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kba
     select_topk(scores, p, budget, sel, stream=stream)
     q_att = q_rot if tq > 1 else q_rot[:, 0]
     sel_att = sel if tq > 1 else sel[:, 0]
-    sparse_attn_decode(q_att, k_cache, v_cache, sel_att, p, out, lse, workspace, stream=stream)
+    sparse_attn_decode(q_att, k_cache, v_cache, sel_att, p, out, lse, workspace, stream=stream, gate=gate)
     return out

@@ -171,6 +171,11 @@ qsa_status_t qsa_index_select_prefill(const uint16_t* q_idx, int64_t q_idx_seq_s
  * lse_seq_stride elements), may be NULL.
  * k_cache / v_cache rows must hold positions 0 .. q_pos0[b] + tq - 1; q and K
  * are expected already rotated.  sel entries outside [0, p/4] are skipped.
+ * gate (may be NULL; bf16, laid out as out with sequence stride
+ * gate_seq_stride): the attention output gate (blog, "Training stability":
+ * the attention output gating mechanism is retained) -- each output value is
+ * multiplied by 1 / (1 + exp(-g)) of its gate logit before rounding; lse is
+ * not gated.  The decode entries below take the same optional gate.
  */
 qsa_status_t qsa_sparse_attn_prefill(const uint16_t* q, int64_t q_seq_stride,
                                      const uint16_t* k_cache, const uint16_t* v_cache,
@@ -179,7 +184,8 @@ qsa_status_t qsa_sparse_attn_prefill(const uint16_t* q, int64_t q_seq_stride,
                                      const int32_t* q_pos0, int32_t batch, int32_t tq,
                                      int32_t budget, float softmax_scale,
                                      uint16_t* out, int64_t out_seq_stride, float* lse,
-                                     int64_t lse_seq_stride, hipStream_t stream);
+                                     int64_t lse_seq_stride, const uint16_t* gate,
+                                     int64_t gate_seq_stride, hipStream_t stream);
 
 /*
  * Decode rows.  The decode entries below take tq = 1 .. QSA_MAX_DECODE_TQ
@@ -207,8 +213,8 @@ qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
                                     const int32_t* sel, int64_t sel_seq_stride,
                                     const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
                                     float softmax_scale, uint16_t* out, int64_t out_seq_stride,
-                                    float* lse, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream);
+                                    float* lse, const uint16_t* gate, int64_t gate_seq_stride,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Steps 2 + 3 fused for decode rows: writes the same scores as
@@ -268,6 +274,7 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
                              float* scores, int64_t scores_ld, int64_t scores_seq_stride,
                              int32_t* sel, int64_t sel_seq_stride,
                              uint16_t* out, int64_t out_seq_stride, float* lse,
+                             const uint16_t* gate, int64_t gate_seq_stride,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -68,9 +68,10 @@ class DevicePrefill:
         self.lse = torch.empty((B, T, 24), dtype=torch.float32, device=dev)
         self.q_rot = torch.empty_like(self.q_raw)
 
-    def run(self):
+    def run(self, gate=None):
         qsa.prefill_layer(self.q_raw, self.k_new, self.q_idx, self.k_idx, self.k_cache, self.v_cache,
-                          self.kbar, self.wl.ctx, self.wl.budget, self.out, self.lse, self.bufs, self.q_rot)
+                          self.kbar, self.wl.ctx, self.wl.budget, self.out, self.lse, self.bufs, self.q_rot,
+                          gate=gate)
         torch.cuda.synchronize()
 
 

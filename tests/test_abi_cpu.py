@@ -99,11 +99,11 @@ def test_index_scores_validation(L):
 
 def test_select_validation(L):
     p = _pos(100)
-    assert L.qsa_select_topk(FAKE, 28, 0, p, 1, 10, 0, FAKE, 0, None, 0, None) == INVALID
+    assert L.qsa_select_topk(FAKE, 28, 0, p, 1, 10, 0, FAKE, 0, None, 0, None, 0, None) == INVALID
     assert "budget" in _err(L)
-    assert L.qsa_select_topk(FAKE, 28, 0, p, 1, 10, 4096, FAKE, 0, None, 0, None) == INVALID
+    assert L.qsa_select_topk(FAKE, 28, 0, p, 1, 10, 4096, FAKE, 0, None, 0, None, 0, None) == INVALID
     assert L.qsa_select_topk(FAKE, 28, 0, p, 1, 10, 8, NULL, 0, None, 0, None) == INVALID
-    assert L.qsa_select_topk(FAKE, 24, 0, p, 1, 10, 8, FAKE, 0, None, 0, None) == INVALID
+    assert L.qsa_select_topk(FAKE, 24, 0, p, 1, 10, 8, FAKE, 0, None, 0, None, 0, None) == INVALID
     assert L.qsa_select_topk(FAKE, 28, 0, _pos(100, 100), 2, 10, 8, FAKE, 80, None, 0, None) == INVALID  # seq stride 0
     assert L.qsa_select_workspace_bytes(1, 8192, 512) == 0
 
@@ -134,10 +134,10 @@ def test_index_select_prefill_validation(L):
 def test_attention_validation(L):
     p = _pos(40)
     # only invalid combinations are exercised: a valid one would launch
-    assert L.qsa_sparse_attn_prefill(FAKE, 0, FAKE, FAKE, 0, FAKE, 0, p, 1, 4, 0, 0.0625, FAKE, 0, None, 0, None) == INVALID
-    assert L.qsa_sparse_attn_prefill(FAKE, 0, FAKE, FAKE, 0, FAKE, 0, p, 1, 4, 16, 0.0, FAKE, 0, None, 0, None) == INVALID
-    assert L.qsa_sparse_attn_prefill(FAKE, 0, NULL, FAKE, 0, FAKE, 0, p, 1, 4, 16, 0.0625, FAKE, 0, None, 0, None) == INVALID
-    assert L.qsa_sparse_attn_prefill(FAKE, 0, FAKE, FAKE, 0, FAKE + 2, 0, p, 1, 4, 16, 0.0625, FAKE, 0, None, 0, None) == INVALID
+    assert L.qsa_sparse_attn_prefill(FAKE, 0, FAKE, FAKE, 0, FAKE, 0, p, 1, 4, 0, 0.0625, FAKE, 0, None, 0, None, 0, None) == INVALID
+    assert L.qsa_sparse_attn_prefill(FAKE, 0, FAKE, FAKE, 0, FAKE, 0, p, 1, 4, 16, 0.0, FAKE, 0, None, 0, None, 0, None) == INVALID
+    assert L.qsa_sparse_attn_prefill(FAKE, 0, NULL, FAKE, 0, FAKE, 0, p, 1, 4, 16, 0.0625, FAKE, 0, None, 0, None, 0, None) == INVALID
+    assert L.qsa_sparse_attn_prefill(FAKE, 0, FAKE, FAKE, 0, FAKE + 2, 0, p, 1, 4, 16, 0.0625, FAKE, 0, None, 0, None, 0, None) == INVALID
 
 
 def test_decode_workspace(L):
@@ -148,19 +148,19 @@ def test_decode_workspace(L):
     assert L.qsa_decode_workspace_bytes(4, 4, 512) > 0            # 16 rows share the ~256 split workgroups
     p = _pos(1048576, 1048576, 1048576, 1048576)
     st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048577 * 512, FAKE, 512, p, 4, 1, 512, 0.0625, FAKE,
-                                  6144, FAKE, FAKE, need - 16, None)
+                                  6144, FAKE, NULL, 0, FAKE, need - 16, None)
     assert st == WORKSPACE, _err(L)
     st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048577 * 512, FAKE, 512, p, 4, 1, 512, 0.0625, FAKE,
-                                  6144, FAKE, NULL, need, None)
+                                  6144, FAKE, NULL, 0, NULL, need, None)
     assert st == WORKSPACE
     # KV sequence stride too small for position 1048576
     st = L.qsa_sparse_attn_decode(FAKE, 6144, FAKE, FAKE, 1048576 * 512, FAKE, 512, p, 4, 1, 512, 0.0625, FAKE,
-                                  6144, FAKE, FAKE, need, None)
+                                  6144, FAKE, NULL, 0, FAKE, need, None)
     assert st == INVALID
     # two tokens per sequence: sel rows must hold tq * budget per sequence
     need2 = L.qsa_decode_workspace_bytes(4, 2, 512)
     st = L.qsa_sparse_attn_decode(FAKE, 2 * 6144, FAKE, FAKE, 1048578 * 512, FAKE, 512, p, 4, 2, 512, 0.0625,
-                                  FAKE, 2 * 6144, FAKE, FAKE, need2, None)
+                                  FAKE, 2 * 6144, FAKE, NULL, 0, FAKE, need2, None)
     assert st == INVALID and "sel_seq_stride" in _err(L)
 
 
@@ -185,7 +185,7 @@ def test_decode_step_validation(L):
         return L.qsa_decode_step(FAKE, tq * 24 * 256, FAKE, v_new, tq * 2 * 256, FAKE, tq * 4 * 128, k_idx_new,
                                  FAKE, FAKE, 9004 * 512, k_idx, k_idx_stride, FAKE, 2252 * 128,
                                  p, B, tq, budget, 0.0625, 1.0e7, FAKE, ld, tq * ld, FAKE, tq * budget, FAKE,
-                                 tq * 24 * 256, NULL, FAKE, ws, None)
+                                 tq * 24 * 256, NULL, NULL, 0, FAKE, ws, None)
 
     assert call(k_idx=NULL) == INVALID
     assert "k_idx" in L.qsa_last_error().decode()

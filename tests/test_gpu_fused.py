@@ -288,6 +288,7 @@ def test_multi_token_decode_step_matches_primitives(pos, tq, budget):
     k_new = torch.randn((B, tq, 2, 256), generator=g).to(bf).to(dev)
     v_new = torch.randn((B, tq, 2, 256), generator=g).to(bf).to(dev)
     k_idx_new = (torch.randn((B, tq, 128), generator=g) / math.sqrt(128)).to(bf).to(dev)
+    gate = (torch.randn((B, tq, 24, 256), generator=g) * 3).to(bf).to(dev)    # the output gate too
     ld = max(4, ((L - 1) // 4 + 3) // 4 * 4)
     outs = []
     for fused in (False, True):
@@ -305,12 +306,12 @@ def test_multi_token_decode_step_matches_primitives(pos, tq, budget):
             ws = qsa.decode_step_workspace(B, budget, tq=tq)
             for _ in range(2):                        # the second call reuses the workspace
                 qsa.decode_step(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel, ws,
-                                v_new=v_new, k_idx_new=k_idx_new)
+                                v_new=v_new, k_idx_new=k_idx_new, gate=gate)
             assert int(ws[:B * tq * (4096 + 16) * 4].count_nonzero()) == 0
         else:
             qsa.decode_step_primitives(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel,
                                        qsa.decode_workspace(B, budget, tq=tq), torch.empty_like(q_raw),
-                                       v_new=v_new, k_idx_new=k_idx_new)
+                                       v_new=v_new, k_idx_new=k_idx_new, gate=gate)
         torch.cuda.synchronize()
         per = []
         for b in range(B):

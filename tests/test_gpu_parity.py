@@ -419,3 +419,63 @@ def test_multi_token_decode_steps_match_the_oracle_rows():
     rows = sorted(res)
     compare_rows(oracle_layer(x), x, rows, lambda b, t: res[(b, t)][0], lambda b, t: res[(b, t)][1],
                  lambda b, t: res[(b, t)][2], lambda b, t: res[(b, t)][3])
+
+
+# ------------------------------------------------------------------ output gate
+
+def _gate(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * 3).to(torch.bfloat16)
+
+
+def test_gated_attention_prefill_and_decode_with_oracle_selection():
+    """The output gate fused into the prefill epilogue and the decode merge
+    (1 and 3 tokens per sequence) against the oracle's gated rows; LSE is
+    the ungated one."""
+    ctx, tq, budget = 3000, 3, 512
+    wl = I.custom_workload("prefill", batch=2, ctx=ctx, tq=tq, budget=budget, seed=91)
+    say(f"gated attention {wl.name}")
+    x = I.make_inputs(wl)
+    gate = _gate((2, tq, 24, 256), 5)
+    layer = O.OracleLayer(O.bits(x.q), O.bits(x.q_idx), O.bits(x.k), O.bits(x.v), O.bits(x.k_idx), x.q_pos0,
+                          budget, gate=O.bits(gate))
+    rows = [(b, ctx + i) for b in range(2) for i in range(tq)]
+    ref = layer.rows(rows)
+    qd, kd = _oracle_inputs_for_attention(x)
+    sel = torch.from_numpy(np.stack([r.sel for r in ref]).reshape(2, tq, budget)).cuda()
+    out = torch.empty((2, tq, 24, 256), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((2, tq, 24), dtype=torch.float32, device="cuda")
+    qsa.sparse_attn_prefill(qd, kd, x.v.cuda(), sel, [ctx, ctx], out, lse, gate=gate.cuda())
+    _check_attention(out.float().cpu().numpy().reshape(-1, 24, 256), lse.cpu().numpy().reshape(-1, 24), ref)
+    # decode form, all 3 tokens per sequence in one call
+    out_d = torch.empty_like(out)
+    lse_d = torch.empty_like(lse)
+    ws = qsa.decode_workspace(2, budget, tq=tq)
+    qsa.sparse_attn_decode(qd, kd, x.v.cuda(), sel, [ctx, ctx], out_d, lse_d, ws, gate=gate.cuda())
+    _check_attention(out_d.float().cpu().numpy().reshape(-1, 24, 256), lse_d.cpu().numpy().reshape(-1, 24), ref)
+    # one token per sequence
+    out_1 = torch.empty((2, 24, 256), dtype=torch.bfloat16, device="cuda")
+    lse_1 = torch.empty((2, 24), dtype=torch.float32, device="cuda")
+    qsa.sparse_attn_decode(qd[:, 0].contiguous(), kd, x.v.cuda(), sel[:, 0].contiguous(), [ctx, ctx], out_1, lse_1,
+                           qsa.decode_workspace(2, budget), gate=gate[:, 0].contiguous().cuda())
+    ref1 = [ref[0], ref[tq]]
+    _check_attention(out_1.float().cpu().numpy(), lse_1.cpu().numpy(), ref1)
+
+
+def test_gated_prefill_layer_end_to_end():
+    """A whole prefill chunk with the output gate against the oracle's gated
+    rows under the end-to-end protocol."""
+    wl = I.custom_workload("prefill", batch=1, ctx=2000, tq=300, budget=64, n_needles=4, seed=93, chunk=128)
+    say(f"gated prefill layer {wl.name}")
+    x = I.make_inputs(wl)
+    gate = _gate((1, 300, 24, 256), 6)
+    dp = DevicePrefill(x)
+    dp.run(gate=gate.cuda())
+    layer = O.OracleLayer(O.bits(x.q), O.bits(x.q_idx), O.bits(x.k), O.bits(x.v), O.bits(x.k_idx), x.q_pos0,
+                          wl.budget, gate=O.bits(gate))
+    sel = dp.bufs.sel.cpu().numpy()
+    out = dp.out.float().cpu().numpy()
+    lse = dp.lse.cpu().numpy()
+    rows = [(0, 2000 + i) for i in range(0, 300, 7)]
+    compare_rows(layer, x, rows, None, lambda b, t: sel[b, t - 2000], lambda b, t: out[b, t - 2000],
+                 lambda b, t: lse[b, t - 2000])
