@@ -36,6 +36,12 @@ Readings taken where the pages are silent (each restated at its function):
                 own block are attended only up to the query itself;
   rotary      = rotate-half pairing (i, i + 32) inside the first 64 dims,
                 angle = position * theta**(-i / 32), applied to Q and K only;
+  static YaRN = (optional; model card, "Processing Ultra-Long Texts": rope_type
+                yarn, factor 4, original_max_position_embeddings 262144, for
+                contexts past 262144) the YaRN paper's NTK-by-parts blend of
+                the frequencies with the frameworks' integer ramp ends and
+                beta_fast 32 / beta_slow 1, cos and sin scaled by 0.1 ln s + 1
+                (the pages name the method and its parameters only);
   output gate = (optional) out * sigmoid(g) per head dim, g an input of the
                 output's shape (blog, "Training stability": the attention
                 output gating mechanism is retained; its definition is not
@@ -94,18 +100,70 @@ def rope_inv_freq(rot_dim: int = 64, theta: float = ROPE_THETA) -> np.ndarray:
     return theta ** (-2.0 * i / rot_dim)
 
 
+@dataclass(frozen=True)
+class Yarn:
+    """Static YaRN rotary scaling (model card, "Processing Ultra-Long Texts":
+    rope_type yarn, factor 4.0, original_max_position_embeddings 262144; a
+    context of about 512K is better served by factor 2).  beta_fast and
+    beta_slow are the YaRN paper's alpha / beta bounds on rotation counts."""
+    factor: float = 4.0
+    original_max: int = 262144
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+
+
+def yarn_inv_freq(yarn: Yarn, rot_dim: int = 64, theta: float = ROPE_THETA) -> tuple[np.ndarray, float]:
+    """Frequencies and cos/sin factor of static YaRN (Peng et al., 2023,
+    "YaRN: Efficient Context Window Extension of Large Language Models":
+    NTK-by-parts interpolation plus the attention temperature), static, i.e.
+    one table for every length, as the model card says the frameworks do.
+
+    Pair i turns L * w_i / (2 pi) times over the original context L, where
+    w_i = theta**(-2i/rot_dim).  Solving that count = rho for i gives
+    i(rho) = (rot_dim / 2) * ln(L / (2 pi rho)) / ln(theta).  The ramp runs
+    from lo = floor(i(beta_fast)) to hi = ceil(i(beta_slow)) (lo at least 0,
+    hi at most rot_dim - 1, hi nudged by 0.001 if they meet): pairs at or
+    below lo keep w_i (many turns: extrapolated), pairs at or above hi take
+    w_i / s (interpolated), and in between the two blend linearly in i.
+    cos and sin are multiplied by 0.1 * ln(s) + 1 (the paper's sqrt(1/t)).
+    s = 1 returns the plain frequencies and factor 1.
+    """
+    w = rope_inv_freq(rot_dim, theta)
+    s = float(yarn.factor)
+    if s <= 1.0:
+        return w, 1.0
+    L = float(yarn.original_max)
+
+    def pair_at(rho: float) -> float:
+        return (rot_dim / 2) * np.log(L / (2.0 * np.pi * rho)) / np.log(theta)
+
+    lo = max(np.floor(pair_at(yarn.beta_fast)), 0.0)
+    hi = min(np.ceil(pair_at(yarn.beta_slow)), rot_dim - 1.0)
+    if lo == hi:
+        hi += 0.001
+    i = np.arange(rot_dim // 2, dtype=np.float64)
+    ramp = np.clip((i - lo) / (hi - lo), 0.0, 1.0)      # 0: keep w_i, 1: w_i / s
+    inv = (w / s) * ramp + w * (1.0 - ramp)
+    return inv, 0.1 * np.log(s) + 1.0
+
+
 def rope_rotate_f64(x: np.ndarray, positions: np.ndarray, rot_dim: int = 64,
-                    theta: float = ROPE_THETA) -> np.ndarray:
+                    theta: float = ROPE_THETA, yarn: Yarn | None = None) -> np.ndarray:
     """Unrounded rotary embedding.  x: float64 [..., T, H, D]; positions: [T].
 
     Pair (i, i + rot_dim/2) of the rotary slice is turned by the angle
     position * inv_freq[i]:  (a, b) -> (a cos - b sin, b cos + a sin).
-    Dimensions from rot_dim on pass through unchanged.
+    Dimensions from rot_dim on pass through unchanged.  With yarn, inv_freq
+    and the factor on cos and sin come from yarn_inv_freq.
     """
     half = rot_dim // 2
-    ang = np.asarray(positions, np.float64)[:, None] * rope_inv_freq(rot_dim, theta)[None, :]
-    c = np.cos(ang)[:, None, :]
-    s = np.sin(ang)[:, None, :]
+    if yarn is None:
+        inv, m = rope_inv_freq(rot_dim, theta), 1.0
+    else:
+        inv, m = yarn_inv_freq(yarn, rot_dim, theta)
+    ang = np.asarray(positions, np.float64)[:, None] * inv[None, :]
+    c = (np.cos(ang) * m)[:, None, :]
+    s = (np.sin(ang) * m)[:, None, :]
     a = x[..., :half]
     b = x[..., half:rot_dim]
     out = np.array(x, dtype=np.float64, copy=True)
@@ -115,9 +173,9 @@ def rope_rotate_f64(x: np.ndarray, positions: np.ndarray, rot_dim: int = 64,
 
 
 def rope_rotate(x_bits: np.ndarray, positions: np.ndarray, rot_dim: int = 64,
-                theta: float = ROPE_THETA) -> np.ndarray:
+                theta: float = ROPE_THETA, yarn: Yarn | None = None) -> np.ndarray:
     """Rotary embedding of bf16 tensors [..., T, H, D]; result rounded once to bf16."""
-    return f64_to_bf16(rope_rotate_f64(bf16_to_f64(x_bits), positions, rot_dim, theta))
+    return f64_to_bf16(rope_rotate_f64(bf16_to_f64(x_bits), positions, rot_dim, theta, yarn))
 
 
 # --------------------------------------------------------------------------
@@ -266,13 +324,15 @@ class OracleLayer:
     are rotated here (K rows stand in the cache rotated), block keys are
     compressed here from k_idx, then every row is scored, selected and
     attended independently.  gate (optional, bf16 bits [B, tq, Hq, D]) gates
-    the outputs (output_gate).
+    the outputs (output_gate).  yarn (optional) selects static YaRN rotary.
     """
 
     def __init__(self, q, q_idx, k, v, k_idx, q_pos0, budget: int,
-                 rot_dim: int = 64, theta: float = ROPE_THETA, scale: float | None = None, gate=None):
+                 rot_dim: int = 64, theta: float = ROPE_THETA, scale: float | None = None, gate=None,
+                 yarn: Yarn | None = None):
         self.q, self.q_idx, self.k, self.v, self.k_idx = q, q_idx, k, v, k_idx
         self.gate = gate
+        self.yarn = yarn
         self.q_pos0 = np.asarray(q_pos0, np.int64)
         self.budget = budget
         self.rot_dim, self.theta = rot_dim, theta
@@ -308,8 +368,9 @@ class OracleLayer:
                 if sel_override is not None and (b, t) in sel_override:
                     sel = np.asarray(sel_override[(b, t)], np.int32)
                 tok = expand_tokens(sel, t)
-                qr = rope_rotate(self.q[b, r_idx[i]][None], np.array([t]), self.rot_dim, self.theta)[0]
-                kr = rope_rotate(self.k[b, tok], tok, self.rot_dim, self.theta)
+                qr = rope_rotate(self.q[b, r_idx[i]][None], np.array([t]), self.rot_dim, self.theta,
+                                 self.yarn)[0]
+                kr = rope_rotate(self.k[b, tok], tok, self.rot_dim, self.theta, self.yarn)
                 out, lse = attend(bf16_to_f64(qr), bf16_to_f64(kr), bf16_to_f64(self.v[b, tok]),
                                   self.scale)
                 if self.gate is not None:

@@ -32,7 +32,7 @@ def _compress_exact_mean(k_idx_bits, b0, b1):
 
 
 def _rope_factory(sign=1.0, interleaved=False, theta=O.ROPE_THETA, rot=64):
-    def f(x, positions, rot_dim=64, th=O.ROPE_THETA):
+    def f(x, positions, rot_dim=64, th=O.ROPE_THETA, yarn=None):
         half = rot // 2
         ang = np.asarray(positions, np.float64)[:, None] * (theta ** (-2.0 * np.arange(half) / rot))[None]
         c = np.cos(ang)[:, None, :]
@@ -47,6 +47,21 @@ def _rope_factory(sign=1.0, interleaved=False, theta=O.ROPE_THETA, rot=64):
             out[..., :half] = a * c - b * s
             out[..., half:rot] = b * c + a * s
         return out
+    return f
+
+
+def _yarn_factory(reverse=False, no_mscale=False, round_ends=False, times_s=False):
+    def f(yarn, rot_dim=64, theta=O.ROPE_THETA):
+        w = O.rope_inv_freq(rot_dim, theta)
+        s, L = yarn.factor, yarn.original_max
+        at = lambda rho: (rot_dim / 2) * np.log(L / (2 * np.pi * rho)) / np.log(theta)
+        lo = np.round(at(32.0)) if round_ends else np.floor(at(32.0))
+        hi = np.round(at(1.0)) if round_ends else np.ceil(at(1.0))
+        ramp = np.clip((np.arange(rot_dim // 2) - lo) / (hi - lo), 0, 1)
+        if reverse:
+            ramp = 1 - ramp
+        interp = w * s if times_s else w / s
+        return interp * ramp + w * (1 - ramp), (1.0 if no_mscale else 0.1 * np.log(s) + 1)
     return f
 
 
@@ -110,6 +125,14 @@ MUTANTS = [
     ("rope: theta 1e4", "rope_rotate_f64", _rope_factory(theta=1e4), [P.test_rope_complex_form]),
     ("rope: 128 rotary dims", "rope_rotate_f64", _rope_factory(rot=128),
      [P.test_rope_leaves_dims_past_the_slice, P.test_rope_complex_form]),
+    ("yarn: ramp reversed (high frequencies interpolated)", "yarn_inv_freq", _yarn_factory(reverse=True),
+     [P.test_yarn_table_for_the_model_card_config_by_hand]),
+    ("yarn: no factor on cos and sin", "yarn_inv_freq", _yarn_factory(no_mscale=True),
+     [P.test_yarn_table_for_the_model_card_config_by_hand, P.test_yarn_rotation_complex_form_and_norms]),
+    ("yarn: ramp ends rounded to nearest", "yarn_inv_freq", _yarn_factory(round_ends=True),
+     [P.test_yarn_table_for_the_model_card_config_by_hand]),
+    ("yarn: frequencies multiplied by s", "yarn_inv_freq", _yarn_factory(times_s=True),
+     [P.test_yarn_table_for_the_model_card_config_by_hand]),
     ("select: ties to the higher index", "select_blocks", _select_factory(tie_high=True),
      [P.test_select_golden]),
     ("select: own block outside the budget", "select_blocks", _select_factory(own_outside_budget=True),

@@ -111,6 +111,79 @@ def test_rope_rounding_is_single_step():
     assert np.array_equal(O.rope_rotate(x, pos), O.f64_to_bf16(O.rope_rotate_f64(O.bf16_to_f64(x), pos)))
 
 
+
+# ---------------------------------------------------------------- static YaRN
+
+def test_yarn_table_for_the_model_card_config_by_hand():
+    # model card "Processing Ultra-Long Texts": theta 1e7, factor 4, original 262144,
+    # 64 rotary dims.  Pair i turns 262144 * 1e7^(-i/32) / (2 pi) times over the original
+    # context; that count is 32 at i = 32 ln(262144 / 64 pi) / ln 1e7 = 14.24 and 1 at
+    # i = 32 ln(262144 / 2 pi) / ln 1e7 = 21.12, so the ramp runs from pair 14 to pair 22.
+    assert 14 < 32 * math.log(262144 / (64 * math.pi)) / math.log(1e7) < 14.5
+    assert 21 < 32 * math.log(262144 / (2 * math.pi)) / math.log(1e7) < 21.5
+    inv, m = O.yarn_inv_freq(O.Yarn(factor=4.0, original_max=262144))
+    w = np.array([1e7 ** (-i / 32.0) for i in range(32)])
+    assert np.allclose(inv[:15], w[:15], rtol=1e-14, atol=0)          # pairs 0..14 kept
+    assert np.allclose(inv[22:], w[22:] / 4, rtol=1e-14, atol=0)      # pairs 22..31 divided by 4
+    for i in range(15, 22):                                            # linear blend in i
+        g = (i - 14) / 8.0
+        assert math.isclose(inv[i], w[i] * (1 - g) + w[i] / 4 * g, rel_tol=1e-14)
+    assert math.isclose(m, 1 + 0.1 * math.log(4.0), rel_tol=1e-15)
+
+
+@pytest.mark.parametrize("theta,factor,orig", [(1e7, 4.0, 262144), (1e7, 2.0, 262144),
+                                               (1e4, 8.0, 4096), (5e5, 3.0, 32768), (1e7, 1.5, 1 << 20)])
+def test_yarn_matches_the_transformers_routine(theta, factor, orig):
+    # an independent implementation of the frameworks' static YaRN (float32 there)
+    tr = pytest.importorskip("transformers")
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    cfg = tr.PretrainedConfig()
+    cfg.hidden_size, cfg.num_attention_heads, cfg.head_dim = 24 * 256, 24, 256
+    cfg.max_position_embeddings = int(orig * factor)
+    cfg.rope_parameters = {"rope_type": "yarn", "rope_theta": theta, "partial_rotary_factor": 0.25,
+                           "factor": factor, "original_max_position_embeddings": orig}
+    ref_inv, ref_m = ROPE_INIT_FUNCTIONS["yarn"](cfg, torch.device("cpu"))
+    inv, m = O.yarn_inv_freq(O.Yarn(factor=factor, original_max=orig), theta=theta)
+    assert np.allclose(inv, ref_inv.double().numpy(), rtol=2e-6, atol=0)
+    assert math.isclose(m, ref_m, rel_tol=1e-12)
+
+
+def test_yarn_factor_one_is_plain_rotary():
+    x = O.bf16_to_f64(_rand_bf16((3, 2, 256), 8))
+    pos = np.array([1, 300000, 1048575])
+    assert np.array_equal(O.rope_rotate_f64(x, pos, yarn=O.Yarn(factor=1.0)), O.rope_rotate_f64(x, pos))
+
+
+def test_yarn_rotation_complex_form_and_norms():
+    # each pair turned by e^{i p w'_i} and scaled by 1 + 0.1 ln 4; dims past 64 untouched
+    yarn = O.Yarn()
+    inv, _ = O.yarn_inv_freq(yarn)
+    mf = 1 + 0.1 * math.log(4.0)
+    x = O.bf16_to_f64(_rand_bf16((3, 2, 256), 9))
+    pos = np.array([0, 262145, 1048575])
+    y = O.rope_rotate_f64(x, pos, yarn=yarn)
+    assert np.array_equal(y[..., 64:], x[..., 64:])
+    for ti, p in enumerate(pos):
+        for i in range(32):
+            z = complex(x[ti, 0, i], x[ti, 0, 32 + i]) * cmath.exp(1j * p * inv[i]) * mf
+            assert abs(y[ti, 0, i] - z.real) < 1e-9 and abs(y[ti, 0, 32 + i] - z.imag) < 1e-9
+    nx = x[..., :32] ** 2 + x[..., 32:64] ** 2
+    ny = y[..., :32] ** 2 + y[..., 32:64] ** 2
+    assert np.allclose(ny, nx * mf * mf, rtol=1e-12, atol=1e-12)
+
+
+def test_yarn_relative_position():
+    # <Y(m) q, Y(n) k> = <Y(m - n) q, Y(0) k>: the scaled rotation still depends on m - n only
+    yarn = O.Yarn()
+    q = O.bf16_to_f64(_rand_bf16((1, 1, 256), 10))
+    k = O.bf16_to_f64(_rand_bf16((1, 1, 256), 11))
+    for m, n in [(5, 3), (262144, 1), (1048575, 943718)]:
+        lhs = np.dot(O.rope_rotate_f64(q, np.array([m]), yarn=yarn)[0, 0, :64],
+                     O.rope_rotate_f64(k, np.array([n]), yarn=yarn)[0, 0, :64])
+        rhs = np.dot(O.rope_rotate_f64(q, np.array([m - n]), yarn=yarn)[0, 0, :64],
+                     O.rope_rotate_f64(k, np.array([0]), yarn=yarn)[0, 0, :64])
+        assert abs(lhs - rhs) < 1e-8
+
 # ---------------------------------------------------------------- compression
 
 def test_compress_golden():
