@@ -11,7 +11,9 @@ each: its K/V/indexer-key rows appended, scores, selection, attention) under
 "decode", and the same step with 4 new tokens per sequence (the shape of
 multi-token prediction or speculative verification) under
 "decode_multi_token".  Inputs are seeded synthetic tensors already resident
-in HBM.
+in HBM.  Rotary uses the model card's static YaRN table (factor 4 over 262144
+positions), as contexts past 262144 call for; --rope plain selects the plain
+table (the same work).
 
 Timing: W untimed warm-up steps, then K steps between two device
 synchronisations; per-kernel durations come from HIP events recorded on the
@@ -58,6 +60,9 @@ def parse():
     ap.add_argument("--decode-tq", type=int, default=4,
                     help="also time a decode step of this many new tokens per sequence (1 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=48, help="oracle rows timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--rope", choices=("yarn", "plain"), default="yarn",
+                    help="rotary table: the model card's static YaRN (factor 4 over 262144, for contexts past "
+                         "262144) or plain rotary")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -101,10 +106,10 @@ def prefill_geometry(wl, c0: int, c1: int):
 # ------------------------------------------------------------------ device set-up
 
 class Prefill:
-    def __init__(self, wl, x, torch, qsa):
+    def __init__(self, wl, x, torch, qsa, rope=None):
         B, L, ctx, T = wl.batch, wl.length, wl.ctx, wl.tq
         dev = "cuda"
-        self.wl, self.qsa, self.torch = wl, qsa, torch
+        self.wl, self.qsa, self.torch, self.rope = wl, qsa, torch, rope
         self.q_raw = x.q.to(dev)
         self.k_new = x.k[:, ctx:].contiguous().to(dev)
         self.q_idx = x.q_idx.to(dev)
@@ -112,7 +117,7 @@ class Prefill:
         self.v_cache = x.v.to(dev)
         self.k_cache = x.k.to(dev)
         if ctx > 0:
-            qsa.rope_apply(self.k_cache[:, :ctx], [0] * B)
+            qsa.rope_apply(self.k_cache[:, :ctx], [0] * B, rope=rope)
         self.kbar = torch.zeros((B, max(1, L // 4), 128), dtype=torch.bfloat16, device=dev)
         if ctx // 4 > 0:
             qsa.compress_block_keys(self.k_idx, 0, ctx // 4, self.kbar)
@@ -128,8 +133,8 @@ class Prefill:
         B, T, ctx = wl.batch, wl.tq, wl.ctx
         pos = [ctx] * B
         with timer("rope"):
-            q.rope_apply(self.q_raw, pos, out=self.q_rot)
-            q.rope_apply(self.k_new, pos, out=self.k_cache[:, ctx:ctx + T])
+            q.rope_apply(self.q_raw, pos, out=self.q_rot, rope=self.rope)
+            q.rope_apply(self.k_new, pos, out=self.k_cache[:, ctx:ctx + T], rope=self.rope)
         with timer("compress"):
             q.compress_block_keys(self.k_idx, ctx // 4, (ctx + T) // 4, self.kbar)
         ch = self.bufs.chunk
@@ -145,16 +150,16 @@ class Prefill:
 
 
 class Decode:
-    def __init__(self, wl, x, torch, qsa):
+    def __init__(self, wl, x, torch, qsa, rope=None):
         B, ctx = wl.batch, wl.ctx
         dev = "cuda"
-        self.wl, self.qsa, self.torch = wl, qsa, torch
+        self.wl, self.qsa, self.torch, self.rope = wl, qsa, torch, rope
         self.pos = ctx
         # caches with room for up to 4 new tokens (the multi-token step)
         L = ctx + 4
         self.k_cache = torch.zeros((B, L, 2, 256), dtype=torch.bfloat16, device=dev)
         self.k_cache[:, :ctx + 1].copy_(x.k)
-        qsa.rope_apply(self.k_cache[:, :ctx], [0] * B)
+        qsa.rope_apply(self.k_cache[:, :ctx], [0] * B, rope=rope)
         self.v_cache = torch.zeros_like(self.k_cache)
         self.v_cache[:, :ctx + 1].copy_(x.v)
         self.k_idx = torch.zeros((B, L, 128), dtype=torch.bfloat16, device=dev)
@@ -197,7 +202,7 @@ class Decode:
     def multi_step(self):
         self.qsa.decode_step(self.m_q, self.m_k, self.m_q_idx, self.k_idx, self.k_cache, self.v_cache, self.kbar,
                              self.pos, self.wl.budget, self.m_out, self.m_lse, self.m_scores, self.m_sel, self.m_ws,
-                             v_new=self.m_v, k_idx_new=self.m_k_idx)
+                             v_new=self.m_v, k_idx_new=self.m_k_idx, rope=self.rope)
 
     def step(self, timer):
         """One serving decode step through the single qsa_decode_step call: the
@@ -208,7 +213,7 @@ class Decode:
         with timer("decode_step"):
             q.decode_step(self.q_raw, self.k_new, self.q_idx, self.k_idx, self.k_cache, self.v_cache, self.kbar,
                           self.pos, wl.budget, self.out, self.lse, self.scores, self.sel, self.ws,
-                          v_new=self.v_new, k_idx_new=self.k_idx_new)
+                          v_new=self.v_new, k_idx_new=self.k_idx_new, rope=self.rope)
 
 
 class EventTimer:
@@ -286,7 +291,8 @@ def cpu_baseline(wl, x, n_rows: int, args):
     rows = I.sample_rows(wl, n_rows)
     B = O.bits
     with threadpool_limits(limits=1):
-        layer = O.OracleLayer(B(x.q), B(x.q_idx), B(x.k), B(x.v), B(x.k_idx), x.q_pos0, wl.budget)
+        layer = O.OracleLayer(B(x.q), B(x.q_idx), B(x.k), B(x.v), B(x.k_idx), x.q_pos0, wl.budget,
+                              yarn=O.Yarn() if args.rope == "yarn" else None)
         t0 = time.perf_counter()
         for b in sorted({r[0] for r in rows}):
             layer.kbar_bits(b)
@@ -331,7 +337,8 @@ def main():
     t0 = time.time()
     x = I.make_inputs(wl)
     log(args, f"inputs {wl.name}: {time.time() - t0:.1f}s")
-    pf = Prefill(wl, x, torch, qsa)
+    rope = qsa.YARN if args.rope == "yarn" else None
+    pf = Prefill(wl, x, torch, qsa, rope)
     for _ in range(args.warmup):
         pf.step(NullTimer())
     torch.cuda.synchronize()
@@ -382,7 +389,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "new_tokens": wl.tq, "cached_tokens": wl.ctx,
                    "context": wl.length, "budget_blocks": wl.budget, "block_tokens": 4,
-                   "query_chunk": wl.chunk, "heads": "24q/2kv x 256, indexer 4q/1k x 128"},
+                   "query_chunk": wl.chunk, "heads": "24q/2kv x 256, indexer 4q/1k x 128",
+                   "rope": "static YaRN, factor 4 over 262144" if args.rope == "yarn" else "plain, theta 1e7"},
         "roofline": roofline,
         "mfma": mfma,
         "kernels_ms_per_step": {k: t / args.steps for k, (t, n) in kern.items()},
@@ -399,7 +407,7 @@ def main():
         t0 = time.time()
         dx = I.make_inputs(dwl)
         log(args, f"inputs {dwl.name}: {time.time() - t0:.1f}s")
-        dd = Decode(dwl, dx, torch, qsa)
+        dd = Decode(dwl, dx, torch, qsa, rope)
         del dx
         flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 

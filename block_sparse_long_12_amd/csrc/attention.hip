@@ -195,6 +195,8 @@ struct RopeAngle {
 __device__ __forceinline__ RopeAngle rope_angle(int p, const InvFreq& inv) {
     RopeAngle a;
     sincos(static_cast<double>(p) * inv.f[threadIdx.x & 31], &a.sn, &a.cs);
+    a.sn *= inv.m;
+    a.cs *= inv.m;
     return a;
 }
 
@@ -307,7 +309,7 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
     const int64_t rows = static_cast<int64_t>(batch) * tq;
     if (rows == 0) return hipSuccess;
     const float c = scale * 1.4426950408889634f;
-    const InvFreq inv = make_inv_freq(1.0e7);
+    const InvFreq inv = make_inv_freq(qsa_rope_t{1.0e7, 1.0, 0});
     hipLaunchKernelGGL(attn_prefill_kernel, dim3(static_cast<unsigned>(rows)), dim3(128), 0, stream,
                        q, qs, k, v, kvs, sel, sels, pos0, tq, budget, scale, c, out, os, lse, lss, gate, gs, inv,
                        0);
@@ -464,7 +466,7 @@ hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* 
                                  const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                                  const Positions& pos, int batch, int tq, int budget, float scale,
                                  uint16_t* out, int64_t os, float* lse, const uint16_t* gate, int64_t gs,
-                                 void* ws, double rope_theta, hipStream_t stream) {
+                                 void* ws, const qsa_rope_t* rope, hipStream_t stream) {
     const int rows = batch * tq;
     if (rows == 0) return hipSuccess;
     int n_split, bps;
@@ -472,10 +474,10 @@ hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* 
     float* ws_ml = static_cast<float*>(ws);
     float* ws_acc = ws_ml + static_cast<size_t>(rows) * n_split * kHq * 2;
     const float c = scale * 1.4426950408889634f;
-    const InvFreq inv = make_inv_freq(rope_theta > 0.0 ? rope_theta : 1.0e7);
+    const InvFreq inv = make_inv_freq(rope != nullptr ? *rope : qsa_rope_t{1.0e7, 1.0, 0});
     hipLaunchKernelGGL(attn_decode_split_kernel, dim3(static_cast<unsigned>(rows * n_split)),
                        dim3(128), 0, stream, q, qs, k, v, kvs, sel, sels, pos, budget, tq, n_split, bps,
-                       c, ws_ml, ws_acc, inv, rope_theta > 0.0 ? 1 : 0);
+                       c, ws_ml, ws_acc, inv, rope != nullptr ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(static_cast<unsigned>(rows * kHq)), dim3(256),
@@ -489,7 +491,7 @@ hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
                               uint16_t* out, int64_t os, float* lse, const uint16_t* gate, int64_t gs,
                               void* ws, hipStream_t stream) {
     return launch_attn_decode_ex(q, qs, k, v, kvs, sel, sels, pos, batch, tq, budget, scale, out, os, lse,
-                                 gate, gs, ws, 0.0, stream);
+                                 gate, gs, ws, nullptr, stream);
 }
 
 }  // namespace qsa

@@ -489,7 +489,7 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
         ap.kis = append->kis;
         ap.kbar = append->kbar;
         ap.kbs = append->kbs;
-        ap.inv = make_inv_freq(append->rope_theta > 0.0 ? append->rope_theta : 1.0e7);
+        ap.inv = make_inv_freq(append->rope);
     }
     hipError_t e;
     // one token per sequence: the rows are appended by the scan; several: first,

@@ -57,6 +57,15 @@ qsa_status_t check_batch(int32_t batch) {
     return QSA_OK;
 }
 
+// Rotary parameters: NULL means the model card's plain rotary (theta 1e7).
+qsa_status_t take_rope(const qsa_rope_t* rope, qsa_rope_t& out) {
+    out = rope != nullptr ? *rope : qsa_rope_t{1.0e7, 1.0, 0};
+    CHECK(isfinite(out.theta) && out.theta > 1.0, "rope theta must be finite and > 1");
+    CHECK(isfinite(out.yarn_factor) && out.yarn_factor >= 1.0, "yarn_factor must be finite and >= 1");
+    CHECK(out.yarn_factor == 1.0 || out.yarn_original_max >= 1, "yarn_original_max must be >= 1 with YaRN");
+    return QSA_OK;
+}
+
 #define TRY(expr)                          \
     do {                                   \
         qsa_status_t _s = (expr);          \
@@ -91,7 +100,7 @@ const char* qsa_last_error(void) { return g_err; }
 qsa_status_t qsa_rope_apply(const uint16_t* x, int64_t x_seq_stride, int64_t x_tok_stride,
                             uint16_t* y, int64_t y_seq_stride, int64_t y_tok_stride,
                             int32_t batch, int32_t n_tokens, int32_t n_heads,
-                            const int32_t* pos0, double rope_theta, hipStream_t stream) {
+                            const int32_t* pos0, const qsa_rope_t* rope, hipStream_t stream) {
     TRY(check_batch(batch));
     CHECK(x != nullptr && y != nullptr, "x or y is NULL");
     CHECK(aligned16(x) && aligned16(y), "x and y must be 16-byte aligned");
@@ -102,7 +111,8 @@ qsa_status_t qsa_rope_apply(const uint16_t* x, int64_t x_seq_stride, int64_t x_t
           "token stride smaller than n_heads * 256");
     CHECK(batch == 1 || (stride_ok(x_seq_stride) && stride_ok(y_seq_stride)),
           "sequence strides must be positive multiples of 8");
-    CHECK(isfinite(rope_theta) && rope_theta > 1.0, "rope_theta must be finite and > 1");
+    qsa_rope_t rp;
+    TRY(take_rope(rope, rp));
     qsa::Positions p;
     TRY(take_positions(pos0, batch, n_tokens, "pos0", p));
     const bool in_place = (x == y);
@@ -110,7 +120,7 @@ qsa_status_t qsa_rope_apply(const uint16_t* x, int64_t x_seq_stride, int64_t x_t
           "in-place rotation needs identical strides");
     if (n_tokens == 0) return ok();
     return hip_result(qsa::launch_rope(x, x_seq_stride, x_tok_stride, y, y_seq_stride, y_tok_stride,
-                                       batch, n_tokens, n_heads, p, rope_theta, in_place, stream),
+                                       batch, n_tokens, n_heads, p, rp, in_place, stream),
                       "rope_apply launch");
 }
 
@@ -409,7 +419,7 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
                              uint16_t* k_idx, int64_t k_idx_seq_stride,
                              uint16_t* kbar, int64_t kbar_seq_stride,
                              const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
-                             float softmax_scale, double rope_theta,
+                             float softmax_scale, const qsa_rope_t* rope,
                              float* scores, int64_t scores_ld, int64_t scores_seq_stride,
                              int32_t* sel, int64_t sel_seq_stride,
                              uint16_t* out, int64_t out_seq_stride, float* lse,
@@ -429,7 +439,8 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
     CHECK(k_idx_new == nullptr || k_idx != nullptr, "k_idx_new needs the k_idx cache");
     CHECK(k_idx_new == nullptr || aligned16(k_idx_new), "k_idx_new must be 16-byte aligned");
     CHECK(k_idx == nullptr || aligned16(k_idx), "k_idx must be 16-byte aligned");
-    CHECK(isfinite(rope_theta) && rope_theta > 1.0, "rope_theta must be finite and > 1");
+    qsa_rope_t rp;
+    TRY(take_rope(rope, rp));
     if (batch > 1) {
         int64_t max_len = 0;
         for (int b = 0; b < batch; ++b) max_len = p.p[b] + tq > max_len ? p.p[b] + tq : max_len;
@@ -460,7 +471,7 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
     ap.kis = k_idx_seq_stride;
     ap.kbar = kbar;
     ap.kbs = kbar_seq_stride;
-    ap.rope_theta = rope_theta;
+    ap.rope = rp;
     hipError_t e = qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq,
                                                    budget, scores, scores_seq_stride, scores_ld, sel, sel_seq_stride,
                                                    workspace, &ap, stream);
@@ -468,7 +479,7 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
     return hip_result(qsa::launch_attn_decode_ex(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
                                                  sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
                                                  out_seq_stride, lse, gate, gate_seq_stride,
-                                                 static_cast<char*>(workspace) + sel_ws, rope_theta, stream),
+                                                 static_cast<char*>(workspace) + sel_ws, &rp, stream),
                       "decode_step attention launch");
 }
 

@@ -68,7 +68,7 @@ namespace qsa {
 
 hipError_t launch_rope(const uint16_t* x, int64_t xs, int64_t xt, uint16_t* y, int64_t ys,
                        int64_t yt, int batch, int n_tokens, int n_heads, const Positions& pos0,
-                       double theta, bool in_place, hipStream_t stream);
+                       const qsa_rope_t& rope, bool in_place, hipStream_t stream);
 
 hipError_t launch_compress(const uint16_t* k_idx, int64_t ks, int batch, int block_begin,
                            int block_end, uint16_t* kbar, int64_t kbs, hipStream_t stream);
@@ -125,13 +125,13 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
 constexpr int kMaxDecodeTq = QSA_MAX_DECODE_TQ;
 
 size_t decode_workspace_bytes(int rows, int budget);
-// decode attention with optional rotation of q on load (rope_theta > 0);
+// decode attention with optional rotation of q on load (rope non-null);
 // gate (nullable, laid out as out with sequence stride gs): the output gate
 hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* k,
                                  const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                                  const Positions& pos, int batch, int tq, int budget, float scale,
                                  uint16_t* out, int64_t os, float* lse, const uint16_t* gate, int64_t gs,
-                                 void* ws, double rope_theta, hipStream_t stream);
+                                 void* ws, const qsa_rope_t* rope, hipStream_t stream);
 
 // fused decode index-select (scores + selection of the decode rows); the
 // workspace must be zero before its first use and is left zero by each call
@@ -152,7 +152,7 @@ struct DecodeAppend {
     int64_t kis;                 // completes (p % 4 == 3) is compressed into kbar[b][p / 4]
     uint16_t* kbar;
     int64_t kbs;
-    double rope_theta;
+    qsa_rope_t rope;             // rotary parameters of the K rows
 };
 
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,

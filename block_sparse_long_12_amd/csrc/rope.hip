@@ -20,10 +20,10 @@ __global__ __launch_bounds__(256) void rope_kernel(const uint16_t* x, int64_t xs
 
 hipError_t launch_rope(const uint16_t* x, int64_t xs, int64_t xt, uint16_t* y, int64_t ys,
                        int64_t yt, int batch, int n_tokens, int n_heads, const Positions& pos0,
-                       double theta, bool in_place, hipStream_t stream) {
+                       const qsa_rope_t& rope, bool in_place, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(batch) * n_tokens;
     if (rows == 0) return hipSuccess;
-    const InvFreq inv = make_inv_freq(theta);
+    const InvFreq inv = make_inv_freq(rope);
     const unsigned grid = static_cast<unsigned>((rows + 3) / 4);
     hipLaunchKernelGGL(rope_kernel, dim3(grid), dim3(256), 0, stream, x, xs, xt, y, ys, yt, batch,
                        n_tokens, n_heads, pos0, inv, in_place);

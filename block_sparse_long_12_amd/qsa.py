@@ -32,13 +32,36 @@ _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
 _sz = ctypes.c_size_t
 
+
+class Rope(ctypes.Structure):
+    """Rotary parameters (qsa_rope_t): theta, and static YaRN with scale factor
+    yarn_factor over yarn_original_max positions (yarn_factor 1: plain rotary)."""
+    _fields_ = [("theta", ctypes.c_double), ("yarn_factor", ctypes.c_double), ("yarn_original_max", ctypes.c_int64)]
+
+
+def rope_params(theta: float = ROPE_THETA, yarn_factor: float = 1.0, yarn_original_max: int = 0) -> Rope:
+    return Rope(float(theta), float(yarn_factor), int(yarn_original_max))
+
+
+# model card, "Processing Ultra-Long Texts": static YaRN for contexts past 262144
+YARN = rope_params(ROPE_THETA, 4.0, 262144)
+_rope_p = ctypes.POINTER(Rope)
+
+
+def _rope_arg(rope: Rope | None):
+    if rope is None:
+        return None
+    if not isinstance(rope, Rope):
+        raise QSAError("rope must be a qsa.Rope (see rope_params)")
+    return ctypes.byref(rope)
+
 _SIGNATURES = {
     "qsa_abi_version": (_i32, []),
     "qsa_get_dims": (_i32, [_c_p]),
     "qsa_status_string": (ctypes.c_char_p, [_i32]),
     "qsa_last_error": (ctypes.c_char_p, []),
     "qsa_rope_apply": (_i32, [_c_p, _i64, _i64, _c_p, _i64, _i64, _i32, _i32, _i32, _c_p,
-                              ctypes.c_double, _c_p]),
+                              _rope_p, _c_p]),
     "qsa_compress_block_keys": (_i32, [_c_p, _i64, _i32, _i32, _i32, _c_p, _i64, _c_p]),
     "qsa_index_scores": (_i32, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _c_p, _i64, _i64, _c_p]),
     "qsa_select_workspace_bytes": (_sz, [_i32, _i32, _i32]),
@@ -56,7 +79,7 @@ _SIGNATURES = {
                                        _i64, _c_p, _sz, _c_p]),
     "qsa_decode_step_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "qsa_decode_step": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _i64, _c_p, _i64,
-                               _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, ctypes.c_double, _c_p, _i64,
+                               _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, _rope_p, _c_p, _i64,
                                _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p, _sz, _c_p]),
 }
 
@@ -85,7 +108,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        if L.qsa_abi_version() != 1:
+        if L.qsa_abi_version() != 2:
             raise QSAError("libqsa ABI version mismatch")
         _LIB = L
     return _LIB
@@ -149,9 +172,11 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, inner: tuple[int, ...]
 # ------------------------------------------------------------------ steps
 
 def rope_apply(x: torch.Tensor, pos0, out: torch.Tensor | None = None,
-               theta: float = ROPE_THETA, stream=None) -> torch.Tensor:
+               rope: Rope | None = None, stream=None) -> torch.Tensor:
     """Rotate dims 0..63 of x [B, T, H, 256] (bf16) at positions pos0[b] + t.
-    out=None rotates in place; otherwise out [B, T, H, 256] receives the result."""
+    out=None rotates in place; otherwise out [B, T, H, 256] receives the result.
+    rope: rotary parameters (None: theta 1e7, no YaRN; YARN: the model card's
+    static YaRN)."""
     _need(x, "x", torch.bfloat16, (D,))
     B, T, H = x.shape[0], x.shape[1], x.shape[2]
     y = x if out is None else out
@@ -160,7 +185,7 @@ def rope_apply(x: torch.Tensor, pos0, out: torch.Tensor | None = None,
         if tuple(out.shape) != tuple(x.shape):
             raise QSAError("out must have the shape of x")
     _check(lib().qsa_rope_apply(_ptr(x), x.stride(0), x.stride(1), _ptr(y), y.stride(0), y.stride(1),
-                                B, T, H, _positions(pos0, B), float(theta), _stream(stream)),
+                                B, T, H, _positions(pos0, B), _rope_arg(rope), _stream(stream)),
            "qsa_rope_apply")
     return y
 
@@ -328,7 +353,7 @@ class PrefillBuffers:
 
 
 def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0: int, budget: int,
-                  out, lse, bufs: PrefillBuffers, q_rot, stream=None, gate=None):
+                  out, lse, bufs: PrefillBuffers, q_rot, stream=None, gate=None, rope: Rope | None = None):
     """One QSA layer over tq new tokens of every sequence, all at q_pos0.
 
     q_raw [B, tq, 24, 256] and k_new_raw [B, tq, 2, 256] are unrotated; the
@@ -336,12 +361,12 @@ def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0
     are expected in v_cache already, k_idx rows in k_idx).  Steps: rotary
     (Q -> q_rot, K -> cache), compress the blocks the chunk completes, then per
     query chunk the fused index-select, then attention (with the optional
-    output gate [B, tq, 24, 256]).
+    output gate [B, tq, 24, 256]).  rope: rotary parameters (see rope_apply).
     """
     B, tq = q_raw.shape[0], q_raw.shape[1]
     pos = [q_pos0] * B
-    rope_apply(q_raw, pos, out=q_rot, stream=stream)
-    rope_apply(k_new_raw, pos, out=k_cache[:, q_pos0:q_pos0 + tq], stream=stream)
+    rope_apply(q_raw, pos, out=q_rot, rope=rope, stream=stream)
+    rope_apply(k_new_raw, pos, out=k_cache[:, q_pos0:q_pos0 + tq], rope=rope, stream=stream)
     b0, b1 = q_pos0 // BLOCK, (q_pos0 + tq) // BLOCK
     compress_block_keys(k_idx, b0, b1, kbar, stream=stream)
     for c0 in range(0, tq, bufs.chunk):
@@ -396,7 +421,7 @@ def _decode_positions(pos, B: int) -> list[int]:
 
 def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,
                 out, lse, scores, sel, workspace, stream=None, scale: float = 1.0 / math.sqrt(D),
-                v_new=None, k_idx_new=None, gate=None):
+                v_new=None, k_idx_new=None, gate=None, rope: Rope | None = None):
     """One decode step through the single qsa_decode_step call, for tq new
     tokens per sequence (tq = q_raw.shape[1], 1 .. 4): token t of sequence b
     at position pos[b] + t (pos an int: the same for all sequences).
@@ -406,7 +431,8 @@ def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, bud
     k_idx_new [B, tq, 128] (optional) are appended to v_cache / k_idx; without
     them those rows are expected in place. kbar must hold the blocks before
     pos[b] // 4; the step writes the key of every block a new token completes
-    (from k_idx). scores [B, tq, ld], sel [B, tq, budget], out [B, 24, 256]
+    (from k_idx). rope: rotary parameters of q and the new K rows (see
+    rope_apply). scores [B, tq, ld], sel [B, tq, budget], out [B, 24, 256]
     (tq = 1) or [B, tq, 24, 256], lse [B, 24] or [B, tq, 24], gate (optional
     output gate) like out. workspace comes from decode_step_workspace(B,
     budget, tq=tq).
@@ -455,7 +481,7 @@ def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, bud
     _check(lib().qsa_decode_step(_ptr(q_raw), q_raw.stride(0), _ptr(k_new_raw), _ptr(v_new), k_new_raw.stride(0),
                                  _ptr(q_idx), q_idx.stride(0), _ptr(k_idx_new), _ptr(k_cache), _ptr(v_cache),
                                  k_cache.stride(0), _ptr(k_idx), 0 if k_idx is None else k_idx.stride(0),
-                                 _ptr(kbar), kbar.stride(0), p, B, tq, budget, float(scale), ROPE_THETA,
+                                 _ptr(kbar), kbar.stride(0), p, B, tq, budget, float(scale), _rope_arg(rope),
                                  _ptr(scores), scores.shape[-1], scores.stride(0), _ptr(sel), sel.stride(0),
                                  _ptr(out), out.stride(0), _ptr(lse), g_ptr, g_stride, _ptr(workspace),
                                  workspace.numel(), _stream(stream)),
@@ -465,15 +491,15 @@ def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, bud
 
 def decode_step_primitives(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,
                            out, lse, scores, sel, workspace, q_rot, stream=None, v_new=None, k_idx_new=None,
-                           gate=None):
+                           gate=None, rope: Rope | None = None):
     """The same decode step as a chain of the primitive calls (rotary, row
     copies, block compression, scores, selection, attention); workspace from
     decode_workspace(B, budget, tq=tq)."""
     B, tq = q_raw.shape[0], q_raw.shape[1]
     p = _decode_positions(pos, B)
-    rope_apply(q_raw, p, out=q_rot, stream=stream)
+    rope_apply(q_raw, p, out=q_rot, rope=rope, stream=stream)
     for b in range(B):
-        rope_apply(k_new_raw[b:b + 1], [p[b]], out=k_cache[b:b + 1, p[b]:p[b] + tq], stream=stream)
+        rope_apply(k_new_raw[b:b + 1], [p[b]], out=k_cache[b:b + 1, p[b]:p[b] + tq], rope=rope, stream=stream)
         if v_new is not None:
             v_cache[b, p[b]:p[b] + tq].copy_(v_new[b])
         if k_idx_new is not None:

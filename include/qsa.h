@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 #define QSA_MAX_BATCH 256
 #define QSA_MAX_BUDGET 2048
 
@@ -75,20 +75,43 @@ const char*  qsa_status_string(qsa_status_t s);
 const char*  qsa_last_error(void);
 
 /*
+ * Rotary parameters (model card, "Processing Ultra-Long Texts",
+ * rope_parameters): rope_theta (1e7 for this model) and optional static YaRN
+ * (rope_type "yarn": scale factor s over original_max_position_embeddings L;
+ * the card gives s = 4, L = 262144 for contexts past 262144, s = 2 for about
+ * 512K).  Passed by HOST pointer, read during the call; NULL means
+ * {1e7, 1, 0}.  theta must be finite and > 1, yarn_factor finite and >= 1
+ * (1: plain rotary), yarn_original_max >= 1 when yarn_factor > 1; otherwise
+ * QSA_ERR_INVALID_ARGUMENT.
+ */
+typedef struct {
+    double  theta;
+    double  yarn_factor;
+    int64_t yarn_original_max;
+} qsa_rope_t;
+
+/*
  * Step 0 -- rotary embedding (model card, "Processing Ultra-Long Texts",
  * rope_parameters: rope_theta 1e7, partial_rotary_factor 0.25, i.e. the first
  * 64 of 256 dims; mRoPE sections [11, 11, 10] reduce to 1-D rotary for text).
  * For every row (b, i) and head h of x [B][n_tokens][n_heads][256]:
- * pair (d, d + 32), d < 32, is turned by angle p * theta^(-d/32) with
- * p = pos0[b] + i:  (a, c) -> (a cos - c sin, c cos + a sin).  Angles, sines
- * and the rotation are evaluated in float64, the result rounded once to bf16;
+ * pair (d, d + 32), d < 32, is turned by angle p * w_d with
+ * p = pos0[b] + i:  (a, c) -> (a cos - c sin, c cos + a sin) * m.  Plain
+ * rotary: w_d = theta^(-d/32), m = 1.  Static YaRN (YaRN paper, Peng et al.
+ * 2023, NTK-by-parts interpolation and attention temperature; the same table
+ * at every length): pair d turns L w_d / (2 pi) times over the original
+ * context; with i(rho) = 32 ln(L / (2 pi rho)) / ln theta the pair index
+ * turning rho times, lo = floor(i(32)) (>= 0), hi = ceil(i(1)) (<= 63),
+ * g_d = clamp((d - lo) / (hi - lo), 0, 1): w_d becomes
+ * (w_d / s) g_d + w_d (1 - g_d), and m = 1 + 0.1 ln s.  Angles, sines and
+ * the rotation are evaluated in float64, the result rounded once to bf16;
  * dims 64..255 are copied unchanged.  y may equal x (same strides) for an
  * in-place update; otherwise x and y must not overlap.
  */
 qsa_status_t qsa_rope_apply(const uint16_t* x, int64_t x_seq_stride, int64_t x_tok_stride,
                             uint16_t* y, int64_t y_seq_stride, int64_t y_tok_stride,
                             int32_t batch, int32_t n_tokens, int32_t n_heads,
-                            const int32_t* pos0, double rope_theta, hipStream_t stream);
+                            const int32_t* pos0, const qsa_rope_t* rope, hipStream_t stream);
 
 /*
  * Step 1 -- block keys (blog, "Attention: GDN + QSA": aggregate into
@@ -252,7 +275,8 @@ qsa_status_t qsa_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_st
  *  - scores the candidate blocks of each row and selects as
  *    qsa_index_select_decode does;
  *  - attends with q (unrotated; rotated on load exactly as qsa_rope_apply
- *    would) over each row's selection and own block.
+ *    would with the same rope parameters) over each row's selection and own
+ *    block.
  * k_idx NULL: no indexer-key append and no compression.  k_new / v_new share
  * kv_new_seq_stride; k_cache and v_cache share kv_seq_stride; k_idx is
  * [B][L][128] with k_idx_seq_stride.  Equals the chain rope_apply + row
@@ -270,7 +294,7 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
                              uint16_t* k_idx, int64_t k_idx_seq_stride,
                              uint16_t* kbar, int64_t kbar_seq_stride,
                              const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
-                             float softmax_scale, double rope_theta,
+                             float softmax_scale, const qsa_rope_t* rope,
                              float* scores, int64_t scores_ld, int64_t scores_seq_stride,
                              int32_t* sel, int64_t sel_seq_stride,
                              uint16_t* out, int64_t out_seq_stride, float* lse,

@@ -47,9 +47,9 @@ def score_bound(q_idx_bits: np.ndarray, kbar_bits: np.ndarray) -> np.ndarray:
 class DevicePrefill:
     """A prefill workload on the device, run through the HIP path."""
 
-    def __init__(self, x: I.Inputs):
+    def __init__(self, x: I.Inputs, rope=None):
         wl = x.workload
-        self.x, self.wl = x, wl
+        self.x, self.wl, self.rope = x, wl, rope
         B, L, ctx, T = wl.batch, wl.length, wl.ctx, wl.tq
         dev = "cuda"
         self.q_raw = x.q.to(dev)
@@ -59,7 +59,7 @@ class DevicePrefill:
         self.v_cache = x.v.to(dev)
         self.k_cache = x.k.to(dev)
         if ctx > 0:     # the cached prefix is stored rotated
-            qsa.rope_apply(self.k_cache[:, :ctx], [0] * B)
+            qsa.rope_apply(self.k_cache[:, :ctx], [0] * B, rope=rope)
         self.kbar = torch.zeros((B, max(1, L // 4), 128), dtype=torch.bfloat16, device=dev)
         if ctx // 4 > 0:
             qsa.compress_block_keys(self.k_idx, 0, ctx // 4, self.kbar)
@@ -71,7 +71,7 @@ class DevicePrefill:
     def run(self, gate=None):
         qsa.prefill_layer(self.q_raw, self.k_new, self.q_idx, self.k_idx, self.k_cache, self.v_cache,
                           self.kbar, self.wl.ctx, self.wl.budget, self.out, self.lse, self.bufs, self.q_rot,
-                          gate=gate)
+                          gate=gate, rope=self.rope)
         torch.cuda.synchronize()
 
 
@@ -107,9 +107,10 @@ class DeviceDecode:
         torch.cuda.synchronize()
 
 
-def oracle_layer(x: I.Inputs) -> O.OracleLayer:
+def oracle_layer(x: I.Inputs, yarn: O.Yarn | None = None) -> O.OracleLayer:
     B = O.bits
-    return O.OracleLayer(B(x.q), B(x.q_idx), B(x.k), B(x.v), B(x.k_idx), x.q_pos0, x.workload.budget)
+    return O.OracleLayer(B(x.q), B(x.q_idx), B(x.k), B(x.v), B(x.k_idx), x.q_pos0, x.workload.budget,
+                         yarn=yarn)
 
 
 def compare_rows(layer: O.OracleLayer, x: I.Inputs, rows, gpu_scores, gpu_sel, gpu_out, gpu_lse):

@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_dims_and_strings(L):
     assert qsa.dims() == dict(block=4, hq=24, hkv=2, d=256, rot_dim=64, hi=4, di=128)
-    assert L.qsa_abi_version() == 1
+    assert L.qsa_abi_version() == 2
     for s in range(5):
         assert L.qsa_status_string(s)
 
@@ -64,18 +64,28 @@ def _err(L):
     return L.qsa_last_error().decode()
 
 
+def _rope(theta, factor=1.0, orig=0):
+    return ctypes.byref(qsa.rope_params(theta, factor, orig))
+
+
 def test_rope_validation(L):
     p = _pos(0)
-    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 0, 1, 1, p, 1e7, None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 0, 1, 1, p, None, None) == INVALID
     assert "batch" in _err(L)
-    assert L.qsa_rope_apply(NULL, 0, 256, FAKE, 0, 256, 1, 1, 1, p, 1e7, None) == INVALID
-    assert L.qsa_rope_apply(FAKE + 2, 0, 256, FAKE, 0, 256, 1, 1, 1, p, 1e7, None) == INVALID
-    assert L.qsa_rope_apply(FAKE, 0, 255, FAKE, 0, 256, 1, 1, 1, p, 1e7, None) == INVALID
-    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 2, p, 1e7, None) == INVALID   # stride < heads*256
-    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 1, p, 0.5, None) == INVALID
-    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 1, _pos(-3), 1e7, None) == INVALID
-    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 1, None, 1e7, None) == INVALID
-    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 512, 1, 1, 1, p, 1e7, None) == INVALID   # in place, strides differ
+    assert L.qsa_rope_apply(NULL, 0, 256, FAKE, 0, 256, 1, 1, 1, p, None, None) == INVALID
+    assert L.qsa_rope_apply(FAKE + 2, 0, 256, FAKE, 0, 256, 1, 1, 1, p, None, None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 255, FAKE, 0, 256, 1, 1, 1, p, None, None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 2, p, None, None) == INVALID   # stride < heads*256
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 1, p, _rope(0.5), None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 1, _pos(-3), None, None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 1, None, None, None) == INVALID
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 512, 1, 1, 1, p, None, None) == INVALID   # in place, strides differ
+    # YaRN parameters: factor below 1, NaN factor, no original length
+    for bad in (_rope(1e7, 0.5, 262144), _rope(1e7, float("nan"), 262144), _rope(1e7, 4.0, 0),
+                _rope(float("inf"))):
+        assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 1, 1, p, bad, None) == INVALID
+    # zero tokens with valid parameters launches nothing and succeeds
+    assert L.qsa_rope_apply(FAKE, 0, 256, FAKE, 0, 256, 1, 0, 1, p, _rope(1e7, 4.0, 262144), None) == 0
 
 
 def test_compress_validation(L):
@@ -181,10 +191,10 @@ def test_decode_step_validation(L):
     ws_need = L.qsa_decode_step_workspace_bytes(B, 1, budget)
     assert ws_need > 0 and L.qsa_decode_step_workspace_bytes(0, 1, budget) == 0
 
-    def call(v_new=FAKE, k_idx_new=FAKE, k_idx=FAKE, k_idx_stride=9001 * 128, ws=ws_need, tq=1):
+    def call(v_new=FAKE, k_idx_new=FAKE, k_idx=FAKE, k_idx_stride=9001 * 128, ws=ws_need, tq=1, rope=None):
         return L.qsa_decode_step(FAKE, tq * 24 * 256, FAKE, v_new, tq * 2 * 256, FAKE, tq * 4 * 128, k_idx_new,
                                  FAKE, FAKE, 9004 * 512, k_idx, k_idx_stride, FAKE, 2252 * 128,
-                                 p, B, tq, budget, 0.0625, 1.0e7, FAKE, ld, tq * ld, FAKE, tq * budget, FAKE,
+                                 p, B, tq, budget, 0.0625, rope, FAKE, ld, tq * ld, FAKE, tq * budget, FAKE,
                                  tq * 24 * 256, NULL, NULL, 0, FAKE, ws, None)
 
     assert call(k_idx=NULL) == INVALID
@@ -196,3 +206,5 @@ def test_decode_step_validation(L):
     assert call(ws=ws_need - 1) == WORKSPACE
     assert call(tq=5) == INVALID and "tq" in L.qsa_last_error().decode()
     assert call(tq=4, k_idx_stride=9001 * 128) == INVALID          # rows 9001 .. 9003 out of reach
+    assert call(rope=_rope(1e7, 0.9, 262144)) == INVALID and "yarn" in L.qsa_last_error().decode()
+    assert call(rope=_rope(1.0)) == INVALID

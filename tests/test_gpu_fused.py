@@ -267,14 +267,17 @@ def test_decode_step_appends_rows_and_compresses(pos, budget):
 
 # ---------------------------------------------------------------- several decode tokens per sequence
 
-@pytest.mark.parametrize("pos,tq,budget", [([4097, 9000, 70001], 4, 512), ([4099, 8191], 2, 512),
-                                           ([131069, 131072], 3, 512), ([1, 6], 4, 8)])
-def test_multi_token_decode_step_matches_primitives(pos, tq, budget):
+@pytest.mark.parametrize("pos,tq,budget,yarn", [([4097, 9000, 70001], 4, 512, False), ([4099, 8191], 2, 512, False),
+                                                ([131069, 131072], 3, 512, False), ([1, 6], 4, 8, False),
+                                                ([262143, 300001], 3, 512, True), ([5, 9000], 2, 64, True)])
+def test_multi_token_decode_step_matches_primitives(pos, tq, budget, yarn):
     """tq new tokens per sequence in one step (one pass over the block keys
     scores every token) equal the primitive chain bit for bit: the appended
     rows, the key of every block a new token completes (a later token of the
-    same step scores it), scores, selections, outputs and LSEs."""
-    say(f"multi-token decode_step pos={pos} tq={tq} budget={budget}")
+    same step scores it), scores, selections, outputs and LSEs.  yarn: the
+    step rotates q and the new K rows with the static-YaRN table."""
+    say(f"multi-token decode_step pos={pos} tq={tq} budget={budget} yarn={yarn}")
+    rope = qsa.YARN if yarn else None
     B = len(pos)
     L = max(pos) + tq
     dev = "cuda"
@@ -293,7 +296,7 @@ def test_multi_token_decode_step_matches_primitives(pos, tq, budget):
     outs = []
     for fused in (False, True):
         kc, v, ki = k_cpu.to(dev), v_cpu.to(dev), ki_cpu.to(dev)
-        qsa.rope_apply(kc, [0] * B)
+        qsa.rope_apply(kc, [0] * B, rope=rope)
         kb = torch.full((B, L // 4 + 1, 128), 9.0, dtype=bf, device=dev)
         for b in range(B):
             if pos[b] // 4:
@@ -306,12 +309,12 @@ def test_multi_token_decode_step_matches_primitives(pos, tq, budget):
             ws = qsa.decode_step_workspace(B, budget, tq=tq)
             for _ in range(2):                        # the second call reuses the workspace
                 qsa.decode_step(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel, ws,
-                                v_new=v_new, k_idx_new=k_idx_new, gate=gate)
+                                v_new=v_new, k_idx_new=k_idx_new, gate=gate, rope=rope)
             assert int(ws[:B * tq * (4096 + 16) * 4].count_nonzero()) == 0
         else:
             qsa.decode_step_primitives(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel,
                                        qsa.decode_workspace(B, budget, tq=tq), torch.empty_like(q_raw),
-                                       v_new=v_new, k_idx_new=k_idx_new, gate=gate)
+                                       v_new=v_new, k_idx_new=k_idx_new, gate=gate, rope=rope)
         torch.cuda.synchronize()
         per = []
         for b in range(B):

@@ -34,21 +34,32 @@ def _lib():
 
 # ------------------------------------------------------------------ step 0
 
+ROPES = {
+    "plain": (None, None),
+    "yarn4": (qsa.YARN, O.Yarn(factor=4.0, original_max=262144)),
+    "yarn2_theta5e5": (qsa.rope_params(5e5, 2.0, 32768), O.Yarn(factor=2.0, original_max=32768)),
+}
+
+
+@pytest.mark.parametrize("rope", list(ROPES))
 @pytest.mark.parametrize("heads", [24, 2])
-def test_rope_matches_oracle(heads):
-    say(f"rope heads={heads}")
+def test_rope_matches_oracle(heads, rope):
+    say(f"rope heads={heads} {rope}")
+    dev_rope, yarn = ROPES[rope]
+    theta = 5e5 if rope == "yarn2_theta5e5" else O.ROPE_THETA
     x = _rand_bf16((2, 37, heads, 256), 1 + heads)
     pos0 = [0, 1048000]
     xd = x.cuda()
     yd = torch.empty_like(xd)
-    qsa.rope_apply(xd, pos0, out=yd)
+    qsa.rope_apply(xd, pos0, out=yd, rope=dev_rope)
     got = bits(yd)
-    ref = np.stack([O.rope_rotate(bits(x[b]), np.arange(37) + pos0[b]) for b in range(2)])
+    ref = np.stack([O.rope_rotate(bits(x[b]), np.arange(37) + pos0[b], theta=theta, yarn=yarn)
+                    for b in range(2)])
     assert np.array_equal(got[..., 64:], bits(x)[..., 64:])
     ulp = bf16_ulp_diff(got, ref)
     assert ulp.max() <= 1 and np.mean(ulp == 0) >= 0.9999, (ulp.max(), np.mean(ulp == 0))
     # in place equals out of place
-    qsa.rope_apply(xd, pos0)
+    qsa.rope_apply(xd, pos0, rope=dev_rope)
     assert np.array_equal(bits(xd), got)
 
 
@@ -375,12 +386,15 @@ def test_consecutive_decode_steps_match_the_oracle_rows():
                  lambda b, t: res[(b, t)][2], lambda b, t: res[(b, t)][3])
 
 
-def test_multi_token_decode_steps_match_the_oracle_rows():
+@pytest.mark.parametrize("ctx,n_steps,yarn", [(30001, 3, False), (270001, 2, True)],
+                         ids=["ctx30001", "ctx270001_yarn"])
+def test_multi_token_decode_steps_match_the_oracle_rows(ctx, n_steps, yarn):
     """Decode steps of 3 new tokens each (the shape of speculative
     verification), run back to back, give the oracle's causal QSA rows for
     every token; blocks completed inside a step are scored by its later
-    tokens."""
-    B, ctx, tq, n_steps, budget = 2, 30001, 3, 3, 512
+    tokens.  With yarn: the model card's static YaRN rotary past 262144."""
+    B, tq, budget = 2, 3, 512
+    dev_rope, o_yarn = (qsa.YARN, O.Yarn()) if yarn else (None, None)
     S = tq * n_steps
     wl = I.custom_workload("prefill", batch=B, ctx=ctx, tq=S, budget=budget, n_needles=4, seed=47)
     say(f"multi-token decode steps {wl.name}")
@@ -391,7 +405,7 @@ def test_multi_token_decode_steps_match_the_oracle_rows():
     v = torch.zeros_like(kc)
     ki = torch.zeros((B, L, 128), dtype=torch.bfloat16, device=dev)
     kc[:, :ctx] = x.k[:, :ctx].to(dev)
-    qsa.rope_apply(kc[:, :ctx], [0] * B)
+    qsa.rope_apply(kc[:, :ctx], [0] * B, rope=dev_rope)
     v[:, :ctx] = x.v[:, :ctx].to(dev)
     ki[:, :ctx] = x.k_idx[:, :ctx].to(dev)
     kb = torch.zeros((B, L // 4 + 1, 128), dtype=torch.bfloat16, device=dev)
@@ -409,7 +423,7 @@ def test_multi_token_decode_steps_match_the_oracle_rows():
         qsa.decode_step(x.q[:, sl].contiguous().to(dev), x.k[:, t0:t0 + tq].contiguous().to(dev),
                         x.q_idx[:, sl].contiguous().to(dev), ki, kc, v, kb, t0, budget, out, lse, scores, sel, ws,
                         v_new=x.v[:, t0:t0 + tq].contiguous().to(dev),
-                        k_idx_new=x.k_idx[:, t0:t0 + tq].contiguous().to(dev))
+                        k_idx_new=x.k_idx[:, t0:t0 + tq].contiguous().to(dev), rope=dev_rope)
         torch.cuda.synchronize()
         for b in range(B):
             for t in range(tq):
@@ -417,7 +431,7 @@ def test_multi_token_decode_steps_match_the_oracle_rows():
                 res[(b, p)] = (scores[b, t, :p // 4].cpu().numpy(), sel[b, t].cpu().numpy(),
                                out[b, t].float().cpu().numpy(), lse[b, t].cpu().numpy())
     rows = sorted(res)
-    compare_rows(oracle_layer(x), x, rows, lambda b, t: res[(b, t)][0], lambda b, t: res[(b, t)][1],
+    compare_rows(oracle_layer(x, o_yarn), x, rows, lambda b, t: res[(b, t)][0], lambda b, t: res[(b, t)][1],
                  lambda b, t: res[(b, t)][2], lambda b, t: res[(b, t)][3])
 
 
@@ -479,3 +493,22 @@ def test_gated_prefill_layer_end_to_end():
     rows = [(0, 2000 + i) for i in range(0, 300, 7)]
     compare_rows(layer, x, rows, None, lambda b, t: sel[b, t - 2000], lambda b, t: out[b, t - 2000],
                  lambda b, t: lse[b, t - 2000])
+
+
+# ------------------------------------------------------------------ static YaRN
+
+def test_yarn_prefill_layer_end_to_end():
+    """A prefill chunk past 262144 positions with the model card's static
+    YaRN (factor 4 over 262144) against the oracle's YaRN rows under the
+    end-to-end protocol; the cached prefix is rotated with the same table."""
+    wl = I.custom_workload("prefill", batch=1, ctx=263000, tq=200, budget=512, n_needles=4, seed=95, chunk=128)
+    say(f"yarn prefill layer {wl.name}")
+    x = I.make_inputs(wl)
+    dp = DevicePrefill(x, rope=qsa.YARN)
+    dp.run()
+    sel = dp.bufs.sel.cpu().numpy()
+    out = dp.out.float().cpu().numpy()
+    lse = dp.lse.cpu().numpy()
+    rows = [(0, 263000 + i) for i in range(0, 200, 9)]
+    compare_rows(oracle_layer(x, O.Yarn()), x, rows, None, lambda b, t: sel[b, t - 263000],
+                 lambda b, t: out[b, t - 263000], lambda b, t: lse[b, t - 263000])
