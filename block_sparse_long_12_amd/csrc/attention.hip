@@ -56,9 +56,19 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Paged caches: the sequence's block-table row, the page size and the
+// page of the query position (the row that stands in for empty slots).
+struct KvPages {
+    const int32_t* tbl;
+    int shift;
+    int n_pages;
+    int pp;
+};
+
+template <bool kPaged>
 __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                                            const int32_t* __restrict__ selrow, int cb, int blk_end, int p,
-                                           Chunk& ch) {
+                                           const KvPages& kp, Chunk& ch) {
     const int lane = threadIdx.x & 63;
     const int c16 = lane & 15;
     const int G = lane >> 4;
@@ -76,7 +86,18 @@ __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ kg, cons
     const int j = (slot_blk < blk_end) ? jl : -1;
     const int n = kBlock * j + (c16 & 3);
     const bool valid = (j >= 0) && (j <= p / kBlock) && (n <= p);
-    const int64_t row = valid ? n : p;
+    int64_t row = valid ? n : p;
+    if constexpr (kPaged) {
+        // page of each of the 4 blocks (wave-uniform: scalar loads); a slot
+        // that holds no legal block reads the query's own row, in page pp
+        auto page = [&](int sb) {
+            const int tok = (sb >= 0 && sb <= p / kBlock) ? kBlock * sb : p;
+            return min(max(kp.tbl[tok >> kp.shift], 0), kp.n_pages - 1);
+        };
+        const int g0 = page(s0), g1 = page(s1), g2 = page(s2), g3 = page(s3);
+        const int gl = (q4 == 0) ? g0 : (q4 == 1) ? g1 : (q4 == 2) ? g2 : g3;
+        row = (static_cast<int64_t>(valid ? gl : kp.pp) << kp.shift) | (row & ((int64_t{1} << kp.shift) - 1));
+    }
     const uint16_t* kr = kg + row * (kHkv * kD);
     const uint16_t* vr = vg + row * (kHkv * kD);
 #pragma unroll
@@ -148,7 +169,8 @@ __device__ __forceinline__ void attend_chunk(const Chunk& ch, const bf16x8_t (&q
 }
 
 // Attend over sel[blk_begin .. blk_end) for the query at position p.
-// kg / vg point at KV head g of the sequence (token stride 2 * 256).
+// kg / vg point at KV head g of the sequence (token stride 2 * 256), or of
+// the page pool when kPaged.
 // `cur` must hold the loads of the first chunk (issued by the caller, so they
 // can overlap the query set-up).  Chunks are processed in statically unrolled
 // groups of kUnroll with two named buffers: inside a group the code is
@@ -156,11 +178,11 @@ __device__ __forceinline__ void attend_chunk(const Chunk& ch, const bf16x8_t (&q
 // next chunk's rows stay in flight (a loop-carried pipeline makes the
 // compiler drain all loads at every loop head).  Steps past the end re-read
 // the last chunk's rows (cache hits) and are skipped.
-template <int kUnroll>
+template <int kUnroll, bool kPaged>
 __device__ __forceinline__ void attend_blocks(const uint16_t* __restrict__ kg,
                                               const uint16_t* __restrict__ vg,
                                               const int32_t* __restrict__ selrow, int blk_begin,
-                                              int blk_end, int p, const bf16x8_t (&qf)[8],
+                                              int blk_end, int p, const KvPages& kp, const bf16x8_t (&qf)[8],
                                               float c, WaveState& st, uint16_t* vt, Chunk& cur) {
     const int last = blk_begin + (blk_end - 1 - blk_begin) / 4 * 4;      // first block of the last chunk
     Chunk other;
@@ -170,9 +192,9 @@ __device__ __forceinline__ void attend_blocks(const uint16_t* __restrict__ kg,
             const int c0 = cb + 4 * u;
             const int c1 = c0 + 4;
             const int c2 = c1 + 4;
-            load_chunk(kg, vg, selrow, min(c1, last), blk_end, p, other);
+            load_chunk<kPaged>(kg, vg, selrow, min(c1, last), blk_end, p, kp, other);
             if (c0 < blk_end && cur.vmask != 0ull) attend_chunk(cur, qf, c, st, vt);
-            load_chunk(kg, vg, selrow, min(c2, last), blk_end, p, cur);
+            load_chunk<kPaged>(kg, vg, selrow, min(c2, last), blk_end, p, kp, cur);
             if (c1 < blk_end && other.vmask != 0ull) attend_chunk(other, qf, c, st, vt);
         }
     }
@@ -253,12 +275,33 @@ __device__ __forceinline__ void init_state(WaveState& st) {
 
 // ---------------------------------------------------------------- prefill
 
+// K / V of the sequence, or of the page pool: KV head g's base and the
+// sequence's pages
+template <bool kPaged>
+__device__ __forceinline__ void kv_bases(const uint16_t* k, const uint16_t* v, int64_t kvs, const PageMap& pm,
+                                         int b, int g, int p, const uint16_t*& kg, const uint16_t*& vg,
+                                         KvPages& kp) {
+    if constexpr (kPaged) {
+        kg = k + g * kD;
+        vg = v + g * kD;
+        kp.tbl = pm.table + b * pm.ts;
+        kp.shift = pm.shift;
+        kp.n_pages = pm.n_pages;
+        kp.pp = min(max(kp.tbl[p >> pm.shift], 0), pm.n_pages - 1);
+    } else {
+        kg = k + b * kvs + g * kD;
+        vg = v + b * kvs + g * kD;
+        kp = KvPages{};
+    }
+}
+
+template <bool kPaged>
 __global__ __launch_bounds__(128) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int64_t qs, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs, const int32_t* __restrict__ sel, int64_t sels,
     Positions pos0, int tq, int budget, float scale, float c, uint16_t* __restrict__ out,
     int64_t os, float* __restrict__ lse, int64_t lss, const uint16_t* __restrict__ gate, int64_t gs,
-    InvFreq inv, int rope_q) {
+    InvFreq inv, int rope_q, PageMap pm) {
     __shared__ uint16_t vt_all[2 * kVtElems];
     const int g = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -270,17 +313,18 @@ __global__ __launch_bounds__(128) void attn_prefill_kernel(
     const int head = g * kGroup + c16;
     const bool head_ok = c16 < kGroup;
 
-    const uint16_t* kg = k + b * kvs + g * kD;
-    const uint16_t* vg = v + b * kvs + g * kD;
+    const uint16_t *kg, *vg;
+    KvPages kp;
+    kv_bases<kPaged>(k, v, kvs, pm, b, g, p, kg, vg, kp);
     const int32_t* selrow = sel + b * sels + static_cast<int64_t>(i) * budget;
     Chunk first;
-    load_chunk(kg, vg, selrow, 0, budget, p, first);
+    load_chunk<kPaged>(kg, vg, selrow, 0, budget, p, kp, first);
     bf16x8_t qf[8];
     const uint16_t* qrow = q + b * qs + static_cast<int64_t>(i) * (kHq * kD);
     load_q_frags(qrow + (head_ok ? head : 0) * kD, head_ok, p, rope_q ? &inv : nullptr, qf);
     WaveState st;
     init_state(st);
-    attend_blocks<8>(kg, vg, selrow, 0, budget, p, qf, c, st, vt_all + g * kVtElems, first);
+    attend_blocks<8, kPaged>(kg, vg, selrow, 0, budget, p, kp, qf, c, st, vt_all + g * kVtElems, first);
 
     if (head_ok) {
         const float inv_l = 1.f / st.l;
@@ -305,14 +349,19 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
                                const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                                const Positions& pos0, int batch, int tq, int budget, float scale,
                                uint16_t* out, int64_t os, float* lse, int64_t lss, const uint16_t* gate,
-                               int64_t gs, hipStream_t stream) {
+                               int64_t gs, const PageMap* pm, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(batch) * tq;
     if (rows == 0) return hipSuccess;
     const float c = scale * 1.4426950408889634f;
     const InvFreq inv = make_inv_freq(qsa_rope_t{1.0e7, 1.0, 0});
-    hipLaunchKernelGGL(attn_prefill_kernel, dim3(static_cast<unsigned>(rows)), dim3(128), 0, stream,
-                       q, qs, k, v, kvs, sel, sels, pos0, tq, budget, scale, c, out, os, lse, lss, gate, gs, inv,
-                       0);
+    if (pm != nullptr)
+        hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(static_cast<unsigned>(rows)), dim3(128), 0, stream,
+                           q, qs, k, v, kvs, sel, sels, pos0, tq, budget, scale, c, out, os, lse, lss, gate, gs,
+                           inv, 0, *pm);
+    else
+        hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(static_cast<unsigned>(rows)), dim3(128), 0, stream,
+                           q, qs, k, v, kvs, sel, sels, pos0, tq, budget, scale, c, out, os, lse, lss, gate, gs,
+                           inv, 0, PageMap{});
     return hipGetLastError();
 }
 
@@ -340,11 +389,12 @@ size_t decode_workspace_bytes(int rows, int budget) {
     return static_cast<size_t>(rows) * s * kHq * (2 + kD) * sizeof(float);
 }
 
+template <bool kPaged>
 __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     const uint16_t* __restrict__ q, int64_t qs, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs, const int32_t* __restrict__ sel, int64_t sels,
     Positions pos, int budget, int tq, int n_split, int bps, float c, float* __restrict__ ws_ml,
-    float* __restrict__ ws_acc, InvFreq inv, int rope_q) {
+    float* __restrict__ ws_acc, InvFreq inv, int rope_q, PageMap pm) {
     __shared__ uint16_t vt_all[2 * kVtElems];
     const int g = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -362,18 +412,19 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
 
     const int blk_begin = s * bps;
     const int blk_end = min(budget, blk_begin + bps);
-    const uint16_t* kg = k + b * kvs + g * kD;
-    const uint16_t* vg = v + b * kvs + g * kD;
     // query loads first, then the selection and the first chunk; the rotary
     // angles are computed while those are in flight
     bf16x8_t qf[8];
     issue_q_frags(qrow + (head_ok ? head : 0) * kD, head_ok, qf);
+    const uint16_t *kg, *vg;
+    KvPages kp;
+    kv_bases<kPaged>(k, v, kvs, pm, b, g, p, kg, vg, kp);
     Chunk first;
-    load_chunk(kg, vg, selrow, blk_begin, blk_end, p, first);
+    load_chunk<kPaged>(kg, vg, selrow, blk_begin, blk_end, p, kp, first);
     if (rope_q) rotate_q_frags(rope_angle(p, inv), qf);
     WaveState st;
     init_state(st);
-    attend_blocks<2>(kg, vg, selrow, blk_begin, blk_end, p, qf, c, st, vt_all + g * kVtElems, first);
+    attend_blocks<2, kPaged>(kg, vg, selrow, blk_begin, blk_end, p, kp, qf, c, st, vt_all + g * kVtElems, first);
     if (head_ok) {
         const int64_t idx = (static_cast<int64_t>(r) * n_split + s) * kHq + head;
         if (G == 0) {
@@ -466,7 +517,7 @@ hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* 
                                  const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                                  const Positions& pos, int batch, int tq, int budget, float scale,
                                  uint16_t* out, int64_t os, float* lse, const uint16_t* gate, int64_t gs,
-                                 void* ws, const qsa_rope_t* rope, hipStream_t stream) {
+                                 void* ws, const qsa_rope_t* rope, const PageMap* pm, hipStream_t stream) {
     const int rows = batch * tq;
     if (rows == 0) return hipSuccess;
     int n_split, bps;
@@ -475,9 +526,14 @@ hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* 
     float* ws_acc = ws_ml + static_cast<size_t>(rows) * n_split * kHq * 2;
     const float c = scale * 1.4426950408889634f;
     const InvFreq inv = make_inv_freq(rope != nullptr ? *rope : qsa_rope_t{1.0e7, 1.0, 0});
-    hipLaunchKernelGGL(attn_decode_split_kernel, dim3(static_cast<unsigned>(rows * n_split)),
-                       dim3(128), 0, stream, q, qs, k, v, kvs, sel, sels, pos, budget, tq, n_split, bps,
-                       c, ws_ml, ws_acc, inv, rope != nullptr ? 1 : 0);
+    if (pm != nullptr)
+        hipLaunchKernelGGL(attn_decode_split_kernel<true>, dim3(static_cast<unsigned>(rows * n_split)),
+                           dim3(128), 0, stream, q, qs, k, v, kvs, sel, sels, pos, budget, tq, n_split, bps,
+                           c, ws_ml, ws_acc, inv, rope != nullptr ? 1 : 0, *pm);
+    else
+        hipLaunchKernelGGL(attn_decode_split_kernel<false>, dim3(static_cast<unsigned>(rows * n_split)),
+                           dim3(128), 0, stream, q, qs, k, v, kvs, sel, sels, pos, budget, tq, n_split, bps,
+                           c, ws_ml, ws_acc, inv, rope != nullptr ? 1 : 0, PageMap{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(static_cast<unsigned>(rows * kHq)), dim3(256),
@@ -491,7 +547,7 @@ hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
                               uint16_t* out, int64_t os, float* lse, const uint16_t* gate, int64_t gs,
                               void* ws, hipStream_t stream) {
     return launch_attn_decode_ex(q, qs, k, v, kvs, sel, sels, pos, batch, tq, budget, scale, out, os, lse,
-                                 gate, gs, ws, nullptr, stream);
+                                 gate, gs, ws, nullptr, nullptr, stream);
 }
 
 }  // namespace qsa

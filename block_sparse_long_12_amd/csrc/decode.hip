@@ -94,27 +94,34 @@ struct AppendArgs {
 // and attention runs in a later launch.  With several, a block an earlier new
 // token completes is a candidate of the later ones, so it runs in its own
 // launch (decode_append_kernel) before the scan.
-__device__ __forceinline__ void append_rows(const AppendArgs& ap, int b, int p0, int tq, int wave) {
+// With kPaged the caches are page pools: token rows and block-key rows go
+// through the block table (pm).
+template <bool kPaged>
+__device__ __forceinline__ void append_rows(const AppendArgs& ap, const PageMap& pm, int b, int p0, int tq,
+                                            int wave) {
     const int lane = threadIdx.x & 63;
+    // element offset of token x's row (row_elems per token) in its cache
+    auto tok_off = [&](int64_t seq_stride, int x, int row_elems) -> int64_t {
+        return kPaged ? phys_token(pm, b, x) * row_elems : b * seq_stride + static_cast<int64_t>(x) * row_elems;
+    };
     if (wave == 0 && ap.k_new != nullptr)
         for (int t = 0; t < tq; ++t)
-            rope_row_wave(ap.k_new + b * ap.kns + t * (kHkv * kD),
-                          ap.k_cache + b * ap.kvs + static_cast<int64_t>(p0 + t) * (kHkv * kD), kHkv,
-                          static_cast<double>(p0 + t), ap.inv, false);
+            rope_row_wave(ap.k_new + b * ap.kns + t * (kHkv * kD), ap.k_cache + tok_off(ap.kvs, p0 + t, kHkv * kD),
+                          kHkv, static_cast<double>(p0 + t), ap.inv, false);
     if (wave == 1 && ap.v_new != nullptr)        // 2 x 256 values per row: 16 B per lane
         for (int t = 0; t < tq; ++t)
-            *reinterpret_cast<uint4*>(ap.v_cache + b * ap.kvs + static_cast<int64_t>(p0 + t) * (kHkv * kD) + 8 * lane) =
+            *reinterpret_cast<uint4*>(ap.v_cache + tok_off(ap.kvs, p0 + t, kHkv * kD) + 8 * lane) =
                 *reinterpret_cast<const uint4*>(ap.v_new + b * ap.vns + t * (kHkv * kD) + 8 * lane);
     if (wave == 2 && ap.k_idx != nullptr && lane < kDi / 8) {
-        uint16_t* kr = ap.k_idx + b * ap.kis + 8 * lane;
+        uint16_t* kr = ap.k_idx + 8 * lane;
         const uint16_t* kn = ap.k_idx_new != nullptr ? ap.k_idx_new + b * ap.kins + 8 * lane : nullptr;
         auto row = [&](int x) -> uint4 {           // indexer key row x of this sequence, this lane's 8 dims
             return (kn != nullptr && x >= p0) ? *reinterpret_cast<const uint4*>(kn + (x - p0) * kDi)
-                                              : *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(x) * kDi);
+                                              : *reinterpret_cast<const uint4*>(kr + tok_off(ap.kis, x, kDi));
         };
         if (kn != nullptr)
             for (int t = 0; t < tq; ++t)
-                *reinterpret_cast<uint4*>(kr + static_cast<int64_t>(p0 + t) * kDi) =
+                *reinterpret_cast<uint4*>(kr + tok_off(ap.kis, p0 + t, kDi)) =
                     *reinterpret_cast<const uint4*>(kn + t * kDi);
         for (int t = 0; t < tq; ++t) {
             const int x = p0 + t;
@@ -122,22 +129,25 @@ __device__ __forceinline__ void append_rows(const AppendArgs& ap, int b, int p0,
             uint4 r[kBlock];
 #pragma unroll
             for (int i = 0; i < kBlock; ++i) r[i] = row(x - (kBlock - 1) + i);
-            *reinterpret_cast<uint4*>(ap.kbar + b * ap.kbs + static_cast<int64_t>(x / kBlock) * kDi + 8 * lane) =
-                compress_rows(r);
+            const int64_t kb_off = kPaged ? phys_block(pm, b, x / kBlock) * kDi
+                                          : b * ap.kbs + static_cast<int64_t>(x / kBlock) * kDi;
+            *reinterpret_cast<uint4*>(ap.kbar + kb_off + 8 * lane) = compress_rows(r);
         }
     }
 }
 
-__global__ __launch_bounds__(192) void decode_append_kernel(Positions pos, int tq, AppendArgs ap) {
-    append_rows(ap, blockIdx.x, pos.p[blockIdx.x], tq, threadIdx.x >> 6);
+template <bool kPaged>
+__global__ __launch_bounds__(192) void decode_append_kernel(Positions pos, int tq, AppendArgs ap, PageMap pm) {
+    append_rows<kPaged>(ap, pm, blockIdx.x, pos.p[blockIdx.x], tq, threadIdx.x >> 6);
 }
 
-// hist: tq x 4096 words of dynamic LDS (one histogram per token)
-template <int STEPS>
+// hist: tq x 4096 words of dynamic LDS (one histogram per token).  kPaged:
+// kbar (and the caches the append writes) are page pools behind pm.
+template <int STEPS, bool kPaged>
 __global__ __launch_bounds__(256) void decode_scan_kernel(
     const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
     Positions pos, int budget, int tq, int wg_per_seq, float* __restrict__ scores,
-    int64_t ss, int64_t sld, DecodeWs ws, AppendArgs ap, int append) {
+    int64_t ss, int64_t sld, DecodeWs ws, AppendArgs ap, int append, PageMap pm) {
     extern __shared__ uint32_t hist[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     const int p0 = pos.p[b];
     const int o_last = (p0 + tq - 1) / kBlock;           // blocks below the last token's own block
 
-    if (append && g == 0) append_rows(ap, b, p0, tq, wave);
+    if (append && g == 0) append_rows<kPaged>(ap, pm, b, p0, tq, wave);
 
     for (int k = tid; k < tq * kDecHistBins; k += 256) hist[k] = 0;
     __syncthreads();
@@ -162,10 +172,16 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     uint32_t* hist_c = hist + (c16 < tq ? c16 : 0) * kDecHistBins;
     bf16x8_t qf[kIdxSlices];
     load_index_q(q_idx + b * qs, 0, tq, qf);            // tokens 0 .. tq-1 in columns 0 .. tq-1, zero elsewhere
-    const uint16_t* kb = kbar + b * kbs;
+    const uint16_t* kb = kPaged ? kbar : kbar + b * kbs;
     float* sb = scores + b * ss + (c16 < tq ? c16 : 0) * sld;
     const int j_lo = g * (256 * STEPS);
     const int j_hi = min(o_last, j_lo + 256 * STEPS);
+    auto load_tile = [&](int jt, bf16x8_t (&kf)[4]) {
+        if constexpr (kPaged)
+            load_index_k_paged(kb, pm, b, jt, j_hi, kf);
+        else
+            load_index_k(kb, jt, j_hi, kf);
+    };
     // two named buffers, loop unrolled by two: one group computes while the
     // next is in flight (the next-group address is clamped, never skipped)
     auto step_of = [&](int j) { return (j < j_hi) ? j : (j_hi - 1) / 64 * 64; };
@@ -194,13 +210,13 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     if (j0 < j_hi) {
         bf16x8_t buf[2][4][4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) load_index_k(kb, j0 + 16 * nt, j_hi, buf[0][nt]);
+        for (int nt = 0; nt < 4; ++nt) load_tile(j0 + 16 * nt, buf[0][nt]);
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             if (st + 1 < STEPS) {
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
-                    load_index_k(kb, step_of(j0 + 256 * (st + 1)) + 16 * nt, j_hi, buf[(st + 1) & 1][nt]);
+                    load_tile(step_of(j0 + 256 * (st + 1)) + 16 * nt, buf[(st + 1) & 1][nt]);
             }
             if (j0 + 256 * st < j_hi) score_group(buf[st & 1], j0 + 256 * st);
         }
@@ -461,7 +477,8 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
                                       int64_t kbs, const Positions& pos, int batch, int tq, int budget,
                                       float* scores, int64_t ss, int64_t sld, int32_t* sel, int64_t sels,
-                                      void* ws, const DecodeAppend* append, hipStream_t stream) {
+                                      void* ws, const DecodeAppend* append, const PageMap* pm,
+                                      hipStream_t stream) {
     const int rows = batch * tq;
     int o_max = 0;
     for (int b = 0; b < batch; ++b) o_max = max(o_max, (pos.p[b] + tq - 1) / kBlock);
@@ -495,32 +512,38 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
     // one token per sequence: the rows are appended by the scan; several: first,
     // because a block an earlier new token completes is scored for the later ones
     int scan_appends = append != nullptr ? 1 : 0;
+    const PageMap pmv = pm != nullptr ? *pm : PageMap{};
     if (append != nullptr && tq > 1) {
-        hipLaunchKernelGGL(decode_append_kernel, dim3(static_cast<unsigned>(batch)), dim3(192), 0, stream, pos, tq,
-                           ap);
+        if (pm != nullptr)
+            hipLaunchKernelGGL(decode_append_kernel<true>, dim3(static_cast<unsigned>(batch)), dim3(192), 0, stream,
+                               pos, tq, ap, pmv);
+        else
+            hipLaunchKernelGGL(decode_append_kernel<false>, dim3(static_cast<unsigned>(batch)), dim3(192), 0, stream,
+                               pos, tq, ap, pmv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         scan_appends = 0;
     }
     const dim3 grid(static_cast<unsigned>(batch * wg_scan));
     const size_t lds = static_cast<size_t>(tq) * kDecHistBins * 4;
-    switch (steps) {
-        case 8:
-            hipLaunchKernelGGL(decode_scan_kernel<8>, grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               tq, wg_scan, scores, ss, sld, w, ap, scan_appends);
-            break;
-        case 4:
-            hipLaunchKernelGGL(decode_scan_kernel<4>, grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               tq, wg_scan, scores, ss, sld, w, ap, scan_appends);
-            break;
-        case 2:
-            hipLaunchKernelGGL(decode_scan_kernel<2>, grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               tq, wg_scan, scores, ss, sld, w, ap, scan_appends);
-            break;
-        default:
-            hipLaunchKernelGGL(decode_scan_kernel<1>, grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, budget,
-                               tq, wg_scan, scores, ss, sld, w, ap, scan_appends);
-            break;
+#define QSA_SCAN(S, P)                                                                                       \
+    hipLaunchKernelGGL((decode_scan_kernel<S, P>), grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, \
+                       budget, tq, wg_scan, scores, ss, sld, w, ap, scan_appends, pmv)
+    if (pm != nullptr) {
+        switch (steps) {
+            case 8: QSA_SCAN(8, true); break;
+            case 4: QSA_SCAN(4, true); break;
+            case 2: QSA_SCAN(2, true); break;
+            default: QSA_SCAN(1, true); break;
+        }
+    } else {
+        switch (steps) {
+            case 8: QSA_SCAN(8, false); break;
+            case 4: QSA_SCAN(4, false); break;
+            case 2: QSA_SCAN(2, false); break;
+            default: QSA_SCAN(1, false); break;
+        }
     }
+#undef QSA_SCAN
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(decode_filter_kernel, dim3(static_cast<unsigned>(rows * wg_filt)), dim3(256), 0,
                        stream, scores, ss, sld, pos, budget, tq, wg_filt, w);

@@ -86,4 +86,16 @@ __device__ __forceinline__ void load_index_k(const uint16_t* kb, int j0, int j_e
     load_index_k_row(kb, min(j0 + static_cast<int>(threadIdx.x & 15), j_end - 1), kf);
 }
 
+// The same tile from a paged block-key pool: j0 is a multiple of 16 and a
+// page holds a multiple of 16 blocks, so the tile's rows (clamped ones fall in
+// the tile of j_end - 1) share one page, read once per wave (scalar load).
+__device__ __forceinline__ void load_index_k_paged(const uint16_t* pool, const PageMap& pm, int b, int j0,
+                                                   int j_end, bf16x8_t (&kf)[4]) {
+    const int jr = min(j0, j_end - 1);
+    const int pg = page_of(pm, b, static_cast<int64_t>(jr) * kBlock);
+    const int j = min(j0 + static_cast<int>(threadIdx.x & 15), j_end - 1);
+    const int64_t row = (static_cast<int64_t>(pg) << (pm.shift - 2)) | (j & ((1 << (pm.shift - 2)) - 1));
+    load_index_k_row(pool + row * kDi, 0, kf);
+}
+
 }  // namespace qsa

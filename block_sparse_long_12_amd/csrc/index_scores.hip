@@ -52,15 +52,26 @@ __shared__ int lrow_base[kWgTok];
 __shared__ int lwcnt[4];
 
 // Block of column jv: itself, or in sample mode run jv / 256 of kSampleRuns
-// runs of 256 blocks spread evenly over [0, omin).
-template <int kMode>
+// runs of 256 blocks spread evenly over [0, omin) (with paged block keys each
+// run starts on a multiple of 16 blocks, so a 16-block tile stays inside one
+// page).
+template <int kMode, bool kPaged = false>
 __device__ __forceinline__ int column_block(int jv, int omin) {
     if (kMode == kModeSample) {
         const int run = jv >> 8;
-        return static_cast<int>(static_cast<int64_t>(run) * (omin - 256) / (kSampleRuns - 1)) + (jv & 255);
+        int base = static_cast<int>(static_cast<int64_t>(run) * (omin - 256) / (kSampleRuns - 1));
+        if (kPaged) base &= ~15;
+        return base + (jv & 255);
     }
     return jv;
 }
+
+// Paged block keys: the sequence's block-table row and the page geometry.
+struct KbPages {
+    const int32_t* tbl;
+    int shift;          // log2 of tokens per page
+    int n_pages;
+};
 
 // Stages one step of kbar into t with LDS-direct loads (no registers): wave
 // w fills rows 16w .. 16w + 15 with 4 loads of 1 KiB; lane L of load i
@@ -74,16 +85,28 @@ __device__ __forceinline__ int column_block(int jv, int omin) {
 // The instruction has no register results (it writes LDS only, and its
 // address registers are read at issue); completion is tracked explicitly by
 // the vmcnt waits of the step loop.
-template <int kMode>
-__device__ __forceinline__ void stage_dma(const uint16_t* kb, int j0, int j_end, int omin, KTile& t) {
+template <int kMode, bool kPaged = false>
+__device__ __forceinline__ void stage_dma(const uint16_t* kb, int j0, int j_end, int omin, const KbPages& kp,
+                                          KTile& t) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // paged: the wave's 16 rows form one 16-block tile (the step start is a
+    // multiple of 64, sample runs start on multiples of 16, and clamped rows
+    // fall in the tile of j_end - 1), so one wave-uniform table read serves
+    // them all
+    int64_t page_base = 0;
+    if constexpr (kPaged) {
+        const int jr = column_block<kMode, true>(min(j0 + 16 * wave, j_end - 1), omin);
+        const int pg = min(max(kp.tbl[(jr * kBlock) >> kp.shift], 0), kp.n_pages - 1);
+        page_base = static_cast<int64_t>(pg) << (kp.shift - 2);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 16 * wave + 4 * i + (lane >> 4);
         const int c = (lane & 15) ^ (r & 15);
-        const int j = column_block<kMode>(min(j0 + r, j_end - 1), omin);
-        const uint16_t* src = kb + static_cast<int64_t>(j) * kDi + 8 * c;
+        const int j = column_block<kMode, kPaged>(min(j0 + r, j_end - 1), omin);
+        const int64_t row = kPaged ? (page_base | (j & ((1 << (kp.shift - 2)) - 1))) : static_cast<int64_t>(j);
+        const uint16_t* src = kb + row * kDi + 8 * c;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(
             static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&t.chunk[16 * wave + 4 * i][0])));
 #pragma clang diagnostic push
@@ -179,11 +202,12 @@ __device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf
     }
 }
 
-template <int kMode>
+template <int kMode, bool kPaged>
 __global__ __launch_bounds__(256) void index_kernel(
     const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
     Positions pos0, int tq, int n_wt, int n_cc, int cols_per_chunk, int64_t n_wg,
-    float* __restrict__ scores, int64_t ld, int64_t ss, const int* __restrict__ flags, IndexCollect col) {
+    float* __restrict__ scores, int64_t ld, int64_t ss, const int* __restrict__ flags, IndexCollect col,
+    PageMap pm) {
     // workgroups are dealt to the 8 XCDs round-robin; renumber them so each
     // XCD works through one contiguous range, and the row tiles that share a
     // column chunk of kbar share that XCD's L2
@@ -217,7 +241,9 @@ __global__ __launch_bounds__(256) void index_kernel(
     bf16x8_t qf[kIdxSlices];
     load_index_q(q_idx + b * qs, t0, tq, qf);
 
-    const uint16_t* kb = kbar + b * kbs;
+    // block keys of the sequence, or the page pool and the sequence's table row
+    const uint16_t* kb = kPaged ? kbar : kbar + b * kbs;
+    const KbPages kp{kPaged ? pm.table + b * pm.ts : nullptr, pm.shift, pm.n_pages};
     const int n_steps = (j_end - j_begin + kColStep - 1) / kColStep;
 
     if constexpr (kMode == kModeCollect) {
@@ -232,14 +258,14 @@ __global__ __launch_bounds__(256) void index_kernel(
         __syncthreads();
         // two LDS buffers: step s + 1 loads while step s is scored; the loop
         // issues no other vector memory op, so "all landed" is vmcnt(0)
-        stage_dma<kMode>(kb, j_begin, j_end, omin, tA);
+        stage_dma<kMode, kPaged>(kb, j_begin, j_end, omin, kp, tA);
         for (int s = 0; s < n_steps; s += 2) {
             wait_and_meet<0>();
-            stage_dma<kMode>(kb, j_begin + kColStep * (s + 1), j_end, omin, tB);
+            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 1), j_end, omin, kp, tB);
             if (has_rows) collect_step(tA, qf, j_begin + kColStep * s, lim, tau, tok - t_wg, j_begin, seg, cnt);
             if (s + 1 >= n_steps) break;
             wait_and_meet<0>();
-            stage_dma<kMode>(kb, j_begin + kColStep * (s + 2), j_end, omin, tA);
+            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 2), j_end, omin, kp, tA);
             if (has_rows) collect_step(tB, qf, j_begin + kColStep * (s + 1), lim, tau, tok - t_wg, j_begin, seg, cnt);
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);               // no load into LDS outlives the workgroup
@@ -283,19 +309,19 @@ __global__ __launch_bounds__(256) void index_kernel(
         __builtin_amdgcn_s_waitcnt(0x0f70);               // B in registers before the load pipeline starts
         float* sb = scores + b * ss;
         // three LDS buffers: step s is scored while steps s + 1 and s + 2 load
-        stage_dma<kMode>(kb, j_begin, j_end, omin, tA);
-        stage_dma<kMode>(kb, j_begin + kColStep, j_end, omin, tB);
+        stage_dma<kMode, kPaged>(kb, j_begin, j_end, omin, kp, tA);
+        stage_dma<kMode, kPaged>(kb, j_begin + kColStep, j_end, omin, kp, tB);
         for (int s = 0; s < n_steps; s += 3) {
             step_sync(s, has_rows);
-            stage_dma<kMode>(kb, j_begin + kColStep * (s + 2), j_end, omin, tC);
+            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 2), j_end, omin, kp, tC);
             if (has_rows) store_step(tA, qf, j_begin + kColStep * s, j_end, t0, tq, sb, ld);
             if (s + 1 >= n_steps) break;
             step_sync(s + 1, has_rows);
-            stage_dma<kMode>(kb, j_begin + kColStep * (s + 3), j_end, omin, tA);
+            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 3), j_end, omin, kp, tA);
             if (has_rows) store_step(tB, qf, j_begin + kColStep * (s + 1), j_end, t0, tq, sb, ld);
             if (s + 2 >= n_steps) break;
             step_sync(s + 2, has_rows);
-            stage_dma<kMode>(kb, j_begin + kColStep * (s + 4), j_end, omin, tB);
+            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 4), j_end, omin, kp, tB);
             if (has_rows) store_step(tC, qf, j_begin + kColStep * (s + 2), j_end, t0, tq, sb, ld);
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);               // no load into LDS outlives the workgroup
@@ -320,14 +346,18 @@ template <int kMode>
 static hipError_t launch_mode(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
                               const Positions& pos0, int batch, int tq, int jmax, int max_cols, float* scores,
                               int64_t ld, int64_t ss, const int* flags, const IndexCollect& col,
-                              hipStream_t stream) {
+                              const PageMap* pm, hipStream_t stream) {
     if (tq <= 0 || jmax <= 0) return hipSuccess;
     int n_wt, n_cc, cpc;
     int64_t n_wg;
     index_grid(jmax, batch, tq, max_cols, &n_wt, &n_cc, &cpc, &n_wg);
     const unsigned grid = static_cast<unsigned>((n_wg + 7) / 8 * 8);
-    hipLaunchKernelGGL(index_kernel<kMode>, dim3(grid), dim3(256), 0, stream, q_idx, qs, kbar, kbs, pos0, tq,
-                       n_wt, n_cc, cpc, n_wg, scores, ld, ss, flags, col);
+    if (pm != nullptr)
+        hipLaunchKernelGGL((index_kernel<kMode, true>), dim3(grid), dim3(256), 0, stream, q_idx, qs, kbar, kbs,
+                           pos0, tq, n_wt, n_cc, cpc, n_wg, scores, ld, ss, flags, col, *pm);
+    else
+        hipLaunchKernelGGL((index_kernel<kMode, false>), dim3(grid), dim3(256), 0, stream, q_idx, qs, kbar, kbs,
+                           pos0, tq, n_wt, n_cc, cpc, n_wg, scores, ld, ss, flags, col, PageMap{});
     return hipGetLastError();
 }
 
@@ -340,25 +370,26 @@ static int max_visible_block(const Positions& pos0, int batch, int tq) {
 hipError_t launch_index_scores(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
                                int64_t kbs, const Positions& pos0, int batch, int tq,
                                float* scores, int64_t ld, int64_t ss, const int* row_flags,
-                               const int* n_flagged, hipStream_t stream) {
+                               const int* n_flagged, const PageMap* pm, hipStream_t stream) {
     IndexCollect col{};
     col.n_flagged = n_flagged;
     return launch_mode<kModeScores>(q_idx, qs, kbar, kbs, pos0, batch, tq, max_visible_block(pos0, batch, tq),
-                                    4096, scores, ld, ss, row_flags, col, stream);
+                                    4096, scores, ld, ss, row_flags, col, pm, stream);
 }
 
 hipError_t launch_index_sample(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
-                               const Positions& pos0, int batch, int tq, float* sample, hipStream_t stream) {
+                               const Positions& pos0, int batch, int tq, float* sample, const PageMap* pm,
+                               hipStream_t stream) {
     return launch_mode<kModeSample>(q_idx, qs, kbar, kbs, pos0, batch, tq, kSampleCols, 4096, sample,
                                     kSampleCols, static_cast<int64_t>(tq) * kSampleCols, nullptr, IndexCollect{},
-                                    stream);
+                                    pm, stream);
 }
 
 hipError_t launch_index_collect(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
                                 const Positions& pos0, int batch, int tq, int max_cols, const IndexCollect& col,
-                                hipStream_t stream) {
+                                const PageMap* pm, hipStream_t stream) {
     return launch_mode<kModeCollect>(q_idx, qs, kbar, kbs, pos0, batch, tq, max_visible_block(pos0, batch, tq),
-                                     max_cols, nullptr, 0, 0, nullptr, col, stream);
+                                     max_cols, nullptr, 0, 0, nullptr, col, pm, stream);
 }
 
 }  // namespace qsa

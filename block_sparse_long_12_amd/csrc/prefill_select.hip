@@ -135,19 +135,19 @@ __global__ __launch_bounds__(kFinNT) void prefill_finalize_kernel(Positions pos0
 hipError_t launch_prefill_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
                                        const Positions& pos0, int batch, int tq, int budget, float* scores,
                                        int64_t ld, int64_t ss, int32_t* sel, int64_t sels, void* ws,
-                                       hipStream_t stream) {
+                                       const PageMap* pm, hipStream_t stream) {
     if (tq <= 0) return hipSuccess;
     int omin = 0x7fffffff;
     for (int b = 0; b < batch; ++b) omin = min(omin, pos0.p[b] / kBlock);
     if (budget > kResMaxBudget || omin < kFusedMinBlocks) {
         hipError_t e = launch_index_scores(q_idx, qs, kbar, kbs, pos0, batch, tq, scores, ld, ss, nullptr, nullptr,
-                                           stream);
+                                           pm, stream);
         if (e != hipSuccess) return e;
         return launch_select(scores, ld, ss, pos0, batch, tq, budget, sel, sels, nullptr, stream);
     }
     const PrefillWs w = carve(ws, batch, tq);
     const unsigned rows = static_cast<unsigned>(static_cast<int64_t>(batch) * tq);
-    hipError_t e = launch_index_sample(q_idx, qs, kbar, kbs, pos0, batch, tq, w.sample, stream);
+    hipError_t e = launch_index_sample(q_idx, qs, kbar, kbs, pos0, batch, tq, w.sample, pm, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(threshold_kernel, dim3(rows), dim3(kThrNT), 0, stream, w.sample, pos0, tq, budget, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -160,11 +160,11 @@ hipError_t launch_prefill_index_select(const uint16_t* q_idx, int64_t qs, const 
     col.tau = w.tau;
     col.row_cnt = w.row_cnt;
     col.list = w.list;
-    e = launch_index_collect(q_idx, qs, kbar, kbs, pos0, batch, tq, static_cast<int>(cols), col, stream);
+    e = launch_index_collect(q_idx, qs, kbar, kbs, pos0, batch, tq, static_cast<int>(cols), col, pm, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_finalize_kernel, dim3(rows), dim3(kFinNT), 0, stream, pos0, tq, budget, w, sel, sels);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = launch_index_scores(q_idx, qs, kbar, kbs, pos0, batch, tq, scores, ld, ss, w.flags, w.n_flagged, stream);
+    e = launch_index_scores(q_idx, qs, kbar, kbs, pos0, batch, tq, scores, ld, ss, w.flags, w.n_flagged, pm, stream);
     if (e != hipSuccess) return e;
     return launch_select(scores, ld, ss, pos0, batch, tq, budget, sel, sels, w.flags, stream);
 }

@@ -66,6 +66,36 @@ qsa_status_t take_rope(const qsa_rope_t* rope, qsa_rope_t& out) {
     return QSA_OK;
 }
 
+// Paged cache: geometry and table checks; the pools a call uses are checked
+// by the caller (need_*).  Every sequence's table row must reach the page of
+// its last token pos[b] + span - 1.
+qsa_status_t take_paged(const qsa_paged_cache_t* c, const qsa::Positions& p, int32_t batch, int32_t span,
+                        bool need_kv, bool need_k_idx, bool need_kbar, qsa::PageMap& pm) {
+    CHECK(c != nullptr, "cache is NULL");
+    CHECK(c->block_table != nullptr && (reinterpret_cast<uintptr_t>(c->block_table) & 3u) == 0,
+          "block_table must be non-NULL and 4-byte aligned");
+    const int32_t P = c->page_tokens;
+    CHECK(P >= 64 && P <= 65536 && (P & (P - 1)) == 0, "page_tokens = %d must be a power of two in [64, 65536]", P);
+    CHECK(c->n_pages >= 1, "n_pages = %d must be >= 1", c->n_pages);
+    CHECK(!need_kv || (c->k != nullptr && c->v != nullptr && aligned16(c->k) && aligned16(c->v)),
+          "cache k and v must be non-NULL and 16-byte aligned");
+    CHECK(!need_k_idx || (c->k_idx != nullptr && aligned16(c->k_idx)),
+          "cache k_idx must be non-NULL and 16-byte aligned");
+    CHECK(!need_kbar || (c->kbar != nullptr && aligned16(c->kbar)), "cache kbar must be non-NULL and 16-byte aligned");
+    int64_t pages = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t n = (int64_t{p.p[b]} + span + P - 1) / P;
+        pages = n > pages ? n : pages;
+    }
+    CHECK(batch == 1 || c->table_stride >= pages, "table_stride = %lld smaller than the %lld pages a row reaches",
+          static_cast<long long>(c->table_stride), static_cast<long long>(pages));
+    pm.table = c->block_table;
+    pm.ts = c->table_stride;
+    pm.shift = __builtin_ctz(static_cast<unsigned>(P));
+    pm.n_pages = c->n_pages;
+    return QSA_OK;
+}
+
 #define TRY(expr)                          \
     do {                                   \
         qsa_status_t _s = (expr);          \
@@ -175,7 +205,8 @@ qsa_status_t qsa_index_scores(const uint16_t* q_idx, int64_t q_idx_seq_stride,
     CHECK(batch == 1 || stride_ok(kbar_seq_stride), "kbar_seq_stride must be a positive multiple of 8");
     TRY(check_scores_layout(scores, scores_ld, scores_seq_stride, batch, tq, p));
     return hip_result(qsa::launch_index_scores(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch,
-                                               tq, scores, scores_ld, scores_seq_stride, nullptr, nullptr, stream),
+                                               tq, scores, scores_ld, scores_seq_stride, nullptr, nullptr, nullptr,
+                                               stream),
                       "index_scores launch");
 }
 
@@ -212,13 +243,17 @@ size_t qsa_index_select_prefill_workspace_bytes(int32_t batch, int32_t tq) {
     return qsa::prefill_select_ws_bytes(batch, tq);
 }
 
-qsa_status_t qsa_index_select_prefill(const uint16_t* q_idx, int64_t q_idx_seq_stride,
-                                      const uint16_t* kbar, int64_t kbar_seq_stride,
-                                      const int32_t* q_pos0, int32_t batch, int32_t tq, int32_t budget,
-                                      float* scores, int64_t scores_ld, int64_t scores_seq_stride,
-                                      int32_t* sel, int64_t sel_seq_stride,
-                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// kbar is contiguous [B][*][128] with kbar_seq_stride, or (cache non-NULL)
+// the paged block-key pool of `cache`
+static qsa_status_t index_select_prefill_impl(const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                              const uint16_t* kbar, int64_t kbar_seq_stride,
+                                              const qsa_paged_cache_t* cache,
+                                              const int32_t* q_pos0, int32_t batch, int32_t tq, int32_t budget,
+                                              float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                              int32_t* sel, int64_t sel_seq_stride,
+                                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
     TRY(check_batch(batch));
+    if (cache != nullptr) kbar = cache->kbar;
     CHECK(q_idx != nullptr && kbar != nullptr, "q_idx or kbar is NULL");
     CHECK(aligned16(q_idx) && aligned16(kbar), "q_idx and kbar must be 16-byte aligned");
     CHECK(tq >= 0, "tq = %d is negative", tq);
@@ -230,7 +265,11 @@ qsa_status_t qsa_index_select_prefill(const uint16_t* q_idx, int64_t q_idx_seq_s
     if (tq == 0) return ok();
     CHECK(batch == 1 || (stride_ok(q_idx_seq_stride) && q_idx_seq_stride >= int64_t{tq} * qsa::kHi * qsa::kDi),
           "q_idx_seq_stride must be a multiple of 8 and >= tq * 4 * 128");
-    CHECK(batch == 1 || stride_ok(kbar_seq_stride), "kbar_seq_stride must be a positive multiple of 8");
+    qsa::PageMap pm{};
+    if (cache != nullptr)
+        TRY(take_paged(cache, p, batch, tq, false, false, true, pm));
+    else
+        CHECK(batch == 1 || stride_ok(kbar_seq_stride), "kbar_seq_stride must be a positive multiple of 8");
     TRY(check_scores_layout(scores, scores_ld, scores_seq_stride, batch, tq, p));
     CHECK(batch == 1 || sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
     const size_t need = qsa::prefill_select_ws_bytes(batch, tq);
@@ -240,8 +279,32 @@ qsa_status_t qsa_index_select_prefill(const uint16_t* q_idx, int64_t q_idx_seq_s
     CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, "workspace must be 256-byte aligned");
     return hip_result(qsa::launch_prefill_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq,
                                                        budget, scores, scores_ld, scores_seq_stride, sel,
-                                                       sel_seq_stride, workspace, stream),
+                                                       sel_seq_stride, workspace, cache != nullptr ? &pm : nullptr,
+                                                       stream),
                       "index_select_prefill launch");
+}
+
+qsa_status_t qsa_index_select_prefill(const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                      const uint16_t* kbar, int64_t kbar_seq_stride,
+                                      const int32_t* q_pos0, int32_t batch, int32_t tq, int32_t budget,
+                                      float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                      int32_t* sel, int64_t sel_seq_stride,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return index_select_prefill_impl(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, nullptr, q_pos0, batch, tq,
+                                     budget, scores, scores_ld, scores_seq_stride, sel, sel_seq_stride, workspace,
+                                     workspace_bytes, stream);
+}
+
+qsa_status_t qsa_index_select_prefill_paged(const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                            const qsa_paged_cache_t* cache,
+                                            const int32_t* q_pos0, int32_t batch, int32_t tq, int32_t budget,
+                                            float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                            int32_t* sel, int64_t sel_seq_stride,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    CHECK(cache != nullptr, "cache is NULL");
+    return index_select_prefill_impl(q_idx, q_idx_seq_stride, nullptr, 0, cache, q_pos0, batch, tq, budget, scores,
+                                     scores_ld, scores_seq_stride, sel, sel_seq_stride, workspace, workspace_bytes,
+                                     stream);
 }
 
 static qsa_status_t check_attn_common(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -257,6 +320,50 @@ static qsa_status_t check_attn_common(const uint16_t* q, const uint16_t* k, cons
     return QSA_OK;
 }
 
+// k_cache / v_cache contiguous with kv_seq_stride, or (cache non-NULL) the
+// paged pools of `cache`
+static qsa_status_t sparse_attn_prefill_impl(const uint16_t* q, int64_t q_seq_stride,
+                                             const uint16_t* k_cache, const uint16_t* v_cache,
+                                             int64_t kv_seq_stride, const qsa_paged_cache_t* cache,
+                                             const int32_t* sel, int64_t sel_seq_stride,
+                                             const int32_t* q_pos0, int32_t batch, int32_t tq,
+                                             int32_t budget, float softmax_scale,
+                                             uint16_t* out, int64_t out_seq_stride, float* lse,
+                                             int64_t lse_seq_stride, const uint16_t* gate, int64_t gate_seq_stride,
+                                             hipStream_t stream) {
+    TRY(check_batch(batch));
+    if (cache != nullptr) {
+        k_cache = cache->k;
+        v_cache = cache->v;
+    }
+    TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
+    CHECK(tq >= 0, "tq = %d is negative", tq);
+    CHECK(lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) == 0, "lse must be 4-byte aligned");
+    CHECK(gate == nullptr || aligned16(gate), "gate must be 16-byte aligned");
+    qsa::Positions p;
+    TRY(take_positions(q_pos0, batch, tq, "q_pos0", p));
+    if (tq == 0) return ok();
+    qsa::PageMap pm{};
+    if (cache != nullptr) TRY(take_paged(cache, p, batch, tq, true, false, false, pm));
+    if (batch > 1) {
+        int64_t max_len = 0;
+        for (int b = 0; b < batch; ++b) max_len = p.p[b] + tq > max_len ? p.p[b] + tq : max_len;
+        CHECK(stride_ok(q_seq_stride) && q_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD, "q_seq_stride too small");
+        CHECK(stride_ok(out_seq_stride) && out_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD, "out_seq_stride too small");
+        CHECK(cache != nullptr || (stride_ok(kv_seq_stride) && kv_seq_stride >= max_len * qsa::kHkv * qsa::kD),
+              "kv_seq_stride smaller than the rows the queries reach");
+        CHECK(sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
+        CHECK(lse == nullptr || lse_seq_stride >= int64_t{tq} * qsa::kHq, "lse_seq_stride < tq * 24");
+        CHECK(gate == nullptr || (stride_ok(gate_seq_stride) && gate_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD),
+              "gate_seq_stride too small");
+    }
+    return hip_result(qsa::launch_attn_prefill(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
+                                               sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
+                                               out_seq_stride, lse, lse_seq_stride, gate, gate_seq_stride,
+                                               cache != nullptr ? &pm : nullptr, stream),
+                      "sparse_attn_prefill launch");
+}
+
 qsa_status_t qsa_sparse_attn_prefill(const uint16_t* q, int64_t q_seq_stride,
                                      const uint16_t* k_cache, const uint16_t* v_cache,
                                      int64_t kv_seq_stride,
@@ -266,30 +373,23 @@ qsa_status_t qsa_sparse_attn_prefill(const uint16_t* q, int64_t q_seq_stride,
                                      uint16_t* out, int64_t out_seq_stride, float* lse,
                                      int64_t lse_seq_stride, const uint16_t* gate, int64_t gate_seq_stride,
                                      hipStream_t stream) {
-    TRY(check_batch(batch));
-    TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
-    CHECK(tq >= 0, "tq = %d is negative", tq);
-    CHECK(lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) == 0, "lse must be 4-byte aligned");
-    CHECK(gate == nullptr || aligned16(gate), "gate must be 16-byte aligned");
-    qsa::Positions p;
-    TRY(take_positions(q_pos0, batch, tq, "q_pos0", p));
-    if (tq == 0) return ok();
-    if (batch > 1) {
-        int64_t max_len = 0;
-        for (int b = 0; b < batch; ++b) max_len = p.p[b] + tq > max_len ? p.p[b] + tq : max_len;
-        CHECK(stride_ok(q_seq_stride) && q_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD, "q_seq_stride too small");
-        CHECK(stride_ok(out_seq_stride) && out_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD, "out_seq_stride too small");
-        CHECK(stride_ok(kv_seq_stride) && kv_seq_stride >= max_len * qsa::kHkv * qsa::kD,
-              "kv_seq_stride smaller than the rows the queries reach");
-        CHECK(sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
-        CHECK(lse == nullptr || lse_seq_stride >= int64_t{tq} * qsa::kHq, "lse_seq_stride < tq * 24");
-        CHECK(gate == nullptr || (stride_ok(gate_seq_stride) && gate_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD),
-              "gate_seq_stride too small");
-    }
-    return hip_result(qsa::launch_attn_prefill(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
-                                               sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
-                                               out_seq_stride, lse, lse_seq_stride, gate, gate_seq_stride, stream),
-                      "sparse_attn_prefill launch");
+    return sparse_attn_prefill_impl(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, nullptr, sel, sel_seq_stride,
+                                    q_pos0, batch, tq, budget, softmax_scale, out, out_seq_stride, lse,
+                                    lse_seq_stride, gate, gate_seq_stride, stream);
+}
+
+qsa_status_t qsa_sparse_attn_prefill_paged(const uint16_t* q, int64_t q_seq_stride,
+                                           const qsa_paged_cache_t* cache,
+                                           const int32_t* sel, int64_t sel_seq_stride,
+                                           const int32_t* q_pos0, int32_t batch, int32_t tq,
+                                           int32_t budget, float softmax_scale,
+                                           uint16_t* out, int64_t out_seq_stride, float* lse,
+                                           int64_t lse_seq_stride, const uint16_t* gate, int64_t gate_seq_stride,
+                                           hipStream_t stream) {
+    CHECK(cache != nullptr, "cache is NULL");
+    return sparse_attn_prefill_impl(q, q_seq_stride, nullptr, nullptr, 0, cache, sel, sel_seq_stride, q_pos0, batch,
+                                    tq, budget, softmax_scale, out, out_seq_stride, lse, lse_seq_stride, gate,
+                                    gate_seq_stride, stream);
 }
 
 static bool tq_ok(int32_t tq) { return tq >= 1 && tq <= qsa::kMaxDecodeTq; }
@@ -304,7 +404,7 @@ size_t qsa_decode_workspace_bytes(int32_t batch, int32_t tq, int32_t budget) {
 static qsa_status_t check_decode_attn(const qsa::Positions& p, int32_t batch, int32_t tq, int32_t budget,
                                       int64_t q_seq_stride, int64_t kv_seq_stride, int64_t sel_seq_stride,
                                       int64_t out_seq_stride, const float* lse, const uint16_t* gate,
-                                      int64_t gate_seq_stride) {
+                                      int64_t gate_seq_stride, bool paged = false) {
     CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
     CHECK(gate == nullptr || aligned16(gate), "gate must be 16-byte aligned");
     CHECK(gate == nullptr || batch == 1 ||
@@ -317,7 +417,7 @@ static qsa_status_t check_decode_attn(const qsa::Positions& p, int32_t batch, in
         CHECK(stride_ok(q_seq_stride) && q_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD, "q_seq_stride too small");
         CHECK(stride_ok(out_seq_stride) && out_seq_stride >= int64_t{tq} * qsa::kHq * qsa::kD,
               "out_seq_stride too small");
-        CHECK(stride_ok(kv_seq_stride) && kv_seq_stride >= max_len * qsa::kHkv * qsa::kD,
+        CHECK(paged || (stride_ok(kv_seq_stride) && kv_seq_stride >= max_len * qsa::kHkv * qsa::kD),
               "kv_seq_stride smaller than the rows the queries reach");
         CHECK(sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
     }
@@ -360,7 +460,7 @@ static qsa_status_t check_index_select_decode(const uint16_t* q_idx, int64_t q_i
                                               const uint16_t* kbar, int64_t kbar_seq_stride,
                                               const qsa::Positions& p, int32_t batch, int32_t tq, int32_t budget,
                                               const float* scores, int64_t scores_ld, int64_t scores_seq_stride,
-                                              const int32_t* sel, int64_t sel_seq_stride) {
+                                              const int32_t* sel, int64_t sel_seq_stride, bool paged = false) {
     CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
     CHECK(q_idx != nullptr && kbar != nullptr && scores != nullptr && sel != nullptr,
           "q_idx, kbar, scores and sel must be non-NULL");
@@ -375,7 +475,8 @@ static qsa_status_t check_index_select_decode(const uint16_t* q_idx, int64_t q_i
     if (batch > 1) {
         CHECK(stride_ok(q_idx_seq_stride) && q_idx_seq_stride >= int64_t{tq} * qsa::kHi * qsa::kDi,
               "q_idx_seq_stride too small");
-        CHECK(stride_ok(kbar_seq_stride) && kbar_seq_stride >= o_max * qsa::kDi, "kbar_seq_stride too small");
+        CHECK(paged || (stride_ok(kbar_seq_stride) && kbar_seq_stride >= o_max * qsa::kDi),
+              "kbar_seq_stride too small");
         CHECK(scores_seq_stride % 4 == 0 && scores_seq_stride >= int64_t{tq} * scores_ld,
               "scores_seq_stride must be a multiple of 4 and >= tq * scores_ld");
         CHECK(sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
@@ -402,7 +503,7 @@ qsa_status_t qsa_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_st
     CHECK(aligned16(workspace), "workspace must be 16-byte aligned");
     return hip_result(qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq,
                                                       budget, scores, scores_seq_stride, scores_ld, sel,
-                                                      sel_seq_stride, workspace, nullptr, stream),
+                                                      sel_seq_stride, workspace, nullptr, nullptr, stream),
                       "index_select_decode launch");
 }
 
@@ -411,29 +512,40 @@ size_t qsa_decode_step_workspace_bytes(int32_t batch, int32_t tq, int32_t budget
     return align256(qsa::decode_select_ws_bytes(batch * tq)) + qsa::decode_workspace_bytes(batch * tq, budget);
 }
 
-qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
-                             const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
-                             const uint16_t* q_idx, int64_t q_idx_seq_stride,
-                             const uint16_t* k_idx_new,
-                             uint16_t* k_cache, uint16_t* v_cache, int64_t kv_seq_stride,
-                             uint16_t* k_idx, int64_t k_idx_seq_stride,
-                             uint16_t* kbar, int64_t kbar_seq_stride,
-                             const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
-                             float softmax_scale, const qsa_rope_t* rope,
-                             float* scores, int64_t scores_ld, int64_t scores_seq_stride,
-                             int32_t* sel, int64_t sel_seq_stride,
-                             uint16_t* out, int64_t out_seq_stride, float* lse,
-                             const uint16_t* gate, int64_t gate_seq_stride,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// caches contiguous (per-sequence strides), or (cache non-NULL) the paged
+// pools of `cache`
+static qsa_status_t decode_step_impl(const uint16_t* q, int64_t q_seq_stride,
+                                     const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
+                                     const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                     const uint16_t* k_idx_new,
+                                     uint16_t* k_cache, uint16_t* v_cache, int64_t kv_seq_stride,
+                                     uint16_t* k_idx, int64_t k_idx_seq_stride,
+                                     uint16_t* kbar, int64_t kbar_seq_stride, const qsa_paged_cache_t* cache,
+                                     const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
+                                     float softmax_scale, const qsa_rope_t* rope,
+                                     float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                     int32_t* sel, int64_t sel_seq_stride,
+                                     uint16_t* out, int64_t out_seq_stride, float* lse,
+                                     const uint16_t* gate, int64_t gate_seq_stride,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
     TRY(check_batch(batch));
     CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
     qsa::Positions p;
     TRY(take_positions(q_pos, batch, tq, "q_pos", p));
+    const bool paged = cache != nullptr;
+    qsa::PageMap pm{};
+    if (paged) {
+        TRY(take_paged(cache, p, batch, tq, true, false, true, pm));
+        k_cache = cache->k;
+        v_cache = cache->v;
+        k_idx = cache->k_idx;
+        kbar = cache->kbar;
+    }
     TRY(check_index_select_decode(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq, budget, scores,
-                                  scores_ld, scores_seq_stride, sel, sel_seq_stride));
+                                  scores_ld, scores_seq_stride, sel, sel_seq_stride, paged));
     TRY(check_attn_common(q, k_cache, v_cache, sel, out, budget, softmax_scale));
     TRY(check_decode_attn(p, batch, tq, budget, q_seq_stride, kv_seq_stride, sel_seq_stride, out_seq_stride, lse,
-                          gate, gate_seq_stride));
+                          gate, gate_seq_stride, paged));
     CHECK(k_new != nullptr && aligned16(k_new), "k_new must be non-NULL and 16-byte aligned");
     CHECK(v_new == nullptr || aligned16(v_new), "v_new must be 16-byte aligned");
     CHECK(k_idx_new == nullptr || k_idx != nullptr, "k_idx_new needs the k_idx cache");
@@ -446,9 +558,10 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
         for (int b = 0; b < batch; ++b) max_len = p.p[b] + tq > max_len ? p.p[b] + tq : max_len;
         CHECK(stride_ok(kv_new_seq_stride) && kv_new_seq_stride >= int64_t{tq} * qsa::kHkv * qsa::kD,
               "kv_new_seq_stride too small");
-        CHECK(k_idx == nullptr || (stride_ok(k_idx_seq_stride) && k_idx_seq_stride >= max_len * qsa::kDi),
+        CHECK(paged || k_idx == nullptr ||
+                  (stride_ok(k_idx_seq_stride) && k_idx_seq_stride >= max_len * qsa::kDi),
               "k_idx_seq_stride smaller than the rows the new tokens reach");
-        CHECK(k_idx == nullptr || kbar_seq_stride >= (max_len / qsa::kBlock) * qsa::kDi,
+        CHECK(paged || k_idx == nullptr || kbar_seq_stride >= (max_len / qsa::kBlock) * qsa::kDi,
               "kbar_seq_stride smaller than the blocks the new tokens complete");
     }
     const size_t sel_ws = align256(qsa::decode_select_ws_bytes(batch * tq));
@@ -474,13 +587,87 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
     ap.rope = rp;
     hipError_t e = qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq,
                                                    budget, scores, scores_seq_stride, scores_ld, sel, sel_seq_stride,
-                                                   workspace, &ap, stream);
+                                                   workspace, &ap, paged ? &pm : nullptr, stream);
     if (e != hipSuccess) return hip_result(e, "decode_step index-select launch");
     return hip_result(qsa::launch_attn_decode_ex(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
                                                  sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
                                                  out_seq_stride, lse, gate, gate_seq_stride,
-                                                 static_cast<char*>(workspace) + sel_ws, &rp, stream),
+                                                 static_cast<char*>(workspace) + sel_ws, &rp,
+                                                 paged ? &pm : nullptr, stream),
                       "decode_step attention launch");
+}
+
+qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
+                             const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
+                             const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                             const uint16_t* k_idx_new,
+                             uint16_t* k_cache, uint16_t* v_cache, int64_t kv_seq_stride,
+                             uint16_t* k_idx, int64_t k_idx_seq_stride,
+                             uint16_t* kbar, int64_t kbar_seq_stride,
+                             const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
+                             float softmax_scale, const qsa_rope_t* rope,
+                             float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                             int32_t* sel, int64_t sel_seq_stride,
+                             uint16_t* out, int64_t out_seq_stride, float* lse,
+                             const uint16_t* gate, int64_t gate_seq_stride,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_step_impl(q, q_seq_stride, k_new, v_new, kv_new_seq_stride, q_idx, q_idx_seq_stride, k_idx_new,
+                            k_cache, v_cache, kv_seq_stride, k_idx, k_idx_seq_stride, kbar, kbar_seq_stride, nullptr,
+                            q_pos, batch, tq, budget, softmax_scale, rope, scores, scores_ld, scores_seq_stride, sel,
+                            sel_seq_stride, out, out_seq_stride, lse, gate, gate_seq_stride, workspace,
+                            workspace_bytes, stream);
+}
+
+qsa_status_t qsa_decode_step_paged(const uint16_t* q, int64_t q_seq_stride,
+                                   const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
+                                   const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                   const uint16_t* k_idx_new, const qsa_paged_cache_t* cache,
+                                   const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
+                                   float softmax_scale, const qsa_rope_t* rope,
+                                   float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                   int32_t* sel, int64_t sel_seq_stride,
+                                   uint16_t* out, int64_t out_seq_stride, float* lse,
+                                   const uint16_t* gate, int64_t gate_seq_stride,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    CHECK(cache != nullptr, "cache is NULL");
+    return decode_step_impl(q, q_seq_stride, k_new, v_new, kv_new_seq_stride, q_idx, q_idx_seq_stride, k_idx_new,
+                            nullptr, nullptr, 0, nullptr, 0, nullptr, 0, cache, q_pos, batch, tq, budget,
+                            softmax_scale, rope, scores, scores_ld, scores_seq_stride, sel, sel_seq_stride, out,
+                            out_seq_stride, lse, gate, gate_seq_stride, workspace, workspace_bytes, stream);
+}
+
+qsa_status_t qsa_paged_append(const qsa_paged_cache_t* cache,
+                              const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
+                              const uint16_t* k_idx_new, int64_t k_idx_new_seq_stride,
+                              const int32_t* pos0, int32_t batch, int32_t n_tokens, const qsa_rope_t* rope,
+                              hipStream_t stream) {
+    TRY(check_batch(batch));
+    CHECK(n_tokens >= 0, "n_tokens = %d is negative", n_tokens);
+    CHECK(k_new == nullptr || aligned16(k_new), "k_new must be 16-byte aligned");
+    CHECK(v_new == nullptr || aligned16(v_new), "v_new must be 16-byte aligned");
+    CHECK(k_idx_new == nullptr || aligned16(k_idx_new), "k_idx_new must be 16-byte aligned");
+    qsa::Positions p;
+    TRY(take_positions(pos0, batch, n_tokens, "pos0", p));
+    qsa_rope_t rp;
+    TRY(take_rope(rope, rp));
+    qsa::PageMap pm{};
+    CHECK(cache != nullptr, "cache is NULL");
+    const bool compress = cache->kbar != nullptr;
+    TRY(take_paged(cache, p, batch, n_tokens, k_new != nullptr || v_new != nullptr,
+                   k_idx_new != nullptr || compress, compress, pm));
+    if (n_tokens == 0) return ok();
+    if (batch > 1) {
+        CHECK((k_new == nullptr && v_new == nullptr) ||
+                  (stride_ok(kv_new_seq_stride) && kv_new_seq_stride >= int64_t{n_tokens} * qsa::kHkv * qsa::kD),
+              "kv_new_seq_stride too small");
+        CHECK(k_idx_new == nullptr ||
+                  (stride_ok(k_idx_new_seq_stride) && k_idx_new_seq_stride >= int64_t{n_tokens} * qsa::kDi),
+              "k_idx_new_seq_stride too small");
+    }
+    return hip_result(qsa::launch_paged_append(pm, cache->k, cache->v, cache->k_idx, cache->kbar, k_new, v_new,
+                                               kv_new_seq_stride, k_idx_new, k_idx_new_seq_stride, p, batch,
+                                               n_tokens, rp, stream),
+                      "paged_append launch");
 }
 
 }  // extern "C"

@@ -23,6 +23,34 @@ struct Positions {
     int32_t p[QSA_MAX_BATCH];
 };
 
+// Paged caches (block table): token n of sequence b sits in page
+// table[b * ts + (n >> shift)], row n & (P - 1) of it, P = 1 << shift tokens per
+// page (a multiple of 64, so a page holds whole micro-blocks and whole
+// 16-block tiles of block keys: block j sits in the page of token 4j, row
+// j & (P/4 - 1)).  Page ids read from the table are clamped to
+// [0, n_pages), so every access stays inside the pools whatever the table
+// holds.
+struct PageMap {
+    const int32_t* table;
+    int64_t ts;
+    int shift;
+    int n_pages;
+};
+
+__device__ __forceinline__ int page_of(const PageMap& pm, int b, int64_t n) {
+    const int pg = pm.table[b * pm.ts + (n >> pm.shift)];
+    return min(max(pg, 0), pm.n_pages - 1);
+}
+
+// physical token row of token n, and physical block-key row of block j
+__device__ __forceinline__ int64_t phys_token(const PageMap& pm, int b, int64_t n) {
+    return (static_cast<int64_t>(page_of(pm, b, n)) << pm.shift) | (n & ((int64_t{1} << pm.shift) - 1));
+}
+__device__ __forceinline__ int64_t phys_block(const PageMap& pm, int b, int64_t j) {
+    return (static_cast<int64_t>(page_of(pm, b, j * 4)) << (pm.shift - 2)) |
+           (j & ((int64_t{1} << (pm.shift - 2)) - 1));
+}
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -74,11 +102,12 @@ hipError_t launch_compress(const uint16_t* k_idx, int64_t ks, int batch, int blo
                            int block_end, uint16_t* kbar, int64_t kbs, hipStream_t stream);
 
 // row_flags (may be null): only the 64-row tiles holding a row with a nonzero flag are
-// scored, and nothing while *n_flagged (if given) is zero
+// scored, and nothing while *n_flagged (if given) is zero.  pm (may be null):
+// kbar is a page pool addressed through the block table (here and below).
 hipError_t launch_index_scores(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
                                int64_t kbs, const Positions& pos0, int batch, int tq,
                                float* scores, int64_t ld, int64_t ss, const int* row_flags,
-                               const int* n_flagged, hipStream_t stream);
+                               const int* n_flagged, const PageMap* pm, hipStream_t stream);
 
 // row_flags (may be null): only rows with a nonzero flag are selected; their flags are cleared
 hipError_t launch_select(const float* scores, int64_t ld, int64_t ss, const Positions& pos0,
@@ -99,10 +128,11 @@ struct IndexCollect {
 };
 
 hipError_t launch_index_sample(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
-                               const Positions& pos0, int batch, int tq, float* sample, hipStream_t stream);
+                               const Positions& pos0, int batch, int tq, float* sample, const PageMap* pm,
+                               hipStream_t stream);
 hipError_t launch_index_collect(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
                                 const Positions& pos0, int batch, int tq, int max_cols, const IndexCollect& col,
-                                hipStream_t stream);
+                                const PageMap* pm, hipStream_t stream);
 
 size_t prefill_select_ws_bytes(int batch, int tq);
 // whole index-select of a prefill chunk; scores [B][tq][ld] is used only by rows
@@ -110,13 +140,13 @@ size_t prefill_select_ws_bytes(int batch, int tq);
 hipError_t launch_prefill_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
                                        const Positions& pos0, int batch, int tq, int budget, float* scores,
                                        int64_t ld, int64_t ss, int32_t* sel, int64_t sels, void* ws,
-                                       hipStream_t stream);
+                                       const PageMap* pm, hipStream_t stream);
 
 hipError_t launch_attn_prefill(const uint16_t* q, int64_t qs, const uint16_t* k,
                                const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                                const Positions& pos0, int batch, int tq, int budget, float scale,
                                uint16_t* out, int64_t os, float* lse, int64_t lss, const uint16_t* gate,
-                               int64_t gs, hipStream_t stream);
+                               int64_t gs, const PageMap* pm, hipStream_t stream);
 
 // Decode rows: tq (1 .. kMaxDecodeTq) consecutive query tokens per sequence,
 // token t of sequence b at position pos[b] + t; row r = b * tq + t.  Per
@@ -126,12 +156,13 @@ constexpr int kMaxDecodeTq = QSA_MAX_DECODE_TQ;
 
 size_t decode_workspace_bytes(int rows, int budget);
 // decode attention with optional rotation of q on load (rope non-null);
-// gate (nullable, laid out as out with sequence stride gs): the output gate
+// gate (nullable, laid out as out with sequence stride gs): the output gate;
+// pm (nullable): k / v are page pools addressed through the block table
 hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* k,
                                  const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                                  const Positions& pos, int batch, int tq, int budget, float scale,
                                  uint16_t* out, int64_t os, float* lse, const uint16_t* gate, int64_t gs,
-                                 void* ws, const qsa_rope_t* rope, hipStream_t stream);
+                                 void* ws, const qsa_rope_t* rope, const PageMap* pm, hipStream_t stream);
 
 // fused decode index-select (scores + selection of the decode rows); the
 // workspace must be zero before its first use and is left zero by each call
@@ -158,7 +189,16 @@ struct DecodeAppend {
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
                                       int64_t kbs, const Positions& pos, int batch, int tq, int budget,
                                       float* scores, int64_t ss, int64_t sld, int32_t* sel, int64_t sels,
-                                      void* ws, const DecodeAppend* append, hipStream_t stream);
+                                      void* ws, const DecodeAppend* append, const PageMap* pm,
+                                      hipStream_t stream);
+// Paged caches: the new tokens [pos0[b], pos0[b] + n_tokens) of every sequence
+// are written into their pages (K rotated, V, indexer keys; null inputs are
+// skipped), then the key of every block they complete (when kbar is given).
+hipError_t launch_paged_append(const PageMap& pm, uint16_t* k, uint16_t* v, uint16_t* k_idx, uint16_t* kbar,
+                               const uint16_t* k_new, const uint16_t* v_new, int64_t kvns,
+                               const uint16_t* k_idx_new, int64_t kins, const Positions& pos0, int batch,
+                               int n_tokens, const qsa_rope_t& rope, hipStream_t stream);
+
 hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
                               const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                               const Positions& pos, int batch, int tq, int budget, float scale,

@@ -48,6 +48,15 @@ YARN = rope_params(ROPE_THETA, 4.0, 262144)
 _rope_p = ctypes.POINTER(Rope)
 
 
+class _PagedCacheC(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_idx", ctypes.c_void_p),
+                ("kbar", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
+                ("page_tokens", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
+
+
+_paged_p = ctypes.POINTER(_PagedCacheC)
+
+
 def _rope_arg(rope: Rope | None):
     if rope is None:
         return None
@@ -81,6 +90,14 @@ _SIGNATURES = {
     "qsa_decode_step": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _i64, _c_p, _i64,
                                _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, _rope_p, _c_p, _i64,
                                _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p, _sz, _c_p]),
+    "qsa_paged_append": (_i32, [_paged_p, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _rope_p, _c_p]),
+    "qsa_index_select_prefill_paged": (_i32, [_c_p, _i64, _paged_p, _c_p, _i32, _i32, _i32, _c_p, _i64, _i64,
+                                              _c_p, _i64, _c_p, _sz, _c_p]),
+    "qsa_sparse_attn_prefill_paged": (_i32, [_c_p, _i64, _paged_p, _c_p, _i64, _c_p, _i32, _i32, _i32,
+                                             ctypes.c_float, _c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p]),
+    "qsa_decode_step_paged": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _paged_p, _c_p, _i32, _i32,
+                                     _i32, ctypes.c_float, _rope_p, _c_p, _i64, _i64, _c_p, _i64, _c_p, _i64,
+                                     _c_p, _c_p, _i64, _c_p, _sz, _c_p]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -108,7 +125,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        if L.qsa_abi_version() != 2:
+        if L.qsa_abi_version() != 3:
             raise QSAError("libqsa ABI version mismatch")
         _LIB = L
     return _LIB
@@ -514,4 +531,160 @@ def decode_step_primitives(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kba
     q_att = q_rot if tq > 1 else q_rot[:, 0]
     sel_att = sel if tq > 1 else sel[:, 0]
     sparse_attn_decode(q_att, k_cache, v_cache, sel_att, p, out, lse, workspace, stream=stream, gate=gate)
+    return out
+
+
+# ------------------------------------------------------------------ paged caches
+
+class PagedCache:
+    """Paged caches with a block table (device tensors): k, v [n_pages, P, 2, 256],
+    k_idx [n_pages, P, 128], kbar [n_pages, P/4, 128] and table int32
+    [batch, max_pages]: token n of sequence b sits in page table[b, n // P],
+    row n % P.  Sequences may share the pages of a common prefix."""
+
+    def __init__(self, n_pages: int, page_tokens: int, batch: int, max_pages: int, device="cuda",
+                 with_k_idx: bool = True):
+        P = int(page_tokens)
+        if P < 64 or P & (P - 1):
+            raise QSAError("page_tokens must be a power of two >= 64")
+        bf = torch.bfloat16
+        self.page_tokens, self.n_pages = P, int(n_pages)
+        self.k = torch.zeros((n_pages, P, HKV, D), dtype=bf, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.k_idx = torch.zeros((n_pages, P, DI), dtype=bf, device=device) if with_k_idx else None
+        self.kbar = torch.zeros((n_pages, P // BLOCK, DI), dtype=bf, device=device)
+        self.table = torch.zeros((batch, max_pages), dtype=torch.int32, device=device)
+
+    def c_struct(self) -> _PagedCacheC:
+        for name in ("k", "v", "kbar", "table"):
+            t = getattr(self, name)
+            if not t.is_contiguous():
+                raise QSAError(f"paged cache {name} must be contiguous")
+        return _PagedCacheC(self.k.data_ptr(), self.v.data_ptr(),
+                            0 if self.k_idx is None else self.k_idx.data_ptr(), self.kbar.data_ptr(),
+                            self.table.data_ptr(), self.table.stride(0), self.page_tokens, self.n_pages)
+
+
+def paged_append(cache: PagedCache, pos0, k_new=None, v_new=None, k_idx_new=None, rope: Rope | None = None,
+                 stream=None) -> None:
+    """Write the new tokens pos0[b] .. pos0[b] + T - 1 into their pages: k_new
+    [B, T, 2, 256] rotated (as rope_apply), v_new [B, T, 2, 256], k_idx_new
+    [B, T, 128] (None: skipped), then the key of every block they complete."""
+    ref = next((t for t in (k_new, v_new, k_idx_new) if t is not None), None)
+    if ref is None:
+        raise QSAError("paged_append needs at least one of k_new, v_new, k_idx_new")
+    B, T = ref.shape[0], ref.shape[1]
+    for t, name, inner in ((k_new, "k_new", (HKV, D)), (v_new, "v_new", (HKV, D)), (k_idx_new, "k_idx_new", (DI,))):
+        if t is not None:
+            _need(t, name, torch.bfloat16, inner)
+            if t.shape[0] != B or t.shape[1] != T:
+                raise QSAError(f"{name} must be [B, T, ...] like the other new rows")
+    if k_new is not None and v_new is not None and k_new.stride(0) != v_new.stride(0):
+        raise QSAError("k_new and v_new must share the sequence stride")
+    kv = k_new if k_new is not None else v_new
+    c = cache.c_struct()
+    _check(lib().qsa_paged_append(ctypes.byref(c), _ptr(k_new), _ptr(v_new), 0 if kv is None else kv.stride(0),
+                                  _ptr(k_idx_new), 0 if k_idx_new is None else k_idx_new.stride(0),
+                                  _positions(pos0, B), B, T, _rope_arg(rope), _stream(stream)),
+           "qsa_paged_append")
+
+
+def index_select_prefill_paged(q_idx: torch.Tensor, cache: PagedCache, q_pos0, budget: int, scores: torch.Tensor,
+                               sel: torch.Tensor, workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """index_select_prefill with the block keys in the paged cache."""
+    _need(q_idx, "q_idx", torch.bfloat16, (HI, DI))
+    _need(scores, "scores", torch.float32, ())
+    _need(sel, "sel", torch.int32, (budget,))
+    B, T = q_idx.shape[0], q_idx.shape[1]
+    if scores.shape[0] != B or scores.shape[1] < T or sel.shape[0] != B or sel.shape[1] != T:
+        raise QSAError("scores / sel shapes do not cover the queries")
+    c = cache.c_struct()
+    _check(lib().qsa_index_select_prefill_paged(_ptr(q_idx), q_idx.stride(0), ctypes.byref(c), _positions(q_pos0, B),
+                                                B, T, budget, _ptr(scores), scores.stride(1), scores.stride(0),
+                                                _ptr(sel), sel.stride(0), _ptr(workspace), workspace.numel(),
+                                                _stream(stream)),
+           "qsa_index_select_prefill_paged")
+    return sel
+
+
+def sparse_attn_prefill_paged(q: torch.Tensor, cache: PagedCache, sel: torch.Tensor, q_pos0, out: torch.Tensor,
+                              lse: torch.Tensor | None = None, scale: float = 1.0 / math.sqrt(D), stream=None,
+                              gate=None) -> torch.Tensor:
+    """sparse_attn_prefill with K / V gathered from the paged cache."""
+    _need(q, "q", torch.bfloat16, (HQ, D))
+    _need(out, "out", torch.bfloat16, (HQ, D))
+    B, T = q.shape[0], q.shape[1]
+    budget = sel.shape[-1]
+    _need(sel, "sel", torch.int32, (budget,))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (HQ,))
+        if tuple(lse.shape) != (B, T, HQ):
+            raise QSAError("lse must be [B, T, 24]")
+    g_ptr, g_stride = _gate_args(gate, out)
+    c = cache.c_struct()
+    _check(lib().qsa_sparse_attn_prefill_paged(_ptr(q), q.stride(0), ctypes.byref(c), _ptr(sel), sel.stride(0),
+                                               _positions(q_pos0, B), B, T, budget, float(scale), _ptr(out),
+                                               out.stride(0), _ptr(lse), 0 if lse is None else lse.stride(0),
+                                               g_ptr, g_stride, _stream(stream)),
+           "qsa_sparse_attn_prefill_paged")
+    return out
+
+
+def decode_step_paged(q_raw, k_new_raw, q_idx, cache: PagedCache, pos, budget: int, out, lse, scores, sel,
+                      workspace, stream=None, scale: float = 1.0 / math.sqrt(D), v_new=None, k_idx_new=None,
+                      gate=None, rope: Rope | None = None):
+    """decode_step on the paged cache (same arguments, the caches replaced by
+    `cache`); workspace from decode_step_workspace(B, budget, tq=tq)."""
+    B, tq = q_raw.shape[0], q_raw.shape[1]
+    p_list = _decode_positions(pos, B)
+    _need(q_raw, "q", torch.bfloat16, (HQ, D))
+    _need(k_new_raw, "k_new", torch.bfloat16, (HKV, D))
+    _need(q_idx, "q_idx", torch.bfloat16, (HI, DI))
+    _need(out, "out", torch.bfloat16, (HQ, D))
+    _need(scores, "scores", torch.float32, ())
+    _need(sel, "sel", torch.int32, (budget,))
+    if k_new_raw.shape[1] != tq or q_idx.numel() != B * tq * HI * DI or out.numel() != B * tq * HQ * D:
+        raise QSAError("k_new, q_idx and out must hold tq rows per sequence")
+    if sel.numel() != B * tq * budget or scores.numel() < B * tq * scores.shape[-1]:
+        raise QSAError("sel / scores must hold [B, tq, ...]")
+    if v_new is not None:
+        _need(v_new, "v_new", torch.bfloat16, (HKV, D))
+        if v_new.stride(0) != k_new_raw.stride(0) or v_new.shape[1] != tq:
+            raise QSAError("v_new must match k_new in shape and sequence stride")
+    if k_idx_new is not None and (not isinstance(k_idx_new, torch.Tensor) or k_idx_new.device.type != "cuda"
+                                  or k_idx_new.dtype != torch.bfloat16 or not k_idx_new.is_contiguous()
+                                  or k_idx_new.numel() != B * tq * DI):
+        raise QSAError("k_idx_new must be a contiguous bf16 device tensor [B, tq, 128]")
+    if lse is not None and (not lse.is_contiguous() or lse.numel() != B * tq * HQ):
+        raise QSAError("lse must be contiguous [B, tq, 24]")
+    g_ptr, g_stride = _gate_args(gate, out)
+    c = cache.c_struct()
+    _check(lib().qsa_decode_step_paged(_ptr(q_raw), q_raw.stride(0), _ptr(k_new_raw), _ptr(v_new),
+                                       k_new_raw.stride(0), _ptr(q_idx), q_idx.stride(0), _ptr(k_idx_new),
+                                       ctypes.byref(c), _positions(p_list, B), B, tq, budget, float(scale),
+                                       _rope_arg(rope), _ptr(scores), scores.shape[-1], scores.stride(0), _ptr(sel),
+                                       sel.stride(0), _ptr(out), out.stride(0), _ptr(lse), g_ptr, g_stride,
+                                       _ptr(workspace), workspace.numel(), _stream(stream)),
+           "qsa_decode_step_paged")
+    return out
+
+
+def prefill_layer_paged(q_raw, k_new_raw, v_new, q_idx, k_idx_new, cache: PagedCache, q_pos0: int, budget: int,
+                        out, lse, bufs: PrefillBuffers, q_rot, stream=None, gate=None, rope: Rope | None = None):
+    """prefill_layer on the paged cache: the new K (rotated), V and indexer-key
+    rows are written into their pages with the keys of the blocks they
+    complete (paged_append), then per query chunk the fused index-select and
+    attention read through the block table."""
+    B, tq = q_raw.shape[0], q_raw.shape[1]
+    pos = [q_pos0] * B
+    rope_apply(q_raw, pos, out=q_rot, rope=rope, stream=stream)
+    paged_append(cache, pos, k_new=k_new_raw, v_new=v_new, k_idx_new=k_idx_new, rope=rope, stream=stream)
+    for c0 in range(0, tq, bufs.chunk):
+        c1 = min(tq, c0 + bufs.chunk)
+        cpos = [q_pos0 + c0] * B
+        index_select_prefill_paged(q_idx[:, c0:c1], cache, cpos, budget, bufs.scores, bufs.sel[:, c0:c1],
+                                   bufs.workspace, stream=stream)
+        sparse_attn_prefill_paged(q_rot[:, c0:c1], cache, bufs.sel[:, c0:c1], cpos, out[:, c0:c1],
+                                  None if lse is None else lse[:, c0:c1], stream=stream,
+                                  gate=None if gate is None else gate[:, c0:c1])
     return out

@@ -18,6 +18,8 @@
  *   qsa_index_select_prefill steps 2 + 3 for a prefill chunk, no score matrix
  *   qsa_sparse_attn_prefill  attention over the selected tokens  (step 4)
  *   qsa_sparse_attn_decode   the same for one new token per sequence
+ *   qsa_decode_step          a whole serving decode step in one call
+ *   qsa_*_paged              the same on paged caches (block table)
  *
  * Conventions shared by every call
  *   - bf16 tensors are passed as uint16_t bit patterns; every tensor pointer
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 #define QSA_MAX_BATCH 256
 #define QSA_MAX_BUDGET 2048
 
@@ -300,6 +302,87 @@ qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,
                              uint16_t* out, int64_t out_seq_stride, float* lse,
                              const uint16_t* gate, int64_t gate_seq_stride,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Paged caches with a block table (Qwen3.8-Flash-Next blog, section
+ * "Attention: GDN + QSA": online serving with high prefix-cache reuse, a 90%
+ * prefix-cache hit rate).  The four caches are pools of pages of P tokens:
+ *   k, v    [n_pages][P][2][256]   (K rotated, as in the contiguous caches)
+ *   k_idx   [n_pages][P][128]
+ *   kbar    [n_pages][P/4][128]
+ * block_table is DEVICE int32 [batch][table_stride]: token n of sequence b
+ * sits in page block_table[b][n / P], row n % P of it (block j in the page
+ * of token 4j, row j % (P/4)).  One table serves all four pools.  P is a power
+ * of two in [64, 65536]; each sequence's table row must hold the pages of
+ * its tokens up to the last position a call touches (checked against
+ * table_stride when batch > 1; the entries themselves live on the device and
+ * are not read by the host).  Page ids are clamped to [0, n_pages) on the
+ * device, so a bad table gives wrong values, never an access outside the
+ * pools.  Sequences may share pages (a common prefix); pages that a call
+ * writes must belong to one sequence only.  Results are bit-identical to the
+ * contiguous entry points on the same logical contents.
+ */
+typedef struct {
+    uint16_t*      k;
+    uint16_t*      v;
+    uint16_t*      k_idx;
+    uint16_t*      kbar;
+    const int32_t* block_table;
+    int64_t        table_stride;
+    int32_t        page_tokens;
+    int32_t        n_pages;
+} qsa_paged_cache_t;
+
+/*
+ * Steps 0 + 1 on a paged cache: the new tokens pos0[b] .. pos0[b] + n_tokens - 1
+ * of every sequence are written into their pages -- the unrotated key rows
+ * k_new [B][T][2][256] rotated as qsa_rope_apply would, v_new [B][T][2][256]
+ * copied (k_new and v_new share kv_new_seq_stride), k_idx_new [B][T][128]
+ * copied; a NULL input is skipped.  Then, when cache->kbar is non-NULL, the
+ * key of every block the new tokens complete (4j + 3 in the range) is written
+ * exactly as qsa_compress_block_keys would, from the block's rows in k_idx.
+ */
+qsa_status_t qsa_paged_append(const qsa_paged_cache_t* cache,
+                              const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
+                              const uint16_t* k_idx_new, int64_t k_idx_new_seq_stride,
+                              const int32_t* pos0, int32_t batch, int32_t n_tokens, const qsa_rope_t* rope,
+                              hipStream_t stream);
+
+/* qsa_index_select_prefill with the block keys read from cache->kbar through
+ * the block table (workspace: qsa_index_select_prefill_workspace_bytes). */
+qsa_status_t qsa_index_select_prefill_paged(const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                            const qsa_paged_cache_t* cache,
+                                            const int32_t* q_pos0, int32_t batch, int32_t tq, int32_t budget,
+                                            float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                            int32_t* sel, int64_t sel_seq_stride,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* qsa_sparse_attn_prefill with K and V gathered from cache->k / cache->v
+ * through the block table. */
+qsa_status_t qsa_sparse_attn_prefill_paged(const uint16_t* q, int64_t q_seq_stride,
+                                           const qsa_paged_cache_t* cache,
+                                           const int32_t* sel, int64_t sel_seq_stride,
+                                           const int32_t* q_pos0, int32_t batch, int32_t tq,
+                                           int32_t budget, float softmax_scale,
+                                           uint16_t* out, int64_t out_seq_stride, float* lse,
+                                           int64_t lse_seq_stride, const uint16_t* gate, int64_t gate_seq_stride,
+                                           hipStream_t stream);
+
+/* qsa_decode_step on a paged cache: the new rows go to their pages, the block
+ * keys and the K / V rows are read through the block table
+ * (workspace: qsa_decode_step_workspace_bytes).  cache->k_idx may be NULL
+ * (then k_idx_new must be NULL and no block key is written). */
+qsa_status_t qsa_decode_step_paged(const uint16_t* q, int64_t q_seq_stride,
+                                   const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
+                                   const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                   const uint16_t* k_idx_new, const qsa_paged_cache_t* cache,
+                                   const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
+                                   float softmax_scale, const qsa_rope_t* rope,
+                                   float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                   int32_t* sel, int64_t sel_seq_stride,
+                                   uint16_t* out, int64_t out_seq_stride, float* lse,
+                                   const uint16_t* gate, int64_t gate_seq_stride,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_dims_and_strings(L):
     assert qsa.dims() == dict(block=4, hq=24, hkv=2, d=256, rot_dim=64, hi=4, di=128)
-    assert L.qsa_abi_version() == 2
+    assert L.qsa_abi_version() == 3
     for s in range(5):
         assert L.qsa_status_string(s)
 
@@ -208,3 +208,62 @@ def test_decode_step_validation(L):
     assert call(tq=4, k_idx_stride=9001 * 128) == INVALID          # rows 9001 .. 9003 out of reach
     assert call(rope=_rope(1e7, 0.9, 262144)) == INVALID and "yarn" in L.qsa_last_error().decode()
     assert call(rope=_rope(1.0)) == INVALID
+
+
+# ---------------------------------------------------------------- paged caches
+
+def _paged(P=256, n_pages=64, table_stride=16, k=FAKE, v=FAKE, k_idx=FAKE, kbar=FAKE, table=FAKE):
+    return qsa._PagedCacheC(k, v, k_idx, kbar, table, table_stride, P, n_pages)
+
+
+def test_paged_append_validation(L):
+    """qsa_paged_append rejects bad page geometry, a short block table, a
+    missing pool and misaligned rows before any launch; zero tokens is a no-op."""
+    p2 = _pos(1000, 3000)
+
+    def call(c, batch=2, n=16, k_new=FAKE, pos=p2, rope=None):
+        return L.qsa_paged_append(None if c is None else ctypes.byref(c), k_new, FAKE, n * 512, FAKE, n * 128,
+                                  pos, batch, n, rope, None)
+
+    assert call(None) == INVALID
+    for P in (32, 48, 96, 1 << 17):
+        assert call(_paged(P=P)) == INVALID, P
+    assert "page_tokens" in L.qsa_last_error().decode()
+    assert call(_paged(n_pages=0)) == INVALID
+    assert call(_paged(table=NULL)) == INVALID
+    assert call(_paged(table=FAKE + 2)) == INVALID                     # int32 table misaligned
+    assert call(_paged(table_stride=11)) == INVALID                     # tokens 0 .. 3015 span 12 pages of 256
+    assert "table_stride" in L.qsa_last_error().decode()
+    assert call(_paged(k_idx=NULL)) == INVALID                          # k_idx rows, compression need the pool
+    assert call(_paged(), k_new=FAKE + 8) == INVALID
+    assert call(_paged(), rope=_rope(1e7, 0.5, 262144)) == INVALID
+    assert call(_paged(), n=0) == OK
+
+
+def test_paged_prefill_and_decode_validation(L):
+    p1 = _pos(5000)
+    ws = L.qsa_index_select_prefill_workspace_bytes(1, 8)
+    # index-select: needs the block-key pool
+    assert L.qsa_index_select_prefill_paged(FAKE, 0, ctypes.byref(_paged(kbar=NULL)), p1, 1, 8, 512, FAKE, 1252,
+                                            8 * 1252, FAKE, 8 * 512, FAKE, ws, None) == INVALID
+    assert L.qsa_index_select_prefill_paged(FAKE, 0, None, p1, 1, 8, 512, FAKE, 1252, 8 * 1252, FAKE, 8 * 512,
+                                            FAKE, ws, None) == INVALID
+    # attention: needs K and V pools, a legal page size
+    for c in (_paged(k=NULL), _paged(v=FAKE + 4), _paged(P=100)):
+        assert L.qsa_sparse_attn_prefill_paged(FAKE, 0, ctypes.byref(c), FAKE, 8 * 512, p1, 1, 8, 512, 0.0625,
+                                               FAKE, 0, NULL, 0, NULL, 0, None) == INVALID
+    # decode step: a new indexer-key row needs the k_idx pool; two sequences need the table stride
+    B, budget = 2, 512
+    p2 = _pos(4099, 9000)
+    ld = 9000 // 4 // 4 * 4 + 4
+    wsd = L.qsa_decode_step_workspace_bytes(B, 1, budget)
+
+    def step(c):
+        return L.qsa_decode_step_paged(FAKE, 24 * 256, FAKE, FAKE, 2 * 256, FAKE, 4 * 128, FAKE, ctypes.byref(c),
+                                       p2, B, 1, budget, 0.0625, None, FAKE, ld, ld, FAKE, budget, FAKE, 24 * 256,
+                                       NULL, NULL, 0, FAKE, wsd, None)
+
+    assert step(_paged(k_idx=NULL, table_stride=64)) == INVALID and "k_idx" in L.qsa_last_error().decode()
+    assert step(_paged(table_stride=35)) == INVALID                     # 9001 tokens need 36 pages of 256
+    assert step(_paged(P=64, table_stride=100)) == INVALID              # ... or 141 pages of 64
+    assert step(_paged(kbar=NULL, table_stride=64)) == INVALID and "kbar" in L.qsa_last_error().decode()
