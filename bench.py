@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--decode-tq", type=int, default=4,
                     help="also time a decode step of this many new tokens per sequence (1 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=48, help="oracle rows timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--page-tokens", type=int, default=256,
+                    help="page size of the paged-cache measurements (0 = skip them)")
     ap.add_argument("--rope", choices=("yarn", "plain"), default="yarn",
                     help="rotary table: the model card's static YaRN (factor 4 over 262144, for contexts past "
                          "262144) or plain rotary")
@@ -149,6 +151,54 @@ class Prefill:
                                       cpos, self.out[:, c0:c1], self.lse[:, c0:c1])
 
 
+def random_pages(torch, B, n_log, seed):
+    """A block table naming distinct pages in a random order."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randperm(B * n_log, generator=g).to(torch.int32).view(B, n_log)
+
+
+class PagedPrefill:
+    """The prefill workload on a paged cache: the cached prefix (rotated K,
+    V, indexer keys, block keys) copied into pages of P tokens in a random
+    order; a step appends the chunk's rows (paged_append) and runs the fused
+    index-select and attention through the block table."""
+
+    def __init__(self, pf, P, seed=5):
+        torch, qsa, wl = pf.torch, pf.qsa, pf.wl
+        B, L, ctx = wl.batch, wl.length, wl.ctx
+        self.pf, self.torch, self.qsa, self.wl = pf, torch, qsa, wl
+        n_log = (L + P - 1) // P
+        self.cache = qsa.PagedCache(B * n_log, P, B, n_log)
+        self.cache.table.copy_(random_pages(torch, B, n_log, seed))
+        for b in range(B):
+            self.cache.write_contiguous(b, ctx, k=pf.k_cache[b], v=pf.v_cache[b], k_idx=pf.k_idx[b],
+                                        kbar=pf.kbar[b])
+        self.v_new = pf.v_cache[:, ctx:].contiguous()
+        self.k_idx_new = pf.k_idx[:, ctx:].contiguous()
+        self.bufs = qsa.PrefillBuffers(B, wl.tq, ctx, wl.budget, wl.chunk)
+        torch.cuda.synchronize()
+
+    def step(self, timer=None):
+        wl, q, pf = self.wl, self.qsa, self.pf
+        B, T, ctx = wl.batch, wl.tq, wl.ctx
+        pos = [ctx] * B
+        with timer("rope"):
+            q.rope_apply(pf.q_raw, pos, out=pf.q_rot, rope=pf.rope)
+        with timer("paged_append"):
+            q.paged_append(self.cache, pos, k_new=pf.k_new, v_new=self.v_new, k_idx_new=self.k_idx_new,
+                           rope=pf.rope)
+        ch = self.bufs.chunk
+        for c0 in range(0, T, ch):
+            c1 = min(T, c0 + ch)
+            cpos = [ctx + c0] * B
+            with timer("index_select"):
+                q.index_select_prefill_paged(pf.q_idx[:, c0:c1], self.cache, cpos, wl.budget, self.bufs.scores,
+                                             self.bufs.sel[:, c0:c1], self.bufs.workspace)
+            with timer("sparse_attn_prefill"):
+                q.sparse_attn_prefill_paged(pf.q_rot[:, c0:c1], self.cache, self.bufs.sel[:, c0:c1], cpos,
+                                            pf.out[:, c0:c1], pf.lse[:, c0:c1])
+
+
 class Decode:
     def __init__(self, wl, x, torch, qsa, rope=None):
         B, ctx = wl.batch, wl.ctx
@@ -203,6 +253,23 @@ class Decode:
         self.qsa.decode_step(self.m_q, self.m_k, self.m_q_idx, self.k_idx, self.k_cache, self.v_cache, self.kbar,
                              self.pos, self.wl.budget, self.m_out, self.m_lse, self.m_scores, self.m_sel, self.m_ws,
                              v_new=self.m_v, k_idx_new=self.m_k_idx, rope=self.rope)
+
+    def paged_setup(self, P, seed=9):
+        """The same caches copied into pages of P tokens in a random order."""
+        torch, qsa, wl = self.torch, self.qsa, self.wl
+        B, L = wl.batch, self.k_cache.shape[1]
+        n_log = (L + P - 1) // P
+        self.cache = qsa.PagedCache(B * n_log, P, B, n_log)
+        self.cache.table.copy_(random_pages(torch, B, n_log, seed))
+        for b in range(B):
+            self.cache.write_contiguous(b, self.pos, k=self.k_cache[b], v=self.v_cache[b], k_idx=self.k_idx[b],
+                                        kbar=self.kbar[b])
+        torch.cuda.synchronize()
+
+    def paged_step(self):
+        self.qsa.decode_step_paged(self.q_raw, self.k_new, self.q_idx, self.cache, self.pos, self.wl.budget,
+                                   self.out, self.lse, self.scores, self.sel, self.ws, v_new=self.v_new,
+                                   k_idx_new=self.k_idx_new, rope=self.rope)
 
     def step(self, timer):
         """One serving decode step through the single qsa_decode_step call: the
@@ -399,6 +466,31 @@ def main():
         "gather_bytes_per_step": geo["gathered_tokens"] * 2 * 2 * 256 * 2,
     }
     log(args, f"prefill: {ms_per_step:.1f} ms/step, {value:.0f} tok/s; kernels {rec['kernels_ms_per_step']}")
+    if args.page_tokens > 0:
+        pp = PagedPrefill(pf, args.page_tokens)
+        for _ in range(args.warmup):
+            pp.step(NullTimer())
+        torch.cuda.synchronize()
+        ptimer = EventTimer(torch)
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            pp.step(ptimer)
+        torch.cuda.synchronize()
+        p_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+        pk = ptimer.totals()
+        pa_ms, pa_n = pk["sparse_attn_prefill"]
+        pa_avg_s = pa_ms / pa_n / 1e3
+        rec["prefill_paged"] = {
+            "page_tokens": args.page_tokens,
+            "pages": "random page order, the cached prefix copied in before timing",
+            "ms_per_step": p_ms,
+            "tokens_per_s": tokens / (p_ms / 1e3),
+            "kernels_ms_per_step": {k: t / args.steps for k, (t, n) in pk.items()},
+            "sparse_attn_prefill_hbm_frac": attn_bytes_per_launch / pa_avg_s / HBM_PEAK,
+            "note": "paged_append also copies the chunk's V and indexer-key rows into their pages",
+        }
+        log(args, f"prefill, paged: {p_ms:.1f} ms/step; kernels {rec['prefill_paged']['kernels_ms_per_step']}")
+        del pp
     del pf
     torch.cuda.empty_cache()
 
@@ -503,6 +595,31 @@ def main():
                 "data": "synthetic new-token rows of the workload's distributions",
             }
             log(args, f"decode, {mt} tokens per sequence: median {m_med * 1e3:.1f} us/step")
+        if args.page_tokens > 0:
+            dd.paged_setup(args.page_tokens)
+            for _ in range(3):
+                dd.paged_step()
+            torch.cuda.synchronize()
+            p_ms = []
+            for _ in range(args.decode_steps):
+                flush.sum()
+                s = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                s.record()
+                dd.paged_step()
+                e.record()
+                torch.cuda.synchronize()
+                p_ms.append(s.elapsed_time(e))
+            p_ms.sort()
+            p_med = p_ms[len(p_ms) // 2]
+            rec["decode_paged"] = {
+                "page_tokens": args.page_tokens,
+                "pages": "random page order",
+                "step_us_median": p_med * 1e3,
+                "step_us_min": p_ms[0] * 1e3,
+                "hbm_frac_step": step_bytes / (p_med / 1e3) / HBM_PEAK,
+            }
+            log(args, f"decode, paged: median {p_med * 1e3:.1f} us/step")
         del dd, flush
         torch.cuda.empty_cache()
 

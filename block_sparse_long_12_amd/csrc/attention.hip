@@ -108,6 +108,52 @@ __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ kg, cons
     ch.vmask = __ballot(valid);
 }
 
+// A row's selection resolved once into LDS (resolve_selection): for slot i
+// the cache row of the block's first token (physical with paged caches) and
+// how many of its 4 tokens are attended (0: no legal block; fewer than 4: the
+// own block, cut at the query).  Per chunk a lane then needs one LDS read
+// instead of a chain of dependent memory loads.
+template <bool kPaged>
+__device__ __forceinline__ void resolve_selection(const int32_t* __restrict__ selrow, int n, int p,
+                                                  const KvPages& kp, int32_t* row, int32_t* nv) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int s = selrow[i];
+        const bool legal = s >= 0 && s <= p / kBlock;
+        const int tok = legal ? kBlock * s : p;
+        int r = tok;
+        if constexpr (kPaged) {
+            const int pg = min(max(kp.tbl[tok >> kp.shift], 0), kp.n_pages - 1);
+            r = (pg << kp.shift) | (tok & ((1 << kp.shift) - 1));
+        }
+        row[i] = r;
+        nv[i] = legal ? min(kBlock, p - kBlock * s + 1) : 0;
+    }
+}
+
+// The chunk of slots cb .. cb+3 from the resolved selection; row_p is the
+// query's own row, read by lanes with nothing to attend.
+__device__ __forceinline__ void load_chunk_lds(const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+                                               const int32_t* row, const int32_t* nv, int cb, int blk_end,
+                                               int row_p, Chunk& ch) {
+    const int lane = threadIdx.x & 63;
+    const int c16 = lane & 15;
+    const int G = lane >> 4;
+    const int slot = cb + (c16 >> 2);
+    const bool in = slot < blk_end;
+    const int rb = row[in ? slot : cb];
+    const int cnt = in ? nv[slot] : 0;
+    const bool valid = (c16 & 3) < cnt;
+    const int64_t r = valid ? rb + (c16 & 3) : row_p;
+    const uint16_t* kr = kg + r * (kHkv * kD);
+    const uint16_t* vr = vg + r * (kHkv * kD);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        ch.ka[s] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * s + 8 * G);
+        ch.vv[s] = *reinterpret_cast<const bf16x8_t*>(vr + 8 * (4 * s + G));
+    }
+    ch.vmask = __ballot(valid);
+}
+
 __device__ __forceinline__ void attend_chunk(const Chunk& ch, const bf16x8_t (&qf)[8], float c,
                                              WaveState& st, uint16_t* vt) {
     const int lane = threadIdx.x & 63;
@@ -168,9 +214,8 @@ __device__ __forceinline__ void attend_chunk(const Chunk& ch, const bf16x8_t (&q
     wave_lds_sync();
 }
 
-// Attend over sel[blk_begin .. blk_end) for the query at position p.
-// kg / vg point at KV head g of the sequence (token stride 2 * 256), or of
-// the page pool when kPaged.
+// Attend over the slots blk_begin .. blk_end of the selection for the query
+// at position p; load(cb, chunk) issues the loads of slots cb .. cb + 3.
 // `cur` must hold the loads of the first chunk (issued by the caller, so they
 // can overlap the query set-up).  Chunks are processed in statically unrolled
 // groups of kUnroll with two named buffers: inside a group the code is
@@ -178,11 +223,8 @@ __device__ __forceinline__ void attend_chunk(const Chunk& ch, const bf16x8_t (&q
 // next chunk's rows stay in flight (a loop-carried pipeline makes the
 // compiler drain all loads at every loop head).  Steps past the end re-read
 // the last chunk's rows (cache hits) and are skipped.
-template <int kUnroll, bool kPaged>
-__device__ __forceinline__ void attend_blocks(const uint16_t* __restrict__ kg,
-                                              const uint16_t* __restrict__ vg,
-                                              const int32_t* __restrict__ selrow, int blk_begin,
-                                              int blk_end, int p, const KvPages& kp, const bf16x8_t (&qf)[8],
+template <int kUnroll, typename Load>
+__device__ __forceinline__ void attend_blocks(Load&& load, int blk_begin, int blk_end, const bf16x8_t (&qf)[8],
                                               float c, WaveState& st, uint16_t* vt, Chunk& cur) {
     const int last = blk_begin + (blk_end - 1 - blk_begin) / 4 * 4;      // first block of the last chunk
     Chunk other;
@@ -192,9 +234,9 @@ __device__ __forceinline__ void attend_blocks(const uint16_t* __restrict__ kg,
             const int c0 = cb + 4 * u;
             const int c1 = c0 + 4;
             const int c2 = c1 + 4;
-            load_chunk<kPaged>(kg, vg, selrow, min(c1, last), blk_end, p, kp, other);
+            load(min(c1, last), other);
             if (c0 < blk_end && cur.vmask != 0ull) attend_chunk(cur, qf, c, st, vt);
-            load_chunk<kPaged>(kg, vg, selrow, min(c2, last), blk_end, p, kp, cur);
+            load(min(c2, last), cur);
             if (c1 < blk_end && other.vmask != 0ull) attend_chunk(other, qf, c, st, vt);
         }
     }
@@ -239,13 +281,6 @@ __device__ __forceinline__ void rotate_q_frags(const RopeAngle& a, bf16x8_t (&qf
         lo[e] = rotate_half_elem(x, y, cs, sn, true);
         hi[e] = rotate_half_elem(y, x, cs, sn, false);
     }
-}
-
-// Loads (and, with `rope`, rotates) the query fragments.
-__device__ __forceinline__ void load_q_frags(const uint16_t* qh, bool ok, int p, const InvFreq* rope,
-                                             bf16x8_t (&qf)[8]) {
-    issue_q_frags(qh, ok, qf);
-    if (rope != nullptr) rotate_q_frags(rope_angle(p, *rope), qf);
 }
 
 // Output gate (blog, "Training stability": the attention output gating
@@ -303,6 +338,8 @@ __global__ __launch_bounds__(128) void attn_prefill_kernel(
     int64_t os, float* __restrict__ lse, int64_t lss, const uint16_t* __restrict__ gate, int64_t gs,
     InvFreq inv, int rope_q, PageMap pm) {
     __shared__ uint16_t vt_all[2 * kVtElems];
+    __shared__ int32_t s_row[QSA_MAX_BUDGET];
+    __shared__ int32_t s_nv[QSA_MAX_BUDGET];
     const int g = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int c16 = lane & 15;
@@ -317,14 +354,19 @@ __global__ __launch_bounds__(128) void attn_prefill_kernel(
     KvPages kp;
     kv_bases<kPaged>(k, v, kvs, pm, b, g, p, kg, vg, kp);
     const int32_t* selrow = sel + b * sels + static_cast<int64_t>(i) * budget;
-    Chunk first;
-    load_chunk<kPaged>(kg, vg, selrow, 0, budget, p, kp, first);
     bf16x8_t qf[8];
     const uint16_t* qrow = q + b * qs + static_cast<int64_t>(i) * (kHq * kD);
-    load_q_frags(qrow + (head_ok ? head : 0) * kD, head_ok, p, rope_q ? &inv : nullptr, qf);
+    issue_q_frags(qrow + (head_ok ? head : 0) * kD, head_ok, qf);
+    resolve_selection<kPaged>(selrow, budget, p, kp, s_row, s_nv);
+    __syncthreads();
+    const int row_p = kPaged ? (kp.pp << kp.shift) | (p & ((1 << kp.shift) - 1)) : p;
+    auto load = [&](int cb, Chunk& ch) { load_chunk_lds(kg, vg, s_row, s_nv, cb, budget, row_p, ch); };
+    Chunk first;
+    load(0, first);
+    if (rope_q) rotate_q_frags(rope_angle(p, inv), qf);
     WaveState st;
     init_state(st);
-    attend_blocks<8, kPaged>(kg, vg, selrow, 0, budget, p, kp, qf, c, st, vt_all + g * kVtElems, first);
+    attend_blocks<8>(load, 0, budget, qf, c, st, vt_all + g * kVtElems, first);
 
     if (head_ok) {
         const float inv_l = 1.f / st.l;
@@ -424,7 +466,8 @@ __global__ __launch_bounds__(128) void attn_decode_split_kernel(
     if (rope_q) rotate_q_frags(rope_angle(p, inv), qf);
     WaveState st;
     init_state(st);
-    attend_blocks<2, kPaged>(kg, vg, selrow, blk_begin, blk_end, p, kp, qf, c, st, vt_all + g * kVtElems, first);
+    auto load = [&](int cb, Chunk& ch) { load_chunk<kPaged>(kg, vg, selrow, cb, blk_end, p, kp, ch); };
+    attend_blocks<2>(load, blk_begin, blk_end, qf, c, st, vt_all + g * kVtElems, first);
     if (head_ok) {
         const int64_t idx = (static_cast<int64_t>(r) * n_split + s) * kHq + head;
         if (G == 0) {

@@ -77,6 +77,7 @@ qsa_status_t take_paged(const qsa_paged_cache_t* c, const qsa::Positions& p, int
     const int32_t P = c->page_tokens;
     CHECK(P >= 64 && P <= 65536 && (P & (P - 1)) == 0, "page_tokens = %d must be a power of two in [64, 65536]", P);
     CHECK(c->n_pages >= 1, "n_pages = %d must be >= 1", c->n_pages);
+    CHECK(int64_t{c->n_pages} * P <= INT32_MAX, "n_pages * page_tokens must stay below 2^31 rows");
     CHECK(!need_kv || (c->k != nullptr && c->v != nullptr && aligned16(c->k) && aligned16(c->v)),
           "cache k and v must be non-NULL and 16-byte aligned");
     CHECK(!need_k_idx || (c->k_idx != nullptr && aligned16(c->k_idx)),

@@ -555,6 +555,37 @@ class PagedCache:
         self.kbar = torch.zeros((n_pages, P // BLOCK, DI), dtype=bf, device=device)
         self.table = torch.zeros((batch, max_pages), dtype=torch.int32, device=device)
 
+    def _rows(self, b: int, n_tok: int) -> torch.Tensor:
+        n = torch.arange(n_tok, device=self.table.device)
+        return self.table[b][n // self.page_tokens].long() * self.page_tokens + n % self.page_tokens
+
+    def _blocks(self, b: int, n_blk: int) -> torch.Tensor:
+        j = torch.arange(n_blk, device=self.table.device)
+        per = self.page_tokens // BLOCK
+        return self.table[b][(BLOCK * j) // self.page_tokens].long() * per + j % per
+
+    def write_contiguous(self, b: int, upto: int, k=None, v=None, k_idx=None, kbar=None) -> None:
+        """Copy tokens 0 .. upto - 1 of sequence b from contiguous caches
+        (k, v [L, 2, 256], k_idx [L, 128]) and the keys of its complete blocks
+        (kbar [L/4, 128]) into the pages its table row names."""
+        r = self._rows(b, upto)
+        if k is not None:
+            self.k.view(-1, HKV, D)[r] = k[:upto]
+        if v is not None:
+            self.v.view(-1, HKV, D)[r] = v[:upto]
+        if k_idx is not None:
+            self.k_idx.view(-1, DI)[r] = k_idx[:upto]
+        if kbar is not None and upto // BLOCK:
+            self.kbar.view(-1, DI)[self._blocks(b, upto // BLOCK)] = kbar[:upto // BLOCK]
+
+    def read_contiguous(self, b: int, n_tok: int):
+        """Tokens 0 .. n_tok - 1 of sequence b (k, v, k_idx) and the keys of its
+        complete blocks, gathered from the pages into new tensors."""
+        r = self._rows(b, n_tok)
+        k_idx = None if self.k_idx is None else self.k_idx.view(-1, DI)[r]
+        return (self.k.view(-1, HKV, D)[r], self.v.view(-1, HKV, D)[r], k_idx,
+                self.kbar.view(-1, DI)[self._blocks(b, n_tok // BLOCK)])
+
     def c_struct(self) -> _PagedCacheC:
         for name in ("k", "v", "kbar", "table"):
             t = getattr(self, name)

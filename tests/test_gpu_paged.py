@@ -40,37 +40,12 @@ def _table(B, n_log, n_pages, seed, share=0):
     return t
 
 
-def _rows(table, b, n_tok, P):
-    """Physical token rows of tokens 0 .. n_tok - 1 of sequence b."""
-    n = torch.arange(n_tok, device="cuda")
-    return table[b][n // P].long() * P + n % P
-
-
-def _blocks(table, b, n_blk, P):
-    j = torch.arange(n_blk, device="cuda")
-    return table[b][(4 * j) // P].long() * (P // 4) + j % (P // 4)
-
-
 def _scatter(cache, b, upto, k=None, v=None, ki=None, kb=None):
-    """Contiguous rows 0 .. upto - 1 (and their complete blocks) of sequence b into its pages."""
-    P = cache.page_tokens
-    r = _rows(cache.table, b, upto, P)
-    if k is not None:
-        cache.k.view(-1, 2, 256)[r] = k[:upto]
-    if v is not None:
-        cache.v.view(-1, 2, 256)[r] = v[:upto]
-    if ki is not None:
-        cache.k_idx.view(-1, 128)[r] = ki[:upto]
-    if kb is not None and upto // 4:
-        cache.kbar.view(-1, 128)[_blocks(cache.table, b, upto // 4, P)] = kb[:upto // 4]
+    cache.write_contiguous(b, upto, k=k, v=v, k_idx=ki, kbar=kb)
 
 
 def _gather(cache, b, n_tok):
-    P = cache.page_tokens
-    r = _rows(cache.table, b, n_tok, P)
-    blk = _blocks(cache.table, b, n_tok // 4, P)
-    return (cache.k.view(-1, 2, 256)[r], cache.v.view(-1, 2, 256)[r], cache.k_idx.view(-1, 128)[r],
-            cache.kbar.view(-1, 128)[blk])
+    return cache.read_contiguous(b, n_tok)
 
 
 def _same(a, b, what):
