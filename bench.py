@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--decode-tq", type=int, default=4,
                     help="also time a decode step of this many new tokens per sequence (1 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=48, help="oracle rows timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet measurements")
+    ap.add_argument("--gdn-tokens", type=int, default=104858, help="tokens of the Gated DeltaNet prefill")
     ap.add_argument("--page-tokens", type=int, default=256,
                     help="page size of the paged-cache measurements (0 = skip them)")
     ap.add_argument("--rope", choices=("yarn", "plain"), default="yarn",
@@ -384,6 +386,69 @@ def cpu_baseline(wl, x, n_rows: int, args):
 
 # ------------------------------------------------------------------ main
 
+def gdn_measure(args, torch, qsa, I):
+    """The Gated DeltaNet token mixer of the other 3 of 4 layers: a prefill
+    of --gdn-tokens tokens (one sequence, the new-token count of the QSA
+    prefill) and a decode step of 4 sequences, on seeded synthetic inputs."""
+    T, Bd = args.gdn_tokens, 4
+    x = I.make_gdn_inputs(1, T, seed=3)
+    q, k, v, g, beta = (t.cuda() for t in (x.q, x.k, x.v, x.g, x.beta))
+    state = x.s0.cuda()
+    out = torch.empty_like(v)
+    ws = qsa.gdn_prefill_workspace(1, T)
+    for _ in range(args.warmup):
+        qsa.gdn_prefill(q, k, v, g, beta, state, out, ws)
+    torch.cuda.synchronize()
+    t_ms = []
+    for _ in range(max(1, args.steps)):
+        s_ev = torch.cuda.Event(enable_timing=True)
+        e_ev = torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        qsa.gdn_prefill(q, k, v, g, beta, state, out, ws)
+        e_ev.record()
+        torch.cuda.synchronize()
+        t_ms.append(s_ev.elapsed_time(e_ev))
+    t_ms.sort()
+    pre_ms = t_ms[len(t_ms) // 2]
+    # algorithmic bytes: q, k, v, g, beta read and o written once, the state read and written once
+    io = T * (2 * 16 * 128 * 2 + 48 * 128 * 2 * 2 + 48 * 4 * 2) + 2 * 48 * 128 * 128 * 4
+    del x, q, k, v, g, beta, out, ws, state
+    torch.cuda.empty_cache()
+    xd = I.make_gdn_inputs(Bd, 1, seed=4)
+    dq, dk, dv, dg, db = (t[:, 0].contiguous().cuda() for t in (xd.q, xd.k, xd.v, xd.g, xd.beta))
+    dstate = xd.s0.cuda()
+    dout = torch.empty_like(dv)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        qsa.gdn_decode(dq, dk, dv, dg, db, dstate, dout)
+    d_ms = []
+    for _ in range(args.decode_steps):
+        flush.sum()
+        s_ev = torch.cuda.Event(enable_timing=True)
+        e_ev = torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        qsa.gdn_decode(dq, dk, dv, dg, db, dstate, dout)
+        e_ev.record()
+        torch.cuda.synchronize()
+        d_ms.append(s_ev.elapsed_time(e_ev))
+    d_ms.sort()
+    dec_us = d_ms[len(d_ms) // 2] * 1e3
+    dec_bytes = Bd * (2 * 48 * 128 * 128 * 4 + 2 * 16 * 128 * 2 + 2 * 48 * 128 * 2 + 2 * 48 * 4)
+    del flush
+    torch.cuda.empty_cache()
+    res = {
+        "prefill": {"workload": f"gdn_prefill_B1_T{T}", "ms": pre_ms, "tokens_per_s": T / (pre_ms / 1e3),
+                    "algorithmic_bytes": io, "hbm_frac": io / (pre_ms / 1e3) / HBM_PEAK,
+                    "bound": "latency of the chunk-sequential state pass (192 workgroups)"},
+        "decode": {"workload": f"gdn_decode_B{Bd}", "step_us_median": dec_us, "step_us_min": d_ms[0] * 1e3,
+                   "algorithmic_bytes": dec_bytes, "hbm_frac": dec_bytes / (dec_us / 1e6) / HBM_PEAK,
+                   "cache_flushed": True},
+        "data": "synthetic: q, k, v N(0,1) bf16; g = -softplus(z - 3), beta = sigmoid(z'); state N(0, 0.01)",
+    }
+    log(args, f"gdn: prefill {pre_ms:.2f} ms ({T / pre_ms * 1e3:.0f} tok/s), decode {dec_us:.1f} us")
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -622,6 +687,9 @@ def main():
             log(args, f"decode, paged: median {p_med * 1e3:.1f} us/step")
         del dd, flush
         torch.cuda.empty_cache()
+
+    if not args.no_gdn:
+        rec["gdn"] = gdn_measure(args, torch, qsa, I)
 
     if args.cpu_rows > 0:
         rec["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_rows, args)

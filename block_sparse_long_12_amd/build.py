@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build", "libqsa")
 LIB_PATH = os.path.join(HERE, "libqsa.so")
 
 SOURCES = ["rope.hip", "compress.hip", "index_scores.hip", "select.hip", "prefill_select.hip",
-           "attention.hip", "decode.hip", "paged.hip", "qsa_abi.hip"]
+           "attention.hip", "decode.hip", "paged.hip", "gdn.hip", "qsa_abi.hip"]
 ARCH = os.environ.get("QSA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

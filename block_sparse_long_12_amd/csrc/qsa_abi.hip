@@ -671,4 +671,55 @@ qsa_status_t qsa_paged_append(const qsa_paged_cache_t* cache,
                       "paged_append launch");
 }
 
+size_t qsa_gdn_prefill_workspace_bytes(int32_t batch, int32_t n_tokens) {
+    if (batch < 1 || batch > QSA_MAX_BATCH || n_tokens < 0) return 0;
+    return qsa::gdn_prefill_ws_bytes(batch, n_tokens);
+}
+
+static qsa_status_t check_gdn_common(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                                     const float* beta, const float* state, const uint16_t* out) {
+    CHECK(q != nullptr && k != nullptr && v != nullptr && g != nullptr && beta != nullptr && state != nullptr &&
+              out != nullptr,
+          "q, k, v, g, beta, state and out must be non-NULL");
+    CHECK(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(state),
+          "q, k, v, out and state must be 16-byte aligned");
+    CHECK((reinterpret_cast<uintptr_t>(g) & 3u) == 0 && (reinterpret_cast<uintptr_t>(beta) & 3u) == 0,
+          "g and beta must be 4-byte aligned");
+    return QSA_OK;
+}
+
+qsa_status_t qsa_gdn_prefill(const uint16_t* q, const uint16_t* k, int64_t qk_seq_stride,
+                             const uint16_t* v, int64_t v_seq_stride,
+                             const float* g, const float* beta, int64_t gate_seq_stride,
+                             float* state, int32_t batch, int32_t n_tokens,
+                             uint16_t* out, int64_t out_seq_stride,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    TRY(check_batch(batch));
+    TRY(check_gdn_common(q, k, v, g, beta, state, out));
+    CHECK(n_tokens >= 0 && n_tokens <= (1 << 30), "n_tokens = %d outside [0, 2^30]", n_tokens);
+    if (n_tokens == 0) return ok();
+    if (batch > 1) {
+        const int64_t T = n_tokens;
+        CHECK(stride_ok(qk_seq_stride) && qk_seq_stride >= T * 16 * 128, "qk_seq_stride too small");
+        CHECK(stride_ok(v_seq_stride) && v_seq_stride >= T * 48 * 128, "v_seq_stride too small");
+        CHECK(stride_ok(out_seq_stride) && out_seq_stride >= T * 48 * 128, "out_seq_stride too small");
+        CHECK(gate_seq_stride >= T * 48, "gate_seq_stride too small");
+    }
+    const size_t need = qsa::gdn_prefill_ws_bytes(batch, n_tokens);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(QSA_ERR_WORKSPACE, "gdn prefill workspace needs %zu bytes, got %zu", need,
+                    workspace == nullptr ? size_t{0} : workspace_bytes);
+    CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, "workspace must be 256-byte aligned");
+    const qsa::GdnIn in{q, k, qk_seq_stride, v, v_seq_stride, g, beta, gate_seq_stride, state, out, out_seq_stride};
+    return hip_result(qsa::launch_gdn_prefill(in, batch, n_tokens, workspace, stream), "gdn_prefill launch");
+}
+
+qsa_status_t qsa_gdn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                            const float* beta, float* state, int32_t batch, uint16_t* out, hipStream_t stream) {
+    TRY(check_batch(batch));
+    TRY(check_gdn_common(q, k, v, g, beta, state, out));
+    const qsa::GdnIn in{q, k, 16 * 128, v, 48 * 128, g, beta, 48, state, out, 48 * 128};
+    return hip_result(qsa::launch_gdn_decode(in, batch, stream), "gdn_decode launch");
+}
+
 }  // extern "C"

@@ -199,6 +199,25 @@ hipError_t launch_paged_append(const PageMap& pm, uint16_t* k, uint16_t* v, uint
                                const uint16_t* k_idx_new, int64_t kins, const Positions& pos0, int batch,
                                int n_tokens, const qsa_rope_t& rope, hipStream_t stream);
 
+// Gated DeltaNet token mixer: inputs and outputs of one call (T tokens per
+// sequence; decode: T = 1).
+struct GdnIn {
+    const uint16_t* q;   // [B][T][16][128]
+    const uint16_t* k;
+    int64_t qks;         // sequence stride of q and k
+    const uint16_t* v;   // [B][T][48][128]
+    int64_t vs;
+    const float* g;      // [B][T][48]
+    const float* beta;
+    int64_t gs;
+    float* state;        // [B][48][128][128], updated in place
+    uint16_t* out;       // [B][T][48][128]
+    int64_t os;
+};
+size_t gdn_prefill_ws_bytes(int batch, int n_tokens);
+hipError_t launch_gdn_prefill(const GdnIn& in, int batch, int n_tokens, void* ws, hipStream_t stream);
+hipError_t launch_gdn_decode(const GdnIn& in, int batch, hipStream_t stream);
+
 hipError_t launch_attn_decode(const uint16_t* q, int64_t qs, const uint16_t* k,
                               const uint16_t* v, int64_t kvs, const int32_t* sel, int64_t sels,
                               const Positions& pos, int batch, int tq, int budget, float scale,

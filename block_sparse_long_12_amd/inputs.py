@@ -235,3 +235,48 @@ def sample_rows(wl: Workload, n: int, seed: int = 99) -> list[tuple[int, int]]:
         r = int(rng.integers(0, total))
         rows.add((r // wl.tq, wl.ctx + r % wl.tq))
     return sorted(rows)
+
+
+# ---------------------------------------------------------------- Gated DeltaNet
+
+GDN_HK, GDN_HV, GDN_D = 16, 48, 128   # model card "Model Overview": 16 Q/K heads, 48 V heads, dim 128
+_T_GQ, _T_GK, _T_GV, _T_GG, _T_GB, _T_GS = range(10, 16)
+
+
+@dataclass
+class GdnInputs:
+    """q, k [B, T, 16, 128] and v [B, T, 48, 128] bf16; g, beta [B, T, 48]
+    float32; s0 [B, 48, 128, 128] float32 (all CPU tensors)."""
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    s0: torch.Tensor
+
+
+def make_gdn_inputs(batch: int, n_tokens: int, seed: int = 11, state_sigma: float = 0.1,
+                    threads: int | None = None) -> GdnInputs:
+    """Seeded synthetic inputs of the Gated DeltaNet token mixer: q, k, v
+    N(0, 1) in bf16; g = -softplus(z - 3) and beta = sigmoid(z') with z, z'
+    N(0, 1) (a decay exp(g) mostly between 0.9 and 1, writing strengths
+    spread over (0, 1)), drawn in float32; an initial state N(0, state_sigma^2)."""
+    B, T = batch, n_tokens
+    bf = torch.bfloat16
+    q = torch.empty((B, T, GDN_HK, GDN_D), dtype=bf)
+    k = torch.empty_like(q)
+    v = torch.empty((B, T, GDN_HV, GDN_D), dtype=bf)
+    _fill_normal(q, seed, _T_GQ, 1.0, threads)
+    _fill_normal(k, seed, _T_GK, 1.0, threads)
+    _fill_normal(v, seed, _T_GV, 1.0, threads)
+    zg = torch.empty((B, T, GDN_HV), dtype=torch.float32)
+    zb = torch.empty_like(zg)
+    s0 = torch.empty((B, GDN_HV, GDN_D, GDN_D), dtype=torch.float32)
+    for t, tid, sig in ((zg, _T_GG, 1.0), (zb, _T_GB, 1.0), (s0, _T_GS, state_sigma)):
+        flat = t.view(-1)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(tid,))))
+        x = g.standard_normal(flat.numel(), dtype=np.float32)
+        flat.copy_(torch.from_numpy(x * np.float32(sig)))
+    g_log = -torch.nn.functional.softplus(zg - 3.0)
+    beta = torch.sigmoid(zb)
+    return GdnInputs(q, k, v, g_log, beta, s0)

@@ -95,6 +95,10 @@ _SIGNATURES = {
                                               _c_p, _i64, _c_p, _sz, _c_p]),
     "qsa_sparse_attn_prefill_paged": (_i32, [_c_p, _i64, _paged_p, _c_p, _i64, _c_p, _i32, _i32, _i32,
                                              ctypes.c_float, _c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p]),
+    "qsa_gdn_prefill_workspace_bytes": (_sz, [_i32, _i32]),
+    "qsa_gdn_prefill": (_i32, [_c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p, _i32, _i32, _c_p, _i64,
+                               _c_p, _sz, _c_p]),
+    "qsa_gdn_decode": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p]),
     "qsa_decode_step_paged": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _paged_p, _c_p, _i32, _i32,
                                      _i32, ctypes.c_float, _rope_p, _c_p, _i64, _i64, _c_p, _i64, _c_p, _i64,
                                      _c_p, _c_p, _i64, _c_p, _sz, _c_p]),
@@ -125,7 +129,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        if L.qsa_abi_version() != 3:
+        if L.qsa_abi_version() != 4:
             raise QSAError("libqsa ABI version mismatch")
         _LIB = L
     return _LIB
@@ -718,4 +722,55 @@ def prefill_layer_paged(q_raw, k_new_raw, v_new, q_idx, k_idx_new, cache: PagedC
         sparse_attn_prefill_paged(q_rot[:, c0:c1], cache, bufs.sel[:, c0:c1], cpos, out[:, c0:c1],
                                   None if lse is None else lse[:, c0:c1], stream=stream,
                                   gate=None if gate is None else gate[:, c0:c1])
+    return out
+
+
+# ------------------------------------------------------------------ Gated DeltaNet
+
+GDN_HK, GDN_HV, GDN_D = 16, 48, 128
+
+
+def gdn_prefill_workspace(batch: int, n_tokens: int, device="cuda") -> torch.Tensor:
+    """Workspace of gdn_prefill (no initialisation needed)."""
+    n = lib().qsa_gdn_prefill_workspace_bytes(batch, n_tokens)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _gdn_check(q, k, v, g, beta, state, out, tok_dims):
+    for t, name, dt, inner in ((q, "q", torch.bfloat16, (GDN_HK, GDN_D)), (k, "k", torch.bfloat16, (GDN_HK, GDN_D)),
+                               (v, "v", torch.bfloat16, (GDN_HV, GDN_D)), (out, "out", torch.bfloat16, (GDN_HV, GDN_D)),
+                               (g, "g", torch.float32, (GDN_HV,)), (beta, "beta", torch.float32, (GDN_HV,))):
+        _need(t, name, dt, inner)
+        if t.shape[:tok_dims] != q.shape[:tok_dims]:
+            raise QSAError(f"{name} must match q in its leading dims")
+    if q.stride() != k.stride() or g.stride() != beta.stride():
+        raise QSAError("q / k and g / beta must share strides")
+    _need(state, "state", torch.float32, (GDN_HV, GDN_D, GDN_D))
+    if not state.is_contiguous() or state.shape[0] != q.shape[0]:
+        raise QSAError("state must be contiguous [B, 48, 128, 128]")
+
+
+def gdn_prefill(q, k, v, g, beta, state, out, workspace, stream=None):
+    """Gated DeltaNet over T tokens per sequence: q, k [B, T, 16, 128], v and out
+    [B, T, 48, 128] (bf16), g and beta [B, T, 48] (float32), state [B, 48, 128,
+    128] (float32, updated in place to the state after the T tokens)."""
+    _gdn_check(q, k, v, g, beta, state, out, 2)
+    B, T = q.shape[0], q.shape[1]
+    _check(lib().qsa_gdn_prefill(_ptr(q), _ptr(k), q.stride(0), _ptr(v), v.stride(0), _ptr(g), _ptr(beta),
+                                 g.stride(0), _ptr(state), B, T, _ptr(out), out.stride(0), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)),
+           "qsa_gdn_prefill")
+    return out
+
+
+def gdn_decode(q, k, v, g, beta, state, out, stream=None):
+    """One Gated DeltaNet token per sequence: q, k [B, 16, 128], v and out
+    [B, 48, 128], g and beta [B, 48]; state updated in place."""
+    _gdn_check(q, k, v, g, beta, state, out, 1)
+    for t in (q, k, v, g, beta, out):
+        if not t.is_contiguous():
+            raise QSAError("gdn_decode takes contiguous tensors")
+    _check(lib().qsa_gdn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), q.shape[0], _ptr(out),
+                                _stream(stream)),
+           "qsa_gdn_decode")
     return out

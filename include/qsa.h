@@ -20,6 +20,7 @@
  *   qsa_sparse_attn_decode   the same for one new token per sequence
  *   qsa_decode_step          a whole serving decode step in one call
  *   qsa_*_paged              the same on paged caches (block table)
+ *   qsa_gdn_prefill / _decode the Gated DeltaNet token mixer of the other layers
  *
  * Conventions shared by every call
  *   - bf16 tensors are passed as uint16_t bit patterns; every tensor pointer
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 3
+#define QSA_ABI_VERSION 4
 #define QSA_MAX_BATCH 256
 #define QSA_MAX_BUDGET 2048
 
@@ -383,6 +384,40 @@ qsa_status_t qsa_decode_step_paged(const uint16_t* q, int64_t q_seq_stride,
                                    uint16_t* out, int64_t out_seq_stride, float* lse,
                                    const uint16_t* gate, int64_t gate_seq_stride,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Gated DeltaNet token mixer of the hybrid layers (Qwen3.8-Flash-Next blog,
+ * section "Attention: GDN + QSA": three of every four layers compress the
+ * history into a fixed-size state; model card, "Model Overview": 48 V heads,
+ * 16 Q/K heads, head dim 128).  The rule is the Gated DeltaNet paper's gated
+ * delta rule; per V head h, on Q/K head h / 3, with the state S (128 x 128,
+ * rows indexed by key dims):
+ *     S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t,
+ * q and k L2-normalised per head, q then scaled by 1/sqrt(128).  Layouts
+ * (bf16 as uint16_t bits, device memory, 16-byte aligned):
+ *   q, k  [B][T][16][128]  (sequence stride qk_seq_stride)
+ *   v     [B][T][48][128]  (v_seq_stride),  out like v (out_seq_stride)
+ *   g, beta float32 [B][T][48] (gate_seq_stride): log decay (<= 0) and
+ *         writing strength per V head and token
+ *   state float32 [B][48][128][128], read as S_0 and overwritten with S_T.
+ * qsa_gdn_prefill takes T tokens per sequence in chunks of 64 (the recurrence
+ * rewritten chunk-parallel: bf16 matrix-core products, fp32 accumulation and
+ * triangular solves, the state in fp32); its workspace
+ * (qsa_gdn_prefill_workspace_bytes, 256-byte aligned) needs no
+ * initialisation.  qsa_gdn_decode takes one token per sequence with fixed
+ * contiguous layouts q, k [B][16][128], v and out [B][48][128], g and beta
+ * [B][48], and applies the recurrence directly in fp32.
+ */
+size_t       qsa_gdn_prefill_workspace_bytes(int32_t batch, int32_t n_tokens);
+qsa_status_t qsa_gdn_prefill(const uint16_t* q, const uint16_t* k, int64_t qk_seq_stride,
+                             const uint16_t* v, int64_t v_seq_stride,
+                             const float* g, const float* beta, int64_t gate_seq_stride,
+                             float* state, int32_t batch, int32_t n_tokens,
+                             uint16_t* out, int64_t out_seq_stride,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+qsa_status_t qsa_gdn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const float* g, const float* beta, float* state, int32_t batch,
+                            uint16_t* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

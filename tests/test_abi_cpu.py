@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_dims_and_strings(L):
     assert qsa.dims() == dict(block=4, hq=24, hkv=2, d=256, rot_dim=64, hi=4, di=128)
-    assert L.qsa_abi_version() == 3
+    assert L.qsa_abi_version() == 4
     for s in range(5):
         assert L.qsa_status_string(s)
 
@@ -267,3 +267,34 @@ def test_paged_prefill_and_decode_validation(L):
     assert step(_paged(table_stride=35)) == INVALID                     # 9001 tokens need 36 pages of 256
     assert step(_paged(P=64, table_stride=100)) == INVALID              # ... or 141 pages of 64
     assert step(_paged(kbar=NULL, table_stride=64)) == INVALID and "kbar" in L.qsa_last_error().decode()
+
+
+# ---------------------------------------------------------------- Gated DeltaNet
+
+def test_gdn_validation(L):
+    """qsa_gdn_prefill / qsa_gdn_decode reject null or misaligned tensors,
+    short strides and a short workspace before any launch; zero tokens is a no-op."""
+    T = 100
+    ws = L.qsa_gdn_prefill_workspace_bytes(2, T)
+    assert ws > 0 and L.qsa_gdn_prefill_workspace_bytes(0, T) == 0 and L.qsa_gdn_prefill_workspace_bytes(2, -1) == 0
+    # 2 chunks of 64 tokens, 2 sequences: 16 Q/K heads x 2 x 32 KiB + 48 V heads x 56.25 KiB per chunk
+    assert ws == 2 * 2 * (16 * 2 * 64 * 128 * 2 + 48 * (64 * 128 * 4 + 64 * 128 * 2 + 64 * 64 * 2 + 64 * 4))
+
+    def pre(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, out=FAKE, n=T, qks=T * 2048, vs=T * 6144,
+            gs=T * 48, os_=T * 6144, w=FAKE, wb=ws, batch=2):
+        return L.qsa_gdn_prefill(q, k, qks, v, vs, g, beta, gs, state, batch, n, out, os_, w, wb, None)
+
+    assert pre(q=NULL) == INVALID
+    assert pre(v=FAKE + 8) == INVALID
+    assert pre(g=FAKE + 2) == INVALID
+    assert pre(state=FAKE + 4) == INVALID
+    assert pre(qks=T * 2048 - 8) == INVALID and "qk_seq_stride" in L.qsa_last_error().decode()
+    assert pre(vs=T * 6144 - 8) == INVALID
+    assert pre(gs=T * 48 - 1) == INVALID
+    assert pre(wb=ws - 1) == WORKSPACE
+    assert pre(w=FAKE + 16) == INVALID                                   # 256-byte alignment
+    assert pre(n=-1) == INVALID
+    assert pre(batch=0) == INVALID
+    assert pre(n=0) == OK
+    assert L.qsa_gdn_decode(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, 2, FAKE, None) == INVALID
+    assert L.qsa_gdn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == INVALID
