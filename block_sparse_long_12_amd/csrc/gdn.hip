@@ -15,12 +15,14 @@
 // the state leaves the chunk as exp(c_last) S_0 + k^T (exp(c_last - c) w).
 //
 //  gdn_prep_kernel   chunk-parallel, one workgroup per (sequence, chunk, Q/K
-//                    head): normalises q and k (bf16), forms k k^T and q k^T
-//                    on the matrix cores, and for each of the head's 3 V heads
-//                    solves the unit lower-triangular system by forward
-//                    substitution in fp32 (one thread per right-hand column,
-//                    its 64 unknowns in registers), writing U (fp32), -Wk and
-//                    P (bf16) and c.
+//                    head): normalises q and k (bf16, every load in flight at
+//                    once), and for each of the head's 3 V heads forms k k^T
+//                    and q k^T on the matrix cores, builds A and P from the
+//                    accumulators, and solves the unit lower-triangular system
+//                    by forward substitution in fp32 (one thread per
+//                    right-hand column, its 64 unknowns in registers),
+//                    writing U (fp32), -Wk and P (bf16) and c.  Sized for 3
+//                    workgroups per CU, so one's loads overlap another's solve.
 //  gdn_state_kernel  sequential over chunks, one workgroup per (sequence, V
 //                    head, 32 state columns): the state block (128 x 32 fp32)
 //                    lives in matrix-core accumulators for the whole call;
@@ -85,8 +87,6 @@ static GdnWs gdn_carve(void* ws, int batch, int nseg) {
 struct PrepSmem {
     alignas(16) uint16_t qn[kGdnC][kGdnD + 8];     // +8: rows 16 B apart in bank phase
     alignas(16) uint16_t kn[kGdnC][kGdnD + 8];
-    float gram[kGdnC][kGdnC + 1];
-    float qk[kGdnC][kGdnC + 1];
     alignas(16) float a[kGdnC][kGdnC];              // strictly lower part used
     float gam[kGdnC];
     float beta[kGdnC];
@@ -94,7 +94,7 @@ struct PrepSmem {
 
 __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
-__global__ __launch_bounds__(256) void gdn_prep_kernel(GdnIn in, GdnWs w, int seg_c0, int nseg, int T) {
+__global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int seg_c0, int nseg, int T) {
     __shared__ PrepSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -162,28 +162,6 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnIn in, GdnWs w, int se
             *reinterpret_cast<uint4*>(kdst + d * kGdnC + 8 * i8) = *reinterpret_cast<const uint4*>(v8);
         }
     }
-    // k k^T and q k^T on the matrix cores: 16 tiles each, wave w takes tile rows w
-    {
-        const int c16 = lane & 15, G = lane >> 4;
-        for (int tj = 0; tj < 4; ++tj) {
-            f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8_t bk = lds_frag(&sm.kn[16 * tj + c16][32 * s + 8 * G]);
-                ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(&sm.kn[16 * wave + c16][32 * s + 8 * G]), bk,
-                                                             ag, 0, 0, 0);
-                aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(&sm.qn[16 * wave + c16][32 * s + 8 * G]), bk,
-                                                             aq, 0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sm.gram[16 * wave + 4 * G + r][16 * tj + c16] = ag[r];
-                sm.qk[16 * wave + 4 * G + r][16 * tj + c16] = aq[r];
-            }
-        }
-    }
-    __syncthreads();
-
     for (int e = 0; e < kGdnGroup; ++e) {
         const int h = hk * kGdnGroup + e;
         const int64_t hs = slot * kGdnHv + h;
@@ -210,12 +188,29 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnIn in, GdnWs w, int se
         }
         __syncthreads();
         // A (strictly lower) and P (lower incl. the diagonal, bf16 to the workspace)
-        uint16_t* pdst = w.p + hs * (kGdnC * kGdnC);
-        for (int x = tid; x < kGdnC * kGdnC; x += 256) {
-            const int i = x / kGdnC, j = x % kGdnC;
-            const float dec = j <= i ? expf(sm.gam[i] - sm.gam[j]) : 0.f;
-            sm.a[i][j] = j < i ? sm.beta[i] * dec * sm.gram[i][j] : 0.f;
-            pdst[x] = f32_to_bf16(dec * sm.qk[i][j]);
+        // straight from k k^T and q k^T on the matrix cores: wave w takes rows 16w .. 16w + 15
+        {
+            const int c16 = lane & 15, G = lane >> 4;
+            uint16_t* pdst = w.p + hs * (kGdnC * kGdnC);
+            for (int tj = 0; tj < 4; ++tj) {
+                f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const bf16x8_t bk = lds_frag(&sm.kn[16 * tj + c16][32 * s + 8 * G]);
+                    ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(&sm.kn[16 * wave + c16][32 * s + 8 * G]),
+                                                                 bk, ag, 0, 0, 0);
+                    aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(&sm.qn[16 * wave + c16][32 * s + 8 * G]),
+                                                                 bk, aq, 0, 0, 0);
+                }
+                const int j = 16 * tj + c16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * wave + 4 * G + r;
+                    const float dec = j <= i ? expf(sm.gam[i] - sm.gam[j]) : 0.f;
+                    sm.a[i][j] = j < i ? sm.beta[i] * dec * ag[r] : 0.f;
+                    pdst[i * kGdnC + j] = f32_to_bf16(dec * aq[r]);
+                }
+            }
         }
         __syncthreads();
         // forward substitution, one right-hand column per thread: columns 0..127 of
@@ -400,14 +395,16 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(GdnIn in, GdnWs w, int s
     const int64_t slot0 = static_cast<int64_t>(b) * nseg;
     gdn_load_ops(w, slot0, hk, h, cb, A);
     // two named operand buffers: chunk l + 1 loads while chunk l computes
+    auto run = [&](const GdnOps& o, int l) {
+        const int t0 = (seg_c0 + l) * kGdnC;
+        gdn_chunk(o, S, sm, in, b, h, cb, t0, min(kGdnC, T - t0));
+    };
     for (int l = 0; l < nseg; l += 2) {
         if (l + 1 < nseg) gdn_load_ops(w, slot0 + l + 1, hk, h, cb, B);
-        const int t0a = (seg_c0 + l) * kGdnC;
-        gdn_chunk(A, S, sm, in, b, h, cb, t0a, min(kGdnC, T - t0a));
+        run(A, l);
         if (l + 1 >= nseg) break;
         if (l + 2 < nseg) gdn_load_ops(w, slot0 + l + 2, hk, h, cb, A);
-        const int t0b = t0a + kGdnC;
-        gdn_chunk(B, S, sm, in, b, h, cb, t0b, min(kGdnC, T - t0b));
+        run(B, l + 1);
     }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
