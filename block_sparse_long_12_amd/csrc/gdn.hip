@@ -94,6 +94,17 @@ struct PrepSmem {
 
 __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
+// Workgroup barrier for data exchanged through LDS only: waits for this wave's
+// LDS operations (not its global loads and stores, which stay in flight), then
+// meets the other waves.  The empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0); vmcnt and expcnt left at their maxima
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int seg_c0, int nseg, int T) {
     __shared__ PrepSmem sm;
     const int tid = threadIdx.x;
@@ -145,7 +156,7 @@ __global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int
         *reinterpret_cast<uint32_t*>(&sm.qn[i][2 * lane]) = qb;
         *reinterpret_cast<uint32_t*>(&sm.kn[i][2 * lane]) = kb;
     }
-    __syncthreads();
+    lds_barrier();
     // normalised rows to the workspace: q token-major, k dim-major
     {
         uint16_t* qdst = w.qn + (slot * kGdnHk + hk) * (kGdnC * kGdnD);
@@ -186,7 +197,7 @@ __global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int
             sm.beta[lane] = b_in;
             w.gam[hs * kGdnC + lane] = c;
         }
-        __syncthreads();
+        lds_barrier();
         // A (strictly lower) and P (lower incl. the diagonal, bf16 to the workspace)
         // straight from k k^T and q k^T on the matrix cores: wave w takes rows 16w .. 16w + 15
         {
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         // forward substitution, one right-hand column per thread: columns 0..127 of
         // beta v, then 128..255 of beta exp(c) k (beta is 0 past the chunk end)
         if (tid < kGdnD) {
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int
 #pragma unroll
             for (int i = 0; i < kGdnC; ++i) wdst[i * kGdnD] = f32_to_bf16(-x[i]);
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -287,13 +298,24 @@ __device__ __forceinline__ void gdn_load_ops(const GdnWs& w, int64_t slot, int h
     o.glast = gm[kGdnC - 1];
 }
 
-struct StateSmem {
+struct StateBuf {
     alignas(16) uint16_t st[kGdnCols][kGdnD + 8];    // bf16 S^T of the block: [column][dim]
     alignas(16) uint16_t wt[kGdnCols][kGdnC + 8];    // bf16 W^T: [column][token]
     alignas(16) uint16_t dwt[kGdnCols][kGdnC + 8];   // bf16 (exp(c_last - c) W)^T
 };
 
-__device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], StateSmem& sm, const GdnIn& in,
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two floats to packed bf16, round to nearest even (one hardware conversion)
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// One chunk.  Consecutive chunks use the two buffers in turn, so the buffer a
+// chunk writes was last read two chunks earlier, before the first barrier of
+// the chunk in between: two barriers per chunk.
+__device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], StateBuf& sm, const GdnIn& in,
                                           int b, int h, int cb, int t0, int n) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c16 = lane & 15, G = lane >> 4;
@@ -303,39 +325,44 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], S
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             uint2 pk;
-            pk.x = f32_to_bf16(S[rt][ct][0]) | (static_cast<uint32_t>(f32_to_bf16(S[rt][ct][1])) << 16);
-            pk.y = f32_to_bf16(S[rt][ct][2]) | (static_cast<uint32_t>(f32_to_bf16(S[rt][ct][3])) << 16);
+            pk.x = cvt_bf16x2(S[rt][ct][0], S[rt][ct][1]);
+            pk.y = cvt_bf16x2(S[rt][ct][2], S[rt][ct][3]);
             *reinterpret_cast<uint2*>(&sm.st[16 * ct + c16][32 * wave + 16 * rt + 4 * G]) = pk;
         }
-    __syncthreads();
-    // W = U - Wk S for tokens 16w .. 16w + 15
+    // decay factors of this lane's 4 rows (computed while the stores drain)
+    float eg[4], ed[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        eg[r] = __expf(o.gr[r]);
+        ed[r] = __expf(o.glast - o.gr[r]);
+    }
+    const float el = __expf(o.glast);
+    lds_barrier();
+    // W = U - Wk S for tokens 16w .. 16w + 15 (U added after the products, so
+    // the prefetched U stays where it landed until here)
     f32x4_t W[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-        W[ct] = f32x4_t{o.u[ct][0], o.u[ct][1], o.u[ct][2], o.u[ct][3]};
+        W[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             W[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.wk[s], lds_frag(&sm.st[16 * ct + c16][32 * s + 8 * G]),
                                                            W[ct], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) W[ct][r] += o.u[ct][r];
     }
     // W^T and (exp(c_last - c) W)^T in bf16 for the next two products
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
         uint2 pw, pd;
-        uint16_t e[4], f[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            e[r] = f32_to_bf16(W[ct][r]);
-            f[r] = f32_to_bf16(expf(o.glast - o.gr[r]) * W[ct][r]);
-        }
-        pw.x = e[0] | (static_cast<uint32_t>(e[1]) << 16);
-        pw.y = e[2] | (static_cast<uint32_t>(e[3]) << 16);
-        pd.x = f[0] | (static_cast<uint32_t>(f[1]) << 16);
-        pd.y = f[2] | (static_cast<uint32_t>(f[3]) << 16);
+        pw.x = cvt_bf16x2(W[ct][0], W[ct][1]);
+        pw.y = cvt_bf16x2(W[ct][2], W[ct][3]);
+        pd.x = cvt_bf16x2(ed[0] * W[ct][0], ed[1] * W[ct][1]);
+        pd.y = cvt_bf16x2(ed[2] * W[ct][2], ed[3] * W[ct][3]);
         *reinterpret_cast<uint2*>(&sm.wt[16 * ct + c16][16 * wave + 4 * G]) = pw;
         *reinterpret_cast<uint2*>(&sm.dwt[16 * ct + c16][16 * wave + 4 * G]) = pd;
     }
-    __syncthreads();
+    lds_barrier();
     // o = exp(c) (q S) + P W for tokens 16w .. 16w + 15
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -345,36 +372,36 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], S
             O = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.qn[s], lds_frag(&sm.st[16 * ct + c16][32 * s + 8 * G]), O,
                                                         0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[r] *= expf(o.gr[r]);
+        for (int r = 0; r < 4; ++r) O[r] *= eg[r];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
             O = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.p[s], lds_frag(&sm.wt[16 * ct + c16][32 * s + 8 * G]), O, 0,
                                                         0, 0);
+        const uint32_t o01 = cvt_bf16x2(O[0], O[1]), o23 = cvt_bf16x2(O[2], O[3]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * wave + 4 * G + r;
+            const uint32_t pr = r < 2 ? o01 : o23;
             if (i < n)
                 in.out[b * in.os + (static_cast<int64_t>(t0 + i) * kGdnHv + h) * kGdnD + kGdnCols * cb + 16 * ct + c16] =
-                    f32_to_bf16(O[r]);
+                    static_cast<uint16_t>(pr >> (16 * (r & 1)));
         }
     }
     // S = exp(c_last) S + k^T (exp(c_last - c) W)
-    const float dl = expf(o.glast);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            S[rt][ct] *= dl;
+            S[rt][ct] *= el;
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 S[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     o.kt[rt][s], lds_frag(&sm.dwt[16 * ct + c16][32 * s + 8 * G]), S[rt][ct], 0, 0, 0);
         }
-    __syncthreads();       // st / wt / dwt are rewritten by the next chunk
 }
 
 __global__ __launch_bounds__(256) void gdn_state_kernel(GdnIn in, GdnWs w, int seg_c0, int nseg, int T) {
-    __shared__ StateSmem sm;
+    __shared__ StateBuf sm[2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c16 = lane & 15, G = lane >> 4;
     const int cb = blockIdx.x % (kGdnD / kGdnCols);
@@ -397,13 +424,16 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(GdnIn in, GdnWs w, int s
     // two named operand buffers: chunk l + 1 loads while chunk l computes
     auto run = [&](const GdnOps& o, int l) {
         const int t0 = (seg_c0 + l) * kGdnC;
-        gdn_chunk(o, S, sm, in, b, h, cb, t0, min(kGdnC, T - t0));
+        gdn_chunk(o, S, sm[l & 1], in, b, h, cb, t0, min(kGdnC, T - t0));
     };
+    // (the next chunk's loads are issued unconditionally, past the end clamped to
+    // the last chunk, so the wait counts stay exact: a skipped load would make the
+    // compiler drain every load in flight)
     for (int l = 0; l < nseg; l += 2) {
-        if (l + 1 < nseg) gdn_load_ops(w, slot0 + l + 1, hk, h, cb, B);
+        gdn_load_ops(w, slot0 + min(l + 1, nseg - 1), hk, h, cb, B);
         run(A, l);
         if (l + 1 >= nseg) break;
-        if (l + 2 < nseg) gdn_load_ops(w, slot0 + l + 2, hk, h, cb, A);
+        gdn_load_ops(w, slot0 + min(l + 2, nseg - 1), hk, h, cb, A);
         run(B, l + 1);
     }
 #pragma unroll
