@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     if (append && g == 0) append_rows<kPaged>(ap, pm, b, p0, tq, wave);
 
     for (int k = tid; k < tq * kDecHistBins; k += 256) hist[k] = 0;
-    __syncthreads();
+    lds_barrier();          // the appended rows' stores need not land before the scan
 
     const int c16 = lane & 15;
     const int G = lane >> 4;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
             if (j0 + 256 * st < j_hi) score_group(buf[st & 1], j0 + 256 * st);
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int t = 0; t < tq; ++t) {
         const int o_t = (p0 + t) / kBlock;
         const int keep_t = min(budget - 1, o_t);
@@ -260,7 +260,14 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(
     if (!(keep > 0 && keep < o)) return;                 // trivial rows need no filter
     uint32_t* ctrl = ws.ctrl + r * kCtrl;
 
-    // this workgroup's scores first (independent of the threshold), 4 float4 per thread
+    // the global histogram the scan completed, then this workgroup's scores
+    // (independent of the threshold): all issued at once, the histogram
+    // first so that waiting for it leaves the scores in flight through the
+    // threshold search (the barriers below wait for LDS work only)
+    const uint4* gh = reinterpret_cast<const uint4*>(ws.hist + static_cast<int64_t>(r) * kDecHistBins);
+    uint4 hv[kDecHistBins / 1024];
+#pragma unroll
+    for (int it = 0; it < kDecHistBins / 1024; ++it) hv[it] = gh[tid + 256 * it];
     const float* row = scores + b * ss + t * sld;
     const int j_lo = g * kFiltPer;
     const int j_hi = min(o, j_lo + kFiltPer);
@@ -270,20 +277,13 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(
         const int j4 = min(j_lo + 4 * tid + 1024 * it, (o - 1) & ~3);   // clamped: always a legal load
         v[it] = *reinterpret_cast<const float4*>(row + j4);
     }
-
-    // the threshold bin, from the global histogram the scan completed (all
-    // 16 words of a thread in flight at once, then stored to LDS)
-    const uint4* gh = reinterpret_cast<const uint4*>(ws.hist + static_cast<int64_t>(r) * kDecHistBins);
-    uint4 hv[kDecHistBins / 1024];
-#pragma unroll
-    for (int it = 0; it < kDecHistBins / 1024; ++it) hv[it] = gh[tid + 256 * it];
 #pragma unroll
     for (int it = 0; it < kDecHistBins / 1024; ++it) reinterpret_cast<uint4*>(sm.hist)[tid + 256 * it] = hv[it];
     if (tid == 0) {
         sm.n_def = 0;
         sm.n_cand = 0;
     }
-    __syncthreads();
+    lds_barrier();
     find_threshold_bin<256>(sm.hist, kDecHistBins, keep, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
     const uint32_t tbin = sm.sh_bin;
     if (g == 0 && tid == 0) {
@@ -311,14 +311,14 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int nd = min(sm.n_def, QSA_MAX_BUDGET);
     const int nc = sm.n_cand;
     if (tid == 0) {
         sm.base_def = nd ? static_cast<int>(atomicAdd(&ctrl[kNDef], static_cast<uint32_t>(nd))) : 0;
         sm.base_cand = nc ? static_cast<int>(atomicAdd(&ctrl[kNCand], static_cast<uint32_t>(nc))) : 0;
     }
-    __syncthreads();
+    lds_barrier();
     int32_t* defl = ws.defl + static_cast<int64_t>(r) * QSA_MAX_BUDGET;
     uint64_t* cand = ws.cand + static_cast<int64_t>(r) * kDecCap;
     for (int k = tid; k < nd; k += 256)
@@ -396,10 +396,10 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         for (int it = 0; it < kDecCap / kFinNT; ++it)
             if (tid + kFinNT * it < inbin) lc[tid + kFinNT * it] = cv[it];
         if (tid == 0) sm.u.m.n_taken = 0;
-        __syncthreads();
+        lds_barrier();
         for (int k = tid; k < inbin; k += kFinNT)
             atomicAdd(&h2[static_cast<uint32_t>(lc[k] >> 40) & (kDecHistBins - 1)], 1u);
-        __syncthreads();
+        lds_barrier();
         find_threshold_bin<kFinNT>(h2, kDecHistBins, remaining, sm.u.m.wave_tot, &sm.u.m.sh_bin, &sm.u.m.sh_above);
         const uint32_t t2 = sm.u.m.sh_bin;
         const int above2 = sm.u.m.sh_above;                   // taken outright
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         // members of the cut sub-bin go to a short list; the rest are decided here
         uint64_t* sub = sm.u.m.sub;
         if (tid == 0) sm.u.m.n_sub = 0;
-        __syncthreads();
+        lds_barrier();
         for (int i = tid; i < inbin; i += kFinNT) {
             const uint64_t x = lc[i];
             const uint32_t d2 = static_cast<uint32_t>(x >> 40) & (kDecHistBins - 1);
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
             else if (d2 == t2)
                 sub[atomicAdd(&sm.u.m.n_sub, 1)] = x;
         }
-        __syncthreads();
+        lds_barrier();
         const int n_sub = sm.u.m.n_sub;
         int32_t* dst = chosen + above + above2;
         if (n_sub <= 256) {
@@ -431,18 +431,18 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         } else {
             const int np2 = next_pow2(n_sub);
             for (int k = n_sub + tid; k < np2; k += kFinNT) sub[k] = 0ull;
-            __syncthreads();
+            lds_barrier();
             bitonic_sort<kFinNT, uint64_t, true>(sub, np2);
             for (int k = tid; k < need2; k += kFinNT) dst[k] = static_cast<int32_t>(~static_cast<uint32_t>(sub[k]));
         }
-        __syncthreads();
+        lds_barrier();
         if (bitmap) {
             for (int k = tid; k < keep; k += kFinNT) {
                 const int v = chosen[k];
                 atomicOr(&sm.u.m.bm[v >> 5], 1u << (v & 31));
             }
             if (tid == 0) out[keep] = o;                     // above every candidate
-            __syncthreads();
+            lds_barrier();
             // thread t owns words 8t .. 8t+7: prefix count of set bits, then emit in order
             constexpr int kWpt = kBitmapWords / kFinNT;
             uint32_t w[kWpt];
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         }
         for (int k = keep + 1 + tid; k < budget; k += kFinNT) out[k] = -1;
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t* gh = ws.hist + static_cast<int64_t>(r) * kDecHistBins;
     for (int k = tid; k < kDecHistBins; k += kFinNT) gh[k] = 0u;
     if (tid < kCtrl) ctrl[tid] = 0u;

@@ -94,16 +94,6 @@ struct PrepSmem {
 
 __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
-// Workgroup barrier for data exchanged through LDS only: waits for this wave's
-// LDS operations (not its global loads and stores, which stay in flight), then
-// meets the other waves.  The empty asm statements keep the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0); vmcnt and expcnt left at their maxima
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 __global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int seg_c0, int nseg, int T) {
     __shared__ PrepSmem sm;

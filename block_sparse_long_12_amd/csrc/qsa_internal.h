@@ -80,6 +80,20 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
     return static_cast<uint16_t>(__float_as_uint(f) >> 16);
 }
 
+// Workgroup barrier for data exchanged through LDS only: waits for this wave's
+// LDS operations (not its global loads and stores, which stay in flight), then
+// meets the other waves.  __syncthreads() carries a workgroup release fence,
+// which also waits for every global load and store in flight; this does not.
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.  Not for data one thread of the workgroup passes to another
+// through global memory.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0); vmcnt and expcnt left at their maxima
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Monotone map of float32 onto uint32 for selection: larger score -> larger
 // key; -0.0 and +0.0 share a key; every NaN maps to 0, below all numbers.
 __device__ __forceinline__ uint32_t score_key(float s) {

@@ -47,7 +47,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* t
         if (lane >= off) x += y;
     }
     if (lane == 63) wave_tot[wave] = x;
-    __syncthreads();
+    lds_barrier();
     int before = 0, all = 0;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) {
@@ -55,7 +55,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* t
         before += (w < wave) ? t : 0;
         all += t;
     }
-    __syncthreads();
+    lds_barrier();
     *total = all;
     return before + x - v;
 }
@@ -76,7 +76,7 @@ __device__ void bitonic_sort(T* a, int n) {
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 }
@@ -113,7 +113,7 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, int nb,
             run += h;
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Writes the final ascending selection: sm.chosen[0 .. keep) plus o.
@@ -125,7 +125,7 @@ __device__ __forceinline__ void write_selection(SelectSmem& sm, int keep, int o,
     const int np2 = next_pow2(nsel);
     if (tid == 0) sm.chosen[keep] = o;
     for (int k = nsel + tid; k < np2; k += NT) sm.chosen[k] = 0x7fffffff;
-    __syncthreads();
+    lds_barrier();
     bitonic_sort<NT, int32_t, false>(sm.chosen, np2);
     for (int k = tid; k < budget; k += NT) out[k] = (k < nsel) ? sm.chosen[k] : -1;
 }
@@ -139,7 +139,7 @@ __device__ __forceinline__ void write_selection(SelectSmem& sm, int keep, int o,
 template <int NT>
 __device__ __forceinline__ void rank_take_desc(uint64_t* cand, int n, int take, int32_t* dst) {
     if (threadIdx.x == 0 && (n & 1)) cand[n] = 0ull;
-    __syncthreads();
+    lds_barrier();
     const int n2 = (n + 1) >> 1;
     const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
     for (int i = threadIdx.x; i < n; i += NT) {
@@ -161,7 +161,7 @@ template <int NT>
 __device__ __forceinline__ void rank_write_ascending(int32_t* vals, int n, int32_t* out) {
     const int n4 = (n + 3) >> 2;
     for (int k = n + threadIdx.x; k < 4 * n4; k += NT) vals[k] = 0x7fffffff;
-    __syncthreads();
+    lds_barrier();
     const int4* v4 = reinterpret_cast<const int4*>(vals);
     for (int i = threadIdx.x; i < n; i += NT) {
         const int32_t x = vals[i];
@@ -202,7 +202,7 @@ __device__ void select_row(const float* __restrict__ row, int o, int keep, int b
         const int nb = 1 << bits;
         const uint32_t dmask = static_cast<uint32_t>(nb - 1);
         for (int k = tid; k < nb; k += NT) sm.hist[k] = 0;
-        __syncthreads();
+        lds_barrier();
         for (int k = tid; k < n4; k += NT) {
             const float4 v = row4[k];
             const float f[4] = {v.x, v.y, v.z, v.w};
@@ -216,21 +216,21 @@ __device__ void select_row(const float* __restrict__ row, int o, int keep, int b
             const uint32_t key = score_key(row[j]);
             if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & dmask], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         find_threshold_bin<NT>(sm.hist, nb, remaining, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
         const uint32_t tb = sm.sh_bin;
         remaining -= sm.sh_above;
         prefix |= tb << shift;
         pmask |= dmask << shift;
         bin_count = static_cast<int>(sm.hist[tb]);
-        __syncthreads();
+        lds_barrier();
     }
 
     if (tid == 0) {
         sm.n_chosen = 0;
         sm.n_cand = 0;
     }
-    __syncthreads();
+    lds_barrier();
 
     if (bin_count <= kSelectCap) {
         for (int k = tid; k < n4; k += NT) {
@@ -253,16 +253,16 @@ __device__ void select_row(const float* __restrict__ row, int o, int keep, int b
             else if (mk == prefix)
                 sm.cand[atomicAdd(&sm.n_cand, 1)] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~j);
         }
-        __syncthreads();
+        lds_barrier();
         const int nc = sm.n_cand;
         const int base = sm.n_chosen;        // == keep - remaining
         const int np2 = next_pow2(nc);
         for (int k = nc + tid; k < np2; k += NT) sm.cand[k] = 0;   // below every real entry
-        __syncthreads();
+        lds_barrier();
         bitonic_sort<NT, uint64_t, true>(sm.cand, np2);
         for (int k = tid; k < remaining; k += NT)
             sm.chosen[base + k] = static_cast<int32_t>(~static_cast<uint32_t>(sm.cand[k]));
-        __syncthreads();
+        lds_barrier();
     } else {
         // all 32 key bits fixed: key == prefix are ties, taken by ascending index
         int tie_base = 0;
@@ -277,7 +277,7 @@ __device__ void select_row(const float* __restrict__ row, int o, int keep, int b
             if (eq && tie_base + rank < remaining) sm.chosen[atomicAdd(&sm.n_chosen, 1)] = j;
             tie_base += total;
         }
-        __syncthreads();
+        lds_barrier();
     }
     write_selection<NT>(sm, keep, o, budget, out);
 }
@@ -319,23 +319,23 @@ template <int NT, int PER>
 __device__ uint32_t sample_threshold_key(const uint32_t (&sk)[PER], int r, ResolveSmem& sm) {
     const int tid = threadIdx.x;
     for (int k = tid; k < 2048; k += NT) sm.hist[k] = 0u;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int e = 0; e < PER; ++e) atomicAdd(&sm.hist[sk[e] >> 21], 1u);
-    __syncthreads();
+    lds_barrier();
     find_threshold_bin<NT>(sm.hist, 2048, r, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
     const uint32_t b1 = sm.sh_bin;
     const int r2 = r - sm.sh_above;
-    __syncthreads();
+    lds_barrier();
     for (int k = tid; k < 2048; k += NT) sm.hist[k] = 0u;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int e = 0; e < PER; ++e)
         if ((sk[e] >> 21) == b1) atomicAdd(&sm.hist[(sk[e] >> 10) & 2047u], 1u);
-    __syncthreads();
+    lds_barrier();
     find_threshold_bin<NT>(sm.hist, 2048, r2, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
     const uint32_t tkey = (b1 << 21) | (sm.sh_bin << 10);
-    __syncthreads();
+    lds_barrier();
     return tkey;
 }
 
@@ -382,7 +382,7 @@ __device__ void finish_from_candidates(const uint64_t (&c)[K], const bool (&cv)[
         sm.wave_hi[wave] = hi;
         sm.wave_lo[wave] = lo;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) {
         hi = sm.wave_hi[w] > hi ? sm.wave_hi[w] : hi;
@@ -397,19 +397,19 @@ __device__ void finish_from_candidates(const uint64_t (&c)[K], const bool (&cv)[
     int bin_count = total;
     while (bin_count > kResShort) {
         for (int k = tid; k < 2048; k += NT) sm.hist[k] = 0u;
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int w = 0; w < K; ++w)
             if (cv[w] && (c[w] & pmask) == prefix)
                 atomicAdd(&sm.hist[static_cast<uint32_t>(c[w] >> sh) & 2047u], 1u);
-        __syncthreads();
+        lds_barrier();
         find_threshold_bin<NT>(sm.hist, 2048, rem, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
         const uint32_t tb = sm.sh_bin;
         rem -= sm.sh_above;
         prefix |= static_cast<uint64_t>(tb) << sh;
         pmask |= 2047ull << sh;
         bin_count = static_cast<int>(sm.hist[tb]);
-        __syncthreads();
+        lds_barrier();
         if (sh == 0) break;
         sh = sh > 11 ? sh - 11 : 0;
     }
@@ -417,7 +417,7 @@ __device__ void finish_from_candidates(const uint64_t (&c)[K], const bool (&cv)[
         sm.n_chosen = 0;
         sm.n_short = 0;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int w = 0; w < K; ++w) {
         if (cv[w]) {
@@ -426,18 +426,18 @@ __device__ void finish_from_candidates(const uint64_t (&c)[K], const bool (&cv)[
             else if (mk == prefix) sm.shortl[atomicAdd(&sm.n_short, 1)] = c[w];
         }
     }
-    __syncthreads();
+    lds_barrier();
     rank_take_desc<NT>(sm.shortl, sm.n_short, rem, sm.chosen + (keep - rem));
     if (bitmap != nullptr && o <= 32 * kResBitmapWords) {
         constexpr int kWpt = kResBitmapWords / NT;
         for (int k = tid; k < kResBitmapWords; k += NT) bitmap[k] = 0u;
-        __syncthreads();                                  // chosen complete, bitmap clear
+        lds_barrier();                                  // chosen complete, bitmap clear
         for (int k = tid; k < keep; k += NT) {
             const int v = sm.chosen[k];
             atomicOr(&bitmap[v >> 5], 1u << (v & 31));
         }
         if (tid == 0) out[keep] = o;                      // above every candidate
-        __syncthreads();
+        lds_barrier();
         uint32_t wv[kWpt];
         int cnt = 0;
 #pragma unroll
