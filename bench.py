@@ -386,6 +386,39 @@ def cpu_baseline(wl, x, n_rows: int, args):
 
 # ------------------------------------------------------------------ main
 
+def achievable_peaks(torch):
+    """Context for the rooflines (not the kernels here): a 1 GiB device copy
+    (read + write bytes over time) and a 8192^3 bf16 matrix product through
+    torch's library GEMM, each the best of 5 after a warm-up."""
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    x = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
+    y = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(5):
+            s_ev = torch.cuda.Event(enable_timing=True)
+            e_ev = torch.cuda.Event(enable_timing=True)
+            s_ev.record()
+            fn()
+            e_ev.record()
+            torch.cuda.synchronize()
+            t.append(s_ev.elapsed_time(e_ev) / 1e3)
+        return min(t)
+
+    t_copy = best(lambda: b.copy_(a))
+    t_mm = best(lambda: torch.matmul(x, y))
+    res = {"hbm_copy_GBs": 2 * a.numel() * 4 / t_copy / 1e9,
+           "bf16_gemm_TFLOPs": 2 * 8192 ** 3 / t_mm / 1e12,
+           "note": "measured context: 1 GiB device copy; 8192^3 bf16 torch.matmul"}
+    del a, b, x, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def gdn_measure(args, torch, qsa, I):
     """The Gated DeltaNet token mixer of the other 3 of 4 layers: a prefill
     of --gdn-tokens tokens (one sequence, the new-token count of the QSA
@@ -690,6 +723,7 @@ def main():
 
     if not args.no_gdn:
         rec["gdn"] = gdn_measure(args, torch, qsa, I)
+    rec["achievable_peaks"] = achievable_peaks(torch)
 
     if args.cpu_rows > 0:
         rec["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_rows, args)
