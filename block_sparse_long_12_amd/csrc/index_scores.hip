@@ -184,22 +184,35 @@ __device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf
     step_scores(t, qf, acc);
     const int lane = threadIdx.x & 63;
     const int jl = j0 + 4 * (lane >> 4);
+    // an appended score passed >= tau, so it is not NaN: its key is score_key's
+    // (-0.0 and +0.0 share 0x80000000) without the NaN case
+    auto key_of = [](float f) -> uint32_t {
+        const uint32_t u = __float_as_uint(f);
+        return u == 0x80000000u ? 0x80000000u : (u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u));
+    };
+    auto scan = [&](auto in_limit) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const bool q = jl + 16 * (e >> 2) + (e & 3) < lim && acc[e >> 2][e & 3] >= tau;
-        const uint64_t m = __ballot(q);
-        if (m != 0ull) {                                  // wave-uniform
-            if (q) {
-                const int pos = cnt + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                          static_cast<uint32_t>(m >> 32),
-                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
-                if (pos < kCollectCap / 4)
-                    seg[pos] = (static_cast<uint64_t>(score_key(acc[e >> 2][e & 3])) << 32) |
-                               static_cast<uint32_t>((row_local << 16) | (jl + 16 * (e >> 2) + (e & 3) - j_begin));
+        for (int e = 0; e < 16; ++e) {
+            const bool q = in_limit(jl + 16 * (e >> 2) + (e & 3)) && acc[e >> 2][e & 3] >= tau;
+            const uint64_t m = __ballot(q);
+            if (m != 0ull) {                              // wave-uniform
+                if (q) {
+                    const int pos = cnt + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                              static_cast<uint32_t>(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+                    if (pos < kCollectCap / 4)
+                        seg[pos] = (static_cast<uint64_t>(key_of(acc[e >> 2][e & 3])) << 32) |
+                                   static_cast<uint32_t>((row_local << 16) | (jl + 16 * (e >> 2) + (e & 3) - j_begin));
+                }
+                cnt += __popcll(m);
             }
-            cnt += __popcll(m);
         }
-    }
+    };
+    // the block limit matters only in the steps that reach some lane's limit
+    if (__all(j0 + kColStep <= lim))
+        scan([](int) { return true; });
+    else
+        scan([lim](int j) { return j < lim; });
 }
 
 template <int kMode, bool kPaged>
