@@ -85,11 +85,50 @@ struct KbPages {
 // The instruction has no register results (it writes LDS only, and its
 // address registers are read at issue); completion is tracked explicitly by
 // the vmcnt waits of the step loop.
-template <int kMode, bool kPaged = false>
-__device__ __forceinline__ void stage_dma(const uint16_t* kb, int j0, int j_end, int omin, const KbPages& kp,
-                                          KTile& t) {
+// Byte offset of lane L's 16-byte chunk for load i of a step, from the
+// step's first row (see stage_dma).
+struct DmaOffsets {
+    uint32_t off[4];
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets() {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    DmaOffsets d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * i + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        d.off[i] = static_cast<uint32_t>((r * kDi + 8 * c) * 2);
+    }
+    return d;
+}
+
+template <int kMode, bool kPaged = false>
+__device__ __forceinline__ void stage_dma(const uint16_t* kb, int j0, int j_end, int omin, const KbPages& kp,
+                                          const DmaOffsets& d, KTile& t) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if constexpr (!kPaged && kMode != kModeSample) {
+        // a step wholly below j_end needs no clamp: the step's rows start at
+        // a scalar base and each lane's byte offset from it is fixed, so the
+        // loads take the scalar-base form and cost no vector address arithmetic
+        if (j0 + kColStep <= j_end) {
+            const uint16_t* base = kb + static_cast<int64_t>(j0) * kDi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t off = d.off[i];
+                const uint32_t lds = __builtin_amdgcn_readfirstlane(
+                    static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&t.chunk[16 * wave + 4 * i][0])));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+                asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+                             : "memory", "m0");
+#pragma clang diagnostic pop
+            }
+            return;
+        }
+    }
     // paged: the wave's 16 rows form one 16-block tile (the step start is a
     // multiple of 64, sample runs start on multiples of 16, and clamped rows
     // fall in the tile of j_end - 1), so one wave-uniform table read serves
@@ -194,7 +233,7 @@ __device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const bool q = in_limit(jl + 16 * (e >> 2) + (e & 3)) && acc[e >> 2][e & 3] >= tau;
-            const uint64_t m = __ballot(q);
+            const uint64_t m = __builtin_amdgcn_ballot_w64(q);
             if (m != 0ull) {                              // wave-uniform
                 if (q) {
                     const int pos = cnt + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
@@ -258,6 +297,7 @@ __global__ __launch_bounds__(256) void index_kernel(
     const uint16_t* kb = kPaged ? kbar : kbar + b * kbs;
     const KbPages kp{kPaged ? pm.table + b * pm.ts : nullptr, pm.shift, pm.n_pages};
     const int n_steps = (j_end - j_begin + kColStep - 1) / kColStep;
+    const DmaOffsets dof = dma_offsets();
 
     if constexpr (kMode == kModeCollect) {
         const int tok = t0 + (lane & 15);
@@ -271,14 +311,14 @@ __global__ __launch_bounds__(256) void index_kernel(
         __syncthreads();
         // two LDS buffers: step s + 1 loads while step s is scored; the loop
         // issues no other vector memory op, so "all landed" is vmcnt(0)
-        stage_dma<kMode, kPaged>(kb, j_begin, j_end, omin, kp, tA);
+        stage_dma<kMode, kPaged>(kb, j_begin, j_end, omin, kp, dof, tA);
         for (int s = 0; s < n_steps; s += 2) {
             wait_and_meet<0>();
-            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 1), j_end, omin, kp, tB);
+            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 1), j_end, omin, kp, dof, tB);
             if (has_rows) collect_step(tA, qf, j_begin + kColStep * s, lim, tau, tok - t_wg, j_begin, seg, cnt);
             if (s + 1 >= n_steps) break;
             wait_and_meet<0>();
-            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 2), j_end, omin, kp, tA);
+            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 2), j_end, omin, kp, dof, tA);
             if (has_rows) collect_step(tB, qf, j_begin + kColStep * (s + 1), lim, tau, tok - t_wg, j_begin, seg, cnt);
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);               // no load into LDS outlives the workgroup
@@ -322,19 +362,19 @@ __global__ __launch_bounds__(256) void index_kernel(
         __builtin_amdgcn_s_waitcnt(0x0f70);               // B in registers before the load pipeline starts
         float* sb = scores + b * ss;
         // three LDS buffers: step s is scored while steps s + 1 and s + 2 load
-        stage_dma<kMode, kPaged>(kb, j_begin, j_end, omin, kp, tA);
-        stage_dma<kMode, kPaged>(kb, j_begin + kColStep, j_end, omin, kp, tB);
+        stage_dma<kMode, kPaged>(kb, j_begin, j_end, omin, kp, dof, tA);
+        stage_dma<kMode, kPaged>(kb, j_begin + kColStep, j_end, omin, kp, dof, tB);
         for (int s = 0; s < n_steps; s += 3) {
             step_sync(s, has_rows);
-            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 2), j_end, omin, kp, tC);
+            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 2), j_end, omin, kp, dof, tC);
             if (has_rows) store_step(tA, qf, j_begin + kColStep * s, j_end, t0, tq, sb, ld);
             if (s + 1 >= n_steps) break;
             step_sync(s + 1, has_rows);
-            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 3), j_end, omin, kp, tA);
+            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 3), j_end, omin, kp, dof, tA);
             if (has_rows) store_step(tB, qf, j_begin + kColStep * (s + 1), j_end, t0, tq, sb, ld);
             if (s + 2 >= n_steps) break;
             step_sync(s + 2, has_rows);
-            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 4), j_end, omin, kp, tB);
+            stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 4), j_end, omin, kp, dof, tB);
             if (has_rows) store_step(tC, qf, j_begin + kColStep * (s + 2), j_end, t0, tq, sb, ld);
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);               // no load into LDS outlives the workgroup
