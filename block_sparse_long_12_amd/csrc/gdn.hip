@@ -16,13 +16,14 @@
 //
 //  gdn_prep_kernel   chunk-parallel, one workgroup per (sequence, chunk, Q/K
 //                    head): normalises q and k (bf16, every load in flight at
-//                    once), and for each of the head's 3 V heads forms k k^T
-//                    and q k^T on the matrix cores, builds A and P from the
-//                    accumulators, and solves the unit lower-triangular system
-//                    by forward substitution in fp32 (one thread per
-//                    right-hand column, its 64 unknowns in registers),
-//                    writing U (fp32), -Wk and P (bf16) and c.  Sized for 3
-//                    workgroups per CU, so one's loads overlap another's solve.
+//                    once) and forms k k^T and q k^T once on the matrix cores;
+//                    then for each of the head's 3 V heads builds A and P from
+//                    the accumulators, inverts I + A in fp32 by 16 x 16 blocks
+//                    (diagonal blocks by substitution, the rest as fp32
+//                    matrix-core products, in place in LDS) and forms U and Wk
+//                    as bf16 matrix-core products of the column-scaled inverse
+//                    (split into bf16 hi + lo) with V and k, writing U (fp32),
+//                    -Wk and P (bf16) and c.
 //  gdn_state_kernel  sequential over chunks, one workgroup per (sequence, V
 //                    head, 32 state columns): the state block (128 x 32 fp32)
 //                    lives in matrix-core accumulators for the whole call;
@@ -84,22 +85,75 @@ static GdnWs gdn_carve(void* ws, int batch, int nseg) {
 
 // ---------------------------------------------------------------- prep
 
-struct PrepSmem {
-    alignas(16) uint16_t qn[kGdnC][kGdnD + 8];     // +8: rows 16 B apart in bank phase
-    alignas(16) uint16_t kn[kGdnC][kGdnD + 8];
-    alignas(16) float a[kGdnC][kGdnC];              // strictly lower part used
-    float gam[kGdnC];
-    float beta[kGdnC];
-};
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two floats to packed bf16, round to nearest even (one hardware conversion)
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
 
 __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
+// LDS of the prep kernel.  The normalised rows (first phase) and, per V head,
+// V^T with the triangular matrix (A, then (I + A)^-1 in place) share one region.
+struct alignas(16) PrepSmem {
+    union {
+        struct {
+            uint16_t qn[kGdnC][kGdnD + 8];     // +8: rows 16 B apart in bank phase
+            uint16_t kn[kGdnC][kGdnD + 8];
+        } p1;
+        struct {
+            uint16_t vt[kGdnD][kGdnC + 8];     // V^T: [dim][token]
+            float t[kGdnC * kGdnC];            // element (i, j) at tix(i, j)
+        } p2;
+    };
+    uint16_t kt[kGdnD][kGdnC + 8];             // k^T: [dim][token]
+    float gam[kGdnC];                          // cumulative log decay
+    float beta[kGdnC];
+    float bexp[kGdnC];                         // beta exp(c)
+};
 
-__global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int seg_c0, int nseg, int T) {
+// Row i of the 64 x 64 matrix holds its 16-byte chunk q (columns 4q .. 4q + 3)
+// at position q ^ (i % 16): the 16 rows of a block read the same chunk from 16
+// different bank groups.
+__device__ __forceinline__ int tix(int i, int j) { return i * kGdnC + ((((j >> 2) ^ i) & 15) << 2) + (j & 3); }
+
+// acc + X Y for the 16 x 16 blocks X = (xr, xc) and Y = (yr, yc) of t, fp32 on
+// the matrix cores (A operand: row l % 16, column 4q + l / 16; B operand: row
+// 4q + l / 16, column l % 16; result rows 4(l / 16) + r, column l % 16)
+__device__ __forceinline__ f32x4_t blk_mma(const float* t, int lane, int xr, int xc, int yr, int yc, f32x4_t acc) {
+    const int c16 = lane & 15, G = lane >> 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(t[tix(16 * xr + c16, 16 * xc + 4 * q + G)],
+                                                   t[tix(16 * yr + 4 * q + G, 16 * yc + c16)], acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ __forceinline__ void blk_store(float* t, int lane, int br, int bc, const f32x4_t& v, float sign) {
+    const int c16 = lane & 15, G = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[tix(16 * br + 4 * G + r, 16 * bc + c16)] = sign * v[r];
+}
+
+// Tokens 2p, 2p + 1 (8 bf16 each, dims 8d .. 8d + 7) into dst[dim][token] as
+// packed token pairs.
+__device__ __forceinline__ void put_pair_t(uint16_t (*dst)[kGdnC + 8], int p, int d, const uint4& a, const uint4& c) {
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, cv[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        *reinterpret_cast<uint32_t*>(&dst[8 * d + 2 * k][2 * p]) = (av[k] & 0xffffu) | (cv[k] << 16);
+        *reinterpret_cast<uint32_t*>(&dst[8 * d + 2 * k + 1][2 * p]) = (av[k] >> 16) | (cv[k] & 0xffff0000u);
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void gdn_prep_kernel(GdnIn in, GdnWs w, int seg_c0, int nseg, int T) {
     __shared__ PrepSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int c16 = lane & 15, G = lane >> 4;
     const int hk = blockIdx.x % kGdnHk;
     const int rest = blockIdx.x / kGdnHk;
     const int cl = rest % nseg;
@@ -115,6 +169,20 @@ __global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int
         g_in = in.g[gi];
         b_in = in.beta[gi];
     }
+    // V rows of one head for the transposed write: item m covers tokens 2p, 2p + 1
+    // (p = tid / 16 + 16m, rows past the chunk end read its last row) at dims 8d .. 8d + 7 (d = tid % 16)
+    uint4 vraw[2][2];
+    auto load_v = [&](int h) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int tok = min(2 * ((tid >> 4) + 16 * m) + x, n - 1);
+                vraw[m][x] = *reinterpret_cast<const uint4*>(
+                    in.v + b * in.vs + (static_cast<int64_t>(t0 + tok) * kGdnHv + h) * kGdnD + 8 * (tid & 15));
+            }
+    };
+    load_v(hk * kGdnGroup);
     // normalised q / sqrt(128) and k, rounded to bf16: wave w takes rows 16w .. 16w+15,
     // lane L dims 2L, 2L+1; all 32 loads of a lane are issued before any is used
     uint32_t qraw[16], kraw[16];
@@ -143,37 +211,60 @@ __global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int
         const float ik = sk > 0.f ? 1.f / sqrtf(sk) : 0.f;
         const uint32_t qb = f32_to_bf16(q0 * iq) | (static_cast<uint32_t>(f32_to_bf16(q1 * iq)) << 16);
         const uint32_t kb = f32_to_bf16(k0 * ik) | (static_cast<uint32_t>(f32_to_bf16(k1 * ik)) << 16);
-        *reinterpret_cast<uint32_t*>(&sm.qn[i][2 * lane]) = qb;
-        *reinterpret_cast<uint32_t*>(&sm.kn[i][2 * lane]) = kb;
+        *reinterpret_cast<uint32_t*>(&sm.p1.qn[i][2 * lane]) = qb;
+        *reinterpret_cast<uint32_t*>(&sm.p1.kn[i][2 * lane]) = kb;
     }
     lds_barrier();
-    // normalised rows to the workspace: q token-major, k dim-major
+    // normalised q to the workspace (token-major); k^T into LDS
     {
         uint16_t* qdst = w.qn + (slot * kGdnHk + hk) * (kGdnC * kGdnD);
         for (int e = tid; e < kGdnC * kGdnD / 8; e += 256) {
             const int i = e / (kGdnD / 8), d8 = e % (kGdnD / 8);
-            *reinterpret_cast<uint4*>(qdst + i * kGdnD + 8 * d8) = *reinterpret_cast<const uint4*>(&sm.qn[i][8 * d8]);
+            *reinterpret_cast<uint4*>(qdst + i * kGdnD + 8 * d8) = *reinterpret_cast<const uint4*>(&sm.p1.qn[i][8 * d8]);
         }
-        uint16_t* kdst = w.knt + (slot * kGdnHk + hk) * (kGdnD * kGdnC);
-        for (int e = tid; e < kGdnD * kGdnC / 8; e += 256) {      // 8 tokens of one dim per store
-            const int d = e / (kGdnC / 8), i8 = e % (kGdnC / 8);
-            uint16_t v8[8];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) v8[x] = sm.kn[8 * i8 + x][d];
-            *reinterpret_cast<uint4*>(kdst + d * kGdnC + 8 * i8) = *reinterpret_cast<const uint4*>(v8);
+        for (int m = 0; m < 2; ++m) {
+            const int p = (tid >> 4) + 16 * m, d = tid & 15;
+            put_pair_t(sm.kt, p, d, *reinterpret_cast<const uint4*>(&sm.p1.kn[2 * p][8 * d]),
+                       *reinterpret_cast<const uint4*>(&sm.p1.kn[2 * p + 1][8 * d]));
         }
     }
+    // k k^T and q k^T of the chunk (shared by the 3 V heads): wave w takes rows 16w .. 16w + 15
+    f32x4_t kk[4], qk[4];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+        kk[tj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        qk[tj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const bf16x8_t bk = lds_frag(&sm.p1.kn[16 * tj + c16][32 * s + 8 * G]);
+            kk[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(&sm.p1.kn[16 * wave + c16][32 * s + 8 * G]), bk,
+                                                             kk[tj], 0, 0, 0);
+            qk[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(&sm.p1.qn[16 * wave + c16][32 * s + 8 * G]), bk,
+                                                             qk[tj], 0, 0, 0);
+        }
+    }
+    lds_barrier();
+    // k^T to the workspace (dim-major)
+    {
+        uint16_t* kdst = w.knt + (slot * kGdnHk + hk) * (kGdnD * kGdnC);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 256 * m, d = e >> 3, i8 = e & 7;
+            *reinterpret_cast<uint4*>(kdst + d * kGdnC + 8 * i8) = *reinterpret_cast<const uint4*>(&sm.kt[d][8 * i8]);
+        }
+    }
+    float* t = sm.p2.t;
+#pragma unroll 1
     for (int e = 0; e < kGdnGroup; ++e) {
         const int h = hk * kGdnGroup + e;
         const int64_t hs = slot * kGdnHv + h;
-        // this head's V rows for the substitution, in flight during the work below
-        float x[kGdnC];
-        const int col = tid & (kGdnD - 1);
-        if (tid < kGdnD) {
-#pragma unroll
-            for (int i = 0; i < kGdnC; ++i)
-                x[i] = bf16_to_f32(in.v[b * in.vs + (static_cast<int64_t>(t0 + min(i, n - 1)) * kGdnHv + h) * kGdnD + col]);
-        }
+        // the lane index, opaque to the compiler in each pass: the per-lane
+        // addresses below are recomputed per head instead of being hoisted out
+        // of the loop and held (spilled) across it
+        int lane = tid & 63;
+        asm volatile("" : "+v"(lane));
+        const int c16 = lane & 15, G = lane >> 4;
         // gates; rows past the chunk end write nothing (beta 0) and keep the decay.
         // The cumulative log decay is an inclusive scan over the wave that holds the head.
         if (wave == e) {
@@ -185,61 +276,154 @@ __global__ __launch_bounds__(256, 3) void gdn_prep_kernel(GdnIn in, GdnWs w, int
             }
             sm.gam[lane] = c;
             sm.beta[lane] = b_in;
+            sm.bexp[lane] = b_in * expf(c);
             w.gam[hs * kGdnC + lane] = c;
         }
-        lds_barrier();
-        // A (strictly lower) and P (lower incl. the diagonal, bf16 to the workspace)
-        // straight from k k^T and q k^T on the matrix cores: wave w takes rows 16w .. 16w + 15
-        {
-            const int c16 = lane & 15, G = lane >> 4;
-            uint16_t* pdst = w.p + hs * (kGdnC * kGdnC);
-            for (int tj = 0; tj < 4; ++tj) {
-                f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const bf16x8_t bk = lds_frag(&sm.kn[16 * tj + c16][32 * s + 8 * G]);
-                    ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(&sm.kn[16 * wave + c16][32 * s + 8 * G]),
-                                                                 bk, ag, 0, 0, 0);
-                    aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(&sm.qn[16 * wave + c16][32 * s + 8 * G]),
-                                                                 bk, aq, 0, 0, 0);
-                }
+        for (int m = 0; m < 2; ++m) put_pair_t(sm.p2.vt, (tid >> 4) + 16 * m, tid & 15, vraw[m][0], vraw[m][1]);
+        lds_barrier();
+        if (e + 1 < kGdnGroup) load_v(h + 1);               // the next head's rows, in flight from here
+        // A (strictly lower) into t, P (lower incl. the diagonal, bf16) to the workspace
+        {
+            uint16_t* pdst = w.p + hs * (kGdnC * kGdnC);
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
                 const int j = 16 * tj + c16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * wave + 4 * G + r;
                     const float dec = j <= i ? expf(sm.gam[i] - sm.gam[j]) : 0.f;
-                    sm.a[i][j] = j < i ? sm.beta[i] * dec * ag[r] : 0.f;
-                    pdst[i * kGdnC + j] = f32_to_bf16(dec * aq[r]);
+                    t[tix(i, j)] = j < i ? sm.beta[i] * dec * kk[tj][r] : 0.f;
+                    pdst[i * kGdnC + j] = f32_to_bf16(dec * qk[tj][r]);
                 }
             }
         }
         lds_barrier();
-        // forward substitution, one right-hand column per thread: columns 0..127 of
-        // beta v, then 128..255 of beta exp(c) k (beta is 0 past the chunk end)
-        if (tid < kGdnD) {
+        // (I + A)^-1 in place, by 16 x 16 blocks.  The diagonal blocks: wave d
+        // inverts block d by substitution, column l % 16 per lane.
+        {
+            const int d = wave, c = c16;
+            float x[16];
 #pragma unroll
-            for (int i = 0; i < kGdnC; ++i) x[i] *= sm.beta[i];
-        } else {
+            for (int r = 0; r < 16; ++r) {
+                const float* row = t + (16 * d + r) * kGdnC;
+                float acc = r == c ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 0; i < kGdnC; ++i) x[i] = sm.beta[i] * expf(sm.gam[i]) * bf16_to_f32(sm.kn[i][col]);
-        }
+                for (int q = 0; q < 4; ++q) {
+                    if (4 * q >= r) break;
+                    const float4 a = *reinterpret_cast<const float4*>(row + ((((4 * d + q) ^ r) & 15) << 2));
+                    const float av[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-        for (int i = 1; i < kGdnC; ++i) {
-            float acc = x[i];
+                    for (int u = 0; u < 4; ++u)
+                        if (4 * q + u < r) acc -= av[u] * x[4 * q + u];
+                }
+                x[r] = acc;
+                __builtin_amdgcn_sched_barrier(0);        // one row's loads at a time (registers)
+            }
+            if (lane < 16) {
 #pragma unroll
-            for (int j = 0; j < i; ++j) acc -= sm.a[i][j] * x[j];
-            x[i] = acc;
-        }
-        if (tid < kGdnD) {
-            float* udst = w.u + hs * (kGdnC * kGdnD) + col;
-#pragma unroll
-            for (int i = 0; i < kGdnC; ++i) udst[i * kGdnD] = x[i];
-        } else {
-            uint16_t* wdst = w.wk + hs * (kGdnC * kGdnD) + col;
-#pragma unroll
-            for (int i = 0; i < kGdnC; ++i) wdst[i * kGdnD] = f32_to_bf16(-x[i]);
+                for (int r = 0; r < 16; ++r) t[tix(16 * d + r, 16 * d + c)] = x[r];
+            }
         }
         lds_barrier();
+        // the 32 x 32 diagonal halves: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22
+        if (wave & 1) {
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4_t X = blk_mma(t, lane, wave, wave - 1, wave - 1, wave - 1, z);
+            blk_store(t, lane, wave, wave - 1, X, 1.f);
+            const f32x4_t Y = blk_mma(t, lane, wave, wave, wave, wave - 1, z);
+            blk_store(t, lane, wave, wave - 1, Y, -1.f);
+        }
+        lds_barrier();
+        // the lower-left 32 x 32 half: -T_hi A_lowleft T_lo, one 16 x 16 block (a, bc) per wave
+        {
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            const int a = 2 + (wave >> 1), bc = wave & 1;
+            f32x4_t Z;
+            if (bc == 0)
+                Z = blk_mma(t, lane, a, 1, 1, 0, blk_mma(t, lane, a, 0, 0, 0, z));
+            else
+                Z = blk_mma(t, lane, a, 1, 1, 1, z);
+            lds_barrier();
+            blk_store(t, lane, a, bc, Z, 1.f);
+            lds_barrier();
+            f32x4_t Y = blk_mma(t, lane, a, 2, 2, bc, z);
+            if (a == 3) Y = blk_mma(t, lane, 3, 3, 3, bc, Y);
+            lds_barrier();
+            blk_store(t, lane, a, bc, Y, -1.f);
+        }
+        lds_barrier();
+        // U = T diag(beta) V and Wk = T diag(beta exp(c)) k on the matrix cores, each
+        // scaled T split into bf16 hi + lo; wave w takes column tiles 2w, 2w + 1
+        {
+            bf16x8_t vb[2][2], kb[2][2];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    vb[cc][s] = lds_frag(&sm.p2.vt[16 * (2 * wave + cc) + c16][32 * s + 8 * G]);
+                    kb[cc][s] = lds_frag(&sm.kt[16 * (2 * wave + cc) + c16][32 * s + 8 * G]);
+                }
+            float* udst = w.u + hs * (kGdnC * kGdnD);
+            uint16_t* wdst = w.wk + hs * (kGdnC * kGdnD);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4_t U[2], W[2];
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    U[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    W[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+                const int i = 16 * rt + c16;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (s == 1 && rt < 2) break;                  // T rows below 32 end before column 32
+                    float tr[8];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const float4 v = *reinterpret_cast<const float4*>(t + i * kGdnC +
+                                                                          ((((8 * s + 2 * G + hh) ^ i) & 15) << 2));
+                        tr[4 * hh] = v.x;
+                        tr[4 * hh + 1] = v.y;
+                        tr[4 * hh + 2] = v.z;
+                        tr[4 * hh + 3] = v.w;
+                    }
+                    uint32_t uh[4], ul[4], wh[4], wl[4];
+#pragma unroll
+                    for (int x = 0; x < 8; x += 2) {
+                        const int j = 32 * s + 8 * G + x;
+                        const float a0 = tr[x] * sm.beta[j], a1 = tr[x + 1] * sm.beta[j + 1];
+                        const float e0 = tr[x] * sm.bexp[j], e1 = tr[x + 1] * sm.bexp[j + 1];
+                        const uint32_t ha = cvt_bf16x2(a0, a1), he = cvt_bf16x2(e0, e1);
+                        uh[x / 2] = ha;
+                        wh[x / 2] = he;
+                        ul[x / 2] = cvt_bf16x2(a0 - __uint_as_float(ha << 16), a1 - __uint_as_float(ha & 0xffff0000u));
+                        wl[x / 2] = cvt_bf16x2(e0 - __uint_as_float(he << 16), e1 - __uint_as_float(he & 0xffff0000u));
+                    }
+                    const bf16x8_t fuh = __builtin_bit_cast(bf16x8_t, uh), ful = __builtin_bit_cast(bf16x8_t, ul);
+                    const bf16x8_t fwh = __builtin_bit_cast(bf16x8_t, wh), fwl = __builtin_bit_cast(bf16x8_t, wl);
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) {
+                        U[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fuh, vb[cc][s], U[cc], 0, 0, 0);
+                        U[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ful, vb[cc][s], U[cc], 0, 0, 0);
+                        W[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fwh, kb[cc][s], W[cc], 0, 0, 0);
+                        W[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fwl, kb[cc][s], W[cc], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int col = 16 * (2 * wave + cc) + c16;
+                    const uint32_t w01 = cvt_bf16x2(-W[cc][0], -W[cc][1]), w23 = cvt_bf16x2(-W[cc][2], -W[cc][3]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * rt + 4 * G + r;
+                        udst[row * kGdnD + col] = U[cc][r];
+                        wdst[row * kGdnD + col] = static_cast<uint16_t>((r < 2 ? w01 : w23) >> (16 * (r & 1)));
+                    }
+                }
+            }
+        }
+        lds_barrier();                                      // t, V^T and the gates are rewritten by the next head
     }
 }
 
@@ -294,13 +478,6 @@ struct StateBuf {
     alignas(16) uint16_t dwt[kGdnCols][kGdnC + 8];   // bf16 (exp(c_last - c) W)^T
 };
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// two floats to packed bf16, round to nearest even (one hardware conversion)
-__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
-}
 
 // One chunk.  Consecutive chunks use the two buffers in turn, so the buffer a
 // chunk writes was last read two chunks earlier, before the first barrier of

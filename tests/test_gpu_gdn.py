@@ -1,7 +1,7 @@
 """Gated DeltaNet token mixer on the GPU against the float64 oracle.
 
 Prefill runs the chunk-parallel form (bf16 matrix-core products with fp32
-accumulation, fp32 triangular solves and state); its tolerance comes from
+accumulation, an fp32 inverse of the triangular system, fp32 state); its tolerance comes from
 that arithmetic: the same rounding emulated in float64 differs from the exact
 recurrence by at most 0.028 x rms(o) (mean 0.0026 x rms) over 3000-12000
 tokens of these inputs, flat in the length because the decay forgets old
