@@ -41,7 +41,9 @@ constexpr int kGdnHv = 48;          // V heads
 constexpr int kGdnGroup = kGdnHv / kGdnHk;
 constexpr int kGdnD = 128;          // head dim (keys and values)
 constexpr int kGdnC = 64;           // tokens per chunk
-constexpr int kGdnCols = 32;        // state columns per state-pass workgroup
+constexpr int kGdnCols = 32;        // state columns per decode workgroup
+constexpr int kStCols = 32;         // state columns per state-pass workgroup
+constexpr int kStCt = kStCols / 16; // their 16-column tiles
 constexpr int kGdnSegChunks = 512;  // chunks per workspace segment
 
 // Workspace of one segment (nseg chunks), per sequence b and chunk l:
@@ -436,7 +438,7 @@ struct GdnOps {
     bf16x8_t qn[4];      // q rows, same layout
     bf16x8_t p[2];       // P rows 16w + l%16, tokens 32s + 8(l/16) ..
     bf16x8_t kt[2][2];   // k^T rows (dims) 32w + 16rt + l%16, tokens 32s + 8(l/16) ..
-    float u[2][4];       // U rows 16w + 4(l/16) + r, column 16ct + l%16 of the block
+    float u[kStCt][4];   // U rows 16w + 4(l/16) + r, column 16ct + l%16 of the block
     float gr[4];         // c of rows 16w + 4(l/16) + r
     float glast;         // c of the chunk's last token
 };
@@ -461,9 +463,9 @@ __device__ __forceinline__ void gdn_load_ops(const GdnWs& w, int64_t slot, int h
         o.kt[rt][0] = *reinterpret_cast<const bf16x8_t*>(kt + 16 * rt * kGdnC);
         o.kt[rt][1] = *reinterpret_cast<const bf16x8_t*>(kt + 16 * rt * kGdnC + 32);
     }
-    const float* u = w.u + hs * (kGdnC * kGdnD) + (16 * wave + 4 * G) * kGdnD + kGdnCols * cb + c16;
+    const float* u = w.u + hs * (kGdnC * kGdnD) + (16 * wave + 4 * G) * kGdnD + kStCols * cb + c16;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < kStCt; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o.u[ct][r] = u[r * kGdnD + 16 * ct];
     const float* gm = w.gam + hs * kGdnC;
@@ -473,16 +475,16 @@ __device__ __forceinline__ void gdn_load_ops(const GdnWs& w, int64_t slot, int h
 }
 
 struct StateBuf {
-    alignas(16) uint16_t st[kGdnCols][kGdnD + 8];    // bf16 S^T of the block: [column][dim]
-    alignas(16) uint16_t wt[kGdnCols][kGdnC + 8];    // bf16 W^T: [column][token]
-    alignas(16) uint16_t dwt[kGdnCols][kGdnC + 8];   // bf16 (exp(c_last - c) W)^T
+    alignas(16) uint16_t st[kStCols][kGdnD + 8];    // bf16 S^T of the block: [column][dim]
+    alignas(16) uint16_t wt[kStCols][kGdnC + 8];    // bf16 W^T: [column][token]
+    alignas(16) uint16_t dwt[kStCols][kGdnC + 8];   // bf16 (exp(c_last - c) W)^T
 };
 
 
 // One chunk.  Consecutive chunks use the two buffers in turn, so the buffer a
 // chunk writes was last read two chunks earlier, before the first barrier of
 // the chunk in between: two barriers per chunk.
-__device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], StateBuf& sm, const GdnIn& in,
+__device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][kStCt], StateBuf& sm, const GdnIn& in,
                                           int b, int h, int cb, int t0, int n) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c16 = lane & 15, G = lane >> 4;
@@ -490,7 +492,7 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], S
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < kStCt; ++ct) {
             uint2 pk;
             pk.x = cvt_bf16x2(S[rt][ct][0], S[rt][ct][1]);
             pk.y = cvt_bf16x2(S[rt][ct][2], S[rt][ct][3]);
@@ -507,9 +509,9 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], S
     lds_barrier();
     // W = U - Wk S for tokens 16w .. 16w + 15 (U added after the products, so
     // the prefetched U stays where it landed until here)
-    f32x4_t W[2];
+    f32x4_t W[kStCt];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < kStCt; ++ct) {
         W[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -520,7 +522,7 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], S
     }
     // W^T and (exp(c_last - c) W)^T in bf16 for the next two products
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < kStCt; ++ct) {
         uint2 pw, pd;
         pw.x = cvt_bf16x2(W[ct][0], W[ct][1]);
         pw.y = cvt_bf16x2(W[ct][2], W[ct][3]);
@@ -532,7 +534,7 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], S
     lds_barrier();
     // o = exp(c) (q S) + P W for tokens 16w .. 16w + 15
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < kStCt; ++ct) {
         f32x4_t O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -550,7 +552,7 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], S
             const int i = 16 * wave + 4 * G + r;
             const uint32_t pr = r < 2 ? o01 : o23;
             if (i < n)
-                in.out[b * in.os + (static_cast<int64_t>(t0 + i) * kGdnHv + h) * kGdnD + kGdnCols * cb + 16 * ct + c16] =
+                in.out[b * in.os + (static_cast<int64_t>(t0 + i) * kGdnHv + h) * kGdnD + kStCols * cb + 16 * ct + c16] =
                     static_cast<uint16_t>(pr >> (16 * (r & 1)));
         }
     }
@@ -558,7 +560,7 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][2], S
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < kStCt; ++ct) {
             S[rt][ct] *= el;
 #pragma unroll
             for (int s = 0; s < 2; ++s)
@@ -571,18 +573,22 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(GdnIn in, GdnWs w, int s
     __shared__ StateBuf sm[2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c16 = lane & 15, G = lane >> 4;
-    const int cb = blockIdx.x % (kGdnD / kGdnCols);
-    const int rest = blockIdx.x / (kGdnD / kGdnCols);
+    // workgroups are dealt to the 8 XCDs round-robin; renumber them so the
+    // column blocks of one head run on one XCD and share its L2 copy of the
+    // head's chunk operands (the grid, batch x 48 x blocks, is a multiple of 8)
+    const int wg = static_cast<int>((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8);
+    const int cb = wg % (kGdnD / kStCols);
+    const int rest = wg / (kGdnD / kStCols);
     const int h = rest % kGdnHv;
     const int b = rest / kGdnHv;
     const int hk = h / kGdnGroup;
     // the state block: rows 32w + 16rt + 4(l/16) + r, column 32cb + 16ct + l%16
-    float* sg = in.state + (static_cast<int64_t>(b) * kGdnHv + h) * (kGdnD * kGdnD) + kGdnCols * cb + c16;
-    f32x4_t S[2][2];
+    float* sg = in.state + (static_cast<int64_t>(b) * kGdnHv + h) * (kGdnD * kGdnD) + kStCols * cb + c16;
+    f32x4_t S[2][kStCt];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < kStCt; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[rt][ct][r] = sg[(32 * wave + 16 * rt + 4 * G + r) * kGdnD + 16 * ct];
     GdnOps A, B;
@@ -606,7 +612,7 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(GdnIn in, GdnWs w, int s
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < kStCt; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) sg[(32 * wave + 16 * rt + 4 * G + r) * kGdnD + 16 * ct] = S[rt][ct][r];
 }
@@ -620,7 +626,7 @@ hipError_t launch_gdn_prefill(const GdnIn& in, int batch, int n_tokens, void* ws
                            in, w, c0, nseg, n_tokens);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(gdn_state_kernel, dim3(static_cast<unsigned>(batch * kGdnHv * (kGdnD / kGdnCols))),
+        hipLaunchKernelGGL(gdn_state_kernel, dim3(static_cast<unsigned>(batch * kGdnHv * (kGdnD / kStCols))),
                            dim3(256), 0, stream, in, w, c0, nseg, n_tokens);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
