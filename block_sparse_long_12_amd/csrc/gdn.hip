@@ -443,34 +443,62 @@ struct GdnOps {
     float glast;         // c of the chunk's last token
 };
 
-__device__ __forceinline__ void gdn_load_ops(const GdnWs& w, int64_t slot, int hk, int h, int cb, GdnOps& o) {
+// Per-lane byte offsets of a wave's operands from their per-chunk bases, fixed
+// for the whole call: each load is a scalar base plus a 32-bit lane offset.
+struct GdnOff {
+    uint32_t a;     // -Wk and q rows 16w + l%16, dims 8(l/16) ..
+    uint32_t p;     // P rows 16w + l%16, tokens 8(l/16) ..
+    uint32_t kt;    // k^T rows 32w + l%16, tokens 8(l/16) ..
+    uint32_t u;     // U rows 16w + 4(l/16), column l%16 of the block
+    uint32_t g;     // c of rows 16w + 4(l/16) ..
+};
+
+__device__ __forceinline__ GdnOff gdn_offsets(int cb) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c16 = lane & 15, G = lane >> 4;
+    GdnOff f;
+    f.a = static_cast<uint32_t>(((16 * wave + c16) * kGdnD + 8 * G) * 2);
+    f.p = static_cast<uint32_t>(((16 * wave + c16) * kGdnC + 8 * G) * 2);
+    f.kt = static_cast<uint32_t>(((32 * wave + c16) * kGdnC + 8 * G) * 2);
+    f.u = static_cast<uint32_t>(((16 * wave + 4 * G) * kGdnD + kStCols * cb + c16) * 4);
+    f.g = static_cast<uint32_t>((16 * wave + 4 * G) * 4);
+    return f;
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_off(const void* base, uint32_t off) {
+    return *reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
+__device__ __forceinline__ void gdn_load_ops(const GdnWs& w, int64_t slot, int hk, int h, const GdnOff& f, GdnOps& o) {
     const int64_t hs = slot * kGdnHv + h;
-    const uint16_t* wk = w.wk + hs * (kGdnC * kGdnD) + (16 * wave + c16) * kGdnD + 8 * G;
-    const uint16_t* qn = w.qn + (slot * kGdnHk + hk) * (kGdnC * kGdnD) + (16 * wave + c16) * kGdnD + 8 * G;
+    const uint16_t* wk = w.wk + hs * (kGdnC * kGdnD);
+    const uint16_t* qn = w.qn + (slot * kGdnHk + hk) * (kGdnC * kGdnD);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        o.wk[s] = *reinterpret_cast<const bf16x8_t*>(wk + 32 * s);
-        o.qn[s] = *reinterpret_cast<const bf16x8_t*>(qn + 32 * s);
+        o.wk[s] = ld_off<bf16x8_t>(wk, f.a + 64 * s);
+        o.qn[s] = ld_off<bf16x8_t>(qn, f.a + 64 * s);
     }
-    const uint16_t* pp = w.p + hs * (kGdnC * kGdnC) + (16 * wave + c16) * kGdnC + 8 * G;
-    o.p[0] = *reinterpret_cast<const bf16x8_t*>(pp);
-    o.p[1] = *reinterpret_cast<const bf16x8_t*>(pp + 32);
-    const uint16_t* kt = w.knt + (slot * kGdnHk + hk) * (kGdnD * kGdnC) + (32 * wave + c16) * kGdnC + 8 * G;
+    const uint16_t* pp = w.p + hs * (kGdnC * kGdnC);
+    o.p[0] = ld_off<bf16x8_t>(pp, f.p);
+    o.p[1] = ld_off<bf16x8_t>(pp, f.p + 64);
+    const uint16_t* kt = w.knt + (slot * kGdnHk + hk) * (kGdnD * kGdnC);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-        o.kt[rt][0] = *reinterpret_cast<const bf16x8_t*>(kt + 16 * rt * kGdnC);
-        o.kt[rt][1] = *reinterpret_cast<const bf16x8_t*>(kt + 16 * rt * kGdnC + 32);
+        o.kt[rt][0] = ld_off<bf16x8_t>(kt, f.kt + 16 * rt * kGdnC * 2);
+        o.kt[rt][1] = ld_off<bf16x8_t>(kt, f.kt + 16 * rt * kGdnC * 2 + 64);
     }
-    const float* u = w.u + hs * (kGdnC * kGdnD) + (16 * wave + 4 * G) * kGdnD + kStCols * cb + c16;
+    const float* u = w.u + hs * (kGdnC * kGdnD);
 #pragma unroll
     for (int ct = 0; ct < kStCt; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o.u[ct][r] = u[r * kGdnD + 16 * ct];
+        for (int r = 0; r < 4; ++r) o.u[ct][r] = ld_off<float>(u, f.u + (r * kGdnD + 16 * ct) * 4);
     const float* gm = w.gam + hs * kGdnC;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o.gr[r] = gm[16 * wave + 4 * G + r];
+    const float4 g4 = ld_off<float4>(gm, f.g);
+    o.gr[0] = g4.x;
+    o.gr[1] = g4.y;
+    o.gr[2] = g4.z;
+    o.gr[3] = g4.w;
     o.glast = gm[kGdnC - 1];
 }
 
@@ -593,7 +621,8 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(GdnIn in, GdnWs w, int s
             for (int r = 0; r < 4; ++r) S[rt][ct][r] = sg[(32 * wave + 16 * rt + 4 * G + r) * kGdnD + 16 * ct];
     GdnOps A, B;
     const int64_t slot0 = static_cast<int64_t>(b) * nseg;
-    gdn_load_ops(w, slot0, hk, h, cb, A);
+    const GdnOff off = gdn_offsets(cb);
+    gdn_load_ops(w, slot0, hk, h, off, A);
     // two named operand buffers: chunk l + 1 loads while chunk l computes
     auto run = [&](const GdnOps& o, int l) {
         const int t0 = (seg_c0 + l) * kGdnC;
@@ -603,10 +632,10 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(GdnIn in, GdnWs w, int s
     // the last chunk, so the wait counts stay exact: a skipped load would make the
     // compiler drain every load in flight)
     for (int l = 0; l < nseg; l += 2) {
-        gdn_load_ops(w, slot0 + min(l + 1, nseg - 1), hk, h, cb, B);
+        gdn_load_ops(w, slot0 + min(l + 1, nseg - 1), hk, h, off, B);
         run(A, l);
         if (l + 1 >= nseg) break;
-        gdn_load_ops(w, slot0 + min(l + 2, nseg - 1), hk, h, cb, A);
+        gdn_load_ops(w, slot0 + min(l + 2, nseg - 1), hk, h, off, A);
         run(B, l + 1);
     }
 #pragma unroll
