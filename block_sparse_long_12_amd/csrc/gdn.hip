@@ -50,7 +50,7 @@ constexpr int kGdnSegChunks = 512;  // chunks per workspace segment
 struct GdnWs {
     uint16_t* qn;    // [B][nseg][16][64][128]  normalised q / sqrt(128), token-major
     uint16_t* knt;   // [B][nseg][16][128][64]  normalised k, dim-major
-    float* u;        // [B][nseg][48][64][128]
+    float* u;        // [B][nseg][48][16][128][4]  rows 4q .. 4q + 3 of a column together
     uint16_t* wk;    // [B][nseg][48][64][128]  -Wk
     uint16_t* p;     // [B][nseg][48][64][64]
     float* gam;      // [B][nseg][48][64]       cumulative log decay in the chunk
@@ -416,10 +416,10 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(GdnIn in, GdnWs w, int
                 for (int cc = 0; cc < 2; ++cc) {
                     const int col = 16 * (2 * wave + cc) + c16;
                     const uint32_t w01 = cvt_bf16x2(-W[cc][0], -W[cc][1]), w23 = cvt_bf16x2(-W[cc][2], -W[cc][3]);
+                    *reinterpret_cast<f32x4_t*>(udst + ((4 * rt + G) * kGdnD + col) * 4) = U[cc];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = 16 * rt + 4 * G + r;
-                        udst[row * kGdnD + col] = U[cc][r];
                         wdst[row * kGdnD + col] = static_cast<uint16_t>((r < 2 ? w01 : w23) >> (16 * (r & 1)));
                     }
                 }
@@ -449,7 +449,7 @@ struct GdnOff {
     uint32_t a;     // -Wk and q rows 16w + l%16, dims 8(l/16) ..
     uint32_t p;     // P rows 16w + l%16, tokens 8(l/16) ..
     uint32_t kt;    // k^T rows 32w + l%16, tokens 8(l/16) ..
-    uint32_t u;     // U rows 16w + 4(l/16), column l%16 of the block
+    uint32_t u;     // U rows 16w + 4(l/16) .. + 3, column l%16 of the block (one float4)
     uint32_t g;     // c of rows 16w + 4(l/16) ..
 };
 
@@ -460,7 +460,7 @@ __device__ __forceinline__ GdnOff gdn_offsets(int cb) {
     f.a = static_cast<uint32_t>(((16 * wave + c16) * kGdnD + 8 * G) * 2);
     f.p = static_cast<uint32_t>(((16 * wave + c16) * kGdnC + 8 * G) * 2);
     f.kt = static_cast<uint32_t>(((32 * wave + c16) * kGdnC + 8 * G) * 2);
-    f.u = static_cast<uint32_t>(((16 * wave + 4 * G) * kGdnD + kStCols * cb + c16) * 4);
+    f.u = static_cast<uint32_t>(((4 * wave + G) * kGdnD + kStCols * cb + c16) * 16);
     f.g = static_cast<uint32_t>((16 * wave + 4 * G) * 4);
     return f;
 }
@@ -490,9 +490,11 @@ __device__ __forceinline__ void gdn_load_ops(const GdnWs& w, int64_t slot, int h
     }
     const float* u = w.u + hs * (kGdnC * kGdnD);
 #pragma unroll
-    for (int ct = 0; ct < kStCt; ++ct)
+    for (int ct = 0; ct < kStCt; ++ct) {
+        const f32x4_t u4 = ld_off<f32x4_t>(u, f.u + 16 * ct * 16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o.u[ct][r] = ld_off<float>(u, f.u + (r * kGdnD + 16 * ct) * 4);
+        for (int r = 0; r < 4; ++r) o.u[ct][r] = u4[r];
+    }
     const float* gm = w.gam + hs * kGdnC;
     const float4 g4 = ld_off<float4>(gm, f.g);
     o.gr[0] = g4.x;
