@@ -109,15 +109,27 @@ __device__ __forceinline__ void stage_dma(const uint16_t* kb, int j0, int j_end,
                                           const DmaOffsets& d, KTile& t) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if constexpr (!kPaged && kMode != kModeSample) {
+    if constexpr (kMode != kModeSample) {
         // a step wholly below j_end needs no clamp: the step's rows start at
         // a scalar base and each lane's byte offset from it is fixed, so the
-        // loads take the scalar-base form and cost no vector address arithmetic
+        // loads take the scalar-base form and cost no vector address
+        // arithmetic.  Paged, the base is the wave's first row: its 16 rows
+        // are one 16-aligned run inside one page (pages hold >= 16 blocks).
         if (j0 + kColStep <= j_end) {
-            const uint16_t* base = kb + static_cast<int64_t>(j0) * kDi;
+            const uint16_t* base;
+            uint32_t sub = 0;
+            if constexpr (kPaged) {
+                const int jw = j0 + 16 * wave;
+                const int pg = __builtin_amdgcn_readfirstlane(min(max(kp.tbl[(jw * kBlock) >> kp.shift], 0), kp.n_pages - 1));
+                const int64_t row0 = (static_cast<int64_t>(pg) << (kp.shift - 2)) | (jw & ((1 << (kp.shift - 2)) - 1));
+                base = kb + row0 * kDi;
+                sub = static_cast<uint32_t>(16 * wave * kDi * 2);
+            } else {
+                base = kb + static_cast<int64_t>(j0) * kDi;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t off = d.off[i];
+                const uint32_t off = d.off[i] - sub;
                 const uint32_t lds = __builtin_amdgcn_readfirstlane(
                     static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&t.chunk[16 * wave + 4 * i][0])));
 #pragma clang diagnostic push
