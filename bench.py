@@ -485,7 +485,7 @@ def gdn_measure(args, torch, qsa, I):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus N with N > 1 is not supported",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus N with N > 1 is not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
     QSA_OK = 0,
     QSA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or stride */
-    QSA_ERR_UNSUPPORTED = 2,      /* legal but outside what this build handles  */
+    QSA_ERR_UNSUPPORTED = 2,      /* legal but outside what the library handles */
     QSA_ERR_WORKSPACE = 3,        /* workspace missing or too small             */
     QSA_ERR_HIP = 4               /* a HIP runtime call or launch failed        */
 } qsa_status_t;
