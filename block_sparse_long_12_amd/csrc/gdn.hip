@@ -14,7 +14,12 @@
 // then o = exp(c) (q S_0) + P w with P_ij = exp(c_i - c_j) q_i.k_j (j <= i), and
 // the state leaves the chunk as exp(c_last) S_0 + k^T (exp(c_last - c) w).
 //
-//  gdn_prep_kernel   chunk-parallel, one workgroup per (sequence, chunk, Q/K
+//  gdn_prefill_kernel one launch per workspace segment of 512 chunks, with two
+//                    roles: the state pass over segment s in its first
+//                    workgroups and the prep of segment s + 1 in the rest (the
+//                    prep depends only on the inputs, so it runs on the CUs
+//                    the state pass leaves idle; two workspace halves in turn).
+//   prep role        chunk-parallel, one workgroup per (sequence, chunk, Q/K
 //                    head): normalises q and k (bf16, every load in flight at
 //                    once) and forms k k^T and q k^T once on the matrix cores;
 //                    then for each of the head's 3 V heads builds A and P from
@@ -24,7 +29,7 @@
 //                    as bf16 matrix-core products of the column-scaled inverse
 //                    (split into bf16 hi + lo) with V and k, writing U (fp32),
 //                    -Wk and P (bf16) and c.
-//  gdn_state_kernel  sequential over chunks, one workgroup per (sequence, V
+//   state role       sequential over chunks, one workgroup per (sequence, V
 //                    head, 32 state columns): the state block (128 x 32 fp32)
 //                    lives in matrix-core accumulators for the whole call;
 //                    per chunk W = U - Wk S, o = exp(c)(q S) + P W and the
@@ -64,7 +69,8 @@ static size_t gdn_seg_bytes(int batch, int nseg) {
 
 size_t gdn_prefill_ws_bytes(int batch, int n_tokens) {
     const int chunks = (n_tokens + kGdnC - 1) / kGdnC;
-    return gdn_seg_bytes(batch, chunks < kGdnSegChunks ? chunks : kGdnSegChunks);
+    // two segments' operands when there are several: one is read while the next is written
+    return gdn_seg_bytes(batch, chunks < kGdnSegChunks ? chunks : kGdnSegChunks) * (chunks > kGdnSegChunks ? 2 : 1);
 }
 
 static GdnWs gdn_carve(void* ws, int batch, int nseg) {
@@ -150,14 +156,14 @@ __device__ __forceinline__ void put_pair_t(uint16_t (*dst)[kGdnC + 8], int p, in
     }
 }
 
-__global__ __launch_bounds__(256, 2) void gdn_prep_kernel(GdnIn in, GdnWs w, int seg_c0, int nseg, int T) {
-    __shared__ PrepSmem sm;
+__device__ __forceinline__ void gdn_prep_body(const GdnIn& in, const GdnWs& w, int seg_c0, int nseg, int T, int bid,
+                                              PrepSmem& sm) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int c16 = lane & 15, G = lane >> 4;
-    const int hk = blockIdx.x % kGdnHk;
-    const int rest = blockIdx.x / kGdnHk;
+    const int hk = bid % kGdnHk;
+    const int rest = bid / kGdnHk;
     const int cl = rest % nseg;
     const int b = rest / nseg;
     const int t0 = (seg_c0 + cl) * kGdnC;
@@ -599,14 +605,14 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][kStCt
         }
 }
 
-__global__ __launch_bounds__(256) void gdn_state_kernel(GdnIn in, GdnWs w, int seg_c0, int nseg, int T) {
-    __shared__ StateBuf sm[2];
+__device__ __forceinline__ void gdn_state_body(const GdnIn& in, const GdnWs& w, int seg_c0, int nseg, int T, int bid,
+                                               int nwg, StateBuf (&sm)[2]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c16 = lane & 15, G = lane >> 4;
     // workgroups are dealt to the 8 XCDs round-robin; renumber them so the
     // column blocks of one head run on one XCD and share its L2 copy of the
-    // head's chunk operands (the grid, batch x 48 x blocks, is a multiple of 8)
-    const int wg = static_cast<int>((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8);
+    // head's chunk operands (their count, batch x 48 x blocks, is a multiple of 8)
+    const int wg = (bid % 8) * (nwg / 8) + bid / 8;
     const int cb = wg % (kGdnD / kStCols);
     const int rest = wg / (kGdnD / kStCols);
     const int h = rest % kGdnHv;
@@ -648,18 +654,45 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(GdnIn in, GdnWs w, int s
             for (int r = 0; r < 4; ++r) sg[(32 * wave + 16 * rt + 4 * G + r) * kGdnD + 16 * ct] = S[rt][ct][r];
 }
 
+// One launch per workspace segment: its first nwg_state workgroups run the
+// state pass over segment s while the rest run the prep of segment s + 1 (which
+// depends only on the inputs), so the prep fills the CUs the chunk-sequential
+// state pass leaves idle.  Consecutive segments use the two halves of the
+// workspace in turn; each half is written by one launch and read by the next.
+union GdnSmem {
+    PrepSmem p;
+    StateBuf s[2];
+};
+
+__global__ __launch_bounds__(256, 2) void gdn_prefill_kernel(GdnIn in, GdnWs ws_state, int c0_state, int nseg_state,
+                                                            int nwg_state, GdnWs ws_prep, int c0_prep, int nseg_prep,
+                                                            int T) {
+    __shared__ GdnSmem sm;
+    const int bid = static_cast<int>(blockIdx.x);
+    if (bid < nwg_state)
+        gdn_state_body(in, ws_state, c0_state, nseg_state, T, bid, nwg_state, sm.s);
+    else
+        gdn_prep_body(in, ws_prep, c0_prep, nseg_prep, T, bid - nwg_state, sm.p);
+}
+
 hipError_t launch_gdn_prefill(const GdnIn& in, int batch, int n_tokens, void* ws, hipStream_t stream) {
     const int chunks = (n_tokens + kGdnC - 1) / kGdnC;
-    for (int c0 = 0; c0 < chunks; c0 += kGdnSegChunks) {
-        const int nseg = min(kGdnSegChunks, chunks - c0);
-        const GdnWs w = gdn_carve(ws, batch, nseg);
-        hipLaunchKernelGGL(gdn_prep_kernel, dim3(static_cast<unsigned>(batch * nseg * kGdnHk)), dim3(256), 0, stream,
-                           in, w, c0, nseg, n_tokens);
-        hipError_t e = hipGetLastError();
+    const int nsegs = (chunks + kGdnSegChunks - 1) / kGdnSegChunks;
+    const size_t half = gdn_seg_bytes(batch, min(chunks, kGdnSegChunks));
+    auto seg_len = [&](int s) { return min(kGdnSegChunks, chunks - s * kGdnSegChunks); };
+    auto seg_ws = [&](int s) { return gdn_carve(static_cast<char*>(ws) + (s & 1) * half, batch, seg_len(s)); };
+    const int nwg_state = batch * kGdnHv * (kGdnD / kStCols);
+    for (int s = -1; s < nsegs; ++s) {
+        const bool st = s >= 0, pr = s + 1 < nsegs;
+        const int n_st = st ? nwg_state : 0;
+        const int n_pr = pr ? batch * seg_len(s + 1) * kGdnHk : 0;
+        const GdnWs w_st = st ? seg_ws(s) : GdnWs{};
+        const GdnWs w_pr = pr ? seg_ws(s + 1) : GdnWs{};
+        hipLaunchKernelGGL(gdn_prefill_kernel, dim3(static_cast<unsigned>(n_st + n_pr)), dim3(256), 0, stream, in, w_st,
+                           st ? s * kGdnSegChunks : 0, st ? seg_len(s) : 0, n_st, w_pr,
+                           pr ? (s + 1) * kGdnSegChunks : 0, pr ? seg_len(s + 1) : 0, n_tokens);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(gdn_state_kernel, dim3(static_cast<unsigned>(batch * kGdnHv * (kGdnD / kStCols))),
-                           dim3(256), 0, stream, in, w, c0, nseg, n_tokens);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
 }
