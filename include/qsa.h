@@ -401,10 +401,12 @@ qsa_status_t qsa_decode_step_paged(const uint16_t* q, int64_t q_seq_stride,
  *         writing strength per V head and token
  *   state float32 [B][48][128][128], read as S_0 and overwritten with S_T.
  * qsa_gdn_prefill takes T tokens per sequence in chunks of 64 (the recurrence
- * rewritten chunk-parallel: bf16 matrix-core products, fp32 accumulation and
- * triangular solves, the state in fp32); its workspace
- * (qsa_gdn_prefill_workspace_bytes, 256-byte aligned) needs no
- * initialisation.  qsa_gdn_decode takes one token per sequence with fixed
+ * rewritten chunk-parallel: bf16 matrix-core products, fp32 accumulation, an
+ * fp32 inverse of each chunk's triangular system, the state in fp32); its
+ * workspace (qsa_gdn_prefill_workspace_bytes, 256-byte aligned: the operands
+ * of up to 512 chunks per sequence, twice over when T spans more than 512
+ * chunks) needs no initialisation, and a workspace sized for T serves any
+ * shorter call.  qsa_gdn_decode takes one token per sequence with fixed
  * contiguous layouts q, k [B][16][128], v and out [B][48][128], g and beta
  * [B][48], and applies the recurrence directly in fp32.
  */
