@@ -61,6 +61,8 @@ def parse():
                     help="also time a decode step of this many new tokens per sequence (1 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=48, help="oracle rows timed for cpu_baseline (0 = skip)")
     ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet measurements")
+    ap.add_argument("--serial", action="store_true",
+                    help="prefill on one stream (index-select, then attention, per query chunk)")
     ap.add_argument("--gdn-tokens", type=int, default=104858, help="tokens of the Gated DeltaNet prefill")
     ap.add_argument("--page-tokens", type=int, default=256,
                     help="page size of the paged-cache measurements (0 = skip them)")
@@ -129,11 +131,19 @@ class Prefill:
         self.out = torch.empty((B, T, 24, 256), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, T, 24), dtype=torch.float32, device=dev)
         self.q_rot = torch.empty_like(self.q_raw)
+        self.side = torch.cuda.Stream()      # default priority
+        self.overlap = True
         torch.cuda.synchronize()
 
     def step(self, timer=None):
-        """One layer step; `timer(name)` returns a context that brackets launches with events."""
-        wl, q = self.wl, self.qsa
+        """One layer step; `timer(name, stream)` returns a context that brackets launches with events.
+
+        With `overlap` (the default) the index-selects of the query chunks run in
+        order on a second stream and each chunk's attention waits only for its
+        own selection, so the selection of chunk c + 1 (matrix-core bound)
+        runs beside the attention of chunk c (HBM bound); the kernels and
+        their results are the same as in the one-stream order."""
+        wl, q, torch = self.wl, self.qsa, self.torch
         B, T, ctx = wl.batch, wl.tq, wl.ctx
         pos = [ctx] * B
         with timer("rope"):
@@ -142,15 +152,36 @@ class Prefill:
         with timer("compress"):
             q.compress_block_keys(self.k_idx, ctx // 4, (ctx + T) // 4, self.kbar)
         ch = self.bufs.chunk
-        for c0 in range(0, T, ch):
-            c1 = min(T, c0 + ch)
-            cpos = [ctx + c0] * B
-            with timer("index_select"):
-                q.index_select_prefill(self.q_idx[:, c0:c1], self.kbar, cpos, wl.budget, self.bufs.scores,
-                                       self.bufs.sel[:, c0:c1], self.bufs.workspace)
+        chunks = [(c0, min(T, c0 + ch)) for c0 in range(0, T, ch)]
+        if not self.overlap:
+            for c0, c1 in chunks:
+                cpos = [ctx + c0] * B
+                with timer("index_select"):
+                    q.index_select_prefill(self.q_idx[:, c0:c1], self.kbar, cpos, wl.budget, self.bufs.scores,
+                                           self.bufs.sel[:, c0:c1], self.bufs.workspace)
+                with timer("sparse_attn_prefill"):
+                    q.sparse_attn_prefill(self.q_rot[:, c0:c1], self.k_cache, self.v_cache,
+                                          self.bufs.sel[:, c0:c1], cpos, self.out[:, c0:c1], self.lse[:, c0:c1])
+            return
+        main = torch.cuda.current_stream()
+        ready = torch.cuda.Event()
+        ready.record(main)
+        self.side.wait_event(ready)                  # block keys compressed
+        done = []
+        for c0, c1 in chunks:
+            with timer("index_select", self.side):
+                q.index_select_prefill(self.q_idx[:, c0:c1], self.kbar, [ctx + c0] * B, wl.budget,
+                                       self.bufs.scores, self.bufs.sel[:, c0:c1], self.bufs.workspace,
+                                       stream=self.side)
+            e = torch.cuda.Event()
+            e.record(self.side)
+            done.append(e)
+        for (c0, c1), e in zip(chunks, done):
+            main.wait_event(e)
             with timer("sparse_attn_prefill"):
                 q.sparse_attn_prefill(self.q_rot[:, c0:c1], self.k_cache, self.v_cache, self.bufs.sel[:, c0:c1],
-                                      cpos, self.out[:, c0:c1], self.lse[:, c0:c1])
+                                      [ctx + c0] * B, self.out[:, c0:c1], self.lse[:, c0:c1])
+        main.wait_stream(self.side)
 
 
 def random_pages(torch, B, n_log, seed):
@@ -190,15 +221,36 @@ class PagedPrefill:
             q.paged_append(self.cache, pos, k_new=pf.k_new, v_new=self.v_new, k_idx_new=self.k_idx_new,
                            rope=pf.rope)
         ch = self.bufs.chunk
-        for c0 in range(0, T, ch):
-            c1 = min(T, c0 + ch)
-            cpos = [ctx + c0] * B
-            with timer("index_select"):
-                q.index_select_prefill_paged(pf.q_idx[:, c0:c1], self.cache, cpos, wl.budget, self.bufs.scores,
-                                             self.bufs.sel[:, c0:c1], self.bufs.workspace)
-            with timer("sparse_attn_prefill"):
-                q.sparse_attn_prefill_paged(pf.q_rot[:, c0:c1], self.cache, self.bufs.sel[:, c0:c1], cpos,
-                                            pf.out[:, c0:c1], pf.lse[:, c0:c1])
+        chunks = [(c0, min(T, c0 + ch)) for c0 in range(0, T, ch)]
+        torch = self.torch
+        side = pf.side if pf.overlap else torch.cuda.current_stream()
+        main = torch.cuda.current_stream()
+        if pf.overlap:                               # the same two-stream order as Prefill.step
+            ready = torch.cuda.Event()
+            ready.record(main)
+            side.wait_event(ready)
+        done = []
+        for c0, c1 in chunks:
+            with timer("index_select", side):
+                q.index_select_prefill_paged(pf.q_idx[:, c0:c1], self.cache, [ctx + c0] * B, wl.budget,
+                                             self.bufs.scores, self.bufs.sel[:, c0:c1], self.bufs.workspace,
+                                             stream=side)
+            e = torch.cuda.Event()
+            e.record(side)
+            done.append(e)
+            if not pf.overlap:
+                self._attend(timer, c0, c1)
+        if pf.overlap:
+            for (c0, c1), e in zip(chunks, done):
+                main.wait_event(e)
+                self._attend(timer, c0, c1)
+            main.wait_stream(side)
+
+    def _attend(self, timer, c0, c1):
+        pf, wl = self.pf, self.wl
+        with timer("sparse_attn_prefill"):
+            self.qsa.sparse_attn_prefill_paged(pf.q_rot[:, c0:c1], self.cache, self.bufs.sel[:, c0:c1],
+                                               [wl.ctx + c0] * wl.batch, pf.out[:, c0:c1], pf.lse[:, c0:c1])
 
 
 class Decode:
@@ -293,17 +345,17 @@ class EventTimer:
         self.torch = torch
         self.pairs = []          # (name, start, end)
 
-    def __call__(self, name):
+    def __call__(self, name, stream=None):
         timer = self
 
         class _Ctx:
             def __enter__(self_inner):
                 self_inner.s = timer.torch.cuda.Event(enable_timing=True)
-                self_inner.s.record()
+                self_inner.s.record(stream)
 
             def __exit__(self_inner, *exc):
                 e = timer.torch.cuda.Event(enable_timing=True)
-                e.record()
+                e.record(stream)
                 timer.pairs.append((name, self_inner.s, e))
                 return False
 
@@ -319,7 +371,7 @@ class EventTimer:
 
 
 class NullTimer:
-    def __call__(self, name):
+    def __call__(self, name, stream=None):
         class _Ctx:
             def __enter__(self):
                 return None
@@ -504,6 +556,7 @@ def main():
     log(args, f"inputs {wl.name}: {time.time() - t0:.1f}s")
     rope = qsa.YARN if args.rope == "yarn" else None
     pf = Prefill(wl, x, torch, qsa, rope)
+    pf.overlap = not args.serial
     for _ in range(args.warmup):
         pf.step(NullTimer())
     torch.cuda.synchronize()
@@ -557,6 +610,9 @@ def main():
                    "query_chunk": wl.chunk, "heads": "24q/2kv x 256, indexer 4q/1k x 128",
                    "rope": "static YaRN, factor 4 over 262144" if args.rope == "yarn" else "plain, theta 1e7"},
         "roofline": roofline,
+        "schedule": ("one stream: per query chunk the index-select, then attention" if args.serial else
+                     "two streams: the query chunks' index-selects in order on a second stream, each chunk's "
+                     "attention after its own selection (kernel times overlap, so they sum past ms_per_step)"),
         "mfma": mfma,
         "kernels_ms_per_step": {k: t / args.steps for k, (t, n) in kern.items()},
         "launches_per_step": {k: n // args.steps for k, (t, n) in kern.items()},
