@@ -374,7 +374,8 @@ class PrefillBuffers:
 
 
 def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0: int, budget: int,
-                  out, lse, bufs: PrefillBuffers, q_rot, stream=None, gate=None, rope: Rope | None = None):
+                  out, lse, bufs: PrefillBuffers, q_rot, stream=None, gate=None, rope: Rope | None = None,
+                  side_stream=None):
     """One QSA layer over tq new tokens of every sequence, all at q_pos0.
 
     q_raw [B, tq, 24, 256] and k_new_raw [B, tq, 2, 256] are unrotated; the
@@ -383,6 +384,10 @@ def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0
     (Q -> q_rot, K -> cache), compress the blocks the chunk completes, then per
     query chunk the fused index-select, then attention (with the optional
     output gate [B, tq, 24, 256]).  rope: rotary parameters (see rope_apply).
+    side_stream: when given, the query chunks' index-selects run in order on it
+    and each chunk's attention (on `stream`) waits only for its own selection,
+    so the selection of chunk c + 1 runs beside the attention of chunk c; the
+    kernels and their results are the same.
     """
     B, tq = q_raw.shape[0], q_raw.shape[1]
     pos = [q_pos0] * B
@@ -390,14 +395,34 @@ def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0
     rope_apply(k_new_raw, pos, out=k_cache[:, q_pos0:q_pos0 + tq], rope=rope, stream=stream)
     b0, b1 = q_pos0 // BLOCK, (q_pos0 + tq) // BLOCK
     compress_block_keys(k_idx, b0, b1, kbar, stream=stream)
-    for c0 in range(0, tq, bufs.chunk):
-        c1 = min(tq, c0 + bufs.chunk)
-        cpos = [q_pos0 + c0] * B
-        index_select_prefill(q_idx[:, c0:c1], kbar, cpos, budget, bufs.scores, bufs.sel[:, c0:c1],
-                             bufs.workspace, stream=stream)
-        sparse_attn_prefill(q_rot[:, c0:c1], k_cache, v_cache, bufs.sel[:, c0:c1], cpos, out[:, c0:c1],
-                            None if lse is None else lse[:, c0:c1], stream=stream,
+    chunks = [(c0, min(tq, c0 + bufs.chunk)) for c0 in range(0, tq, bufs.chunk)]
+
+    def attend(c0, c1):
+        sparse_attn_prefill(q_rot[:, c0:c1], k_cache, v_cache, bufs.sel[:, c0:c1], [q_pos0 + c0] * B,
+                            out[:, c0:c1], None if lse is None else lse[:, c0:c1], stream=stream,
                             gate=None if gate is None else gate[:, c0:c1])
+
+    if side_stream is None:
+        for c0, c1 in chunks:
+            index_select_prefill(q_idx[:, c0:c1], kbar, [q_pos0 + c0] * B, budget, bufs.scores,
+                                 bufs.sel[:, c0:c1], bufs.workspace, stream=stream)
+            attend(c0, c1)
+        return out
+    main = torch.cuda.current_stream() if stream is None else stream
+    ready = torch.cuda.Event()
+    ready.record(main)
+    side_stream.wait_event(ready)                    # block keys compressed
+    done = []
+    for c0, c1 in chunks:
+        index_select_prefill(q_idx[:, c0:c1], kbar, [q_pos0 + c0] * B, budget, bufs.scores,
+                             bufs.sel[:, c0:c1], bufs.workspace, stream=side_stream)
+        e = torch.cuda.Event()
+        e.record(side_stream)
+        done.append(e)
+    for (c0, c1), e in zip(chunks, done):
+        main.wait_event(e)
+        attend(c0, c1)
+    main.wait_stream(side_stream)
     return out
 
 
@@ -705,7 +730,8 @@ def decode_step_paged(q_raw, k_new_raw, q_idx, cache: PagedCache, pos, budget: i
 
 
 def prefill_layer_paged(q_raw, k_new_raw, v_new, q_idx, k_idx_new, cache: PagedCache, q_pos0: int, budget: int,
-                        out, lse, bufs: PrefillBuffers, q_rot, stream=None, gate=None, rope: Rope | None = None):
+                        out, lse, bufs: PrefillBuffers, q_rot, stream=None, gate=None, rope: Rope | None = None,
+                  side_stream=None):
     """prefill_layer on the paged cache: the new K (rotated), V and indexer-key
     rows are written into their pages with the keys of the blocks they
     complete (paged_append), then per query chunk the fused index-select and
