@@ -195,12 +195,20 @@ def _plant_needles(wl: Workload, q_idx: torch.Tensor, k_idx: torch.Tensor,
             out.append((b, t, j))
             break
     needles = np.array(out, dtype=np.int64).reshape(-1, 3)
-    for b, t, j in needles:
+    plant_needles(q_idx, k_idx, q_pos0, needles)
+    return needles
+
+
+def plant_needles(q_idx: torch.Tensor, k_idx: torch.Tensor, q_pos0, needles) -> None:
+    """Plant needles (b, t, j) in place: the 4 indexer keys of block j of
+    sequence b become bf16(4 * u), u the unit vector along the sum of the 4
+    indexer query heads of the token at position t (row t - q_pos0[b] of
+    q_idx).  q_idx [B, tq, 4, 128] and k_idx [B, L, 128] are CPU bf16."""
+    for b, t, j in np.asarray(needles, dtype=np.int64).reshape(-1, 3):
         row = q_idx[b, t - int(q_pos0[b])].to(torch.float64).sum(dim=0)
         u = row / row.norm()
         key = (4.0 * u).to(torch.bfloat16)
         k_idx[b, BLOCK * j: BLOCK * j + BLOCK, :] = key
-    return needles
 
 
 def make_inputs(wl: Workload | str, threads: int | None = None) -> Inputs:

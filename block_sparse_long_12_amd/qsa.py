@@ -397,25 +397,40 @@ def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0
     compress_block_keys(k_idx, b0, b1, kbar, stream=stream)
     chunks = [(c0, min(tq, c0 + bufs.chunk)) for c0 in range(0, tq, bufs.chunk)]
 
+    def select(c0, c1, st):
+        index_select_prefill(q_idx[:, c0:c1], kbar, [q_pos0 + c0] * B, budget, bufs.scores,
+                             bufs.sel[:, c0:c1], bufs.workspace, stream=st)
+
     def attend(c0, c1):
         sparse_attn_prefill(q_rot[:, c0:c1], k_cache, v_cache, bufs.sel[:, c0:c1], [q_pos0 + c0] * B,
                             out[:, c0:c1], None if lse is None else lse[:, c0:c1], stream=stream,
                             gate=None if gate is None else gate[:, c0:c1])
 
+    _chunk_schedule(chunks, select, attend, stream, side_stream)
+    return out
+
+
+def _chunk_schedule(chunks, select, attend, stream, side_stream):
+    """Run select(c0, c1, stream) then attend(c0, c1) for every query chunk.
+
+    One stream: select and attend alternate on `stream`.  With side_stream:
+    the selections run in order on side_stream (which first waits for the
+    work already queued on `stream`) and each chunk's attention on `stream`
+    waits on an event of its own selection, so selection c + 1 runs beside
+    attention c.  The selections share one scratch workspace, which the
+    in-order side stream makes safe; `stream` finally waits for side_stream."""
     if side_stream is None:
         for c0, c1 in chunks:
-            index_select_prefill(q_idx[:, c0:c1], kbar, [q_pos0 + c0] * B, budget, bufs.scores,
-                                 bufs.sel[:, c0:c1], bufs.workspace, stream=stream)
+            select(c0, c1, stream)
             attend(c0, c1)
-        return out
+        return
     main = torch.cuda.current_stream() if stream is None else stream
     ready = torch.cuda.Event()
     ready.record(main)
-    side_stream.wait_event(ready)                    # block keys compressed
+    side_stream.wait_event(ready)                    # rotary, appends and block keys done
     done = []
     for c0, c1 in chunks:
-        index_select_prefill(q_idx[:, c0:c1], kbar, [q_pos0 + c0] * B, budget, bufs.scores,
-                             bufs.sel[:, c0:c1], bufs.workspace, stream=side_stream)
+        select(c0, c1, side_stream)
         e = torch.cuda.Event()
         e.record(side_stream)
         done.append(e)
@@ -423,7 +438,6 @@ def prefill_layer(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, q_pos0
         main.wait_event(e)
         attend(c0, c1)
     main.wait_stream(side_stream)
-    return out
 
 
 def index_select_workspace(batch: int, device="cuda", tq: int = 1) -> torch.Tensor:
@@ -731,23 +745,28 @@ def decode_step_paged(q_raw, k_new_raw, q_idx, cache: PagedCache, pos, budget: i
 
 def prefill_layer_paged(q_raw, k_new_raw, v_new, q_idx, k_idx_new, cache: PagedCache, q_pos0: int, budget: int,
                         out, lse, bufs: PrefillBuffers, q_rot, stream=None, gate=None, rope: Rope | None = None,
-                  side_stream=None):
+                        side_stream=None):
     """prefill_layer on the paged cache: the new K (rotated), V and indexer-key
     rows are written into their pages with the keys of the blocks they
     complete (paged_append), then per query chunk the fused index-select and
-    attention read through the block table."""
+    attention read through the block table.  side_stream: the two-stream
+    order of prefill_layer (same kernels, same results)."""
     B, tq = q_raw.shape[0], q_raw.shape[1]
     pos = [q_pos0] * B
     rope_apply(q_raw, pos, out=q_rot, rope=rope, stream=stream)
     paged_append(cache, pos, k_new=k_new_raw, v_new=v_new, k_idx_new=k_idx_new, rope=rope, stream=stream)
-    for c0 in range(0, tq, bufs.chunk):
-        c1 = min(tq, c0 + bufs.chunk)
-        cpos = [q_pos0 + c0] * B
-        index_select_prefill_paged(q_idx[:, c0:c1], cache, cpos, budget, bufs.scores, bufs.sel[:, c0:c1],
-                                   bufs.workspace, stream=stream)
-        sparse_attn_prefill_paged(q_rot[:, c0:c1], cache, bufs.sel[:, c0:c1], cpos, out[:, c0:c1],
+    chunks = [(c0, min(tq, c0 + bufs.chunk)) for c0 in range(0, tq, bufs.chunk)]
+
+    def select(c0, c1, st):
+        index_select_prefill_paged(q_idx[:, c0:c1], cache, [q_pos0 + c0] * B, budget, bufs.scores,
+                                   bufs.sel[:, c0:c1], bufs.workspace, stream=st)
+
+    def attend(c0, c1):
+        sparse_attn_prefill_paged(q_rot[:, c0:c1], cache, bufs.sel[:, c0:c1], [q_pos0 + c0] * B, out[:, c0:c1],
                                   None if lse is None else lse[:, c0:c1], stream=stream,
                                   gate=None if gate is None else gate[:, c0:c1])
+
+    _chunk_schedule(chunks, select, attend, stream, side_stream)
     return out
 
 

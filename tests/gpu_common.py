@@ -116,8 +116,11 @@ def oracle_layer(x: I.Inputs, yarn: O.Yarn | None = None) -> O.OracleLayer:
 def compare_rows(layer: O.OracleLayer, x: I.Inputs, rows, gpu_scores, gpu_sel, gpu_out, gpu_lse):
     """The end-to-end protocol on query rows [(b, t)]:
       (i)   GPU scores within the float32 accumulation bound of the oracle's;
-      (ii)  where the selected sets differ, every swapped pair is a near tie
-            (oracle scores within the two bounds);
+      (ii)  where GPU scores are given, the GPU selection is exactly the
+            oracle's selection over those scores (select_blocks on the GPU's
+            own float32 row); where the selected sets differ from the
+            oracle's own, every swapped pair is a near tie (oracle scores
+            within the two bounds);
       (iii) the GPU output equals the oracle's attention recomputed with the
             GPU's own selection (max-abs / mean-abs tolerances);
       (iv)  every planted needle of the row is selected.
@@ -141,6 +144,9 @@ def compare_rows(layer: O.OracleLayer, x: I.Inputs, rows, gpu_scores, gpu_sel, g
             assert np.all(err <= bound), (b, t, float(err.max()), float(bound[np.argmax(err - bound)]))
             worst_score = max(worst_score, float((err / bound).max()))
         sgpu = gpu_sel(b, t)
+        if sg is not None:
+            exact = O.select_blocks(np.asarray(sg[:o], np.float32), t, layer.budget)
+            assert np.array_equal(np.asarray(sgpu, np.int32), exact), (b, t, "selection of the GPU's own scores")
         A = set(int(v) for v in sgpu if v >= 0)
         Bs = set(int(v) for v in r.sel if v >= 0)
         assert len(A) == len(Bs) and o in A, (b, t)
@@ -171,3 +177,84 @@ def compare_rows(layer: O.OracleLayer, x: I.Inputs, rows, gpu_scores, gpu_sel, g
         f"max_abs={max_abs:.3g} mean_abs={mean_abs:.3g} lse_abs={lse_abs:.3g}")
     assert max_abs <= MAX_ABS and mean_abs <= MEAN_ABS and lse_abs <= LSE_ABS
     return swaps
+
+
+def ragged_decode_inputs(pos, tq: int, seed: int, needles_per_seq: int = 3, share: int = 0) -> I.Inputs:
+    """Seeded inputs of a decode step whose sequences sit at different
+    positions: sequence b holds pos[b] cached rows and its tq new tokens at
+    pos[b] .. pos[b] + tq - 1 (rows pos[b] + t of k, v, k_idx and row t of q,
+    q_idx).  The first `share` rows of every sequence are sequence 0's (one
+    shared prefix).  Needles: needles_per_seq blocks per sequence, each
+    aligned to one of its new tokens, in blocks complete before that token."""
+    B = len(pos)
+    wl = I.custom_workload("prefill", batch=B, ctx=max(pos), tq=tq, budget=512, n_needles=0, seed=seed)
+    x = I.make_inputs(wl)
+    x.q_pos0 = np.asarray(pos, np.int32)
+    rng = np.random.default_rng(seed)
+    items = []
+    for b in range(B):
+        used = set()
+        for i in range(needles_per_seq):
+            t = int(pos[b]) + i % tq
+            j = int(rng.integers(0, t // 4))
+            if j in used or 4 * j + 4 <= share and b > 0:
+                continue            # one needle per block; shared blocks belong to sequence 0
+            used.add(j)
+            items.append((b, t, j))
+    x.needles = np.asarray(items, np.int64).reshape(-1, 3)
+    I.plant_needles(x.q_idx, x.k_idx, x.q_pos0, x.needles)
+    for b in range(1, B):       # after planting: the shared rows carry sequence 0's needles too
+        x.k[b, :share], x.v[b, :share], x.k_idx[b, :share] = x.k[0, :share], x.v[0, :share], x.k_idx[0, :share]
+    return x
+
+
+class DeviceRaggedDecode:
+    """Device caches of ragged_decode_inputs: sequence b's first pos[b] rows
+    in place (K rotated, block keys of its complete blocks), every row from
+    pos[b] on (those the step writes) and every later block key filled with
+    garbage; new-token tensors [B, tq, ...]."""
+
+    def __init__(self, x: I.Inputs, tq: int, rope=None):
+        pos = [int(p) for p in x.q_pos0]
+        B = len(pos)
+        dev = "cuda"
+        L = x.k.shape[1]
+        self.pos, self.tq = pos, tq
+        g = torch.Generator().manual_seed(12345)
+        junk = lambda shape: (torch.randn(shape, generator=g) * 7).to(torch.bfloat16)
+        k = junk(x.k.shape)
+        v = junk(x.v.shape)
+        ki = junk(x.k_idx.shape)
+        for b in range(B):
+            k[b, :pos[b]], v[b, :pos[b]], ki[b, :pos[b]] = x.k[b, :pos[b]], x.v[b, :pos[b]], x.k_idx[b, :pos[b]]
+        self.k_cache, self.v_cache, self.k_idx = k.to(dev), v.to(dev), ki.to(dev)
+        self.kbar = junk((B, L // 4 + 1, 128)).to(dev)
+        for b in range(B):
+            qsa.rope_apply(self.k_cache[b:b + 1, :pos[b]], [0], rope=rope)
+            qsa.compress_block_keys(self.k_idx[b:b + 1], 0, pos[b] // 4, self.kbar[b:b + 1])
+        sl = lambda t: torch.stack([t[b, pos[b]:pos[b] + tq] for b in range(B)]).contiguous().to(dev)
+        self.k_new, self.v_new, self.k_idx_new = sl(x.k), sl(x.v), sl(x.k_idx)
+        self.q_raw = x.q[:, :tq].contiguous().to(dev)
+        self.q_idx = x.q_idx[:, :tq].contiguous().to(dev)
+        self.ld = max(4, (max(p + tq - 1 for p in pos) // 4 + 3) // 4 * 4)
+        self.scores = torch.full((B, tq, self.ld), float("nan"), device=dev)
+        self.sel = torch.empty((B, tq, 512), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, tq, 24, 256), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, tq, 24), dtype=torch.float32, device=dev)
+
+    def results(self):
+        """{(b, t): (scores [o], sel, out, lse)} of the step's rows."""
+        sc, se = self.scores.cpu().numpy(), self.sel.cpu().numpy()
+        ou, ls = self.out.float().cpu().numpy(), self.lse.cpu().numpy()
+        res = {}
+        for b, p in enumerate(self.pos):
+            for t in range(self.tq):
+                res[(b, p + t)] = (sc[b, t, :(p + t) // 4], se[b, t], ou[b, t], ls[b, t])
+        return res
+
+
+def compare_result_rows(layer: O.OracleLayer, x: I.Inputs, res: dict):
+    """compare_rows over a {(b, t): (scores, sel, out, lse)} map."""
+    rows = sorted(res)
+    return compare_rows(layer, x, rows, lambda b, t: res[(b, t)][0], lambda b, t: res[(b, t)][1],
+                        lambda b, t: res[(b, t)][2], lambda b, t: res[(b, t)][3])

@@ -16,7 +16,9 @@ import torch
 
 from block_sparse_long_12_amd import qsa
 from oracle import qsa_oracle as O
-from tests.gpu_common import compare_rows, say
+from tests.gpu_common import (DeviceRaggedDecode, compare_result_rows, compare_rows, oracle_layer,
+                              ragged_decode_inputs, say)
+from tests.test_gpu_parity import check_appended_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -127,6 +129,35 @@ def test_paged_decode_step_matches_contiguous(ctx, tq, P, share, yarn, gated):
         _same(gkb, kb[b, :n // 4], f"block keys {b}")
 
 
+@pytest.mark.parametrize("pos,tq,P,share,yarn", [
+    ([70001, 4099, 130000], 1, 256, 0, False),
+    ([70003, 70001, 66000], 4, 256, 65536, False),        # three sequences on one 64K-token prefix
+    ([270001, 262142], 3, 1024, 131072, True),           # static YaRN past 262144, a 128K-token shared prefix
+])
+def test_paged_decode_step_matches_the_oracle_rows(pos, tq, P, share, yarn):
+    """The paged decode step (random page order, sequences sharing the pages
+    of one prefix, positions differing per sequence) against the oracle's
+    causal rows: rows and block keys it leaves in the pages, then scores,
+    selection, output and LSE under the end-to-end protocol."""
+    say(f"paged decode vs oracle pos={pos} tq={tq} P={P} share={share} yarn={yarn}")
+    dev_rope, o_yarn = (qsa.YARN, O.Yarn()) if yarn else (None, None)
+    B = len(pos)
+    x = ragged_decode_inputs(pos, tq, seed=P + tq + share % 997, share=share)
+    d = DeviceRaggedDecode(x, tq, rope=dev_rope)          # rotated prefixes and their block keys
+    L = x.k.shape[1]
+    cache = _new_cache(B, P, L, share, seed=P * 3 + tq)
+    for b in range(B):
+        _scatter(cache, b, pos[b], d.k_cache[b], d.v_cache[b], d.k_idx[b], d.kbar[b])
+    ws = qsa.decode_step_workspace(B, 512, tq=tq)
+    qsa.decode_step_paged(d.q_raw, d.k_new, d.q_idx, cache, pos, 512, d.out, d.lse, d.scores, d.sel, ws,
+                          v_new=d.v_new, k_idx_new=d.k_idx_new, rope=dev_rope)
+    torch.cuda.synchronize()
+    rows = [_gather(cache, b, pos[b] + tq) for b in range(B)]
+    check_appended_rows(x, pos, tq, lambda b: rows[b][0][pos[b]:].cpu(), lambda b: rows[b][1][pos[b]:].cpu(),
+                        lambda b: rows[b][2][pos[b]:].cpu(), lambda b, j: rows[b][3][j].cpu(), yarn=o_yarn)
+    compare_result_rows(oracle_layer(x, o_yarn), x, d.results())
+
+
 # ---------------------------------------------------------------- prefill
 
 def _prefill_inputs(B, ctx, T, share, seed):
@@ -213,3 +244,36 @@ def test_shared_prefix_paged_prefill_matches_the_oracle():
     rows = [(b, ctx + i) for b in range(B) for i in range(0, T, 5)]
     compare_rows(layer, types.SimpleNamespace(needles=[]), rows, None, lambda b, t: sel[b, t - ctx],
                  lambda b, t: out[b, t - ctx], lambda b, t: lse[b, t - ctx])
+
+
+def test_paged_two_stream_prefill_matches_one_stream():
+    """prefill_layer_paged with a side stream (the query chunks'
+    index-selects on it, fused path: the first row sees more than 16384
+    blocks) gives the one-stream selections, outputs and LSE bit for bit."""
+    B, ctx, T, chunk, budget, P = 1, 70000, 1536, 512, 512, 256
+    say(f"paged two-stream prefill B={B} ctx={ctx} T={T} chunk={chunk}")
+    x = _prefill_inputs(B, ctx, T, 0, seed=23)
+    dev = "cuda"
+    res = []
+    for side in (None, torch.cuda.Stream()):
+        k_full = x.k.to(dev)
+        k_pre = k_full[:, :ctx].clone()
+        qsa.rope_apply(k_pre, [0] * B)
+        ki_full = x.k_idx.to(dev)
+        kb = torch.zeros((B, (ctx + T) // 4, 128), dtype=bf, device=dev)
+        qsa.compress_block_keys(ki_full, 0, ctx // 4, kb)
+        cache = _new_cache(B, P, ctx + T, 0, seed=29)
+        v_full = x.v.to(dev)
+        _scatter(cache, 0, ctx, k_pre[0], v_full[0], ki_full[0], kb[0])
+        bufs = qsa.PrefillBuffers(B, T, ctx, budget, chunk)
+        out = torch.empty((B, T, 24, 256), dtype=bf, device=dev)
+        lse = torch.empty((B, T, 24), dtype=torch.float32, device=dev)
+        q_raw = x.q.to(dev)
+        qsa.prefill_layer_paged(q_raw, k_full[:, ctx:].contiguous(), v_full[:, ctx:].contiguous(), x.q_idx.to(dev),
+                                ki_full[:, ctx:].contiguous(), cache, ctx, budget, out, lse, bufs,
+                                torch.empty_like(q_raw), side_stream=side)
+        torch.cuda.synchronize()
+        res.append((bufs.sel.clone(), out, lse))
+    _same(res[0][0], res[1][0], "sel")
+    _same(res[0][1], res[1][1], "out")
+    _same(res[0][2], res[1][2], "lse")

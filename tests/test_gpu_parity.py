@@ -15,8 +15,9 @@ import torch
 from block_sparse_long_12_amd import inputs as I
 from block_sparse_long_12_amd import qsa
 from oracle import qsa_oracle as O
-from tests.gpu_common import (MAX_ABS, MEAN_ABS, LSE_ABS, DeviceDecode, DevicePrefill, bf16_ulp_diff,
-                              bits, compare_rows, oracle_layer, say, score_bound)
+from tests.gpu_common import (MAX_ABS, MEAN_ABS, LSE_ABS, DeviceDecode, DevicePrefill, DeviceRaggedDecode,
+                              bf16_ulp_diff, bits, compare_result_rows, compare_rows, oracle_layer,
+                              ragged_decode_inputs, say, score_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -433,6 +434,55 @@ def test_multi_token_decode_steps_match_the_oracle_rows(ctx, n_steps, yarn):
     rows = sorted(res)
     compare_rows(oracle_layer(x, o_yarn), x, rows, lambda b, t: res[(b, t)][0], lambda b, t: res[(b, t)][1],
                  lambda b, t: res[(b, t)][2], lambda b, t: res[(b, t)][3])
+
+
+RAGGED = [([70001, 4099, 130000], 1, False), ([70001, 4099, 130000], 3, False),
+          ([270001, 4099, 262142], 4, True)]
+
+
+def check_appended_rows(x, pos, tq, k_rows, v_rows, ki_rows, kbar_of, yarn=None):
+    """The rows a decode step appended for sequence b at pos[b] .. pos[b] + tq - 1:
+    K rotated (within 1 bf16 ulp of the oracle's rotation, at least 99% equal),
+    V and indexer keys bit for bit, and the key of every block a new token
+    completes equal to the oracle's compression (bit for bit).
+    k_rows(b) / v_rows(b) / ki_rows(b) -> the tq rows in the cache (CPU bf16);
+    kbar_of(b, j) -> block key j of sequence b (CPU bf16 [128])."""
+    same = total = 0
+    for b, p in enumerate(pos):
+        ref_k = O.rope_rotate(bits(x.k[b, p:p + tq]), np.arange(p, p + tq), yarn=yarn)
+        ulp = bf16_ulp_diff(bits(k_rows(b)), ref_k)
+        assert ulp.max() <= 1, (b, int(ulp.max()))
+        same += int((ulp == 0).sum())
+        total += ulp.size
+        assert np.array_equal(bits(v_rows(b)), bits(x.v[b, p:p + tq])), b
+        assert np.array_equal(bits(ki_rows(b)), bits(x.k_idx[b, p:p + tq])), b
+        for t in range(p, p + tq):
+            if t % 4 == 3:
+                j = t // 4
+                ref = O.compress_block_keys(bits(x.k_idx[b]), j, j + 1)[0]
+                assert np.array_equal(bits(kbar_of(b, j)), ref), (b, j)
+    assert same >= 0.99 * total, (same, total)
+
+
+@pytest.mark.parametrize("pos,tq,yarn", RAGGED, ids=["tq1", "tq3", "tq4_yarn"])
+def test_ragged_decode_step_matches_the_oracle_rows(pos, tq, yarn):
+    """One serving decode step whose sequences sit at different positions
+    (rows of other lengths' garbage past each sequence's end) against the
+    oracle's causal rows: the appended rows and completed block keys, then
+    scores, selection, output and LSE under the end-to-end protocol."""
+    say(f"ragged decode step pos={pos} tq={tq} yarn={yarn}")
+    dev_rope, o_yarn = (qsa.YARN, O.Yarn()) if yarn else (None, None)
+    x = ragged_decode_inputs(pos, tq, seed=sum(pos) % 1000 + tq)
+    d = DeviceRaggedDecode(x, tq, rope=dev_rope)
+    ws = qsa.decode_step_workspace(len(pos), 512, tq=tq)
+    qsa.decode_step(d.q_raw, d.k_new, d.q_idx, d.k_idx, d.k_cache, d.v_cache, d.kbar, pos, 512, d.out, d.lse,
+                    d.scores, d.sel, ws, v_new=d.v_new, k_idx_new=d.k_idx_new, rope=dev_rope)
+    torch.cuda.synchronize()
+    check_appended_rows(x, pos, tq, lambda b: d.k_cache[b, pos[b]:pos[b] + tq].cpu(),
+                        lambda b: d.v_cache[b, pos[b]:pos[b] + tq].cpu(),
+                        lambda b: d.k_idx[b, pos[b]:pos[b] + tq].cpu(), lambda b, j: d.kbar[b, j].cpu(),
+                        yarn=o_yarn)
+    compare_result_rows(oracle_layer(x, o_yarn), x, d.results())
 
 
 # ------------------------------------------------------------------ output gate

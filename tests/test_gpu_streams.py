@@ -13,7 +13,9 @@ from tests.gpu_common import DevicePrefill, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("B,ctx,T,chunk,budget", [(1, 40000, 2048, 512, 64), (2, 12000, 1500, 512, 512)])
+@pytest.mark.parametrize("B,ctx,T,chunk,budget", [(1, 40000, 2048, 512, 64), (2, 12000, 1500, 512, 512),
+                                                   (1, 70000, 1536, 512, 512)],     # fused index-select path
+                         ids=["exact-ctx40000", "exact-ctx12000", "fused-ctx70000"])
 def test_two_stream_prefill_matches_one_stream(B, ctx, T, chunk, budget):
     say(f"two-stream prefill B={B} ctx={ctx} T={T} chunk={chunk} budget={budget}")
     x = I.make_inputs(I.custom_workload("prefill", B, ctx, T, budget, seed=11, chunk=chunk))
