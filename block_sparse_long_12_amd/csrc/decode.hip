@@ -3,29 +3,37 @@
 // sequence): the same scores and the same selection as index_scores_kernel
 // followed by select_kernel, spread over hundreds of workgroups per row.  The
 // tokens of a sequence share one pass over its block keys (they are columns
-// of the same matrix-core tiles).  Three launches; every hand-off between workgroups
-// goes through a kernel boundary or a device-scope atomic, never through an
-// in-kernel fence (an agent-scope fence writes back and invalidates the L2 of
-// the XCD, which costs microseconds per workgroup on this part):
+// of the same matrix-core tiles).  Two launches:
 //
-//  decode_scan_kernel      B x G workgroups, long-lived waves that stream
-//                          64-block groups with the next group's loads in
-//                          flight.  Scores every candidate with the shared MFMA
-//                          block_scores (bit-identical to index_scores_kernel),
-//                          stores the scores, counts the top 12 bits of each
-//                          ordered key in an LDS histogram per token and adds
-//                          them to per-row global histograms.  In a decode step
-//                          it also appends the new rows (append_rows).
-//  decode_filter_kernel    rows x F workgroups: each finds the threshold bin from
-//                          the global histogram, then collects its slice's keys
-//                          above the bin (winners) and in the bin (candidates)
-//                          in LDS and appends them to per-row lists with
-//                          one atomic reservation per list.
-//  decode_finalize_kernel  one workgroup per row: sorts the candidates, takes the ones
-//                          still needed, merges, sorts ascending and writes sel;
-//                          if the bin overflowed the list it runs the full radix
-//                          select on the stored row.  Leaves the histogram and
-//                          counters zeroed for the next call.
+//  decode_scan_kernel      B x G scan workgroups (plus, in a decode step, one
+//                          side workgroup per sequence that appends the new
+//                          rows and writes the rotated queries, off the scan's
+//                          critical path).  A scan workgroup streams 64-block
+//                          groups of its range with the next group's loads in
+//                          flight, scores them with the shared MFMA
+//                          block_scores (bit-identical to index_scores_kernel)
+//                          and keeps the scores in LDS -- nothing else in the
+//                          loop.  Then each wave, alone, finds a key T that at
+//                          least K of its own blocks of every row reach (K a
+//                          few times its expected share of the selection) by a
+//                          search over the key bits with ballots, and lists
+//                          every candidate whose key is >= T; the workgroup
+//                          writes its scores to global memory in full lines and
+//                          its list entries to the row's candidate list (one
+//                          reservation per workgroup and row), and max T per row.
+//  decode_finalize_kernel  one workgroup per row: the exact top `keep` of the
+//                          list (one radix level over the listed keys' own
+//                          range, then the cut bin's members ranked), valid
+//                          because every key >= max T is listed, so the list's
+//                          cut is the row's when the cut key is >= max T;
+//                          otherwise (or when a list overflows) the full radix
+//                          select on the stored row.  Emits ascending through
+//                          a block bitmap and leaves the row's control words
+//                          zeroed.
+//
+// Workspace: control words for the largest possible row count at offset 0
+// (zero before the first call, left zero by every call, so one workspace
+// serves calls of any shape), then the candidate lists (no initialisation).
 #include "compress_common.h"
 #include "index_common.h"
 #include "rope_common.h"
@@ -33,39 +41,48 @@
 
 namespace qsa {
 
-constexpr int kDecHistBits = 12;
-constexpr int kDecHistBins = 1 << kDecHistBits;
-constexpr int kDecShift = 32 - kDecHistBits;
-constexpr int kDecCap = 4096;        // threshold-bin candidates sorted in LDS by the last workgroup
+constexpr int kDecCap = 4096;        // cut-bin members resolved in LDS by the finalize
 constexpr int kCtrl = 16;            // control words per row
+constexpr int kDecMaxRows = QSA_MAX_BATCH * QSA_MAX_DECODE_TQ;
+constexpr int kListCap = 6144;       // candidates listed per row
 
-enum { kDoneScan = 0, kDoneFilter, kNDef, kNCand, kBin, kAbove, kInBin };
+enum { kNList = 0, kMaxT, kOverflow };
 
 // per row r = b * tq + t (token t of sequence b, at position q_pos[b] + t)
 struct DecodeWs {
-    uint32_t* hist;     // [rows][4096]
-    uint32_t* ctrl;     // [rows][16]
-    int32_t* defl;      // [rows][QSA_MAX_BUDGET]  keys above the threshold bin
-    uint64_t* cand;     // [rows][kDecCap]         keys in the threshold bin: key << 32 | ~j
+    uint32_t* ctrl;     // [kDecMaxRows][kCtrl]   zero between calls
+    uint64_t* list;     // [rows][kListCap]       key << 32 | ~j, any order
 };
 
 size_t decode_select_ws_bytes(int rows) {
-    return static_cast<size_t>(rows) *
-           (kDecHistBins * 4 + kCtrl * 4 + QSA_MAX_BUDGET * 4 + kDecCap * 8);
+    return static_cast<size_t>(kDecMaxRows) * kCtrl * 4 + static_cast<size_t>(rows) * kListCap * 8;
 }
 
-static DecodeWs carve(void* ws, int rows) {
+static DecodeWs carve(void* ws) {
     char* p = static_cast<char*>(ws);
     DecodeWs w;
-    w.hist = reinterpret_cast<uint32_t*>(p);
-    p += static_cast<size_t>(rows) * kDecHistBins * 4;
     w.ctrl = reinterpret_cast<uint32_t*>(p);
-    p += static_cast<size_t>(rows) * kCtrl * 4;
-    w.defl = reinterpret_cast<int32_t*>(p);
-    p += static_cast<size_t>(rows) * QSA_MAX_BUDGET * 4;
-    w.cand = reinterpret_cast<uint64_t*>(p);
+    w.list = reinterpret_cast<uint64_t*>(p + static_cast<size_t>(kDecMaxRows) * kCtrl * 4);
     return w;
 }
+
+// Candidates a wave lists for a row keeping `keep` of o candidates, n_w of
+// them among the wave's blocks: the expected share m = keep n_w / o plus
+// 4 sqrt(m) + 6, so that for blocks ranked at random a wave holds more of the
+// selection than it lists with probability below 1e-6 (a Poisson tail).  The
+// cut is exact whatever the count: more only costs list space, fewer sends
+// skewed rows to the slower exact path.
+__device__ __forceinline__ int wave_keep(int keep, int o, int n_w) {
+    const float m = static_cast<float>(keep) * static_cast<float>(n_w) / static_cast<float>(o);
+    return min(n_w, static_cast<int>(ceilf(m + 4.f * sqrtf(m))) + 6);
+}
+
+// Queries of a decode step rotated for attention (q_rot [B][tq][24][256]).
+struct QrotArgs {
+    const uint16_t* q;      // unrotated [B][tq][24][256], sequence stride qs (null: not written)
+    int64_t qs;
+    uint16_t* q_rot;        // [B * tq][24][256]
+};
 
 // Device copy of DecodeAppend, with the rotary table.
 struct AppendArgs {
@@ -141,41 +158,76 @@ __global__ __launch_bounds__(192) void decode_append_kernel(Positions pos, int t
     append_rows<kPaged>(ap, pm, blockIdx.x, pos.p[blockIdx.x], tq, threadIdx.x >> 6);
 }
 
-// hist: tq x 4096 words of dynamic LDS (one histogram per token).  kPaged:
-// kbar (and the caches the append writes) are page pools behind pm.
+constexpr int kEmitPerRow = 512;     // candidates one scan workgroup lists per row (LDS)
+
+struct ScanSmem {
+    uint64_t emit[kMaxDecodeTq][kEmitPerRow];
+    int n_emit[kMaxDecodeTq];
+    uint32_t max_t[kMaxDecodeTq];
+    int base[kMaxDecodeTq];
+};
+
+// Scores of the 4 tiles of a 64-block group: the tiles' 12-deep chains
+// interleaved (each tile accumulates in the order of block_scores, so the
+// bits are the same).
+__device__ __forceinline__ void group_scores(const bf16x8_t (&kf)[4][4], const bf16x8_t (&qf)[kIdxSlices],
+                                             f32x4_t (&acc)[4]) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kIdxSlices; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[nt][ks & 3], qf[ks], acc[nt], 0, 0, 0);
+}
+
+// Grid: n_side side workgroups first (one per sequence when the step appends
+// rows or rotates queries, else none), then B x wg_per_seq scan workgroups.
+// Dynamic LDS: tq x (256 * STEPS) scores.  kPaged: kbar (and the caches the
+// append writes) are page pools behind pm.
 template <int STEPS, bool kPaged>
 __global__ __launch_bounds__(256) void decode_scan_kernel(
     const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
-    Positions pos, int budget, int tq, int wg_per_seq, float* __restrict__ scores,
-    int64_t ss, int64_t sld, DecodeWs ws, AppendArgs ap, int append, PageMap pm) {
-    extern __shared__ uint32_t hist[];
+    Positions pos, int budget, int tq, int n_side, int wg_per_seq, float* __restrict__ scores,
+    int64_t ss, int64_t sld, DecodeWs ws, AppendArgs ap, int append, QrotArgs qr, PageMap pm) {
+    constexpr int R = 256 * STEPS;                      // blocks per scan workgroup
+    extern __shared__ float lds_sc[];                   // [tq][R]
+    __shared__ ScanSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // scalar: loop control stays uniform
-    const int b = blockIdx.x / wg_per_seq;
-    const int g = blockIdx.x % wg_per_seq;
+
+    if (static_cast<int>(blockIdx.x) < n_side) {
+        // side workgroup of sequence b: append the new rows, rotate the queries
+        const int b = blockIdx.x;
+        const int p0 = pos.p[b];
+        if (append) append_rows<kPaged>(ap, pm, b, p0, tq, wave);
+        if (qr.q != nullptr)
+            for (int t = 0; t < tq; ++t)
+                rope_row_wave(qr.q + b * qr.qs + (t * kHq + 6 * wave) * kD,
+                              qr.q_rot + (static_cast<int64_t>(b * tq + t) * kHq + 6 * wave) * kD, 6,
+                              static_cast<double>(p0 + t), ap.inv, false);
+        return;
+    }
+    const int bid = blockIdx.x - n_side;
+    const int b = bid / wg_per_seq;
+    const int g = bid % wg_per_seq;
     const int p0 = pos.p[b];
     const int o_last = (p0 + tq - 1) / kBlock;           // blocks below the last token's own block
 
-    if (append && g == 0) append_rows<kPaged>(ap, pm, b, p0, tq, wave);
-
-    for (int k = tid; k < tq * kDecHistBins; k += 256) hist[k] = 0;
-    lds_barrier();          // the appended rows' stores need not land before the scan
-
     const int c16 = lane & 15;
     const int G = lane >> 4;
-    // column c16 < tq: token c16, its candidates j < o_c; histogram only when
-    // its selection is not trivial
-    const int o_c = (p0 + c16) / kBlock;
-    const int keep_c = min(budget - 1, o_c);
-    const bool col_hist = c16 < tq && keep_c > 0 && keep_c < o_c;
-    uint32_t* hist_c = hist + (c16 < tq ? c16 : 0) * kDecHistBins;
+    if (tid < kMaxDecodeTq) {
+        sm.n_emit[tid] = 0;
+        sm.max_t[tid] = 0u;
+    }
+    lds_barrier();
     bf16x8_t qf[kIdxSlices];
     load_index_q(q_idx + b * qs, 0, tq, qf);            // tokens 0 .. tq-1 in columns 0 .. tq-1, zero elsewhere
     const uint16_t* kb = kPaged ? kbar : kbar + b * kbs;
-    float* sb = scores + b * ss + (c16 < tq ? c16 : 0) * sld;
-    const int j_lo = g * (256 * STEPS);
-    const int j_hi = min(o_last, j_lo + 256 * STEPS);
+    float* lb = lds_sc + (c16 < tq ? c16 : 0) * R;
+    const int j_lo = g * R;
+    const int j_hi = min(o_last, j_lo + R);
     auto load_tile = [&](int jt, bf16x8_t (&kf)[4]) {
         if constexpr (kPaged)
             load_index_k_paged(kb, pm, b, jt, j_hi, kf);
@@ -186,21 +238,15 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     // next is in flight (the next-group address is clamped, never skipped)
     auto step_of = [&](int j) { return (j < j_hi) ? j : (j_hi - 1) / 64 * 64; };
     // 4 tiles of 16 blocks; the lanes of column c < tq hold token c's scores,
-    // 4 consecutive blocks each
-    const int lim_c = min(j_hi, o_c);
+    // 4 consecutive blocks each, kept in LDS
     auto score_group = [&](const bf16x8_t (&kf)[4][4], int j0) {
+        f32x4_t acc[4];
+        group_scores(kf, qf, acc);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            const f32x4_t s = block_scores(kf[nt], qf);
             const int jj = j0 + 16 * nt + 4 * G;
-            if (c16 < tq && jj < j_hi) {
-                *reinterpret_cast<float4*>(sb + jj) = make_float4(s[0], s[1], s[2], s[3]);
-                if (col_hist) {
-#pragma unroll
-                    for (int n = 0; n < 4; ++n)
-                        if (jj + n < lim_c) atomicAdd(&hist_c[score_key(s[n]) >> kDecShift], 1u);
-                }
-            }
+            if (c16 < tq && jj < j_hi)
+                *reinterpret_cast<float4*>(lb + (jj - j_lo)) = make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
         }
     };
     // STEPS groups of 64 blocks per wave (stride 256 over the workgroup's
@@ -221,130 +267,150 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
             if (j0 + 256 * st < j_hi) score_group(buf[st & 1], j0 + 256 * st);
         }
     }
-    lds_barrier();
+    // Per row, this wave's candidates: its blocks j0 + 256 st + lane (one per
+    // step) -- it reads back only what it wrote, so no workgroup barrier.
+    __builtin_amdgcn_s_waitcnt(0xc07f);                  // this wave's LDS stores done
     for (int t = 0; t < tq; ++t) {
         const int o_t = (p0 + t) / kBlock;
         const int keep_t = min(budget - 1, o_t);
         if (!(keep_t > 0 && keep_t < o_t)) continue;     // uniform
-        uint32_t* gh = ws.hist + static_cast<int64_t>(b * tq + t) * kDecHistBins;
-        for (int k = tid; k < kDecHistBins; k += 256) {
-            const uint32_t v = hist[t * kDecHistBins + k];
-            if (v) atomicAdd(&gh[k], v);
+        const int lim = min(j_hi, o_t);
+        uint32_t key[STEPS];
+        bool ok[STEPS];
+        int n_w = 0;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const int j = j0 + 256 * st + lane;
+            ok[st] = j < lim;
+            key[st] = ok[st] ? score_key(lds_sc[t * R + (j - j_lo)]) : 0u;
+            n_w += __popcll(__ballot(ok[st]));
         }
-    }
-}
-
-struct FilterSmem {
-    alignas(16) uint32_t hist[kDecHistBins];
-    int32_t def[QSA_MAX_BUDGET];
-    uint64_t cand[kDecCap];
-    int wave_tot[4];
-    uint32_t sh_bin;
-    int sh_above, n_def, n_cand, base_def, base_cand;
-};
-
-constexpr int kFiltPer = 4096;      // scores per filter workgroup: 4 float4 per thread
-
-__global__ __launch_bounds__(256) void decode_filter_kernel(
-    const float* __restrict__ scores, int64_t ss, int64_t sld, Positions pos, int budget, int tq, int wg_per_row,
-    DecodeWs ws) {
-    __shared__ FilterSmem sm;
-    const int tid = threadIdx.x;
-    const int r = blockIdx.x / wg_per_row;                 // row = token t of sequence b
-    const int g = blockIdx.x % wg_per_row;
-    const int b = r / tq;
-    const int t = r % tq;
-    const int p = pos.p[b] + t;
-    const int o = p / kBlock;
-    const int keep = min(budget - 1, o);
-    if (!(keep > 0 && keep < o)) return;                 // trivial rows need no filter
-    uint32_t* ctrl = ws.ctrl + r * kCtrl;
-
-    // the global histogram the scan completed, then this workgroup's scores
-    // (independent of the threshold): all issued at once, the histogram
-    // first so that waiting for it leaves the scores in flight through the
-    // threshold search (the barriers below wait for LDS work only)
-    const uint4* gh = reinterpret_cast<const uint4*>(ws.hist + static_cast<int64_t>(r) * kDecHistBins);
-    uint4 hv[kDecHistBins / 1024];
+        if (n_w == 0) continue;                          // uniform
+        const int kw = wave_keep(keep_t, o_t, n_w);
+        // T with at least kw of the wave's keys >= T (0: every candidate
+        // listed), built from the top bit down, keeping a bit while enough
+        // keys reach the prefix.  For kw <= 64 it is the kw-th largest of the
+        // 64 lane maxima (at most the kw-th largest key: kw lanes each hold a
+        // key >= it), one ballot per bit; else the kw-th largest key itself.
+        uint32_t T = 0u;
+        if (kw < n_w) {
+            if (kw <= 64) {
+                uint32_t lmax = 0u;
 #pragma unroll
-    for (int it = 0; it < kDecHistBins / 1024; ++it) hv[it] = gh[tid + 256 * it];
-    const float* row = scores + b * ss + t * sld;
-    const int j_lo = g * kFiltPer;
-    const int j_hi = min(o, j_lo + kFiltPer);
-    float4 v[4];
+                for (int st = 0; st < STEPS; ++st) lmax = max(lmax, key[st]);
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t c = T | (1u << bit);
+                    if (__popcll(__ballot(lmax >= c)) >= kw) T = c;
+                }
+            } else {
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t c = T | (1u << bit);
+                    int cnt = 0;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int j4 = min(j_lo + 4 * tid + 1024 * it, (o - 1) & ~3);   // clamped: always a legal load
-        v[it] = *reinterpret_cast<const float4*>(row + j4);
-    }
+                    for (int st = 0; st < STEPS; ++st) cnt += __popcll(__ballot(ok[st] && key[st] >= c));
+                    if (cnt >= kw) T = c;
+                }
+            }
+        }
+        // list every candidate with key >= T (at least kw of them)
+        int my = 0;
 #pragma unroll
-    for (int it = 0; it < kDecHistBins / 1024; ++it) reinterpret_cast<uint4*>(sm.hist)[tid + 256 * it] = hv[it];
-    if (tid == 0) {
-        sm.n_def = 0;
-        sm.n_cand = 0;
-    }
-    lds_barrier();
-    find_threshold_bin<256>(sm.hist, kDecHistBins, keep, sm.wave_tot, &sm.sh_bin, &sm.sh_above);
-    const uint32_t tbin = sm.sh_bin;
-    if (g == 0 && tid == 0) {
-        ctrl[kBin] = tbin;
-        ctrl[kAbove] = static_cast<uint32_t>(sm.sh_above);
-        ctrl[kInBin] = sm.hist[tbin];
-    }
-
+        for (int st = 0; st < STEPS; ++st) my += (ok[st] && key[st] >= T) ? 1 : 0;
+        int tot = my;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int j4 = j_lo + 4 * tid + 1024 * it;
-        const float f[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(tot, off);
+            if (lane >= off) tot += y;
+        }
+        const int excl = tot - my;
+        const int wave_n = __shfl(tot, 63);
+        int wbase = 0;
+        if (lane == 0) {
+            wbase = atomicAdd(&sm.n_emit[t], wave_n);
+            if (T != 0u) atomicMax(&sm.max_t[t], T);
+        }
+        wbase = __shfl(wbase, 0);
+        int k = wbase + excl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = j4 + e;
-            if (j >= j_hi) continue;
-            const uint32_t key = score_key(f[e]);
-            const uint32_t bin = key >> kDecShift;
-            if (bin > tbin) {
-                const int k = atomicAdd(&sm.n_def, 1);
-                if (k < QSA_MAX_BUDGET) sm.def[k] = j;
-            } else if (bin == tbin) {
-                const int k = atomicAdd(&sm.n_cand, 1);
-                if (k < kDecCap) sm.cand[k] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~j);
+        for (int st = 0; st < STEPS; ++st) {
+            if (ok[st] && key[st] >= T) {
+                if (k < kEmitPerRow)
+                    sm.emit[t][k] = (static_cast<uint64_t>(key[st]) << 32) |
+                                    static_cast<uint32_t>(~(j0 + 256 * st + lane));
+                ++k;
             }
         }
     }
     lds_barrier();
-    const int nd = min(sm.n_def, QSA_MAX_BUDGET);
-    const int nc = sm.n_cand;
-    if (tid == 0) {
-        sm.base_def = nd ? static_cast<int>(atomicAdd(&ctrl[kNDef], static_cast<uint32_t>(nd))) : 0;
-        sm.base_cand = nc ? static_cast<int>(atomicAdd(&ctrl[kNCand], static_cast<uint32_t>(nc))) : 0;
+    // the scores in full lines: token t's blocks [j_lo, j_hi) from LDS
+    {
+        const int n = j_hi - j_lo;
+        for (int t = 0; t < tq; ++t) {
+            float* sb = scores + b * ss + t * sld + j_lo;
+            for (int i = 4 * tid; i < n; i += 1024)
+                *reinterpret_cast<float4*>(sb + i) = *reinterpret_cast<const float4*>(lds_sc + t * R + i);
+        }
+    }
+    if (tid < tq) {
+        const int ne = sm.n_emit[tid];
+        uint32_t* ctrl = ws.ctrl + (b * tq + tid) * kCtrl;
+        sm.base[tid] = ne ? static_cast<int>(atomicAdd(&ctrl[kNList], static_cast<uint32_t>(min(ne, kEmitPerRow)))) : 0;
+        if (sm.max_t[tid] != 0u) atomicMax(&ctrl[kMaxT], sm.max_t[tid]);
+        if (ne > kEmitPerRow) atomicOr(&ctrl[kOverflow], 1u);
     }
     lds_barrier();
-    int32_t* defl = ws.defl + static_cast<int64_t>(r) * QSA_MAX_BUDGET;
-    uint64_t* cand = ws.cand + static_cast<int64_t>(r) * kDecCap;
-    for (int k = tid; k < nd; k += 256)
-        if (sm.base_def + k < QSA_MAX_BUDGET) defl[sm.base_def + k] = sm.def[k];
-    for (int k = tid; k < min(nc, kDecCap); k += 256)
-        if (sm.base_cand + k < kDecCap) cand[sm.base_cand + k] = sm.cand[k];
+    for (int t = 0; t < tq; ++t) {
+        const int nl = min(sm.n_emit[t], kEmitPerRow);
+        const int base = sm.base[t];
+        uint64_t* list = ws.list + static_cast<int64_t>(b * tq + t) * kListCap;
+        for (int k = tid; k < nl; k += 256)
+            if (base + k < kListCap) list[base + k] = sm.emit[t][k];
+    }
 }
 
-constexpr int kFinNT = 1024;                 // finalize threads
+constexpr int kFinNT = 512;                  // finalize threads
+constexpr int kFinPer = kListCap / kFinNT;   // list entries per thread
+constexpr int kRankMax = 1024;               // cut-bin members ranked directly
+constexpr int kFinBins = 2048;               // radix bins over the listed keys' range
+constexpr int kFinBits = 11;
 constexpr int kBitmapWords = 8192;           // ascending order by bitmap for candidates j < 262144
 
 struct FinalizeSmem {
     union {
-        SelectSmem s;                                        // overflow: full radix select
+        SelectSmem s;                                        // fallback: full radix select
         struct {
+            alignas(16) int32_t chosen[QSA_MAX_BUDGET + 4];  // selection, any order
+            alignas(16) uint64_t cand[kDecCap];              // cut-bin members
+            uint32_t h[kFinBins];                            // radix level
             uint32_t bm[kBitmapWords];                       // one bit per candidate block
-            alignas(16) int32_t chosen[QSA_MAX_BUDGET];      // selection, any order
-            alignas(16) uint64_t cand[kDecCap];              // threshold-bin candidates
-            uint32_t h2[kDecHistBins];                       // second radix level over them
-            alignas(16) uint64_t sub[kDecCap];               // members of the cut sub-bin
             int wave_tot[16];
-            uint32_t sh_bin;
-            int sh_above, n_taken, n_sub;
+            uint32_t wave_min[16], wave_max[16];
+            uint32_t sh_bin, kstar;
+            int sh_above, n_taken, n_cand;
         } m;
     } u;
 };
+
+// set bits of the wave mask m below this lane
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+}
+
+// entries x of cand[0 .. n) ranked by (key, ~j) descending: those with rank
+// < take go to dst[rank]; the one of rank take - 1 (the cut) leaves its key in
+// *kstar.  Every thread must call it.
+template <int NT>
+__device__ __forceinline__ void rank_cut(const uint64_t* cand, int n, int take, int32_t* dst, uint32_t* kstar) {
+    for (int i = threadIdx.x; i < n; i += NT) {
+        const uint64_t x = cand[i];
+        int rk = 0;
+#pragma unroll 8
+        for (int k = 0; k < n; ++k) rk += cand[k] > x ? 1 : 0;
+        if (rk < take) dst[rk] = static_cast<int32_t>(~static_cast<uint32_t>(x));
+        if (rk == take - 1) *kstar = static_cast<uint32_t>(x >> 32);
+    }
+}
 
 __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __restrict__ scores, int64_t ss,
                                                                  int64_t sld, Positions pos, int budget, int tq,
@@ -360,96 +426,138 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
     const int keep = min(budget - 1, o);
     int32_t* out = sel + b * sels + t * budget;
     uint32_t* ctrl = ws.ctrl + r * kCtrl;
-    if (trivial_selection(keep, o, budget, out, kFinNT)) return;   // nothing was accumulated
+    if (trivial_selection(keep, o, budget, out, kFinNT)) return;   // nothing was listed
 
-    // every load of both lists in flight at once, with the control words (the
-    // lists have fixed capacities: unused tails are read and dropped)
-    const int32_t* __restrict__ defl = ws.defl + static_cast<int64_t>(r) * QSA_MAX_BUDGET;
-    const uint64_t* __restrict__ cg = ws.cand + static_cast<int64_t>(r) * kDecCap;
-    int32_t dv[QSA_MAX_BUDGET / kFinNT];
-    uint64_t cv[kDecCap / kFinNT];
+    // the list, every load in flight at once with the control words (fixed
+    // capacity: entries past the count are read and dropped)
+    const uint64_t* __restrict__ lg = ws.list + static_cast<int64_t>(r) * kListCap;
+    uint64_t e[kFinPer];
 #pragma unroll
-    for (int it = 0; it < QSA_MAX_BUDGET / kFinNT; ++it) dv[it] = defl[tid + kFinNT * it];
+    for (int i = 0; i < kFinPer; ++i) e[i] = lg[tid + kFinNT * i];
+    const int n = static_cast<int>(ctrl[kNList]);
+    const uint32_t max_t = ctrl[kMaxT];
+    const bool listed = ctrl[kOverflow] == 0u && n <= kListCap && n >= keep;
+    uint32_t* h = sm.u.m.h;
+    int32_t* chosen = sm.u.m.chosen;
+    bool exact = listed;
+    if (listed) {
+        // one radix level over the listed keys' own range [kmin, kmax]: bin =
+        // (key - kmin) >> shift < 4096 (the listed keys all sit in the tail, so
+        // the top key bits would crowd them into a few bins and serialize the
+        // LDS atomics)
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-    for (int it = 0; it < kDecCap / kFinNT; ++it) cv[it] = cg[tid + kFinNT * it];
-    const int above = static_cast<int>(ctrl[kAbove]);
-    const int inbin = static_cast<int>(ctrl[kInBin]);
-    const int remaining = keep - above;
-    if (inbin > kDecCap) {
+        for (int i = 0; i < kFinPer; ++i)
+            if (tid + kFinNT * i < n) {
+                const uint32_t k = static_cast<uint32_t>(e[i] >> 32);
+                kmin = min(kmin, k);
+                kmax = max(kmax, k);
+            }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), off)));
+            kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), off)));
+        }
+        if ((tid & 63) == 0) {
+            sm.u.m.wave_min[tid >> 6] = kmin;
+            sm.u.m.wave_max[tid >> 6] = kmax;
+        }
+        for (int k = tid; k < kFinBins; k += kFinNT) h[k] = 0u;
+        if (tid == 0) {
+            sm.u.m.n_taken = 0;
+            sm.u.m.n_cand = 0;
+            sm.u.m.kstar = 0u;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int w = 0; w < kFinNT / 64; ++w) {
+            kmin = min(kmin, sm.u.m.wave_min[w]);
+            kmax = max(kmax, sm.u.m.wave_max[w]);
+        }
+        const uint32_t span = kmax - kmin;
+        const int shift = span < kFinBins ? 0 : 32 - __clz(static_cast<int>(span >> kFinBits));
+        auto bin_of = [&](uint64_t x) { return (static_cast<uint32_t>(x >> 32) - kmin) >> shift; };
+#pragma unroll
+        for (int i = 0; i < kFinPer; ++i)
+            if (tid + kFinNT * i < n) atomicAdd(&h[bin_of(e[i])], 1u);
+        lds_barrier();
+        find_threshold_bin<kFinNT>(h, kFinBins, keep, sm.u.m.wave_tot, &sm.u.m.sh_bin, &sm.u.m.sh_above);
+        const uint32_t tbin = sm.u.m.sh_bin;
+        const int above = sm.u.m.sh_above;
+        const int inbin = static_cast<int>(h[tbin]);
+        exact = inbin <= kDecCap;
+        if (exact) {
+            // keys above the cut bin are taken; the cut bin's members go to cand
+            // (positions by ballot and lane count: one LDS atomic per wave and
+            // pass, not one per entry on a single counter)
+            uint64_t* lc = sm.u.m.cand;
+            uint64_t m_up[kFinPer], m_in[kFinPer];
+            int n_up = 0, n_in = 0;
+#pragma unroll
+            for (int i = 0; i < kFinPer; ++i) {
+                const bool ok = tid + kFinNT * i < n;
+                const uint32_t d1 = bin_of(e[i]);
+                m_up[i] = __ballot(ok && d1 > tbin);
+                m_in[i] = __ballot(ok && d1 == tbin);
+                n_up += __popcll(m_up[i]);
+                n_in += __popcll(m_in[i]);
+            }
+            int b_up = 0, b_in = 0;
+            if ((tid & 63) == 0) {
+                b_up = n_up ? atomicAdd(&sm.u.m.n_taken, n_up) : 0;
+                b_in = n_in ? atomicAdd(&sm.u.m.n_cand, n_in) : 0;
+            }
+            b_up = __shfl(b_up, 0);
+            b_in = __shfl(b_in, 0);
+#pragma unroll
+            for (int i = 0; i < kFinPer; ++i) {
+                const int lane = tid & 63;
+                if ((m_up[i] >> lane) & 1ull)
+                    chosen[b_up + lanes_below(m_up[i])] = static_cast<int32_t>(~static_cast<uint32_t>(e[i]));
+                if ((m_in[i] >> lane) & 1ull) lc[b_in + lanes_below(m_in[i])] = e[i];
+                b_up += __popcll(m_up[i]);
+                b_in += __popcll(m_in[i]);
+            }
+            lds_barrier();
+            const int remaining = keep - above;
+            if (inbin <= kRankMax) {
+                rank_cut<kFinNT>(lc, inbin, remaining, chosen + above, &sm.u.m.kstar);
+            } else {
+                // many members (tie floods): sorted, the first `remaining` taken
+                const int np2 = next_pow2(inbin);
+                for (int k = inbin + tid; k < np2; k += kFinNT) lc[k] = 0ull;
+                lds_barrier();
+                bitonic_sort<kFinNT, uint64_t, true>(lc, np2);
+                for (int k = tid; k < remaining; k += kFinNT)
+                    chosen[above + k] = static_cast<int32_t>(~static_cast<uint32_t>(lc[k]));
+                if (tid == 0) sm.u.m.kstar = static_cast<uint32_t>(lc[remaining - 1] >> 32);
+            }
+            lds_barrier();
+            // every key >= max T is listed: the cut is exact if the cut key reaches max T
+            exact = sm.u.m.kstar >= max_t;
+        }
+    }
+    if (!exact) {
         select_row<kFinNT>(scores + b * ss + t * sld, o, keep, budget, out, sm.u.s);
     } else {
-        int32_t* chosen = sm.u.m.chosen;
-        const bool bitmap = o <= 32 * kBitmapWords;             // every chosen j < o has a bit; o goes last
-        if (bitmap)
-            for (int k = tid; k < kBitmapWords; k += kFinNT) sm.u.m.bm[k] = 0u;
-#pragma unroll
-        for (int it = 0; it < QSA_MAX_BUDGET / kFinNT; ++it)
-            if (tid + kFinNT * it < above) chosen[tid + kFinNT * it] = dv[it];
-        if (tid == 0) chosen[keep] = o;
-        // candidates of the threshold bin share the top 12 key bits: a second
-        // radix level on the next 12 bits (LDS histogram) splits them into
-        // those surely taken, the few in the sub-bin holding the cut, and the rest
-        uint64_t* lc = sm.u.m.cand;
-        uint32_t* h2 = sm.u.m.h2;
-        for (int k = tid; k < kDecHistBins; k += kFinNT) h2[k] = 0u;
-#pragma unroll
-        for (int it = 0; it < kDecCap / kFinNT; ++it)
-            if (tid + kFinNT * it < inbin) lc[tid + kFinNT * it] = cv[it];
-        if (tid == 0) sm.u.m.n_taken = 0;
-        lds_barrier();
-        for (int k = tid; k < inbin; k += kFinNT)
-            atomicAdd(&h2[static_cast<uint32_t>(lc[k] >> 40) & (kDecHistBins - 1)], 1u);
-        lds_barrier();
-        find_threshold_bin<kFinNT>(h2, kDecHistBins, remaining, sm.u.m.wave_tot, &sm.u.m.sh_bin, &sm.u.m.sh_above);
-        const uint32_t t2 = sm.u.m.sh_bin;
-        const int above2 = sm.u.m.sh_above;                   // taken outright
-        const int need2 = remaining - above2;                 // still to take from sub-bin t2
-        // members of the cut sub-bin go to a short list; the rest are decided here
-        uint64_t* sub = sm.u.m.sub;
-        if (tid == 0) sm.u.m.n_sub = 0;
-        lds_barrier();
-        for (int i = tid; i < inbin; i += kFinNT) {
-            const uint64_t x = lc[i];
-            const uint32_t d2 = static_cast<uint32_t>(x >> 40) & (kDecHistBins - 1);
-            if (d2 > t2)
-                chosen[above + atomicAdd(&sm.u.m.n_taken, 1)] = static_cast<int32_t>(~static_cast<uint32_t>(x));
-            else if (d2 == t2)
-                sub[atomicAdd(&sm.u.m.n_sub, 1)] = x;
-        }
-        lds_barrier();
-        const int n_sub = sm.u.m.n_sub;
-        int32_t* dst = chosen + above + above2;
-        if (n_sub <= 256) {
-            // rank among the few members of the sub-bin: full key, then index
-            for (int i = tid; i < n_sub; i += kFinNT) {
-                const uint64_t x = sub[i];
-                int r = 0;
-#pragma unroll 8
-                for (int k = 0; k < n_sub; ++k) r += sub[k] > x ? 1 : 0;
-                if (r < need2) dst[r] = static_cast<int32_t>(~static_cast<uint32_t>(x));
-            }
-        } else {
-            const int np2 = next_pow2(n_sub);
-            for (int k = n_sub + tid; k < np2; k += kFinNT) sub[k] = 0ull;
+        if (o <= 32 * kBitmapWords) {
+            // ascending through a bitmap of the candidate blocks: every chosen
+            // j < o sets its bit; thread t owns words kWpt t .. kWpt t + kWpt - 1
+            uint32_t* bm = sm.u.m.bm;
+            for (int k = tid; k < kBitmapWords; k += kFinNT) bm[k] = 0u;
             lds_barrier();
-            bitonic_sort<kFinNT, uint64_t, true>(sub, np2);
-            for (int k = tid; k < need2; k += kFinNT) dst[k] = static_cast<int32_t>(~static_cast<uint32_t>(sub[k]));
-        }
-        lds_barrier();
-        if (bitmap) {
             for (int k = tid; k < keep; k += kFinNT) {
                 const int v = chosen[k];
-                atomicOr(&sm.u.m.bm[v >> 5], 1u << (v & 31));
+                atomicOr(&bm[v >> 5], 1u << (v & 31));
             }
             if (tid == 0) out[keep] = o;                     // above every candidate
             lds_barrier();
-            // thread t owns words 8t .. 8t+7: prefix count of set bits, then emit in order
             constexpr int kWpt = kBitmapWords / kFinNT;
             uint32_t w[kWpt];
             int cnt = 0;
 #pragma unroll
             for (int q = 0; q < kWpt; ++q) {
-                w[q] = sm.u.m.bm[kWpt * tid + q];
+                w[q] = bm[kWpt * tid + q];
                 cnt += __popc(w[q]);
             }
             int total;
@@ -464,21 +572,19 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
                 }
             }
         } else {
+            if (tid == 0) chosen[keep] = o;              // above every candidate
             rank_write_ascending<kFinNT>(chosen, keep + 1, out);
         }
         for (int k = keep + 1 + tid; k < budget; k += kFinNT) out[k] = -1;
     }
-    lds_barrier();
-    uint32_t* gh = ws.hist + static_cast<int64_t>(r) * kDecHistBins;
-    for (int k = tid; k < kDecHistBins; k += kFinNT) gh[k] = 0u;
     if (tid < kCtrl) ctrl[tid] = 0u;
 }
 
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
                                       int64_t kbs, const Positions& pos, int batch, int tq, int budget,
                                       float* scores, int64_t ss, int64_t sld, int32_t* sel, int64_t sels,
-                                      void* ws, const DecodeAppend* append, const PageMap* pm,
-                                      hipStream_t stream) {
+                                      void* ws, const DecodeAppend* append, const DecodeQrot* qrot,
+                                      const PageMap* pm, hipStream_t stream) {
     const int rows = batch * tq;
     int o_max = 0;
     for (int b = 0; b < batch; ++b) o_max = max(o_max, (pos.p[b] + tq - 1) / kBlock);
@@ -487,11 +593,10 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
     const int64_t groups = static_cast<int64_t>(batch) * ((o_max + 255) / 256);
     const int steps = groups >= 8 * 512 ? 8 : groups >= 4 * 512 ? 4 : groups >= 2 * 512 ? 2 : 1;
     const int wg_scan = max(1, (o_max + 256 * steps - 1) / (256 * steps));
-    // filter: kFiltPer scores per workgroup
-    const int wg_filt = max(1, (o_max + kFiltPer - 1) / kFiltPer);
 
-    const DecodeWs w = carve(ws, rows);
+    const DecodeWs w = carve(ws);
     AppendArgs ap{};
+    qsa_rope_t rope{1.0e7, 1.0, 0};
     if (append != nullptr) {
         ap.k_new = append->k_new;
         ap.kns = append->kns;
@@ -506,11 +611,20 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
         ap.kis = append->kis;
         ap.kbar = append->kbar;
         ap.kbs = append->kbs;
-        ap.inv = make_inv_freq(append->rope);
+        rope = append->rope;
     }
+    QrotArgs qr{};
+    if (qrot != nullptr) {
+        qr.q = qrot->q;
+        qr.qs = qrot->qs;
+        qr.q_rot = qrot->q_rot;
+        rope = qrot->rope;
+    }
+    ap.inv = make_inv_freq(rope);
     hipError_t e;
-    // one token per sequence: the rows are appended by the scan; several: first,
-    // because a block an earlier new token completes is scored for the later ones
+    // one token per sequence: the rows are appended by the scan's side
+    // workgroups; several: first, because a block an earlier new token
+    // completes is scored for the later ones
     int scan_appends = append != nullptr ? 1 : 0;
     const PageMap pmv = pm != nullptr ? *pm : PageMap{};
     if (append != nullptr && tq > 1) {
@@ -523,11 +637,12 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
         if ((e = hipGetLastError()) != hipSuccess) return e;
         scan_appends = 0;
     }
-    const dim3 grid(static_cast<unsigned>(batch * wg_scan));
-    const size_t lds = static_cast<size_t>(tq) * kDecHistBins * 4;
+    const int n_side = (scan_appends || qr.q != nullptr) ? batch : 0;
+    const dim3 grid(static_cast<unsigned>(n_side + batch * wg_scan));
+    const size_t lds = static_cast<size_t>(tq) * 256 * steps * 4;
 #define QSA_SCAN(S, P)                                                                                       \
     hipLaunchKernelGGL((decode_scan_kernel<S, P>), grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, \
-                       budget, tq, wg_scan, scores, ss, sld, w, ap, scan_appends, pmv)
+                       budget, tq, n_side, wg_scan, scores, ss, sld, w, ap, scan_appends, qr, pmv)
     if (pm != nullptr) {
         switch (steps) {
             case 8: QSA_SCAN(8, true); break;
@@ -544,9 +659,6 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
         }
     }
 #undef QSA_SCAN
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_filter_kernel, dim3(static_cast<unsigned>(rows * wg_filt)), dim3(256), 0,
-                       stream, scores, ss, sld, pos, budget, tq, wg_filt, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(decode_finalize_kernel, dim3(static_cast<unsigned>(rows)), dim3(kFinNT), 0, stream,
                        scores, ss, sld, pos, budget, tq, w, sel, sels);

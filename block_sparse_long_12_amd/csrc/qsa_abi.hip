@@ -7,6 +7,7 @@
 
 #include "qsa_internal.h"
 
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -504,13 +505,25 @@ qsa_status_t qsa_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_st
     CHECK(aligned16(workspace), "workspace must be 16-byte aligned");
     return hip_result(qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq,
                                                       budget, scores, scores_seq_stride, scores_ld, sel,
-                                                      sel_seq_stride, workspace, nullptr, nullptr, stream),
+                                                      sel_seq_stride, workspace, nullptr, nullptr, nullptr, stream),
                       "index_select_decode launch");
+}
+
+// decode step workspace: index-select part | attention partials | rotated
+// queries.  The partials region holds max(256, rows) (row, split) slots, an
+// upper bound for every budget (a row is split at most 256 / rows ways), so
+// the total grows with the row count and a workspace sized for the largest
+// call serves every smaller one.
+static size_t step_attn_offset(int32_t rows) { return align256(qsa::decode_select_ws_bytes(rows)); }
+static size_t step_qrot_offset(int32_t rows) {
+    const size_t slots = rows > 256 ? static_cast<size_t>(rows) : size_t{256};
+    return step_attn_offset(rows) + align256(slots * qsa::kHq * (2 + qsa::kD) * sizeof(float));
 }
 
 size_t qsa_decode_step_workspace_bytes(int32_t batch, int32_t tq, int32_t budget) {
     if (batch < 1 || batch > QSA_MAX_BATCH || !tq_ok(tq) || budget < 1 || budget > QSA_MAX_BUDGET) return 0;
-    return align256(qsa::decode_select_ws_bytes(batch * tq)) + qsa::decode_workspace_bytes(batch * tq, budget);
+    const int32_t rows = batch * tq;
+    return step_qrot_offset(rows) + static_cast<size_t>(rows) * qsa::kHq * qsa::kD * 2;
 }
 
 // caches contiguous (per-sequence strides), or (cache non-NULL) the paged
@@ -528,7 +541,8 @@ static qsa_status_t decode_step_impl(const uint16_t* q, int64_t q_seq_stride,
                                      int32_t* sel, int64_t sel_seq_stride,
                                      uint16_t* out, int64_t out_seq_stride, float* lse,
                                      const uint16_t* gate, int64_t gate_seq_stride,
-                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                     bool validate_only = false) {
     TRY(check_batch(batch));
     CHECK(tq_ok(tq), "tq = %d outside [1, %d]", tq, qsa::kMaxDecodeTq);
     qsa::Positions p;
@@ -565,12 +579,14 @@ static qsa_status_t decode_step_impl(const uint16_t* q, int64_t q_seq_stride,
         CHECK(paged || k_idx == nullptr || kbar_seq_stride >= (max_len / qsa::kBlock) * qsa::kDi,
               "kbar_seq_stride smaller than the blocks the new tokens complete");
     }
-    const size_t sel_ws = align256(qsa::decode_select_ws_bytes(batch * tq));
-    const size_t need = sel_ws + qsa::decode_workspace_bytes(batch * tq, budget);
+    if (validate_only) return QSA_OK;
+    const size_t need = qsa_decode_step_workspace_bytes(batch, tq, budget);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(QSA_ERR_WORKSPACE, "decode step workspace needs %zu bytes, got %zu", need,
                     workspace == nullptr ? size_t{0} : workspace_bytes);
     CHECK(aligned16(workspace), "workspace must be 16-byte aligned");
+    char* wsb = static_cast<char*>(workspace);
+    uint16_t* q_rot = reinterpret_cast<uint16_t*>(wsb + step_qrot_offset(batch * tq));
     qsa::DecodeAppend ap{};
     ap.k_new = k_new;
     ap.kns = kv_new_seq_stride;
@@ -586,15 +602,16 @@ static qsa_status_t decode_step_impl(const uint16_t* q, int64_t q_seq_stride,
     ap.kbar = kbar;
     ap.kbs = kbar_seq_stride;
     ap.rope = rp;
+    const qsa::DecodeQrot qr{q, q_seq_stride, q_rot, rp};
     hipError_t e = qsa::launch_decode_index_select(q_idx, q_idx_seq_stride, kbar, kbar_seq_stride, p, batch, tq,
                                                    budget, scores, scores_seq_stride, scores_ld, sel, sel_seq_stride,
-                                                   workspace, &ap, paged ? &pm : nullptr, stream);
+                                                   workspace, &ap, &qr, paged ? &pm : nullptr, stream);
     if (e != hipSuccess) return hip_result(e, "decode_step index-select launch");
-    return hip_result(qsa::launch_attn_decode_ex(q, q_seq_stride, k_cache, v_cache, kv_seq_stride, sel,
-                                                 sel_seq_stride, p, batch, tq, budget, softmax_scale, out,
-                                                 out_seq_stride, lse, gate, gate_seq_stride,
-                                                 static_cast<char*>(workspace) + sel_ws, &rp,
-                                                 paged ? &pm : nullptr, stream),
+    return hip_result(qsa::launch_attn_decode_ex(q_rot, int64_t{tq} * qsa::kHq * qsa::kD, k_cache, v_cache,
+                                                 kv_seq_stride, sel, sel_seq_stride, p, batch, tq, budget,
+                                                 softmax_scale, out, out_seq_stride, lse, gate, gate_seq_stride,
+                                                 wsb + step_attn_offset(batch * tq), nullptr, paged ? &pm : nullptr,
+                                                 stream),
                       "decode_step attention launch");
 }
 

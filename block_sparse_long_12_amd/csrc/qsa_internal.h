@@ -179,7 +179,9 @@ hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* 
                                  void* ws, const qsa_rope_t* rope, const PageMap* pm, hipStream_t stream);
 
 // fused decode index-select (scores + selection of the decode rows); the
-// workspace must be zero before its first use and is left zero by each call
+// workspace starts with control words laid out for the largest row count,
+// which must be zero before the first use and are left zero by each call
+// (so one workspace serves calls of any shape)
 size_t decode_select_ws_bytes(int rows);
 // Rows a decode step appends at each sequence's new positions p0 .. p0+tq-1
 // before it scores (every pointer may be null: then that part is not done).
@@ -200,11 +202,21 @@ struct DecodeAppend {
     qsa_rope_t rope;             // rotary parameters of the K rows
 };
 
+// Queries of a decode step rotated once for its attention, by side
+// workgroups of the scan: q [B][tq][24][256] (sequence stride qs) rotated
+// into q_rot [B * tq][24][256] with `rope`, as qsa_rope_apply would.
+struct DecodeQrot {
+    const uint16_t* q;
+    int64_t qs;
+    uint16_t* q_rot;
+    qsa_rope_t rope;
+};
+
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
                                       int64_t kbs, const Positions& pos, int batch, int tq, int budget,
                                       float* scores, int64_t ss, int64_t sld, int32_t* sel, int64_t sels,
-                                      void* ws, const DecodeAppend* append, const PageMap* pm,
-                                      hipStream_t stream);
+                                      void* ws, const DecodeAppend* append, const DecodeQrot* qrot,
+                                      const PageMap* pm, hipStream_t stream);
 // Paged caches: the new tokens [pos0[b], pos0[b] + n_tokens) of every sequence
 // are written into their pages (K rotated, V, indexer keys; null inputs are
 // skipped), then the key of every block they complete (when kbar is given).

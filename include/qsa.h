@@ -245,14 +245,18 @@ qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
 /*
  * Steps 2 + 3 fused for decode rows: writes the same scores as
  * qsa_index_scores (q_pos0 = q_pos, the same tq) and the same selection as
- * qsa_select_topk, bit for bit, in three launches that spread each row over
- * many workgroups (a scan that also histograms the score keys, a threshold
- * filter, a per-row exact finish).  scores [B][tq][scores_ld] float with
- * scores_ld >= (q_pos + tq - 1)/4 rounded up to a multiple of 4 (entries past
- * a row's own block are scratch), 16-byte aligned.  The workspace
- * (qsa_index_select_decode_workspace_bytes) must be zero-filled before its
- * first use; every call leaves it zeroed again.  Calls that share a
- * workspace must not overlap.
+ * qsa_select_topk, bit for bit, in two launches that spread each row over
+ * many workgroups (a scan whose workgroups each list their own top
+ * candidates of every row, then a per-row exact finish over the lists, with
+ * the full radix select of the stored row where a list cannot decide).
+ * scores [B][tq][scores_ld] float with scores_ld >= (q_pos + tq - 1)/4
+ * rounded up to a multiple of 4 (entries past a row's own block are
+ * scratch), 16-byte aligned.  The workspace
+ * (qsa_index_select_decode_workspace_bytes) starts with control words laid
+ * out for the largest row count: it must be zero-filled before its first
+ * use, and every call leaves them zeroed again, so one workspace serves
+ * calls of any shape it is large enough for.  Calls that share a workspace
+ * must not overlap.
  */
 size_t       qsa_index_select_decode_workspace_bytes(int32_t batch, int32_t tq);
 qsa_status_t qsa_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_stride,
@@ -277,16 +281,17 @@ qsa_status_t qsa_index_select_decode(const uint16_t* q_idx, int64_t q_idx_seq_st
  *    a block the last token completes serves the next steps);
  *  - scores the candidate blocks of each row and selects as
  *    qsa_index_select_decode does;
- *  - attends with q (unrotated; rotated on load exactly as qsa_rope_apply
- *    would with the same rope parameters) over each row's selection and own
- *    block.
+ *  - attends with q (unrotated; rotated once, exactly as qsa_rope_apply
+ *    would with the same rope parameters, into the workspace) over each
+ *    row's selection and own block.
  * k_idx NULL: no indexer-key append and no compression.  k_new / v_new share
  * kv_new_seq_stride; k_cache and v_cache share kv_seq_stride; k_idx is
  * [B][L][128] with k_idx_seq_stride.  Equals the chain rope_apply + row
  * copies + compress_block_keys + index_scores + select_topk +
  * sparse_attn_decode bit for bit.  The workspace
  * (qsa_decode_step_workspace_bytes) must be zero-filled before its first use;
- * every call leaves it zeroed again.
+ * every call leaves the control words at its start zeroed again (the rest is
+ * scratch), so it serves calls of any shape it is large enough for.
  */
 size_t       qsa_decode_step_workspace_bytes(int32_t batch, int32_t tq, int32_t budget);
 qsa_status_t qsa_decode_step(const uint16_t* q, int64_t q_seq_stride,

@@ -22,6 +22,10 @@ from tests.gpu_common import say
 
 pytestmark = pytest.mark.gpu
 
+# the decode workspaces start with 16 control words for each of the most rows
+# a call can have (256 sequences x 4 tokens); they must be zero between calls
+CTRL_BYTES = 256 * 4 * 16 * 4
+
 
 def _rand(shape, seed, sigma):
     g = torch.Generator().manual_seed(seed)
@@ -74,10 +78,9 @@ def test_index_select_decode_matches_primitives(kind, pos, budget):
             o = pos[b] // 4
             assert torch.equal(s_f[b, 0, :o].view(torch.int32), s_ref[b, 0, :o].view(torch.int32)), (rep, b)
         assert torch.equal(sel_f, sel_ref), rep
-        # histogram and control words (the head of the workspace) are left zeroed;
-        # the candidate lists after them are scratch
-        head = B * (4096 + 16) * 4
-        assert int(ws[:head].count_nonzero()) == 0, "histogram / control words not left zeroed"
+        # the control words (the head of the workspace) are left zeroed; the
+        # candidate lists after them are scratch
+        assert int(ws[:CTRL_BYTES].count_nonzero()) == 0, "control words not left zeroed"
 
 
 @pytest.mark.parametrize("ctx,budget,B", [(32768, 512, 8), (5001, 64, 3), (99, 512, 2), (131072, 512, 2)])
@@ -310,7 +313,7 @@ def test_multi_token_decode_step_matches_primitives(pos, tq, budget, yarn):
             for _ in range(2):                        # the second call reuses the workspace
                 qsa.decode_step(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel, ws,
                                 v_new=v_new, k_idx_new=k_idx_new, gate=gate, rope=rope)
-            assert int(ws[:B * tq * (4096 + 16) * 4].count_nonzero()) == 0
+            assert int(ws[:CTRL_BYTES].count_nonzero()) == 0
         else:
             qsa.decode_step_primitives(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel,
                                        qsa.decode_workspace(B, budget, tq=tq), torch.empty_like(q_raw),
@@ -358,3 +361,52 @@ def test_multi_token_index_select_decode_matches_primitives(pos, tq, budget):
             o = (pos[b] + t) // 4
             assert torch.equal(s_f[b, t, :o].view(torch.int32), s_ref[b, t, :o].view(torch.int32)), (b, t)
     assert torch.equal(sel_f, sel_ref)
+
+
+def test_decode_step_workspace_reused_across_shapes():
+    """One decode-step workspace (sized for the largest call) serves steps
+    whose row counts grow and shrink (B x tq = 2, 12, 4, 12): every call
+    equals the primitive chain bit for bit and leaves the control words
+    zeroed, so a call with more rows never reads what a smaller one left."""
+    dev, bf, budget = "cuda", torch.bfloat16, 512
+    shapes = [([70001, 4099], 1), ([9000, 70001, 4099, 30000], 3), ([4099, 70001], 2), ([30000, 9000, 4099, 70001], 3)]
+    ws = qsa.decode_step_workspace(4, budget, tq=3)
+    for i, (pos, tq) in enumerate(shapes):
+        say(f"decode_step reuse {i}: pos={pos} tq={tq}")
+        B = len(pos)
+        L = max(pos) + tq
+        g = torch.Generator().manual_seed(100 + i)
+        k_cpu = torch.randn((B, L, 2, 256), generator=g).to(bf)
+        v_cpu = torch.randn((B, L, 2, 256), generator=g).to(bf)
+        ki_cpu = (torch.randn((B, L, 128), generator=g) / math.sqrt(128)).to(bf)
+        q_raw = torch.randn((B, tq, 24, 256), generator=g).to(bf).to(dev)
+        q_idx = (torch.randn((B, tq, 4, 128), generator=g) / math.sqrt(128)).to(bf).to(dev)
+        k_new = torch.randn((B, tq, 2, 256), generator=g).to(bf).to(dev)
+        ld = max(4, ((L - 1) // 4 + 3) // 4 * 4)
+        res = []
+        for fused in (False, True):
+            kc, v, ki = k_cpu.to(dev), v_cpu.to(dev), ki_cpu.to(dev)
+            qsa.rope_apply(kc, [0] * B)
+            kb = torch.zeros((B, L // 4 + 1, 128), dtype=bf, device=dev)
+            for b in range(B):
+                qsa.compress_block_keys(ki[b:b + 1], 0, pos[b] // 4, kb[b:b + 1])
+            scores = torch.full((B, tq, ld), float("nan"), device=dev)
+            sel = torch.empty((B, tq, budget), dtype=torch.int32, device=dev)
+            lead = (B,) if tq == 1 else (B, tq)        # one token: [B, 24, 256] outputs
+            out = torch.empty(lead + (24, 256), dtype=bf, device=dev)
+            lse = torch.empty(lead + (24,), dtype=torch.float32, device=dev)
+            if fused:
+                qsa.decode_step(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel, ws)
+            else:
+                qsa.decode_step_primitives(q_raw, k_new, q_idx, ki, kc, v, kb, pos, budget, out, lse, scores, sel,
+                                           qsa.decode_workspace(B, budget, tq=tq), torch.empty_like(q_raw))
+            torch.cuda.synchronize()
+            res.append((sel.clone(), out.clone(), lse.clone(),
+                        [scores[b, t, :(pos[b] + t) // 4].clone() for b in range(B) for t in range(tq)]))
+        (sa, oa, la, ca), (sb, ob, lb, cb) = res
+        assert torch.equal(sa, sb), i
+        assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)), i
+        assert torch.equal(la, lb), i
+        for x, y in zip(ca, cb):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), i
+        assert int(ws[:CTRL_BYTES].count_nonzero()) == 0, i
