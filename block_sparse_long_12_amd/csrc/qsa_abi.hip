@@ -5,7 +5,15 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "qsa_internal.h"
+
+// Scratch of qsa_decode_step_noalloc: one copy per GPU the library runs on,
+// held until the process ends.  Host code never uses this name as an address
+// (on the host it only stands for the symbol); it takes each device's address
+// from hipGetSymbolAddress, once, with that device current.
+static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES];
 
 
 namespace {
@@ -103,6 +111,50 @@ qsa_status_t take_paged(const qsa_paged_cache_t* c, const qsa::Positions& p, int
         qsa_status_t _s = (expr);          \
         if (_s != QSA_OK) return _s;       \
     } while (0)
+
+// ---- per-device state of the static scratch
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+    void* ptr = nullptr;     // device address of `scratch` on this device
+    bool clean = false;      // zero-filled, and every call since has left its control words zeroed
+};
+
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxDevices];
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
+    for (size_t i = blockIdx.x * size_t{256} + threadIdx.x; i < n16; i += size_t{gridDim.x} * 256)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The current device's scratch; on its first use there (or after a call that
+// failed part-way) the whole array is zero-filled on `stream` by a kernel
+// (no memset node, so the call may sit in a captured graph).
+qsa_status_t scratch_for_current_device(hipStream_t stream, ScratchSlot** slot_out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_result(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(QSA_ERR_UNSUPPORTED, "device %d beyond the %d the static scratch serves", dev, kMaxDevices);
+    ScratchSlot& s = g_scratch[dev];
+    if (s.ptr == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) return hip_result(e, "hipGetSymbolAddress(scratch)");
+        s.ptr = ptr;
+    }
+    if (!s.clean) {
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, stream, static_cast<uint4*>(s.ptr),
+                           size_t{QSA_NOALLOC_SCRATCH_BYTES} / 16);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_result(e, "scratch zero-fill launch");
+        s.clean = true;
+    }
+    *slot_out = &s;
+    return QSA_OK;
+}
 
 }  // namespace
 
@@ -652,6 +704,44 @@ qsa_status_t qsa_decode_step_paged(const uint16_t* q, int64_t q_seq_stride,
                             nullptr, nullptr, 0, nullptr, 0, nullptr, 0, cache, q_pos, batch, tq, budget,
                             softmax_scale, rope, scores, scores_ld, scores_seq_stride, sel, sel_seq_stride, out,
                             out_seq_stride, lse, gate, gate_seq_stride, workspace, workspace_bytes, stream);
+}
+
+qsa_status_t qsa_decode_step_noalloc(const uint16_t* q, int64_t q_seq_stride,
+                                     const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
+                                     const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                     const uint16_t* k_idx_new,
+                                     uint16_t* k_cache, uint16_t* v_cache, int64_t kv_seq_stride,
+                                     uint16_t* k_idx, int64_t k_idx_seq_stride,
+                                     uint16_t* kbar, int64_t kbar_seq_stride,
+                                     const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
+                                     float softmax_scale, const qsa_rope_t* rope,
+                                     float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                     int32_t* sel, int64_t sel_seq_stride,
+                                     uint16_t* out, int64_t out_seq_stride, float* lse,
+                                     const uint16_t* gate, int64_t gate_seq_stride, hipStream_t stream) {
+    const size_t need = qsa_decode_step_workspace_bytes(batch, tq, budget);
+    if (need == 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "batch = %d, tq = %d or budget = %d out of range", batch, tq, budget);
+    if (need > QSA_NOALLOC_SCRATCH_BYTES)
+        return fail(QSA_ERR_WORKSPACE, "decode step needs %zu bytes of scratch; the static buffer holds %zu", need,
+                    size_t{QSA_NOALLOC_SCRATCH_BYTES});
+    // every argument check first (no HIP call): a rejected call leaves the scratch as it was
+    TRY(decode_step_impl(q, q_seq_stride, k_new, v_new, kv_new_seq_stride, q_idx, q_idx_seq_stride, k_idx_new,
+                         k_cache, v_cache, kv_seq_stride, k_idx, k_idx_seq_stride, kbar, kbar_seq_stride, nullptr,
+                         q_pos, batch, tq, budget, softmax_scale, rope, scores, scores_ld, scores_seq_stride, sel,
+                         sel_seq_stride, out, out_seq_stride, lse, gate, gate_seq_stride, nullptr, 0, stream,
+                         /*validate_only=*/true));
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchSlot* slot = nullptr;
+    TRY(scratch_for_current_device(stream, &slot));
+    const qsa_status_t st = decode_step_impl(q, q_seq_stride, k_new, v_new, kv_new_seq_stride, q_idx,
+                                             q_idx_seq_stride, k_idx_new, k_cache, v_cache, kv_seq_stride, k_idx,
+                                             k_idx_seq_stride, kbar, kbar_seq_stride, nullptr, q_pos, batch, tq,
+                                             budget, softmax_scale, rope, scores, scores_ld, scores_seq_stride, sel,
+                                             sel_seq_stride, out, out_seq_stride, lse, gate, gate_seq_stride,
+                                             slot->ptr, QSA_NOALLOC_SCRATCH_BYTES, stream);
+    if (st != QSA_OK) slot->clean = false;       // launched part-way: zero-fill again on the next call
+    return st;
 }
 
 qsa_status_t qsa_paged_append(const qsa_paged_cache_t* cache,

@@ -90,6 +90,9 @@ _SIGNATURES = {
     "qsa_decode_step": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _i64, _c_p, _i64,
                                _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, _rope_p, _c_p, _i64,
                                _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p, _sz, _c_p]),
+    "qsa_decode_step_noalloc": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _i64, _c_p,
+                                       _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, _rope_p, _c_p,
+                                       _i64, _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p]),
     "qsa_paged_append": (_i32, [_paged_p, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _rope_p, _c_p]),
     "qsa_index_select_prefill_paged": (_i32, [_c_p, _i64, _paged_p, _c_p, _i32, _i32, _i32, _c_p, _i64, _i64,
                                               _c_p, _i64, _c_p, _sz, _c_p]),
@@ -497,8 +500,50 @@ def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, bud
     output gate) like out. workspace comes from decode_step_workspace(B,
     budget, tq=tq).
     """
-    B, tq = q_raw.shape[0], q_raw.shape[1]
+    B = q_raw.shape[0]
     p_list = _decode_positions(pos, B)
+    _decode_step_check(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, p_list, budget, out, lse, scores,
+                       sel, v_new, k_idx_new)
+    args = _decode_step_args(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, p_list, budget, out, lse,
+                             scores, sel, scale, v_new, k_idx_new, gate, rope)
+    _check(lib().qsa_decode_step(*args, _ptr(workspace), workspace.numel(), _stream(stream)), "qsa_decode_step")
+    return out
+
+
+def _decode_step_args(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, p_list, budget, out, lse, scores,
+                      sel, scale, v_new, k_idx_new, gate, rope):
+    """The C arguments of qsa_decode_step up to (not including) the workspace."""
+    B, tq = q_raw.shape[0], q_raw.shape[1]
+    p = _positions(p_list, B)
+    g_ptr, g_stride = _gate_args(gate, out)
+    return (_ptr(q_raw), q_raw.stride(0), _ptr(k_new_raw), _ptr(v_new), k_new_raw.stride(0),
+            _ptr(q_idx), q_idx.stride(0), _ptr(k_idx_new), _ptr(k_cache), _ptr(v_cache),
+            k_cache.stride(0), _ptr(k_idx), 0 if k_idx is None else k_idx.stride(0),
+            _ptr(kbar), kbar.stride(0), p, B, tq, budget, float(scale), _rope_arg(rope),
+            _ptr(scores), scores.shape[-1], scores.stride(0), _ptr(sel), sel.stride(0),
+            _ptr(out), out.stride(0), _ptr(lse), g_ptr, g_stride)
+
+
+def decode_step_noalloc(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,
+                        out, lse, scores, sel, stream=None, scale: float = 1.0 / math.sqrt(D),
+                        v_new=None, k_idx_new=None, gate=None, rope: Rope | None = None):
+    """decode_step without a workspace (qsa_decode_step_noalloc): the library's
+    static per-GPU scratch serves instead, so the call allocates nothing.  Calls
+    that overlap on one GPU race; shapes beyond the scratch raise QSAError."""
+    B = q_raw.shape[0]
+    p_list = _decode_positions(pos, B)
+    _decode_step_check(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, p_list, budget, out, lse, scores,
+                       sel, v_new, k_idx_new)
+    args = _decode_step_args(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, p_list, budget, out, lse,
+                             scores, sel, scale, v_new, k_idx_new, gate, rope)
+    _check(lib().qsa_decode_step_noalloc(*args, _stream(stream)), "qsa_decode_step_noalloc")
+    return out
+
+
+def _decode_step_check(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, p_list, budget, out, lse, scores,
+                       sel, v_new, k_idx_new):
+    """Tensor checks of decode_step and decode_step_noalloc."""
+    B, tq = q_raw.shape[0], q_raw.shape[1]
     _need(q_raw, "q", torch.bfloat16, (HQ, D))
     _need(k_new_raw, "k_new", torch.bfloat16, (HKV, D))
     _need(q_idx, "q_idx", torch.bfloat16, (HI, DI))
@@ -536,17 +581,6 @@ def decode_step(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, bud
         raise QSAError("scores do not cover the candidate blocks")
     if kbar.shape[1] < max((x + tq) // BLOCK if k_idx is not None else (x + tq - 1) // BLOCK for x in p_list):
         raise QSAError("kbar does not cover the candidate (and completed) blocks")
-    p = _positions(p_list, B)
-    g_ptr, g_stride = _gate_args(gate, out)
-    _check(lib().qsa_decode_step(_ptr(q_raw), q_raw.stride(0), _ptr(k_new_raw), _ptr(v_new), k_new_raw.stride(0),
-                                 _ptr(q_idx), q_idx.stride(0), _ptr(k_idx_new), _ptr(k_cache), _ptr(v_cache),
-                                 k_cache.stride(0), _ptr(k_idx), 0 if k_idx is None else k_idx.stride(0),
-                                 _ptr(kbar), kbar.stride(0), p, B, tq, budget, float(scale), _rope_arg(rope),
-                                 _ptr(scores), scores.shape[-1], scores.stride(0), _ptr(sel), sel.stride(0),
-                                 _ptr(out), out.stride(0), _ptr(lse), g_ptr, g_stride, _ptr(workspace),
-                                 workspace.numel(), _stream(stream)),
-           "qsa_decode_step")
-    return out
 
 
 def decode_step_primitives(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,

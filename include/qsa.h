@@ -374,6 +374,36 @@ qsa_status_t qsa_sparse_attn_prefill_paged(const uint16_t* q, int64_t q_seq_stri
                                            int64_t lse_seq_stride, const uint16_t* gate, int64_t gate_seq_stride,
                                            hipStream_t stream);
 
+/*
+ * qsa_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as qsa_decode_step (bit for bit), without the
+ * workspace: its kernels use a static device buffer of
+ * QSA_NOALLOC_SCRATCH_BYTES per GPU instead, which the library holds from the
+ * first call on that GPU until the process ends (on that first call the
+ * buffer is zero-filled by a kernel on `stream`; no memset).  The call makes
+ * no hipMalloc/hipFree and no allocating library call.  Shapes whose
+ * qsa_decode_step_workspace_bytes exceeds the buffer (about 158 rows of
+ * batch x tq) are rejected with QSA_ERR_WORKSPACE before anything runs.  All
+ * calls on one GPU share its buffer, which keeps the last call's contents:
+ * calls that overlap on one GPU (other streams or threads) race and must be
+ * serialised by the caller.
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+qsa_status_t qsa_decode_step_noalloc(const uint16_t* q, int64_t q_seq_stride,
+                                     const uint16_t* k_new, const uint16_t* v_new, int64_t kv_new_seq_stride,
+                                     const uint16_t* q_idx, int64_t q_idx_seq_stride,
+                                     const uint16_t* k_idx_new,
+                                     uint16_t* k_cache, uint16_t* v_cache, int64_t kv_seq_stride,
+                                     uint16_t* k_idx, int64_t k_idx_seq_stride,
+                                     uint16_t* kbar, int64_t kbar_seq_stride,
+                                     const int32_t* q_pos, int32_t batch, int32_t tq, int32_t budget,
+                                     float softmax_scale, const qsa_rope_t* rope,
+                                     float* scores, int64_t scores_ld, int64_t scores_seq_stride,
+                                     int32_t* sel, int64_t sel_seq_stride,
+                                     uint16_t* out, int64_t out_seq_stride, float* lse,
+                                     const uint16_t* gate, int64_t gate_seq_stride, hipStream_t stream);
+
 /* qsa_decode_step on a paged cache: the new rows go to their pages, the block
  * keys and the K / V rows are read through the block table
  * (workspace: qsa_decode_step_workspace_bytes).  cache->k_idx may be NULL

@@ -205,6 +205,21 @@ def test_decode_step_validation(L):
     assert "k_idx_seq_stride" in L.qsa_last_error().decode()
     assert call(ws=ws_need - 1) == WORKSPACE
     assert call(tq=5) == INVALID and "tq" in L.qsa_last_error().decode()
+
+    # the allocation-free variant: the same checks, and shapes beyond its static
+    # scratch rejected before any HIP call
+    def call_na(k_idx=FAKE, tq=1, batch=B, pos=p):
+        return L.qsa_decode_step_noalloc(FAKE, tq * 24 * 256, FAKE, FAKE, tq * 2 * 256, FAKE, tq * 4 * 128, FAKE,
+                                         FAKE, FAKE, 9004 * 512, k_idx, 9001 * 128, FAKE, 2252 * 128,
+                                         pos, batch, tq, budget, 0.0625, None, FAKE, ld, tq * ld, FAKE,
+                                         tq * budget, FAKE, tq * 24 * 256, NULL, NULL, 0, None)
+
+    assert call_na(k_idx=NULL) == INVALID and "k_idx" in L.qsa_last_error().decode()
+    assert call_na(tq=5) == INVALID
+    assert call_na(batch=0) == INVALID
+    big = _pos(*([4099] * 64))
+    assert L.qsa_decode_step_workspace_bytes(64, 4, budget) > 16 << 20
+    assert call_na(batch=64, tq=4, pos=big) == WORKSPACE and "static" in L.qsa_last_error().decode()
     assert call(tq=4, k_idx_stride=9001 * 128) == INVALID          # rows 9001 .. 9003 out of reach
     assert call(rope=_rope(1e7, 0.9, 262144)) == INVALID and "yarn" in L.qsa_last_error().decode()
     assert call(rope=_rope(1.0)) == INVALID
