@@ -59,7 +59,10 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-tq", type=int, default=4,
                     help="also time a decode step of this many new tokens per sequence (1 = skip)")
-    ap.add_argument("--cpu-rows", type=int, default=48, help="oracle rows timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle rows timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations (2048-token prefill, 32K decode of 32 sequences, "
+                         "131072-token prefill)")
     ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet measurements")
     ap.add_argument("--serial", action="store_true",
                     help="prefill on one stream (index-select, then attention, per query chunk)")
@@ -69,8 +72,37 @@ def parse():
     ap.add_argument("--rope", choices=("yarn", "plain"), default="yarn",
                     help="rotary table: the model card's static YaRN (factor 4 over 262144, for contexts past "
                          "262144) or plain rotary")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill measurements (for counter runs of the decode kernels)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run the calibration kernels of known traffic for the HBM byte counters: a 1 GiB "
+                         "device copy and a gather of 2^21 random 512-byte rows from a 2 GiB buffer")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
+
+
+def calibrate(torch):
+    """Kernels of known traffic for scaling the FETCH_SIZE / WRITE_SIZE
+    counters: a 1 GiB copy (reads and writes 2^30 bytes) and a gather of
+    2^21 distinct random rows of 512 bytes out of a 2 GiB bf16 buffer (reads
+    2^30 bytes of rows plus 2^24 bytes of int64 indices, writes 2^30 bytes;
+    the shape of the attention's K/V row gathers)."""
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    buf = torch.ones((1 << 22, 256), dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(3)
+    idx = torch.randperm(1 << 22, generator=g, device="cuda")[: 1 << 21].contiguous()
+    out = torch.empty((1 << 21, 256), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+        torch.index_select(buf, 0, idx, out=out)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": {
+        "copy": {"read_bytes": 1 << 30, "write_bytes": 1 << 30, "kernel": "__amd_rocclr_copyBuffer"},
+        "gather": {"read_bytes": (1 << 30) + (1 << 24), "write_bytes": 1 << 30,
+                   "rows": 1 << 21, "row_bytes": 512, "source_bytes": 1 << 31,
+                   "kernel": "torch index_select (index_elementwise_kernel)"}}}))
 
 
 def log(args, *a):
@@ -404,7 +436,44 @@ def measured_traffic(kernel: str, src: str):
 
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(wl, x, n_rows: int, args):
+def cpu_info():
+    """The host the oracle runs on: logical CPUs, those this process may use,
+    and the CPU model."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count(), "usable": usable, "model": model}
+
+
+_ORACLE = {}
+
+
+def _oracle_rows(rows):
+    """Worker of the oracle pool: the layer (inherited at fork) on some rows,
+    one BLAS thread; returns the seconds it took."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        _ORACLE["layer"].rows(rows)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(wl, x, n_rows: int, args, workers: int):
+    """The oracle (oracle/qsa_oracle.py, numpy float64, as it stands) on a
+    seeded sample of rows of a workload: block keys of the whole context once,
+    then the rows on one core and on a pool of `workers` processes (one BLAS
+    thread each), each extrapolated to the whole workload."""
+    import multiprocessing as mp
+
     from threadpoolctl import threadpool_limits
 
     from block_sparse_long_12_amd import inputs as I
@@ -418,22 +487,41 @@ def cpu_baseline(wl, x, n_rows: int, args):
         for b in sorted({r[0] for r in rows}):
             layer.kbar_bits(b)
         t_setup = time.perf_counter() - t0
+    _ORACLE["layer"] = layer
+    n1 = max(1, len(rows) // 8)
+    t_one = _oracle_rows(rows[:n1]) / n1                  # seconds per row on one core
+    parts = [rows[i::workers] for i in range(workers)]
+    with mp.get_context("fork").Pool(workers) as pool:
         t0 = time.perf_counter()
-        layer.rows(rows)
-        t_rows = time.perf_counter() - t0
-    per_row = t_rows / len(rows)
+        pool.map(_oracle_rows, parts)
+        t_pool = (time.perf_counter() - t0) / len(rows)   # wall seconds per row on the pool
+    _ORACLE.clear()
     total_rows = wl.batch * wl.tq
-    full = t_setup + per_row * total_rows
-    log(args, f"cpu oracle: {len(rows)} rows in {t_rows:.2f}s (+{t_setup:.2f}s block keys)")
+    prefill = wl.kind == "prefill"
+    # a prefill step compresses its chunk's blocks; a decode step finds the
+    # block keys cached (as the GPU step does), so its time is the rows' alone
+    setup = t_setup if prefill else 0.0
+    full_pool = setup + t_pool * total_rows
+    full_one = setup + t_one * total_rows
+    log(args, f"cpu oracle {wl.name}: {len(rows)} rows, {t_one * 1e3:.1f} ms/row on one core, "
+              f"{t_pool * 1e3:.2f} ms/row on {workers} processes (+{t_setup:.2f}s block keys)")
     return {
-        "value": total_rows / full if wl.kind == "prefill" else full * 1e6,
-        "unit": "tokens/s" if wl.kind == "prefill" else "us/step",
-        "cores": 1,
+        "value": total_rows / full_pool if prefill else full_pool * 1e6,
+        "unit": "tokens/s" if prefill else "us/step",
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{len(rows)} seeded query rows of {wl.name} (block keys of the whole context compressed "
-                  f"once, {t_setup:.2f}s); per-row time {per_row * 1e3:.1f} ms extrapolated to "
-                  f"{total_rows} rows; numpy float64, 1 BLAS thread",
+        "single_core": total_rows / full_one if prefill else full_one * 1e6,
+        "host": cpu_info(),
+        "sample": f"{len(rows)} seeded query rows of {wl.name} on {workers} processes ({n1} of them also on one "
+                  f"core), numpy float64, one BLAS thread per process; block keys of the whole context "
+                  f"compressed once ({t_setup:.2f}s{'' if prefill else ', not counted: cached in a decode step'}); "
+                  f"extrapolated to the {total_rows} rows of a step",
     }
+
+
+def oracle_workers():
+    """Processes for the oracle pool: the CPUs this process may use, at most 16."""
+    return max(1, min(16, cpu_info()["usable"]))
 
 
 # ------------------------------------------------------------------ main
@@ -534,6 +622,200 @@ def gdn_measure(args, torch, qsa, I):
     return res
 
 
+def time_steps(torch, fn, n, flush=None):
+    """Event times (ms) of n calls of fn on the current stream, sorted; with
+    flush, a read of that buffer before each call evicts the caches."""
+    ts = []
+    for _ in range(n):
+        if flush is not None:
+            flush.sum()
+        s_ev = torch.cuda.Event(enable_timing=True)
+        e_ev = torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        fn()
+        e_ev.record()
+        torch.cuda.synchronize()
+        ts.append(s_ev.elapsed_time(e_ev))
+    ts.sort()
+    return ts
+
+
+def measure_prefill(args, torch, qsa, wl, x, rope, steps, warmup, paged=False):
+    """Times `steps` whole prefill steps of a workload (after `warmup`):
+    rotary, compress, then per query chunk the fused index-select and the
+    attention (two streams unless --serial).  Returns the record and the
+    Prefill object."""
+    pf = Prefill(wl, x, torch, qsa, rope)
+    pf.overlap = not args.serial
+    for _ in range(warmup):
+        pf.step(NullTimer())
+    torch.cuda.synchronize()
+    timer = EventTimer(torch)
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        pf.step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    kern = timer.totals()
+    ms_per_step = wall * 1e3 / steps
+    tokens = wl.batch * wl.tq
+    geo = prefill_geometry(wl, 0, wl.tq)
+    n_chunks = math.ceil(wl.tq / (wl.chunk or wl.tq))
+    attn_ms, attn_n = kern["sparse_attn_prefill"]
+    attn_avg_s = attn_ms / attn_n / 1e3
+    attn_bytes_per_launch = geo["attn_bytes"] / n_chunks
+    idx_ms, idx_n = kern["index_select"]
+    rec = {
+        "ms_per_step": ms_per_step,
+        "tokens_per_s": tokens / (ms_per_step / 1e3),
+        "attention": {"kernel": "sparse_attn_prefill", "ms_per_launch": attn_avg_s * 1e3,
+                      "algorithmic_bytes_per_launch": attn_bytes_per_launch,
+                      "gather_GBs": attn_bytes_per_launch / attn_avg_s / 1e9,
+                      "hbm_frac": attn_bytes_per_launch / attn_avg_s / HBM_PEAK},
+        "mfma": {
+            "index_select_frac": (geo["index_flops"] / n_chunks) / (idx_ms / idx_n / 1e3) / BF16_PEAK,
+            "layer_frac": (geo["index_flops"] + geo["attn_flops"]) / (ms_per_step / 1e3) / BF16_PEAK,
+            "note": "folded indexer minimum (2*128 flop per query-candidate pair) plus attention flops, "
+                    "over event time, against 2.5 PFLOP/s",
+        },
+        "kernels_ms_per_step": {k: t / steps for k, (t, n) in kern.items()},
+        "launches_per_step": {k: n // steps for k, (t, n) in kern.items()},
+        "gpu_ms_per_step": sum(t for t, _ in kern.values()) / steps,
+        "gather_bytes_per_step": geo["gathered_tokens"] * 2 * 2 * 256 * 2,
+    }
+    log(args, f"prefill {wl.name}: {ms_per_step:.1f} ms/step, {rec['tokens_per_s']:.0f} tok/s; "
+              f"kernels {rec['kernels_ms_per_step']}")
+    if paged and args.page_tokens > 0:
+        pp = PagedPrefill(pf, args.page_tokens)
+        for _ in range(warmup):
+            pp.step(NullTimer())
+        torch.cuda.synchronize()
+        ptimer = EventTimer(torch)
+        t_start = time.perf_counter()
+        for _ in range(steps):
+            pp.step(ptimer)
+        torch.cuda.synchronize()
+        p_ms = (time.perf_counter() - t_start) * 1e3 / steps
+        pk = ptimer.totals()
+        pa_ms, pa_n = pk["sparse_attn_prefill"]
+        rec["paged"] = {
+            "page_tokens": args.page_tokens,
+            "pages": "random page order, the cached prefix copied in before timing",
+            "ms_per_step": p_ms,
+            "tokens_per_s": tokens / (p_ms / 1e3),
+            "kernels_ms_per_step": {k: t / steps for k, (t, n) in pk.items()},
+            "sparse_attn_prefill_hbm_frac": attn_bytes_per_launch / (pa_ms / pa_n / 1e3) / HBM_PEAK,
+            "note": "paged_append also copies the chunk's V and indexer-key rows into their pages",
+        }
+        log(args, f"prefill {wl.name}, paged: {p_ms:.1f} ms/step; kernels {rec['paged']['kernels_ms_per_step']}")
+        del pp
+    return rec, pf
+
+
+def decode_bytes(wl, tq=1):
+    """Algorithmic bytes of one decode step: the candidate block keys, the
+    K/V rows of the selected blocks (both KV heads), q read and out written,
+    the selection written."""
+    o = wl.ctx // 4
+    kbar = wl.batch * (o * 128 * 2 + 4 * 128 * 2)
+    gather = wl.batch * sum(attended_tokens(wl.ctx + t, wl.budget) for t in range(tq)) * 2 * 2 * 256 * 2
+    return kbar, kbar + gather + wl.batch * tq * (24 * 256 * 2 * 2 + wl.budget * 4)
+
+
+def measure_decode(args, torch, qsa, I, dwl, rope, extras=True):
+    """The serving decode step of a workload (one qsa_decode_step call per
+    step, caches evicted between steps by reading 1 GiB), its fused
+    index-select alone, and (extras) the 4-token step and the paged step."""
+    t0 = time.time()
+    dx = I.make_inputs(dwl)
+    log(args, f"inputs {dwl.name}: {time.time() - t0:.1f}s")
+    dd = Decode(dwl, dx, torch, qsa, rope)
+    del dx
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        dd.step(NullTimer())
+    torch.cuda.synchronize()
+    steps_ms = time_steps(torch, lambda: dd.step(NullTimer()), args.decode_steps, flush)
+    med = steps_ms[len(steps_ms) // 2]
+    # the dominant kernels alone: the fused index-select (block-key scan and
+    # the selection), same launch configuration as inside the step
+    sel_ws = qsa.index_select_workspace(dwl.batch)
+    idx_ms = time_steps(torch, lambda: qsa.index_select_decode(dd.q_idx, dd.kbar, [dd.pos] * dwl.batch, dwl.budget,
+                                                               dd.scores, dd.sel, sel_ws), args.decode_steps, flush)
+    idx_avg = sum(idx_ms) / len(idx_ms) / 1e3
+    kbar_bytes, step_bytes = decode_bytes(dwl)
+    rec = {
+        "workload": dwl.name,
+        "batch": dwl.batch,
+        "context": dwl.ctx,
+        "budget_blocks": dwl.budget,
+        "step_us_median": med * 1e3,
+        "step_us_min": steps_ms[0] * 1e3,
+        "steps": args.decode_steps,
+        "cache_flushed": True,
+        "hbm_frac_step": step_bytes / (med / 1e3) / HBM_PEAK,
+        "algorithmic_bytes_per_step": step_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_scan_kernel + decode_finalize_kernel (qsa_index_select_decode)",
+            "achieved": kbar_bytes / idx_avg / 1e9,
+            "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": kbar_bytes / idx_avg / HBM_PEAK,
+            "launch_us": idx_avg * 1e6,
+            "traffic": measured_traffic("decode_index_select", "decode.hip"),
+        },
+    }
+    log(args, f"decode {dwl.name}: median {med * 1e3:.1f} us/step; index-select {idx_avg * 1e6:.1f} us")
+    if extras and args.decode_tq > 1:
+        # tq new tokens per sequence in one step: one pass over the block
+        # keys scores all of them; each row has its own selection and attention
+        mt = args.decode_tq
+        dd.multi_setup(mt)
+        for _ in range(3):
+            dd.multi_step()
+        torch.cuda.synchronize()
+        m_ms = time_steps(torch, dd.multi_step, args.decode_steps, flush)
+        m_med = m_ms[len(m_ms) // 2]
+        _, m_bytes = decode_bytes(dwl, mt)
+        rec["multi_token"] = {
+            "tokens_per_sequence": mt,
+            "step_us_median": m_med * 1e3,
+            "step_us_min": m_ms[0] * 1e3,
+            "us_per_token": m_med * 1e3 / (dwl.batch * mt),
+            "single_token_us_per_token": med * 1e3 / dwl.batch,
+            "hbm_frac_step": m_bytes / (m_med / 1e3) / HBM_PEAK,
+            "algorithmic_bytes_per_step": m_bytes,
+            "data": "synthetic new-token rows of the workload's distributions",
+        }
+        log(args, f"decode {dwl.name}, {mt} tokens per sequence: median {m_med * 1e3:.1f} us/step")
+    if extras and args.page_tokens > 0:
+        dd.paged_setup(args.page_tokens)
+        for _ in range(3):
+            dd.paged_step()
+        torch.cuda.synchronize()
+        p_ms = time_steps(torch, dd.paged_step, args.decode_steps, flush)
+        p_med = p_ms[len(p_ms) // 2]
+        rec["paged"] = {
+            "page_tokens": args.page_tokens,
+            "pages": "random page order",
+            "step_us_median": p_med * 1e3,
+            "step_us_min": p_ms[0] * 1e3,
+            "hbm_frac_step": step_bytes / (p_med / 1e3) / HBM_PEAK,
+        }
+        log(args, f"decode {dwl.name}, paged: median {p_med * 1e3:.1f} us/step")
+    del dd, flush
+    torch.cuda.empty_cache()
+    return rec
+
+
+def summary_prefill(r):
+    return {"ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"],
+            "mfma_frac": r["mfma"]["layer_frac"], "index_select_mfma_frac": r["mfma"]["index_select_frac"],
+            "gather_GBs": r["attention"]["gather_GBs"], "attention_hbm_frac": r["attention"]["hbm_frac"],
+            "kernels_ms_per_step": r["kernels_ms_per_step"]}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -549,57 +831,19 @@ def main():
         _b.build()
     qsa.lib()
     assert torch.cuda.is_available(), "bench needs a GPU"
-
-    wl = I.WORKLOADS[args.workload]
-    t0 = time.time()
-    x = I.make_inputs(wl)
-    log(args, f"inputs {wl.name}: {time.time() - t0:.1f}s")
+    if args.calibrate:
+        calibrate(torch)
+        return
     rope = qsa.YARN if args.rope == "yarn" else None
-    pf = Prefill(wl, x, torch, qsa, rope)
-    pf.overlap = not args.serial
-    for _ in range(args.warmup):
-        pf.step(NullTimer())
-    torch.cuda.synchronize()
-    timer = EventTimer(torch)
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        pf.step(timer)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    kern = timer.totals()
-    ms_per_step = wall * 1e3 / args.steps
-    step_gpu_ms = sum(t for t, _ in kern.values()) / args.steps
-    tokens = wl.batch * wl.tq
-    value = tokens / (ms_per_step / 1e3)
-
-    geo = prefill_geometry(wl, 0, wl.tq)
-    n_chunks = math.ceil(wl.tq / (wl.chunk or wl.tq))
-    attn_ms, attn_n = kern["sparse_attn_prefill"]
-    attn_avg_s = attn_ms / attn_n / 1e3
-    attn_bytes_per_launch = geo["attn_bytes"] / n_chunks
-    idx_ms, idx_n = kern["index_select"]
-    roofline = {
-        "bound": "hbm",
-        "kernel": "sparse_attn_prefill",
-        "achieved": attn_bytes_per_launch / attn_avg_s / 1e9,
-        "peak": HBM_PEAK / 1e9,
-        "unit": "GB/s",
-        "frac": attn_bytes_per_launch / attn_avg_s / HBM_PEAK,
-        "traffic": measured_traffic("sparse_attn_prefill", "attention.hip"),
-    }
-    mfma = {
-        "index_select_frac": (geo["index_flops"] / n_chunks) / (idx_ms / idx_n / 1e3) / BF16_PEAK,
-        "layer_frac": (geo["index_flops"] + geo["attn_flops"]) / (ms_per_step / 1e3) / BF16_PEAK,
-        "note": "folded indexer minimum (2*128 flop per query-candidate pair) plus attention flops",
-    }
+    wl = I.WORKLOADS[args.workload]
     rec = {
         "metric": METRIC,
-        "value": value,
+        "value": None,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -609,180 +853,72 @@ def main():
                    "context": wl.length, "budget_blocks": wl.budget, "block_tokens": 4,
                    "query_chunk": wl.chunk, "heads": "24q/2kv x 256, indexer 4q/1k x 128",
                    "rope": "static YaRN, factor 4 over 262144" if args.rope == "yarn" else "plain, theta 1e7"},
-        "roofline": roofline,
-        "schedule": ("one stream: per query chunk the index-select, then attention" if args.serial else
-                     "two streams: the query chunks' index-selects in order on a second stream, each chunk's "
-                     "attention after its own selection (kernel times overlap, so they sum past ms_per_step)"),
-        "mfma": mfma,
-        "kernels_ms_per_step": {k: t / args.steps for k, (t, n) in kern.items()},
-        "launches_per_step": {k: n // args.steps for k, (t, n) in kern.items()},
-        "gpu_ms_per_step": step_gpu_ms,
-        "gather_bytes_per_step": geo["gathered_tokens"] * 2 * 2 * 256 * 2,
     }
-    log(args, f"prefill: {ms_per_step:.1f} ms/step, {value:.0f} tok/s; kernels {rec['kernels_ms_per_step']}")
-    if args.page_tokens > 0:
-        pp = PagedPrefill(pf, args.page_tokens)
-        for _ in range(args.warmup):
-            pp.step(NullTimer())
-        torch.cuda.synchronize()
-        ptimer = EventTimer(torch)
-        t_start = time.perf_counter()
-        for _ in range(args.steps):
-            pp.step(ptimer)
-        torch.cuda.synchronize()
-        p_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
-        pk = ptimer.totals()
-        pa_ms, pa_n = pk["sparse_attn_prefill"]
-        pa_avg_s = pa_ms / pa_n / 1e3
-        rec["prefill_paged"] = {
-            "page_tokens": args.page_tokens,
-            "pages": "random page order, the cached prefix copied in before timing",
-            "ms_per_step": p_ms,
-            "tokens_per_s": tokens / (p_ms / 1e3),
-            "kernels_ms_per_step": {k: t / args.steps for k, (t, n) in pk.items()},
-            "sparse_attn_prefill_hbm_frac": attn_bytes_per_launch / pa_avg_s / HBM_PEAK,
-            "note": "paged_append also copies the chunk's V and indexer-key rows into their pages",
+    x = None
+    if not args.no_prefill:
+        t0 = time.time()
+        x = I.make_inputs(wl)
+        log(args, f"inputs {wl.name}: {time.time() - t0:.1f}s")
+        pre, pf = measure_prefill(args, torch, qsa, wl, x, rope, args.steps, args.warmup, paged=True)
+        del pf
+        torch.cuda.empty_cache()
+        a = pre["attention"]
+        rec["value"] = pre["tokens_per_s"]
+        rec["ms_per_step"] = pre["ms_per_step"]
+        rec["roofline"] = {
+            "bound": "hbm",
+            "kernel": "sparse_attn_prefill",
+            "achieved": a["gather_GBs"],
+            "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": a["hbm_frac"],
+            "traffic": measured_traffic("sparse_attn_prefill", "attention.hip"),
         }
-        log(args, f"prefill, paged: {p_ms:.1f} ms/step; kernels {rec['prefill_paged']['kernels_ms_per_step']}")
-        del pp
-    del pf
-    torch.cuda.empty_cache()
+        rec["schedule"] = ("one stream: per query chunk the index-select, then attention" if args.serial else
+                           "two streams: the query chunks' index-selects in order on a second stream, each "
+                           "chunk's attention after its own selection (kernel times overlap, so they sum past "
+                           "ms_per_step)")
+        for k in ("mfma", "kernels_ms_per_step", "launches_per_step", "gpu_ms_per_step", "gather_bytes_per_step"):
+            rec[k] = pre[k]
+        if "paged" in pre:
+            rec["prefill_paged"] = pre["paged"]
 
     if not args.no_decode:
-        dwl = I.WORKLOADS[args.decode_workload]
-        t0 = time.time()
-        dx = I.make_inputs(dwl)
-        log(args, f"inputs {dwl.name}: {time.time() - t0:.1f}s")
-        dd = Decode(dwl, dx, torch, qsa, rope)
-        del dx
-        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dec = measure_decode(args, torch, qsa, I, I.WORKLOADS[args.decode_workload], rope)
+        for k, dst in (("multi_token", "decode_multi_token"), ("paged", "decode_paged")):
+            if k in dec:
+                rec[dst] = dec.pop(k)
+        rec["decode"] = dec
 
-        for _ in range(3):
-            dd.step(NullTimer())
-        torch.cuda.synchronize()
-        steps_ms = []
-        dtimer = NullTimer()
-        for _ in range(args.decode_steps):
-            flush.sum()
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
-            s.record()
-            dd.step(dtimer)
-            e.record()
-            torch.cuda.synchronize()
-            steps_ms.append(s.elapsed_time(e))
-        steps_ms.sort()
-        med = steps_ms[len(steps_ms) // 2]
-        # the dominant kernels alone: the fused index-select (block-key scan +
-        # threshold filter), same launch configuration as inside the step
-        sel_ws = qsa.index_select_workspace(dwl.batch)
-        idx_ms = []
-        for _ in range(args.decode_steps):
-            flush.sum()
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
-            s.record()
-            qsa.index_select_decode(dd.q_idx, dd.kbar, [dd.pos] * dwl.batch, dwl.budget, dd.scores, dd.sel, sel_ws)
-            e.record()
-            torch.cuda.synchronize()
-            idx_ms.append(s.elapsed_time(e))
-        idx_avg = sum(idx_ms) / len(idx_ms) / 1e3
-        o = dwl.ctx // 4
-        kbar_bytes = dwl.batch * (o * 128 * 2 + 4 * 128 * 2)
-        gather = dwl.batch * attended_tokens(dwl.ctx, dwl.budget) * 2 * 2 * 256 * 2
-        step_bytes = kbar_bytes + gather + dwl.batch * (24 * 256 * 2 * 2 + dwl.budget * 4)
-        rec["decode"] = {
-            "workload": dwl.name,
-            "batch": dwl.batch,
-            "context": dwl.ctx,
-            "budget_blocks": dwl.budget,
-            "step_us_median": med * 1e3,
-            "step_us_min": steps_ms[0] * 1e3,
-            "steps": args.decode_steps,
-            "cache_flushed": True,
-            "hbm_frac_step": step_bytes / (med / 1e3) / HBM_PEAK,
-            "algorithmic_bytes_per_step": step_bytes,
-            "roofline": {
-                "bound": "hbm",
-                "kernel": "decode_scan_kernel + decode_filter_kernel (qsa_index_select_decode)",
-                "achieved": kbar_bytes / idx_avg / 1e9,
-                "peak": HBM_PEAK / 1e9,
-                "unit": "GB/s",
-                "frac": kbar_bytes / idx_avg / HBM_PEAK,
-                "launch_us": idx_avg * 1e6,
-                "traffic": measured_traffic("decode_index_select", "decode.hip"),
-            },
-        }
-        log(args, f"decode: median {med * 1e3:.1f} us/step; index-select {idx_avg * 1e6:.1f} us")
-        if args.decode_tq > 1:
-            # tq new tokens per sequence in one step: one pass over the block
-            # keys scores all of them; each row has its own selection and attention
-            mt = args.decode_tq
-            dd.multi_setup(mt)
-            for _ in range(3):
-                dd.multi_step()
-            torch.cuda.synchronize()
-            m_ms = []
-            for _ in range(args.decode_steps):
-                flush.sum()
-                s = torch.cuda.Event(enable_timing=True)
-                e = torch.cuda.Event(enable_timing=True)
-                s.record()
-                dd.multi_step()
-                e.record()
-                torch.cuda.synchronize()
-                m_ms.append(s.elapsed_time(e))
-            m_ms.sort()
-            m_med = m_ms[len(m_ms) // 2]
-            m_gather = dwl.batch * sum(attended_tokens(dwl.ctx + t, dwl.budget) for t in range(mt)) * 2 * 2 * 256 * 2
-            m_bytes = kbar_bytes + m_gather + dwl.batch * mt * (24 * 256 * 2 * 2 + dwl.budget * 4)
-            rec["decode_multi_token"] = {
-                "tokens_per_sequence": mt,
-                "batch": dwl.batch,
-                "context": dwl.ctx,
-                "step_us_median": m_med * 1e3,
-                "step_us_min": m_ms[0] * 1e3,
-                "us_per_token": m_med * 1e3 / (dwl.batch * mt),
-                "single_token_us_per_token": med * 1e3 / dwl.batch,
-                "hbm_frac_step": m_bytes / (m_med / 1e3) / HBM_PEAK,
-                "algorithmic_bytes_per_step": m_bytes,
-                "data": "synthetic new-token rows of the workload's distributions",
-            }
-            log(args, f"decode, {mt} tokens per sequence: median {m_med * 1e3:.1f} us/step")
-        if args.page_tokens > 0:
-            dd.paged_setup(args.page_tokens)
-            for _ in range(3):
-                dd.paged_step()
-            torch.cuda.synchronize()
-            p_ms = []
-            for _ in range(args.decode_steps):
-                flush.sum()
-                s = torch.cuda.Event(enable_timing=True)
-                e = torch.cuda.Event(enable_timing=True)
-                s.record()
-                dd.paged_step()
-                e.record()
-                torch.cuda.synchronize()
-                p_ms.append(s.elapsed_time(e))
-            p_ms.sort()
-            p_med = p_ms[len(p_ms) // 2]
-            rec["decode_paged"] = {
-                "page_tokens": args.page_tokens,
-                "pages": "random page order",
-                "step_us_median": p_med * 1e3,
-                "step_us_min": p_ms[0] * 1e3,
-                "hbm_frac_step": step_bytes / (p_med / 1e3) / HBM_PEAK,
-            }
-            log(args, f"decode, paged: median {p_med * 1e3:.1f} us/step")
-        del dd, flush
+    if not args.no_configs:
+        # the other configurations: the 2048-token prefill, the 32K-context
+        # decode of 32 sequences, the 131072-token prefill in 8192-query chunks
+        cfg = {}
+        w0 = I.WORKLOADS["prefill_T2048_budget64"]
+        r0, _ = measure_prefill(args, torch, qsa, w0, I.make_inputs(w0), None, 20, 3)
+        cfg[w0.name] = summary_prefill(r0)
+        cfg[w0.name]["note"] = "the 4 MiB of K/V stay in the L2 and MALL: gather_GBs is mostly cache bandwidth"
+        w1 = I.WORKLOADS["decode_B32_ctx32K"]
+        d1 = measure_decode(args, torch, qsa, I, w1, None, extras=False)
+        cfg[w1.name] = {k: d1[k] for k in ("step_us_median", "step_us_min", "hbm_frac_step",
+                                           "algorithmic_bytes_per_step")}
+        cfg[w1.name]["index_select_us"] = d1["roofline"]["launch_us"]
+        w2 = I.WORKLOADS["prefill_T131072"]
+        r2, _ = measure_prefill(args, torch, qsa, w2, I.make_inputs(w2), None, 2, 1)
+        cfg[w2.name] = summary_prefill(r2)
         torch.cuda.empty_cache()
+        rec["configs"] = cfg
 
     if not args.no_gdn:
         rec["gdn"] = gdn_measure(args, torch, qsa, I)
     rec["achievable_peaks"] = achievable_peaks(torch)
 
-    if args.cpu_rows > 0:
-        rec["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_rows, args)
+    if args.cpu_rows > 0 and x is not None:
+        workers = oracle_workers()
+        rec["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_rows, args, workers)
+        del x
+        dwl = I.WORKLOADS[args.decode_workload]
+        rec["cpu_baseline_decode"] = cpu_baseline(dwl, I.make_inputs(dwl), dwl.batch, args, min(workers, dwl.batch))
     print(json.dumps(rec))
 
 

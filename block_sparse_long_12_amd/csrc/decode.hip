@@ -167,20 +167,6 @@ struct ScanSmem {
     int base[kMaxDecodeTq];
 };
 
-// Scores of the 4 tiles of a 64-block group: the tiles' 12-deep chains
-// interleaved (each tile accumulates in the order of block_scores, so the
-// bits are the same).
-__device__ __forceinline__ void group_scores(const bf16x8_t (&kf)[4][4], const bf16x8_t (&qf)[kIdxSlices],
-                                             f32x4_t (&acc)[4]) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < kIdxSlices; ++ks)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[nt][ks & 3], qf[ks], acc[nt], 0, 0, 0);
-}
-
 // Grid: n_side side workgroups first (one per sequence when the step appends
 // rows or rotates queries, else none), then B x wg_per_seq scan workgroups.
 // Dynamic LDS: tq x (256 * STEPS) scores.  kPaged: kbar (and the caches the
@@ -241,7 +227,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     // 4 consecutive blocks each, kept in LDS
     auto score_group = [&](const bf16x8_t (&kf)[4][4], int j0) {
         f32x4_t acc[4];
-        group_scores(kf, qf, acc);
+        block_scores4(kf, qf, acc);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int jj = j0 + 16 * nt + 4 * G;

@@ -32,6 +32,20 @@ __device__ __forceinline__ f32x4_t block_scores(const bf16x8_t (&kf)[4], const b
     return acc;
 }
 
+// The same scores for 4 tiles at once: the tiles' chains interleaved
+// slice by slice, so consecutive MFMAs never wait on each other's result
+// (each tile still accumulates in block_scores' order: the same bits).
+__device__ __forceinline__ void block_scores4(const bf16x8_t (&kf)[4][4], const bf16x8_t (&qf)[kIdxSlices],
+                                              f32x4_t (&acc)[4]) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kIdxSlices; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[nt][ks & 3], qf[ks], acc[nt], 0, 0, 0);
+}
+
 // B operand for the 16 tokens t0 .. t0 + 15 of one sequence's q_idx
 // [T][4][128] (512 contiguous values per token): lane column l%16 is token
 // t0 + l%16, whose 4 heads are summed and split into the three terms;

@@ -196,16 +196,15 @@ __device__ __forceinline__ void step_scores(const KTile& t, const bf16x8_t (&qf)
     const int lane = threadIdx.x & 63;
     const int c16 = lane & 15;
     const int G = lane >> 4;
+    bf16x8_t kf[4][4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        bf16x8_t kf[4];
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint4 v = t.chunk[16 * nt + c16][(4 * q + G) ^ c16];
-            kf[q] = *reinterpret_cast<const bf16x8_t*>(&v);
+            kf[nt][q] = *reinterpret_cast<const bf16x8_t*>(&v);
         }
-        acc[nt] = block_scores(kf, qf);
-    }
+    block_scores4(kf, qf, acc);
 }
 
 __device__ __forceinline__ void store_step(const KTile& t, const bf16x8_t (&qf)[kIdxSlices], int j0, int j_end, int t0,
