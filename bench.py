@@ -82,8 +82,9 @@ def parse():
 
 
 def calibrate(torch):
-    """Kernels of known traffic for scaling the FETCH_SIZE / WRITE_SIZE
-    counters: a 1 GiB copy (reads and writes 2^30 bytes) and a gather of
+    """Kernels of known traffic for checking the memory-traffic counters
+    (TCC_EA0_RDREQ_DRAM_32B / TCC_EA0_WRREQ_WRITE_DRAM_32B, and the derived
+    FETCH_SIZE / WRITE_SIZE): a 1 GiB copy (reads and writes 2^30 bytes) and a gather of
     2^21 distinct random rows of 512 bytes out of a 2 GiB bf16 buffer (reads
     2^30 bytes of rows plus 2^24 bytes of int64 indices, writes 2^30 bytes;
     the shape of the attention's K/V row gathers)."""
