@@ -21,7 +21,8 @@
 //              of 256), stored compactly; feeds the per-row thresholds;
 //   collect -- no score matrix: scores at or above the row's threshold are
 //              appended to per-wave LDS lists and, at the end, to the row's
-//              global candidate list (one atomic per row and workgroup).
+//              global candidate list (one atomic per row and workgroup) as
+//              (ordered key, ~block) pairs.
 // Causality: a workgroup stops at the last block its last row sees; collect
 // also drops each row's blocks at or past its own block.
 #include "index_common.h"
@@ -192,19 +193,35 @@ __device__ __forceinline__ void step_sync(int s, bool has_rows) {
 
 // Scores of one staged step (4 tiles of 16 blocks) for the wave's 16 rows:
 // lane l ends with blocks j0 + 16 nt + 4 (l / 16) .. + 3 of token l % 16.
+template <int kTilesLive = 4>
 __device__ __forceinline__ void step_scores(const KTile& t, const bf16x8_t (&qf)[kIdxSlices], f32x4_t (&acc)[4]) {
     const int lane = threadIdx.x & 63;
     const int c16 = lane & 15;
     const int G = lane >> 4;
-    bf16x8_t kf[4][4];
+    if constexpr (kTilesLive == 4) {
+        bf16x8_t kf[4][4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint4 v = t.chunk[16 * nt + c16][(4 * q + G) ^ c16];
-            kf[nt][q] = *reinterpret_cast<const bf16x8_t*>(&v);
+            for (int q = 0; q < 4; ++q) {
+                const uint4 v = t.chunk[16 * nt + c16][(4 * q + G) ^ c16];
+                kf[nt][q] = *reinterpret_cast<const bf16x8_t*>(&v);
+            }
+        block_scores4(kf, qf, acc);
+    } else {
+        // one 16-block tile at a time: 16 operand registers live instead of
+        // 64, so more waves fit on a SIMD
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            bf16x8_t kf[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 v = t.chunk[16 * nt + c16][(4 * q + G) ^ c16];
+                kf[q] = *reinterpret_cast<const bf16x8_t*>(&v);
+            }
+            acc[nt] = block_scores(kf, qf);
         }
-    block_scores4(kf, qf, acc);
+    }
 }
 
 __device__ __forceinline__ void store_step(const KTile& t, const bf16x8_t (&qf)[kIdxSlices], int j0, int j_end, int t0,
@@ -221,48 +238,69 @@ __device__ __forceinline__ void store_step(const KTile& t, const bf16x8_t (&qf)[
     }
 }
 
-// collect: append (key << 32 | row_local << 16 | (j - j_begin)) for every
-// score of the lane's row at or above its threshold tau, for blocks below
-// lim (the row's own block and the chunk end), to the wave's own LDS list:
-// one ballot per score slot, positions by mbcnt, the count kept wave-uniform
-// (no atomics).  For a number tau whose key has zero low bits, score >= tau
-// (IEEE) holds exactly when score_key(score) >= score_key(tau); a NaN tau
-// passes nothing.
+// Ordered key of a score that passed >= tau (so not NaN): -0.0 and +0.0
+// share 0x80000000, as in score_key.
+__device__ __forceinline__ uint32_t passed_key(uint32_t u) {
+    return u == 0x80000000u ? 0x80000000u : (u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u));
+}
+
+// collect: append (score bits << 32 | row_local << 16 | (j - j_begin)) for
+// every score of the lane's row at or above its threshold tau, for blocks
+// below lim (the row's own block and the chunk end), to the wave's own LDS
+// list: one ballot per score slot, positions by mbcnt, the count kept
+// wave-uniform in a scalar register (no atomics).  The ordered key is formed
+// later, once per listed candidate.  A NaN tau passes nothing.
+//
+// Most slots pass in no lane, so a slot costs one compare into a scalar
+// mask; a passing slot costs its position (two mbcnt), the packed index (one
+// add from the step's per-lane base) and the LDS write.  While the list has
+// room for every lane of the slot (a scalar test) no lane checks its
+// position.
+template <bool kLimit>
+__device__ __forceinline__ void collect_scan(const f32x4_t (&acc)[4], int jl, int lim, float tau, uint32_t base,
+                                             uint64_t* seg, int& cnt) {
+    constexpr int kWaveCap = kCollectCap / 4;
+    int c = __builtin_amdgcn_readfirstlane(cnt);
+    bool q[16];
+    uint64_t m[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int off = 16 * (e >> 2) + (e & 3);
+        q[e] = (!kLimit || jl + off < lim) && acc[e >> 2][e & 3] >= tau;
+        m[e] = __builtin_amdgcn_ballot_w64(q[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        if (m[e] != 0ull) {                               // wave-uniform
+            const int off = 16 * (e >> 2) + (e & 3);
+            const float v = acc[e >> 2][e & 3];
+            const int c0 = c;
+            const int n = __popcll(m[e]);
+            c = c0 + n;
+            if (q[e]) {
+                const int pos = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                    static_cast<uint32_t>(m[e] >> 32),
+                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m[e]), static_cast<uint32_t>(c0))));
+                if (c0 + n <= kWaveCap || pos < kWaveCap)
+                    seg[pos] = (static_cast<uint64_t>(__float_as_uint(v)) << 32) | (base + static_cast<uint32_t>(off));
+            }
+        }
+    }
+    cnt = c;
+}
+
 __device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf)[kIdxSlices], int j0, int lim,
                                              float tau, int row_local, int j_begin, uint64_t* seg, int& cnt) {
     f32x4_t acc[4];
-    step_scores(t, qf, acc);
+    step_scores<1>(t, qf, acc);
     const int lane = threadIdx.x & 63;
     const int jl = j0 + 4 * (lane >> 4);
-    // an appended score passed >= tau, so it is not NaN: its key is score_key's
-    // (-0.0 and +0.0 share 0x80000000) without the NaN case
-    auto key_of = [](float f) -> uint32_t {
-        const uint32_t u = __float_as_uint(f);
-        return u == 0x80000000u ? 0x80000000u : (u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u));
-    };
-    auto scan = [&](auto in_limit) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const bool q = in_limit(jl + 16 * (e >> 2) + (e & 3)) && acc[e >> 2][e & 3] >= tau;
-            const uint64_t m = __builtin_amdgcn_ballot_w64(q);
-            if (m != 0ull) {                              // wave-uniform
-                if (q) {
-                    const int pos = cnt + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                              static_cast<uint32_t>(m >> 32),
-                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
-                    if (pos < kCollectCap / 4)
-                        seg[pos] = (static_cast<uint64_t>(key_of(acc[e >> 2][e & 3])) << 32) |
-                                   static_cast<uint32_t>((row_local << 16) | (jl + 16 * (e >> 2) + (e & 3) - j_begin));
-                }
-                cnt += __popcll(m);
-            }
-        }
-    };
+    const uint32_t base = static_cast<uint32_t>((row_local << 16) | (jl - j_begin));
     // the block limit matters only in the steps that reach some lane's limit
     if (__all(j0 + kColStep <= lim))
-        scan([](int) { return true; });
+        collect_scan<false>(acc, jl, lim, tau, base, seg, cnt);
     else
-        scan([lim](int j) { return j < lim; });
+        collect_scan<true>(acc, jl, lim, tau, base, seg, cnt);
 }
 
 template <int kMode, bool kPaged>
@@ -365,7 +403,8 @@ __global__ __launch_bounds__(256) void index_kernel(
                 if (pos < kRowCap) {
                     const int j = j_begin + static_cast<int>(e & 0xffffu);
                     col.list[(static_cast<int64_t>(b) * tq + t_wg + rl) * kRowCap + pos] =
-                        (e & 0xffffffff00000000ull) | static_cast<uint32_t>(~j);
+                        (static_cast<uint64_t>(passed_key(static_cast<uint32_t>(e >> 32))) << 32) |
+                        static_cast<uint32_t>(~j);
                 }
             }
         }

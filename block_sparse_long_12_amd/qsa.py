@@ -20,7 +20,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqsa.so")
+# QSA_LIBRARY names another build of the same library (the host-sanitizer
+# build of block_sparse_long_12_amd.build_sanitize); default: the in-tree one.
+LIB_PATH = os.environ.get("QSA_LIBRARY") or os.path.join(HERE, "libqsa.so")
 
 BLOCK, HQ, HKV, D, ROT, HI, DI = 4, 24, 2, 256, 64, 4, 128
 ROPE_THETA = 1.0e7
