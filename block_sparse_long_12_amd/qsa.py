@@ -28,6 +28,7 @@ BLOCK, HQ, HKV, D, ROT, HI, DI = 4, 24, 2, 256, 64, 4, 128
 ROPE_THETA = 1.0e7
 MAX_BATCH = 256
 MAX_BUDGET = 2048
+NOALLOC_SCRATCH_BYTES = 16 << 20      # QSA_NOALLOC_SCRATCH_BYTES: the static scratch of decode_step_noalloc
 
 _c_p = ctypes.c_void_p
 _i64 = ctypes.c_int64

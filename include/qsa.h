@@ -383,8 +383,9 @@ qsa_status_t qsa_sparse_attn_prefill_paged(const uint16_t* q, int64_t q_seq_stri
  * first call on that GPU until the process ends (on that first call the
  * buffer is zero-filled by a kernel on `stream`; no memset).  The call makes
  * no hipMalloc/hipFree and no allocating library call.  Shapes whose
- * qsa_decode_step_workspace_bytes exceeds the buffer (about 158 rows of
- * batch x tq) are rejected with QSA_ERR_WORKSPACE before anything runs.  All
+ * qsa_decode_step_workspace_bytes exceeds the buffer (more than 168 rows of
+ * batch x tq, at any budget) are rejected with QSA_ERR_WORKSPACE before
+ * anything runs.  All
  * calls on one GPU share its buffer, which keeps the last call's contents:
  * calls that overlap on one GPU (other streams or threads) race and must be
  * serialised by the caller.

@@ -23,8 +23,9 @@ Readings taken where the pages are silent (each restated at its function):
   block key   = mean of the block's 4 indexer keys, summed in float32 in token
                 order, times 0.25, rounded to bf16 (nearest, ties to even);
   block score = sum over the 4 indexer heads of q_h . kbar, no weights, no
-                scale, no activation; computed exactly (float64) and rounded
-                once to float32;
+                scale, no activation; computed in float64 (each bf16 x bf16
+                product exact, the 512-term sum within 2^-44 of sum |q k|,
+                far below the float32 rounding) and rounded once to float32;
   candidates  = complete blocks strictly before the query's own block
                 o(t) = floor(t / 4); the own block is always selected and
                 counts toward the budget;

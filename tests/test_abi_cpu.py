@@ -220,6 +220,14 @@ def test_decode_step_validation(L):
     big = _pos(*([4099] * 64))
     assert L.qsa_decode_step_workspace_bytes(64, 4, budget) > 16 << 20
     assert call_na(batch=64, tq=4, pos=big) == WORKSPACE and "static" in L.qsa_last_error().decode()
+    # the static buffer serves 168 rows (batch x tq) at any budget, not 169
+    m = re.search(r"#define QSA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == qsa.NOALLOC_SCRATCH_BYTES
+    for b, t in ((168, 1), (42, 4), (56, 3)):
+        assert L.qsa_decode_step_workspace_bytes(b, t, 2048) <= qsa.NOALLOC_SCRATCH_BYTES
+    for b, t in ((169, 1), (43, 4), (57, 3)):
+        assert L.qsa_decode_step_workspace_bytes(b, t, 64) > qsa.NOALLOC_SCRATCH_BYTES
+        assert call_na(batch=b, tq=t, pos=_pos(*([4099] * b))) == WORKSPACE
     assert call(tq=4, k_idx_stride=9001 * 128) == INVALID          # rows 9001 .. 9003 out of reach
     assert call(rope=_rope(1e7, 0.9, 262144)) == INVALID and "yarn" in L.qsa_last_error().decode()
     assert call(rope=_rope(1.0)) == INVALID

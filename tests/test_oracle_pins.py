@@ -225,6 +225,22 @@ def test_scores_bruteforce_tiny():
             assert got[r, j] == np.float32(math.fsum(terms))
 
 
+def test_scores_are_the_correctly_rounded_sum_on_many_entries():
+    """2400 entries, rows of very different magnitudes: each score is the
+    float32 rounding of the exact sum of its 512 products (math.fsum), the
+    float64 product sum inside the oracle being far finer than that
+    rounding."""
+    q = _rand_bf16((40, 4, 128), 31)
+    kb = _rand_bf16((60, 128), 32)
+    q = O.f64_to_bf16(O.bf16_to_f64(q) * np.float64(2.0) ** np.arange(-20, 20)[:, None, None])  # exact scaling
+    got = O.index_scores(q, O.bf16_to_f64(kb))
+    qf, kf = O.bf16_to_f64(q), O.bf16_to_f64(kb)
+    for r in range(40):
+        for j in range(60):
+            terms = (qf[r, :, :] * kf[j][None, :]).ravel().tolist()
+            assert got[r, j] == np.float32(math.fsum(terms)), (r, j)
+
+
 def test_scores_basis_queries_pick_key_entries():
     kb = _rand_bf16((6, 128), 12)
     q = np.zeros((1, 4, 128), np.uint16)
