@@ -626,6 +626,8 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
     const int n_side = (scan_appends || qr.q != nullptr) ? batch : 0;
     const dim3 grid(static_cast<unsigned>(n_side + batch * wg_scan));
     const size_t lds = static_cast<size_t>(tq) * 256 * steps * 4;
+    const ScanTiming timing = scan_timing();
+    if (timing.begin != nullptr && (e = hipEventRecord(timing.begin, stream)) != hipSuccess) return e;
 #define QSA_SCAN(S, P)                                                                                       \
     hipLaunchKernelGGL((decode_scan_kernel<S, P>), grid, dim3(256), lds, stream, q_idx, qs, kbar, kbs, pos, \
                        budget, tq, n_side, wg_scan, scores, ss, sld, w, ap, scan_appends, qr, pmv)
@@ -646,6 +648,7 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
     }
 #undef QSA_SCAN
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (timing.end != nullptr && (e = hipEventRecord(timing.end, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(decode_finalize_kernel, dim3(static_cast<unsigned>(rows)), dim3(kFinNT), 0, stream,
                        scores, ss, sld, pos, budget, tq, w, sel, sels);
     return hipGetLastError();

@@ -19,6 +19,7 @@ static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local qsa::ScanTiming g_scan_timing{nullptr, nullptr};
 
 qsa_status_t fail(qsa_status_t s, const char* fmt, ...) {
     va_list ap;
@@ -158,6 +159,10 @@ qsa_status_t scratch_for_current_device(hipStream_t stream, ScratchSlot** slot_o
 
 }  // namespace
 
+namespace qsa {
+ScanTiming& scan_timing() { return g_scan_timing; }
+}  // namespace qsa
+
 extern "C" {
 
 int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
@@ -180,6 +185,11 @@ const char* qsa_status_string(qsa_status_t s) {
 }
 
 const char* qsa_last_error(void) { return g_err; }
+
+qsa_status_t qsa_set_scan_timing_events(void* begin_event, void* end_event) {
+    g_scan_timing = qsa::ScanTiming{static_cast<hipEvent_t>(begin_event), static_cast<hipEvent_t>(end_event)};
+    return QSA_OK;
+}
 
 qsa_status_t qsa_rope_apply(const uint16_t* x, int64_t x_seq_stride, int64_t x_tok_stride,
                             uint16_t* y, int64_t y_seq_stride, int64_t y_tok_stride,

@@ -183,6 +183,12 @@ hipError_t launch_attn_decode_ex(const uint16_t* q, int64_t qs, const uint16_t* 
 // which must be zero before the first use and are left zero by each call
 // (so one workspace serves calls of any shape)
 size_t decode_select_ws_bytes(int rows);
+// Events the decode index-select records around its scan launch (both null:
+// none); per host thread, set through qsa_set_scan_timing_events.
+struct ScanTiming {
+    hipEvent_t begin, end;
+};
+ScanTiming& scan_timing();
 // Rows a decode step appends at each sequence's new positions p0 .. p0+tq-1
 // before it scores (every pointer may be null: then that part is not done).
 struct DecodeAppend {

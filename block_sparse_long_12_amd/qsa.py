@@ -93,6 +93,7 @@ _SIGNATURES = {
     "qsa_decode_step": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _i64, _c_p, _i64,
                                _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, _rope_p, _c_p, _i64,
                                _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p, _sz, _c_p]),
+    "qsa_set_scan_timing_events": (_i32, [_c_p, _c_p]),
     "qsa_decode_step_noalloc": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _i64, _c_p,
                                        _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, _rope_p, _c_p,
                                        _i64, _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p]),
@@ -525,6 +526,21 @@ def _decode_step_args(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, p_
             _ptr(kbar), kbar.stride(0), p, B, tq, budget, float(scale), _rope_arg(rope),
             _ptr(scores), scores.shape[-1], scores.stride(0), _ptr(sel), sel.stride(0),
             _ptr(out), out.stride(0), _ptr(lse), g_ptr, g_stride)
+
+
+def set_scan_timing_events(begin=None, end=None) -> None:
+    """Measurement hook (qsa_set_scan_timing_events): while set, every decode
+    index-select on this thread records the torch events `begin` / `end` (timing
+    enabled, already recorded once so that torch considers them created) right
+    before and after its block-key scan launch; None, None turns it off."""
+    def handle(e):
+        if e is None:
+            return None
+        h = int(e.cuda_event)
+        if h == 0:
+            raise QSAError("record the event once before handing it to the library")
+        return h
+    lib().qsa_set_scan_timing_events(handle(begin), handle(end))
 
 
 def decode_step_noalloc(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,

@@ -78,6 +78,18 @@ const char*  qsa_status_string(qsa_status_t s);
 const char*  qsa_last_error(void);
 
 /*
+ * Measurement hook, not part of the method: while set on the calling host
+ * thread, every decode index-select (qsa_index_select_decode and the decode
+ * steps, which run it) records `begin_event` on its stream right before it
+ * launches the block-key scan kernel and `end_event` right after, so the
+ * caller can time that kernel alone with hipEventElapsedTime.  The events are
+ * caller-owned hipEvent_t handles (created with timing enabled, on the device
+ * of the calls); NULL, NULL turns the hook off.  Only stores the two
+ * handles; always returns QSA_OK.
+ */
+qsa_status_t qsa_set_scan_timing_events(void* begin_event, void* end_event);
+
+/*
  * Rotary parameters (model card, "Processing Ultra-Long Texts",
  * rope_parameters): rope_theta (1e7 for this model) and optional static YaRN
  * (rope_type "yarn": scale factor s over original_max_position_embeddings L;

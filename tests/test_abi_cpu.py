@@ -49,6 +49,14 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name)
 
 
+def test_scan_timing_hook_only_stores_handles(L):
+    """The measurement hook takes opaque event handles (or NULL) and makes no
+    HIP call; NULL, NULL turns it off."""
+    assert L.qsa_set_scan_timing_events(None, None) == OK
+    assert L.qsa_set_scan_timing_events(FAKE, FAKE) == OK
+    assert L.qsa_set_scan_timing_events(None, None) == OK
+
+
 def test_dims_and_strings(L):
     assert qsa.dims() == dict(block=4, hq=24, hkv=2, d=256, rot_dim=64, hi=4, di=128)
     assert L.qsa_abi_version() == 4
