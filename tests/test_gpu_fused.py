@@ -53,7 +53,9 @@ CASES = [("normal", [1048576 // 16, 70001, 4096 + 3], 512), ("normal", [9000, 90
          ("normal", [1048576, 1048576, 1048576, 1048576], 1024),
          ("normal", [65536, 65537, 65540, 65543], 64),
          ("equal", [70000, 70000, 70000], 512),               # every key equal: the threshold bin overflows
-         ("few_values", [80000, 66000], 512)]                 # tie groups of thousands at the threshold
+         ("few_values", [80000, 66000], 512),                 # tie groups of thousands at the threshold
+         ("normal", [28000] * 40, 2048),        # 40 rows: two-step scan waves keep > 64 (the exact key search)
+         ("normal", [1048576] * 4, 2048)]       # the largest budget at 1M context
 
 
 @pytest.mark.parametrize("kind,pos,budget", CASES, ids=[f"{k}-{p[0]}-{b}" for k, p, b in CASES])
