@@ -354,7 +354,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     }
 }
 
-constexpr int kFinNT = 512;                  // finalize threads
+constexpr int kFinNT = 1024;                 // finalize threads
 constexpr int kFinPer = kListCap / kFinNT;   // list entries per thread
 constexpr int kRankMax = 1024;               // cut-bin members ranked directly
 constexpr int kFinBins = 2048;               // radix bins over the listed keys' range
