@@ -85,6 +85,45 @@ def test_index_select_decode_matches_primitives(kind, pos, budget):
         assert int(ws[:CTRL_BYTES].count_nonzero()) == 0, "control words not left zeroed"
 
 
+def test_scan_timing_hook_times_the_scan_and_changes_nothing():
+    """With the measurement hook set, the decode index-select records the two
+    events around its scan launch (a positive elapsed time no longer than the
+    whole call) and returns the same scores and selection bit for bit."""
+    say("scan timing hook")
+    pos, budget = [70001, 130000], 512
+    B, nblk = len(pos), max(pos) // 4
+    q = _rand((B, 1, 4, 128), 5, 1 / math.sqrt(128)).cuda()
+    kbar = _kbar("normal", B, nblk, 6).cuda()
+    ld = (nblk + 3) // 4 * 4
+    ws = qsa.index_select_workspace(B)
+    outs = []
+    for hooked in (False, True):
+        s_f = torch.full((B, 1, ld), float("nan"), device="cuda")
+        sel_f = torch.empty((B, 1, budget), dtype=torch.int32, device="cuda")
+        b_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b_ev.record()
+        e_ev.record()
+        torch.cuda.synchronize()
+        if hooked:
+            qsa.set_scan_timing_events(b_ev, e_ev)
+        try:
+            c0.record()
+            qsa.index_select_decode(q, kbar, pos, budget, s_f, sel_f, ws)
+            c1.record()
+            torch.cuda.synchronize()
+        finally:
+            qsa.set_scan_timing_events(None, None)
+        if hooked:
+            scan_ms, call_ms = b_ev.elapsed_time(e_ev), c0.elapsed_time(c1)
+            assert 0.0 < scan_ms <= call_ms, (scan_ms, call_ms)
+        outs.append((s_f, sel_f))
+    for b in range(B):
+        o = pos[b] // 4
+        assert torch.equal(outs[0][0][b, 0, :o].view(torch.int32), outs[1][0][b, 0, :o].view(torch.int32))
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
 @pytest.mark.parametrize("ctx,budget,B", [(32768, 512, 8), (5001, 64, 3), (99, 512, 2), (131072, 512, 2)])
 def test_decode_step_matches_primitives(ctx, budget, B):
     say(f"decode_step ctx={ctx} budget={budget} B={B}")
