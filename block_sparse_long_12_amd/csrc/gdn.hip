@@ -542,6 +542,12 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][kStCt
         ed[r] = __expf(o.glast - o.gr[r]);
     }
     const float el = __expf(o.glast);
+    // the chunk's output rows as a buffer of exactly its n valid tokens: the
+    // stores of rows past the sequence end fall outside it and the hardware
+    // drops them, so every store is issued unconditionally and the wait
+    // counts for the prefetched operands stay exact
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        in.out + b * in.os + static_cast<int64_t>(t0) * (kGdnHv * kGdnD), 0, n * (kGdnHv * kGdnD * 2), 0x00020000);
     lds_barrier();
     // W = U - Wk S for tokens 16w .. 16w + 15 (U added after the products, so
     // the prefetched U stays where it landed until here)
@@ -587,9 +593,8 @@ __device__ __forceinline__ void gdn_chunk(const GdnOps& o, f32x4_t (&S)[2][kStCt
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * wave + 4 * G + r;
             const uint32_t pr = r < 2 ? o01 : o23;
-            if (i < n)
-                in.out[b * in.os + (static_cast<int64_t>(t0 + i) * kGdnHv + h) * kGdnD + kStCols * cb + 16 * ct + c16] =
-                    static_cast<uint16_t>(pr >> (16 * (r & 1)));
+            const uint32_t off = static_cast<uint32_t>(((i * kGdnHv + h) * kGdnD + kStCols * cb + 16 * ct + c16) * 2);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pr >> (16 * (r & 1))), orsrc, off, 0, 0);
         }
     }
     // S = exp(c_last) S + k^T (exp(c_last - c) W)
