@@ -10,7 +10,8 @@ The same line carries the 1M-context serving decode step (B=4, one new token
 each: its K/V/indexer-key rows appended, scores, selection, attention) under
 "decode", and the same step with 4 new tokens per sequence (the shape of
 multi-token prediction or speculative verification) under
-"decode_multi_token".  Inputs are seeded synthetic tensors already resident
+"decode_multi_token", and one sequence at the same context under
+"decode_single_sequence".  Inputs are seeded synthetic tensors already resident
 in HBM.  Rotary uses the model card's static YaRN table (factor 4 over 262144
 positions), as contexts past 262144 call for; --rope plain selects the plain
 table (the same work).
@@ -741,8 +742,15 @@ def measure_decode(args, torch, qsa, I, dwl, rope, extras=True):
     # the dominant kernels alone: the fused index-select (block-key scan and
     # the selection), same launch configuration as inside the step
     sel_ws = qsa.index_select_workspace(dwl.batch)
-    idx_ms = time_steps(torch, lambda: qsa.index_select_decode(dd.q_idx, dd.kbar, [dd.pos] * dwl.batch, dwl.budget,
-                                                               dd.scores, dd.sel, sel_ws), args.decode_steps, flush)
+    # rows that leave the candidate lists for the exact path (diagnostic hook)
+    exact_rows = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qsa.set_decode_fallback_counter(exact_rows)
+    try:
+        idx_ms = time_steps(torch, lambda: qsa.index_select_decode(dd.q_idx, dd.kbar, [dd.pos] * dwl.batch,
+                                                                   dwl.budget, dd.scores, dd.sel, sel_ws),
+                            args.decode_steps, flush)
+    finally:
+        qsa.set_decode_fallback_counter(None)
     idx_avg = sum(idx_ms) / len(idx_ms) / 1e3
     # the block-key scan alone, the dominant kernel: events the library records
     # on the call's stream right before and after the scan launch
@@ -787,6 +795,8 @@ def measure_decode(args, torch, qsa, I, dwl, rope, extras=True):
             "kernels": "decode_scan_kernel + decode_finalize_kernel",
             "call_us": idx_avg * 1e6,
             "hbm_frac": kbar_bytes / idx_avg / HBM_PEAK,
+            "exact_path_rows": int(exact_rows.item()),
+            "rows_selected": dwl.batch * len(idx_ms),
         },
     }
     log(args, f"decode {dwl.name}: median {med * 1e3:.1f} us/step; index-select {idx_avg * 1e6:.1f} us, "
@@ -913,6 +923,16 @@ def main():
             if k in dec:
                 rec[dst] = dec.pop(k)
         rec["decode"] = dec
+        # one sequence at the same context (the scan plan gives it longer
+        # candidate lists instead of fewer workgroups)
+        w = I.WORKLOADS[args.decode_workload]
+        w1 = I.custom_workload("decode", 1, w.ctx, 1, w.budget, n_needles=w.n_needles, seed=w.seed)
+        d1 = measure_decode(args, torch, qsa, I, w1, rope, extras=False)
+        rec["decode_single_sequence"] = {k: d1[k] for k in ("workload", "step_us_median", "step_us_min",
+                                                            "hbm_frac_step", "algorithmic_bytes_per_step")}
+        rec["decode_single_sequence"]["index_select"] = d1["index_select"]
+        rec["decode_single_sequence"]["scan_us"] = d1["roofline"]["launch_us"]
+        torch.cuda.empty_cache()
 
     if not args.no_configs:
         # the other configurations: the 2048-token prefill, the 32K-context

@@ -44,37 +44,67 @@ namespace qsa {
 constexpr int kDecCap = 4096;        // cut-bin members resolved in LDS by the finalize
 constexpr int kCtrl = 16;            // control words per row
 constexpr int kDecMaxRows = QSA_MAX_BATCH * QSA_MAX_DECODE_TQ;
-constexpr int kListCap = 6144;       // candidates listed per row
+constexpr int kListCap = 6144;       // candidates listed per row: the smallest capacity
+constexpr int kListCapMax = 4 * kListCap;
+constexpr int kListRowsMin = 32;     // the workspace lists at least this many rows' worth
 
 enum { kNList = 0, kMaxT, kOverflow };
 
 // per row r = b * tq + t (token t of sequence b, at position q_pos[b] + t)
 struct DecodeWs {
     uint32_t* ctrl;     // [kDecMaxRows][kCtrl]   zero between calls
-    uint64_t* list;     // [rows][kListCap]       key << 32 | ~j, any order
+    uint64_t* list;     // [rows][cap]            key << 32 | ~j, any order
+    int cap;            // list entries per row in this call: kListCap, 2 kListCap or 4 kListCap
 };
 
+// The lists take max(rows, kListRowsMin) x kListCap entries, so a call with
+// fewer rows may give each row a longer list (2x up to 16 rows, 4x up to 8).
 size_t decode_select_ws_bytes(int rows) {
-    return static_cast<size_t>(kDecMaxRows) * kCtrl * 4 + static_cast<size_t>(rows) * kListCap * 8;
+    return static_cast<size_t>(kDecMaxRows) * kCtrl * 4 +
+           static_cast<size_t>(max(rows, kListRowsMin)) * kListCap * 8;
 }
 
-static DecodeWs carve(void* ws) {
+// The largest list capacity per row the workspace holds for `rows` rows.
+static int list_cap_avail(int rows) {
+    int c = kListCap;
+    while (2 * c <= kListCapMax && static_cast<int64_t>(rows) * 2 * c <= int64_t{max(rows, kListRowsMin)} * kListCap)
+        c *= 2;
+    return c;
+}
+
+static DecodeWs carve(void* ws, int cap) {
     char* p = static_cast<char*>(ws);
     DecodeWs w;
     w.ctrl = reinterpret_cast<uint32_t*>(p);
     w.list = reinterpret_cast<uint64_t*>(p + static_cast<size_t>(kDecMaxRows) * kCtrl * 4);
+    w.cap = cap;
     return w;
 }
 
 // Candidates a wave lists for a row keeping `keep` of o candidates, n_w of
-// them among the wave's blocks: the expected share m = keep n_w / o plus
-// 4 sqrt(m) + 6, so that for blocks ranked at random a wave holds more of the
-// selection than it lists with probability below 1e-6 (a Poisson tail).  The
-// cut is exact whatever the count: more only costs list space, fewer sends
-// skewed rows to the slower exact path.
-__device__ __forceinline__ int wave_keep(int keep, int o, int n_w) {
+// them among the wave's blocks: with blocks ranked at random the wave holds
+// about Poisson(m) of the selection, m = keep n_w / o, and m + 5.5 sqrt(m) + 4
+// bounds that count except with probability below 1e-7 (checked against the
+// Poisson quantiles for m from 0.01 to 400; at most 3 above them).  The cut
+// is exact whatever the count: more only costs list space, fewer sends skewed
+// rows to the slower exact path.
+__host__ __device__ inline int wave_keep(int keep, int o, int n_w) {
     const float m = static_cast<float>(keep) * static_cast<float>(n_w) / static_cast<float>(o);
-    return min(n_w, static_cast<int>(ceilf(m + 4.f * sqrtf(m))) + 6);
+    return min(n_w, static_cast<int>(ceilf(m + 5.5f * sqrtf(m) + 4.f)));
+}
+
+constexpr int kLaneMaxKeep = 64;     // largest kw whose threshold comes from the lanes' two largest keys
+
+// Entries a wave of n_w blocks lists for a row, bounded from above for blocks
+// ranked at random: only a lane's third or later key can reach T without
+// being one of the 128 values T is taken from, which keeps the count within
+// kw (1 + (kw / 64)^2) (simulated means: 11.02 for kw = 11 and 8 keys per
+// lane, 19.2 for 19 and 8, 28.6 for 28 and 16, 44.3 for 42 and 32); with the
+// exact search, kw.
+static double wave_listed(int kw, int n_w) {
+    if (kw >= n_w) return n_w;
+    if (kw > kLaneMaxKeep) return kw;
+    return kw * (1.0 + (kw / 64.0) * (kw / 64.0));
 }
 
 // Queries of a decode step rotated for attention (q_rot [B][tq][24][256]).
@@ -275,18 +305,22 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
         const int kw = wave_keep(keep_t, o_t, n_w);
         // T with at least kw of the wave's keys >= T (0: every candidate
         // listed), built from the top bit down, keeping a bit while enough
-        // keys reach the prefix.  For kw <= 64 it is the kw-th largest of the
-        // 64 lane maxima (at most the kw-th largest key: kw lanes each hold a
-        // key >= it), one ballot per bit; else the kw-th largest key itself.
+        // keys reach the prefix.  For kw <= kLaneMaxKeep it is the kw-th
+        // largest of the 128 values made of each lane's two largest keys (at
+        // most the kw-th largest key: kw distinct keys reach it), two ballots
+        // per bit; else the kw-th largest key itself, STEPS ballots per bit.
         uint32_t T = 0u;
         if (kw < n_w) {
-            if (kw <= 64) {
-                uint32_t lmax = 0u;
+            if (kw <= kLaneMaxKeep) {
+                uint32_t l1 = 0u, l2 = 0u;                   // the lane's two largest keys
 #pragma unroll
-                for (int st = 0; st < STEPS; ++st) lmax = max(lmax, key[st]);
+                for (int st = 0; st < STEPS; ++st) {
+                    l2 = max(l2, min(l1, key[st]));
+                    l1 = max(l1, key[st]);
+                }
                 for (int bit = 31; bit >= 0; --bit) {
                     const uint32_t c = T | (1u << bit);
-                    if (__popcll(__ballot(lmax >= c)) >= kw) T = c;
+                    if (__popcll(__ballot(l1 >= c)) + __popcll(__ballot(l2 >= c)) >= kw) T = c;
                 }
             } else {
                 for (int bit = 31; bit >= 0; --bit) {
@@ -348,14 +382,13 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
     for (int t = 0; t < tq; ++t) {
         const int nl = min(sm.n_emit[t], kEmitPerRow);
         const int base = sm.base[t];
-        uint64_t* list = ws.list + static_cast<int64_t>(b * tq + t) * kListCap;
+        uint64_t* list = ws.list + static_cast<int64_t>(b * tq + t) * ws.cap;
         for (int k = tid; k < nl; k += 256)
-            if (base + k < kListCap) list[base + k] = sm.emit[t][k];
+            if (base + k < ws.cap) list[base + k] = sm.emit[t][k];
     }
 }
 
 constexpr int kFinNT = 1024;                 // finalize threads
-constexpr int kFinPer = kListCap / kFinNT;   // list entries per thread
 constexpr int kRankMax = 1024;               // cut-bin members ranked directly
 constexpr int kFinBins = 2048;               // radix bins over the listed keys' range
 constexpr int kFinBits = 11;
@@ -398,10 +431,12 @@ __device__ __forceinline__ void rank_cut(const uint64_t* cand, int n, int take, 
     }
 }
 
+// kPer list entries per thread: ws.cap = kPer * kFinNT.
+template <int kPer>
 __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __restrict__ scores, int64_t ss,
                                                                  int64_t sld, Positions pos, int budget, int tq,
                                                                  DecodeWs ws, int32_t* __restrict__ sel,
-                                                                 int64_t sels) {
+                                                                 int64_t sels, uint32_t* fallback_count) {
     __shared__ FinalizeSmem sm;
     const int tid = threadIdx.x;
     const int r = blockIdx.x;                             // row = token t of sequence b
@@ -416,13 +451,13 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
 
     // the list, every load in flight at once with the control words (fixed
     // capacity: entries past the count are read and dropped)
-    const uint64_t* __restrict__ lg = ws.list + static_cast<int64_t>(r) * kListCap;
-    uint64_t e[kFinPer];
+    const uint64_t* __restrict__ lg = ws.list + static_cast<int64_t>(r) * (kPer * kFinNT);
+    uint64_t e[kPer];
 #pragma unroll
-    for (int i = 0; i < kFinPer; ++i) e[i] = lg[tid + kFinNT * i];
+    for (int i = 0; i < kPer; ++i) e[i] = lg[tid + kFinNT * i];
     const int n = static_cast<int>(ctrl[kNList]);
     const uint32_t max_t = ctrl[kMaxT];
-    const bool listed = ctrl[kOverflow] == 0u && n <= kListCap && n >= keep;
+    const bool listed = ctrl[kOverflow] == 0u && n <= kPer * kFinNT && n >= keep;
     uint32_t* h = sm.u.m.h;
     int32_t* chosen = sm.u.m.chosen;
     bool exact = listed;
@@ -433,7 +468,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         // LDS atomics)
         uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-        for (int i = 0; i < kFinPer; ++i)
+        for (int i = 0; i < kPer; ++i)
             if (tid + kFinNT * i < n) {
                 const uint32_t k = static_cast<uint32_t>(e[i] >> 32);
                 kmin = min(kmin, k);
@@ -464,7 +499,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         const int shift = span < kFinBins ? 0 : 32 - __clz(static_cast<int>(span >> kFinBits));
         auto bin_of = [&](uint64_t x) { return (static_cast<uint32_t>(x >> 32) - kmin) >> shift; };
 #pragma unroll
-        for (int i = 0; i < kFinPer; ++i)
+        for (int i = 0; i < kPer; ++i)
             if (tid + kFinNT * i < n) atomicAdd(&h[bin_of(e[i])], 1u);
         lds_barrier();
         find_threshold_bin<kFinNT>(h, kFinBins, keep, sm.u.m.wave_tot, &sm.u.m.sh_bin, &sm.u.m.sh_above);
@@ -477,10 +512,10 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
             // (positions by ballot and lane count: one LDS atomic per wave and
             // pass, not one per entry on a single counter)
             uint64_t* lc = sm.u.m.cand;
-            uint64_t m_up[kFinPer], m_in[kFinPer];
+            uint64_t m_up[kPer], m_in[kPer];
             int n_up = 0, n_in = 0;
 #pragma unroll
-            for (int i = 0; i < kFinPer; ++i) {
+            for (int i = 0; i < kPer; ++i) {
                 const bool ok = tid + kFinNT * i < n;
                 const uint32_t d1 = bin_of(e[i]);
                 m_up[i] = __ballot(ok && d1 > tbin);
@@ -496,7 +531,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
             b_up = __shfl(b_up, 0);
             b_in = __shfl(b_in, 0);
 #pragma unroll
-            for (int i = 0; i < kFinPer; ++i) {
+            for (int i = 0; i < kPer; ++i) {
                 const int lane = tid & 63;
                 if ((m_up[i] >> lane) & 1ull)
                     chosen[b_up + lanes_below(m_up[i])] = static_cast<int32_t>(~static_cast<uint32_t>(e[i]));
@@ -524,6 +559,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         }
     }
     if (!exact) {
+        if (fallback_count != nullptr && tid == 0) atomicAdd(fallback_count, 1u);
         select_row<kFinNT>(scores + b * ss + t * sld, o, keep, budget, out, sm.u.s);
     } else {
         if (o <= 32 * kBitmapWords) {
@@ -566,6 +602,66 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
     if (tid < kCtrl) ctrl[tid] = 0u;
 }
 
+// Scan granularity (256 * steps blocks per workgroup, 64 * steps per wave) and
+// list capacity per row.  A row's list holds about wave_listed entries per
+// wave, so longer waves give shorter lists but fewer workgroups.  Measured
+// at 1M context, budget 512: one sequence scanned by 128 workgroups instead
+// of 256 takes about 5 us longer, by 64 about 19 us; doubling the list
+// capacity costs the finalize about 2.5 us; with 4 tokens per sequence,
+// 256 workgroups instead of 512 cost about 11 us.  So the plan takes the
+// longest steps that still give every CU a workgroup (two when tq > 1; the
+// steps start at the largest of 8, 4, 2, 1 that gives about two), then,
+// going down to the starting steps, the first whose expected list plus 4
+// standard deviations fits a capacity the workspace holds (kListCap,
+// 2 kListCap, 4 kListCap: the smallest that fits) with the thresholds taken
+// from the lanes' two largest keys; if none, longer steps; then the exact
+// threshold search.  The dynamic LDS (tq x 256 x steps floats) stays within
+// 64 KiB.  A list that still overflows sends its row to the exact path.
+static void scan_plan(int batch, int tq, int o, int keep, int* steps, int* cap) {
+    const int64_t groups = static_cast<int64_t>(batch) * ((o + 255) / 256);
+    const int s0 = groups >= 8 * 512 ? 8 : groups >= 4 * 512 ? 4 : groups >= 2 * 512 ? 2 : 1;
+    const int s_max = tq <= 2 ? 32 : 16;
+    const int avail = list_cap_avail(batch * tq);
+    auto wgs = [&](int st) { return static_cast<int64_t>(batch) * ((o + 256 * st - 1) / (256 * st)); };
+    // the longest steps that give every CU a workgroup (two with several
+    // tokens per sequence: the per-row listing after the stream grows with tq,
+    // and a second workgroup per CU overlaps it)
+    const int64_t min_wgs = tq > 1 ? 512 : 256;
+    int s_full = s0;
+    while (2 * s_full <= s_max && wgs(2 * s_full) >= min_wgs) s_full *= 2;
+    auto lane_max = [&](int st) { return wave_keep(keep, o, min(64 * st, o)) <= kLaneMaxKeep; };
+    // the smallest capacity that holds the expected list (per-wave spread
+    // about sqrt(listed - kw + 1)), or 0
+    auto cap_for = [&](int st) {
+        if (keep <= 0 || keep >= o) return kListCap;         // trivial rows list nothing
+        const int n_w = min(64 * st, o);
+        const int kw = wave_keep(keep, o, n_w);
+        const double per = wave_listed(kw, n_w);
+        const double waves = (o + n_w - 1) / n_w;
+        const double need = waves * per + 4.0 * sqrt(waves * (per - kw + 1.0));
+        for (int c = kListCap; c <= avail; c *= 2)
+            if (need <= c) return c;
+        return 0;
+    };
+    auto take = [&](int st) {
+        const int c = cap_for(st);
+        if (c == 0) return false;
+        *steps = st;
+        *cap = c;
+        return true;
+    };
+    for (int st = s_full; st >= s0; st /= 2)
+        if (lane_max(st) && take(st)) return;
+    for (int st = 2 * s_full; st <= s_max; st *= 2)
+        if (lane_max(st) && take(st)) return;
+    for (int st = s_full; st >= s0; st /= 2)
+        if (take(st)) return;
+    for (int st = 2 * s_full; st <= s_max; st *= 2)
+        if (take(st)) return;
+    *steps = s0;                                             // rows that overflow take the exact path
+    *cap = avail;
+}
+
 hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar,
                                       int64_t kbs, const Positions& pos, int batch, int tq, int budget,
                                       float* scores, int64_t ss, int64_t sld, int32_t* sel, int64_t sels,
@@ -574,13 +670,11 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
     const int rows = batch * tq;
     int o_max = 0;
     for (int b = 0; b < batch; ++b) o_max = max(o_max, (pos.p[b] + tq - 1) / kBlock);
-    // scan: 256 * STEPS blocks per workgroup; STEPS is the largest of 8, 4, 2, 1
-    // that still gives about 2 workgroups per CU
-    const int64_t groups = static_cast<int64_t>(batch) * ((o_max + 255) / 256);
-    const int steps = groups >= 8 * 512 ? 8 : groups >= 4 * 512 ? 4 : groups >= 2 * 512 ? 2 : 1;
+    int steps, cap;
+    scan_plan(batch, tq, o_max, min(budget - 1, o_max), &steps, &cap);
     const int wg_scan = max(1, (o_max + 256 * steps - 1) / (256 * steps));
 
-    const DecodeWs w = carve(ws);
+    const DecodeWs w = carve(ws, cap);
     AppendArgs ap{};
     qsa_rope_t rope{1.0e7, 1.0, 0};
     if (append != nullptr) {
@@ -633,6 +727,8 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
                        budget, tq, n_side, wg_scan, scores, ss, sld, w, ap, scan_appends, qr, pmv)
     if (pm != nullptr) {
         switch (steps) {
+            case 32: QSA_SCAN(32, true); break;
+            case 16: QSA_SCAN(16, true); break;
             case 8: QSA_SCAN(8, true); break;
             case 4: QSA_SCAN(4, true); break;
             case 2: QSA_SCAN(2, true); break;
@@ -640,6 +736,8 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
         }
     } else {
         switch (steps) {
+            case 32: QSA_SCAN(32, false); break;
+            case 16: QSA_SCAN(16, false); break;
             case 8: QSA_SCAN(8, false); break;
             case 4: QSA_SCAN(4, false); break;
             case 2: QSA_SCAN(2, false); break;
@@ -649,8 +747,15 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
 #undef QSA_SCAN
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (timing.end != nullptr && (e = hipEventRecord(timing.end, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_finalize_kernel, dim3(static_cast<unsigned>(rows)), dim3(kFinNT), 0, stream,
-                       scores, ss, sld, pos, budget, tq, w, sel, sels);
+#define QSA_FIN(P)                                                                                            \
+    hipLaunchKernelGGL(decode_finalize_kernel<P>, dim3(static_cast<unsigned>(rows)), dim3(kFinNT), 0, stream, \
+                       scores, ss, sld, pos, budget, tq, w, sel, sels, decode_fallback_counter())
+    switch (cap) {
+        case 4 * kListCap: QSA_FIN(4 * kListCap / kFinNT); break;
+        case 2 * kListCap: QSA_FIN(2 * kListCap / kFinNT); break;
+        default: QSA_FIN(kListCap / kFinNT); break;
+    }
+#undef QSA_FIN
     return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 thread_local qsa::ScanTiming g_scan_timing{nullptr, nullptr};
+thread_local uint32_t* g_fallback_counter = nullptr;
 
 qsa_status_t fail(qsa_status_t s, const char* fmt, ...) {
     va_list ap;
@@ -161,6 +162,7 @@ qsa_status_t scratch_for_current_device(hipStream_t stream, ScratchSlot** slot_o
 
 namespace qsa {
 ScanTiming& scan_timing() { return g_scan_timing; }
+uint32_t*& decode_fallback_counter() { return g_fallback_counter; }
 }  // namespace qsa
 
 extern "C" {
@@ -188,6 +190,11 @@ const char* qsa_last_error(void) { return g_err; }
 
 qsa_status_t qsa_set_scan_timing_events(void* begin_event, void* end_event) {
     g_scan_timing = qsa::ScanTiming{static_cast<hipEvent_t>(begin_event), static_cast<hipEvent_t>(end_event)};
+    return QSA_OK;
+}
+
+qsa_status_t qsa_set_decode_fallback_counter(uint32_t* counter) {
+    g_fallback_counter = counter;
     return QSA_OK;
 }
 

@@ -189,6 +189,9 @@ struct ScanTiming {
     hipEvent_t begin, end;
 };
 ScanTiming& scan_timing();
+// Device counter of decode rows that take the exact path (null: not counted);
+// per host thread, set through qsa_set_decode_fallback_counter.
+uint32_t*& decode_fallback_counter();
 // Rows a decode step appends at each sequence's new positions p0 .. p0+tq-1
 // before it scores (every pointer may be null: then that part is not done).
 struct DecodeAppend {

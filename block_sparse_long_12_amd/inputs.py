@@ -107,7 +107,7 @@ WORKLOADS: dict[str, Workload] = {w.name: w for w in [
 
 def custom_workload(kind: str, batch: int, ctx: int, tq: int, budget: int,
                     n_needles: int = 0, seed: int = 7, chunk: int | None = None) -> Workload:
-    """A workload of arbitrary (small) size with the same distributions."""
+    """A workload of any size with the same distributions."""
     name = f"{kind}_B{batch}_ctx{ctx}_T{tq}_budget{budget}_seed{seed}"
     return Workload(name, kind, batch, ctx, tq, budget, n_needles, seed, chunk)
 

@@ -94,6 +94,7 @@ _SIGNATURES = {
                                _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, _rope_p, _c_p, _i64,
                                _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p, _sz, _c_p]),
     "qsa_set_scan_timing_events": (_i32, [_c_p, _c_p]),
+    "qsa_set_decode_fallback_counter": (_i32, [_c_p]),
     "qsa_decode_step_noalloc": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _i64, _c_p,
                                        _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, ctypes.c_float, _rope_p, _c_p,
                                        _i64, _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _i64, _c_p]),
@@ -541,6 +542,17 @@ def set_scan_timing_events(begin=None, end=None) -> None:
             raise QSAError("record the event once before handing it to the library")
         return h
     lib().qsa_set_scan_timing_events(handle(begin), handle(end))
+
+
+def set_decode_fallback_counter(counter=None) -> None:
+    """Diagnostic hook (qsa_set_decode_fallback_counter): while set, every
+    decode index-select on this thread adds 1 to the one-element device tensor
+    `counter` (int32 or uint32 storage) for each row that takes the exact path
+    over the stored scores; None turns it off."""
+    if counter is not None:
+        if not (counter.is_cuda and counter.numel() == 1 and counter.element_size() == 4):
+            raise QSAError("counter must be a one-element 4-byte device tensor")
+    lib().qsa_set_decode_fallback_counter(None if counter is None else counter.data_ptr())
 
 
 def decode_step_noalloc(q_raw, k_new_raw, q_idx, k_idx, k_cache, v_cache, kbar, pos, budget: int,

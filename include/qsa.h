@@ -90,6 +90,19 @@ const char*  qsa_last_error(void);
 qsa_status_t qsa_set_scan_timing_events(void* begin_event, void* end_event);
 
 /*
+ * Diagnostic hook, not part of the method: while set on the calling host
+ * thread, every decode index-select adds 1 to the device uint32 at `counter`
+ * for each row that takes its exact path over the stored scores instead of
+ * the candidate list (the list overflowed, or its cut fell below a scan
+ * wave's threshold: score patterns far from random order, such as large tie
+ * groups).  The selection is the same either way; the exact path is slower.
+ * `counter` is caller-owned device memory on the device of the calls; the
+ * caller zeroes and reads it.  NULL turns the hook off.  Only stores the
+ * pointer; always returns QSA_OK.
+ */
+qsa_status_t qsa_set_decode_fallback_counter(uint32_t* counter);
+
+/*
  * Rotary parameters (model card, "Processing Ultra-Long Texts",
  * rope_parameters): rope_theta (1e7 for this model) and optional static YaRN
  * (rope_type "yarn": scale factor s over original_max_position_embeddings L;
@@ -260,7 +273,12 @@ qsa_status_t qsa_sparse_attn_decode(const uint16_t* q, int64_t q_seq_stride,
  * qsa_select_topk, bit for bit, in two launches that spread each row over
  * many workgroups (a scan whose workgroups each list their own top
  * candidates of every row, then a per-row exact finish over the lists, with
- * the full radix select of the stored row where a list cannot decide).
+ * the full radix select of the stored row where a list cannot decide).  The
+ * scan's workgroup size in blocks and each row's list capacity are chosen
+ * per call from batch, tq, the longest context and the budget, so that
+ * randomly ordered scores fit the lists (qsa_set_decode_fallback_counter
+ * counts the rows that do not); the workspace holds lists for at least 8
+ * rows, which calls with fewer rows use as longer lists.
  * scores [B][tq][scores_ld] float with scores_ld >= (q_pos + tq - 1)/4
  * rounded up to a multiple of 4 (entries past a row's own block are
  * scratch), 16-byte aligned.  The workspace

@@ -57,6 +57,14 @@ def test_scan_timing_hook_only_stores_handles(L):
     assert L.qsa_set_scan_timing_events(None, None) == OK
 
 
+def test_decode_fallback_counter_hook_only_stores_the_pointer(L):
+    """The diagnostic hook takes a device pointer (or NULL) and touches no
+    memory when set; NULL turns it off."""
+    assert L.qsa_set_decode_fallback_counter(None) == OK
+    assert L.qsa_set_decode_fallback_counter(FAKE) == OK
+    assert L.qsa_set_decode_fallback_counter(None) == OK
+
+
 def test_dims_and_strings(L):
     assert qsa.dims() == dict(block=4, hq=24, hkv=2, d=256, rot_dim=64, hi=4, di=128)
     assert L.qsa_abi_version() == 4

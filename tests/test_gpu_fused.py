@@ -85,6 +85,45 @@ def test_index_select_decode_matches_primitives(kind, pos, budget):
         assert int(ws[:CTRL_BYTES].count_nonzero()) == 0, "control words not left zeroed"
 
 
+# (kind, positions, budget, rows expected on the exact path): random scores
+# at long context, one to four sequences and the largest budget, must all
+# stay on the candidate lists (the scan's plan sizes the waves and the lists
+# for them); equal keys send every row to the exact path
+FAST_CASES = [("normal", [1048576], 512, 0), ("normal", [1048576, 1048579], 512, 0),
+              ("normal", [1048576, 1000000, 1048575], 512, 0), ("normal", [1048576] * 4, 512, 0),
+              ("normal", [1048576] * 4, 2048, 0), ("normal", [1048576], 2048, 0), ("normal", [262144], 512, 0),
+              ("normal", [131072] * 8, 512, 0), ("normal", [32768] * 32, 512, 0),
+              ("equal", [300000, 300000], 512, 2)]
+
+
+@pytest.mark.parametrize("kind,pos,budget,n_exact", FAST_CASES,
+                         ids=[f"{k}-{len(p)}x{p[0]}-{b}" for k, p, b, _ in FAST_CASES])
+def test_index_select_decode_stays_on_the_candidate_lists(kind, pos, budget, n_exact):
+    say(f"index_select_decode fast path {kind} B={len(pos)} pos={pos[0]} budget={budget}")
+    B = len(pos)
+    nblk = max(pos) // 4
+    q = _rand((B, 1, 4, 128), sum(pos) + 1, 1 / math.sqrt(128)).cuda()
+    kbar = _kbar(kind, B, nblk, budget + 1).cuda()
+    ld = (nblk + 3) // 4 * 4
+    s_ref = torch.empty((B, 1, ld), device="cuda")
+    sel_ref = torch.empty((B, 1, budget), dtype=torch.int32, device="cuda")
+    qsa.index_scores(q, kbar, pos, s_ref)
+    qsa.select_topk(s_ref, pos, budget, sel_ref)
+    ws = qsa.index_select_workspace(B)
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s_f = torch.empty_like(s_ref)
+    sel_f = torch.empty_like(sel_ref)
+    qsa.set_decode_fallback_counter(counter)
+    try:
+        qsa.index_select_decode(q, kbar, pos, budget, s_f, sel_f, ws)
+        torch.cuda.synchronize()
+    finally:
+        qsa.set_decode_fallback_counter(None)
+    assert torch.equal(sel_f, sel_ref)
+    assert int(counter.item()) == n_exact
+    assert int(ws[:CTRL_BYTES].count_nonzero()) == 0
+
+
 def test_scan_timing_hook_times_the_scan_and_changes_nothing():
     """With the measurement hook set, the decode index-select records the two
     events around its scan launch (a positive elapsed time no longer than the
