@@ -432,6 +432,180 @@ __device__ __forceinline__ void rank_cut(const uint64_t* cand, int n, int take, 
 }
 
 // kPer list entries per thread: ws.cap = kPer * kFinNT.
+// The top `keep` of entries e by (key, ~j) -- thread tid holds entries
+// tid + kFinNT i, i < P, the first n of all valid -- into sm.u.m.chosen (any
+// order), leaving the keep-th largest key in sm.u.m.kstar: one radix level over
+// the entries' own key range, keys above the cut bin taken, the bin's members
+// ranked.  False (nothing decided) when the cut bin holds more than kDecCap.
+// Every thread must call it.
+template <int P>
+__device__ __forceinline__ bool take_top(const uint64_t (&e)[P], int n, int keep, FinalizeSmem& sm) {
+    const int tid = threadIdx.x;
+    uint32_t* h = sm.u.m.h;
+    int32_t* chosen = sm.u.m.chosen;
+    // one radix level over the entries' own key range [kmin, kmax]: bin =
+    // (key - kmin) >> shift < 4096 (the entries all sit in the tail, so the
+    // top key bits would crowd them into a few bins and serialize the LDS
+    // atomics)
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+        if (tid + kFinNT * i < n) {
+            const uint32_t k = static_cast<uint32_t>(e[i] >> 32);
+            kmin = min(kmin, k);
+            kmax = max(kmax, k);
+        }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), off)));
+        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), off)));
+    }
+    if ((tid & 63) == 0) {
+        sm.u.m.wave_min[tid >> 6] = kmin;
+        sm.u.m.wave_max[tid >> 6] = kmax;
+    }
+    for (int k = tid; k < kFinBins; k += kFinNT) h[k] = 0u;
+    if (tid == 0) {
+        sm.u.m.n_taken = 0;
+        sm.u.m.n_cand = 0;
+        sm.u.m.kstar = 0u;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int w = 0; w < kFinNT / 64; ++w) {
+        kmin = min(kmin, sm.u.m.wave_min[w]);
+        kmax = max(kmax, sm.u.m.wave_max[w]);
+    }
+    const uint32_t span = kmax - kmin;
+    const int shift = span < kFinBins ? 0 : 32 - __clz(static_cast<int>(span >> kFinBits));
+    auto bin_of = [&](uint64_t x) { return (static_cast<uint32_t>(x >> 32) - kmin) >> shift; };
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+        if (tid + kFinNT * i < n) atomicAdd(&h[bin_of(e[i])], 1u);
+    lds_barrier();
+    find_threshold_bin<kFinNT>(h, kFinBins, keep, sm.u.m.wave_tot, &sm.u.m.sh_bin, &sm.u.m.sh_above);
+    const uint32_t tbin = sm.u.m.sh_bin;
+    const int above = sm.u.m.sh_above;
+    const int inbin = static_cast<int>(h[tbin]);
+    if (inbin > kDecCap) return false;                    // uniform
+    {
+        // keys above the cut bin are taken; the cut bin's members go to cand
+        // (positions by ballot and lane count: one LDS atomic per wave and
+        // pass, not one per entry on a single counter)
+        uint64_t* lc = sm.u.m.cand;
+        uint64_t m_up[P], m_in[P];
+        int n_up = 0, n_in = 0;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const bool ok = tid + kFinNT * i < n;
+            const uint32_t d1 = bin_of(e[i]);
+            m_up[i] = __ballot(ok && d1 > tbin);
+            m_in[i] = __ballot(ok && d1 == tbin);
+            n_up += __popcll(m_up[i]);
+            n_in += __popcll(m_in[i]);
+        }
+        int b_up = 0, b_in = 0;
+        if ((tid & 63) == 0) {
+            b_up = n_up ? atomicAdd(&sm.u.m.n_taken, n_up) : 0;
+            b_in = n_in ? atomicAdd(&sm.u.m.n_cand, n_in) : 0;
+        }
+        b_up = __shfl(b_up, 0);
+        b_in = __shfl(b_in, 0);
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int lane = tid & 63;
+            if ((m_up[i] >> lane) & 1ull)
+                chosen[b_up + lanes_below(m_up[i])] = static_cast<int32_t>(~static_cast<uint32_t>(e[i]));
+            if ((m_in[i] >> lane) & 1ull) lc[b_in + lanes_below(m_in[i])] = e[i];
+            b_up += __popcll(m_up[i]);
+            b_in += __popcll(m_in[i]);
+        }
+        lds_barrier();
+        const int remaining = keep - above;
+        if (inbin <= kRankMax) {
+            rank_cut<kFinNT>(lc, inbin, remaining, chosen + above, &sm.u.m.kstar);
+        } else {
+            // many members (tie floods): sorted, the first `remaining` taken
+            const int np2 = next_pow2(inbin);
+            for (int k = inbin + tid; k < np2; k += kFinNT) lc[k] = 0ull;
+            lds_barrier();
+            bitonic_sort<kFinNT, uint64_t, true>(lc, np2);
+            for (int k = tid; k < remaining; k += kFinNT)
+                chosen[above + k] = static_cast<int32_t>(~static_cast<uint32_t>(lc[k]));
+            if (tid == 0) sm.u.m.kstar = static_cast<uint32_t>(lc[remaining - 1] >> 32);
+        }
+        lds_barrier();
+    }
+    return true;
+}
+
+// A row whose list missed part of its selection (some scan wave held more of
+// it than it listed: scores far from random order, e.g. a run of recent
+// blocks that all score high): the list's own cut kl (its keep-th largest key)
+// is at most the row's, so every entry of the row's selection has a key >= kl.
+// One pass over the stored row collects those entries into cand; when they fit,
+// the top `keep` of them by (key, ~j) go to chosen and the row is decided (true);
+// otherwise (more than kDecCap keys >= kl: tie floods) false.
+__device__ __forceinline__ bool recover_from_row(const float* __restrict__ row, int o, int keep, FinalizeSmem& sm) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const uint32_t kl = sm.u.m.kstar;
+    uint64_t* lc = sm.u.m.cand;
+    lds_barrier();                                        // every thread has read kstar
+    if (tid == 0) sm.u.m.n_cand = 0;
+    lds_barrier();
+    constexpr int kIn = 8;                                // float4 loads in flight per thread
+    for (int j0 = 4 * tid; j0 < o; j0 += 4 * kFinNT * kIn) {
+        float4 v[kIn];
+#pragma unroll
+        for (int u = 0; u < kIn; ++u) {
+            const int j = j0 + 4 * kFinNT * u;          // rows are padded to a multiple of 4 floats
+            v[u] = j < o ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        // this lane's keys >= kl among its 4 kIn values, then one LDS
+        // reservation per wave: the lane's count (<= 32) by its 6 bits, each
+        // a ballot, so the lane's offset is a sum of shifted lane counts
+        auto val = [&](int u, int e) { return e == 0 ? v[u].x : e == 1 ? v[u].y : e == 2 ? v[u].z : v[u].w; };
+        uint32_t pass = 0u;                               // bit 4u + e: value e of load u passes
+#pragma unroll
+        for (int u = 0; u < kIn; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j0 + 4 * kFinNT * u + e < o && score_key(val(u, e)) >= kl) pass |= 1u << (4 * u + e);
+        const int my = __popc(pass);
+        int off = 0, tot = 0;
+#pragma unroll
+        for (int bit = 0; bit < 6; ++bit) {
+            const uint64_t m = __ballot((my >> bit) & 1);
+            off += lanes_below(m) << bit;
+            tot += __popcll(m) << bit;
+        }
+        if (tot != 0) {                                   // wave-uniform
+            int wb = 0;
+            if (lane == 0) wb = atomicAdd(&sm.u.m.n_cand, tot);
+            int pos = __shfl(wb, 0) + off;
+#pragma unroll
+            for (int u = 0; u < kIn; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if ((pass >> (4 * u + e)) & 1u) {
+                        const uint32_t j = static_cast<uint32_t>(j0 + 4 * kFinNT * u + e);
+                        if (pos < kDecCap) lc[pos] = (static_cast<uint64_t>(score_key(val(u, e))) << 32) | ~j;
+                        ++pos;
+                    }
+        }
+    }
+    lds_barrier();
+    const int n = sm.u.m.n_cand;
+    if (n > kDecCap) return false;                        // uniform
+    constexpr int kP = kDecCap / kFinNT;
+    uint64_t e[kP];
+#pragma unroll
+    for (int i = 0; i < kP; ++i) e[i] = tid + kFinNT * i < n ? lc[tid + kFinNT * i] : 0ull;
+    lds_barrier();                                        // cand and its count are reused below
+    return take_top<kP>(e, n, keep, sm);
+}
+
 template <int kPer>
 __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __restrict__ scores, int64_t ss,
                                                                  int64_t sld, Positions pos, int budget, int tq,
@@ -458,108 +632,18 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
     const int n = static_cast<int>(ctrl[kNList]);
     const uint32_t max_t = ctrl[kMaxT];
     const bool listed = ctrl[kOverflow] == 0u && n <= kPer * kFinNT && n >= keep;
-    uint32_t* h = sm.u.m.h;
     int32_t* chosen = sm.u.m.chosen;
-    bool exact = listed;
+    bool exact = false;
+    bool cut_known = false;                               // sm.u.m.kstar holds the list's own cut
     if (listed) {
-        // one radix level over the listed keys' own range [kmin, kmax]: bin =
-        // (key - kmin) >> shift < 4096 (the listed keys all sit in the tail, so
-        // the top key bits would crowd them into a few bins and serialize the
-        // LDS atomics)
-        uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (tid + kFinNT * i < n) {
-                const uint32_t k = static_cast<uint32_t>(e[i] >> 32);
-                kmin = min(kmin, k);
-                kmax = max(kmax, k);
-            }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), off)));
-            kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), off)));
-        }
-        if ((tid & 63) == 0) {
-            sm.u.m.wave_min[tid >> 6] = kmin;
-            sm.u.m.wave_max[tid >> 6] = kmax;
-        }
-        for (int k = tid; k < kFinBins; k += kFinNT) h[k] = 0u;
-        if (tid == 0) {
-            sm.u.m.n_taken = 0;
-            sm.u.m.n_cand = 0;
-            sm.u.m.kstar = 0u;
-        }
-        lds_barrier();
-#pragma unroll
-        for (int w = 0; w < kFinNT / 64; ++w) {
-            kmin = min(kmin, sm.u.m.wave_min[w]);
-            kmax = max(kmax, sm.u.m.wave_max[w]);
-        }
-        const uint32_t span = kmax - kmin;
-        const int shift = span < kFinBins ? 0 : 32 - __clz(static_cast<int>(span >> kFinBits));
-        auto bin_of = [&](uint64_t x) { return (static_cast<uint32_t>(x >> 32) - kmin) >> shift; };
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (tid + kFinNT * i < n) atomicAdd(&h[bin_of(e[i])], 1u);
-        lds_barrier();
-        find_threshold_bin<kFinNT>(h, kFinBins, keep, sm.u.m.wave_tot, &sm.u.m.sh_bin, &sm.u.m.sh_above);
-        const uint32_t tbin = sm.u.m.sh_bin;
-        const int above = sm.u.m.sh_above;
-        const int inbin = static_cast<int>(h[tbin]);
-        exact = inbin <= kDecCap;
-        if (exact) {
-            // keys above the cut bin are taken; the cut bin's members go to cand
-            // (positions by ballot and lane count: one LDS atomic per wave and
-            // pass, not one per entry on a single counter)
-            uint64_t* lc = sm.u.m.cand;
-            uint64_t m_up[kPer], m_in[kPer];
-            int n_up = 0, n_in = 0;
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const bool ok = tid + kFinNT * i < n;
-                const uint32_t d1 = bin_of(e[i]);
-                m_up[i] = __ballot(ok && d1 > tbin);
-                m_in[i] = __ballot(ok && d1 == tbin);
-                n_up += __popcll(m_up[i]);
-                n_in += __popcll(m_in[i]);
-            }
-            int b_up = 0, b_in = 0;
-            if ((tid & 63) == 0) {
-                b_up = n_up ? atomicAdd(&sm.u.m.n_taken, n_up) : 0;
-                b_in = n_in ? atomicAdd(&sm.u.m.n_cand, n_in) : 0;
-            }
-            b_up = __shfl(b_up, 0);
-            b_in = __shfl(b_in, 0);
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int lane = tid & 63;
-                if ((m_up[i] >> lane) & 1ull)
-                    chosen[b_up + lanes_below(m_up[i])] = static_cast<int32_t>(~static_cast<uint32_t>(e[i]));
-                if ((m_in[i] >> lane) & 1ull) lc[b_in + lanes_below(m_in[i])] = e[i];
-                b_up += __popcll(m_up[i]);
-                b_in += __popcll(m_in[i]);
-            }
-            lds_barrier();
-            const int remaining = keep - above;
-            if (inbin <= kRankMax) {
-                rank_cut<kFinNT>(lc, inbin, remaining, chosen + above, &sm.u.m.kstar);
-            } else {
-                // many members (tie floods): sorted, the first `remaining` taken
-                const int np2 = next_pow2(inbin);
-                for (int k = inbin + tid; k < np2; k += kFinNT) lc[k] = 0ull;
-                lds_barrier();
-                bitonic_sort<kFinNT, uint64_t, true>(lc, np2);
-                for (int k = tid; k < remaining; k += kFinNT)
-                    chosen[above + k] = static_cast<int32_t>(~static_cast<uint32_t>(lc[k]));
-                if (tid == 0) sm.u.m.kstar = static_cast<uint32_t>(lc[remaining - 1] >> 32);
-            }
-            lds_barrier();
-            // every key >= max T is listed: the cut is exact if the cut key reaches max T
-            exact = sm.u.m.kstar >= max_t;
-        }
+        cut_known = take_top<kPer>(e, n, keep, sm);
+        // every key >= max T is listed: the cut is exact if the cut key reaches max T
+        exact = cut_known && sm.u.m.kstar >= max_t;
     }
+    if (!exact && fallback_count != nullptr && tid == 0) atomicAdd(fallback_count, 1u);
+    if (!exact && cut_known)
+        exact = recover_from_row(scores + b * ss + t * sld, o, keep, sm);
     if (!exact) {
-        if (fallback_count != nullptr && tid == 0) atomicAdd(fallback_count, 1u);
         select_row<kFinNT>(scores + b * ss + t * sld, o, keep, budget, out, sm.u.s);
     } else {
         if (o <= 32 * kBitmapWords) {

@@ -96,6 +96,56 @@ FAST_CASES = [("normal", [1048576], 512, 0), ("normal", [1048576, 1048579], 512,
               ("equal", [300000, 300000], 512, 2)]
 
 
+def _boost_recent(q, kbar, pos, n_recent, sigmas):
+    """Raise the scores of each sequence's n_recent most recent blocks by
+    about `sigmas` standard deviations of its scores (the shape of attention
+    that favours the local context), along the sequence's summed query."""
+    qf = q.float().sum(dim=2)[:, 0]                          # [B, 128]: the 4 heads summed
+    kb = kbar.float()
+    for b, p in enumerate(pos):
+        o = p // 4
+        u = qf[b]
+        sd = float(u.norm()) / math.sqrt(512)                 # score spread of N(0, 1/512) block keys
+        kb[b, o - n_recent:o] += (sigmas * sd / float(u.dot(u))) * u
+    return kb.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("pos,budget", [([1048576, 1048576], 512), ([1048576], 2048), ([200000] * 4, 512)])
+def test_index_select_decode_recovers_clustered_selections(pos, budget):
+    """Selections concentrated in the most recent blocks: the scan's waves
+    that hold them list too few, every row leaves the candidate lists, and
+    the one-pass recovery over the stored row must still give the primitive
+    chain's selection."""
+    say(f"index_select_decode clustered B={len(pos)} pos={pos[0]} budget={budget}")
+    B = len(pos)
+    nblk = max(pos) // 4
+    q = _rand((B, 1, 4, 128), 11 + sum(pos), 1 / math.sqrt(128))
+    kbar = _boost_recent(q, _kbar("normal", B, nblk, budget + 3), pos, 3000, 4.0).cuda()
+    q = q.cuda()
+    ld = (nblk + 3) // 4 * 4
+    s_ref = torch.empty((B, 1, ld), device="cuda")
+    sel_ref = torch.empty((B, 1, budget), dtype=torch.int32, device="cuda")
+    qsa.index_scores(q, kbar, pos, s_ref)
+    qsa.select_topk(s_ref, pos, budget, sel_ref)
+    # most of each selection lies in the boosted blocks
+    for b in range(B):
+        o = pos[b] // 4
+        assert int((sel_ref[b, 0] >= o - 3000).sum()) > budget // 2
+    ws = qsa.index_select_workspace(B)
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s_f = torch.empty_like(s_ref)
+    sel_f = torch.empty_like(sel_ref)
+    qsa.set_decode_fallback_counter(counter)
+    try:
+        qsa.index_select_decode(q, kbar, pos, budget, s_f, sel_f, ws)
+        torch.cuda.synchronize()
+    finally:
+        qsa.set_decode_fallback_counter(None)
+    assert torch.equal(sel_f, sel_ref)
+    assert int(counter.item()) == B
+    assert int(ws[:CTRL_BYTES].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("kind,pos,budget,n_exact", FAST_CASES,
                          ids=[f"{k}-{len(p)}x{p[0]}-{b}" for k, p, b, _ in FAST_CASES])
 def test_index_select_decode_stays_on_the_candidate_lists(kind, pos, budget, n_exact):
