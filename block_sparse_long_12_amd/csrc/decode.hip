@@ -55,6 +55,8 @@ struct DecodeWs {
     uint32_t* ctrl;     // [kDecMaxRows][kCtrl]   zero between calls
     uint64_t* list;     // [rows][cap]            key << 32 | ~j, any order
     int cap;            // list entries per row in this call: kListCap, 2 kListCap or 4 kListCap
+    int steps;          // scan geometry: 256 * steps blocks per workgroup,
+    int wg;             // wg workgroups per sequence (4 waves each)
 };
 
 // The lists take max(rows, kListRowsMin) x kListCap entries, so a call with
@@ -72,12 +74,14 @@ static int list_cap_avail(int rows) {
     return c;
 }
 
-static DecodeWs carve(void* ws, int cap) {
+static DecodeWs carve(void* ws, int cap, int steps, int wg) {
     char* p = static_cast<char*>(ws);
     DecodeWs w;
     w.ctrl = reinterpret_cast<uint32_t*>(p);
     w.list = reinterpret_cast<uint64_t*>(p + static_cast<size_t>(kDecMaxRows) * kCtrl * 4);
     w.cap = cap;
+    w.steps = steps;
+    w.wg = wg;
     return w;
 }
 
@@ -539,71 +543,139 @@ __device__ __forceinline__ bool take_top(const uint64_t (&e)[P], int n, int keep
     return true;
 }
 
+constexpr int kIncMax = 32;          // incomplete waves re-read before a whole-row pass is cheaper
+
+// Appends the entries whose `in` is set to sm.u.m.cand: one LDS reservation
+// per wave (a wave-uniform call).
+__device__ __forceinline__ void append_cand(bool in, uint64_t entry, FinalizeSmem& sm) {
+    const uint64_t m = __ballot(in);
+    if (m == 0ull) return;
+    int wb = 0;
+    if ((threadIdx.x & 63) == 0) wb = atomicAdd(&sm.u.m.n_cand, __popcll(m));
+    const int pos = __shfl(wb, 0) + lanes_below(m);
+    if (in && pos < kDecCap) sm.u.m.cand[pos] = entry;
+}
+
 // A row whose list missed part of its selection (some scan wave held more of
-// it than it listed: scores far from random order, e.g. a run of recent
-// blocks that all score high): the list's own cut kl (its keep-th largest key)
-// is at most the row's, so every entry of the row's selection has a key >= kl.
-// One pass over the stored row collects those entries into cand; when they fit,
-// the top `keep` of them by (key, ~j) go to chosen and the row is decided (true);
-// otherwise (more than kDecCap keys >= kl: tie floods) false.
-__device__ __forceinline__ bool recover_from_row(const float* __restrict__ row, int o, int keep, FinalizeSmem& sm) {
+// it than it listed: scores far from random order, such as a run of recent
+// blocks that all score high).  The list's own cut kl (its keep-th largest
+// key) is at most the row's, so the row's selection lies among its keys >= kl;
+// these are collected into sm.u.m.cand and the same radix cut as the list
+// path decides the row (false: it could not, nothing decided).
+//
+// First from the list and the waves: a wave listed every one of its keys
+// >= its threshold T, and its smallest listed key m is >= T, so a wave with
+// m <= kl listed all of its keys >= kl; only the waves with m > kl (a few,
+// when high scores cluster) are re-read from the stored row, for their keys
+// in [kl, m) -- none of them listed.  m comes from the list itself (the wave
+// of an entry follows from its block).  With more than kIncMax such waves,
+// one pass over the whole stored row instead.  More than kDecCap keys >= kl
+// (tie floods): false.
+__device__ __forceinline__ bool recover(int n, const float* __restrict__ row, int o, int keep, const DecodeWs& ws,
+                                        int r, FinalizeSmem& sm) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const uint32_t kl = sm.u.m.kstar;
-    uint64_t* lc = sm.u.m.cand;
+    const uint64_t* __restrict__ list = ws.list + static_cast<int64_t>(r) * ws.cap;
+    const int n_waves = ws.wg * 4;
+    const int R = 256 * ws.steps;
+    uint32_t* wmin = sm.u.m.bm;                           // per wave: its smallest listed key (the bitmap is free here)
+    int* inc = reinterpret_cast<int*>(sm.u.m.h);          // the waves to re-read (the histogram is free here)
+    auto wave_of = [&](int j) { return (j / R) * 4 + ((j % R) >> 6) % 4; };
     lds_barrier();                                        // every thread has read kstar
-    if (tid == 0) sm.u.m.n_cand = 0;
-    lds_barrier();
-    constexpr int kIn = 8;                                // float4 loads in flight per thread
-    for (int j0 = 4 * tid; j0 < o; j0 += 4 * kFinNT * kIn) {
-        float4 v[kIn];
-#pragma unroll
-        for (int u = 0; u < kIn; ++u) {
-            const int j = j0 + 4 * kFinNT * u;          // rows are padded to a multiple of 4 floats
-            v[u] = j < o ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+    bool whole_row = n_waves > kBitmapWords;              // uniform
+    if (!whole_row) {
+        for (int w = tid; w < n_waves; w += kFinNT) wmin[w] = 0xffffffffu;
+        if (tid == 0) {
+            sm.u.m.n_cand = 0;
+            sm.u.m.n_taken = 0;                           // count of waves to re-read
         }
-        // this lane's keys >= kl among its 4 kIn values, then one LDS
-        // reservation per wave: the lane's count (<= 32) by its 6 bits, each
-        // a ballot, so the lane's offset is a sum of shifted lane counts
-        auto val = [&](int u, int e) { return e == 0 ? v[u].x : e == 1 ? v[u].y : e == 2 ? v[u].z : v[u].w; };
-        uint32_t pass = 0u;                               // bit 4u + e: value e of load u passes
-#pragma unroll
-        for (int u = 0; u < kIn; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (j0 + 4 * kFinNT * u + e < o && score_key(val(u, e)) >= kl) pass |= 1u << (4 * u + e);
-        const int my = __popc(pass);
-        int off = 0, tot = 0;
-#pragma unroll
-        for (int bit = 0; bit < 6; ++bit) {
-            const uint64_t m = __ballot((my >> bit) & 1);
-            off += lanes_below(m) << bit;
-            tot += __popcll(m) << bit;
+        lds_barrier();
+        for (int i = tid; i < n; i += kFinNT) {
+            const uint64_t x = list[i];
+            atomicMin(&wmin[wave_of(static_cast<int>(~static_cast<uint32_t>(x)))], static_cast<uint32_t>(x >> 32));
         }
-        if (tot != 0) {                                   // wave-uniform
-            int wb = 0;
-            if (lane == 0) wb = atomicAdd(&sm.u.m.n_cand, tot);
-            int pos = __shfl(wb, 0) + off;
+        lds_barrier();
+        for (int w = tid; w < n_waves; w += kFinNT)
+            if (wmin[w] > kl && (w >> 2) * R + 64 * (w & 3) < o) {   // a wave with blocks below o
+                const int k = atomicAdd(&sm.u.m.n_taken, 1);
+                if (k < kIncMax) inc[k] = w;
+            }
+        lds_barrier();
+        whole_row = sm.u.m.n_taken > kIncMax;             // uniform
+    } else {
+        if (tid == 0) sm.u.m.n_cand = 0;
+        lds_barrier();
+    }
+    if (!whole_row) {
+        for (int i0 = 0; i0 < n; i0 += kFinNT) {          // uniform
+            const uint64_t x = i0 + tid < n ? list[i0 + tid] : 0ull;
+            append_cand(i0 + tid < n && static_cast<uint32_t>(x >> 32) >= kl, x, sm);
+        }
+        const int n_inc = sm.u.m.n_taken;
+        for (int k = 0; k < n_inc; ++k) {                 // uniform
+            const int w = inc[k];
+            const uint32_t T = wmin[w];
+            const int j_w = (w >> 2) * R + 64 * (w & 3);  // the wave's blocks: j_w + 256 st + lane
+            for (int q = tid; q < 64 * ws.steps; q += kFinNT) {
+                const int j = j_w + 256 * (q >> 6) + (q & 63);
+                const uint32_t key = j < o ? score_key(row[j]) : 0u;
+                append_cand(j < o && key >= kl && key < T, (static_cast<uint64_t>(key) << 32) | ~static_cast<uint32_t>(j),
+                            sm);
+            }
+        }
+    } else {
+        constexpr int kIn = 8;                            // float4 loads in flight per thread
+        for (int j0 = 4 * tid; j0 < o; j0 += 4 * kFinNT * kIn) {
+            float4 v[kIn];
+#pragma unroll
+            for (int u = 0; u < kIn; ++u) {
+                const int j = j0 + 4 * kFinNT * u;      // rows are padded to a multiple of 4 floats
+                v[u] = j < o ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            // this lane's keys >= kl among its 4 kIn values, then one LDS
+            // reservation per wave: the lane's count (<= 32) by its 6 bits, each
+            // a ballot, so the lane's offset is a sum of shifted lane counts
+            auto val = [&](int u, int e) { return e == 0 ? v[u].x : e == 1 ? v[u].y : e == 2 ? v[u].z : v[u].w; };
+            uint32_t pass = 0u;                           // bit 4u + e: value e of load u passes
 #pragma unroll
             for (int u = 0; u < kIn; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if ((pass >> (4 * u + e)) & 1u) {
-                        const uint32_t j = static_cast<uint32_t>(j0 + 4 * kFinNT * u + e);
-                        if (pos < kDecCap) lc[pos] = (static_cast<uint64_t>(score_key(val(u, e))) << 32) | ~j;
-                        ++pos;
-                    }
+                    if (j0 + 4 * kFinNT * u + e < o && score_key(val(u, e)) >= kl) pass |= 1u << (4 * u + e);
+            const int my = __popc(pass);
+            int off = 0, tot = 0;
+#pragma unroll
+            for (int bit = 0; bit < 6; ++bit) {
+                const uint64_t m = __ballot((my >> bit) & 1);
+                off += lanes_below(m) << bit;
+                tot += __popcll(m) << bit;
+            }
+            if (tot != 0) {                               // wave-uniform
+                int wb = 0;
+                if (lane == 0) wb = atomicAdd(&sm.u.m.n_cand, tot);
+                int pos = __shfl(wb, 0) + off;
+#pragma unroll
+                for (int u = 0; u < kIn; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if ((pass >> (4 * u + e)) & 1u) {
+                            const uint32_t j = static_cast<uint32_t>(j0 + 4 * kFinNT * u + e);
+                            if (pos < kDecCap) sm.u.m.cand[pos] = (static_cast<uint64_t>(score_key(val(u, e))) << 32) | ~j;
+                            ++pos;
+                        }
+            }
         }
     }
     lds_barrier();
-    const int n = sm.u.m.n_cand;
-    if (n > kDecCap) return false;                        // uniform
+    const int n2 = sm.u.m.n_cand;
+    if (n2 > kDecCap) return false;                       // uniform
     constexpr int kP = kDecCap / kFinNT;
-    uint64_t e[kP];
+    uint64_t e2[kP];
 #pragma unroll
-    for (int i = 0; i < kP; ++i) e[i] = tid + kFinNT * i < n ? lc[tid + kFinNT * i] : 0ull;
+    for (int i = 0; i < kP; ++i) e2[i] = tid + kFinNT * i < n2 ? sm.u.m.cand[tid + kFinNT * i] : 0ull;
     lds_barrier();                                        // cand and its count are reused below
-    return take_top<kP>(e, n, keep, sm);
+    return take_top<kP>(e2, n2, keep, sm);
 }
 
 template <int kPer>
@@ -641,8 +713,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
         exact = cut_known && sm.u.m.kstar >= max_t;
     }
     if (!exact && fallback_count != nullptr && tid == 0) atomicAdd(fallback_count, 1u);
-    if (!exact && cut_known)
-        exact = recover_from_row(scores + b * ss + t * sld, o, keep, sm);
+    if (__builtin_expect(!exact && cut_known, 0)) exact = recover(n, scores + b * ss + t * sld, o, keep, ws, r, sm);
     if (!exact) {
         select_row<kFinNT>(scores + b * ss + t * sld, o, keep, budget, out, sm.u.s);
     } else {
@@ -758,7 +829,7 @@ hipError_t launch_decode_index_select(const uint16_t* q_idx, int64_t qs, const u
     scan_plan(batch, tq, o_max, min(budget - 1, o_max), &steps, &cap);
     const int wg_scan = max(1, (o_max + 256 * steps - 1) / (256 * steps));
 
-    const DecodeWs w = carve(ws, cap);
+    const DecodeWs w = carve(ws, cap, steps, wg_scan);
     AppendArgs ap{};
     qsa_rope_t rope{1.0e7, 1.0, 0};
     if (append != nullptr) {
