@@ -37,6 +37,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -415,11 +416,18 @@ class NullTimer:
         return _Ctx()
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
 def source_hash(*names) -> str:
+    """Hash of kernel sources with comments removed and blank space collapsed,
+    so that a counter record stays attached to the code it measured."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "block_sparse_long_12_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "block_sparse_long_12_amd", "csrc", n), encoding="utf-8") as f:
+            text = f.read()
+        code = _CODE_TOKENS.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,7 +15,7 @@
 //                          and keeps the scores in LDS -- nothing else in the
 //                          loop.  Then each wave, alone, finds a key T that at
 //                          least K of its own blocks of every row reach (K a
-//                          few times its expected share of the selection) by a
+//                          Poisson bound on its share of the selection) by a
 //                          search over the key bits with ballots, and lists
 //                          every candidate whose key is >= T; the workgroup
 //                          writes its scores to global memory in full lines and
@@ -26,10 +26,15 @@
 //                          range, then the cut bin's members ranked), valid
 //                          because every key >= max T is listed, so the list's
 //                          cut is the row's when the cut key is >= max T;
-//                          otherwise (or when a list overflows) the full radix
-//                          select on the stored row.  Emits ascending through
-//                          a block bitmap and leaves the row's control words
-//                          zeroed.
+//                          otherwise the list's cut is still a lower bound and
+//                          the row is recovered from the listed keys above it
+//                          plus the stored scores of the few waves that can
+//                          hold more (or of the whole row); with tie floods or
+//                          an overflowed list, the full radix select on the
+//                          stored row.  Emits ascending through a block bitmap
+//                          and leaves the row's control words zeroed.
+// The host plans each call (scan_plan): blocks per workgroup and the list
+// capacity per row, from the batch, tq, context and budget.
 //
 // Workspace: control words for the largest possible row count at offset 0
 // (zero before the first call, left zero by every call, so one workspace
