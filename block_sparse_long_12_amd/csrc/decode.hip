@@ -781,6 +781,11 @@ static void scan_plan(int batch, int tq, int o, int keep, int* steps, int* cap) 
     const int64_t groups = static_cast<int64_t>(batch) * ((o + 255) / 256);
     const int s0 = groups >= 8 * 512 ? 8 : groups >= 4 * 512 ? 4 : groups >= 2 * 512 ? 2 : 1;
     const int s_max = tq <= 2 ? 32 : 16;
+    if (keep <= 0 || keep >= o) {                         // trivial rows list nothing
+        *steps = s0;
+        *cap = kListCap;
+        return;
+    }
     const int avail = list_cap_avail(batch * tq);
     auto wgs = [&](int st) { return static_cast<int64_t>(batch) * ((o + 256 * st - 1) / (256 * st)); };
     // the longest steps that give every CU a workgroup (two with several
@@ -793,7 +798,6 @@ static void scan_plan(int batch, int tq, int o, int keep, int* steps, int* cap) 
     // the smallest capacity that holds the expected list (per-wave spread
     // about sqrt(listed - kw + 1)), or 0
     auto cap_for = [&](int st) {
-        if (keep <= 0 || keep >= o) return kListCap;         // trivial rows list nothing
         const int n_w = min(64 * st, o);
         const int kw = wave_keep(keep, o, n_w);
         const double per = wave_listed(kw, n_w);

@@ -17,12 +17,17 @@
 // memory path once per 64 rows.  Three modes share the machinery:
 //   scores  -- store every score (4 float4 per lane per step), three LDS
 //              buffers so loads run two steps ahead of the stores;
-//   sample  -- the same over a fixed sample of blocks (16 evenly spread runs
-//              of 256), stored compactly; feeds the per-row thresholds;
+//   sample  -- the same over a fixed sample of blocks (256 evenly spread
+//              runs of 16), stored compactly; feeds the per-row thresholds;
 //   collect -- no score matrix: scores at or above the row's threshold are
 //              appended to per-wave LDS lists and, at the end, to the row's
 //              global candidate list (one atomic per row and workgroup) as
-//              (ordered key, ~block) pairs.
+//              (ordered key, ~block) pairs.  A workgroup whose LDS lists
+//              overflow (candidates dense in a stretch of blocks: high scores
+//              that cluster) hands nothing off and marks itself;
+//   collect retry -- run after collect with the same grid: only the marked
+//              workgroups score their blocks again, and a candidate that finds
+//              its wave's list full goes straight to its row's global list.
 // Causality: a workgroup stops at the last block its last row sees; collect
 // also drops each row's blocks at or past its own block.
 #include "index_common.h"
@@ -34,7 +39,7 @@ constexpr int kTokTile = 16;    // query rows per wave
 constexpr int kWgTok = 64;      // query rows per workgroup
 constexpr int kColStep = 64;    // blocks per step
 
-enum { kModeScores = 0, kModeSample = 1, kModeCollect = 2 };
+enum { kModeScores = 0, kModeSample = 1, kModeCollect = 2, kModeCollectRetry = 3 };
 
 // One step of kbar in LDS: block jb of the step is row jb (256 bytes); the
 // 16-byte chunk c of row r is stored at position c ^ (r % 16), so the 16
@@ -52,17 +57,19 @@ __shared__ int lrow[kWgTok];
 __shared__ int lrow_base[kWgTok];
 __shared__ int lwcnt[4];
 
-// Block of column jv: itself, or in sample mode run jv / 256 of kSampleRuns
-// runs of 256 blocks spread evenly over [0, omin) (with paged block keys each
-// run starts on a multiple of 16 blocks, so a 16-block tile stays inside one
-// page).
+// Block of column jv: itself, or in sample mode run jv / 16 of kSampleRuns
+// runs of 16 blocks spread evenly over [0, omin) (with paged block keys each
+// run starts on a multiple of 16 blocks, so the run's tile stays inside one
+// page).  Short runs spread wide keep the sample representative when high
+// scores cluster in a stretch of blocks (a run of 256 inside such a stretch
+// over-weighted it 16-fold).
 template <int kMode, bool kPaged = false>
 __device__ __forceinline__ int column_block(int jv, int omin) {
     if (kMode == kModeSample) {
-        const int run = jv >> 8;
-        int base = static_cast<int>(static_cast<int64_t>(run) * (omin - 256) / (kSampleRuns - 1));
+        const int run = jv / kSampleRunLen;
+        int base = static_cast<int>(static_cast<int64_t>(run) * (omin - kSampleRunLen) / (kSampleRuns - 1));
         if (kPaged) base &= ~15;
-        return base + (jv & 255);
+        return base + jv % kSampleRunLen;
     }
     return jv;
 }
@@ -255,10 +262,11 @@ __device__ __forceinline__ uint32_t passed_key(uint32_t u) {
 // mask; a passing slot costs its position (two mbcnt), the packed index (one
 // add from the step's per-lane base) and the LDS write.  While the list has
 // room for every lane of the slot (a scalar test) no lane checks its
-// position.
-template <bool kLimit>
+// position.  With kSpill (the retry pass) a candidate that finds the list
+// full goes to its row's global list (one atomic on its count each).
+template <bool kLimit, bool kSpill>
 __device__ __forceinline__ void collect_scan(const f32x4_t (&acc)[4], int jl, int lim, float tau, uint32_t base,
-                                             uint64_t* seg, int& cnt) {
+                                             uint64_t* seg, int& cnt, uint64_t* row_list, int* row_cnt) {
     constexpr int kWaveCap = kCollectCap / 4;
     int c = __builtin_amdgcn_readfirstlane(cnt);
     bool q[16];
@@ -281,16 +289,24 @@ __device__ __forceinline__ void collect_scan(const f32x4_t (&acc)[4], int jl, in
                 const int pos = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
                     static_cast<uint32_t>(m[e] >> 32),
                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m[e]), static_cast<uint32_t>(c0))));
-                if (c0 + n <= kWaveCap || pos < kWaveCap)
+                if (c0 + n <= kWaveCap || pos < kWaveCap) {
                     seg[pos] = (static_cast<uint64_t>(__float_as_uint(v)) << 32) | (base + static_cast<uint32_t>(off));
+                } else if constexpr (kSpill) {
+                    const int gp = atomicAdd(row_cnt, 1);
+                    if (gp < kRowCap)
+                        row_list[gp] = (static_cast<uint64_t>(passed_key(__float_as_uint(v))) << 32) |
+                                       static_cast<uint32_t>(~(jl + off));
+                }
             }
         }
     }
     cnt = c;
 }
 
+template <bool kSpill>
 __device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf)[kIdxSlices], int j0, int lim,
-                                             float tau, int row_local, int j_begin, uint64_t* seg, int& cnt) {
+                                             float tau, int row_local, int j_begin, uint64_t* seg, int& cnt,
+                                             uint64_t* row_list, int* row_cnt) {
     f32x4_t acc[4];
     step_scores<1>(t, qf, acc);
     const int lane = threadIdx.x & 63;
@@ -298,9 +314,9 @@ __device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf
     const uint32_t base = static_cast<uint32_t>((row_local << 16) | (jl - j_begin));
     // the block limit matters only in the steps that reach some lane's limit
     if (__all(j0 + kColStep <= lim))
-        collect_scan<false>(acc, jl, lim, tau, base, seg, cnt);
+        collect_scan<false, kSpill>(acc, jl, lim, tau, base, seg, cnt, row_list, row_cnt);
     else
-        collect_scan<true>(acc, jl, lim, tau, base, seg, cnt);
+        collect_scan<true, kSpill>(acc, jl, lim, tau, base, seg, cnt, row_list, row_cnt);
 }
 
 template <int kMode, bool kPaged>
@@ -333,6 +349,7 @@ __global__ __launch_bounds__(256) void index_kernel(
     const int j_begin = cc * cols_per_chunk;
     const int j_end = min(j_begin + cols_per_chunk, jmax);
     if (j_begin >= j_end) return;                         // whole workgroup
+    if (kMode == kModeCollectRetry && col.wg_flag[wg] == 0) return;   // its lists fit in the first pass
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -348,10 +365,13 @@ __global__ __launch_bounds__(256) void index_kernel(
     const int n_steps = (j_end - j_begin + kColStep - 1) / kColStep;
     const DmaOffsets dof = dma_offsets();
 
-    if constexpr (kMode == kModeCollect) {
+    if constexpr (kMode == kModeCollect || kMode == kModeCollectRetry) {
+        constexpr bool kSpill = kMode == kModeCollectRetry;
         const int tok = t0 + (lane & 15);
         const int64_t row = static_cast<int64_t>(b) * tq + tok;
         const float tau = tok < tq ? col.tau[row] : __uint_as_float(0x7fc00000u);
+        uint64_t* row_list = col.list + row * kRowCap;     // this lane's row (used only when tok < tq)
+        int* row_cnt = col.row_cnt + row;
         const int lim = min((pos0.p[b] + tok) / kBlock, j_end);
         if (threadIdx.x < kWgTok) lrow[threadIdx.x] = 0;
         uint64_t* seg = lcand + wave * (kCollectCap / 4);    // this wave's list
@@ -364,23 +384,28 @@ __global__ __launch_bounds__(256) void index_kernel(
         for (int s = 0; s < n_steps; s += 2) {
             wait_and_meet<0>();
             stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 1), j_end, omin, kp, dof, tB);
-            if (has_rows) collect_step(tA, qf, j_begin + kColStep * s, lim, tau, tok - t_wg, j_begin, seg, cnt);
+            if (has_rows)
+                collect_step<kSpill>(tA, qf, j_begin + kColStep * s, lim, tau, tok - t_wg, j_begin, seg, cnt, row_list,
+                                     row_cnt);
             if (s + 1 >= n_steps) break;
             wait_and_meet<0>();
             stage_dma<kMode, kPaged>(kb, j_begin + kColStep * (s + 2), j_end, omin, kp, dof, tA);
-            if (has_rows) collect_step(tB, qf, j_begin + kColStep * (s + 1), lim, tau, tok - t_wg, j_begin, seg, cnt);
+            if (has_rows)
+                collect_step<kSpill>(tB, qf, j_begin + kColStep * (s + 1), lim, tau, tok - t_wg, j_begin, seg, cnt,
+                                     row_list, row_cnt);
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);               // no load into LDS outlives the workgroup
         __syncthreads();
-        // hand the lists to the rows: count per row, one global reservation per row
-        if (lane == 0) lwcnt[wave] = cnt;
+        // hand the lists to the rows: count per row, one global reservation
+        // per row (in the retry pass, what did not fit went to the rows already)
+        if (lane == 0) lwcnt[wave] = kSpill ? min(cnt, kCollectCap / 4) : cnt;
         __syncthreads();
-        bool overflow = false;
+        if constexpr (!kSpill) {
+            bool overflow = false;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) overflow |= lwcnt[w] > kCollectCap / 4;
-        if (overflow) {                                   // a list overflowed: every row of the tile falls back
-            if (threadIdx.x < n_tok_wg) atomicAdd(&col.row_cnt[static_cast<int64_t>(b) * tq + t_wg + threadIdx.x], kRowCap + 1);
-            return;
+            for (int w = 0; w < 4; ++w) overflow |= lwcnt[w] > kCollectCap / 4;
+            if (threadIdx.x == 0) col.wg_flag[wg] = overflow ? 1 : 0;
+            if (overflow) return;                         // the retry pass redoes this workgroup
         }
         int slot[kCollectCap / 256];
 #pragma unroll
@@ -491,8 +516,12 @@ hipError_t launch_index_sample(const uint16_t* q_idx, int64_t qs, const uint16_t
 hipError_t launch_index_collect(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,
                                 const Positions& pos0, int batch, int tq, int max_cols, const IndexCollect& col,
                                 const PageMap* pm, hipStream_t stream) {
-    return launch_mode<kModeCollect>(q_idx, qs, kbar, kbs, pos0, batch, tq, max_visible_block(pos0, batch, tq),
-                                     max_cols, nullptr, 0, 0, nullptr, col, pm, stream);
+    const int jmax = max_visible_block(pos0, batch, tq);
+    hipError_t e = launch_mode<kModeCollect>(q_idx, qs, kbar, kbs, pos0, batch, tq, jmax, max_cols, nullptr, 0, 0,
+                                             nullptr, col, pm, stream);
+    if (e != hipSuccess) return e;
+    return launch_mode<kModeCollectRetry>(q_idx, qs, kbar, kbs, pos0, batch, tq, jmax, max_cols, nullptr, 0, 0,
+                                          nullptr, col, pm, stream);
 }
 
 }  // namespace qsa

@@ -3,13 +3,15 @@
 // GDN + QSA": blocks are scored and the most relevant ones kept; model card:
 // budget 512 blocks), without writing and re-reading the score matrix.
 //
-//  1. sample      the indexer scores a fixed sample of 4096 blocks per row (16
-//                 runs of 256 spread over the blocks every row of the chunk
+//  1. sample      the indexer scores a fixed sample of 4096 blocks per row (256
+//                 runs of 16 spread over the blocks every row of the chunk
 //                 sees);
 //  2. threshold   per row, a key threshold from the sample whose expected
 //                 count in the whole row is threshold_target(keep);
 //  3. collect     the indexer scores every block; scores at or above the
-//                 row's threshold go to the row's candidate list;
+//                 row's threshold go to the row's candidate list (a second
+//                 launch redoes the workgroups whose LDS lists overflowed,
+//                 sending what does not fit straight to the rows' lists);
 //  4. finalize    per row: if the list holds at least `keep` entries and did
 //                 not overflow, it contains the row's exact top `keep`, which
 //                 an exact radix select finishes; otherwise the row is flagged;
@@ -160,6 +162,9 @@ hipError_t launch_prefill_index_select(const uint16_t* q_idx, int64_t qs, const 
     col.tau = w.tau;
     col.row_cnt = w.row_cnt;
     col.list = w.list;
+    // one byte per collect workgroup, over the sample (read by the threshold
+    // kernel before the collect starts; rows x 16 KiB hold any grid's flags)
+    col.wg_flag = reinterpret_cast<uint8_t*>(w.sample);
     e = launch_index_collect(q_idx, qs, kbar, kbs, pos0, batch, tq, static_cast<int>(cols), col, pm, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_finalize_kernel, dim3(rows), dim3(kFinNT), 0, stream, pos0, tq, budget, w, sel, sels);

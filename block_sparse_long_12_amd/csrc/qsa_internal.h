@@ -129,8 +129,9 @@ hipError_t launch_select(const float* scores, int64_t ld, int64_t ss, const Posi
                          hipStream_t stream);
 
 // ---- fused prefill index-select (threshold from a sample, candidate lists) ----
-constexpr int kSampleRuns = 16;                   // sample runs of 256 blocks per sequence
-constexpr int kSampleCols = kSampleRuns * 256;    // sampled scores per row
+constexpr int kSampleRuns = 256;                  // sample runs per sequence
+constexpr int kSampleRunLen = 16;                 // blocks per run: one 16-block tile
+constexpr int kSampleCols = kSampleRuns * kSampleRunLen;    // sampled scores per row
 constexpr int kCollectCap = 2048;                 // candidates listed in LDS per workgroup
 constexpr int kRowCap = 4096;                     // candidates kept per row
 
@@ -139,6 +140,7 @@ struct IndexCollect {
     int* row_cnt;               // [rows] candidates appended (zero before the launch)
     uint64_t* list;             // [rows][kRowCap] key << 32 | ~j
     const int* n_flagged;       // scores mode with row flags: nothing to do while *n_flagged == 0
+    uint8_t* wg_flag;           // collect: per workgroup, its LDS lists overflowed (the retry pass redoes it)
 };
 
 hipError_t launch_index_sample(const uint16_t* q_idx, int64_t qs, const uint16_t* kbar, int64_t kbs,

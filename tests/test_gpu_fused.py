@@ -255,12 +255,12 @@ def test_decode_step_matches_primitives(ctx, budget, B):
 
 # ---------------------------------------------------------------- prefill index-select
 
-SAMPLE_RUNS = 16     # the fused prefill index-select samples this many runs of 256 blocks per row
+SAMPLE_RUNS, RUN_LEN = 256, 16    # the fused prefill index-select samples 256 runs of 16 blocks per row
 
 
 def _run_starts(omin):
-    """First block of each sampled run of 256 blocks (spread evenly over [0, omin))."""
-    return [r * (omin - 256) // (SAMPLE_RUNS - 1) for r in range(SAMPLE_RUNS)]
+    """First block of each sampled run (spread evenly over [0, omin))."""
+    return [r * (omin - RUN_LEN) // (SAMPLE_RUNS - 1) for r in range(SAMPLE_RUNS)]
 
 
 def _prefill_kbar(kind, B, nblk, seed, pos0):
@@ -270,7 +270,7 @@ def _prefill_kbar(kind, B, nblk, seed, pos0):
         kb = _rand((B, nblk, 128), seed, 1 / math.sqrt(512)) * 0.01
         for b in range(B):
             for s in _run_starts(pos0[b] // 4):
-                kb[b, s:s + 256] = kb[b, s:s + 256] * 100 + 0.05
+                kb[b, s:s + RUN_LEN] = kb[b, s:s + RUN_LEN] * 100 + 0.05
         return kb.to(torch.bfloat16)
     raise ValueError(kind)
 
@@ -317,6 +317,40 @@ def test_index_select_prefill_matches_primitives(kind, pos0, tq, budget, path):
                 assert n_flagged == 0
             elif path == "fallback":
                 assert n_flagged > 0
+
+
+def test_index_select_prefill_clustered_scores_stay_fused():
+    """Every query shares a component along which the 3000 blocks before the
+    chunk score about 4 standard deviations high (most selections then lie
+    there, as with attention that favours the recent context): the sample of
+    short runs spread over the blocks still sets thresholds that hold the
+    selections, so no row takes the exact fallback."""
+    pos0, tq, budget = [120000], 512, 512
+    say(f"index_select_prefill clustered pos0={pos0} tq={tq} budget={budget}")
+    B = len(pos0)
+    nblk = (pos0[0] + tq - 1) // 4 + 1
+    q = _rand((B, tq, 4, 128), 21, 1 / math.sqrt(128)).float()
+    g = torch.Generator().manual_seed(22)
+    c = torch.randn(128, generator=g)
+    qn = float(q.sum(dim=2)[0].norm(dim=-1).mean())
+    c = c / c.norm() * (0.5 * qn)
+    q[:, :, 0, :] += c
+    kb = _kbar("normal", B, nblk, 23).float()
+    o = pos0[0] // 4
+    kb[0, o - 3000:o] += (4.0 * qn / math.sqrt(512) / float(c.dot(c))) * c
+    q, kbar = q.to(torch.bfloat16).cuda(), kb.to(torch.bfloat16).cuda()
+    ld = (nblk + 3) // 4 * 4
+    s_ref = torch.empty((B, tq, ld), device="cuda")
+    sel_ref = torch.empty((B, tq, budget), dtype=torch.int32, device="cuda")
+    qsa.index_scores(q, kbar, pos0, s_ref)
+    qsa.select_topk(s_ref, pos0, budget, sel_ref)
+    assert float((sel_ref >= o - 3000).float().mean()) > 0.5     # the cluster holds most selections
+    ws = qsa.index_select_prefill_workspace(B, tq)
+    sel = torch.full((B, tq, budget), -7, dtype=torch.int32, device="cuda")
+    qsa.index_select_prefill(q, kbar, pos0, budget, torch.empty((B, tq, ld), device="cuda"), sel, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel_ref)
+    assert int(ws[:4].view(torch.int32)[0]) == 0                 # rows on the exact fallback
 
 
 def test_index_select_prefill_workspace_reuse_across_shapes():
