@@ -319,13 +319,18 @@ __device__ __forceinline__ void collect_step(const KTile& t, const bf16x8_t (&qf
         collect_scan<true, kSpill>(acc, jl, lim, tau, base, seg, cnt, row_list, row_cnt);
 }
 
-// One tile of the grid: 64 query rows of sequence b against one column chunk.
 template <int kMode, bool kPaged>
-__device__ __forceinline__ void index_tile(
-    int64_t wg, const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
-    const Positions& pos0, int tq, int n_wt, int n_cc, int cols_per_chunk,
-    float* __restrict__ scores, int64_t ld, int64_t ss, const int* __restrict__ flags, const IndexCollect& col,
-    const PageMap& pm) {
+__global__ __launch_bounds__(256) void index_kernel(
+    const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
+    Positions pos0, int tq, int n_wt, int n_cc, int cols_per_chunk, int64_t n_wg,
+    float* __restrict__ scores, int64_t ld, int64_t ss, const int* __restrict__ flags, IndexCollect col,
+    PageMap pm) {
+    // workgroups are dealt to the 8 XCDs round-robin; renumber them so each
+    // XCD works through one contiguous range, and the row tiles that share a
+    // column chunk of kbar share that XCD's L2
+    const int64_t per_xcd = gridDim.x / 8;                // the grid is a multiple of 8
+    const int64_t wg = static_cast<int64_t>(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (wg >= n_wg) return;                               // whole workgroup
     const int wt = static_cast<int>(wg % n_wt);
     const int64_t rest = wg / n_wt;
     const int cc = static_cast<int>(rest % n_cc);
@@ -334,6 +339,7 @@ __device__ __forceinline__ void index_tile(
     const int t_wg = wt * kWgTok;
     const int n_tok_wg = min(kWgTok, tq - t_wg);
     if (kMode == kModeScores && flags != nullptr) {       // only the row tiles holding a flagged row
+        if (col.n_flagged != nullptr && *col.n_flagged == 0) return;
         const int tid = threadIdx.x;
         const bool mine = tid < n_tok_wg && flags[static_cast<int64_t>(b) * tq + t_wg + tid] != 0;
         if (!__syncthreads_or(mine)) return;
@@ -450,40 +456,6 @@ __device__ __forceinline__ void index_tile(
     }
 }
 
-// Workgroups are dealt to the 8 XCDs round-robin; renumber them so each XCD
-// works through one contiguous range, and the row tiles that share a column
-// chunk of kbar share that XCD's L2.
-template <int kMode, bool kPaged>
-__global__ __launch_bounds__(256) void index_kernel(
-    const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
-    Positions pos0, int tq, int n_wt, int n_cc, int cols_per_chunk, int64_t n_wg,
-    float* __restrict__ scores, int64_t ld, int64_t ss, IndexCollect col, PageMap pm) {
-    const int64_t per_xcd = gridDim.x / 8;                // the grid is a multiple of 8
-    const int64_t wg = static_cast<int64_t>(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (wg >= n_wg) return;                               // whole workgroup
-    index_tile<kMode, kPaged>(wg, q_idx, qs, kbar, kbs, pos0, tq, n_wt, n_cc, cols_per_chunk, scores, ld, ss,
-                              nullptr, col, pm);
-}
-
-// Scores of the row tiles holding a flagged row (the fallback of the fused
-// prefill index-select), nothing while *n_flagged is zero.  A small grid
-// walks the tiles: the common case has no flagged row, and a grid of one
-// workgroup per tile would then still cost a round of dispatches for every
-// tile -- long when another stream's kernels hold most of the chip.
-template <bool kPaged>
-__global__ __launch_bounds__(256) void index_fallback_kernel(
-    const uint16_t* __restrict__ q_idx, int64_t qs, const uint16_t* __restrict__ kbar, int64_t kbs,
-    Positions pos0, int tq, int n_wt, int n_cc, int cols_per_chunk, int64_t n_wg,
-    float* __restrict__ scores, int64_t ld, int64_t ss, const int* __restrict__ flags, IndexCollect col,
-    PageMap pm) {
-    if (col.n_flagged != nullptr && *col.n_flagged == 0) return;
-    for (int64_t wg = blockIdx.x; wg < n_wg; wg += gridDim.x) {      // uniform
-        index_tile<kModeScores, kPaged>(wg, q_idx, qs, kbar, kbs, pos0, tq, n_wt, n_cc, cols_per_chunk, scores, ld,
-                                        ss, flags, col, pm);
-        __syncthreads();                                  // the tile's LDS reads end before the next tile's loads land
-    }
-}
-
 // Grid: batch x column chunks x 64-row tiles, the chunk width a multiple of
 // 64 blocks (at most max_cols) so that a few thousand workgroups fill the chip.
 static void index_grid(int jmax, int batch, int tq, int max_cols, int* n_wt, int* n_cc, int* cols_per_chunk,
@@ -507,24 +479,13 @@ static hipError_t launch_mode(const uint16_t* q_idx, int64_t qs, const uint16_t*
     int n_wt, n_cc, cpc;
     int64_t n_wg;
     index_grid(jmax, batch, tq, max_cols, &n_wt, &n_cc, &cpc, &n_wg);
-    const PageMap pmv = pm != nullptr ? *pm : PageMap{};
-    if (kMode == kModeScores && flags != nullptr) {
-        const unsigned grid = static_cast<unsigned>(n_wg < int64_t{kFallbackGrid} ? n_wg : int64_t{kFallbackGrid});
-        if (pm != nullptr)
-            hipLaunchKernelGGL(index_fallback_kernel<true>, dim3(grid), dim3(256), 0, stream, q_idx, qs, kbar, kbs,
-                               pos0, tq, n_wt, n_cc, cpc, n_wg, scores, ld, ss, flags, col, pmv);
-        else
-            hipLaunchKernelGGL(index_fallback_kernel<false>, dim3(grid), dim3(256), 0, stream, q_idx, qs, kbar, kbs,
-                               pos0, tq, n_wt, n_cc, cpc, n_wg, scores, ld, ss, flags, col, pmv);
-        return hipGetLastError();
-    }
     const unsigned grid = static_cast<unsigned>((n_wg + 7) / 8 * 8);
     if (pm != nullptr)
         hipLaunchKernelGGL((index_kernel<kMode, true>), dim3(grid), dim3(256), 0, stream, q_idx, qs, kbar, kbs,
-                           pos0, tq, n_wt, n_cc, cpc, n_wg, scores, ld, ss, col, pmv);
+                           pos0, tq, n_wt, n_cc, cpc, n_wg, scores, ld, ss, flags, col, *pm);
     else
         hipLaunchKernelGGL((index_kernel<kMode, false>), dim3(grid), dim3(256), 0, stream, q_idx, qs, kbar, kbs,
-                           pos0, tq, n_wt, n_cc, cpc, n_wg, scores, ld, ss, col, pmv);
+                           pos0, tq, n_wt, n_cc, cpc, n_wg, scores, ld, ss, flags, col, PageMap{});
     return hipGetLastError();
 }
 

@@ -145,7 +145,7 @@ hipError_t launch_prefill_index_select(const uint16_t* q_idx, int64_t qs, const 
         hipError_t e = launch_index_scores(q_idx, qs, kbar, kbs, pos0, batch, tq, scores, ld, ss, nullptr, nullptr,
                                            pm, stream);
         if (e != hipSuccess) return e;
-        return launch_select(scores, ld, ss, pos0, batch, tq, budget, sel, sels, nullptr, nullptr, stream);
+        return launch_select(scores, ld, ss, pos0, batch, tq, budget, sel, sels, nullptr, stream);
     }
     const PrefillWs w = carve(ws, batch, tq);
     const unsigned rows = static_cast<unsigned>(static_cast<int64_t>(batch) * tq);
@@ -171,7 +171,7 @@ hipError_t launch_prefill_index_select(const uint16_t* q_idx, int64_t qs, const 
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = launch_index_scores(q_idx, qs, kbar, kbs, pos0, batch, tq, scores, ld, ss, w.flags, w.n_flagged, pm, stream);
     if (e != hipSuccess) return e;
-    return launch_select(scores, ld, ss, pos0, batch, tq, budget, sel, sels, w.flags, w.n_flagged, stream);
+    return launch_select(scores, ld, ss, pos0, batch, tq, budget, sel, sels, w.flags, stream);
 }
 
 }  // namespace qsa

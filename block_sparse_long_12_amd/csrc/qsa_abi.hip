@@ -305,7 +305,7 @@ qsa_status_t qsa_select_topk(const float* scores, int64_t scores_ld, int64_t sco
     TRY(check_scores_layout(scores, scores_ld, scores_seq_stride, batch, tq, p));
     CHECK(batch == 1 || sel_seq_stride >= int64_t{tq} * budget, "sel_seq_stride < tq * budget");
     return hip_result(qsa::launch_select(scores, scores_ld, scores_seq_stride, p, batch, tq, budget, sel,
-                                         sel_seq_stride, nullptr, nullptr, stream),
+                                         sel_seq_stride, nullptr, stream),
                       "select_topk launch");
 }
 

@@ -123,14 +123,10 @@ hipError_t launch_index_scores(const uint16_t* q_idx, int64_t qs, const uint16_t
                                float* scores, int64_t ld, int64_t ss, const int* row_flags,
                                const int* n_flagged, const PageMap* pm, hipStream_t stream);
 
-// row_flags (may be null): only rows with a nonzero flag are selected, and none while
-// *n_flagged (if given) is zero; their flags are cleared
+// row_flags (may be null): only rows with a nonzero flag are selected; their flags are cleared
 hipError_t launch_select(const float* scores, int64_t ld, int64_t ss, const Positions& pos0,
                          int batch, int tq, int budget, int32_t* sel, int64_t sels, int* row_flags,
-                         const int* n_flagged, hipStream_t stream);
-
-// workgroups of the launches that redo flagged rows (they walk the rows or tiles)
-constexpr unsigned kFallbackGrid = 1024;
+                         hipStream_t stream);
 
 // ---- fused prefill index-select (threshold from a sample, candidate lists) ----
 constexpr int kSampleRuns = 256;                  // sample runs per sequence

@@ -15,50 +15,20 @@ __device__ __forceinline__ bool take_flagged_row(int* flags, int64_t row, int* s
     return f != 0;
 }
 
-// One row of the multi-pass radix select.
 template <int NT>
-__device__ __forceinline__ void select_one_row(const float* __restrict__ scores, int64_t ld, int64_t ss,
-                                               const Positions& pos0, int tq, int budget, int32_t* __restrict__ sel,
-                                               int64_t sels, int64_t row, SelectSmem& sm) {
-    const int b = static_cast<int>(row / tq);
-    const int i = static_cast<int>(row % tq);
+__global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ scores, int64_t ld,
+                                                    int64_t ss, Positions pos0, int tq, int budget,
+                                                    int32_t* __restrict__ sel, int64_t sels, int* flags) {
+    __shared__ SelectSmem sm;
+    __shared__ int sh_flag;
+    const int b = blockIdx.x / tq;
+    const int i = blockIdx.x % tq;
+    if (!take_flagged_row(flags, blockIdx.x, &sh_flag)) return;
     const int p = pos0.p[b] + i;
     const int o = p / kBlock;
     const int keep = min(budget - 1, o);
     select_row<NT>(scores + b * ss + static_cast<int64_t>(i) * ld, o, keep, budget,
                    sel + b * sels + static_cast<int64_t>(i) * budget, sm);
-}
-
-template <int NT>
-__global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ scores, int64_t ld,
-                                                    int64_t ss, Positions pos0, int tq, int budget,
-                                                    int32_t* __restrict__ sel, int64_t sels) {
-    __shared__ SelectSmem sm;
-    select_one_row<NT>(scores, ld, ss, pos0, tq, budget, sel, sels, blockIdx.x, sm);
-}
-
-// The flagged rows of an earlier pass, nothing while *n_flagged (if given) is
-// zero: a small grid whose workgroups walk the rows, so the common case with
-// no flagged row costs one round of dispatches, not one per row.
-template <typename RowFn>
-__device__ __forceinline__ void walk_flagged_rows(int64_t rows, int* flags, const int* n_flagged, int* sh_flag,
-                                                  RowFn&& fn) {
-    if (n_flagged != nullptr && *n_flagged == 0) return;
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {       // uniform
-        if (take_flagged_row(flags, row, sh_flag)) fn(row);
-        __syncthreads();                                  // the row's LDS use ends before the next row's begins
-    }
-}
-
-template <int NT>
-__global__ __launch_bounds__(NT) void select_fallback_kernel(const float* __restrict__ scores, int64_t ld,
-                                                             int64_t ss, Positions pos0, int tq, int budget,
-                                                             int32_t* __restrict__ sel, int64_t sels, int* flags,
-                                                             int64_t rows, const int* n_flagged) {
-    __shared__ SelectSmem sm;
-    __shared__ int sh_flag;
-    walk_flagged_rows(rows, flags, n_flagged, &sh_flag,
-                      [&](int64_t row) { select_one_row<NT>(scores, ld, ss, pos0, tq, budget, sel, sels, row, sm); });
 }
 
 // ---------------------------------------------------------------------------
@@ -110,12 +80,15 @@ __device__ __forceinline__ void wave_append(bool q, float s, int j, uint64_t* se
     }
 }
 
-__device__ __forceinline__ void sampled_row(const float* __restrict__ scores, int64_t ld, int64_t ss,
-                                            const Positions& pos0, int tq, int budget, int32_t* __restrict__ sel,
-                                            int64_t sels, int64_t row_id, SelectAllSmem& smu) {
+__global__ __launch_bounds__(kSpNT) void select_sampled_kernel(const float* __restrict__ scores, int64_t ld,
+                                                               int64_t ss, Positions pos0, int tq, int budget,
+                                                               int32_t* __restrict__ sel, int64_t sels, int* flags) {
+    __shared__ SelectAllSmem smu;
+    __shared__ int sh_flag;
     SampledSmem& sm = smu.s;
-    const int b = static_cast<int>(row_id / tq);
-    const int i = static_cast<int>(row_id % tq);
+    const int b = blockIdx.x / tq;
+    const int i = blockIdx.x % tq;
+    if (!take_flagged_row(flags, blockIdx.x, &sh_flag)) return;
     const int o = (pos0.p[b] + i) / kBlock;
     const int keep = min(budget - 1, o);
     const float* row = scores + b * ss + static_cast<int64_t>(i) * ld;
@@ -207,47 +180,20 @@ __device__ __forceinline__ void sampled_row(const float* __restrict__ scores, in
                                             reinterpret_cast<uint32_t*>(sm.cand));
 }
 
-__global__ __launch_bounds__(kSpNT) void select_sampled_kernel(const float* __restrict__ scores, int64_t ld,
-                                                               int64_t ss, Positions pos0, int tq, int budget,
-                                                               int32_t* __restrict__ sel, int64_t sels) {
-    __shared__ SelectAllSmem smu;
-    sampled_row(scores, ld, ss, pos0, tq, budget, sel, sels, blockIdx.x, smu);
-}
-
-__global__ __launch_bounds__(kSpNT) void select_sampled_fallback_kernel(
-    const float* __restrict__ scores, int64_t ld, int64_t ss, Positions pos0, int tq, int budget,
-    int32_t* __restrict__ sel, int64_t sels, int* flags, int64_t rows, const int* n_flagged) {
-    __shared__ SelectAllSmem smu;
-    __shared__ int sh_flag;
-    walk_flagged_rows(rows, flags, n_flagged, &sh_flag,
-                      [&](int64_t row) { sampled_row(scores, ld, ss, pos0, tq, budget, sel, sels, row, smu); });
-}
-
 hipError_t launch_select(const float* scores, int64_t ld, int64_t ss, const Positions& pos0,
                          int batch, int tq, int budget, int32_t* sel, int64_t sels, int* flags,
-                         const int* n_flagged, hipStream_t stream) {
+                         hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(batch) * tq;
     if (rows == 0) return hipSuccess;
-    if (flags != nullptr) {
-        const unsigned grid = static_cast<unsigned>(rows < int64_t{kFallbackGrid} ? rows : int64_t{kFallbackGrid});
-        if (budget <= kResMaxBudget)
-            hipLaunchKernelGGL(select_sampled_fallback_kernel, dim3(grid), dim3(kSpNT), 0, stream, scores, ld, ss,
-                               pos0, tq, budget, sel, sels, flags, rows, n_flagged);
-        else
-            hipLaunchKernelGGL(select_fallback_kernel<256>, dim3(grid), dim3(256), 0, stream, scores, ld, ss, pos0,
-                               tq, budget, sel, sels, flags, rows, n_flagged);
-        return hipGetLastError();
-    }
-    const dim3 grid(static_cast<unsigned>(rows));
     if (budget <= kResMaxBudget) {
-        hipLaunchKernelGGL(select_sampled_kernel, grid, dim3(kSpNT), 0, stream, scores, ld, ss, pos0, tq, budget,
-                           sel, sels);
+        hipLaunchKernelGGL(select_sampled_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSpNT), 0, stream,
+                           scores, ld, ss, pos0, tq, budget, sel, sels, flags);
     } else if (rows < 1024) {
-        hipLaunchKernelGGL(select_kernel<1024>, grid, dim3(1024), 0, stream, scores, ld, ss, pos0, tq, budget, sel,
-                           sels);
+        hipLaunchKernelGGL(select_kernel<1024>, dim3(static_cast<unsigned>(rows)), dim3(1024), 0,
+                           stream, scores, ld, ss, pos0, tq, budget, sel, sels, flags);
     } else {
-        hipLaunchKernelGGL(select_kernel<256>, grid, dim3(256), 0, stream, scores, ld, ss, pos0, tq, budget, sel,
-                           sels);
+        hipLaunchKernelGGL(select_kernel<256>, dim3(static_cast<unsigned>(rows)), dim3(256), 0,
+                           stream, scores, ld, ss, pos0, tq, budget, sel, sels, flags);
     }
     return hipGetLastError();
 }

@@ -282,8 +282,8 @@ PREFILL_CASES = [
     ("normal", [80000], 200, 1025, "unfused"),
     ("normal", [30000], 300, 512, "unfused"),
     ("equal", [70000, 70000], 300, 512, "fallback"),
-    # more flagged rows (2600) and row tiles than the fallback launches have
-    # workgroups (1024): each workgroup redoes several rows and tiles
+    # every one of 2600 rows flagged: the fallback redoes 5822 row tiles of
+    # scores and 2600 row selections
     ("equal", [70000], 2600, 512, "fallback"),
     ("few_values", [66000], 500, 512, "either"),
     ("sample_high", [160000], 256, 512, "fallback"),
