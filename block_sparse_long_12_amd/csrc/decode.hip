@@ -426,16 +426,21 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 }
 
 // entries x of cand[0 .. n) ranked by (key, ~j) descending: those with rank
-// < take go to dst[rank]; the one of rank take - 1 (the cut) leaves its key in
-// *kstar.  Every thread must call it.
+// < take go to dst[rank] (and set their block's bit in bm, if given); the one
+// of rank take - 1 (the cut) leaves its key in *kstar.  Every thread must call it.
 template <int NT>
-__device__ __forceinline__ void rank_cut(const uint64_t* cand, int n, int take, int32_t* dst, uint32_t* kstar) {
+__device__ __forceinline__ void rank_cut(const uint64_t* cand, int n, int take, int32_t* dst, uint32_t* kstar,
+                                         uint32_t* bm) {
     for (int i = threadIdx.x; i < n; i += NT) {
         const uint64_t x = cand[i];
         int rk = 0;
 #pragma unroll 8
         for (int k = 0; k < n; ++k) rk += cand[k] > x ? 1 : 0;
-        if (rk < take) dst[rk] = static_cast<int32_t>(~static_cast<uint32_t>(x));
+        if (rk < take) {
+            const int32_t v = static_cast<int32_t>(~static_cast<uint32_t>(x));
+            dst[rk] = v;
+            if (bm != nullptr) atomicOr(&bm[v >> 5], 1u << (v & 31));
+        }
         if (rk == take - 1) *kstar = static_cast<uint32_t>(x >> 32);
     }
 }
@@ -446,12 +451,15 @@ __device__ __forceinline__ void rank_cut(const uint64_t* cand, int n, int take, 
 // order), leaving the keep-th largest key in sm.u.m.kstar: one radix level over
 // the entries' own key range, keys above the cut bin taken, the bin's members
 // ranked.  False (nothing decided) when the cut bin holds more than kDecCap.
-// Every thread must call it.
+// With set_bits (candidates below 32 kBitmapWords) each chosen block also sets
+// its bit in sm.u.m.bm, which must be clear: the ascending emission then needs
+// no pass of its own.  Every thread must call it.
 template <int P>
-__device__ __forceinline__ bool take_top(const uint64_t (&e)[P], int n, int keep, FinalizeSmem& sm) {
+__device__ __forceinline__ bool take_top(const uint64_t (&e)[P], int n, int keep, bool set_bits, FinalizeSmem& sm) {
     const int tid = threadIdx.x;
     uint32_t* h = sm.u.m.h;
     int32_t* chosen = sm.u.m.chosen;
+    uint32_t* bm = set_bits ? sm.u.m.bm : nullptr;
     // one radix level over the entries' own key range [kmin, kmax]: bin =
     // (key - kmin) >> shift < 4096 (the entries all sit in the tail, so the
     // top key bits would crowd them into a few bins and serialize the LDS
@@ -523,8 +531,11 @@ __device__ __forceinline__ bool take_top(const uint64_t (&e)[P], int n, int keep
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const int lane = tid & 63;
-            if ((m_up[i] >> lane) & 1ull)
-                chosen[b_up + lanes_below(m_up[i])] = static_cast<int32_t>(~static_cast<uint32_t>(e[i]));
+            if ((m_up[i] >> lane) & 1ull) {
+                const int32_t v = static_cast<int32_t>(~static_cast<uint32_t>(e[i]));
+                chosen[b_up + lanes_below(m_up[i])] = v;
+                if (bm != nullptr) atomicOr(&bm[v >> 5], 1u << (v & 31));
+            }
             if ((m_in[i] >> lane) & 1ull) lc[b_in + lanes_below(m_in[i])] = e[i];
             b_up += __popcll(m_up[i]);
             b_in += __popcll(m_in[i]);
@@ -532,15 +543,18 @@ __device__ __forceinline__ bool take_top(const uint64_t (&e)[P], int n, int keep
         lds_barrier();
         const int remaining = keep - above;
         if (inbin <= kRankMax) {
-            rank_cut<kFinNT>(lc, inbin, remaining, chosen + above, &sm.u.m.kstar);
+            rank_cut<kFinNT>(lc, inbin, remaining, chosen + above, &sm.u.m.kstar, bm);
         } else {
             // many members (tie floods): sorted, the first `remaining` taken
             const int np2 = next_pow2(inbin);
             for (int k = inbin + tid; k < np2; k += kFinNT) lc[k] = 0ull;
             lds_barrier();
             bitonic_sort<kFinNT, uint64_t, true>(lc, np2);
-            for (int k = tid; k < remaining; k += kFinNT)
-                chosen[above + k] = static_cast<int32_t>(~static_cast<uint32_t>(lc[k]));
+            for (int k = tid; k < remaining; k += kFinNT) {
+                const int32_t v = static_cast<int32_t>(~static_cast<uint32_t>(lc[k]));
+                chosen[above + k] = v;
+                if (bm != nullptr) atomicOr(&bm[v >> 5], 1u << (v & 31));
+            }
             if (tid == 0) sm.u.m.kstar = static_cast<uint32_t>(lc[remaining - 1] >> 32);
         }
         lds_barrier();
@@ -680,7 +694,10 @@ __device__ __forceinline__ bool recover(int n, const float* __restrict__ row, in
 #pragma unroll
     for (int i = 0; i < kP; ++i) e2[i] = tid + kFinNT * i < n2 ? sm.u.m.cand[tid + kFinNT * i] : 0ull;
     lds_barrier();                                        // cand and its count are reused below
-    return take_top<kP>(e2, n2, keep, sm);
+    const bool bits = o <= 32 * kBitmapWords;
+    if (bits)                                             // the first cut's bits, then wmin, were here
+        for (int k = tid; k < kBitmapWords; k += kFinNT) sm.u.m.bm[k] = 0u;
+    return take_top<kP>(e2, n2, keep, bits, sm);
 }
 
 template <int kPer>
@@ -708,12 +725,17 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
     for (int i = 0; i < kPer; ++i) e[i] = lg[tid + kFinNT * i];
     const int n = static_cast<int>(ctrl[kNList]);
     const uint32_t max_t = ctrl[kMaxT];
+    // the block bitmap of the ascending emission, cleared while the list is in
+    // flight; the cut sets the chosen blocks' bits as it takes them
+    const bool bits = o <= 32 * kBitmapWords;
+    if (bits)
+        for (int k = tid; k < kBitmapWords; k += kFinNT) sm.u.m.bm[k] = 0u;
     const bool listed = ctrl[kOverflow] == 0u && n <= kPer * kFinNT && n >= keep;
     int32_t* chosen = sm.u.m.chosen;
     bool exact = false;
     bool cut_known = false;                               // sm.u.m.kstar holds the list's own cut
     if (listed) {
-        cut_known = take_top<kPer>(e, n, keep, sm);
+        cut_known = take_top<kPer>(e, n, keep, bits, sm);
         // every key >= max T is listed: the cut is exact if the cut key reaches max T
         exact = cut_known && sm.u.m.kstar >= max_t;
     }
@@ -722,18 +744,12 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
     if (!exact) {
         select_row<kFinNT>(scores + b * ss + t * sld, o, keep, budget, out, sm.u.s);
     } else {
-        if (o <= 32 * kBitmapWords) {
-            // ascending through a bitmap of the candidate blocks: every chosen
-            // j < o sets its bit; thread t owns words kWpt t .. kWpt t + kWpt - 1
+        if (bits) {
+            // ascending through the bitmap of the chosen blocks (every chosen
+            // j < o set its bit in the cut, behind a barrier since); thread t
+            // owns words kWpt t .. kWpt t + kWpt - 1
             uint32_t* bm = sm.u.m.bm;
-            for (int k = tid; k < kBitmapWords; k += kFinNT) bm[k] = 0u;
-            lds_barrier();
-            for (int k = tid; k < keep; k += kFinNT) {
-                const int v = chosen[k];
-                atomicOr(&bm[v >> 5], 1u << (v & 31));
-            }
             if (tid == 0) out[keep] = o;                     // above every candidate
-            lds_barrier();
             constexpr int kWpt = kBitmapWords / kFinNT;
             uint32_t w[kWpt];
             int cnt = 0;
@@ -746,11 +762,11 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
             int base = block_exclusive_scan<kFinNT>(cnt, sm.u.m.wave_tot, &total);
 #pragma unroll
             for (int q = 0; q < kWpt; ++q) {
-                uint32_t bits = w[q];
-                while (bits) {
-                    const int bit = __ffs(bits) - 1;
+                uint32_t wq = w[q];
+                while (wq) {
+                    const int bit = __ffs(wq) - 1;
                     out[base++] = 32 * (kWpt * tid + q) + bit;
-                    bits &= bits - 1;
+                    wq &= wq - 1;
                 }
             }
         } else {

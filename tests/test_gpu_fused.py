@@ -506,7 +506,10 @@ def test_multi_token_decode_step_matches_primitives(pos, tq, budget, yarn):
     assert torch.equal(la.view(torch.uint8), lb.view(torch.uint8))
 
 
-@pytest.mark.parametrize("pos,tq,budget", [([70001, 262141], 4, 512), ([5000, 5001, 5002], 3, 64)])
+@pytest.mark.parametrize("pos,tq,budget", [([70001, 262141], 4, 512), ([5000, 5001, 5002], 3, 64),
+                                            # the most rows a call takes: 256 sequences of 4 tokens
+                                            ([8000 + 37 * b for b in range(256)], 4, 512)],
+                         ids=["B2-tq4", "B3-tq3", "B256-tq4"])
 def test_multi_token_index_select_decode_matches_primitives(pos, tq, budget):
     say(f"multi-token index_select_decode pos={pos} tq={tq}")
     B = len(pos)
