@@ -370,16 +370,20 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(
             }
         }
     }
-    lds_barrier();
-    // the scores in full lines: token t's blocks [j_lo, j_hi) from LDS
+    // the scores of this wave's own blocks (j0 + 256 st .. + 63) in full
+    // lines from LDS, issued before the workgroup meets: the wave reads back
+    // only what it wrote
     {
         const int n = j_hi - j_lo;
         for (int t = 0; t < tq; ++t) {
             float* sb = scores + b * ss + t * sld + j_lo;
-            for (int i = 4 * tid; i < n; i += 1024)
-                *reinterpret_cast<float4*>(sb + i) = *reinterpret_cast<const float4*>(lds_sc + t * R + i);
+            for (int st = lane >> 4; st < STEPS; st += 4) {
+                const int i = 64 * wave + 256 * st + 4 * (lane & 15);
+                if (i < n) *reinterpret_cast<float4*>(sb + i) = *reinterpret_cast<const float4*>(lds_sc + t * R + i);
+            }
         }
     }
+    lds_barrier();
     if (tid < tq) {
         const int ne = sm.n_emit[tid];
         uint32_t* ctrl = ws.ctrl + (b * tq + tid) * kCtrl;
@@ -759,7 +763,7 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(const float* __
                 cnt += __popc(w[q]);
             }
             int total;
-            int base = block_exclusive_scan<kFinNT>(cnt, sm.u.m.wave_tot, &total);
+            int base = block_exclusive_scan<kFinNT, false>(cnt, sm.u.m.wave_tot, &total);   // wave_tot not used again
 #pragma unroll
             for (int q = 0; q < kWpt; ++q) {
                 uint32_t wq = w[q];

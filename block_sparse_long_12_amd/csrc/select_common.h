@@ -36,7 +36,11 @@ struct SelectSmem {
     uint32_t sh_bin;
 };
 
-template <int NT>
+// Exclusive prefix sum of v over the workgroup; *total gets the sum.  With
+// kTrailingSync false the call ends without the barrier that keeps wave_tot
+// from being rewritten while slower threads still read it: for callers whose
+// next write of wave_tot is behind a barrier of their own anyway.
+template <int NT, bool kTrailingSync = true>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -55,7 +59,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* t
         before += (w < wave) ? t : 0;
         all += t;
     }
-    lds_barrier();
+    if (kTrailingSync) lds_barrier();
     *total = all;
     return before + x - v;
 }
@@ -100,7 +104,7 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, int nb,
     int local = 0;
     for (int q = 0; q < bpt; ++q) local += static_cast<int>(hist[hi - q]);
     int total;
-    const int above = block_exclusive_scan<NT>(local, wave_tot, &total);
+    const int above = block_exclusive_scan<NT, false>(local, wave_tot, &total);   // the barrier below follows
     if (above < remaining && above + local >= remaining) {
         int run = above;
         for (int q = 0; q < bpt; ++q) {
@@ -446,7 +450,7 @@ __device__ void finish_from_candidates(const uint64_t (&c)[K], const bool (&cv)[
             cnt += __popc(wv[q]);
         }
         int all;
-        int base = block_exclusive_scan<NT>(cnt, sm.wave_tot, &all);
+        int base = block_exclusive_scan<NT, false>(cnt, sm.wave_tot, &all);   // wave_tot is not used again
 #pragma unroll
         for (int q = 0; q < kWpt; ++q) {
             uint32_t bits = wv[q];
