@@ -705,6 +705,9 @@ hipError_t launch_gdn_prefill(const GdnIn& in, int batch, int n_tokens, void* ws
 // ---------------------------------------------------------------- decode
 
 // Thread t holds state rows 16 (t / 32) .. + 15 of column 32cb + t % 32.
+// Only LDS data crosses threads (each thread reads and rewrites its own
+// state rows), so the barriers are LDS-only: the output's reduction does not
+// wait for the state rows still being written back.
 __global__ __launch_bounds__(256) void gdn_decode_kernel(GdnIn in) {
     __shared__ float s_q[kGdnD], s_k[kGdnD];
     __shared__ float red[2][8][kGdnCols];
@@ -737,13 +740,13 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(GdnIn in) {
         s_norm[0][tid >> 6] = sq;
         s_norm[1][tid >> 6] = sk;
     }
-    __syncthreads();
+    lds_barrier();
     const float nq = s_norm[0][0] + s_norm[0][1], nk = s_norm[1][0] + s_norm[1][1];
     if (tid < kGdnD) {
         s_q[tid] = nq > 0.f ? qv / (sqrtf(nq) * sqrtf(static_cast<float>(kGdnD))) : 0.f;
         s_k[tid] = nk > 0.f ? kv / sqrtf(nk) : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     const float alpha = expf(in.g[b * in.gs + h]);
     const float beta = in.beta[b * in.gs + h];
     // k^T S for this column
@@ -751,7 +754,7 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(GdnIn in) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) ks += s_k[d0 + r] * s[r];
     red[0][tid / kGdnCols][j] = ks;
-    __syncthreads();
+    lds_barrier();
     float kst = 0.f;
 #pragma unroll
     for (int x = 0; x < 8; ++x) kst += red[0][x][j];
@@ -765,7 +768,7 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(GdnIn in) {
         sg[(d0 + r) * kGdnD] = s[r];
     }
     red[1][tid / kGdnCols][j] = os;
-    __syncthreads();
+    lds_barrier();
     if (tid < kGdnCols) {
         float o = 0.f;
 #pragma unroll
