@@ -437,9 +437,17 @@ def test_decode_step_appends_rows_and_compresses(pos, budget):
 
 # ---------------------------------------------------------------- several decode tokens per sequence
 
-@pytest.mark.parametrize("pos,tq,budget,yarn", [([4097, 9000, 70001], 4, 512, False), ([4099, 8191], 2, 512, False),
-                                                ([131069, 131072], 3, 512, False), ([1, 6], 4, 8, False),
-                                                ([262143, 300001], 3, 512, True), ([5, 9000], 2, 64, True)])
+MULTI_STEP_CASES = [([4097, 9000, 70001], 4, 512, False), ([4099, 8191], 2, 512, False),
+                    ([131069, 131072], 3, 512, False), ([1, 6], 4, 8, False),
+                    ([262143, 300001], 3, 512, True), ([5, 9000], 2, 64, True),
+                    # the most rows a step takes (256 sequences of 4 tokens: one attention split
+                    # per row), the shorter rows keeping every candidate
+                    ([2000 + 7 * b for b in range(256)], 4, 512, False)]
+
+
+@pytest.mark.parametrize("pos,tq,budget,yarn", MULTI_STEP_CASES,
+                         ids=[f"B{len(c[0])}-pos{c[0][0]}-tq{c[1]}-b{c[2]}{'-yarn' if c[3] else ''}"
+                              for c in MULTI_STEP_CASES])
 def test_multi_token_decode_step_matches_primitives(pos, tq, budget, yarn):
     """tq new tokens per sequence in one step (one pass over the block keys
     scores every token) equal the primitive chain bit for bit: the appended
