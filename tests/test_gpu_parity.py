@@ -562,3 +562,44 @@ def test_yarn_prefill_layer_end_to_end():
     rows = [(0, 263000 + i) for i in range(0, 200, 9)]
     compare_rows(oracle_layer(x, O.Yarn()), x, rows, None, lambda b, t: sel[b, t - 263000],
                  lambda b, t: out[b, t - 263000], lambda b, t: lse[b, t - 263000])
+
+
+def test_decode_step_at_position_zero_returns_the_new_value_rows():
+    """A sequence with nothing cached: the selection is the own block alone,
+    which holds only the new token, so softmax gives that token weight 1.  At
+    position 0 the rotation is the identity.  Every head of KV group g then
+    returns the token's V row of group g bit for bit; the LSE is the scaled
+    logit q.k, within 2^-15 sum |q k| (float32 accumulation of 256 bf16
+    products); the selection is [0, -1, ...]."""
+    say("decode_step at position 0")
+    B, budget, L = 3, 64, 8
+    dev, bf = "cuda", torch.bfloat16
+    g = torch.Generator().manual_seed(5)
+    q_raw = torch.randn((B, 1, 24, 256), generator=g).to(bf)
+    k_new = torch.randn((B, 1, 2, 256), generator=g).to(bf)
+    v_new = torch.randn((B, 1, 2, 256), generator=g).to(bf)
+    q_idx = (torch.randn((B, 1, 4, 128), generator=g) / math.sqrt(128)).to(bf)
+    k_idx_new = (torch.randn((B, 1, 128), generator=g) / math.sqrt(128)).to(bf)
+    kc = torch.zeros((B, L, 2, 256), dtype=bf, device=dev)
+    vc = torch.zeros_like(kc)
+    ki = torch.zeros((B, L, 128), dtype=bf, device=dev)
+    kb = torch.zeros((B, L // 4 + 1, 128), dtype=bf, device=dev)
+    scores = torch.zeros((B, 1, 4), device=dev)
+    sel = torch.empty((B, 1, budget), dtype=torch.int32, device=dev)
+    out = torch.empty((B, 24, 256), dtype=bf, device=dev)
+    lse = torch.empty((B, 24), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(256)
+    qsa.decode_step(q_raw.to(dev), k_new.to(dev), q_idx.to(dev), ki, kc, vc, kb, 0, budget, out, lse, scores, sel,
+                    qsa.decode_step_workspace(B, budget), scale=scale, v_new=v_new.to(dev),
+                    k_idx_new=k_idx_new.to(dev))
+    torch.cuda.synchronize()
+    assert sel[:, 0, 0].eq(0).all() and sel[:, 0, 1:].eq(-1).all()
+    assert torch.equal(kc[:, 0].cpu().view(torch.int16), k_new[:, 0].view(torch.int16))   # identity rotation
+    o = out.cpu()
+    for h in range(24):
+        assert torch.equal(o[:, h].view(torch.int16), v_new[:, 0, h // 12].view(torch.int16)), h
+    qd = q_raw[:, 0].double()                                      # [B, 24, 256]
+    kd = k_new[:, 0].double()                                      # [B, 2, 256]
+    logit = torch.einsum("bhd,bhd->bh", qd, kd.repeat_interleave(12, dim=1))
+    bound = 2.0 ** -15 * torch.einsum("bhd,bhd->bh", qd.abs(), kd.abs().repeat_interleave(12, dim=1)) + 1e-6
+    assert (lse.cpu().double() - logit * scale).abs().le(bound * scale).all()
