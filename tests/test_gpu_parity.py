@@ -603,3 +603,40 @@ def test_decode_step_at_position_zero_returns_the_new_value_rows():
     logit = torch.einsum("bhd,bhd->bh", qd, kd.repeat_interleave(12, dim=1))
     bound = 2.0 ** -15 * torch.einsum("bhd,bhd->bh", qd.abs(), kd.abs().repeat_interleave(12, dim=1)) + 1e-6
     assert (lse.cpu().double() - logit * scale).abs().le(bound * scale).all()
+
+
+def test_prefill_from_position_zero_first_row_returns_its_value_row():
+    """A prefill of the first 300 tokens: the rows of block 0 select the own
+    block alone ([0, -1, ...]); row 0 attends only token 0, whose rotation is
+    the identity, so every head of KV group g returns V[0, g] bit for bit and
+    the LSE is the scaled logit q.k (within 2^-15 sum |q k|).  Two streams
+    and two query chunks, so the side-stream order is on the path too."""
+    say("prefill_layer from position 0")
+    B, T, budget = 2, 300, 64
+    dev, bf = "cuda", torch.bfloat16
+    g = torch.Generator().manual_seed(8)
+    q_raw = torch.randn((B, T, 24, 256), generator=g).to(bf)
+    k_new = torch.randn((B, T, 2, 256), generator=g).to(bf)
+    v = torch.randn((B, T, 2, 256), generator=g).to(bf)
+    q_idx = (torch.randn((B, T, 4, 128), generator=g) / math.sqrt(128)).to(bf)
+    k_idx = (torch.randn((B, T, 128), generator=g) / math.sqrt(128)).to(bf)
+    kc = torch.zeros((B, T, 2, 256), dtype=bf, device=dev)
+    kb = torch.zeros((B, T // 4 + 1, 128), dtype=bf, device=dev)
+    out = torch.empty((B, T, 24, 256), dtype=bf, device=dev)
+    lse = torch.empty((B, T, 24), dtype=torch.float32, device=dev)
+    bufs = qsa.PrefillBuffers(B, T, 0, budget, 160)
+    scale = 1.0 / math.sqrt(256)
+    qsa.prefill_layer(q_raw.to(dev), k_new.to(dev), q_idx.to(dev), k_idx.to(dev), kc, v.to(dev), kb, 0, budget, out,
+                      lse, bufs, torch.empty((B, T, 24, 256), dtype=bf, device=dev), side_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    sel = bufs.sel.cpu()
+    assert sel[:, :4, 0].eq(0).all() and sel[:, :4, 1:].eq(-1).all()
+    assert torch.equal(kc[:, 0].cpu().view(torch.int16), k_new[:, 0].view(torch.int16))   # identity rotation
+    o = out[:, 0].cpu()
+    for h in range(24):
+        assert torch.equal(o[:, h].view(torch.int16), v[:, 0, h // 12].view(torch.int16)), h
+    qd = q_raw[:, 0].double()
+    kd = k_new[:, 0].double().repeat_interleave(12, dim=1)
+    logit = (qd * kd).sum(-1)
+    bound = 2.0 ** -15 * (qd.abs() * kd.abs()).sum(-1) + 1e-6
+    assert (lse[:, 0].cpu().double() - logit * scale).abs().le(bound * scale).all()
